@@ -1,0 +1,69 @@
+"""Workload registry: the five FNO workloads this library is checked and measured on.
+
+Pure data.  Shapes follow the FNO of the model-parallel FNO page ("Proposed method": 4
+spectral blocks, width 20; "Main findings": 3D and 4D space-time grids) and the
+mixed-precision neural-operator page ("Tiivistelmä": tanh pre-activation, half-precision
+transform and contraction).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional, Tuple
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    cfg_id: int                   # seed namespace of the input generators
+    batch: int
+    width: int                    # channels inside the blocks (Cin = Cout)
+    grid: Tuple[int, ...]         # spatial grid N_0..N_{d-1}; the last axis is contiguous
+    modes: Tuple[int, ...]        # modes per corner m_0..m_{d-1}
+    blocks: int                   # number of spectral blocks
+    mixed: bool                   # tanh pre-activation + bf16 spectral operands
+    train: bool                   # forward + MSE + backward (else forward only)
+    lift_in: Optional[int] = None     # pointwise lift input channels (C2)
+    proj_hidden: Optional[int] = None  # projection hidden width (C2)
+    proj_out: Optional[int] = None
+    zero_bias: bool = False
+    input_kind: str = "grf"       # grf | normal | grf_coords | grf_layered
+    notes: str = ""
+
+    @property
+    def ndim(self) -> int:
+        return len(self.grid)
+
+    @property
+    def points(self) -> int:
+        p = 1
+        for n in self.grid:
+            p *= n
+        return p
+
+    @property
+    def units(self) -> int:
+        """Grid points x channels x batch x blocks: the throughput unit."""
+        return self.batch * self.width * self.points * self.blocks
+
+
+WORKLOADS = {
+    "c1": Workload("c1", 1, 4, 20, (64, 64), (12, 12), 1, False, False,
+                   zero_bias=True, input_kind="normal",
+                   notes="2D single spectral layer, forward only, fp32"),
+    "c2": Workload("c2", 2, 16, 32, (256, 256), (16, 16), 4, False, False,
+                   lift_in=3, proj_hidden=128, proj_out=1, input_kind="grf_coords",
+                   notes="2D FNO stack forward, fp32, lift 3->32, projection 32->128->1"),
+    "c3": Workload("c3", 3, 8, 64, (512, 512), (32, 32), 4, True, True,
+                   notes="2D FNO training step, tanh + bf16 spectral path, fwd+bwd, MSE"),
+    "c4": Workload("c4", 4, 2, 20, (128, 128, 128), (16, 16, 16), 4, False, True,
+                   input_kind="grf_layered",
+                   notes="3D FNO stack fwd+bwd, fp32, layered permeability channel"),
+    "c5": Workload("c5", 5, 1, 20, (128, 128, 128, 20), (12, 12, 12, 8), 4, False, False,
+                   notes="4D space-time block stack forward, fp32"),
+    "c5h": Workload("c5h", 5, 1, 20, (128, 128, 128, 20), (12, 12, 12, 8), 4, True, False,
+                    notes="4D space-time block stack forward, tanh + bf16"),
+}
+
+
+def get(name: str) -> Workload:
+    return WORKLOADS[name.lower()]

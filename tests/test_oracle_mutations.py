@@ -1,0 +1,110 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and show that a pin catches each.
+
+Every mutation below replaces one oracle function with a subtly wrong copy (a flipped
+sign, an index off by one, a dropped term, a transposed or unconjugated operand).  The
+named pin must then fail.  This is what makes the pins meaningful: a pin that passes on a
+broken oracle pins nothing.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle.fno_oracle as O
+from tests import oracle_pins as P
+
+_orig = {name: getattr(O, name) for name in dir(O) if not name.startswith("__")}
+
+
+def _dft_sign_flipped(n, ks, sign):
+    return _orig["dft_matrix"](n, ks, -sign)
+
+
+def _retained_off_by_one(n, m, last):
+    if last:
+        return np.arange(m, dtype=np.int64)
+    return np.concatenate([np.arange(m), np.arange(n - m - 1, n - 1)]).astype(np.int64)
+
+
+def _gamma_all_two(n_last, m_last):
+    return np.full(m_last, 2.0)
+
+
+def _gamma_no_nyquist(n_last, m_last):
+    g = np.full(m_last, 2.0)
+    g[0] = 1.0
+    return g
+
+
+def _expand_bits_reversed(w, modes):
+    d = len(modes)
+    if d < 3:
+        return _orig["expand_weights"](w, modes)
+    ncorner = 1 << (d - 1)
+    perm = []
+    for c in range(ncorner):
+        r = 0
+        for j in range(d - 1):
+            if (c >> j) & 1:
+                r |= 1 << (d - 2 - j)
+        perm.append(r)
+    return _orig["expand_weights"](w[perm], modes)
+
+
+def _mix_conj(xhat, w, modes):
+    return _orig["channel_mix"](xhat, np.conj(w), modes)
+
+
+def _inverse_imag_sign(yhat, shape, modes, unit_scale=False):
+    return _orig["inverse_spectrum"](np.conj(yhat), shape, modes, unit_scale)
+
+
+def _adjoint_no_gamma(g, modes):
+    d = g.ndim - 2
+    return _orig["spectrum"](g, modes) / float(np.prod(g.shape[2:]))
+
+
+def _gelu_prime_no_pdf(z):
+    z = np.asarray(z, dtype=np.float64)
+    return 0.5 * (1.0 + np.vectorize(math.erf)(z / math.sqrt(2.0)))
+
+
+def _bwd_no_conj(x, w, modes, g_yspec, tanh=False):
+    return _orig["spectral_conv_bwd"](x, np.conj(w), modes, g_yspec, tanh)
+
+
+def _block_bwd_no_tanh_prime(x, w, wb, bias, modes, g_y, tanh=False, act=True):
+    r = _orig["block_bwd"](x, w, wb, bias, modes, g_y, tanh=tanh, act=act)
+    if tanh:
+        r = dict(r)
+        r["grad_x"] = r["grad_x"] - r["gx_spec"] + r["gx_spec"] / np.maximum(
+            1.0 - np.tanh(x) ** 2, 1e-300)
+    return r
+
+
+def _block_no_bias(x, w, wb, bias, modes, tanh=False, act=True):
+    return _orig["block_fwd"](x, w, wb, None, modes, tanh=tanh, act=act)
+
+
+MUTATIONS = [
+    ("dft_matrix", _dft_sign_flipped, P.check_spectrum_bruteforce),
+    ("retained_indices", _retained_off_by_one, P.check_spectrum_numpy_fft),
+    ("gamma_weights", _gamma_all_two, P.check_roundtrip_identity),
+    ("gamma_weights", _gamma_no_nyquist, P.check_parseval_and_dc),
+    ("expand_weights", _expand_bits_reversed, P.check_single_mode_closed_form),
+    ("channel_mix", _mix_conj, P.check_single_mode_closed_form),
+    ("inverse_spectrum", _inverse_imag_sign, P.check_inverse_numpy_irfftn),
+    ("adjoint_inverse", _adjoint_no_gamma, P.check_adjoint_identities),
+    ("gelu_prime", _gelu_prime_no_pdf, P.check_gelu),
+    ("spectral_conv_bwd", _bwd_no_conj, P.check_adjoint_identities),
+    ("block_bwd", _block_bwd_no_tanh_prime, P.check_block_finite_differences),
+    ("block_fwd", _block_no_bias, P.check_zero_weight_block),
+]
+
+
+@pytest.mark.parametrize("name,bad,check", MUTATIONS,
+                         ids=[f"{m[0]}:{m[1].__name__}" for m in MUTATIONS])
+def test_pin_catches_mutation(monkeypatch, name, bad, check):
+    monkeypatch.setattr(O, name, bad)
+    with pytest.raises((AssertionError, ValueError)):
+        check(O)
