@@ -1,0 +1,293 @@
+"""ctypes binding of libfno (argument marshalling only).
+
+Every function of ``include/fno.h`` is exposed under its C name and takes plain integers
+for pointers (``tensor.data_ptr()``) and streams (``torch.cuda.current_stream().cuda_stream``).
+``Plan`` wraps a plan for torch tensors: it allocates outputs, workspace and save buffers
+with torch on the plan's device and forwards pointers; every step of the computation runs
+in libfno's HIP kernels.  There is no fallback: if libfno.so is missing or fails to load,
+importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, byref, c_char_p, c_int, c_int32, c_int64, c_size_t, c_uint32, c_void_p
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfno.so")
+
+FNO_OK = 0
+FNO_ERR_INVALID_ARGUMENT = 1
+FNO_ERR_UNSUPPORTED = 2
+FNO_ERR_HIP = 3
+FNO_ERR_OUT_OF_MEMORY = 4
+FNO_ERR_INTERNAL = 5
+
+FNO_DTYPE_F32 = 0
+FNO_DTYPE_BF16 = 1
+FNO_DTYPE_F16 = 2
+
+FNO_FLAG_TANH_PREACT = 1
+FNO_FLAG_GELU = 2
+FNO_FLAG_BIAS = 4
+
+EXPORTS = [
+    "fno_plan_validate", "fno_plan_create", "fno_plan_destroy", "fno_plan_query",
+    "fno_spectral_conv_fwd", "fno_spectral_conv_bwd", "fno_block_fwd", "fno_block_bwd",
+    "fno_pointwise_fwd", "fno_mse_workspace_bytes", "fno_mse_grad", "fno_status_string",
+    "fno_last_error_message",
+]
+
+
+class fno_plan_desc(ctypes.Structure):
+    _fields_ = [("ndim", c_int32), ("spectral_dtype", c_int32), ("flags", c_uint32),
+                ("reserved", c_int32), ("batch", c_int64), ("c_in", c_int64),
+                ("c_out", c_int64), ("n", c_int64 * 4), ("modes", c_int64 * 4)]
+
+
+class FnoError(RuntimeError):
+    def __init__(self, status: int, where: str, msg: str):
+        super().__init__(f"{where}: {status_string(status)}: {msg}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libfno.so not built ({LIB_PATH}); run "
+                           "`python -m fno_spectral_convolution_amd.build`")
+    # torch brings its own HIP runtime; load it first so that libfno's libamdhip64
+    # dependency resolves to that same, already loaded runtime (one HIP runtime per process:
+    # libfno's kernels then run on torch's streams and memory).
+    import torch  # noqa: F401
+    lib = ctypes.CDLL(LIB_PATH)
+    P = c_void_p
+    sig = {
+        "fno_plan_validate": (c_int, [POINTER(fno_plan_desc)]),
+        "fno_plan_create": (c_int, [POINTER(fno_plan_desc), POINTER(c_void_p)]),
+        "fno_plan_destroy": (c_int, [P]),
+        "fno_plan_query": (c_int, [P, POINTER(c_size_t), POINTER(c_size_t), POINTER(c_size_t)]),
+        "fno_spectral_conv_fwd": (c_int, [P, P, P, P, P, P, c_size_t, P]),
+        "fno_spectral_conv_bwd": (c_int, [P, P, P, P, P, P, P, P, c_size_t, P]),
+        "fno_block_fwd": (c_int, [P, P, P, P, P, P, P, P, c_size_t, P]),
+        "fno_block_bwd": (c_int, [P, P, P, P, P, P, P, P, P, P, P, P, c_size_t, P]),
+        "fno_pointwise_fwd": (c_int, [c_int64, c_int64, c_int64, c_int64, c_int64,
+                                      P, P, P, P, P, P, P]),
+        "fno_mse_workspace_bytes": (c_int, [c_int64, POINTER(c_size_t)]),
+        "fno_mse_grad": (c_int, [c_int64, P, P, P, P, P, c_size_t, P]),
+        "fno_status_string": (c_char_p, [c_int]),
+        "fno_last_error_message": (c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def status_string(status: int) -> str:
+    return _lib.fno_status_string(status).decode()
+
+
+def last_error_message() -> str:
+    return _lib.fno_last_error_message().decode()
+
+
+def _check(status: int, where: str):
+    if status != FNO_OK:
+        raise FnoError(status, where, last_error_message())
+
+
+def make_desc(batch, c_in, c_out, grid, modes, dtype=FNO_DTYPE_F32, flags=0) -> fno_plan_desc:
+    d = fno_plan_desc()
+    d.ndim = len(grid)
+    d.spectral_dtype = dtype
+    d.flags = flags
+    d.reserved = 0
+    d.batch, d.c_in, d.c_out = batch, c_in, c_out
+    for j in range(4):
+        d.n[j] = grid[j] if j < len(grid) else 0
+        d.modes[j] = modes[j] if j < len(modes) else 0
+    return d
+
+
+# ---- raw C entry points (same names as the header) ----------------------------------------
+def fno_plan_validate(desc: fno_plan_desc) -> int:
+    return _lib.fno_plan_validate(byref(desc))
+
+
+def fno_plan_create(desc: fno_plan_desc) -> int:
+    out = c_void_p()
+    _check(_lib.fno_plan_create(byref(desc), byref(out)), "fno_plan_create")
+    return out.value
+
+
+def fno_plan_destroy(plan: int) -> None:
+    _check(_lib.fno_plan_destroy(plan), "fno_plan_destroy")
+
+
+def fno_plan_query(plan: int):
+    ws, sv, we = c_size_t(), c_size_t(), c_size_t()
+    _check(_lib.fno_plan_query(plan, byref(ws), byref(sv), byref(we)), "fno_plan_query")
+    return ws.value, sv.value, we.value
+
+
+def fno_spectral_conv_fwd(plan, x, w, y_spec, save, ws, ws_bytes, stream):
+    _check(_lib.fno_spectral_conv_fwd(plan, x, w, y_spec, save, ws, ws_bytes, stream),
+           "fno_spectral_conv_fwd")
+
+
+def fno_spectral_conv_bwd(plan, x, w, save, grad_y_spec, grad_x, grad_w, ws, ws_bytes, stream):
+    _check(_lib.fno_spectral_conv_bwd(plan, x, w, save, grad_y_spec, grad_x, grad_w, ws,
+                                      ws_bytes, stream), "fno_spectral_conv_bwd")
+
+
+def fno_block_fwd(plan, x, w, w_bypass, bias, y, save, ws, ws_bytes, stream):
+    _check(_lib.fno_block_fwd(plan, x, w, w_bypass, bias, y, save, ws, ws_bytes, stream),
+           "fno_block_fwd")
+
+
+def fno_block_bwd(plan, x, w, w_bypass, bias, save, grad_y, grad_x, grad_w, grad_w_bypass,
+                  grad_bias, ws, ws_bytes, stream):
+    _check(_lib.fno_block_bwd(plan, x, w, w_bypass, bias, save, grad_y, grad_x, grad_w,
+                              grad_w_bypass, grad_bias, ws, ws_bytes, stream), "fno_block_bwd")
+
+
+def fno_pointwise_fwd(batch, npts, c_in, hidden, c_out, x, w1, b1, w2, b2, y, stream):
+    _check(_lib.fno_pointwise_fwd(batch, npts, c_in, hidden, c_out, x, w1, b1, w2, b2, y,
+                                  stream), "fno_pointwise_fwd")
+
+
+def fno_mse_workspace_bytes(n: int) -> int:
+    b = c_size_t()
+    _check(_lib.fno_mse_workspace_bytes(n, byref(b)), "fno_mse_workspace_bytes")
+    return b.value
+
+
+def fno_mse_grad(n, y, t, grad, loss, ws, ws_bytes, stream):
+    _check(_lib.fno_mse_grad(n, y, t, grad, loss, ws, ws_bytes, stream), "fno_mse_grad")
+
+
+# ---- torch-facing convenience (allocation + pointer marshalling only) ---------------------
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+class Plan:
+    """One FNO block shape.  Tensors are torch tensors on the plan's device: fields float32
+    [B, C, *grid], spectral weights complex64 [2^(d-1), Cin, Cout, *modes], bypass float32
+    [Cout, Cin], bias float32 [Cout]."""
+
+    def __init__(self, batch, c_in, c_out, grid, modes, mixed=False, tanh=None, gelu=True,
+                 bias=True, device=None):
+        import torch
+        self.torch = torch
+        self.device = torch.device(device) if device is not None else torch.device("cuda")
+        tanh = mixed if tanh is None else tanh
+        flags = (FNO_FLAG_TANH_PREACT if tanh else 0) | (FNO_FLAG_GELU if gelu else 0) | \
+            (FNO_FLAG_BIAS if bias else 0)
+        self.desc = make_desc(batch, c_in, c_out, tuple(grid), tuple(modes),
+                              FNO_DTYPE_BF16 if mixed else FNO_DTYPE_F32, flags)
+        self.batch, self.c_in, self.c_out = batch, c_in, c_out
+        self.grid, self.modes = tuple(grid), tuple(modes)
+        self.flags = flags
+        with torch.cuda.device(self.device):
+            self.handle = fno_plan_create(self.desc)
+        self.ws_bytes, self.save_bytes, self.weight_elems = fno_plan_query(self.handle)
+        self._ws = None
+
+    def close(self):
+        if getattr(self, "handle", None):
+            fno_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # buffers
+    def workspace(self):
+        if self._ws is None:
+            self._ws = self.torch.empty(max(self.ws_bytes, 16), dtype=self.torch.uint8,
+                                        device=self.device)
+        return self._ws
+
+    def new_save(self):
+        return self.torch.empty(max(self.save_bytes, 16), dtype=self.torch.uint8,
+                                device=self.device)
+
+    def _field(self, c):
+        return self.torch.empty((self.batch, c) + self.grid, dtype=self.torch.float32,
+                                device=self.device)
+
+    def _stream(self):
+        return self.torch.cuda.current_stream(self.device).cuda_stream
+
+    # entry points
+    def spectral_conv_fwd(self, x, w, save=None, out=None):
+        y = out if out is not None else self._field(self.c_out)
+        ws = self.workspace()
+        fno_spectral_conv_fwd(self.handle, x.data_ptr(), w.data_ptr(), y.data_ptr(), _ptr(save),
+                              ws.data_ptr(), self.ws_bytes, self._stream())
+        return y
+
+    def spectral_conv_bwd(self, x, w, grad_y_spec, save=None, want_x=True, want_w=True):
+        gx = self._field(self.c_in) if want_x else None
+        gw = self.torch.empty_like(w) if want_w else None
+        ws = self.workspace()
+        fno_spectral_conv_bwd(self.handle, x.data_ptr(), w.data_ptr(), _ptr(save),
+                              grad_y_spec.data_ptr(), _ptr(gx), _ptr(gw), ws.data_ptr(),
+                              self.ws_bytes, self._stream())
+        return gx, gw
+
+    def block_fwd(self, x, w, wb, bias=None, save=None, out=None):
+        y = out if out is not None else self._field(self.c_out)
+        ws = self.workspace()
+        fno_block_fwd(self.handle, x.data_ptr(), w.data_ptr(), wb.data_ptr(), _ptr(bias),
+                      y.data_ptr(), _ptr(save), ws.data_ptr(), self.ws_bytes, self._stream())
+        return y
+
+    def block_bwd(self, x, w, wb, bias, save, grad_y, want=("x", "w", "wb", "bias"), out=None):
+        t = self.torch
+        o = dict(out or {})
+        gx = o.get("x", self._field(self.c_in) if "x" in want else None)
+        gw = o.get("w", t.empty_like(w) if "w" in want else None)
+        gwb = o.get("wb", t.empty_like(wb) if "wb" in want else None)
+        gb = o.get("bias", t.empty(self.c_out, dtype=t.float32, device=self.device)
+                   if "bias" in want else None)
+        ws = self.workspace()
+        fno_block_bwd(self.handle, x.data_ptr(), w.data_ptr(), wb.data_ptr(), _ptr(bias),
+                      _ptr(save), grad_y.data_ptr(), _ptr(gx), _ptr(gw), _ptr(gwb), _ptr(gb),
+                      ws.data_ptr(), self.ws_bytes, self._stream())
+        return {"x": gx, "w": gw, "wb": gwb, "bias": gb}
+
+
+def pointwise(x, w1, b1=None, w2=None, b2=None, out=None):
+    """Lift (w2 None) or projection head on a torch field [B, Cin, *grid]."""
+    import torch
+    batch, cin = x.shape[0], x.shape[1]
+    npts = x[0, 0].numel()
+    hidden = 0 if w2 is None else w1.shape[0]
+    cout = w1.shape[0] if w2 is None else w2.shape[0]
+    y = out if out is not None else torch.empty((batch, cout) + tuple(x.shape[2:]),
+                                                dtype=torch.float32, device=x.device)
+    fno_pointwise_fwd(batch, npts, cin, hidden, cout, x.data_ptr(), w1.data_ptr(), _ptr(b1),
+                      _ptr(w2), _ptr(b2), y.data_ptr(),
+                      torch.cuda.current_stream(x.device).cuda_stream)
+    return y
+
+
+def mse_grad(y, t, grad=None, loss=None, ws=None):
+    import torch
+    n = y.numel()
+    g = grad if grad is not None else torch.empty_like(y)
+    lo = loss if loss is not None else torch.empty(1, dtype=torch.float32, device=y.device)
+    nb = fno_mse_workspace_bytes(n)
+    w = ws if ws is not None else torch.empty(max(nb, 16), dtype=torch.uint8, device=y.device)
+    fno_mse_grad(n, y.data_ptr(), t.data_ptr(), g.data_ptr(), lo.data_ptr(), w.data_ptr(),
+                 w.numel(), torch.cuda.current_stream(y.device).cuda_stream)
+    return lo, g

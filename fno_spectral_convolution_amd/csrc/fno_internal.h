@@ -1,0 +1,104 @@
+// Internal declarations shared by the libfno host runtime and its kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "fno.h"
+
+namespace fno {
+
+constexpr int kMaxDims = 4;
+constexpr int kMaxChannels = 128;   // c_in, c_out limit of the epilogue/mix kernels
+constexpr int kMaxBatchTile = 16;   // batch entries held in registers by the mix kernels
+
+// Geometry of one plan, flattened for kernel arguments (passed by value).
+struct Geom {
+  int d;
+  int B, Cin, Cout;
+  int N[kMaxDims];
+  int M[kMaxDims];
+  int Na, Nb;          // the last two axes: rows (a = d-2) and contiguous (b = d-1)
+  int ma, mb;          // modes per corner on those axes
+  int64_t O;           // prod_{j < d-2} N_j (outer points; 1 in 2D)
+  int64_t P;           // points per field = prod N_j
+  int64_t K;           // retained modes per (batch, channel) = prod_{j<d-1} 2 m_j * m_b
+  int64_t Mprod;       // prod m_j (weights per corner per (i, o))
+  int ncorner;
+  float inv_ntot;      // 1 / P
+  bool bf16;           // spectral operands in bfloat16
+};
+
+// Device tables owned by a plan (all in one allocation).
+struct Tables {
+  const float2* root[kMaxDims];     // (cos, sin)(2 pi t / N_j), t < N_j  (fp32-rounded)
+  const float2* root_bf[kMaxDims];  // same values rounded to bfloat16 (stored as float)
+  const int32_t* mode_woff;         // [K]: offset of mode t in W for (i, o) = (0, 0)
+  const int32_t* woff_mode;         // [ncorner * Mprod]: retained mode of each W element
+};
+
+struct Workspace {
+  // Offsets (bytes) of the buffers inside the caller's workspace.
+  size_t plane_part;   // plane-transform partials [nch][B*C*O][2ma][mb] complex
+  size_t spec_a;       // complex ping buffer (largest intermediate spectrum)
+  size_t spec_b;       // complex pong buffer
+  size_t xhat;         // [B][Cin][K] complex (when the caller gives no save buffer)
+  size_t yhat;         // [B][Cout][K] complex
+  size_t red_part;     // bypass-gradient partials [nred][Cout*Cin + Cout] float
+  size_t total;
+};
+
+}  // namespace fno
+
+struct fno_plan {
+  fno_plan_desc desc;
+  fno::Geom g;
+  fno::Tables t;
+  void* table_mem;
+  int device;
+  int nch;              // chunks of the plane transform along axis a
+  int nred;             // work-groups of the bypass-gradient reduction
+  int64_t complex_max;  // largest intermediate spectrum (complex elements)
+  fno::Workspace ws;
+  size_t save_bytes;
+  size_t save_off_z;    // offset of z inside the save buffer
+};
+
+namespace fno {
+
+// ---- launchers (kernels_*.hip) -------------------------------------------------------------
+// Prologue of the plane transform: how a field value becomes a transform operand.
+enum PlaneIn { PLANE_X = 0, PLANE_TANH = 1, PLANE_GELU_GRAD = 2 };
+
+hipError_t launch_plane_fwd(const fno_plan* p, int plane_in, int chans, const float* in0,
+                            const float* in1, float2* out, hipStream_t s);
+hipError_t launch_outer_fwd(const fno_plan* p, int axis, int chans, const float2* in,
+                            int nparts, int64_t part_stride, float2* out, hipStream_t s);
+hipError_t launch_outer_inv(const fno_plan* p, int axis, int chans, const float2* in,
+                            float2* out, hipStream_t s);
+hipError_t launch_mix_fwd(const fno_plan* p, const float2* xhat, int nparts,
+                          int64_t part_stride, const float2* w, float2* yhat, hipStream_t s);
+hipError_t launch_mix_bwd_dx(const fno_plan* p, const float2* ghat, const float2* w,
+                             float2* ghx, hipStream_t s);
+hipError_t launch_mix_bwd_dw(const fno_plan* p, const float2* xhat, const float2* ghat,
+                             float2* dw, hipStream_t s);
+hipError_t launch_reduce_parts(const float2* in, int nparts, int64_t part_stride, int64_t n,
+                               float2* out, hipStream_t s);
+// Epilogue: last-axis inverse of T [B][C][lines][mb] plus the pointwise part.
+enum EpiMode { EPI_SPECTRAL = 0, EPI_BLOCK = 1 };
+hipError_t launch_epilogue_fwd(const fno_plan* p, int mode, const float2* T, const float* x,
+                               const float* wb, const float* bias, float* y, float* zsave,
+                               hipStream_t s);
+hipError_t launch_epilogue_bwd(const fno_plan* p, int mode, const float2* Tg, const float* x,
+                               const float* wb, const float* gy, const float* z,
+                               float* grad_x, float* red_part, hipStream_t s);
+hipError_t launch_bypass_grad_finish(const fno_plan* p, const float* red_part, float* dwb,
+                                     float* dbias, hipStream_t s);
+hipError_t launch_pointwise(int64_t batch, int64_t npts, int cin, int hidden, int cout,
+                            const float* x, const float* w1, const float* b1, const float* w2,
+                            const float* b2, float* y, hipStream_t s);
+hipError_t launch_mse(int64_t n, const float* y, const float* t, float* g, float* loss,
+                      double* part, int nparts, hipStream_t s);
+
+}  // namespace fno

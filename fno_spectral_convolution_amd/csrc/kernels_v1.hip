@@ -1,0 +1,715 @@
+// Generic (any d = 2..4) kernels of the FNO spectral block: LDS-staged VALU versions.
+//
+// Every transform here is the truncated DFT of the block computed directly for the retained
+// modes only ("spectral convolution from FNO's linear-algebra form" -- model-parallel FNO
+// page, "Proposed method").  Twiddles come from per-axis root tables (cos, sin)(2 pi t / N)
+// built on the host in float64; the index k*p is reduced modulo N in integers.
+//
+// Mixed path (bf16 operands, fp32 accumulation -- mixed-precision neural-operator page,
+// "Tiivistelmä"): every operand of a transform or mix product (pre-activated input,
+// twiddle, spectrum value, weight) is rounded to bfloat16 (nearest-even) before the
+// multiply; products and sums are float32.
+#include "fno_internal.h"
+
+#include <math.h>
+
+namespace fno {
+
+__device__ __forceinline__ float bf16r(float v) {
+  uint32_t u = __float_as_uint(v);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return __uint_as_float(u & 0xffff0000u);
+}
+
+__device__ __forceinline__ float opnd(float v, bool bf) { return bf ? bf16r(v) : v; }
+
+__device__ __forceinline__ float gelu_f(float z) {
+  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+}
+
+__device__ __forceinline__ float gelu_grad_f(float z) {
+  const float cdf = 0.5f * (1.0f + erff(z * 0.70710678118654752f));
+  const float pdf = expf(-0.5f * z * z) * 0.39894228040143268f;
+  return cdf + z * pdf;
+}
+
+// array index of retained position s of an outer axis (N, m): s < m -> s, else N - 2m + s
+__device__ __forceinline__ int kidx(int s, int n, int m) { return s < m ? s : n - 2 * m + s; }
+
+// ------------------------------------------------------------------------------------------
+// Plane transform: rows [r_begin, r_end) of each [Na][Nb] plane -> partial spectrum
+// [2ma][mb] (complex).  Grid (planes, nch), 256 threads.
+constexpr int kPlaneThreads = 256;
+constexpr int kPlaneRB = 8;          // rows staged per step
+constexpr int kPlaneMaxAcc = 16;     // (2ma * mb) / 256 accumulators per thread
+
+template <int PIN>
+__global__ void __launch_bounds__(kPlaneThreads)
+k_plane_fwd(Geom g, const float2* __restrict__ root_b, const float2* __restrict__ root_a,
+            const float* __restrict__ in0, const float* __restrict__ in1,
+            float2* __restrict__ out, int64_t planes, int rows_per_chunk) {
+  extern __shared__ float smem[];
+  const int Na = g.Na, Nb = g.Nb, ma = g.ma, mb = g.mb;
+  float2* s_rb = reinterpret_cast<float2*>(smem);          // [Nb]
+  float2* s_ra = s_rb + Nb;                                 // [Na]
+  float2* s_R = s_ra + Na;                                  // [RB][mb]
+  float* s_x = reinterpret_cast<float*>(s_R + kPlaneRB * mb);  // [RB][Nb]
+  const int tid = threadIdx.x;
+  const int64_t plane = blockIdx.x;
+  const int chunk = blockIdx.y;
+  const bool bf = g.bf16;
+  for (int t = tid; t < Nb; t += kPlaneThreads) s_rb[t] = root_b[t];
+  for (int t = tid; t < Na; t += kPlaneThreads) s_ra[t] = root_a[t];
+  const int r_begin = chunk * rows_per_chunk;
+  const int r_end = min(Na, r_begin + rows_per_chunk);
+  const int nout = 2 * ma * mb;
+  float2 acc[kPlaneMaxAcc];
+#pragma unroll
+  for (int q = 0; q < kPlaneMaxAcc; ++q) acc[q] = make_float2(0.f, 0.f);
+  const int64_t base = plane * (int64_t)Na * Nb;
+  for (int r0 = r_begin; r0 < r_end; r0 += kPlaneRB) {
+    const int nr = min(kPlaneRB, r_end - r0);
+    __syncthreads();
+    for (int e = tid; e < nr * Nb; e += kPlaneThreads) {
+      const int64_t off = base + (int64_t)r0 * Nb + e;
+      float v = in0[off];
+      if (PIN == PLANE_TANH) v = tanhf(v);
+      if (PIN == PLANE_GELU_GRAD) v = v * gelu_grad_f(in1[off]);
+      s_x[e] = opnd(v, bf);
+    }
+    __syncthreads();
+    // last axis: R[r][k] = sum_c x[r][c] e^{-2 pi i k c / Nb}
+    for (int e = tid; e < nr * mb; e += kPlaneThreads) {
+      const int r = e / mb, k = e - r * mb;
+      const float* xr = s_x + r * Nb;
+      float re = 0.f, im = 0.f;
+      int idx = 0;
+      for (int c = 0; c < Nb; ++c) {
+        const float2 w = s_rb[idx];
+        const float xv = xr[c];
+        re += xv * w.x;
+        im -= xv * w.y;
+        idx += k;
+        if (idx >= Nb) idx -= Nb;
+      }
+      s_R[e] = make_float2(opnd(re, bf), opnd(im, bf));
+    }
+    __syncthreads();
+    // axis a: X[s][k] += sum_r R[r][k] e^{-2 pi i ka(s) row / Na}
+#pragma unroll
+    for (int q = 0; q < kPlaneMaxAcc; ++q) {
+      const int o = tid + q * kPlaneThreads;
+      if (o < nout) {
+        const int s = o / mb, k = o - s * mb;
+        const int ka = kidx(s, Na, ma);
+        float2 a = acc[q];
+        for (int r = 0; r < nr; ++r) {
+          const int row = r0 + r;
+          const float2 w = s_ra[(int)(((int64_t)ka * row) % Na)];
+          const float2 R = s_R[r * mb + k];
+          a.x += R.x * w.x + R.y * w.y;
+          a.y += R.y * w.x - R.x * w.y;
+        }
+        acc[q] = a;
+      }
+    }
+  }
+  float2* dst = out + ((int64_t)chunk * planes + plane) * nout;
+#pragma unroll
+  for (int q = 0; q < kPlaneMaxAcc; ++q) {
+    const int o = tid + q * kPlaneThreads;
+    if (o < nout) dst[o] = acc[q];
+  }
+}
+
+hipError_t launch_plane_fwd(const fno_plan* p, int plane_in, int chans, const float* in0,
+                            const float* in1, float2* out, hipStream_t s) {
+  const Geom& g = p->g;
+  const int64_t planes = (int64_t)g.B * chans * g.O;
+  const int rows = (g.Na + p->nch - 1) / p->nch;
+  dim3 grid((unsigned)planes, (unsigned)p->nch);
+  const size_t lds = sizeof(float2) * (g.Nb + g.Na + kPlaneRB * g.mb) +
+                     sizeof(float) * kPlaneRB * g.Nb;
+  const float2* rb = g.bf16 ? p->t.root_bf[g.d - 1] : p->t.root[g.d - 1];
+  const float2* ra = g.bf16 ? p->t.root_bf[g.d - 2] : p->t.root[g.d - 2];
+  switch (plane_in) {
+    case PLANE_X:
+      hipLaunchKernelGGL(k_plane_fwd<PLANE_X>, grid, dim3(kPlaneThreads), lds, s, g, rb, ra,
+                         in0, in1, out, planes, rows);
+      break;
+    case PLANE_TANH:
+      hipLaunchKernelGGL(k_plane_fwd<PLANE_TANH>, grid, dim3(kPlaneThreads), lds, s, g, rb, ra,
+                         in0, in1, out, planes, rows);
+      break;
+    default:
+      hipLaunchKernelGGL(k_plane_fwd<PLANE_GELU_GRAD>, grid, dim3(kPlaneThreads), lds, s, g, rb,
+                         ra, in0, in1, out, planes, rows);
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// Sum of `nparts` partial spectra (fixed order: deterministic).
+__global__ void k_reduce_parts(const float2* __restrict__ in, int nparts, int64_t stride,
+                               int64_t n, float2* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float2 a = in[i];
+  for (int q = 1; q < nparts; ++q) {
+    const float2 v = in[(int64_t)q * stride + i];
+    a.x += v.x;
+    a.y += v.y;
+  }
+  out[i] = a;
+}
+
+hipError_t launch_reduce_parts(const float2* in, int nparts, int64_t part_stride, int64_t n,
+                               float2* out, hipStream_t s) {
+  const int threads = 256;
+  hipLaunchKernelGGL(k_reduce_parts, dim3((unsigned)((n + threads - 1) / threads)),
+                     dim3(threads), 0, s, in, nparts, part_stride, n, out);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// Truncated DFT along one outer axis j: in [pre][Lin][post] -> out [pre][Lout][post].
+// Forward: Lin = N, Lout = 2m, out[s] = sum_p in[p] e^{-i 2 pi k(s) p / N}.
+// Inverse: Lin = 2m, Lout = N, out[p] = sum_s in[s] e^{+i 2 pi k(s) p / N}.
+template <bool INV>
+__global__ void k_outer(const float2* __restrict__ root, int N, int m, int64_t pre,
+                        int64_t post, const float2* __restrict__ in, float2* __restrict__ out,
+                        bool bf) {
+  const int Lin = INV ? 2 * m : N;
+  const int Lout = INV ? N : 2 * m;
+  const int64_t total = pre * Lout * post;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int64_t q = i % post;
+  const int64_t r = i / post;
+  const int lo = (int)(r % Lout);
+  const int64_t pr = r / Lout;
+  const float2* src = in + pr * Lin * post + q;
+  float re = 0.f, im = 0.f;
+  for (int li = 0; li < Lin; ++li) {
+    const int k = INV ? kidx(li, N, m) : kidx(lo, N, m);
+    const int p = INV ? lo : li;
+    const float2 w = root[(int)(((int64_t)k * p) % N)];
+    const float2 v = src[(int64_t)li * post];
+    const float vr = opnd(v.x, bf), vi = opnd(v.y, bf);
+    if (INV) {  // (vr + i vi)(c + i s)
+      re += vr * w.x - vi * w.y;
+      im += vi * w.x + vr * w.y;
+    } else {    // (vr + i vi)(c - i s)
+      re += vr * w.x + vi * w.y;
+      im += vi * w.x - vr * w.y;
+    }
+  }
+  out[i] = make_float2(re, im);
+}
+
+static void outer_shape(const fno_plan* p, int axis, int chans, bool inv, int64_t* pre,
+                        int64_t* post) {
+  const Geom& g = p->g;
+  int64_t a = (int64_t)g.B * chans;
+  for (int i = 0; i < axis; ++i) a *= g.N[i];
+  int64_t b = g.mb;
+  // forward transforms axes d-3..0 after the plane kernel: axes > axis are already 2m;
+  // inverse transforms axes 0..d-2: axes > axis are still 2m.
+  for (int i = axis + 1; i <= g.d - 2; ++i) b *= 2 * g.M[i];
+  (void)inv;
+  *pre = a;
+  *post = b;
+}
+
+hipError_t launch_outer_fwd(const fno_plan* p, int axis, int chans, const float2* in,
+                            int nparts, int64_t part_stride, float2* out, hipStream_t s) {
+  (void)nparts;
+  (void)part_stride;
+  const Geom& g = p->g;
+  int64_t pre, post;
+  outer_shape(p, axis, chans, false, &pre, &post);
+  const int64_t total = pre * 2 * g.M[axis] * post;
+  const float2* root = g.bf16 ? p->t.root_bf[axis] : p->t.root[axis];
+  hipLaunchKernelGGL(k_outer<false>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                     root, g.N[axis], g.M[axis], pre, post, in, out, g.bf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_outer_inv(const fno_plan* p, int axis, int chans, const float2* in,
+                            float2* out, hipStream_t s) {
+  const Geom& g = p->g;
+  int64_t pre, post;
+  outer_shape(p, axis, chans, true, &pre, &post);
+  const int64_t total = pre * (int64_t)g.N[axis] * post;
+  const float2* root = g.bf16 ? p->t.root_bf[axis] : p->t.root[axis];
+  hipLaunchKernelGGL(k_outer<true>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                     root, g.N[axis], g.M[axis], pre, post, in, out, g.bf16);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// Channel mix.  Mode t of [B][C][K]; W element (c, i, o, kappa) at
+// mode_woff[t] + (i * Cout + o) * Mprod.
+__global__ void k_mix_fwd(Geom g, const int32_t* __restrict__ mode_woff,
+                          const float2* __restrict__ xhat, const float2* __restrict__ w,
+                          float2* __restrict__ yhat) {
+  const int64_t K = g.K;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)g.Cout * K) return;
+  const int o = (int)(i / K);
+  const int64_t t = i - (int64_t)o * K;
+  const int64_t wbase = mode_woff[t] + (int64_t)o * g.Mprod;
+  const int64_t wstride = (int64_t)g.Cout * g.Mprod;
+  const bool bf = g.bf16;
+  for (int b0 = 0; b0 < g.B; b0 += kMaxBatchTile) {
+    const int nb = min(kMaxBatchTile, g.B - b0);
+    float2 acc[kMaxBatchTile];
+#pragma unroll
+    for (int b = 0; b < kMaxBatchTile; ++b) acc[b] = make_float2(0.f, 0.f);
+    for (int ci = 0; ci < g.Cin; ++ci) {
+      const float2 wv = w[wbase + ci * wstride];
+      const float wr = opnd(wv.x, bf), wi = opnd(wv.y, bf);
+#pragma unroll
+      for (int b = 0; b < kMaxBatchTile; ++b) {
+        if (b < nb) {
+          const float2 xv = xhat[((int64_t)(b0 + b) * g.Cin + ci) * K + t];
+          const float xr = opnd(xv.x, bf), xi = opnd(xv.y, bf);
+          acc[b].x += xr * wr - xi * wi;
+          acc[b].y += xr * wi + xi * wr;
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kMaxBatchTile; ++b)
+      if (b < nb) yhat[((int64_t)(b0 + b) * g.Cout + o) * K + t] = acc[b];
+  }
+}
+
+hipError_t launch_mix_fwd(const fno_plan* p, const float2* xhat, int nparts,
+                          int64_t part_stride, const float2* w, float2* yhat, hipStream_t s) {
+  (void)nparts;
+  (void)part_stride;
+  const Geom& g = p->g;
+  const int64_t total = (int64_t)g.Cout * g.K;
+  hipLaunchKernelGGL(k_mix_fwd, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, g,
+                     p->t.mode_woff, xhat, w, yhat);
+  return hipGetLastError();
+}
+
+// ghat scale of the adjoint inverse: gamma(k_last) / Ntot
+__device__ __forceinline__ float adj_scale(const Geom& g, int64_t t) {
+  const int kb = (int)(t % g.mb);
+  const bool one = (kb == 0) || (2 * kb == g.Nb);
+  return (one ? 1.0f : 2.0f) * g.inv_ntot;
+}
+
+__global__ void k_mix_bwd_dx(Geom g, const int32_t* __restrict__ mode_woff,
+                             const float2* __restrict__ ghat, const float2* __restrict__ w,
+                             float2* __restrict__ ghx) {
+  const int64_t K = g.K;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)g.Cin * K) return;
+  const int ci = (int)(i / K);
+  const int64_t t = i - (int64_t)ci * K;
+  const int64_t wbase = mode_woff[t] + (int64_t)ci * g.Cout * g.Mprod;
+  const float sc = adj_scale(g, t);
+  const bool bf = g.bf16;
+  for (int b0 = 0; b0 < g.B; b0 += kMaxBatchTile) {
+    const int nb = min(kMaxBatchTile, g.B - b0);
+    float2 acc[kMaxBatchTile];
+#pragma unroll
+    for (int b = 0; b < kMaxBatchTile; ++b) acc[b] = make_float2(0.f, 0.f);
+    for (int o = 0; o < g.Cout; ++o) {
+      const float2 wv = w[wbase + (int64_t)o * g.Mprod];
+      const float wr = opnd(wv.x, bf), wi = opnd(wv.y, bf);
+#pragma unroll
+      for (int b = 0; b < kMaxBatchTile; ++b) {
+        if (b < nb) {
+          const float2 gv = ghat[((int64_t)(b0 + b) * g.Cout + o) * K + t];
+          const float gr = opnd(gv.x * sc, bf), gi = opnd(gv.y * sc, bf);
+          // (gr + i gi) * conj(wr + i wi)
+          acc[b].x += gr * wr + gi * wi;
+          acc[b].y += gi * wr - gr * wi;
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kMaxBatchTile; ++b)
+      if (b < nb) ghx[((int64_t)(b0 + b) * g.Cin + ci) * K + t] = acc[b];
+  }
+}
+
+hipError_t launch_mix_bwd_dx(const fno_plan* p, const float2* ghat, const float2* w,
+                             float2* ghx, hipStream_t s) {
+  const Geom& g = p->g;
+  const int64_t total = (int64_t)g.Cin * g.K;
+  hipLaunchKernelGGL(k_mix_bwd_dx, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, g,
+                     p->t.mode_woff, ghat, w, ghx);
+  return hipGetLastError();
+}
+
+__global__ void k_mix_bwd_dw(Geom g, const int32_t* __restrict__ woff_mode,
+                             const float2* __restrict__ xhat, const float2* __restrict__ ghat,
+                             float2* __restrict__ dw) {
+  const int64_t K = g.K;
+  const int64_t total = (int64_t)g.ncorner * g.Cin * g.Cout * g.Mprod;
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= total) return;
+  const int64_t kap = e % g.Mprod;
+  int64_t r = e / g.Mprod;
+  const int o = (int)(r % g.Cout);
+  r /= g.Cout;
+  const int ci = (int)(r % g.Cin);
+  const int c = (int)(r / g.Cin);
+  const int64_t t = woff_mode[(int64_t)c * g.Mprod + kap];
+  const float sc = adj_scale(g, t);
+  const bool bf = g.bf16;
+  float re = 0.f, im = 0.f;
+  for (int b = 0; b < g.B; ++b) {
+    const float2 xv = xhat[((int64_t)b * g.Cin + ci) * K + t];
+    const float2 gv = ghat[((int64_t)b * g.Cout + o) * K + t];
+    const float xr = opnd(xv.x, bf), xi = opnd(xv.y, bf);
+    const float gr = opnd(gv.x * sc, bf), gi = opnd(gv.y * sc, bf);
+    // conj(x) * g
+    re += xr * gr + xi * gi;
+    im += xr * gi - xi * gr;
+  }
+  dw[e] = make_float2(re, im);
+}
+
+hipError_t launch_mix_bwd_dw(const fno_plan* p, const float2* xhat, const float2* ghat,
+                             float2* dw, hipStream_t s) {
+  const Geom& g = p->g;
+  const int64_t total = (int64_t)g.ncorner * g.Cin * g.Cout * g.Mprod;
+  hipLaunchKernelGGL(k_mix_bwd_dw, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, g,
+                     p->t.woff_mode, xhat, ghat, dw);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// Forward epilogue: y_spec from T [B][C][lines][mb] by the last-axis inverse (gamma/Ntot),
+// then (EPI_BLOCK) + Wb x + bias and GELU.  One thread per point, 256 points per group.
+constexpr int kEpiThreads = 128;
+
+__global__ void __launch_bounds__(kEpiThreads)
+k_epilogue_fwd(Geom g, int mode, bool gelu, const float2* __restrict__ root_b,
+               const float2* __restrict__ T, const float* __restrict__ x,
+               const float* __restrict__ wb, const float* __restrict__ bias,
+               float* __restrict__ y, float* __restrict__ zsave) {
+  extern __shared__ float smem[];
+  const int Cin = g.Cin, Cout = g.Cout, Nb = g.Nb, mb = g.mb;
+  float2* s_rb = reinterpret_cast<float2*>(smem);            // [Nb]
+  float* s_wb = reinterpret_cast<float*>(s_rb + Nb);         // [Cout][Cin]
+  float* s_bias = s_wb + Cout * Cin;                         // [Cout]
+  float* s_x = s_bias + Cout;                                // [Cin][256]
+  const int tid = threadIdx.x;
+  const int b = blockIdx.y;
+  const int64_t P = g.P;
+  const int64_t p = (int64_t)blockIdx.x * kEpiThreads + tid;
+  const bool block = (mode == EPI_BLOCK);
+  for (int t = tid; t < Nb; t += kEpiThreads) s_rb[t] = root_b[t];
+  if (block) {
+    for (int t = tid; t < Cout * Cin; t += kEpiThreads) s_wb[t] = wb[t];
+    for (int t = tid; t < Cout; t += kEpiThreads) s_bias[t] = bias ? bias[t] : 0.f;
+    for (int ci = 0; ci < Cin; ++ci)
+      s_x[ci * kEpiThreads + tid] = (p < P) ? x[((int64_t)b * Cin + ci) * P + p] : 0.f;
+  }
+  __syncthreads();
+  if (p >= P) return;
+  const int64_t line = p / Nb;
+  const int pb = (int)(p - line * Nb);
+  const int64_t lines = P / Nb;
+  const bool bf = g.bf16;
+  for (int o = 0; o < Cout; ++o) {
+    const float2* tr = T + (((int64_t)b * Cout + o) * lines + line) * mb;
+    float ys = 0.f;
+    int idx = 0;
+    for (int k = 0; k < mb; ++k) {
+      const float2 tv = tr[k];
+      const float2 w = s_rb[idx];
+      const float gk = (k == 0 || 2 * k == Nb) ? 1.f : 2.f;
+      ys += gk * (opnd(tv.x, bf) * w.x - opnd(tv.y, bf) * w.y);
+      idx += pb;
+      if (idx >= Nb) idx -= Nb;
+    }
+    float z = ys * g.inv_ntot;
+    if (block) {
+      float acc = s_bias[o];
+      const float* wr = s_wb + o * Cin;
+      for (int ci = 0; ci < Cin; ++ci) acc += wr[ci] * s_x[ci * kEpiThreads + tid];
+      z += acc;
+    }
+    const int64_t off = ((int64_t)b * Cout + o) * P + p;
+    if (zsave) zsave[off] = z;
+    y[off] = (block && gelu) ? gelu_f(z) : z;
+  }
+}
+
+hipError_t launch_epilogue_fwd(const fno_plan* p, int mode, const float2* T, const float* x,
+                               const float* wb, const float* bias, float* y, float* zsave,
+                               hipStream_t s) {
+  const Geom& g = p->g;
+  const size_t lds = sizeof(float2) * g.Nb +
+                     sizeof(float) * ((size_t)g.Cout * g.Cin + g.Cout +
+                                      (mode == EPI_BLOCK ? (size_t)g.Cin * kEpiThreads : 0));
+  dim3 grid((unsigned)((g.P + kEpiThreads - 1) / kEpiThreads), (unsigned)g.B);
+  const bool gelu = (p->desc.flags & FNO_FLAG_GELU) != 0;
+  const float2* rb = g.bf16 ? p->t.root_bf[g.d - 1] : p->t.root[g.d - 1];
+  hipLaunchKernelGGL(k_epilogue_fwd, grid, dim3(kEpiThreads), lds, s, g, mode, gelu, rb, T, x,
+                     wb, (p->desc.flags & FNO_FLAG_BIAS) ? bias : nullptr, y, zsave);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// Backward epilogue.  grad_x[i] = sum_o Wb[o,i] g_z[o] (EPI_BLOCK) + s(x_i) gxs_i with
+// gxs from Tg [B][Cin][lines][mb] by the unit-scale last-axis inverse; per-group partial
+// sums of g_z x^T and g_z for the bypass gradients.  64 points per tile, one wave.
+constexpr int kEbThreads = 64;
+constexpr int kEbPairs = (64 * 64 + 64 + kEbThreads - 1) / kEbThreads;
+
+__global__ void __launch_bounds__(kEbThreads)
+k_epilogue_bwd(Geom g, int mode, bool gelu, bool tanh_pre, const float2* __restrict__ root_b,
+               const float2* __restrict__ Tg, const float* __restrict__ x,
+               const float* __restrict__ wb, const float* __restrict__ gy,
+               const float* __restrict__ z, float* __restrict__ grad_x,
+               float* __restrict__ red_part, int64_t tiles_per_group) {
+  extern __shared__ float smem[];
+  const int Cin = g.Cin, Cout = g.Cout, Nb = g.Nb, mb = g.mb;
+  float2* s_rb = reinterpret_cast<float2*>(smem);      // [Nb]
+  float* s_wb = reinterpret_cast<float*>(s_rb + Nb);   // [Cout][Cin]
+  float* s_gz = s_wb + Cout * Cin;                     // [Cout][128]
+  float* s_x = s_gz + Cout * kEbThreads;               // [Cin][128]
+  const int tid = threadIdx.x;
+  const int b = blockIdx.y;
+  const int64_t P = g.P;
+  const bool block = (mode == EPI_BLOCK);
+  const bool bf = g.bf16;
+  for (int t = tid; t < Nb; t += kEbThreads) s_rb[t] = root_b[t];
+  if (block)
+    for (int t = tid; t < Cout * Cin; t += kEbThreads) s_wb[t] = wb[t];
+  const int npair = Cout * Cin + Cout;
+  // per-thread partial sums of the bypass gradients: pairs tid, tid+128, ...
+  float pacc[kEbPairs];
+  const int my_pairs = block ? (npair + kEbThreads - 1) / kEbThreads : 0;
+#pragma unroll
+  for (int q = 0; q < kEbPairs; ++q) pacc[q] = 0.f;
+  const int64_t lines = P / Nb;
+  const int64_t t_begin = (int64_t)blockIdx.x * tiles_per_group;
+  const int64_t t_end = min((P + kEbThreads - 1) / kEbThreads, t_begin + tiles_per_group);
+  for (int64_t tile = t_begin; tile < t_end; ++tile) {
+    const int64_t p = tile * kEbThreads + tid;
+    const bool live = p < P;
+    __syncthreads();
+    if (block) {
+      for (int o = 0; o < Cout; ++o) {
+        float v = 0.f;
+        if (live) {
+          const int64_t off = ((int64_t)b * Cout + o) * P + p;
+          v = gy[off];
+          if (gelu) v *= gelu_grad_f(z[off]);
+        }
+        s_gz[o * kEbThreads + tid] = v;
+      }
+      for (int ci = 0; ci < Cin; ++ci)
+        s_x[ci * kEbThreads + tid] = live ? x[((int64_t)b * Cin + ci) * P + p] : 0.f;
+    }
+    __syncthreads();
+    if (live && grad_x) {
+      const int64_t line = p / Nb;
+      const int pb = (int)(p - line * Nb);
+      for (int ci = 0; ci < Cin; ++ci) {
+        const float2* tr = Tg + (((int64_t)b * Cin + ci) * lines + line) * mb;
+        float gs = 0.f;
+        int idx = 0;
+        for (int k = 0; k < mb; ++k) {
+          const float2 tv = tr[k];
+          const float2 w = s_rb[idx];
+          gs += opnd(tv.x, bf) * w.x - opnd(tv.y, bf) * w.y;
+          idx += pb;
+          if (idx >= Nb) idx -= Nb;
+        }
+        const int64_t off = ((int64_t)b * Cin + ci) * P + p;
+        if (tanh_pre) {
+          const float xv = block ? s_x[ci * kEbThreads + tid] : x[off];
+          const float th = tanhf(xv);
+          gs *= (1.f - th * th);
+        }
+        if (block) {
+          float acc = 0.f;
+          for (int o = 0; o < Cout; ++o) acc += s_wb[o * Cin + ci] * s_gz[o * kEbThreads + tid];
+          gs += acc;
+        }
+        grad_x[off] = gs;
+      }
+    }
+    if (block) {
+      for (int q = 0; q < my_pairs; ++q) {
+        const int pr = tid + q * kEbThreads;
+        if (pr < npair) {
+          float a = 0.f;
+          if (pr < Cout * Cin) {
+            const int o = pr / Cin, ci = pr - o * Cin;
+            const float* gz = s_gz + o * kEbThreads;
+            const float* xv = s_x + ci * kEbThreads;
+            for (int e = 0; e < kEbThreads; ++e) a += gz[e] * xv[e];
+          } else {
+            const float* gz = s_gz + (pr - Cout * Cin) * kEbThreads;
+            for (int e = 0; e < kEbThreads; ++e) a += gz[e];
+          }
+          pacc[q] += a;
+        }
+      }
+    }
+  }
+  if (block && red_part) {
+    float* dst = red_part + ((int64_t)b * gridDim.x + blockIdx.x) * npair;
+    for (int q = 0; q < my_pairs; ++q) {
+      const int pr = tid + q * kEbThreads;
+      if (pr < npair) dst[pr] = pacc[q];
+    }
+  }
+}
+
+hipError_t launch_epilogue_bwd(const fno_plan* p, int mode, const float2* Tg, const float* x,
+                               const float* wb, const float* gy, const float* z,
+                               float* grad_x, float* red_part, hipStream_t s) {
+  const Geom& g = p->g;
+  const int64_t tiles = (g.P + kEbThreads - 1) / kEbThreads;
+  const int groups = p->nred / g.B;
+  const int64_t tpg = (tiles + groups - 1) / groups;
+  const size_t lds = sizeof(float2) * g.Nb +
+                     sizeof(float) * ((size_t)g.Cout * g.Cin +
+                                      (mode == EPI_BLOCK ? (size_t)(g.Cout + g.Cin) * kEbThreads
+                                                         : 0));
+  const bool gelu = (p->desc.flags & FNO_FLAG_GELU) != 0;
+  const bool tanh_pre = (p->desc.flags & FNO_FLAG_TANH_PREACT) != 0;
+  const float2* rb = g.bf16 ? p->t.root_bf[g.d - 1] : p->t.root[g.d - 1];
+  hipLaunchKernelGGL(k_epilogue_bwd, dim3((unsigned)groups, (unsigned)g.B), dim3(kEbThreads),
+                     lds, s, g, mode, gelu, tanh_pre, rb, Tg, x, wb, gy, z, grad_x, red_part,
+                     tpg);
+  return hipGetLastError();
+}
+
+__global__ void k_bypass_finish(const float* __restrict__ part, int nparts, int cout, int cin,
+                                float* __restrict__ dwb, float* __restrict__ dbias) {
+  const int npair = cout * cin + cout;
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= npair) return;
+  float a = 0.f;
+  for (int q = 0; q < nparts; ++q) a += part[(int64_t)q * npair + e];
+  if (e < cout * cin) {
+    if (dwb) dwb[e] = a;
+  } else if (dbias) {
+    dbias[e - cout * cin] = a;
+  }
+}
+
+hipError_t launch_bypass_grad_finish(const fno_plan* p, const float* red_part, float* dwb,
+                                     float* dbias, hipStream_t s) {
+  const Geom& g = p->g;
+  const int npair = g.Cout * g.Cin + g.Cout;
+  hipLaunchKernelGGL(k_bypass_finish, dim3((npair + 255) / 256), dim3(256), 0, s, red_part,
+                     p->nred, g.Cout, g.Cin, dwb, dbias);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// Pointwise lift / projection.  One thread per point; inputs staged in LDS.
+constexpr int kPwThreads = 256;
+
+__global__ void __launch_bounds__(kPwThreads)
+k_pointwise(int64_t npts, int cin, int hidden, int cout, const float* __restrict__ x,
+            const float* __restrict__ w1, const float* __restrict__ b1,
+            const float* __restrict__ w2, const float* __restrict__ b2, float* __restrict__ y) {
+  extern __shared__ float smem[];
+  float* s_x = smem;  // [cin][256]
+  const int tid = threadIdx.x;
+  const int b = blockIdx.y;
+  const int64_t p = (int64_t)blockIdx.x * kPwThreads + tid;
+  for (int ci = 0; ci < cin; ++ci)
+    s_x[ci * kPwThreads + tid] = (p < npts) ? x[((int64_t)b * cin + ci) * npts + p] : 0.f;
+  __syncthreads();
+  if (p >= npts) return;
+  const float* xv = s_x + tid;
+  if (hidden == 0) {
+    for (int o = 0; o < cout; ++o) {
+      float a = b1 ? b1[o] : 0.f;
+      for (int ci = 0; ci < cin; ++ci) a += w1[o * cin + ci] * xv[ci * kPwThreads];
+      y[((int64_t)b * cout + o) * npts + p] = a;
+    }
+    return;
+  }
+  for (int o0 = 0; o0 < cout; o0 += 8) {
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = (o0 + q < cout && b2) ? b2[o0 + q] : 0.f;
+    for (int h = 0; h < hidden; ++h) {
+      float a = b1 ? b1[h] : 0.f;
+      for (int ci = 0; ci < cin; ++ci) a += w1[h * cin + ci] * xv[ci * kPwThreads];
+      const float act = gelu_f(a);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (o0 + q < cout) acc[q] += w2[(o0 + q) * hidden + h] * act;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (o0 + q < cout) y[((int64_t)b * cout + o0 + q) * npts + p] = acc[q];
+  }
+}
+
+hipError_t launch_pointwise(int64_t batch, int64_t npts, int cin, int hidden, int cout,
+                            const float* x, const float* w1, const float* b1, const float* w2,
+                            const float* b2, float* y, hipStream_t s) {
+  dim3 grid((unsigned)((npts + kPwThreads - 1) / kPwThreads), (unsigned)batch);
+  hipLaunchKernelGGL(k_pointwise, grid, dim3(kPwThreads), sizeof(float) * cin * kPwThreads, s,
+                     npts, cin, hidden, cout, x, w1, b1, w2, b2, y);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// MSE: g = 2 (y - t) / n; per-group partial sums in double, then one fixed-order finish.
+__global__ void k_mse_part(int64_t n, const float* __restrict__ y, const float* __restrict__ t,
+                           float* __restrict__ g, double* __restrict__ part) {
+  __shared__ double s_red[256];
+  const int tid = threadIdx.x;
+  const float sc = (float)(2.0 / (double)n);
+  double a = 0.0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + tid; i < n; i += (int64_t)gridDim.x * 256) {
+    const float d = y[i] - t[i];
+    g[i] = sc * d;
+    a += (double)d * (double)d;
+  }
+  s_red[tid] = a;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) s_red[tid] += s_red[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) part[blockIdx.x] = s_red[0];
+}
+
+__global__ void k_mse_finish(int64_t n, int nparts, const double* __restrict__ part,
+                             float* __restrict__ loss) {
+  __shared__ double s_red[256];
+  const int tid = threadIdx.x;
+  double a = 0.0;
+  for (int i = tid; i < nparts; i += 256) a += part[i];
+  s_red[tid] = a;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) s_red[tid] += s_red[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) *loss = (float)(s_red[0] / (double)n);
+}
+
+hipError_t launch_mse(int64_t n, const float* y, const float* t, float* g, float* loss,
+                      double* part, int nparts, hipStream_t s) {
+  hipLaunchKernelGGL(k_mse_part, dim3(nparts), dim3(256), 0, s, n, y, t, g, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !loss) return e;
+  hipLaunchKernelGGL(k_mse_finish, dim3(1), dim3(256), 0, s, n, nparts, part, loss);
+  return hipGetLastError();
+}
+
+}  // namespace fno

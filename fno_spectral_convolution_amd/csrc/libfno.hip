@@ -1,0 +1,592 @@
+// libfno host runtime: descriptor validation, float64 table build, workspace layout and the
+// launch sequence of each entry point.  All device work is enqueued on the caller's stream;
+// nothing here allocates device memory except fno_plan_create (its tables, once).
+#include "fno_internal.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+#include <string>
+#include <vector>
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fno_status fail(fno_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+fno_status fail(fno_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+fno_status hip_fail(hipError_t e, const char* what) {
+  return fail(FNO_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define FNO_HIP(call, what)                       \
+  do {                                            \
+    hipError_t e_ = (call);                       \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+float round_bf16(float v) {
+  uint32_t u;
+  memcpy(&u, &v, 4);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  u &= 0xffff0000u;
+  float r;
+  memcpy(&r, &u, 4);
+  return r;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fno_status_string(fno_status s) {
+  switch (s) {
+    case FNO_OK: return "FNO_OK";
+    case FNO_ERR_INVALID_ARGUMENT: return "FNO_ERR_INVALID_ARGUMENT";
+    case FNO_ERR_UNSUPPORTED: return "FNO_ERR_UNSUPPORTED";
+    case FNO_ERR_HIP: return "FNO_ERR_HIP";
+    case FNO_ERR_OUT_OF_MEMORY: return "FNO_ERR_OUT_OF_MEMORY";
+    case FNO_ERR_INTERNAL: return "FNO_ERR_INTERNAL";
+  }
+  return "FNO_ERR_UNKNOWN";
+}
+
+const char* fno_last_error_message(void) { return g_last_error.c_str(); }
+
+fno_status fno_plan_validate(const fno_plan_desc* d) {
+  if (!d) return fail(FNO_ERR_INVALID_ARGUMENT, "descriptor is NULL");
+  if (d->ndim < 2 || d->ndim > 4)
+    return fail(FNO_ERR_INVALID_ARGUMENT, "ndim %d not in {2,3,4}", d->ndim);
+  if (d->reserved != 0) return fail(FNO_ERR_INVALID_ARGUMENT, "reserved field must be 0");
+  if (d->flags & ~(uint32_t)(FNO_FLAG_TANH_PREACT | FNO_FLAG_GELU | FNO_FLAG_BIAS))
+    return fail(FNO_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", d->flags);
+  if (d->spectral_dtype != FNO_DTYPE_F32 && d->spectral_dtype != FNO_DTYPE_BF16 &&
+      d->spectral_dtype != FNO_DTYPE_F16)
+    return fail(FNO_ERR_INVALID_ARGUMENT, "unknown spectral dtype %d", d->spectral_dtype);
+  if (d->batch < 1 || d->c_in < 1 || d->c_out < 1)
+    return fail(FNO_ERR_INVALID_ARGUMENT, "batch/c_in/c_out must be >= 1");
+  const int nd = d->ndim;
+  for (int j = 0; j < 4; ++j) {
+    if (j >= nd) {
+      if (d->n[j] != 0 || d->modes[j] != 0)
+        return fail(FNO_ERR_INVALID_ARGUMENT, "n[%d]/modes[%d] must be 0 beyond ndim", j, j);
+      continue;
+    }
+    if (d->n[j] < 2) return fail(FNO_ERR_INVALID_ARGUMENT, "n[%d] = %lld < 2", j, (long long)d->n[j]);
+    const int64_t mmax = (j == nd - 1) ? d->n[j] / 2 + 1 : d->n[j] / 2;
+    if (d->modes[j] < 1 || d->modes[j] > mmax)
+      return fail(FNO_ERR_INVALID_ARGUMENT, "modes[%d] = %lld outside [1, %lld]", j,
+                  (long long)d->modes[j], (long long)mmax);
+  }
+  // limits of the kernels (valid FNO shapes beyond them are UNSUPPORTED)
+  if (d->spectral_dtype == FNO_DTYPE_F16)
+    return fail(FNO_ERR_UNSUPPORTED, "fp16 spectral path not implemented");
+  if (d->c_in > 64 || d->c_out > 64)
+    return fail(FNO_ERR_UNSUPPORTED, "channels > 64 not implemented");
+  const int64_t na = d->n[nd - 2], nb = d->n[nd - 1];
+  const int64_t ma = d->modes[nd - 2], mb = d->modes[nd - 1];
+  if (nb > 4096 || na > 65536)
+    return fail(FNO_ERR_UNSUPPORTED, "last two axes (%lld, %lld) too long", (long long)na,
+                (long long)nb);
+  if (2 * ma * mb > 4096)
+    return fail(FNO_ERR_UNSUPPORTED, "2*m_a*m_b = %lld > 4096", (long long)(2 * ma * mb));
+  // LDS of the plane transform (root tables, 8 staged rows and their spectra)
+  const int64_t lds_plane = 8 * (na + nb + 8 * mb) + 4 * 8 * nb;
+  if (lds_plane > 65536)
+    return fail(FNO_ERR_UNSUPPORTED, "plane transform needs %lld bytes of LDS", (long long)lds_plane);
+  const int64_t lds_epi = 8 * nb + 4 * (d->c_in * d->c_out + d->c_out + 128 * d->c_in);
+  if (lds_epi > 65536)
+    return fail(FNO_ERR_UNSUPPORTED, "epilogue needs %lld bytes of LDS", (long long)lds_epi);
+  double elems = (double)d->batch * (double)(d->c_in > d->c_out ? d->c_in : d->c_out);
+  double wel = (double)(1 << (nd - 1)) * d->c_in * d->c_out;
+  for (int j = 0; j < nd; ++j) {
+    elems *= (double)d->n[j];
+    wel *= (double)d->modes[j];
+  }
+  if (elems >= 2147483648.0) return fail(FNO_ERR_UNSUPPORTED, "field has >= 2^31 elements");
+  if (wel >= 2147483648.0) return fail(FNO_ERR_UNSUPPORTED, "weights have >= 2^31 elements");
+  return FNO_OK;
+}
+
+fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out) {
+  if (!out) return fail(FNO_ERR_INVALID_ARGUMENT, "out is NULL");
+  *out = nullptr;
+  fno_status st = fno_plan_validate(desc);
+  if (st != FNO_OK) return st;
+  fno_plan* p = new (std::nothrow) fno_plan();
+  if (!p) return fail(FNO_ERR_OUT_OF_MEMORY, "host allocation failed");
+  p->desc = *desc;
+  fno::Geom& g = p->g;
+  g.d = desc->ndim;
+  g.B = (int)desc->batch;
+  g.Cin = (int)desc->c_in;
+  g.Cout = (int)desc->c_out;
+  g.P = 1;
+  g.Mprod = 1;
+  g.K = 1;
+  for (int j = 0; j < fno::kMaxDims; ++j) {
+    g.N[j] = j < g.d ? (int)desc->n[j] : 0;
+    g.M[j] = j < g.d ? (int)desc->modes[j] : 0;
+  }
+  for (int j = 0; j < g.d; ++j) {
+    g.P *= g.N[j];
+    g.Mprod *= g.M[j];
+    g.K *= (j == g.d - 1) ? g.M[j] : 2 * g.M[j];
+  }
+  g.Na = g.N[g.d - 2];
+  g.Nb = g.N[g.d - 1];
+  g.ma = g.M[g.d - 2];
+  g.mb = g.M[g.d - 1];
+  g.O = 1;
+  for (int j = 0; j < g.d - 2; ++j) g.O *= g.N[j];
+  g.ncorner = 1 << (g.d - 1);
+  g.inv_ntot = (float)(1.0 / (double)g.P);
+  g.bf16 = desc->spectral_dtype == FNO_DTYPE_BF16;
+  const int cmax = g.Cin > g.Cout ? g.Cin : g.Cout;
+
+  // plane-transform chunking along axis a: enough groups to fill the chip
+  {
+    const int64_t planes = (int64_t)g.B * cmax * g.O;
+    int nch = (int)((2048 + planes - 1) / planes);
+    int maxch = g.Na / 8 > 0 ? g.Na / 8 : 1;
+    if (nch > maxch) nch = maxch;
+    if (nch < 1) nch = 1;
+    p->nch = nch;
+  }
+  {
+    const int64_t tiles = (g.P + 63) / 64;
+    int64_t gpb = 1024 / g.B;
+    if (gpb < 1) gpb = 1;
+    if (gpb > tiles) gpb = tiles;
+    p->nred = (int)(gpb * g.B);
+  }
+  // intermediate spectra: the largest is the fully expanded one before the epilogue
+  {
+    int64_t mx = 0;
+    for (int j = -1; j <= g.d - 2; ++j) {
+      int64_t v = (int64_t)g.B * cmax * g.mb;
+      for (int i = 0; i <= g.d - 2; ++i) v *= (i <= j) ? g.N[i] : 2 * g.M[i];
+      if (v > mx) mx = v;
+    }
+    p->complex_max = mx;
+  }
+  fno::Workspace& w = p->ws;
+  size_t off = 0;
+  const int64_t plane_out = (int64_t)g.B * cmax * g.O * 2 * g.ma * g.mb;
+  w.plane_part = off;
+  off += align_up(sizeof(float2) * (size_t)plane_out * p->nch);
+  w.spec_a = off;
+  off += align_up(sizeof(float2) * (size_t)p->complex_max);
+  w.spec_b = off;
+  off += align_up(sizeof(float2) * (size_t)p->complex_max);
+  w.xhat = off;
+  off += align_up(sizeof(float2) * (size_t)g.B * g.Cin * g.K);
+  w.yhat = off;
+  off += align_up(sizeof(float2) * (size_t)g.B * cmax * g.K);
+  w.red_part = off;
+  off += align_up(sizeof(float) * (size_t)p->nred * (g.Cout * g.Cin + g.Cout));
+  w.total = off;
+  p->save_off_z = align_up(sizeof(float2) * (size_t)g.B * g.Cin * g.K);
+  p->save_bytes = p->save_off_z +
+                  ((desc->flags & FNO_FLAG_GELU) ? align_up(sizeof(float) * (size_t)g.B *
+                                                            g.Cout * g.P)
+                                                 : 0);
+
+  // ---- tables, built in float64 on the host
+  std::vector<size_t> root_off(g.d), rootbf_off(g.d);
+  size_t toff = 0;
+  for (int j = 0; j < g.d; ++j) {
+    root_off[j] = toff;
+    toff += align_up(sizeof(float2) * g.N[j]);
+    rootbf_off[j] = toff;
+    toff += align_up(sizeof(float2) * g.N[j]);
+  }
+  const size_t woff_mode_elems = (size_t)g.ncorner * g.Mprod;
+  const size_t mode_woff_off = toff;
+  toff += align_up(sizeof(int32_t) * (size_t)g.K);
+  const size_t woff_mode_off = toff;
+  toff += align_up(sizeof(int32_t) * woff_mode_elems);
+  std::vector<unsigned char> host(toff, 0);
+  for (int j = 0; j < g.d; ++j) {
+    float2* r = reinterpret_cast<float2*>(host.data() + root_off[j]);
+    float2* rb = reinterpret_cast<float2*>(host.data() + rootbf_off[j]);
+    for (int t = 0; t < g.N[j]; ++t) {
+      const double ang = 2.0 * M_PI * (double)t / (double)g.N[j];
+      const float c = (float)cos(ang), s = (float)sin(ang);
+      r[t] = make_float2(c, s);
+      rb[t] = make_float2(round_bf16(c), round_bf16(s));
+    }
+  }
+  {
+    int32_t* mw = reinterpret_cast<int32_t*>(host.data() + mode_woff_off);
+    int32_t* wm = reinterpret_cast<int32_t*>(host.data() + woff_mode_off);
+    int dims[fno::kMaxDims];
+    for (int j = 0; j < g.d; ++j) dims[j] = (j == g.d - 1) ? g.M[j] : 2 * g.M[j];
+    for (int64_t t = 0; t < g.K; ++t) {
+      int64_t r = t;
+      int s[fno::kMaxDims];
+      for (int j = g.d - 1; j >= 0; --j) {
+        s[j] = (int)(r % dims[j]);
+        r /= dims[j];
+      }
+      int corner = 0;
+      int64_t kap = 0;
+      for (int j = 0; j < g.d; ++j) {
+        int kj = s[j];
+        if (j < g.d - 1 && kj >= g.M[j]) {
+          corner |= 1 << j;
+          kj -= g.M[j];
+        }
+        kap = kap * g.M[j] + kj;
+      }
+      mw[t] = (int32_t)((int64_t)corner * g.Cin * g.Cout * g.Mprod + kap);
+      wm[(int64_t)corner * g.Mprod + kap] = (int32_t)t;
+    }
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    delete p;
+    return hip_fail(e, "hipGetDevice");
+  }
+  p->device = dev;
+  void* mem = nullptr;
+  e = hipMalloc(&mem, toff);
+  if (e != hipSuccess) {
+    delete p;
+    return hip_fail(e, "hipMalloc(plan tables)");
+  }
+  e = hipMemcpy(mem, host.data(), toff, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(mem);
+    delete p;
+    return hip_fail(e, "hipMemcpy(plan tables)");
+  }
+  p->table_mem = mem;
+  unsigned char* base = static_cast<unsigned char*>(mem);
+  for (int j = 0; j < fno::kMaxDims; ++j) {
+    p->t.root[j] = j < g.d ? reinterpret_cast<const float2*>(base + root_off[j]) : nullptr;
+    p->t.root_bf[j] = j < g.d ? reinterpret_cast<const float2*>(base + rootbf_off[j]) : nullptr;
+  }
+  p->t.mode_woff = reinterpret_cast<const int32_t*>(base + mode_woff_off);
+  p->t.woff_mode = reinterpret_cast<const int32_t*>(base + woff_mode_off);
+  *out = p;
+  return FNO_OK;
+}
+
+fno_status fno_plan_destroy(fno_plan* p) {
+  if (!p) return FNO_OK;
+  hipError_t e = hipSuccess;
+  if (p->table_mem) e = hipFree(p->table_mem);
+  delete p;
+  if (e != hipSuccess) return hip_fail(e, "hipFree(plan tables)");
+  return FNO_OK;
+}
+
+fno_status fno_plan_query(const fno_plan* p, size_t* ws, size_t* save, size_t* wel) {
+  if (!p) return fail(FNO_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (ws) *ws = p->ws.total;
+  if (save) *save = p->save_bytes;
+  if (wel) *wel = (size_t)p->g.ncorner * p->g.Cin * p->g.Cout * p->g.Mprod;
+  return FNO_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+#define REQ(ptr, name)                                                       \
+  do {                                                                       \
+    if (!(ptr)) return fail(FNO_ERR_INVALID_ARGUMENT, "%s is NULL", name);   \
+    if (!aligned16(ptr))                                                     \
+      return fail(FNO_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+#define OPT(ptr, name)                                                       \
+  do {                                                                       \
+    if ((ptr) && !aligned16(ptr))                                            \
+      return fail(FNO_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+#define LAUNCH(call, what)                               \
+  do {                                                   \
+    hipError_t e_ = (call);                              \
+    if (e_ != hipSuccess) return hip_fail(e_, what);     \
+  } while (0)
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<unsigned char*>(base) + off);
+}
+
+// Forward transform of a field (channels `chans`) into the retained spectrum `dst`
+// [B][chans][K]:  plane transform of the last two axes, then the remaining outer axes.
+fno_status forward_transform(const fno_plan* p, int plane_in, int chans, const float* in0,
+                             const float* in1, float2* dst, void* ws, hipStream_t s) {
+  const fno::Geom& g = p->g;
+  float2* part = at<float2>(ws, p->ws.plane_part);
+  float2* ping = at<float2>(ws, p->ws.spec_a);
+  float2* pong = at<float2>(ws, p->ws.spec_b);
+  const int64_t plane_out = (int64_t)g.B * chans * g.O * 2 * g.ma * g.mb;
+  const bool more = g.d > 2;
+  float2* plane_dst = (p->nch == 1) ? (more ? ping : dst) : part;
+  LAUNCH(fno::launch_plane_fwd(p, plane_in, chans, in0, in1, plane_dst, s), "plane transform");
+  float2* cur = plane_dst;
+  if (p->nch > 1) {
+    float2* rd = more ? ping : dst;
+    LAUNCH(fno::launch_reduce_parts(part, p->nch, plane_out, plane_out, rd, s), "chunk reduce");
+    cur = rd;
+  }
+  for (int j = g.d - 3; j >= 0; --j) {
+    float2* nxt = (j == 0) ? dst : (cur == ping ? pong : ping);
+    LAUNCH(fno::launch_outer_fwd(p, j, chans, cur, 1, 0, nxt, s), "outer-axis transform");
+    cur = nxt;
+  }
+  return FNO_OK;
+}
+
+// Inverse transform of the outer axes 0..d-2 of a spectrum [B][chans][K] into
+// T [B][chans][lines][mb]; returns the buffer holding T.
+fno_status inverse_outer(const fno_plan* p, int chans, const float2* src, void* ws,
+                         hipStream_t s, const float2** T) {
+  const fno::Geom& g = p->g;
+  float2* ping = at<float2>(ws, p->ws.spec_a);
+  float2* pong = at<float2>(ws, p->ws.spec_b);
+  const float2* cur = src;
+  for (int j = 0; j <= g.d - 2; ++j) {
+    float2* nxt = (cur == ping) ? pong : ping;
+    LAUNCH(fno::launch_outer_inv(p, j, chans, cur, nxt, s), "inverse outer-axis transform");
+    cur = nxt;
+  }
+  *T = cur;
+  return FNO_OK;
+}
+
+fno_status check_ws(const fno_plan* p, void* ws, size_t ws_bytes) {
+  REQ(ws, "workspace");
+  if (ws_bytes < p->ws.total)
+    return fail(FNO_ERR_INVALID_ARGUMENT, "workspace %zu bytes < required %zu", ws_bytes,
+                p->ws.total);
+  return FNO_OK;
+}
+
+int pre_mode(const fno_plan* p) {
+  return (p->desc.flags & FNO_FLAG_TANH_PREACT) ? fno::PLANE_TANH : fno::PLANE_X;
+}
+
+}  // namespace
+
+extern "C" {
+
+fno_status fno_spectral_conv_fwd(const fno_plan* p, const float* x, const float* w,
+                                 float* y_spec, void* save, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  if (!p) return fail(FNO_ERR_INVALID_ARGUMENT, "plan is NULL");
+  REQ(x, "x");
+  REQ(w, "w");
+  REQ(y_spec, "y_spec");
+  OPT(save, "save");
+  fno_status st = check_ws(p, ws, ws_bytes);
+  if (st != FNO_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float2* xhat = save ? static_cast<float2*>(save) : at<float2>(ws, p->ws.xhat);
+  st = forward_transform(p, pre_mode(p), p->g.Cin, x, nullptr, xhat, ws, s);
+  if (st != FNO_OK) return st;
+  float2* yhat = at<float2>(ws, p->ws.yhat);
+  LAUNCH(fno::launch_mix_fwd(p, xhat, 1, 0, reinterpret_cast<const float2*>(w), yhat, s),
+         "channel mix");
+  const float2* T = nullptr;
+  st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T);
+  if (st != FNO_OK) return st;
+  LAUNCH(fno::launch_epilogue_fwd(p, fno::EPI_SPECTRAL, T, x, nullptr, nullptr, y_spec, nullptr,
+                                  s),
+         "epilogue");
+  return FNO_OK;
+}
+
+fno_status fno_block_fwd(const fno_plan* p, const float* x, const float* w, const float* wb,
+                         const float* bias, float* y, void* save, void* ws, size_t ws_bytes,
+                         void* stream) {
+  if (!p) return fail(FNO_ERR_INVALID_ARGUMENT, "plan is NULL");
+  REQ(x, "x");
+  REQ(w, "w");
+  REQ(wb, "w_bypass");
+  REQ(y, "y");
+  if (p->desc.flags & FNO_FLAG_BIAS) REQ(bias, "bias");
+  OPT(save, "save");
+  fno_status st = check_ws(p, ws, ws_bytes);
+  if (st != FNO_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float2* xhat = save ? static_cast<float2*>(save) : at<float2>(ws, p->ws.xhat);
+  st = forward_transform(p, pre_mode(p), p->g.Cin, x, nullptr, xhat, ws, s);
+  if (st != FNO_OK) return st;
+  float2* yhat = at<float2>(ws, p->ws.yhat);
+  LAUNCH(fno::launch_mix_fwd(p, xhat, 1, 0, reinterpret_cast<const float2*>(w), yhat, s),
+         "channel mix");
+  const float2* T = nullptr;
+  st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T);
+  if (st != FNO_OK) return st;
+  float* zsave = (save && (p->desc.flags & FNO_FLAG_GELU)) ? at<float>(save, p->save_off_z)
+                                                            : nullptr;
+  LAUNCH(fno::launch_epilogue_fwd(p, fno::EPI_BLOCK, T, x, wb, bias, y, zsave, s), "epilogue");
+  return FNO_OK;
+}
+
+fno_status fno_spectral_conv_bwd(const fno_plan* p, const float* x, const float* w,
+                                 const void* save, const float* gys, float* grad_x,
+                                 float* grad_w, void* ws, size_t ws_bytes, void* stream) {
+  if (!p) return fail(FNO_ERR_INVALID_ARGUMENT, "plan is NULL");
+  REQ(x, "x");
+  REQ(w, "w");
+  REQ(gys, "grad_y_spec");
+  OPT(save, "save");
+  OPT(grad_x, "grad_x");
+  OPT(grad_w, "grad_w");
+  fno_status st = check_ws(p, ws, ws_bytes);
+  if (st != FNO_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const fno::Geom& g = p->g;
+  float2* ghat = at<float2>(ws, p->ws.yhat);
+  if (grad_w) {
+    const float2* xhat = static_cast<const float2*>(save);
+    if (!xhat) {
+      float2* xh = at<float2>(ws, p->ws.xhat);
+      st = forward_transform(p, pre_mode(p), g.Cin, x, nullptr, xh, ws, s);
+      if (st != FNO_OK) return st;
+      xhat = xh;
+    }
+    st = forward_transform(p, fno::PLANE_X, g.Cout, gys, nullptr, ghat, ws, s);
+    if (st != FNO_OK) return st;
+    LAUNCH(fno::launch_mix_bwd_dw(p, xhat, ghat, reinterpret_cast<float2*>(grad_w), s),
+           "weight gradient");
+  } else {
+    st = forward_transform(p, fno::PLANE_X, g.Cout, gys, nullptr, ghat, ws, s);
+    if (st != FNO_OK) return st;
+  }
+  if (grad_x) {
+    float2* ghx = at<float2>(ws, p->ws.xhat);
+    LAUNCH(fno::launch_mix_bwd_dx(p, ghat, reinterpret_cast<const float2*>(w), ghx, s),
+           "input-gradient mix");
+    const float2* Tg = nullptr;
+    st = inverse_outer(p, g.Cin, ghx, ws, s, &Tg);
+    if (st != FNO_OK) return st;
+    LAUNCH(fno::launch_epilogue_bwd(p, fno::EPI_SPECTRAL, Tg, x, nullptr, nullptr, nullptr,
+                                    grad_x, nullptr, s),
+           "backward epilogue");
+  }
+  return FNO_OK;
+}
+
+fno_status fno_block_bwd(const fno_plan* p, const float* x, const float* w, const float* wb,
+                         const float* bias, const void* save, const float* gy, float* grad_x,
+                         float* grad_w, float* grad_wb, float* grad_bias, void* ws,
+                         size_t ws_bytes, void* stream) {
+  (void)bias;
+  if (!p) return fail(FNO_ERR_INVALID_ARGUMENT, "plan is NULL");
+  REQ(x, "x");
+  REQ(w, "w");
+  REQ(wb, "w_bypass");
+  REQ(gy, "grad_y");
+  const bool gelu = (p->desc.flags & FNO_FLAG_GELU) != 0;
+  if (gelu || grad_w) REQ(save, "save");
+  OPT(save, "save");
+  OPT(grad_x, "grad_x");
+  OPT(grad_w, "grad_w");
+  OPT(grad_wb, "grad_w_bypass");
+  OPT(grad_bias, "grad_bias");
+  fno_status st = check_ws(p, ws, ws_bytes);
+  if (st != FNO_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const fno::Geom& g = p->g;
+  const float* z = gelu ? at<const float>(const_cast<void*>(save), p->save_off_z) : nullptr;
+  float2* ghat = at<float2>(ws, p->ws.yhat);
+  st = forward_transform(p, gelu ? fno::PLANE_GELU_GRAD : fno::PLANE_X, g.Cout, gy, z, ghat,
+                         ws, s);
+  if (st != FNO_OK) return st;
+  if (grad_w)
+    LAUNCH(fno::launch_mix_bwd_dw(p, static_cast<const float2*>(save), ghat,
+                                  reinterpret_cast<float2*>(grad_w), s),
+           "weight gradient");
+  float* red = (grad_wb || grad_bias) ? at<float>(ws, p->ws.red_part) : nullptr;
+  if (grad_x || red) {
+    const float2* Tg = nullptr;
+    if (grad_x) {
+      float2* ghx = at<float2>(ws, p->ws.xhat);
+      LAUNCH(fno::launch_mix_bwd_dx(p, ghat, reinterpret_cast<const float2*>(w), ghx, s),
+             "input-gradient mix");
+      st = inverse_outer(p, g.Cin, ghx, ws, s, &Tg);
+      if (st != FNO_OK) return st;
+    }
+    LAUNCH(fno::launch_epilogue_bwd(p, fno::EPI_BLOCK, Tg, x, wb, gy, z, grad_x, red, s),
+           "backward epilogue");
+    if (red)
+      LAUNCH(fno::launch_bypass_grad_finish(p, red, grad_wb, grad_bias, s), "bypass gradient");
+  }
+  return FNO_OK;
+}
+
+fno_status fno_pointwise_fwd(int64_t batch, int64_t npts, int64_t cin, int64_t hidden,
+                             int64_t cout, const float* x, const float* w1, const float* b1,
+                             const float* w2, const float* b2, float* y, void* stream) {
+  if (batch < 1 || npts < 1 || cin < 1 || cout < 1 || hidden < 0)
+    return fail(FNO_ERR_INVALID_ARGUMENT, "bad pointwise sizes");
+  if (cin > 64 || cout > 128 || hidden > 256)
+    return fail(FNO_ERR_UNSUPPORTED, "pointwise: c_in <= 64, c_out <= 128, hidden <= 256");
+  if (batch > 65535) return fail(FNO_ERR_UNSUPPORTED, "pointwise: batch > 65535");
+  REQ(x, "x");
+  REQ(w1, "w1");
+  REQ(y, "y");
+  OPT(b1, "b1");
+  if (hidden > 0) REQ(w2, "w2");
+  OPT(b2, "b2");
+  LAUNCH(fno::launch_pointwise(batch, npts, (int)cin, (int)hidden, (int)cout, x, w1, b1, w2, b2,
+                               y, static_cast<hipStream_t>(stream)),
+         "pointwise");
+  return FNO_OK;
+}
+
+static int mse_parts(int64_t n) {
+  int64_t g = (n + 255) / 256;
+  return (int)(g < 1024 ? (g < 1 ? 1 : g) : 1024);
+}
+
+fno_status fno_mse_workspace_bytes(int64_t n, size_t* bytes) {
+  if (n < 1 || !bytes) return fail(FNO_ERR_INVALID_ARGUMENT, "bad mse workspace query");
+  *bytes = sizeof(double) * (size_t)mse_parts(n);
+  return FNO_OK;
+}
+
+fno_status fno_mse_grad(int64_t n, const float* y, const float* t, float* grad, float* loss,
+                        void* ws, size_t ws_bytes, void* stream) {
+  if (n < 1) return fail(FNO_ERR_INVALID_ARGUMENT, "n < 1");
+  REQ(y, "y");
+  REQ(t, "t");
+  REQ(grad, "grad");
+  REQ(ws, "workspace");
+  const int parts = mse_parts(n);
+  if (ws_bytes < sizeof(double) * (size_t)parts)
+    return fail(FNO_ERR_INVALID_ARGUMENT, "workspace too small");
+  LAUNCH(fno::launch_mse(n, y, t, grad, loss, static_cast<double*>(ws), parts,
+                         static_cast<hipStream_t>(stream)),
+         "mse");
+  return FNO_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,170 @@
+/*
+ * libfno -- FNO spectral-convolution block on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the spectral block of a Fourier Neural Operator: a truncated real DFT of a
+ * [batch, channel, grid...] field, a per-mode complex channel mix, the zero-padded inverse,
+ * a pointwise 1x1 bypass, a bias and an exact-erf GELU, plus the backward pass.
+ *
+ * Pages cited:
+ *  [MPFNO] "Model-Parallel Fourier Neural Operators as Learned Surrogates for Large-Scale
+ *          Parametric PDEs" (nubint.ai review), section "Proposed method": spectral
+ *          convolution from FNO's linear-algebra form, 4 spectral blocks of width 20,
+ *          gradients by automatic differentiation; "Main findings": 3D and 4D space-time grids.
+ *  [MIXED] "Guaranteed Approximation Bounds and Efficient Mixed-Precision Training for Neural
+ *          Operators" (linnk.ai insight), section "Tiivistelmä": half-precision Fourier
+ *          transform and contraction, tanh pre-activation before the transform.
+ *
+ * Notation (d = ndim spatial axes, axis d-1 contiguous):
+ *   Ntot = prod N_j;  theta_k(p) = 2 pi sum_j k_j p_j / N_j
+ *   retained modes: axis j < d-1 keeps array indices {0..m_j-1} U {N_j-m_j..N_j-1};
+ *                   axis d-1 keeps bins {0..m_{d-1}-1} of its half spectrum.
+ *   xhat[b,i,k] = sum_p x'[b,i,p] e^{-i theta_k(p)},  x' = x or tanh(x) (FNO_FLAG_TANH_PREACT)
+ *   yhat[b,o,k] = sum_i xhat[b,i,k] W[c(k),i,o,kappa(k)]
+ *   y_spec[b,o,p] = (1/Ntot) sum_k gamma(k_{d-1}) Re(yhat[b,o,k] e^{+i theta_k(p)}),
+ *                   gamma = 1 at the DC (and an even axis' Nyquist) bin, else 2
+ *   z = y_spec + sum_i Wb[o,i] x[b,i,p] + bias[o];   y = GELU(z) = z/2 (1 + erf(z/sqrt 2))
+ *
+ * Layouts (all row-major, last index fastest, every pointer 16-byte aligned):
+ *   x, y, grads ... float32 [B, C, N_0, ..., N_{d-1}]
+ *   w, grad_w ..... complex float32 interleaved (re, im) -- the bytes of a complex64 tensor --
+ *                   [2^(d-1) corners][C_in][C_out][m_0]...[m_{d-1}]; bit j of the corner
+ *                   index is set when axis j (j < d-1) is in its high (negative-frequency)
+ *                   range; local index q of a high range is frequency q - m_j.
+ *   w_bypass ...... float32 [C_out][C_in];   bias ... float32 [C_out]
+ *
+ * Ownership: the caller allocates every tensor, the workspace and the save buffer (sizes from
+ * fno_plan_query) on the plan's device and keeps them alive until the stream has run the
+ * call.  A plan owns only its constant tables.  Calls enqueue work on `stream` (a
+ * hipStream_t; NULL = the null stream) and return without synchronising; they never
+ * allocate device memory.  A plan is immutable after creation: concurrent calls on
+ * different streams are safe when each has its own workspace.
+ *
+ * Errors: every function returns an fno_status; nothing aborts or throws across the ABI.
+ *   FNO_ERR_INVALID_ARGUMENT  NULL/misaligned pointer, bad descriptor, workspace too small
+ *   FNO_ERR_UNSUPPORTED       valid FNO shape outside what the kernels implement
+ *   FNO_ERR_HIP               a HIP call or kernel launch failed (detail in
+ *                             fno_last_error_message, thread-local)
+ * Device faults surface at the caller's next synchronisation.
+ */
+#ifndef LIBFNO_FNO_H
+#define LIBFNO_FNO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fno_status {
+  FNO_OK = 0,
+  FNO_ERR_INVALID_ARGUMENT = 1,
+  FNO_ERR_UNSUPPORTED = 2,
+  FNO_ERR_HIP = 3,
+  FNO_ERR_OUT_OF_MEMORY = 4,
+  FNO_ERR_INTERNAL = 5
+} fno_status;
+
+/* Arithmetic of the spectral path (transforms and channel mix).
+ * F32:  float32 operands, float32 accumulation.
+ * BF16: bfloat16 operands (pre-activated input, transform tables, spectra, weights rounded
+ *       to nearest-even on load) with float32 accumulation -- the half-precision transform
+ *       and contraction of [MIXED].  The bypass, bias, GELU and every HBM activation stay
+ *       float32.  */
+typedef enum fno_dtype { FNO_DTYPE_F32 = 0, FNO_DTYPE_BF16 = 1, FNO_DTYPE_F16 = 2 } fno_dtype;
+
+enum {
+  FNO_FLAG_TANH_PREACT = 1u, /* x' = tanh(x) feeds the spectral path only [MIXED] */
+  FNO_FLAG_GELU = 2u,        /* block output y = GELU(z); without it y = z            */
+  FNO_FLAG_BIAS = 4u         /* bias pointer is read; without it bias is taken as 0    */
+};
+
+typedef struct fno_plan_desc {
+  int32_t ndim;           /* spatial dimensions d: 2, 3 or 4                         */
+  int32_t spectral_dtype; /* fno_dtype                                               */
+  uint32_t flags;         /* FNO_FLAG_*                                              */
+  int32_t reserved;       /* must be 0                                               */
+  int64_t batch;          /* B >= 1                                                  */
+  int64_t c_in;           /* input channels  (1..64)                                 */
+  int64_t c_out;          /* output channels (1..64)                                 */
+  int64_t n[4];           /* grid N_0..N_{d-1}; unused entries 0                    */
+  int64_t modes[4];       /* modes per corner m_0..m_{d-1}; 1 <= m_j <= N_j/2 (j<d-1),
+                             1 <= m_{d-1} <= N_{d-1}/2 + 1                           */
+} fno_plan_desc;
+
+typedef struct fno_plan fno_plan;
+
+/* Host-only check of a descriptor (makes no HIP call). */
+fno_status fno_plan_validate(const fno_plan_desc* desc);
+
+/* Validate, build the transform tables in float64 on the host, round them and upload them
+ * once to the current HIP device.  *out receives the plan. */
+fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out);
+
+/* Free a plan's tables (NULL is accepted).  The caller must make sure no enqueued call still
+ * uses the plan. */
+fno_status fno_plan_destroy(fno_plan* plan);
+
+/* Byte sizes of the caller-allocated workspace and save buffer of this plan, and the number
+ * of complex elements of w.  Any output pointer may be NULL. */
+fno_status fno_plan_query(const fno_plan* plan, size_t* workspace_bytes, size_t* save_bytes,
+                          size_t* weight_elems);
+
+/* Spectral convolution only: y_spec = inverse(mix(forward(x')))  (no bypass, bias or GELU).
+ * `save` (nullable, save_bytes) receives the retained spectrum xhat for a later backward. */
+fno_status fno_spectral_conv_fwd(const fno_plan* plan, const float* x, const float* w,
+                                 float* y_spec, void* save, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* Backward of fno_spectral_conv_fwd for the incoming gradient grad_y_spec:
+ *   grad_x = s(x) * adjoint(grad_y_spec) with s = 1 - tanh(x)^2 under FNO_FLAG_TANH_PREACT,
+ *   grad_w = sum_b conj(xhat) ghat  (complex64, W's layout).
+ * `save` (nullable) is the buffer filled by the forward with the same x and w; when NULL the
+ * spectrum is recomputed from x.  grad_x / grad_w may be NULL to skip that output.  Outputs
+ * are overwritten, not accumulated. */
+fno_status fno_spectral_conv_bwd(const fno_plan* plan, const float* x, const float* w,
+                                 const void* save, const float* grad_y_spec, float* grad_x,
+                                 float* grad_w, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/* Full block forward: y = GELU(y_spec + Wb x + bias).  `save` (nullable) receives what
+ * fno_block_bwd needs (the retained spectrum and the pre-activation z). */
+fno_status fno_block_fwd(const fno_plan* plan, const float* x, const float* w,
+                         const float* w_bypass, const float* bias, float* y, void* save,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Full block backward for the incoming gradient grad_y.  `save` must come from
+ * fno_block_fwd with the same inputs (required when FNO_FLAG_GELU is set).
+ * Outputs (each may be NULL to skip): grad_x [B,C_in,N..], grad_w (complex64, W's layout),
+ * grad_w_bypass [C_out][C_in], grad_bias [C_out].  Overwritten, not accumulated; the
+ * reductions over batch and grid are deterministic (bitwise run-to-run). */
+fno_status fno_block_bwd(const fno_plan* plan, const float* x, const float* w,
+                         const float* w_bypass, const float* bias, const void* save,
+                         const float* grad_y, float* grad_x, float* grad_w,
+                         float* grad_w_bypass, float* grad_bias, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Pointwise layers used to lift into and project out of the block stack.
+ * hidden == 0: y = w1 x + b1            (w1 [c_out][c_in], b1 [c_out])
+ * hidden  > 0: y = w2 GELU(w1 x + b1) + b2 (w1 [hidden][c_in], w2 [c_out][hidden])
+ * x [batch][c_in][npts], y [batch][c_out][npts]; biases may be NULL. c_in <= 64, c_out <= 128,
+ * hidden <= 256. */
+fno_status fno_pointwise_fwd(int64_t batch, int64_t npts, int64_t c_in, int64_t hidden,
+                             int64_t c_out, const float* x, const float* w1, const float* b1,
+                             const float* w2, const float* b2, float* y, void* stream);
+
+/* Mean squared error: grad = 2 (y - t) / n and loss = mean((y - t)^2) written to the device
+ * float *loss (deterministic two-stage reduction; nullable).  Workspace size from
+ * fno_mse_workspace_bytes. */
+fno_status fno_mse_workspace_bytes(int64_t n, size_t* bytes);
+fno_status fno_mse_grad(int64_t n, const float* y, const float* t, float* grad, float* loss,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+const char* fno_status_string(fno_status status);
+const char* fno_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBFNO_FNO_H */

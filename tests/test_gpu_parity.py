@@ -1,0 +1,184 @@
+"""HIP path (through the C-ABI) against the fp64 oracle, element by element, on seeded inputs.
+
+Shapes span several work-group tiles with ragged tails, every dimensionality (2D, 3D, 4D
+with a 20-point contiguous axis), odd grids, the largest allowed mode counts, one mode,
+Cin != Cout and batches beyond one register tile.  Each output is compared on its own
+(y_spec, y, grad_x, grad_w, grad_w_bypass, grad_bias): relative L2 <= 1e-5 on the fp32 path,
+<= 1e-2 on the tanh + bf16 path.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle.fno_oracle as O
+from fno_spectral_convolution_amd import inputs
+from tests.gpu_helpers import TOL_F32, TOL_MIXED, announce, check
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # name, batch, cin, cout, grid, modes
+    ("2d_ragged", 2, 3, 5, (24, 20), (5, 4)),
+    ("2d_c1shape", 4, 20, 20, (64, 64), (12, 12)),
+    ("2d_odd_maxmodes", 1, 2, 3, (15, 9), (7, 5)),
+    ("2d_full_spectrum", 1, 3, 3, (8, 8), (4, 5)),
+    ("2d_one_mode", 3, 1, 1, (16, 32), (1, 1)),
+    ("2d_batch20", 20, 2, 2, (8, 16), (2, 3)),
+    ("2d_wide", 2, 64, 64, (32, 64), (8, 16)),
+    ("3d_ragged", 2, 4, 3, (12, 10, 16), (3, 2, 5)),
+    ("4d_t20", 1, 3, 4, (6, 8, 10, 20), (2, 3, 4, 8)),
+]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(a):
+    torch = _torch()
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def _host(t):
+    return t.detach().cpu().numpy()
+
+
+@pytest.fixture(scope="module")
+def L():
+    from fno_spectral_convolution_amd import binding
+    return binding
+
+
+@pytest.mark.parametrize("mixed", [False, True], ids=["f32", "mixed"])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_block_fwd_bwd(L, case, mixed):
+    name, batch, cin, cout, grid, modes = case
+    announce("block", name, "mixed" if mixed else "f32")
+    seed = zlib.crc32(name.encode()) % 1000
+    x, w, wb, b = inputs.small_case(seed, batch, cin, cout, grid, modes)
+    gy = inputs.normal_like(seed, (batch, cout) + grid)
+    tol = TOL_MIXED if mixed else TOL_F32
+    plan = L.Plan(batch, cin, cout, grid, modes, mixed=mixed)
+    tx, tw, twb, tb, tg = (_dev(a) for a in (x, w, wb, b, gy))
+    save = plan.new_save()
+    y = plan.block_fwd(tx, tw, twb, tb, save=save)
+    g = plan.block_bwd(tx, tw, twb, tb, save, tg)
+    _torch().cuda.synchronize()
+    ref = O.block_bwd(x, w, wb, b, modes, gy, tanh=mixed)
+    check("y", _host(y), ref["fwd"]["y"], tol)
+    check("grad_x", _host(g["x"]), ref["grad_x"], tol)
+    check("grad_w", _host(g["w"]), ref["grad_w"], tol)
+    check("grad_wb", _host(g["wb"]), ref["grad_wb"], tol)
+    check("grad_bias", _host(g["bias"]), ref["grad_bias"], tol)
+    plan.close()
+
+
+@pytest.mark.parametrize("mixed", [False, True], ids=["f32", "mixed"])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_spectral_conv_fwd_bwd(L, case, mixed):
+    """The spectral path alone (no bypass to mask its errors), with and without a save."""
+    name, batch, cin, cout, grid, modes = case
+    announce("spectral", name, "mixed" if mixed else "f32")
+    seed = 500 + zlib.crc32(name.encode()) % 1000
+    x, w, _, _ = inputs.small_case(seed, batch, cin, cout, grid, modes)
+    gy = inputs.normal_like(seed, (batch, cout) + grid)
+    tol = TOL_MIXED if mixed else TOL_F32
+    plan = L.Plan(batch, cin, cout, grid, modes, mixed=mixed, gelu=False, bias=False)
+    tx, tw, tg = (_dev(a) for a in (x, w, gy))
+    save = plan.new_save()
+    ys = plan.spectral_conv_fwd(tx, tw, save=save)
+    gx, gw = plan.spectral_conv_bwd(tx, tw, tg, save=save)
+    gx2, gw2 = plan.spectral_conv_bwd(tx, tw, tg, save=None)
+    _torch().cuda.synchronize()
+    fwd = O.spectral_conv_fwd(x, w, modes, tanh=mixed)
+    bwd = O.spectral_conv_bwd(x, w, modes, gy, tanh=mixed)
+    check("y_spec", _host(ys), fwd["y_spec"], tol)
+    check("grad_x", _host(gx), bwd["grad_x"], tol)
+    check("grad_w", _host(gw), bwd["grad_w"], tol)
+    assert np.array_equal(_host(gx), _host(gx2)), "recomputed spectrum changed grad_x"
+    assert np.array_equal(_host(gw), _host(gw2)), "recomputed spectrum changed grad_w"
+    plan.close()
+
+
+@pytest.mark.parametrize("mixed", [False, True], ids=["f32", "mixed"])
+def test_bitwise_deterministic(L, mixed):
+    announce("determinism", mixed)
+    grid, modes = (48, 40), (9, 7)
+    x, w, wb, b = inputs.small_case(11, 3, 6, 6, grid, modes)
+    gy = inputs.normal_like(11, (3, 6) + grid)
+    plan = L.Plan(3, 6, 6, grid, modes, mixed=mixed)
+    tx, tw, twb, tb, tg = (_dev(a) for a in (x, w, wb, b, gy))
+    outs = []
+    for _ in range(2):
+        save = plan.new_save()
+        y = plan.block_fwd(tx, tw, twb, tb, save=save)
+        g = plan.block_bwd(tx, tw, twb, tb, save, tg)
+        _torch().cuda.synchronize()
+        outs.append([_host(y)] + [_host(g[k]) for k in ("x", "w", "wb", "bias")])
+    for a, c in zip(outs[0], outs[1]):
+        assert np.array_equal(a, c)
+    plan.close()
+
+
+def test_gelu_off_and_bias_off(L):
+    """Flags: without GELU the block returns z; without BIAS the bias pointer is ignored."""
+    announce("flags")
+    grid, modes = (16, 24), (4, 6)
+    x, w, wb, b = inputs.small_case(21, 2, 3, 4, grid, modes)
+    gy = inputs.normal_like(21, (2, 4) + grid)
+    plan = L.Plan(2, 3, 4, grid, modes, gelu=False, bias=False)
+    tx, tw, twb, tg = (_dev(a) for a in (x, w, wb, gy))
+    save = plan.new_save()
+    y = plan.block_fwd(tx, tw, twb, None, save=save)
+    g = plan.block_bwd(tx, tw, twb, None, save, tg)
+    _torch().cuda.synchronize()
+    ref = O.block_bwd(x, w, wb, None, modes, gy, act=False)
+    check("z", _host(y), ref["fwd"]["y"], TOL_F32)
+    check("grad_x", _host(g["x"]), ref["grad_x"], TOL_F32)
+    check("grad_w", _host(g["w"]), ref["grad_w"], TOL_F32)
+    check("grad_wb", _host(g["wb"]), ref["grad_wb"], TOL_F32)
+    check("grad_bias", _host(g["bias"]), ref["grad_bias"], TOL_F32)
+    plan.close()
+
+
+def test_pointwise_and_mse(L):
+    announce("pointwise+mse")
+    torch = _torch()
+    g = np.random.default_rng(5)
+    x = g.standard_normal((3, 5, 7, 33)).astype(np.float32)
+    w1 = g.standard_normal((12, 5)).astype(np.float32)
+    b1 = g.standard_normal(12).astype(np.float32)
+    w2 = g.standard_normal((2, 12)).astype(np.float32)
+    b2 = g.standard_normal(2).astype(np.float32)
+    lift = L.pointwise(_dev(x), _dev(w1), _dev(b1))
+    proj = L.pointwise(_dev(x), _dev(w1), _dev(b1), _dev(w2), _dev(b2))
+    t = g.standard_normal((3, 2, 7, 33)).astype(np.float32)
+    loss, grad = L.mse_grad(proj, _dev(t))
+    torch.cuda.synchronize()
+    check("lift", _host(lift), O.pointwise_linear(x, w1, b1), TOL_F32)
+    pref = O.projection_fwd(x, w1, b1, w2, b2)
+    check("projection", _host(proj), pref, TOL_F32)
+    lref, gref = O.mse_loss_grad(_host(proj), t)
+    check("mse_grad", _host(grad), gref, TOL_F32)
+    assert abs(float(_host(loss)[0]) - lref) <= 1e-6 * lref
+
+
+def test_bad_workspace_is_an_error(L):
+    announce("workspace-too-small")
+    torch = _torch()
+    plan = L.Plan(1, 2, 2, (16, 16), (3, 3))
+    x = torch.zeros((1, 2, 16, 16), device="cuda")
+    w = torch.zeros((2, 2, 2, 3, 3), dtype=torch.complex64, device="cuda")
+    y = torch.empty_like(x)
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(L.FnoError) as ei:
+        L.fno_spectral_conv_fwd(plan.handle, x.data_ptr(), w.data_ptr(), y.data_ptr(), None,
+                                ws.data_ptr(), 16, 0)
+    assert ei.value.status == L.FNO_ERR_INVALID_ARGUMENT
+    with pytest.raises(L.FnoError) as ei:
+        L.fno_spectral_conv_fwd(plan.handle, x.data_ptr() + 4, w.data_ptr(), y.data_ptr(), None,
+                                plan.workspace().data_ptr(), plan.ws_bytes, 0)
+    assert ei.value.status == L.FNO_ERR_INVALID_ARGUMENT
+    plan.close()
