@@ -1,0 +1,211 @@
+"""Benchmark: FNO spectral-conv throughput on one MI355X through libfno.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--no-cpu-baseline]
+
+A step is one pass of the workload's whole hot path over one batch of synthetic input
+already resident in HBM.  The default workload is the 2D FNO training step: 4 spectral
+blocks of width 64 on a 512x512 grid, batch 8, modes 32x32 per corner, tanh pre-activation
+and bf16 spectral operands with fp32 accumulation, forward + MSE + backward (input, weight,
+bypass and bias gradients).  Throughput is grid points x channels x batch x blocks per second
+(the forward and backward of a block count once).
+
+Printed: one JSON line with the metric, the per-kernel breakdown measured with HIP events on
+the stream libfno launches on, the roofline of the dominant kernel, and the fp64 oracle timed
+on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_TFLOPS = {"f32_mfma": 157.3, "bf16_mfma": 2516.6, "f32_valu": 78.6}
+METRIC = "FNO spectral-conv fwd+bwd grid-pts·ch/s per MI355X; % HBM/MFMA roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-batch", type=int, default=3)
+    return ap.parse_args()
+
+
+def kernel_model(wl, plan):
+    """Algorithmic bytes and flops per launch of each libfno kernel for this workload.
+
+    Bytes: every input and output buffer of the kernel once (fields, spectra, weights).
+    Flops: the truncated-DFT / mix / bypass arithmetic as the method defines it (direct
+    sums over the retained modes)."""
+    g = plan
+    B, C = wl.batch, wl.width
+    P = wl.points
+    d = wl.ndim
+    U = B * C * P
+    N = list(wl.grid)
+    m = list(wl.modes)
+    Na, Nb, ma, mb = N[-2], N[-1], m[-2], m[-1]
+    K = mb
+    for j in range(d - 1):
+        K *= 2 * m[j]
+    Mprod = 1
+    for v in m:
+        Mprod *= v
+    ncorner = 1 << (d - 1)
+    spec = B * C * K * 8
+    wbytes = ncorner * C * C * Mprod * 8
+    lines = P // Nb
+    T = B * C * lines * mb * 8
+    O = P // (Na * Nb)
+    plane_spec = B * C * O * 2 * ma * mb * 8
+    dft_last = 4 * mb * U                      # real row -> mb complex bins (and back)
+    dft_a = 8 * (2 * ma) * mb * Na * B * C * O  # one complex truncated DFT along axis a
+    bypass = 2 * C * C * P * B
+    mixf = 8 * B * C * C * K
+    model = {
+        "plane_fwd": (4 * U + plane_spec, dft_last + dft_a),
+        "plane_fwd_tanh": (4 * U + plane_spec, dft_last + dft_a),
+        "plane_fwd_gelugrad": (8 * U + plane_spec, dft_last + dft_a),
+        "mix_fwd": (wbytes + 2 * spec, mixf),
+        "mix_bwd_dx": (wbytes + 2 * spec, mixf),
+        "mix_bwd_dw": (wbytes + 2 * spec, mixf),
+        "epilogue_fwd": (4 * U + 4 * U + (4 * U if wl.train else 0) + T, dft_last + bypass),
+        "epilogue_bwd": (16 * U + T, dft_last + 2 * bypass),
+        "mse": (12 * U, 3 * U),
+    }
+    return model
+
+
+def bench_gpu(wl, steps, warmup):
+    import torch
+
+    from fno_spectral_convolution_amd import binding as L
+    from fno_spectral_convolution_amd.stack import StackRunner
+
+    torch.cuda.set_device(0)
+    t0 = time.perf_counter()
+    runner = StackRunner(wl, device="cuda:0")
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t0
+    print(f"[bench] {wl.name}: inputs on device in {setup_s:.1f}s; warmup {warmup}", flush=True)
+    for _ in range(warmup):
+        runner.step()
+    torch.cuda.synchronize()
+    L.fno_timing_reset()
+    L.fno_timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        runner.step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    L.fno_timing_enable(False)
+    kern = L.timing_report()
+    print(f"[bench] timed {steps} steps in {wall:.3f}s", flush=True)
+    return runner, wall, kern
+
+
+def roofline(wl, runner, kern, steps):
+    model = kernel_model(wl, runner.plan)
+    rows = {}
+    for name, (launches, total_ms) in kern.items():
+        avg_s = total_ms / 1e3 / max(launches, 1)
+        b, f = model.get(name, (None, None))
+        rows[name] = {"launches": launches, "avg_us": avg_s * 1e6,
+                      "share": total_ms / max(sum(v[1] for v in kern.values()), 1e-12),
+                      "alg_bytes": b, "alg_flops": f,
+                      "GBps": (b / avg_s / 1e9) if b else None}
+    dom = max((n for n in rows if rows[n]["alg_bytes"]), key=lambda n: kern[n][1])
+    r = rows[dom]
+    avg_s = r["avg_us"] / 1e6
+    # the dominant kernels stream fields: their floor is the HBM time of their bytes
+    ach = r["alg_bytes"] / avg_s / 1e9
+    out = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+           "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+           "alg_bytes_per_launch": r["alg_bytes"], "avg_launch_us": round(r["avg_us"], 2)}
+    return out, rows
+
+
+def cpu_baseline(wl, sample_batch):
+    """The fp64 oracle, as it stands, on a bounded sample: one block's forward + backward for
+    `sample_batch` batch entries of the workload (full grid and width)."""
+    import numpy as np
+
+    import oracle.fno_oracle as O
+    from fno_spectral_convolution_amd import inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    sb = min(sample_batch, wl.batch)
+    g = np.random.default_rng(np.random.SeedSequence([wl.cfg_id, 99]))
+    shape = (sb, wl.width) + tuple(wl.grid)
+    x = g.standard_normal(shape).astype(np.float32)
+    gy = g.standard_normal(shape).astype(np.float32) * 1e-3
+    blk = inputs.block_params(wl, 1)[0]
+    t0 = time.perf_counter()
+    if wl.train:
+        O.block_bwd(x, blk["w"], blk["wb"], blk["bias"], wl.modes, gy, tanh=wl.mixed)
+        what = "fwd+bwd"
+    else:
+        O.block_fwd(x, blk["w"], blk["wb"], blk["bias"], wl.modes, tanh=wl.mixed)
+        what = "fwd"
+    dt = time.perf_counter() - t0
+    units = sb * wl.width * wl.points
+    return {"value": units / dt, "unit": "grid-pts·ch/s", "cores": threads, "kind": "oracle",
+            "sample": f"one block {what} (fp64 numpy oracle), batch {sb} of {wl.batch}, "
+                      f"width {wl.width}, grid {list(wl.grid)}, modes {list(wl.modes)}: "
+                      f"{dt:.2f} s",
+            "seconds": round(dt, 3), "host_cpus": os.cpu_count()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding is a design only).", file=sys.stderr, flush=True)
+        sys.exit(2)
+    from fno_spectral_convolution_amd import configs
+    wl = configs.get(args.workload)
+    runner, wall, kern = bench_gpu(wl, args.steps, args.warmup)
+    ms = wall / args.steps * 1e3
+    value = wl.units / (wall / args.steps)
+    roof, rows = roofline(wl, runner, kern, args.steps)
+    del runner
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", flush=True)
+        cpu = cpu_baseline(wl, args.cpu_sample_batch)
+    dtype = "bf16" if wl.mixed else "f32"
+    rec = {
+        "metric": METRIC, "value": value, "unit": "grid-pts·ch/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.notes}", "batch": wl.batch, "width": wl.width,
+                   "grid": list(wl.grid), "modes": list(wl.modes), "blocks": wl.blocks,
+                   "spectral_precision": "bf16 operands, fp32 accumulate" if wl.mixed
+                   else "fp32", "pointwise_precision": "fp32"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": {k: {"launches": v["launches"], "avg_us": round(v["avg_us"], 2),
+                        "share": round(v["share"], 4),
+                        "GBps": round(v["GBps"], 1) if v["GBps"] else None}
+                    for k, v in sorted(rows.items(), key=lambda kv: -kv[1]["share"])},
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

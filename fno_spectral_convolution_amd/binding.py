@@ -34,7 +34,8 @@ FNO_FLAG_BIAS = 4
 EXPORTS = [
     "fno_plan_validate", "fno_plan_create", "fno_plan_destroy", "fno_plan_query",
     "fno_spectral_conv_fwd", "fno_spectral_conv_bwd", "fno_block_fwd", "fno_block_bwd",
-    "fno_pointwise_fwd", "fno_mse_workspace_bytes", "fno_mse_grad", "fno_status_string",
+    "fno_pointwise_fwd", "fno_mse_workspace_bytes", "fno_mse_grad", "fno_timing_enable",
+    "fno_timing_reset", "fno_timing_count", "fno_timing_get", "fno_status_string",
     "fno_last_error_message",
 ]
 
@@ -74,6 +75,11 @@ def _load():
                                       P, P, P, P, P, P, P]),
         "fno_mse_workspace_bytes": (c_int, [c_int64, POINTER(c_size_t)]),
         "fno_mse_grad": (c_int, [c_int64, P, P, P, P, P, c_size_t, P]),
+        "fno_timing_enable": (c_int, [c_int]),
+        "fno_timing_reset": (c_int, []),
+        "fno_timing_count": (c_int, [POINTER(c_int)]),
+        "fno_timing_get": (c_int, [c_int, POINTER(c_char_p), POINTER(c_int64),
+                                   POINTER(ctypes.c_double)]),
         "fno_status_string": (c_char_p, [c_int]),
         "fno_last_error_message": (c_char_p, []),
     }
@@ -168,6 +174,31 @@ def fno_mse_workspace_bytes(n: int) -> int:
 
 def fno_mse_grad(n, y, t, grad, loss, ws, ws_bytes, stream):
     _check(_lib.fno_mse_grad(n, y, t, grad, loss, ws, ws_bytes, stream), "fno_mse_grad")
+
+
+def fno_timing_enable(enable: bool) -> None:
+    _check(_lib.fno_timing_enable(1 if enable else 0), "fno_timing_enable")
+
+
+def fno_timing_reset() -> None:
+    _check(_lib.fno_timing_reset(), "fno_timing_reset")
+
+
+def fno_timing_count() -> int:
+    n = c_int()
+    _check(_lib.fno_timing_count(byref(n)), "fno_timing_count")
+    return n.value
+
+
+def fno_timing_get(index: int):
+    name, launches, ms = c_char_p(), c_int64(), ctypes.c_double()
+    _check(_lib.fno_timing_get(index, byref(name), byref(launches), byref(ms)), "fno_timing_get")
+    return name.value.decode(), launches.value, ms.value
+
+
+def timing_report() -> dict:
+    """{kernel name: (launches, total ms)} of everything recorded since the last reset."""
+    return {nm: (n, ms) for nm, n, ms in (fno_timing_get(i) for i in range(fno_timing_count()))}
 
 
 # ---- torch-facing convenience (allocation + pointer marshalling only) ---------------------

@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -325,11 +326,98 @@ namespace {
       return fail(FNO_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name); \
   } while (0)
 
-#define LAUNCH(call, what)                               \
-  do {                                                   \
-    hipError_t e_ = (call);                              \
-    if (e_ != hipSuccess) return hip_fail(e_, what);     \
+// Every kernel launch goes through LAUNCH(name, stream, call): `name` keys the optional
+// per-kernel event timer (fno_timing_*).
+#define LAUNCH(name, strm, call)                                          \
+  do {                                                                    \
+    hipError_t e_ = timed_launch(name, strm, [&]() { return (call); });   \
+    if (e_ != hipSuccess) return hip_fail(e_, name);                      \
   } while (0)
+
+struct TimingState {
+  std::mutex mu;
+  bool on = false;
+  struct Pending {
+    const char* name;
+    hipEvent_t a, b;
+  };
+  std::vector<Pending> pending;
+  std::vector<hipEvent_t> pool;
+  std::vector<std::string> names;
+  std::vector<int64_t> launches;
+  std::vector<double> total_ms;
+};
+
+TimingState& timing_state() {
+  static TimingState* t = new TimingState();  // never destroyed: usable at exit
+  return *t;
+}
+
+hipEvent_t timing_event(TimingState& T) {
+  if (!T.pool.empty()) {
+    hipEvent_t e = T.pool.back();
+    T.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Launch through `launch`; when the timer is on, bracket it with two events on `s`.
+template <typename F>
+hipError_t timed_launch(const char* name, hipStream_t s, F&& launch) {
+  TimingState& T = timing_state();
+  hipEvent_t a = nullptr, b = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(T.mu);
+    if (!T.on) return launch();
+    a = timing_event(T);
+    b = timing_event(T);
+  }
+  if (!a || !b) return launch();
+  hipError_t e = hipEventRecord(a, s);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, s);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(T.mu);
+  T.pending.push_back({name, a, b});
+  return hipSuccess;
+}
+
+// Wait for every recorded pair and fold it into the per-name totals (caller holds T.mu).
+hipError_t timing_collect(TimingState& T) {
+  for (auto& r : T.pending) {
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e != hipSuccess) return e;
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) return e;
+    size_t i = 0;
+    while (i < T.names.size() && T.names[i] != r.name) ++i;
+    if (i == T.names.size()) {
+      T.names.push_back(r.name);
+      T.launches.push_back(0);
+      T.total_ms.push_back(0.0);
+    }
+    T.launches[i] += 1;
+    T.total_ms[i] += ms;
+    T.pool.push_back(r.a);
+    T.pool.push_back(r.b);
+  }
+  T.pending.clear();
+  return hipSuccess;
+}
+
+const char* plane_name(int plane_in) {
+  switch (plane_in) {
+    case fno::PLANE_TANH: return "plane_fwd_tanh";
+    case fno::PLANE_GELU_GRAD: return "plane_fwd_gelugrad";
+    default: return "plane_fwd";
+  }
+}
 
 template <typename T>
 T* at(void* base, size_t off) {
@@ -347,16 +435,16 @@ fno_status forward_transform(const fno_plan* p, int plane_in, int chans, const f
   const int64_t plane_out = (int64_t)g.B * chans * g.O * 2 * g.ma * g.mb;
   const bool more = g.d > 2;
   float2* plane_dst = (p->nch == 1) ? (more ? ping : dst) : part;
-  LAUNCH(fno::launch_plane_fwd(p, plane_in, chans, in0, in1, plane_dst, s), "plane transform");
+  LAUNCH(plane_name(plane_in), s, fno::launch_plane_fwd(p, plane_in, chans, in0, in1, plane_dst, s));
   float2* cur = plane_dst;
   if (p->nch > 1) {
     float2* rd = more ? ping : dst;
-    LAUNCH(fno::launch_reduce_parts(part, p->nch, plane_out, plane_out, rd, s), "chunk reduce");
+    LAUNCH("reduce_parts", s, fno::launch_reduce_parts(part, p->nch, plane_out, plane_out, rd, s));
     cur = rd;
   }
   for (int j = g.d - 3; j >= 0; --j) {
     float2* nxt = (j == 0) ? dst : (cur == ping ? pong : ping);
-    LAUNCH(fno::launch_outer_fwd(p, j, chans, cur, 1, 0, nxt, s), "outer-axis transform");
+    LAUNCH("outer_fwd", s, fno::launch_outer_fwd(p, j, chans, cur, 1, 0, nxt, s));
     cur = nxt;
   }
   return FNO_OK;
@@ -372,7 +460,7 @@ fno_status inverse_outer(const fno_plan* p, int chans, const float2* src, void* 
   const float2* cur = src;
   for (int j = 0; j <= g.d - 2; ++j) {
     float2* nxt = (cur == ping) ? pong : ping;
-    LAUNCH(fno::launch_outer_inv(p, j, chans, cur, nxt, s), "inverse outer-axis transform");
+    LAUNCH("outer_inv", s, fno::launch_outer_inv(p, j, chans, cur, nxt, s));
     cur = nxt;
   }
   *T = cur;
@@ -410,14 +498,12 @@ fno_status fno_spectral_conv_fwd(const fno_plan* p, const float* x, const float*
   st = forward_transform(p, pre_mode(p), p->g.Cin, x, nullptr, xhat, ws, s);
   if (st != FNO_OK) return st;
   float2* yhat = at<float2>(ws, p->ws.yhat);
-  LAUNCH(fno::launch_mix_fwd(p, xhat, 1, 0, reinterpret_cast<const float2*>(w), yhat, s),
-         "channel mix");
+  LAUNCH("mix_fwd", s, fno::launch_mix_fwd(p, xhat, 1, 0, reinterpret_cast<const float2*>(w), yhat, s));
   const float2* T = nullptr;
   st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T);
   if (st != FNO_OK) return st;
-  LAUNCH(fno::launch_epilogue_fwd(p, fno::EPI_SPECTRAL, T, x, nullptr, nullptr, y_spec, nullptr,
-                                  s),
-         "epilogue");
+  LAUNCH("epilogue_spec_fwd", s, fno::launch_epilogue_fwd(p, fno::EPI_SPECTRAL, T, x, nullptr, nullptr, y_spec, nullptr,
+                                  s));
   return FNO_OK;
 }
 
@@ -438,14 +524,13 @@ fno_status fno_block_fwd(const fno_plan* p, const float* x, const float* w, cons
   st = forward_transform(p, pre_mode(p), p->g.Cin, x, nullptr, xhat, ws, s);
   if (st != FNO_OK) return st;
   float2* yhat = at<float2>(ws, p->ws.yhat);
-  LAUNCH(fno::launch_mix_fwd(p, xhat, 1, 0, reinterpret_cast<const float2*>(w), yhat, s),
-         "channel mix");
+  LAUNCH("mix_fwd", s, fno::launch_mix_fwd(p, xhat, 1, 0, reinterpret_cast<const float2*>(w), yhat, s));
   const float2* T = nullptr;
   st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T);
   if (st != FNO_OK) return st;
   float* zsave = (save && (p->desc.flags & FNO_FLAG_GELU)) ? at<float>(save, p->save_off_z)
                                                             : nullptr;
-  LAUNCH(fno::launch_epilogue_fwd(p, fno::EPI_BLOCK, T, x, wb, bias, y, zsave, s), "epilogue");
+  LAUNCH("epilogue_fwd", s, fno::launch_epilogue_fwd(p, fno::EPI_BLOCK, T, x, wb, bias, y, zsave, s));
   return FNO_OK;
 }
 
@@ -474,22 +559,19 @@ fno_status fno_spectral_conv_bwd(const fno_plan* p, const float* x, const float*
     }
     st = forward_transform(p, fno::PLANE_X, g.Cout, gys, nullptr, ghat, ws, s);
     if (st != FNO_OK) return st;
-    LAUNCH(fno::launch_mix_bwd_dw(p, xhat, ghat, reinterpret_cast<float2*>(grad_w), s),
-           "weight gradient");
+    LAUNCH("mix_bwd_dw", s, fno::launch_mix_bwd_dw(p, xhat, ghat, reinterpret_cast<float2*>(grad_w), s));
   } else {
     st = forward_transform(p, fno::PLANE_X, g.Cout, gys, nullptr, ghat, ws, s);
     if (st != FNO_OK) return st;
   }
   if (grad_x) {
     float2* ghx = at<float2>(ws, p->ws.xhat);
-    LAUNCH(fno::launch_mix_bwd_dx(p, ghat, reinterpret_cast<const float2*>(w), ghx, s),
-           "input-gradient mix");
+    LAUNCH("mix_bwd_dx", s, fno::launch_mix_bwd_dx(p, ghat, reinterpret_cast<const float2*>(w), ghx, s));
     const float2* Tg = nullptr;
     st = inverse_outer(p, g.Cin, ghx, ws, s, &Tg);
     if (st != FNO_OK) return st;
-    LAUNCH(fno::launch_epilogue_bwd(p, fno::EPI_SPECTRAL, Tg, x, nullptr, nullptr, nullptr,
-                                    grad_x, nullptr, s),
-           "backward epilogue");
+    LAUNCH("epilogue_spec_bwd", s, fno::launch_epilogue_bwd(p, fno::EPI_SPECTRAL, Tg, x, nullptr, nullptr, nullptr,
+                                    grad_x, nullptr, s));
   }
   return FNO_OK;
 }
@@ -521,23 +603,20 @@ fno_status fno_block_bwd(const fno_plan* p, const float* x, const float* w, cons
                          ws, s);
   if (st != FNO_OK) return st;
   if (grad_w)
-    LAUNCH(fno::launch_mix_bwd_dw(p, static_cast<const float2*>(save), ghat,
-                                  reinterpret_cast<float2*>(grad_w), s),
-           "weight gradient");
+    LAUNCH("mix_bwd_dw", s, fno::launch_mix_bwd_dw(p, static_cast<const float2*>(save), ghat,
+                                  reinterpret_cast<float2*>(grad_w), s));
   float* red = (grad_wb || grad_bias) ? at<float>(ws, p->ws.red_part) : nullptr;
   if (grad_x || red) {
     const float2* Tg = nullptr;
     if (grad_x) {
       float2* ghx = at<float2>(ws, p->ws.xhat);
-      LAUNCH(fno::launch_mix_bwd_dx(p, ghat, reinterpret_cast<const float2*>(w), ghx, s),
-             "input-gradient mix");
+      LAUNCH("mix_bwd_dx", s, fno::launch_mix_bwd_dx(p, ghat, reinterpret_cast<const float2*>(w), ghx, s));
       st = inverse_outer(p, g.Cin, ghx, ws, s, &Tg);
       if (st != FNO_OK) return st;
     }
-    LAUNCH(fno::launch_epilogue_bwd(p, fno::EPI_BLOCK, Tg, x, wb, gy, z, grad_x, red, s),
-           "backward epilogue");
+    LAUNCH("epilogue_bwd", s, fno::launch_epilogue_bwd(p, fno::EPI_BLOCK, Tg, x, wb, gy, z, grad_x, red, s));
     if (red)
-      LAUNCH(fno::launch_bypass_grad_finish(p, red, grad_wb, grad_bias, s), "bypass gradient");
+      LAUNCH("bypass_grad_finish", s, fno::launch_bypass_grad_finish(p, red, grad_wb, grad_bias, s));
   }
   return FNO_OK;
 }
@@ -556,9 +635,8 @@ fno_status fno_pointwise_fwd(int64_t batch, int64_t npts, int64_t cin, int64_t h
   OPT(b1, "b1");
   if (hidden > 0) REQ(w2, "w2");
   OPT(b2, "b2");
-  LAUNCH(fno::launch_pointwise(batch, npts, (int)cin, (int)hidden, (int)cout, x, w1, b1, w2, b2,
-                               y, static_cast<hipStream_t>(stream)),
-         "pointwise");
+  LAUNCH("pointwise", static_cast<hipStream_t>(stream), fno::launch_pointwise(batch, npts, (int)cin, (int)hidden, (int)cout, x, w1, b1, w2, b2,
+                               y, static_cast<hipStream_t>(stream)));
   return FNO_OK;
 }
 
@@ -583,10 +661,49 @@ fno_status fno_mse_grad(int64_t n, const float* y, const float* t, float* grad, 
   const int parts = mse_parts(n);
   if (ws_bytes < sizeof(double) * (size_t)parts)
     return fail(FNO_ERR_INVALID_ARGUMENT, "workspace too small");
-  LAUNCH(fno::launch_mse(n, y, t, grad, loss, static_cast<double*>(ws), parts,
-                         static_cast<hipStream_t>(stream)),
-         "mse");
+  LAUNCH("mse", static_cast<hipStream_t>(stream), fno::launch_mse(n, y, t, grad, loss, static_cast<double*>(ws), parts,
+                         static_cast<hipStream_t>(stream)));
+  return FNO_OK;
+}
+
+fno_status fno_timing_enable(int enable) {
+  TimingState& T = timing_state();
+  std::lock_guard<std::mutex> lk(T.mu);
+  T.on = enable != 0;
+  return FNO_OK;
+}
+
+fno_status fno_timing_reset(void) {
+  TimingState& T = timing_state();
+  std::lock_guard<std::mutex> lk(T.mu);
+  hipError_t e = T.pending.empty() ? hipSuccess : timing_collect(T);
+  T.names.clear();
+  T.launches.clear();
+  T.total_ms.clear();
+  if (e != hipSuccess) return hip_fail(e, "fno_timing_reset");
+  return FNO_OK;
+}
+
+fno_status fno_timing_count(int* count) {
+  if (!count) return fail(FNO_ERR_INVALID_ARGUMENT, "count is NULL");
+  TimingState& T = timing_state();
+  std::lock_guard<std::mutex> lk(T.mu);
+  hipError_t e = T.pending.empty() ? hipSuccess : timing_collect(T);
+  if (e != hipSuccess) return hip_fail(e, "fno_timing_count");
+  *count = (int)T.names.size();
+  return FNO_OK;
+}
+
+fno_status fno_timing_get(int index, const char** name, int64_t* launches, double* total_ms) {
+  TimingState& T = timing_state();
+  std::lock_guard<std::mutex> lk(T.mu);
+  if (index < 0 || index >= (int)T.names.size())
+    return fail(FNO_ERR_INVALID_ARGUMENT, "timing index %d out of range", index);
+  if (name) *name = T.names[index].c_str();
+  if (launches) *launches = T.launches[index];
+  if (total_ms) *total_ms = T.total_ms[index];
   return FNO_OK;
 }
 
 }  // extern "C"
+

@@ -160,6 +160,17 @@ fno_status fno_mse_workspace_bytes(int64_t n, size_t* bytes);
 fno_status fno_mse_grad(int64_t n, const float* y, const float* t, float* grad, float* loss,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* Per-kernel timing with HIP events, for measurement (off by default).  While enabled, every
+ * kernel launch of libfno is bracketed by two events recorded on the stream it is launched
+ * on, keyed by the kernel's name (e.g. "plane_fwd_tanh", "epilogue_bwd").  fno_timing_count
+ * waits for the recorded events, folds them into per-name totals and returns the number of
+ * names; fno_timing_get returns name, launch count and summed duration (ms) of entry
+ * `index`.  The name pointer stays valid until the next fno_timing_reset.  Process-wide. */
+fno_status fno_timing_enable(int enable);
+fno_status fno_timing_reset(void);
+fno_status fno_timing_count(int* count);
+fno_status fno_timing_get(int index, const char** name, int64_t* launches, double* total_ms);
+
 const char* fno_status_string(fno_status status);
 const char* fno_last_error_message(void);
 
