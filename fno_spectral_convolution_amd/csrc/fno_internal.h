@@ -36,6 +36,19 @@ struct Tables {
   const float2* root_bf[kMaxDims];  // same values rounded to bfloat16 (stored as float)
   const int32_t* mode_woff;         // [K]: offset of mode t in W for (i, o) = (0, 0)
   const int32_t* woff_mode;         // [ncorner * Mprod]: retained mode of each W element
+  // last-axis inverse tables [Nb][kpad], interleaved (re, im) columns:
+  // gt_fwd = g(k)/Ntot (cos, -sin)(2 pi k p / Nb); gt_unit = (cos, -sin) (adjoint scale)
+  const float* gt_fwd;
+  const float* gt_unit;
+  const uint16_t* gt_fwd_bf;        // the same, bfloat16 bits
+  const uint16_t* gt_unit_bf;
+  // forward plane tables: t1 [Nb][jpad] (col 2k = cos, 2k+1 = -sin of 2 pi k c / Nb) and
+  // f2 [4 ma][Na] (rows < 2 ma: cos, rows >= 2 ma: sin of 2 pi ka(s) row / Na)
+  const float* t1;
+  const uint16_t* t1_bf;
+  const float* f2;
+  const uint16_t* f2_bf;      // bfloat16 of f2
+  const uint16_t* f2_bf_lo;   // bfloat16 of (f2 - f2_bf): f2_bf + f2_bf_lo ~ f2 to 2^-16
 };
 
 struct Workspace {
@@ -58,7 +71,10 @@ struct fno_plan {
   void* table_mem;
   int device;
   int nch;              // chunks of the plane transform along axis a
-  int nred;             // work-groups of the bypass-gradient reduction
+  int nred;             // work-groups of the bypass-gradient reduction (generic kernels)
+  int kpad;             // 2*mb rounded up to 32 (columns of the last-axis tables)
+  int jpad;             // 2*mb rounded up to 16 (columns of the forward plane table t1)
+  int plane_rows;       // rows of axis a per plane-transform chunk
   int64_t complex_max;  // largest intermediate spectrum (complex elements)
   fno::Workspace ws;
   size_t save_bytes;
@@ -93,6 +109,18 @@ hipError_t launch_epilogue_fwd(const fno_plan* p, int mode, const float2* T, con
 hipError_t launch_epilogue_bwd(const fno_plan* p, int mode, const float2* Tg, const float* x,
                                const float* wb, const float* gy, const float* z,
                                float* grad_x, float* red_part, hipStream_t s);
+bool epilogue_fast_ok(const fno_plan* p, int mode, bool fwd);
+int epilogue_bwd_fast_groups(const fno_plan* p);
+hipError_t launch_epilogue_fwd_fast(const fno_plan* p, int mode, const float2* T, const float* x,
+                                    const float* wb, const float* bias, float* y, float* zsave,
+                                    hipStream_t s);
+hipError_t launch_epilogue_bwd_fast(const fno_plan* p, int mode, const float2* Tg,
+                                    const float* x, const float* wb, const float* gy,
+                                    const float* z, float* grad_x, float* red_part,
+                                    hipStream_t s);
+bool plane_fast_ok(const fno_plan* p);
+hipError_t launch_plane_fwd_fast(const fno_plan* p, int plane_in, int chans, const float* in0,
+                                 const float* in1, float2* out, hipStream_t s);
 hipError_t launch_bypass_grad_finish(const fno_plan* p, const float* red_part, float* dwb,
                                      float* dbias, hipStream_t s);
 hipError_t launch_pointwise(int64_t batch, int64_t npts, int cin, int hidden, int cout,

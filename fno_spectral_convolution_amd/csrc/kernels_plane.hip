@@ -1,0 +1,431 @@
+// Matrix-core forward transform of one [Na][Nb] plane (the last two axes of a field).
+//
+//   R[row][j]  = sum_c x'[row][c] T1[c][j]            (j < jpad = 16*NTJ; T1[c][2k] = cos,
+//                                                     T1[c][2k+1] = -sin of 2 pi k c / Nb)
+//   X2[i][j]  += sum_row F2[i][row] R[row][j]          (F2[i] = cos rows i < 2ma, sin rows
+//                                                     i >= 2ma of 2 pi ka(i) row / Na)
+//   X[s][k]    = (X2[s][2k] + X2[2ma+s][2k+1]) + i (X2[s][2k+1] - X2[2ma+s][2k])
+// i.e. the truncated real DFT of the contiguous axis followed by the truncated DFT of the
+// next axis, for the retained modes only (the FNO spectral transform computed from its
+// linear-algebra form -- model-parallel FNO page, "Proposed method").
+//
+// One work-group (4 waves) handles a chunk of rows of one plane.  Rows are streamed with
+// coalesced float4 loads (prefetched one sub-round ahead), pre-activated (tanh, GELU') and
+// staged in LDS; wave w owns N-tile (w % NTJ) of R and keeps its slice of T1 in registers,
+// so the table is never re-read.  R goes to LDS transposed and feeds the second product,
+// whose M-tiles (rows of F2, read through L2) are split over the waves.  Each chunk writes
+// its partial spectrum; chunks are summed by the next kernel in a fixed order.
+#include "fno_internal.h"
+#include "mfma.h"
+
+#include <math.h>
+
+namespace fno {
+
+constexpr int kPlaneMaxModes = 32;  // m_a limit of the matrix-core plane transform
+
+struct PlaneArgs {
+  int Na, Nb, ma, mb;
+  int64_t planes;
+  int rows_per_chunk;
+  const float* in0;
+  const float* in1;
+  const void* t1;        // [Nb][jpad] f32, or bf16 bits
+  const void* f2;        // [4ma][Na] f32, or bf16 bits (hi)
+  const uint16_t* f2lo;  // bf16 residual of f2 (bf16 path)
+  float2* out;           // [nch][planes][2ma][mb]
+};
+
+__device__ __forceinline__ float tanh_fast(float v) {
+  // tanh(|v|) = (1 - e) / (1 + e), e = exp(-2|v|): no cancellation for large |v|, and the
+  // result is rounded to bfloat16 afterwards on the path that uses it
+  const float e = __expf(-2.0f * fabsf(v));
+  const float t = (1.0f - e) / (1.0f + e);
+  return copysignf(t, v);
+}
+
+__device__ __forceinline__ float gelu_grad_plane(float z) {
+  const float cdf = 0.5f * (1.0f + erff(z * 0.70710678118654752f));
+  const float pdf = __expf(-0.5f * z * z) * 0.39894228040143268f;
+  return cdf + z * pdf;
+}
+
+template <int PIN>
+__device__ __forceinline__ float prologue(float v, float w) {
+  if (PIN == PLANE_TANH) return tanh_fast(v);
+  if (PIN == PLANE_GELU_GRAD) return v * gelu_grad_plane(w);
+  return v;
+}
+
+__device__ __forceinline__ float cmp4(const float4& v, int j) {
+  return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
+}
+
+// ------------------------------------------------------------------------------------------
+// Combine X2 (cos rows 0..2ma-1, sin rows 2ma..4ma-1, interleaved re/im columns) held in LDS
+// into the complex partial spectrum of this chunk.
+__device__ __forceinline__ void combine_store(const float* s_x2, int jpad, int ma, int mb,
+                                              float2* dst, int tid) {
+  for (int e = tid; e < 2 * ma * mb; e += 256) {
+    const int sr = e / mb, k = e - sr * mb;
+    const float* c = s_x2 + sr * jpad + 2 * k;
+    const float* sn = s_x2 + (2 * ma + sr) * jpad + 2 * k;
+    dst[e] = make_float2(c[0] + sn[1], c[1] - sn[0]);
+  }
+}
+
+// bf16 operands, fp32 accumulation.  NB = Nb (multiple of 32, <= 512), NTJ = jpad / 16.
+template <int PIN, int NB, int NTJ>
+__global__ void __launch_bounds__(256) k_plane_bf16(PlaneArgs a) {
+  constexpr int SUB = 16 * (4 / NTJ);   // rows per sub-round (one M-tile per wave)
+  constexpr int XS = NB + 8;            // LDS row stride (bf16 elements)
+  constexpr int RS = 64 + 8;            // Rt row stride (bf16 elements)
+  constexpr int KS = NB / 32;           // K-steps of the first product
+  constexpr int LPR = NB / 4;           // float4 per row
+  constexpr int NLD = SUB * LPR / 256;  // float4 loads per thread per sub-round
+  constexpr int JP = 16 * NTJ;
+  static_assert(SUB * LPR % 256 == 0, "sub-round must split evenly");
+  constexpr int LOOP_BYTES = SUB * XS * 2 + JP * RS * 2;
+  constexpr int END_BYTES = 4 * kPlaneMaxModes * JP * 4;
+  __shared__ __attribute__((aligned(16)))
+  unsigned char s_raw[LOOP_BYTES > END_BYTES ? LOOP_BYTES : END_BYTES];
+  uint16_t* s_x = reinterpret_cast<uint16_t*>(s_raw);
+  uint16_t* s_rt = s_x + SUB * XS;
+  float* s_x2 = reinterpret_cast<float*>(s_raw);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, q = lane >> 4;
+  const int jt = wave % NTJ, mt = wave / NTJ;
+  const int IT = a.ma / 4;  // 16-row tiles of F2 (4 ma rows)
+  const int64_t plane = blockIdx.x;
+  const int chunk = blockIdx.y;
+  const int r_begin = chunk * a.rows_per_chunk;
+  const int r_end = min(a.Na, r_begin + a.rows_per_chunk);
+
+  // this wave's slice of T1: B[k][n] = T1[32 s + 8 q + e][16 jt + m]
+  bf16x8 tb[KS];
+  {
+    const uint16_t* t1 = static_cast<const uint16_t*>(a.t1);
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        tb[s][e] = __builtin_bit_cast(__bf16, t1[(32 * s + 8 * q + e) * JP + 16 * jt + m]);
+  }
+  f32x4 x2[2][NTJ];  // i-tiles wave and wave + 4
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int v = 0; v < NTJ; ++v) x2[u][v] = zero4();
+
+  const float* base0 = a.in0 + plane * (int64_t)a.Na * NB;
+  const float* base1 = (PIN == PLANE_GELU_GRAD) ? a.in1 + plane * (int64_t)a.Na * NB : nullptr;
+  float4 pre0[NLD], pre1[NLD];
+  // rows at or beyond r_end are zero (no memory access)
+  auto load_sub = [&](int r0) {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int e = tid + 256 * u;
+      const int row = r0 + e / LPR, c4 = e % LPR;
+      pre0[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      pre1[u] = pre0[u];
+      if (row < r_end) {
+        pre0[u] = *reinterpret_cast<const float4*>(base0 + (int64_t)row * NB + 4 * c4);
+        if (PIN == PLANE_GELU_GRAD)
+          pre1[u] = *reinterpret_cast<const float4*>(base1 + (int64_t)row * NB + 4 * c4);
+      }
+    }
+  };
+  auto stage_sub = [&]() {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int e = tid + 256 * u;
+      const int r = e / LPR, c4 = e % LPR;
+      const float4 v = pre0[u], w = pre1[u];
+      uint2 packed;
+      packed.x = (uint32_t)bf16_bits(prologue<PIN>(v.x, w.x)) |
+                 ((uint32_t)bf16_bits(prologue<PIN>(v.y, w.y)) << 16);
+      packed.y = (uint32_t)bf16_bits(prologue<PIN>(v.z, w.z)) |
+                 ((uint32_t)bf16_bits(prologue<PIN>(v.w, w.w)) << 16);
+      *reinterpret_cast<uint2*>(s_x + r * XS + 4 * c4) = packed;
+    }
+  };
+
+  const uint16_t* f2 = static_cast<const uint16_t*>(a.f2);
+  load_sub(r_begin);
+  for (int r0 = r_begin; r0 < r_end; r0 += 64) {
+    // 64 rows of R per stage, SUB rows per sub-round
+    for (int sub = 0; sub < 64; sub += SUB) {
+      __syncthreads();  // previous readers of s_x / s_rt are done
+      stage_sub();
+      load_sub(r0 + sub + SUB);  // prefetch the next sub-round
+      __syncthreads();
+      f32x4 d = zero4();
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 av =
+            *reinterpret_cast<const bf16x8*>(s_x + (16 * mt + m) * XS + 32 * s + 8 * q);
+        d = mfma_bf16(av, tb[s], d);
+      }
+      // D rows 16 mt + 4 q + r, column 16 jt + m  ->  Rt[column][stage row]
+      uint2 pk;
+      pk.x = (uint32_t)bf16_bits(d[0]) | ((uint32_t)bf16_bits(d[1]) << 16);
+      pk.y = (uint32_t)bf16_bits(d[2]) | ((uint32_t)bf16_bits(d[3]) << 16);
+      *reinterpret_cast<uint2*>(s_rt + (16 * jt + m) * RS + sub + 16 * mt + 4 * q) = pk;
+    }
+    __syncthreads();
+    // second product over these 64 rows, K-steps of 32 rows (slot e <-> row krow + e)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int krow = 32 * ks + 8 * q;
+      bf16x8 bv[NTJ];
+#pragma unroll
+      for (int v = 0; v < NTJ; ++v)
+        bv[v] = *reinterpret_cast<const bf16x8*>(s_rt + (16 * v + m) * RS + krow);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int it = wave + 4 * u;
+        if (it >= IT) break;
+        const int64_t fo = (int64_t)(16 * it + m) * a.Na + r0 + krow;
+        bf16x8 ah, al;
+        if (r0 + krow + 8 <= r_end) {
+          ah = *reinterpret_cast<const bf16x8*>(f2 + fo);
+          al = *reinterpret_cast<const bf16x8*>(a.f2lo + fo);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const bool in = r0 + krow + e < r_end;
+            ah[e] = __builtin_bit_cast(__bf16, in ? f2[fo + e] : (uint16_t)0);
+            al[e] = __builtin_bit_cast(__bf16, in ? a.f2lo[fo + e] : (uint16_t)0);
+          }
+        }
+#pragma unroll
+        for (int v = 0; v < NTJ; ++v) {
+          x2[u][v] = mfma_bf16(ah, bv[v], x2[u][v]);
+          x2[u][v] = mfma_bf16(al, bv[v], x2[u][v]);
+        }
+      }
+    }
+  }
+  __syncthreads();  // the loop buffers are reused for X2
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int it = wave + 4 * u;
+    if (it >= IT) break;
+#pragma unroll
+    for (int v = 0; v < NTJ; ++v)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_x2[(16 * it + 4 * q + r) * JP + 16 * v + m] = x2[u][v][r];
+  }
+  __syncthreads();
+  combine_store(s_x2, JP, a.ma, a.mb,
+                a.out + ((int64_t)chunk * a.planes + plane) * (2 * a.ma * a.mb), tid);
+}
+
+// fp32 operands.  First product with 16x16x4 MFMAs: lane (m, q) reads xs[row][16 g + 4 q ..]
+// and MFMA jj uses component jj (k-slot q <-> column 16 g + 4 q + jj).
+template <int PIN, int NB, int NTJ>
+__global__ void __launch_bounds__(256) k_plane_f32(PlaneArgs a) {
+  constexpr int SUB = 16 * (4 / NTJ);
+  constexpr int XS = NB + 4;
+  constexpr int RS = 64 + 4;
+  constexpr int KG = NB / 16;
+  constexpr int LPR = NB / 4;
+  constexpr int NLD = SUB * LPR / 256;
+  constexpr int JP = 16 * NTJ;
+  static_assert(SUB * LPR % 256 == 0, "sub-round must split evenly");
+  constexpr int LOOP_BYTES = SUB * XS * 4 + JP * RS * 4;
+  constexpr int END_BYTES = 4 * kPlaneMaxModes * JP * 4;
+  __shared__ __attribute__((aligned(16)))
+  unsigned char s_raw[LOOP_BYTES > END_BYTES ? LOOP_BYTES : END_BYTES];
+  float* s_x = reinterpret_cast<float*>(s_raw);
+  float* s_rt = s_x + SUB * XS;
+  float* s_x2 = reinterpret_cast<float*>(s_raw);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, q = lane >> 4;
+  const int jt = wave % NTJ, mt = wave / NTJ;
+  const int IT = a.ma / 4;
+  const int64_t plane = blockIdx.x;
+  const int chunk = blockIdx.y;
+  const int r_begin = chunk * a.rows_per_chunk;
+  const int r_end = min(a.Na, r_begin + a.rows_per_chunk);
+
+  // T1 slice: for group g, MFMA jj: B[q][n] = T1[16 g + 4 q + jj][16 jt + m]
+  float4 tb[KG];
+  {
+    const float* t1 = static_cast<const float*>(a.t1);
+#pragma unroll
+    for (int g = 0; g < KG; ++g)
+      tb[g] = make_float4(t1[(16 * g + 4 * q + 0) * JP + 16 * jt + m],
+                          t1[(16 * g + 4 * q + 1) * JP + 16 * jt + m],
+                          t1[(16 * g + 4 * q + 2) * JP + 16 * jt + m],
+                          t1[(16 * g + 4 * q + 3) * JP + 16 * jt + m]);
+  }
+  f32x4 x2[2][NTJ];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int v = 0; v < NTJ; ++v) x2[u][v] = zero4();
+
+  const float* base0 = a.in0 + plane * (int64_t)a.Na * NB;
+  const float* base1 = (PIN == PLANE_GELU_GRAD) ? a.in1 + plane * (int64_t)a.Na * NB : nullptr;
+  float4 pre0[NLD], pre1[NLD];
+  auto load_sub = [&](int r0) {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int e = tid + 256 * u;
+      const int row = r0 + e / LPR, c4 = e % LPR;
+      pre0[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      pre1[u] = pre0[u];
+      if (row < r_end) {
+        pre0[u] = *reinterpret_cast<const float4*>(base0 + (int64_t)row * NB + 4 * c4);
+        if (PIN == PLANE_GELU_GRAD)
+          pre1[u] = *reinterpret_cast<const float4*>(base1 + (int64_t)row * NB + 4 * c4);
+      }
+    }
+  };
+  auto stage_sub = [&]() {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int e = tid + 256 * u;
+      const int r = e / LPR, c4 = e % LPR;
+      const float4 v = pre0[u], w = pre1[u];
+      *reinterpret_cast<float4*>(s_x + r * XS + 4 * c4) =
+          make_float4(prologue<PIN>(v.x, w.x), prologue<PIN>(v.y, w.y), prologue<PIN>(v.z, w.z),
+                      prologue<PIN>(v.w, w.w));
+    }
+  };
+
+  const float* f2 = static_cast<const float*>(a.f2);
+  load_sub(r_begin);
+  for (int r0 = r_begin; r0 < r_end; r0 += 64) {
+    for (int sub = 0; sub < 64; sub += SUB) {
+      __syncthreads();
+      stage_sub();
+      load_sub(r0 + sub + SUB);
+      __syncthreads();
+      f32x4 d = zero4();
+#pragma unroll
+      for (int g = 0; g < KG; ++g) {
+        const float4 av =
+            *reinterpret_cast<const float4*>(s_x + (16 * mt + m) * XS + 16 * g + 4 * q);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) d = mfma_f32(cmp4(av, jj), cmp4(tb[g], jj), d);
+      }
+      *reinterpret_cast<float4*>(s_rt + (16 * jt + m) * RS + sub + 16 * mt + 4 * q) =
+          make_float4(d[0], d[1], d[2], d[3]);
+    }
+    __syncthreads();
+    // second product: K-groups of 16 rows; MFMA jj uses row 16 kg + 4 q + jj
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) {
+      float4 bv[NTJ];
+#pragma unroll
+      for (int v = 0; v < NTJ; ++v)
+        bv[v] = *reinterpret_cast<const float4*>(s_rt + (16 * v + m) * RS + 16 * kg + 4 * q);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int it = wave + 4 * u;
+        if (it >= IT) break;
+        const int row0 = r0 + 16 * kg + 4 * q;
+        const int64_t fo = (int64_t)(16 * it + m) * a.Na + row0;
+        float4 av;
+        if (row0 + 4 <= r_end) {
+          av = *reinterpret_cast<const float4*>(f2 + fo);
+        } else {
+          av.x = (row0 + 0 < r_end) ? f2[fo + 0] : 0.f;
+          av.y = (row0 + 1 < r_end) ? f2[fo + 1] : 0.f;
+          av.z = (row0 + 2 < r_end) ? f2[fo + 2] : 0.f;
+          av.w = (row0 + 3 < r_end) ? f2[fo + 3] : 0.f;
+        }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int v = 0; v < NTJ; ++v)
+            x2[u][v] = mfma_f32(cmp4(av, jj), cmp4(bv[v], jj), x2[u][v]);
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int it = wave + 4 * u;
+    if (it >= IT) break;
+#pragma unroll
+    for (int v = 0; v < NTJ; ++v)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_x2[(16 * it + 4 * q + r) * JP + 16 * v + m] = x2[u][v][r];
+  }
+  __syncthreads();
+  combine_store(s_x2, JP, a.ma, a.mb,
+                a.out + ((int64_t)chunk * a.planes + plane) * (2 * a.ma * a.mb), tid);
+}
+
+// ------------------------------------------------------------------------------------------
+bool plane_fast_ok(const fno_plan* p) {
+  const Geom& g = p->g;
+  const int jpad = p->jpad;
+  if (!(g.Nb == 64 || g.Nb == 128 || g.Nb == 256 || g.Nb == 512)) return false;
+  if (!(jpad == 16 || jpad == 32 || jpad == 64)) return false;
+  if (g.ma % 4 != 0 || g.ma > kPlaneMaxModes) return false;  // F2: <= 2 tiles of 16 rows/wave
+  // vector loads of F2 rows need 8-aligned row offsets
+  if (g.Na % 8 != 0 || (p->plane_rows % 64 != 0 && p->plane_rows != g.Na)) return false;
+  if (!g.bf16) {
+    const int sub = 16 * (4 / (jpad / 16));
+    if (sub * (g.Nb + 4) * 4 > 48 * 1024) return false;  // LDS of the staged rows
+  }
+  return true;
+}
+
+template <int PIN, int NB, int NTJ>
+static void launch_plane_t(const fno_plan* p, const PlaneArgs& a, dim3 grid, hipStream_t s) {
+  if (p->g.bf16)
+    hipLaunchKernelGGL((k_plane_bf16<PIN, NB, NTJ>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_plane_f32<PIN, NB, NTJ>), grid, dim3(256), 0, s, a);
+}
+
+template <int PIN, int NB>
+static void launch_plane_nb(const fno_plan* p, const PlaneArgs& a, dim3 grid, hipStream_t s) {
+  switch (p->jpad) {
+    case 16: launch_plane_t<PIN, NB, 1>(p, a, grid, s); break;
+    case 32: launch_plane_t<PIN, NB, 2>(p, a, grid, s); break;
+    default: launch_plane_t<PIN, NB, 4>(p, a, grid, s); break;
+  }
+}
+
+template <int PIN>
+static void launch_plane_pin(const fno_plan* p, const PlaneArgs& a, dim3 grid, hipStream_t s) {
+  switch (p->g.Nb) {
+    case 64: launch_plane_nb<PIN, 64>(p, a, grid, s); break;
+    case 128: launch_plane_nb<PIN, 128>(p, a, grid, s); break;
+    case 256: launch_plane_nb<PIN, 256>(p, a, grid, s); break;
+    default: launch_plane_nb<PIN, 512>(p, a, grid, s); break;
+  }
+}
+
+hipError_t launch_plane_fwd_fast(const fno_plan* p, int plane_in, int chans, const float* in0,
+                                 const float* in1, float2* out, hipStream_t s) {
+  const Geom& g = p->g;
+  PlaneArgs a{};
+  a.Na = g.Na;
+  a.Nb = g.Nb;
+  a.ma = g.ma;
+  a.mb = g.mb;
+  a.planes = (int64_t)g.B * chans * g.O;
+  a.rows_per_chunk = p->plane_rows;
+  a.in0 = in0;
+  a.in1 = in1;
+  a.t1 = g.bf16 ? (const void*)p->t.t1_bf : (const void*)p->t.t1;
+  a.f2 = g.bf16 ? (const void*)p->t.f2_bf : (const void*)p->t.f2;
+  a.f2lo = p->t.f2_bf_lo;
+  a.out = out;
+  dim3 grid((unsigned)a.planes, (unsigned)p->nch);
+  switch (plane_in) {
+    case PLANE_X: launch_plane_pin<PLANE_X>(p, a, grid, s); break;
+    case PLANE_TANH: launch_plane_pin<PLANE_TANH>(p, a, grid, s); break;
+    default: launch_plane_pin<PLANE_GELU_GRAD>(p, a, grid, s); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fno

@@ -124,9 +124,10 @@ k_plane_fwd(Geom g, const float2* __restrict__ root_b, const float2* __restrict_
 
 hipError_t launch_plane_fwd(const fno_plan* p, int plane_in, int chans, const float* in0,
                             const float* in1, float2* out, hipStream_t s) {
+  if (plane_fast_ok(p)) return launch_plane_fwd_fast(p, plane_in, chans, in0, in1, out, s);
   const Geom& g = p->g;
   const int64_t planes = (int64_t)g.B * chans * g.O;
-  const int rows = (g.Na + p->nch - 1) / p->nch;
+  const int rows = p->plane_rows;
   dim3 grid((unsigned)planes, (unsigned)p->nch);
   const size_t lds = sizeof(float2) * (g.Nb + g.Na + kPlaneRB * g.mb) +
                      sizeof(float) * kPlaneRB * g.Nb;
@@ -448,6 +449,8 @@ k_epilogue_fwd(Geom g, int mode, bool gelu, const float2* __restrict__ root_b,
 hipError_t launch_epilogue_fwd(const fno_plan* p, int mode, const float2* T, const float* x,
                                const float* wb, const float* bias, float* y, float* zsave,
                                hipStream_t s) {
+  if (epilogue_fast_ok(p, mode, true))
+    return launch_epilogue_fwd_fast(p, mode, T, x, wb, bias, y, zsave, s);
   const Geom& g = p->g;
   const size_t lds = sizeof(float2) * g.Nb +
                      sizeof(float) * ((size_t)g.Cout * g.Cin + g.Cout +
@@ -573,6 +576,8 @@ k_epilogue_bwd(Geom g, int mode, bool gelu, bool tanh_pre, const float2* __restr
 hipError_t launch_epilogue_bwd(const fno_plan* p, int mode, const float2* Tg, const float* x,
                                const float* wb, const float* gy, const float* z,
                                float* grad_x, float* red_part, hipStream_t s) {
+  if (epilogue_fast_ok(p, mode, false))
+    return launch_epilogue_bwd_fast(p, mode, Tg, x, wb, gy, z, grad_x, red_part, s);
   const Geom& g = p->g;
   const int64_t tiles = (g.P + kEbThreads - 1) / kEbThreads;
   const int groups = p->nred / g.B;
@@ -608,8 +613,9 @@ hipError_t launch_bypass_grad_finish(const fno_plan* p, const float* red_part, f
                                      float* dbias, hipStream_t s) {
   const Geom& g = p->g;
   const int npair = g.Cout * g.Cin + g.Cout;
+  const int nparts = epilogue_fast_ok(p, EPI_BLOCK, false) ? epilogue_bwd_fast_groups(p) : p->nred;
   hipLaunchKernelGGL(k_bypass_finish, dim3((npair + 255) / 256), dim3(256), 0, s, red_part,
-                     p->nred, g.Cout, g.Cin, dwb, dbias);
+                     nparts, g.Cout, g.Cin, dwb, dbias);
   return hipGetLastError();
 }
 

@@ -53,6 +53,21 @@ float round_bf16(float v) {
   return r;
 }
 
+// float64 -> bfloat16 bits, round to nearest even (via the float32 rounding of the value)
+uint16_t bf16_bits_host(double v) {
+  const float f = round_bf16((float)v);
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return (uint16_t)(u >> 16);
+}
+
+double bf16_value_host(uint16_t bits) {
+  const uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
 }  // namespace
 
 extern "C" {
@@ -162,14 +177,18 @@ fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out) {
   g.bf16 = desc->spectral_dtype == FNO_DTYPE_BF16;
   const int cmax = g.Cin > g.Cout ? g.Cin : g.Cout;
 
-  // plane-transform chunking along axis a: enough groups to fill the chip
+  p->kpad = (2 * g.mb + 31) / 32 * 32;
+  p->jpad = (2 * g.mb + 15) / 16 * 16;
+  // plane-transform chunking along axis a: about 1024 work-groups, chunks of 64-row multiples
   {
     const int64_t planes = (int64_t)g.B * cmax * g.O;
-    int nch = (int)((2048 + planes - 1) / planes);
-    int maxch = g.Na / 8 > 0 ? g.Na / 8 : 1;
-    if (nch > maxch) nch = maxch;
-    if (nch < 1) nch = 1;
-    p->nch = nch;
+    int64_t want = (1024 + planes - 1) / planes;
+    if (want < 1) want = 1;
+    int rows = (int)((g.Na + want - 1) / want);
+    rows = (rows + 63) / 64 * 64;
+    if (rows > g.Na) rows = g.Na;
+    p->plane_rows = rows;
+    p->nch = (g.Na + rows - 1) / rows;
   }
   {
     const int64_t tiles = (g.P + 63) / 64;
@@ -202,7 +221,11 @@ fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out) {
   w.yhat = off;
   off += align_up(sizeof(float2) * (size_t)g.B * cmax * g.K);
   w.red_part = off;
-  off += align_up(sizeof(float) * (size_t)p->nred * (g.Cout * g.Cin + g.Cout));
+  {
+    const int nfast = fno::epilogue_bwd_fast_groups(p);
+    const int nparts = nfast > p->nred ? nfast : p->nred;
+    off += align_up(sizeof(float) * (size_t)nparts * (g.Cout * g.Cin + g.Cout));
+  }
   w.total = off;
   p->save_off_z = align_up(sizeof(float2) * (size_t)g.B * g.Cin * g.K);
   p->save_bytes = p->save_off_z +
@@ -219,6 +242,27 @@ fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out) {
     rootbf_off[j] = toff;
     toff += align_up(sizeof(float2) * g.N[j]);
   }
+  const size_t gt_elems = (size_t)g.Nb * p->kpad;
+  const size_t gt_fwd_off = toff;
+  toff += align_up(sizeof(float) * gt_elems);
+  const size_t gt_unit_off = toff;
+  toff += align_up(sizeof(float) * gt_elems);
+  const size_t gt_fwd_bf_off = toff;
+  toff += align_up(sizeof(uint16_t) * gt_elems);
+  const size_t gt_unit_bf_off = toff;
+  toff += align_up(sizeof(uint16_t) * gt_elems);
+  const size_t t1_elems = (size_t)g.Nb * p->jpad;
+  const size_t f2_elems = (size_t)4 * g.ma * g.Na;
+  const size_t t1_off = toff;
+  toff += align_up(sizeof(float) * t1_elems);
+  const size_t t1_bf_off = toff;
+  toff += align_up(sizeof(uint16_t) * t1_elems);
+  const size_t f2_off = toff;
+  toff += align_up(sizeof(float) * f2_elems);
+  const size_t f2_bf_off = toff;
+  toff += align_up(sizeof(uint16_t) * f2_elems);
+  const size_t f2_bf_lo_off = toff;
+  toff += align_up(sizeof(uint16_t) * f2_elems);
   const size_t woff_mode_elems = (size_t)g.ncorner * g.Mprod;
   const size_t mode_woff_off = toff;
   toff += align_up(sizeof(int32_t) * (size_t)g.K);
@@ -233,6 +277,67 @@ fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out) {
       const float c = (float)cos(ang), s = (float)sin(ang);
       r[t] = make_float2(c, s);
       rb[t] = make_float2(round_bf16(c), round_bf16(s));
+    }
+  }
+  {
+    // last-axis inverse tables: column 2k = g cos, 2k+1 = -g sin (angle 2 pi ((k p) mod Nb)/Nb)
+    float* gf = reinterpret_cast<float*>(host.data() + gt_fwd_off);
+    float* gu = reinterpret_cast<float*>(host.data() + gt_unit_off);
+    uint16_t* gfb = reinterpret_cast<uint16_t*>(host.data() + gt_fwd_bf_off);
+    uint16_t* gub = reinterpret_cast<uint16_t*>(host.data() + gt_unit_bf_off);
+    const double inv_ntot = 1.0 / (double)g.P;
+    for (int pt = 0; pt < g.Nb; ++pt)
+      for (int k = 0; k < p->kpad / 2; ++k) {
+        double c = 0.0, sn = 0.0, gam = 0.0;
+        if (k < g.mb) {
+          const double ang = 2.0 * M_PI * (double)(((int64_t)k * pt) % g.Nb) / (double)g.Nb;
+          c = cos(ang);
+          sn = sin(ang);
+          gam = (k == 0 || 2 * k == g.Nb) ? 1.0 : 2.0;
+        }
+        const size_t e = (size_t)pt * p->kpad + 2 * k;
+        gf[e] = (float)(gam * inv_ntot * c);
+        gf[e + 1] = (float)(-gam * inv_ntot * sn);
+        gu[e] = (float)c;
+        gu[e + 1] = (float)(-sn);
+        gfb[e] = bf16_bits_host(gam * inv_ntot * c);
+        gfb[e + 1] = bf16_bits_host(-gam * inv_ntot * sn);
+        gub[e] = bf16_bits_host(c);
+        gub[e + 1] = bf16_bits_host(-sn);
+      }
+  }
+  {
+    // forward plane tables
+    float* t1 = reinterpret_cast<float*>(host.data() + t1_off);
+    uint16_t* t1b = reinterpret_cast<uint16_t*>(host.data() + t1_bf_off);
+    for (int c = 0; c < g.Nb; ++c)
+      for (int k = 0; k < p->jpad / 2; ++k) {
+        double cv = 0.0, sv = 0.0;
+        if (k < g.mb) {
+          const double ang = 2.0 * M_PI * (double)(((int64_t)k * c) % g.Nb) / (double)g.Nb;
+          cv = cos(ang);
+          sv = -sin(ang);
+        }
+        const size_t e = (size_t)c * p->jpad + 2 * k;
+        t1[e] = (float)cv;
+        t1[e + 1] = (float)sv;
+        t1b[e] = bf16_bits_host(cv);
+        t1b[e + 1] = bf16_bits_host(sv);
+      }
+    float* f2 = reinterpret_cast<float*>(host.data() + f2_off);
+    uint16_t* f2b = reinterpret_cast<uint16_t*>(host.data() + f2_bf_off);
+    uint16_t* f2l = reinterpret_cast<uint16_t*>(host.data() + f2_bf_lo_off);
+    for (int i = 0; i < 4 * g.ma; ++i) {
+      const int sidx = i % (2 * g.ma);
+      const int ka = sidx < g.ma ? sidx : g.Na - 2 * g.ma + sidx;
+      for (int row = 0; row < g.Na; ++row) {
+        const double ang = 2.0 * M_PI * (double)(((int64_t)ka * row) % g.Na) / (double)g.Na;
+        const double v = i < 2 * g.ma ? cos(ang) : sin(ang);
+        const size_t e = (size_t)i * g.Na + row;
+        f2[e] = (float)v;
+        f2b[e] = bf16_bits_host(v);
+        f2l[e] = bf16_bits_host(v - bf16_value_host(f2b[e]));
+      }
     }
   }
   {
@@ -286,6 +391,15 @@ fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out) {
     p->t.root[j] = j < g.d ? reinterpret_cast<const float2*>(base + root_off[j]) : nullptr;
     p->t.root_bf[j] = j < g.d ? reinterpret_cast<const float2*>(base + rootbf_off[j]) : nullptr;
   }
+  p->t.gt_fwd = reinterpret_cast<const float*>(base + gt_fwd_off);
+  p->t.gt_unit = reinterpret_cast<const float*>(base + gt_unit_off);
+  p->t.gt_fwd_bf = reinterpret_cast<const uint16_t*>(base + gt_fwd_bf_off);
+  p->t.gt_unit_bf = reinterpret_cast<const uint16_t*>(base + gt_unit_bf_off);
+  p->t.t1 = reinterpret_cast<const float*>(base + t1_off);
+  p->t.t1_bf = reinterpret_cast<const uint16_t*>(base + t1_bf_off);
+  p->t.f2 = reinterpret_cast<const float*>(base + f2_off);
+  p->t.f2_bf = reinterpret_cast<const uint16_t*>(base + f2_bf_off);
+  p->t.f2_bf_lo = reinterpret_cast<const uint16_t*>(base + f2_bf_lo_off);
   p->t.mode_woff = reinterpret_cast<const int32_t*>(base + mode_woff_off);
   p->t.woff_mode = reinterpret_cast<const int32_t*>(base + woff_mode_off);
   *out = p;

@@ -1,0 +1,50 @@
+// Thin wrappers over the gfx950 matrix-core builtins used by libfno, with their lane layouts.
+//
+// 16x16x4 f32  : A lane l holds A[l%16][l/16];            B holds B[l/16][l%16]
+// 16x16x32 bf16: A lane l holds A[l%16][8*(l/16) + e];    B holds B[8*(l/16) + e][l%16]
+// 16x16 result : lane l, register r holds D[4*(l/16) + r][l%16]
+// (checked on the device against a host matrix product for these exact builtins)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fno {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// float -> bfloat16 round-to-nearest-even, as raw bits
+__device__ __forceinline__ uint16_t bf16_bits(float v) {
+  uint32_t u = __float_as_uint(v);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(float4 a, float4 b) {
+  bf16x8 r;
+  r[0] = (__bf16)a.x;
+  r[1] = (__bf16)a.y;
+  r[2] = (__bf16)a.z;
+  r[3] = (__bf16)a.w;
+  r[4] = (__bf16)b.x;
+  r[5] = (__bf16)b.y;
+  r[6] = (__bf16)b.z;
+  r[7] = (__bf16)b.w;
+  return r;
+}
+
+__device__ __forceinline__ f32x4 zero4() {
+  f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  return z;
+}
+
+}  // namespace fno

@@ -28,6 +28,13 @@ CASES = [
     ("2d_wide", 2, 64, 64, (32, 64), (8, 16)),
     ("3d_ragged", 2, 4, 3, (12, 10, 16), (3, 2, 5)),
     ("4d_t20", 1, 3, 4, (6, 8, 10, 20), (2, 3, 4, 8)),
+    # shapes taken by the matrix-core kernels (contiguous axis a multiple of 64)
+    ("2d_mc_c16", 2, 16, 16, (40, 128), (6, 10)),
+    ("2d_mc_c32", 3, 32, 32, (24, 256), (5, 16)),
+    ("2d_mc_c48", 2, 48, 48, (16, 64), (4, 8)),
+    ("2d_mc_c64", 2, 64, 64, (64, 512), (8, 32)),
+    ("3d_mc_c20", 1, 20, 20, (10, 12, 64), (3, 4, 8)),
+    ("4d_mc_c16", 1, 16, 16, (4, 6, 8, 64), (2, 2, 3, 6)),
 ]
 
 
