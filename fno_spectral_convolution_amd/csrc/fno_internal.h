@@ -49,6 +49,14 @@ struct Tables {
   const float* f2;
   const uint16_t* f2_bf;      // bfloat16 of f2
   const uint16_t* f2_bf_lo;   // bfloat16 of (f2 - f2_bf): f2_bf + f2_bf_lo ~ f2 to 2^-16
+  // outer-axis transforms of axes 0..d-2: A = [Mr | Mi] with rows = outputs, padded to 16:
+  // oinv[j] [pad16(N_j)][2 pad16(2 m_j)]  (e^{+i theta}),  ofwd[j] [pad16(2 m_j)][2 pad16(N_j)]
+  const float* oinv[kMaxDims];
+  const uint16_t* oinv_bf[kMaxDims];
+  const uint16_t* oinv_bf_lo[kMaxDims];
+  const float* ofwd[kMaxDims];
+  const uint16_t* ofwd_bf[kMaxDims];
+  const uint16_t* ofwd_bf_lo[kMaxDims];
 };
 
 struct Workspace {
@@ -121,6 +129,9 @@ hipError_t launch_epilogue_bwd_fast(const fno_plan* p, int mode, const float2* T
 bool plane_fast_ok(const fno_plan* p);
 hipError_t launch_plane_fwd_fast(const fno_plan* p, int plane_in, int chans, const float* in0,
                                  const float* in1, float2* out, hipStream_t s);
+bool outer_fast_ok(const fno_plan* p, int axis, bool inv);
+hipError_t launch_outer_mfma(const fno_plan* p, int axis, int chans, bool inv, const float2* in,
+                             float2* out, hipStream_t s);
 hipError_t launch_bypass_grad_finish(const fno_plan* p, const float* red_part, float* dwb,
                                      float* dbias, hipStream_t s);
 hipError_t launch_pointwise(int64_t batch, int64_t npts, int cin, int hidden, int cout,

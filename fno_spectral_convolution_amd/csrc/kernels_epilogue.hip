@@ -11,12 +11,14 @@
 //   g_z = g_y GELU'(z),   dWb[o,i] += sum_p g_z[o,p] x[i,p],   dbias[o] += sum_p g_z[o,p]
 // with GU the unit-scale table (the adjoint of the forward transform) and s = 1 - tanh^2.
 //
-// Work split: one wave per group of 16*TM consecutive points of one line (TM = 4 forward,
-// 2 backward) and all channels.  Results are computed transposed (points x channels) so that
-// every lane reads and writes whole float4s of one channel's contiguous points:
+// Work split: a work-group walks a contiguous range of 64-point groups (whole lines of the
+// contiguous axis).  All 256 threads load the group's channel rows with float4 (prefetched one
+// group ahead) into [channel][point] LDS tiles; the spectrum rows of the current line are
+// staged in LDS once per line.  The 4 waves then split the 16x16 output tiles.  Products are
+// computed transposed (points x channels):
 //   spectral part : 16x16x32 bf16 (mixed path) or 16x16x4 f32 MFMA, K = 2 mb (padded)
 //   bypass / grads: 16x16x4 f32 MFMA, K = channels (4 per step) or points (backward dWb)
-// The last-axis table is read through L2 (it is shared by every wave); Wb lives in LDS.
+// The last-axis table is read through L2 (shared by every wave); Wb slices sit in registers.
 #include "fno_internal.h"
 #include "mfma.h"
 
@@ -59,312 +61,331 @@ __device__ __forceinline__ float comp(const float4& v, int j) {
   return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
 }
 
-// Spectral part of one point group: acc[t][nt] (+)= GT^T x Tcat^T.
-//   M-tile t, row m  <-> point p0 + TM*m + t  (A operand: GT row)
-//   N-tile nt, col n <-> channel 16*nt + n    (B operand: Tcat row of that channel)
-template <int C, int TM, bool BF>
-__device__ __forceinline__ void spectral_part(const EpiArgs& a, const float2* Trow0,
-                                              int pb0, int m, int q,
-                                              f32x4 (&acc)[TM][(C + 15) / 16]) {
-  constexpr int NT = (C + 15) / 16;
+constexpr int PG = 64;        // points per group (one line of the contiguous axis holds Nb/PG)
+constexpr int XS = PG + 4;    // LDS row stride (floats) of the [channel][point] tiles
+constexpr int kMaxKpad = 64;  // 2*mb padded; larger spectra take the generic kernels
+
+// Stage the spectrum rows of one line (every channel, 2*mb floats) into LDS as the B operand
+// of the spectral product: bf16 [CP][kpad + 8] or f32 [CP][kpad + 4], zero padded.
+template <int C, bool BF>
+__device__ __forceinline__ void stage_line(const EpiArgs& a, const float2* Trow0,
+                                           unsigned char* tl, int tid) {
+  constexpr int CP = (C + 15) / 16 * 16;
+  const int kst = a.kpad + (BF ? 8 : 4);
+  const int64_t cstride = a.lines * a.mb;
   const int kf_end = 2 * a.mb;
-  const int64_t cstride = a.lines * a.mb;  // complex elements between channels
-  if (BF) {
-    const uint16_t* gt = static_cast<const uint16_t*>(a.gt);
-    for (int s = 0; s < a.kpad / 32; ++s) {
-      const int kf = 32 * s + 8 * q;
-      bf16x8 A[TM];
-#pragma unroll
-      for (int t = 0; t < TM; ++t) {
-        const int p = pb0 + TM * m + t;
-        A[t] = *reinterpret_cast<const bf16x8*>(gt + (int64_t)p * a.kpad + kf);
-      }
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int o = 16 * nt + m;
-        float4 u0 = make_float4(0.f, 0.f, 0.f, 0.f), u1 = u0;
-        if (o < C) {
-          const float* tr = reinterpret_cast<const float*>(Trow0 + (int64_t)o * cstride);
-          if (kf < kf_end) u0 = *reinterpret_cast<const float4*>(tr + kf);
-          if (kf + 4 < kf_end) u1 = *reinterpret_cast<const float4*>(tr + kf + 4);
-        }
-        const bf16x8 Bv = to_bf16x8(u0, u1);
-#pragma unroll
-        for (int t = 0; t < TM; ++t) acc[t][nt] = mfma_bf16(A[t], Bv, acc[t][nt]);
-      }
-    }
-  } else {
-    const float* gt = static_cast<const float*>(a.gt);
-    for (int g = 0; g < a.kpad / 16; ++g) {
-      const int kf = 16 * g + 4 * q;
-      float4 A4[TM];
-#pragma unroll
-      for (int t = 0; t < TM; ++t) {
-        const int p = pb0 + TM * m + t;
-        A4[t] = *reinterpret_cast<const float4*>(gt + (int64_t)p * a.kpad + kf);
-      }
-      float4 B4[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int o = 16 * nt + m;
-        B4[nt] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (o < C && kf < kf_end)
-          B4[nt] = *reinterpret_cast<const float4*>(
-              reinterpret_cast<const float*>(Trow0 + (int64_t)o * cstride) + kf);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int t = 0; t < TM; ++t)
-            acc[t][nt] = mfma_f32(comp(A4[t], j), comp(B4[nt], j), acc[t][nt]);
+  const int g4 = a.kpad / 4;
+  for (int e = tid; e < CP * g4; e += 256) {
+    const int c = e / g4, k4 = 4 * (e - c * g4);
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < C && k4 < kf_end)
+      v = *reinterpret_cast<const float4*>(
+          reinterpret_cast<const float*>(Trow0 + (int64_t)c * cstride) + k4);
+    if (BF) {
+      uint2 pk;
+      pk.x = (uint32_t)bf16_bits(v.x) | ((uint32_t)bf16_bits(v.y) << 16);
+      pk.y = (uint32_t)bf16_bits(v.z) | ((uint32_t)bf16_bits(v.w) << 16);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(tl) + c * kst + k4) = pk;
+    } else {
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(tl) + c * kst + k4) = v;
     }
   }
 }
 
+// Spectral product of one point group for this wave: acc[j] += GT[points of M-tile t] x
+// tl[channel tile ct]^T, with t = tbase + j.  M-tile t, row m <-> point 16 t + m of the group.
+template <int C, int TMW, bool BF>
+__device__ __forceinline__ void spectral_coop(const EpiArgs& a, const unsigned char* tl,
+                                              int pb0, int ct, int tbase, int m, int q,
+                                              f32x4 (&acc)[TMW]) {
+  const int kst = a.kpad + (BF ? 8 : 4);
+  if (BF) {
+    const uint16_t* gt = static_cast<const uint16_t*>(a.gt);
+    const uint16_t* tb = reinterpret_cast<const uint16_t*>(tl) + (16 * ct + m) * kst;
+    for (int s = 0; s < a.kpad / 32; ++s) {
+      const bf16x8 B = *reinterpret_cast<const bf16x8*>(tb + 32 * s + 8 * q);
+#pragma unroll
+      for (int j = 0; j < TMW; ++j) {
+        const int p = pb0 + 16 * (tbase + j) + m;
+        const bf16x8 A = *reinterpret_cast<const bf16x8*>(gt + (int64_t)p * a.kpad + 32 * s + 8 * q);
+        acc[j] = mfma_bf16(A, B, acc[j]);
+      }
+    }
+  } else {
+    const float* gt = static_cast<const float*>(a.gt);
+    const float* tb = reinterpret_cast<const float*>(tl) + (16 * ct + m) * kst;
+    for (int g = 0; g < a.kpad / 16; ++g) {
+      const float4 B4 = *reinterpret_cast<const float4*>(tb + 16 * g + 4 * q);
+#pragma unroll
+      for (int j = 0; j < TMW; ++j) {
+        const int p = pb0 + 16 * (tbase + j) + m;
+        const float4 A4 = *reinterpret_cast<const float4*>(gt + (int64_t)p * a.kpad + 16 * g + 4 * q);
+        acc[j] = mfma_f32(A4.x, B4.x, acc[j]);
+        acc[j] = mfma_f32(A4.y, B4.y, acc[j]);
+        acc[j] = mfma_f32(A4.z, B4.z, acc[j]);
+        acc[j] = mfma_f32(A4.w, B4.w, acc[j]);
+      }
+    }
+  }
+}
+
+// Point-group bookkeeping shared by both epilogues
+struct GroupPos {
+  int b;
+  int64_t p0, gline;  // first point, global line index b * lines + line
+  int pb0;            // position of p0 inside its line
+};
+
+__device__ __forceinline__ GroupPos group_pos(const EpiArgs& a, int64_t pg) {
+  const int64_t pg_per_b = a.P / PG;
+  GroupPos r;
+  r.b = (int)(pg / pg_per_b);
+  r.p0 = (pg - (int64_t)r.b * pg_per_b) * PG;
+  const int64_t line = r.p0 / a.Nb;
+  r.pb0 = (int)(r.p0 - line * a.Nb);
+  r.gline = (int64_t)r.b * a.lines + line;
+  return r;
+}
+
 // ------------------------------------------------------------------------------------------
+// Forward.  The 4 waves split the (channel tile x point M-tile) output tiles of a group:
+// wave w owns channel tile ct = w % NT and M-tiles tbase .. tbase + NT - 1.
 template <int C, bool BF>
 __global__ void __launch_bounds__(256) k_epi_fwd_fast(EpiArgs a) {
-  constexpr int TM = 4;
   constexpr int CP = (C + 15) / 16 * 16;
   constexpr int NT = CP / 16;
-  __shared__ float s_wbt[C * CP];  // Wb^T[i][o], o padded with zeros
+  constexpr int TMW = NT;
+  constexpr int NPT = NT;  // float4 of the x tile per thread
+  __shared__ __attribute__((aligned(16))) float s_x[CP * XS];
+  __shared__ __attribute__((aligned(16))) unsigned char s_tl[CP * (kMaxKpad + 8) * 4];
   __shared__ float s_bias[CP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, q = lane >> 4;
-  if (a.block) {
-    for (int e = tid; e < C * CP; e += 256) {
-      const int i = e / CP, o = e - i * CP;
-      s_wbt[e] = (o < C) ? a.wb[o * C + i] : 0.f;
-    }
-    for (int o = tid; o < CP; o += 256) s_bias[o] = (o < C && a.bias) ? a.bias[o] : 0.f;
+  const int ct = wave % NT, tbase = (wave / NT) * TMW;
+  // Wb^T slice: B operand of K-step kb, lane (n = m, q): Wb[16 ct + m][4 kb + q]
+  float wbr[C / 4];
+  {
+    const int o = 16 * ct + m;
+#pragma unroll
+    for (int kb = 0; kb < C / 4; ++kb)
+      wbr[kb] = (a.block && o < C) ? a.wb[o * C + 4 * kb + q] : 0.f;
   }
-  __syncthreads();
-  const int64_t pg_per_b = a.P / (16 * TM);
+  for (int o = tid; o < CP; o += 256) s_bias[o] = (a.block && o < C && a.bias) ? a.bias[o] : 0.f;
   const int64_t g_begin = (int64_t)blockIdx.x * a.pg_per_wg;
   const int64_t g_end = min(a.npg, g_begin + a.pg_per_wg);
-  for (int64_t pg = g_begin + wave; pg < g_end; pg += 4) {
-    const int b = (int)(pg / pg_per_b);
-    const int64_t p0 = (pg - (int64_t)b * pg_per_b) * (16 * TM);
-    const int64_t line = p0 / a.Nb;
-    const int pb0 = (int)(p0 - line * a.Nb);
-    f32x4 acc[TM][NT];
+  float4 pre[NPT];
+  auto load_x = [&](int64_t pg) {
+    const GroupPos gp = group_pos(a, pg);
 #pragma unroll
-    for (int t = 0; t < TM; ++t)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[t][nt] = zero4();
-    const float2* Trow0 = a.T + ((int64_t)b * C * a.lines + line) * a.mb;
-    spectral_part<C, TM, BF>(a, Trow0, pb0, m, q, acc);
+    for (int u = 0; u < NPT; ++u) {
+      const int e = tid + 256 * u;
+      const int c = e >> 4, c4 = e & 15;
+      pre[u] = (c < C) ? *reinterpret_cast<const float4*>(a.x + ((int64_t)gp.b * C + c) * a.P +
+                                                          gp.p0 + 4 * c4)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  if (a.block && g_begin < g_end) load_x(g_begin);
+  int64_t cur_line = -1;
+  for (int64_t pg = g_begin; pg < g_end; ++pg) {
+    const GroupPos gp = group_pos(a, pg);
+    __syncthreads();  // previous group's readers are done
+    if (gp.gline != cur_line) {
+      const float2* Trow0 = a.T + ((int64_t)gp.b * C * a.lines + (gp.gline - (int64_t)gp.b * a.lines)) * a.mb;
+      stage_line<C, BF>(a, Trow0, s_tl, tid);
+      cur_line = gp.gline;
+    }
     if (a.block) {
-      const float* xb = a.x + (int64_t)b * C * a.P + p0 + TM * m;
-      float4 X[C / 4];
+#pragma unroll
+      for (int u = 0; u < NPT; ++u) {
+        const int e = tid + 256 * u;
+        *reinterpret_cast<float4*>(s_x + (e >> 4) * XS + 4 * (e & 15)) = pre[u];
+      }
+      if (pg + 1 < g_end) load_x(pg + 1);
+    }
+    __syncthreads();
+    f32x4 acc[TMW];
+#pragma unroll
+    for (int j = 0; j < TMW; ++j) acc[j] = zero4();
+    spectral_coop<C, TMW, BF>(a, s_tl, gp.pb0, ct, tbase, m, q, acc);
+    if (a.block) {
 #pragma unroll
       for (int kb = 0; kb < C / 4; ++kb)
-        X[kb] = *reinterpret_cast<const float4*>(xb + (int64_t)(4 * kb + q) * a.P);
 #pragma unroll
-      for (int kb = 0; kb < C / 4; ++kb) {
-        float bw[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) bw[nt] = s_wbt[(4 * kb + q) * CP + 16 * nt + m];
-#pragma unroll
-        for (int t = 0; t < TM; ++t)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) acc[t][nt] = mfma_f32(comp(X[kb], t), bw[nt], acc[t][nt]);
-      }
+        for (int j = 0; j < TMW; ++j)
+          acc[j] = mfma_f32(s_x[(4 * kb + q) * XS + 16 * (tbase + j) + m], wbr[kb], acc[j]);
     }
-    // lane (n = m, q): channel o = 16 nt + m, points p0 + 16 q + 4 r + t
+    // lane (n = m, q): channel 16 ct + m, points 16 t + 4 q + r
+    const int o = 16 * ct + m;
+    if (o < C) {
+      const float bo = s_bias[o];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int o = 16 * nt + m;
-      if (o >= C) continue;
-      const float bo = a.block ? s_bias[o] : 0.f;
-      const int64_t base = ((int64_t)b * C + o) * a.P + p0 + 16 * q;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float4 v = make_float4(acc[0][nt][r] + bo, acc[1][nt][r] + bo, acc[2][nt][r] + bo,
-                               acc[3][nt][r] + bo);
-        if (a.z) *reinterpret_cast<float4*>(a.z + base + 4 * r) = v;
+      for (int j = 0; j < TMW; ++j) {
+        const int64_t off = ((int64_t)gp.b * C + o) * a.P + gp.p0 + 16 * (tbase + j) + 4 * q;
+        float4 v = make_float4(acc[j][0] + bo, acc[j][1] + bo, acc[j][2] + bo, acc[j][3] + bo);
+        if (a.z) *reinterpret_cast<float4*>(a.z + off) = v;
         if (a.block && a.gelu) {
           v.x = gelu_fast(v.x);
           v.y = gelu_fast(v.y);
           v.z = gelu_fast(v.z);
           v.w = gelu_fast(v.w);
         }
-        *reinterpret_cast<float4*>(a.y + base + 4 * r) = v;
+        *reinterpret_cast<float4*>(a.y + off) = v;
       }
     }
   }
 }
 
 // ------------------------------------------------------------------------------------------
-// Backward.  Channel-major register tiles: lane (m, q) holds channel 16*ct + m at the 4*TM
-// consecutive points p0 + 4*TM*q + u, u = 0 .. 4*TM-1 (TM float4s).
+// Backward.  Same tile split for grad_x; the bypass-weight gradient tiles are split too:
+// NT = 4: wave w owns dWb rows 16 w .. (all columns); NT = 2: tile (w >> 1, w & 1);
+// NT = 1: every wave sums a quarter of the points of the single tile.
 template <int C, bool BF, bool TANH>
 __global__ void __launch_bounds__(256) k_epi_bwd_fast(EpiArgs a) {
-  constexpr int TM = 2;
-  constexpr int PG = 16 * TM;      // points per group
-  constexpr int PPL = 4 * TM;      // points per lane
   constexpr int CP = (C + 15) / 16 * 16;
   constexpr int NT = CP / 16;
-  constexpr int GZS = PG + 4;      // row stride of the transpose buffer (floats)
-  constexpr int kGz = 4 * C * GZS;         // per-wave g_z[o][point] transpose tiles
-  constexpr int kRed = C * CP + 16 * CP;   // work-group reduction (reuses the same LDS)
-  __shared__ float s_wb[C * CP];           // Wb[o][i], i padded with zeros
-  __shared__ float s_buf[kGz > kRed ? kGz : kRed];
-  float* s_red = s_buf;
+  constexpr int TMW = NT;
+  constexpr int NPT = NT;
+  constexpr int DT = (NT == 4) ? 4 : 1;  // dWb tiles per wave
+  __shared__ __attribute__((aligned(16))) float s_gz[CP * XS];
+  __shared__ __attribute__((aligned(16))) float s_x[CP * XS];
+  __shared__ __attribute__((aligned(16))) unsigned char s_tl[CP * (kMaxKpad + 8) * 4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, q = lane >> 4;
-  if (a.block)
-    for (int e = tid; e < C * CP; e += 256) {
-      const int o = e / CP, i = e - o * CP;
-      s_wb[e] = (i < C) ? a.wb[o * C + i] : 0.f;
-    }
-  __syncthreads();
-  f32x4 dwb[NT][NT];
-  float dbl[NT];
-#pragma unroll
-  for (int u = 0; u < NT; ++u) {
-    dbl[u] = 0.f;
-#pragma unroll
-    for (int v = 0; v < NT; ++v) dwb[u][v] = zero4();
-  }
-  float* gzw = s_buf + wave * C * GZS;
+  const int ct = wave % NT, tbase = (wave / NT) * TMW;
   const bool want_gx = a.y != nullptr;
-  const int64_t pg_per_b = a.P / PG;
+  const bool need_x = a.block || TANH;
+  // GEMM1 B operand, K-step kb, lane (n = m, q): Wb[o = 4 kb + q][i = 16 ct + m]
+  float wbr[C / 4];
+  {
+    const int i = 16 * ct + m;
+#pragma unroll
+    for (int kb = 0; kb < C / 4; ++kb)
+      wbr[kb] = (a.block && i < C) ? a.wb[(4 * kb + q) * C + i] : 0.f;
+  }
+  const int mo = (NT == 4) ? wave : (NT == 2 ? (wave >> 1) : 0);
+  const int ni0 = (NT == 2) ? (wave & 1) : 0;
+  const bool count_db = (NT != 2) || ((wave & 1) == 0);
+  f32x4 dwb[DT];
+#pragma unroll
+  for (int u = 0; u < DT; ++u) dwb[u] = zero4();
+  float dbl = 0.f;
   const int64_t g_begin = (int64_t)blockIdx.x * a.pg_per_wg;
   const int64_t g_end = min(a.npg, g_begin + a.pg_per_wg);
-  for (int64_t pg = g_begin + wave; pg < g_end; pg += 4) {
-    const int b = (int)(pg / pg_per_b);
-    const int64_t p0 = (pg - (int64_t)b * pg_per_b) * PG;
-    const int64_t line = p0 / a.Nb;
-    const int pb0 = (int)(p0 - line * a.Nb);
-    f32x4 acc[TM][NT];
+  float4 pg_y[NPT], pz[NPT], px[NPT];
+#define FNO_LOAD_TILES(PGI)                                                                    \
+  {                                                                                            \
+    const GroupPos lp = group_pos(a, (PGI));                                                   \
+    _Pragma("unroll") for (int u = 0; u < NPT; ++u) {                                          \
+      const int e = tid + 256 * u;                                                             \
+      const int c = e >> 4, c4 = e & 15;                                                       \
+      const int64_t off = ((int64_t)lp.b * C + c) * a.P + lp.p0 + 4 * c4;                      \
+      const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);                                     \
+      pg_y[u] = (a.block && c < C) ? *reinterpret_cast<const float4*>(a.gy + off) : zero;      \
+      pz[u] = (a.block && a.gelu && c < C) ? *reinterpret_cast<const float4*>(a.zin + off)     \
+                                          : zero;                                             \
+      px[u] = (need_x && c < C) ? *reinterpret_cast<const float4*>(a.x + off) : zero;          \
+    }                                                                                          \
+  }
+  if (g_begin < g_end) FNO_LOAD_TILES(g_begin);
+  int64_t cur_line = -1;
+  for (int64_t pg = g_begin; pg < g_end; ++pg) {
+    const GroupPos gp = group_pos(a, pg);
+    __syncthreads();
+    if (want_gx && gp.gline != cur_line) {
+      const float2* Trow0 = a.T + ((int64_t)gp.b * C * a.lines + (gp.gline - (int64_t)gp.b * a.lines)) * a.mb;
+      stage_line<C, BF>(a, Trow0, s_tl, tid);
+      cur_line = gp.gline;
+    }
 #pragma unroll
-    for (int t = 0; t < TM; ++t)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[t][nt] = zero4();
+    for (int u = 0; u < NPT; ++u) {
+      const int e = tid + 256 * u;
+      const int c = e >> 4, c4 = e & 15;
+      float4 g = pg_y[u];
+      if (a.gelu) {
+        g.x *= gelu_grad_fast(pz[u].x);
+        g.y *= gelu_grad_fast(pz[u].y);
+        g.z *= gelu_grad_fast(pz[u].z);
+        g.w *= gelu_grad_fast(pz[u].w);
+      }
+      *reinterpret_cast<float4*>(s_gz + c * XS + 4 * c4) = g;
+      *reinterpret_cast<float4*>(s_x + c * XS + 4 * c4) = px[u];
+    }
+    if (pg + 1 < g_end) FNO_LOAD_TILES(pg + 1);
+    __syncthreads();
     if (want_gx) {
-      const float2* Trow0 = a.T + ((int64_t)b * C * a.lines + line) * a.mb;
-      spectral_part<C, TM, BF>(a, Trow0, pb0, m, q, acc);
-    }
-    // x, channel-major: X[ct][h] = x[16 ct + m][p0 + PPL q + 4 h .. +3]
-    float4 X[NT][TM];
-    const int64_t fb = (int64_t)b * C * a.P + p0 + PPL * q;
+      f32x4 acc[TMW];
 #pragma unroll
-    for (int ct = 0; ct < NT; ++ct) {
-      const int c = 16 * ct + m;
+      for (int j = 0; j < TMW; ++j) acc[j] = zero4();
+      spectral_coop<C, TMW, BF>(a, s_tl, gp.pb0, ct, tbase, m, q, acc);
+      const int i = 16 * ct + m;
+      if (TANH) {
 #pragma unroll
-      for (int h = 0; h < TM; ++h)
-        X[ct][h] = (c < C && (TANH || a.block))
-                       ? *reinterpret_cast<const float4*>(a.x + fb + (int64_t)c * a.P + 4 * h)
-                           : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    if (TANH) {
-      // acc[t][nt][r] is channel 16 nt + m at point p0 + PPL q + TM r + t
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int t = 0; t < TM; ++t) {
-            const int u = TM * r + t;
-            const float th = tanhf(comp(X[nt][u >> 2], u & 3));
-            acc[t][nt][r] *= (1.f - th * th);
-          }
-    }
-    if (a.block) {
-      // g_z channel-major, then the bypass-weight gradient straight from registers
-      float4 GZ[NT][TM];
-#pragma unroll
-      for (int ct = 0; ct < NT; ++ct) {
-        const int o = 16 * ct + m;
-#pragma unroll
-        for (int h = 0; h < TM; ++h) {
-          float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (o < C) {
-            const int64_t off = fb + (int64_t)o * a.P + 4 * h;
-            g = *reinterpret_cast<const float4*>(a.gy + off);
-            if (a.gelu) {
-              const float4 zz = *reinterpret_cast<const float4*>(a.zin + off);
-              g.x *= gelu_grad_fast(zz.x);
-              g.y *= gelu_grad_fast(zz.y);
-              g.z *= gelu_grad_fast(zz.z);
-              g.w *= gelu_grad_fast(zz.w);
-            }
-            *reinterpret_cast<float4*>(gzw + o * GZS + PPL * q + 4 * h) = g;
-          }
-          GZ[ct][h] = g;
-          dbl[ct] += (g.x + g.y) + (g.z + g.w);
+        for (int j = 0; j < TMW; ++j) {
+          const float4 xv = *reinterpret_cast<const float4*>(s_x + i * XS + 16 * (tbase + j) + 4 * q);
+          const float t0 = tanhf(xv.x), t1 = tanhf(xv.y), t2 = tanhf(xv.z), t3 = tanhf(xv.w);
+          acc[j][0] *= 1.f - t0 * t0;
+          acc[j][1] *= 1.f - t1 * t1;
+          acc[j][2] *= 1.f - t2 * t2;
+          acc[j][3] *= 1.f - t3 * t3;
         }
       }
-      // dWb[o][i] += sum_u GZ(o, u) X(i, u): K-step u takes point p0 + PPL q + u
+      if (a.block) {
 #pragma unroll
-      for (int u = 0; u < PPL; ++u)
+        for (int kb = 0; kb < C / 4; ++kb)
 #pragma unroll
-        for (int mo = 0; mo < NT; ++mo)
-#pragma unroll
-          for (int ni = 0; ni < NT; ++ni)
-            dwb[mo][ni] = mfma_f32(comp(GZ[mo][u >> 2], u & 3), comp(X[ni][u >> 2], u & 3),
-                                   dwb[mo][ni]);
-      // the transposed g_z tile must be complete before this wave reads it back
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // grad_x^T[p][i] += sum_o g_z^T[p][o] Wb[o][i]; A: lane (m, q) = g_z[4kb+q][TM m + t]
-#pragma unroll
-      for (int kb = 0; kb < C / 4 && want_gx; ++kb) {
-        const int o = 4 * kb + q;
-        float At[TM];
-#pragma unroll
-        for (int t = 0; t < TM; ++t) At[t] = gzw[o * GZS + TM * m + t];
-        float bw[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) bw[nt] = s_wb[o * CP + 16 * nt + m];
-#pragma unroll
-        for (int t = 0; t < TM; ++t)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) acc[t][nt] = mfma_f32(At[t], bw[nt], acc[t][nt]);
+          for (int j = 0; j < TMW; ++j)
+            acc[j] = mfma_f32(s_gz[(4 * kb + q) * XS + 16 * (tbase + j) + m], wbr[kb], acc[j]);
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (i < C) {
+#pragma unroll
+        for (int j = 0; j < TMW; ++j) {
+          const int64_t off = ((int64_t)gp.b * C + i) * a.P + gp.p0 + 16 * (tbase + j) + 4 * q;
+          *reinterpret_cast<float4*>(a.y + off) =
+              make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+        }
+      }
     }
-    // grad_x: lane (m, q), channel 16 nt + m, points p0 + PPL q + TM r + t
+    if (a.block) {
+      // dWb[o][i] += sum_points g_z[o][p] x[i][p]; k-slot q of MFMA jj <-> point 16 g + 4 q + jj
+      const int g_lo = (NT == 1) ? wave : 0;
+      const int g_hi = (NT == 1) ? wave + 1 : PG / 16;
+      for (int g = g_lo; g < g_hi; ++g) {
+        const float4 av = *reinterpret_cast<const float4*>(s_gz + (16 * mo + m) * XS + 16 * g + 4 * q);
+        if (count_db) dbl += (av.x + av.y) + (av.z + av.w);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int i = 16 * nt + m;
-      if (i >= C || !want_gx) continue;
-      float v[PPL];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int t = 0; t < TM; ++t) v[TM * r + t] = acc[t][nt][r];
-      float* dst = a.y + fb + (int64_t)i * a.P;
-#pragma unroll
-      for (int h = 0; h < TM; ++h)
-        *reinterpret_cast<float4*>(dst + 4 * h) =
-            make_float4(v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]);
+        for (int u = 0; u < DT; ++u) {
+          const int ni = (NT == 4) ? u : ni0;
+          const float4 bv = *reinterpret_cast<const float4*>(s_x + (16 * ni + m) * XS + 16 * g + 4 * q);
+          dwb[u] = mfma_f32(av.x, bv.x, dwb[u]);
+          dwb[u] = mfma_f32(av.y, bv.y, dwb[u]);
+          dwb[u] = mfma_f32(av.z, bv.z, dwb[u]);
+          dwb[u] = mfma_f32(av.w, bv.w, dwb[u]);
+        }
+      }
     }
   }
+#undef FNO_LOAD_TILES
   if (!a.block || !a.part) return;
-  __syncthreads();  // every wave is done with its transpose tile before s_red reuses it
-  // Deterministic work-group reduction: waves add their partials in order 0..3.
-  // dwb[mo][ni][r] is dWb[16 mo + 4 q + r][16 ni + m]; dbl[ct] is a partial of dbias[16 ct + m].
+  // Deterministic work-group reduction (fixed wave order) into LDS, then one partial row.
+  float* s_red = s_gz;             // [C][CP] dWb
+  float* s_db = s_x;               // [4 waves][4 q][CP] dbias partials
+  __syncthreads();
+  for (int e = tid; e < C * CP; e += 256) s_red[e] = 0.f;
+  for (int e = tid; e < 16 * CP; e += 256) s_db[e] = 0.f;
+  __syncthreads();
   for (int w = 0; w < 4; ++w) {
     if (wave == w) {
 #pragma unroll
-      for (int mo = 0; mo < NT; ++mo)
+      for (int u = 0; u < DT; ++u) {
+        const int ni = (NT == 4) ? u : ni0;
 #pragma unroll
-        for (int ni = 0; ni < NT; ++ni)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int e = (16 * mo + 4 * q + r) * CP + 16 * ni + m;
-            if (16 * mo + 4 * q + r < C)
-              s_red[e] = (w == 0 ? 0.f : s_red[e]) + dwb[mo][ni][r];
-          }
-#pragma unroll
-      for (int ct = 0; ct < NT; ++ct) s_red[C * CP + (w * 4 + q) * CP + 16 * ct + m] = dbl[ct];
+        for (int r = 0; r < 4; ++r) {
+          const int o = 16 * mo + 4 * q + r, i = 16 * ni + m;
+          if (o < C) s_red[o * CP + i] += dwb[u][r];
+        }
+      }
+      s_db[(w * 4 + q) * CP + 16 * mo + m] += dbl;
     }
     __syncthreads();
   }
@@ -377,7 +398,7 @@ __global__ void __launch_bounds__(256) k_epi_bwd_fast(EpiArgs a) {
     } else {
       const int o = e - C * C;
       v = 0.f;
-      for (int k = 0; k < 16; ++k) v += s_red[C * CP + k * CP + o];
+      for (int k = 0; k < 16; ++k) v += s_db[k * CP + o];
     }
     dst[e] = v;
   }
@@ -413,8 +434,8 @@ bool epilogue_fast_ok(const fno_plan* p, int mode, bool fwd) {
   const Geom& g = p->g;
   const int C = fwd ? g.Cout : g.Cin;
   if (mode == EPI_BLOCK && g.Cin != g.Cout) return false;
-  if (!(C == 16 || C == 20 || C == 32 || C == 48 || C == 64)) return false;
-  if (g.Nb % 64 != 0 || g.mb % 2 != 0) return false;
+  if (!(C == 16 || C == 20 || C == 32 || C == 64)) return false;
+  if (g.Nb % 64 != 0 || g.mb % 2 != 0 || p->kpad > kMaxKpad) return false;
   return true;
 }
 
@@ -433,7 +454,9 @@ static EpiArgs make_args(const fno_plan* p, int C, int pg_points, int wgs_cap, i
   if (w > wgs_cap) w = wgs_cap;
   if (w < 1) w = 1;
   a.pg_per_wg = (a.npg + w - 1) / w;
-  a.pg_per_wg = (a.pg_per_wg + 3) / 4 * 4;
+  int64_t per_line = g.Nb / pg_points;  // keep whole lines in one work-group
+  if (per_line < 1) per_line = 1;
+  a.pg_per_wg = (a.pg_per_wg + per_line - 1) / per_line * per_line;
   *wgs = (int)((a.npg + a.pg_per_wg - 1) / a.pg_per_wg);
   return a;
 }
@@ -443,7 +466,7 @@ hipError_t launch_epilogue_fwd_fast(const fno_plan* p, int mode, const float2* T
                                     hipStream_t s) {
   const Geom& g = p->g;
   int wgs = 0;
-  EpiArgs a = make_args(p, g.Cout, 64, 1024, &wgs);
+  EpiArgs a = make_args(p, g.Cout, PG, 1024, &wgs);
   a.x = x;
   a.T = T;
   a.wb = wb;
@@ -457,14 +480,14 @@ hipError_t launch_epilogue_fwd_fast(const fno_plan* p, int mode, const float2* T
     case 16: return launch_fwd_c<16>(a, g.bf16, wgs, s);
     case 20: return launch_fwd_c<20>(a, g.bf16, wgs, s);
     case 32: return launch_fwd_c<32>(a, g.bf16, wgs, s);
-    case 48: return launch_fwd_c<48>(a, g.bf16, wgs, s);
     default: return launch_fwd_c<64>(a, g.bf16, wgs, s);
   }
 }
 
 int epilogue_bwd_fast_groups(const fno_plan* p) {
+  if (!epilogue_fast_ok(p, EPI_BLOCK, false)) return 0;
   int wgs = 0;
-  (void)make_args(p, p->g.Cin, 32, 512, &wgs);
+  (void)make_args(p, p->g.Cin, PG, 1024, &wgs);
   return wgs;
 }
 
@@ -474,7 +497,7 @@ hipError_t launch_epilogue_bwd_fast(const fno_plan* p, int mode, const float2* T
                                     hipStream_t s) {
   const Geom& g = p->g;
   int wgs = 0;
-  EpiArgs a = make_args(p, g.Cin, 32, 512, &wgs);
+  EpiArgs a = make_args(p, g.Cin, PG, 1024, &wgs);
   a.x = x;
   a.T = Tg;
   a.wb = wb;
@@ -490,7 +513,6 @@ hipError_t launch_epilogue_bwd_fast(const fno_plan* p, int mode, const float2* T
     case 16: return launch_bwd_c<16>(a, g.bf16, tanh_pre, wgs, s);
     case 20: return launch_bwd_c<20>(a, g.bf16, tanh_pre, wgs, s);
     case 32: return launch_bwd_c<32>(a, g.bf16, tanh_pre, wgs, s);
-    case 48: return launch_bwd_c<48>(a, g.bf16, tanh_pre, wgs, s);
     default: return launch_bwd_c<64>(a, g.bf16, tanh_pre, wgs, s);
   }
 }

@@ -226,6 +226,7 @@ hipError_t launch_outer_fwd(const fno_plan* p, int axis, int chans, const float2
                             int nparts, int64_t part_stride, float2* out, hipStream_t s) {
   (void)nparts;
   (void)part_stride;
+  if (outer_fast_ok(p, axis, false)) return launch_outer_mfma(p, axis, chans, false, in, out, s);
   const Geom& g = p->g;
   int64_t pre, post;
   outer_shape(p, axis, chans, false, &pre, &post);
@@ -238,6 +239,7 @@ hipError_t launch_outer_fwd(const fno_plan* p, int axis, int chans, const float2
 
 hipError_t launch_outer_inv(const fno_plan* p, int axis, int chans, const float2* in,
                             float2* out, hipStream_t s) {
+  if (outer_fast_ok(p, axis, true)) return launch_outer_mfma(p, axis, chans, true, in, out, s);
   const Geom& g = p->g;
   int64_t pre, post;
   outer_shape(p, axis, chans, true, &pre, &post);

@@ -263,6 +263,25 @@ fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out) {
   toff += align_up(sizeof(uint16_t) * f2_elems);
   const size_t f2_bf_lo_off = toff;
   toff += align_up(sizeof(uint16_t) * f2_elems);
+  // outer-axis twiddle matrices (axes 0..d-2), rows padded to 16, K halves padded to 16
+  size_t oinv_off[fno::kMaxDims][3] = {}, ofwd_off[fno::kMaxDims][3] = {};
+  auto p16 = [](int v) { return (v + 15) / 16 * 16; };
+  for (int j = 0; j <= g.d - 2; ++j) {
+    const size_t ni = (size_t)p16(g.N[j]) * 2 * p16(2 * g.M[j]);
+    const size_t nf = (size_t)p16(2 * g.M[j]) * 2 * p16(g.N[j]);
+    oinv_off[j][0] = toff;
+    toff += align_up(sizeof(float) * ni);
+    oinv_off[j][1] = toff;
+    toff += align_up(sizeof(uint16_t) * ni);
+    oinv_off[j][2] = toff;
+    toff += align_up(sizeof(uint16_t) * ni);
+    ofwd_off[j][0] = toff;
+    toff += align_up(sizeof(float) * nf);
+    ofwd_off[j][1] = toff;
+    toff += align_up(sizeof(uint16_t) * nf);
+    ofwd_off[j][2] = toff;
+    toff += align_up(sizeof(uint16_t) * nf);
+  }
   const size_t woff_mode_elems = (size_t)g.ncorner * g.Mprod;
   const size_t mode_woff_off = toff;
   toff += align_up(sizeof(int32_t) * (size_t)g.K);
@@ -340,6 +359,27 @@ fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out) {
       }
     }
   }
+  for (int j = 0; j <= g.d - 2; ++j) {
+    const int N = g.N[j], m = g.M[j];
+    const int Np = p16(N), Mp = p16(2 * m);
+    auto put = [&](size_t* off, size_t e, double v) {
+      reinterpret_cast<float*>(host.data() + off[0])[e] = (float)v;
+      const uint16_t hi = bf16_bits_host(v);
+      reinterpret_cast<uint16_t*>(host.data() + off[1])[e] = hi;
+      reinterpret_cast<uint16_t*>(host.data() + off[2])[e] = bf16_bits_host(v - bf16_value_host(hi));
+    };
+    for (int pt = 0; pt < N; ++pt)
+      for (int sidx = 0; sidx < 2 * m; ++sidx) {
+        const int k = sidx < m ? sidx : N - 2 * m + sidx;
+        const double ang = 2.0 * M_PI * (double)(((int64_t)k * pt) % N) / (double)N;
+        // inverse: row pt, K = [cos | sin] over retained positions
+        put(oinv_off[j], (size_t)pt * 2 * Mp + sidx, cos(ang));
+        put(oinv_off[j], (size_t)pt * 2 * Mp + Mp + sidx, sin(ang));
+        // forward: row sidx, K = [cos | -sin] over grid points
+        put(ofwd_off[j], (size_t)sidx * 2 * Np + pt, cos(ang));
+        put(ofwd_off[j], (size_t)sidx * 2 * Np + Np + pt, -sin(ang));
+      }
+  }
   {
     int32_t* mw = reinterpret_cast<int32_t*>(host.data() + mode_woff_off);
     int32_t* wm = reinterpret_cast<int32_t*>(host.data() + woff_mode_off);
@@ -400,6 +440,14 @@ fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out) {
   p->t.f2 = reinterpret_cast<const float*>(base + f2_off);
   p->t.f2_bf = reinterpret_cast<const uint16_t*>(base + f2_bf_off);
   p->t.f2_bf_lo = reinterpret_cast<const uint16_t*>(base + f2_bf_lo_off);
+  for (int j = 0; j <= g.d - 2; ++j) {
+    p->t.oinv[j] = reinterpret_cast<const float*>(base + oinv_off[j][0]);
+    p->t.oinv_bf[j] = reinterpret_cast<const uint16_t*>(base + oinv_off[j][1]);
+    p->t.oinv_bf_lo[j] = reinterpret_cast<const uint16_t*>(base + oinv_off[j][2]);
+    p->t.ofwd[j] = reinterpret_cast<const float*>(base + ofwd_off[j][0]);
+    p->t.ofwd_bf[j] = reinterpret_cast<const uint16_t*>(base + ofwd_off[j][1]);
+    p->t.ofwd_bf_lo[j] = reinterpret_cast<const uint16_t*>(base + ofwd_off[j][2]);
+  }
   p->t.mode_woff = reinterpret_cast<const int32_t*>(base + mode_woff_off);
   p->t.woff_mode = reinterpret_cast<const int32_t*>(base + woff_mode_off);
   *out = p;

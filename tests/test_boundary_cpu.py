@@ -92,3 +92,25 @@ def test_null_arguments_rejected_on_host():
 def test_status_strings():
     for s in range(6):
         assert L.status_string(s).startswith("FNO_")
+
+
+@pytest.mark.parametrize("kw", [
+    dict(), dict(grid=(24, 20), modes=(5, 4), c_in=3, c_out=5),
+    dict(grid=(15, 9), modes=(7, 5)), dict(grid=(8, 8), modes=(4, 5)),
+    dict(grid=(64, 512), modes=(8, 32), c_in=64, c_out=64, dtype=1, flags=7),
+    dict(grid=(12, 10, 16), modes=(3, 2, 5)), dict(grid=(10, 12, 64), modes=(3, 4, 8)),
+    dict(grid=(6, 8, 10, 20), modes=(2, 3, 4, 8), batch=1),
+    dict(grid=(128, 128, 128, 20), modes=(12, 12, 12, 8), batch=1),
+    dict(grid=(512, 512), modes=(32, 32), c_in=64, c_out=64, batch=8, dtype=1, flags=7),
+    dict(grid=(16, 32), modes=(1, 1), c_in=1, c_out=1),
+])
+def test_plan_create_host_logic(kw):
+    """fno_plan_create runs its whole host-side part (geometry, chunking, workspace sizing,
+    float64 table build) before its first HIP call; without a GPU it must then fail cleanly
+    with FNO_ERR_HIP, never crash."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: plan creation succeeds instead")
+    with pytest.raises(L.FnoError) as ei:
+        L.fno_plan_create(_desc(**kw))
+    assert ei.value.status == L.FNO_ERR_HIP
