@@ -251,145 +251,6 @@ hipError_t launch_outer_inv(const fno_plan* p, int axis, int chans, const float2
 }
 
 // ------------------------------------------------------------------------------------------
-// Channel mix.  Mode t of [B][C][K]; W element (c, i, o, kappa) at
-// mode_woff[t] + (i * Cout + o) * Mprod.
-__global__ void k_mix_fwd(Geom g, const int32_t* __restrict__ mode_woff,
-                          const float2* __restrict__ xhat, const float2* __restrict__ w,
-                          float2* __restrict__ yhat) {
-  const int64_t K = g.K;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)g.Cout * K) return;
-  const int o = (int)(i / K);
-  const int64_t t = i - (int64_t)o * K;
-  const int64_t wbase = mode_woff[t] + (int64_t)o * g.Mprod;
-  const int64_t wstride = (int64_t)g.Cout * g.Mprod;
-  const bool bf = g.bf16;
-  for (int b0 = 0; b0 < g.B; b0 += kMaxBatchTile) {
-    const int nb = min(kMaxBatchTile, g.B - b0);
-    float2 acc[kMaxBatchTile];
-#pragma unroll
-    for (int b = 0; b < kMaxBatchTile; ++b) acc[b] = make_float2(0.f, 0.f);
-    for (int ci = 0; ci < g.Cin; ++ci) {
-      const float2 wv = w[wbase + ci * wstride];
-      const float wr = opnd(wv.x, bf), wi = opnd(wv.y, bf);
-#pragma unroll
-      for (int b = 0; b < kMaxBatchTile; ++b) {
-        if (b < nb) {
-          const float2 xv = xhat[((int64_t)(b0 + b) * g.Cin + ci) * K + t];
-          const float xr = opnd(xv.x, bf), xi = opnd(xv.y, bf);
-          acc[b].x += xr * wr - xi * wi;
-          acc[b].y += xr * wi + xi * wr;
-        }
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < kMaxBatchTile; ++b)
-      if (b < nb) yhat[((int64_t)(b0 + b) * g.Cout + o) * K + t] = acc[b];
-  }
-}
-
-hipError_t launch_mix_fwd(const fno_plan* p, const float2* xhat, int nparts,
-                          int64_t part_stride, const float2* w, float2* yhat, hipStream_t s) {
-  (void)nparts;
-  (void)part_stride;
-  const Geom& g = p->g;
-  const int64_t total = (int64_t)g.Cout * g.K;
-  hipLaunchKernelGGL(k_mix_fwd, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, g,
-                     p->t.mode_woff, xhat, w, yhat);
-  return hipGetLastError();
-}
-
-// ghat scale of the adjoint inverse: gamma(k_last) / Ntot
-__device__ __forceinline__ float adj_scale(const Geom& g, int64_t t) {
-  const int kb = (int)(t % g.mb);
-  const bool one = (kb == 0) || (2 * kb == g.Nb);
-  return (one ? 1.0f : 2.0f) * g.inv_ntot;
-}
-
-__global__ void k_mix_bwd_dx(Geom g, const int32_t* __restrict__ mode_woff,
-                             const float2* __restrict__ ghat, const float2* __restrict__ w,
-                             float2* __restrict__ ghx) {
-  const int64_t K = g.K;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)g.Cin * K) return;
-  const int ci = (int)(i / K);
-  const int64_t t = i - (int64_t)ci * K;
-  const int64_t wbase = mode_woff[t] + (int64_t)ci * g.Cout * g.Mprod;
-  const float sc = adj_scale(g, t);
-  const bool bf = g.bf16;
-  for (int b0 = 0; b0 < g.B; b0 += kMaxBatchTile) {
-    const int nb = min(kMaxBatchTile, g.B - b0);
-    float2 acc[kMaxBatchTile];
-#pragma unroll
-    for (int b = 0; b < kMaxBatchTile; ++b) acc[b] = make_float2(0.f, 0.f);
-    for (int o = 0; o < g.Cout; ++o) {
-      const float2 wv = w[wbase + (int64_t)o * g.Mprod];
-      const float wr = opnd(wv.x, bf), wi = opnd(wv.y, bf);
-#pragma unroll
-      for (int b = 0; b < kMaxBatchTile; ++b) {
-        if (b < nb) {
-          const float2 gv = ghat[((int64_t)(b0 + b) * g.Cout + o) * K + t];
-          const float gr = opnd(gv.x * sc, bf), gi = opnd(gv.y * sc, bf);
-          // (gr + i gi) * conj(wr + i wi)
-          acc[b].x += gr * wr + gi * wi;
-          acc[b].y += gi * wr - gr * wi;
-        }
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < kMaxBatchTile; ++b)
-      if (b < nb) ghx[((int64_t)(b0 + b) * g.Cin + ci) * K + t] = acc[b];
-  }
-}
-
-hipError_t launch_mix_bwd_dx(const fno_plan* p, const float2* ghat, const float2* w,
-                             float2* ghx, hipStream_t s) {
-  const Geom& g = p->g;
-  const int64_t total = (int64_t)g.Cin * g.K;
-  hipLaunchKernelGGL(k_mix_bwd_dx, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, g,
-                     p->t.mode_woff, ghat, w, ghx);
-  return hipGetLastError();
-}
-
-__global__ void k_mix_bwd_dw(Geom g, const int32_t* __restrict__ woff_mode,
-                             const float2* __restrict__ xhat, const float2* __restrict__ ghat,
-                             float2* __restrict__ dw) {
-  const int64_t K = g.K;
-  const int64_t total = (int64_t)g.ncorner * g.Cin * g.Cout * g.Mprod;
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= total) return;
-  const int64_t kap = e % g.Mprod;
-  int64_t r = e / g.Mprod;
-  const int o = (int)(r % g.Cout);
-  r /= g.Cout;
-  const int ci = (int)(r % g.Cin);
-  const int c = (int)(r / g.Cin);
-  const int64_t t = woff_mode[(int64_t)c * g.Mprod + kap];
-  const float sc = adj_scale(g, t);
-  const bool bf = g.bf16;
-  float re = 0.f, im = 0.f;
-  for (int b = 0; b < g.B; ++b) {
-    const float2 xv = xhat[((int64_t)b * g.Cin + ci) * K + t];
-    const float2 gv = ghat[((int64_t)b * g.Cout + o) * K + t];
-    const float xr = opnd(xv.x, bf), xi = opnd(xv.y, bf);
-    const float gr = opnd(gv.x * sc, bf), gi = opnd(gv.y * sc, bf);
-    // conj(x) * g
-    re += xr * gr + xi * gi;
-    im += xr * gi - xi * gr;
-  }
-  dw[e] = make_float2(re, im);
-}
-
-hipError_t launch_mix_bwd_dw(const fno_plan* p, const float2* xhat, const float2* ghat,
-                             float2* dw, hipStream_t s) {
-  const Geom& g = p->g;
-  const int64_t total = (int64_t)g.ncorner * g.Cin * g.Cout * g.Mprod;
-  hipLaunchKernelGGL(k_mix_bwd_dw, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, g,
-                     p->t.woff_mode, xhat, ghat, dw);
-  return hipGetLastError();
-}
-
-// ------------------------------------------------------------------------------------------
 // Forward epilogue: y_spec from T [B][C][lines][mb] by the last-axis inverse (gamma/Ntot),
 // then (EPI_BLOCK) + Wb x + bias and GELU.  One thread per point, 256 points per group.
 constexpr int kEpiThreads = 128;
@@ -597,17 +458,36 @@ hipError_t launch_epilogue_bwd(const fno_plan* p, int mode, const float2* Tg, co
   return hipGetLastError();
 }
 
-__global__ void k_bypass_finish(const float* __restrict__ part, int nparts, int cout, int cin,
-                                float* __restrict__ dwb, float* __restrict__ dbias) {
+// Sum of the per-work-group bypass-gradient partials.  A group of 256 threads owns 64
+// consecutive entries; thread slice k (0..3) sums partials k, k+4, ... with 4 loads in
+// flight, and the slices are added in the fixed order 0, 1, 2, 3 (deterministic).
+__global__ void __launch_bounds__(256)
+k_bypass_finish(const float* __restrict__ part, int nparts, int cout, int cin,
+                float* __restrict__ dwb, float* __restrict__ dbias) {
+  __shared__ float s_sum[4][64];
   const int npair = cout * cin + cout;
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= npair) return;
-  float a = 0.f;
-  for (int q = 0; q < nparts; ++q) a += part[(int64_t)q * npair + e];
-  if (e < cout * cin) {
-    if (dwb) dwb[e] = a;
-  } else if (dbias) {
-    dbias[e - cout * cin] = a;
+  const int el = threadIdx.x & 63, slice = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + el;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  if (e < npair) {
+    int q = slice;
+    for (; q + 12 < nparts; q += 16) {
+      a0 += part[(int64_t)q * npair + e];
+      a1 += part[(int64_t)(q + 4) * npair + e];
+      a2 += part[(int64_t)(q + 8) * npair + e];
+      a3 += part[(int64_t)(q + 12) * npair + e];
+    }
+    for (; q < nparts; q += 4) a0 += part[(int64_t)q * npair + e];
+  }
+  s_sum[slice][el] = (a0 + a1) + (a2 + a3);
+  __syncthreads();
+  if (slice == 0 && e < npair) {
+    const float v = ((s_sum[0][el] + s_sum[1][el]) + s_sum[2][el]) + s_sum[3][el];
+    if (e < cout * cin) {
+      if (dwb) dwb[e] = v;
+    } else if (dbias) {
+      dbias[e - cout * cin] = v;
+    }
   }
 }
 
@@ -616,7 +496,7 @@ hipError_t launch_bypass_grad_finish(const fno_plan* p, const float* red_part, f
   const Geom& g = p->g;
   const int npair = g.Cout * g.Cin + g.Cout;
   const int nparts = epilogue_fast_ok(p, EPI_BLOCK, false) ? epilogue_bwd_fast_groups(p) : p->nred;
-  hipLaunchKernelGGL(k_bypass_finish, dim3((npair + 255) / 256), dim3(256), 0, s, red_part,
+  hipLaunchKernelGGL(k_bypass_finish, dim3((npair + 63) / 64), dim3(256), 0, s, red_part,
                      nparts, g.Cout, g.Cin, dwb, dbias);
   return hipGetLastError();
 }
@@ -682,7 +562,17 @@ __global__ void k_mse_part(int64_t n, const float* __restrict__ y, const float* 
   const int tid = threadIdx.x;
   const float sc = (float)(2.0 / (double)n);
   double a = 0.0;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + tid; i < n; i += (int64_t)gridDim.x * 256) {
+  const int64_t n4 = n / 4;
+  const float4* y4 = reinterpret_cast<const float4*>(y);
+  const float4* t4 = reinterpret_cast<const float4*>(t);
+  float4* g4 = reinterpret_cast<float4*>(g);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + tid; i < n4; i += (int64_t)gridDim.x * 256) {
+    const float4 yv = y4[i], tv = t4[i];
+    const float4 d = make_float4(yv.x - tv.x, yv.y - tv.y, yv.z - tv.z, yv.w - tv.w);
+    g4[i] = make_float4(sc * d.x, sc * d.y, sc * d.z, sc * d.w);
+    a += (double)(d.x * d.x + d.y * d.y) + (double)(d.z * d.z + d.w * d.w);
+  }
+  for (int64_t i = 4 * n4 + (int64_t)blockIdx.x * 256 + tid; i < n; i += (int64_t)gridDim.x * 256) {
     const float d = y[i] - t[i];
     g[i] = sc * d;
     a += (double)d * (double)d;
