@@ -38,7 +38,26 @@ def parse():
     ap.add_argument("--workload", default="c3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-batch", type=int, default=3)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device copy of this many bytes (counter calibration)")
     return ap.parse_args()
+
+
+def copy_calibration(nbytes: int, reps: int = 3):
+    """A plain device-to-device copy of a known size, used to scale the HBM byte counters."""
+    import torch
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    print(json.dumps({"kind": "copy", "bytes_read": 4 * n, "bytes_written": 4 * n,
+                      "launches": reps, "avg_ms": dt * 1e3,
+                      "GBps_rw": 8 * n / dt / 1e9}), flush=True)
 
 
 def kernel_model(wl, plan):
@@ -172,6 +191,9 @@ def cpu_baseline(wl, sample_batch):
 
 def main():
     args = parse()
+    if args.copy_bytes:
+        copy_calibration(args.copy_bytes)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
               "(the multi-GPU sharding is a design only).", file=sys.stderr, flush=True)

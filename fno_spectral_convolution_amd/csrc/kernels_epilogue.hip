@@ -180,9 +180,10 @@ __global__ void __launch_bounds__(256) k_epi_fwd_fast(EpiArgs a) {
     for (int u = 0; u < NPT; ++u) {
       const int e = tid + 256 * u;
       const int c = e >> 4, c4 = e & 15;
-      pre[u] = (c < C) ? *reinterpret_cast<const float4*>(a.x + ((int64_t)gp.b * C + c) * a.P +
-                                                          gp.p0 + 4 * c4)
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
+      pre[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (c < C)
+        pre[u] = *reinterpret_cast<const float4*>(a.x + ((int64_t)gp.b * C + c) * a.P + gp.p0 +
+                                                  4 * c4);
     }
   };
   if (a.block && g_begin < g_end) load_x(g_begin);
@@ -236,6 +237,29 @@ __global__ void __launch_bounds__(256) k_epi_fwd_fast(EpiArgs a) {
   }
 }
 
+// Backward prefetch of one group: g_y, z and x rows of every channel (thread-strided float4s)
+template <int C, int NPT>
+__device__ __forceinline__ void load_bwd_tiles(const EpiArgs& a, int64_t pg, int tid, bool need_x,
+                                               float4 (&gy)[NPT], float4 (&zz)[NPT],
+                                               float4 (&xx)[NPT]) {
+  const GroupPos lp = group_pos(a, pg);
+  // explicit branches: a conditional between a global load and a local zero would otherwise
+  // be compiled as a select of addresses (a private copy of the zero and flat loads)
+#pragma unroll
+  for (int u = 0; u < NPT; ++u) {
+    const int e = tid + 256 * u;
+    const int c = e >> 4, c4 = e & 15;
+    const int64_t off = ((int64_t)lp.b * C + c) * a.P + lp.p0 + 4 * c4;
+    const bool in = c < C;
+    gy[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    zz[u] = gy[u];
+    xx[u] = gy[u];
+    if (a.block && in) gy[u] = *reinterpret_cast<const float4*>(a.gy + off);
+    if (a.block && a.gelu && in) zz[u] = *reinterpret_cast<const float4*>(a.zin + off);
+    if (need_x && in) xx[u] = *reinterpret_cast<const float4*>(a.x + off);
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 // Backward.  Same tile split for grad_x; the bypass-weight gradient tiles are split too:
 // NT = 4: wave w owns dWb rows 16 w .. (all columns); NT = 2: tile (w >> 1, w & 1);
@@ -273,21 +297,7 @@ __global__ void __launch_bounds__(256) k_epi_bwd_fast(EpiArgs a) {
   const int64_t g_begin = (int64_t)blockIdx.x * a.pg_per_wg;
   const int64_t g_end = min(a.npg, g_begin + a.pg_per_wg);
   float4 pg_y[NPT], pz[NPT], px[NPT];
-#define FNO_LOAD_TILES(PGI)                                                                    \
-  {                                                                                            \
-    const GroupPos lp = group_pos(a, (PGI));                                                   \
-    _Pragma("unroll") for (int u = 0; u < NPT; ++u) {                                          \
-      const int e = tid + 256 * u;                                                             \
-      const int c = e >> 4, c4 = e & 15;                                                       \
-      const int64_t off = ((int64_t)lp.b * C + c) * a.P + lp.p0 + 4 * c4;                      \
-      const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);                                     \
-      pg_y[u] = (a.block && c < C) ? *reinterpret_cast<const float4*>(a.gy + off) : zero;      \
-      pz[u] = (a.block && a.gelu && c < C) ? *reinterpret_cast<const float4*>(a.zin + off)     \
-                                          : zero;                                             \
-      px[u] = (need_x && c < C) ? *reinterpret_cast<const float4*>(a.x + off) : zero;          \
-    }                                                                                          \
-  }
-  if (g_begin < g_end) FNO_LOAD_TILES(g_begin);
+  if (g_begin < g_end) load_bwd_tiles<C, NPT>(a, g_begin, tid, need_x, pg_y, pz, px);
   int64_t cur_line = -1;
   for (int64_t pg = g_begin; pg < g_end; ++pg) {
     const GroupPos gp = group_pos(a, pg);
@@ -311,7 +321,7 @@ __global__ void __launch_bounds__(256) k_epi_bwd_fast(EpiArgs a) {
       *reinterpret_cast<float4*>(s_gz + c * XS + 4 * c4) = g;
       *reinterpret_cast<float4*>(s_x + c * XS + 4 * c4) = px[u];
     }
-    if (pg + 1 < g_end) FNO_LOAD_TILES(pg + 1);
+    if (pg + 1 < g_end) load_bwd_tiles<C, NPT>(a, pg + 1, tid, need_x, pg_y, pz, px);
     __syncthreads();
     if (want_gx) {
       f32x4 acc[TMW];
@@ -365,7 +375,6 @@ __global__ void __launch_bounds__(256) k_epi_bwd_fast(EpiArgs a) {
       }
     }
   }
-#undef FNO_LOAD_TILES
   if (!a.block || !a.part) return;
   // Deterministic work-group reduction (fixed wave order) into LDS, then one partial row.
   float* s_red = s_gz;             // [C][CP] dWb
