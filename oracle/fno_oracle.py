@@ -57,7 +57,8 @@ from scipy.special import erf as _erf
 
 __all__ = [
     "retained_indices", "dft_matrix", "gamma_weights", "spectrum", "expand_weights",
-    "fold_weights", "channel_mix", "inverse_spectrum", "adjoint_inverse", "gelu",
+    "fold_weights", "channel_mix", "inverse_spectrum", "inverse_at_points", "adjoint_inverse",
+    "gelu",
     "gelu_prime", "spectral_conv_fwd", "spectral_conv_bwd", "block_fwd", "block_bwd",
     "pointwise_linear", "projection_fwd", "mse_loss_grad", "stack_fwd", "train_step",
 ]
@@ -196,6 +197,28 @@ def inverse_spectrum(yhat: np.ndarray, shape, modes, unit_scale: bool = False) -
     return real * scale
 
 
+def inverse_at_points(yhat: np.ndarray, shape, modes, points) -> np.ndarray:
+    """F3 evaluated directly at given grid points (non-separable sum over every retained mode).
+
+    ``points`` is an int array [P, d]; returns [B, C, P].  Used to check outputs of fields too
+    large to invert whole.
+    """
+    d = len(shape)
+    pts = np.asarray(points, dtype=np.int64)
+    sets = [retained_indices(shape[j], modes[j], last=(j == d - 1)) for j in range(d)]
+    grids = np.meshgrid(*sets, indexing="ij")
+    ntot = float(np.prod(shape))
+    # phase[k, p] = 2 pi sum_j ((k_j p_j) mod N_j) / N_j
+    phase = np.zeros((grids[0].size, pts.shape[0]))
+    for j in range(d):
+        kp = np.outer(grids[j].ravel(), pts[:, j]) % shape[j]
+        phase += 2.0 * np.pi * kp / shape[j]
+    gam = np.broadcast_to(gamma_weights(shape[d - 1], modes[d - 1]), grids[0].shape).ravel()
+    yk = np.asarray(yhat, dtype=np.complex128).reshape(yhat.shape[0], yhat.shape[1], -1)
+    e = np.exp(1j * phase) * gam[:, None]
+    return np.real(np.tensordot(yk, e, axes=([2], [0]))) / ntot
+
+
 def adjoint_inverse(g: np.ndarray, modes) -> np.ndarray:
     """B2: ghat = (gamma(k_last)/Ntot) sum_p g exp(-i theta_k(p)), the adjoint of F3."""
     d = g.ndim - 2
@@ -225,8 +248,9 @@ def _bcast(v: np.ndarray, nd: int) -> np.ndarray:
 
 
 def _pointwise(wmat: np.ndarray, f: np.ndarray) -> np.ndarray:
-    """out[b,o,p] = sum_i wmat[o,i] f[b,i,p] (a 1x1 convolution)."""
-    return np.einsum("oi,bi...->bo...", np.asarray(wmat, dtype=np.float64), f)
+    """out[b,o,p] = sum_i wmat[o,i] f[b,i,p] (a 1x1 convolution), as one matrix product."""
+    out = np.tensordot(np.asarray(wmat, dtype=np.float64), f, axes=([1], [1]))
+    return np.moveaxis(out, 0, 1)
 
 
 # ----------------------------------------------------------------------------- spectral conv
@@ -279,7 +303,7 @@ def block_bwd(x, w, wb, bias, modes, g_y, tanh: bool = False, act: bool = True):
     fwd = block_fwd(x, w, wb, bias, modes, tanh=tanh, act=act)
     g_z = g_y * gelu_prime(fwd["z"]) if act else g_y
     sp = spectral_conv_bwd(x, w, modes, g_z, tanh=tanh)
-    grad_x = np.einsum("oi,bo...->bi...", np.asarray(wb, dtype=np.float64), g_z) + sp["grad_x"]
+    grad_x = _pointwise(np.asarray(wb, dtype=np.float64).T, g_z) + sp["grad_x"]
     red = (0,) + tuple(range(2, x.ndim))
     grad_wb = np.tensordot(g_z, x, axes=(red, red))
     grad_bias = g_z.sum(axis=red)

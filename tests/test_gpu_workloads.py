@@ -1,0 +1,157 @@
+"""Parity at the five workloads' full sizes, in the launch configuration bench.py times.
+
+Inputs are the workloads' own seeded fields (Gaussian random fields, coordinate and layered
+permeability channels) and block parameters.  Where the oracle can evaluate the whole field in
+seconds it does (C1; C3 and C4 one block forward + backward over the full batch; C2 the whole
+stack on sampled batch entries, which the stack never mixes).  For the 4D space-time share
+(C5, 3.4 GB per field) the oracle computes the full retained spectrum and then the block output
+directly at sampled grid points.  The spectral path is also compared on its own (y_spec and the
+spectral part of grad_x), since at these weight scales the bypass dominates the block output.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle.fno_oracle as O
+from fno_spectral_convolution_amd import configs, inputs
+from tests.gpu_helpers import TOL_F32, TOL_MIXED, announce, check
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(a):
+    return _torch().from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def _host(t):
+    return t.detach().cpu().numpy()
+
+
+_FIELDS = {}
+
+
+def _field(wl):
+    """The workload's seeded input field, generated once per module (C5 and C5h share it)."""
+    key = (wl.cfg_id, wl.batch, wl.width, tuple(wl.grid), wl.input_kind)
+    if key not in _FIELDS:
+        _FIELDS.clear()
+        _FIELDS[key] = inputs.field(wl, inputs.STREAM_INPUT, channels=wl.width)
+    return _FIELDS[key]
+
+
+@pytest.fixture(scope="module")
+def L():
+    from fno_spectral_convolution_amd import binding
+    return binding
+
+
+def _grad_in(wl, scale):
+    g = np.random.default_rng(np.random.SeedSequence([wl.cfg_id, 77]))
+    return (g.standard_normal((wl.batch, wl.width) + tuple(wl.grid)) * scale).astype(np.float32)
+
+
+def _block_case(L, name, grad_scale):
+    """One block of the workload at full size: forward, backward and the spectral path alone."""
+    wl = configs.get(name)
+    tol = TOL_MIXED if wl.mixed else TOL_F32
+    announce("workload block", name, wl.batch, wl.width, wl.grid, wl.modes)
+    x = _field(wl)
+    blk = inputs.block_params(wl, 1)[0]
+    gy = _grad_in(wl, grad_scale)
+    plan = L.Plan(wl.batch, wl.width, wl.width, wl.grid, wl.modes, mixed=wl.mixed)
+    tx, tw, twb, tb, tg = (_dev(a) for a in (x, blk["w"], blk["wb"], blk["bias"], gy))
+    save = plan.new_save()
+    y = plan.block_fwd(tx, tw, twb, tb, save=save)
+    g = plan.block_bwd(tx, tw, twb, tb, save, tg)
+    _torch().cuda.synchronize()
+    y, gx, gw, gwb, gb = _host(y), _host(g["x"]), _host(g["w"]), _host(g["wb"]), _host(g["bias"])
+    del save, g
+    ref = O.block_bwd(x, blk["w"], blk["wb"], blk["bias"], wl.modes, gy, tanh=wl.mixed)
+    check("y", y, ref["fwd"]["y"], tol)
+    check("grad_x", gx, ref["grad_x"], tol)
+    check("grad_w", gw, ref["grad_w"], tol)
+    check("grad_wb", gwb, ref["grad_wb"], tol)
+    check("grad_bias", gb, ref["grad_bias"], tol)
+    # the spectral path on its own: forward y_spec and the adjoint applied to the oracle's g_z
+    sp = L.Plan(wl.batch, wl.width, wl.width, wl.grid, wl.modes, mixed=wl.mixed, gelu=False,
+                bias=False)
+    ys = sp.spectral_conv_fwd(tx, tw)
+    gxs, _ = sp.spectral_conv_bwd(tx, tw, _dev(ref["g_z"].astype(np.float32)), want_w=False)
+    _torch().cuda.synchronize()
+    check("y_spec", _host(ys), ref["fwd"]["y_spec"], tol)
+    check("grad_x spectral part", _host(gxs), ref["gx_spec"], tol)
+    plan.close()
+    sp.close()
+
+
+def test_c1_block_full(L):
+    _block_case(L, "c1", 1.0)
+
+
+def test_c3_block_full(L):
+    _block_case(L, "c3", 1e-3)
+
+
+def test_c4_block_full(L):
+    _block_case(L, "c4", 1e-3)
+
+
+def test_c2_stack_sampled_batches(L):
+    """The full C2 stack (lift, 4 blocks, projection) on the GPU, as bench.py runs it; the
+    oracle evaluates the same stack for batch entries 0 and 15."""
+    from fno_spectral_convolution_amd.stack import StackRunner
+    wl = configs.get("c2")
+    announce("workload stack c2")
+    runner = StackRunner(wl, device="cuda")
+    out = _host(runner.step())
+    _torch().cuda.synchronize()
+    hi = runner.host
+    for b in (0, wl.batch - 1):
+        want = O.stack_fwd(hi["x"][b:b + 1], hi["blocks"], wl.modes,
+                           lift=hi["lift_proj"]["lift"], proj=hi["lift_proj"]["proj"])
+        check(f"stack output batch {b}", out[b:b + 1], want, TOL_F32)
+
+
+@pytest.mark.parametrize("name", ["c5", "c5h"])
+def test_c5_block_sampled_points(L, name):
+    """4D space-time share [1, 20, 128^3 x 20]: y and y_spec at 512 sampled grid points."""
+    wl = configs.get(name)
+    tol = TOL_MIXED if wl.mixed else TOL_F32
+    announce("workload block sampled", name)
+    torch = _torch()
+    x = _field(wl)
+    blk = inputs.block_params(wl, 1)[0]
+    plan = L.Plan(wl.batch, wl.width, wl.width, wl.grid, wl.modes, mixed=wl.mixed)
+    tx = _dev(x)
+    tw, twb, tb = _dev(blk["w"]), _dev(blk["wb"]), _dev(blk["bias"])
+    y = plan.block_fwd(tx, tw, twb, tb)
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    pts = np.stack([rng.integers(0, n, 512) for n in wl.grid], axis=1)
+    flat = np.ravel_multi_index(tuple(pts.T), wl.grid)
+    idx = torch.from_numpy(flat).to("cuda")
+    y_s = _host(y.reshape(wl.batch, wl.width, -1)[:, :, idx])
+    del y
+    sp = L.Plan(wl.batch, wl.width, wl.width, wl.grid, wl.modes, mixed=wl.mixed, gelu=False,
+                bias=False)
+    ys = sp.spectral_conv_fwd(tx, tw)
+    ys_s = _host(ys.reshape(wl.batch, wl.width, -1)[:, :, idx])
+    del ys, tx
+    torch.cuda.synchronize()
+    xp = np.tanh(x.astype(np.float64)) if wl.mixed else x
+    xhat = O.spectrum(xp, wl.modes)
+    del xp
+    yhat = O.channel_mix(xhat, blk["w"], wl.modes)
+    want_spec = O.inverse_at_points(yhat, wl.grid, wl.modes, pts)
+    xs = x.reshape(wl.batch, wl.width, -1)[:, :, flat].astype(np.float64)
+    z = want_spec + np.einsum("oi,bip->bop", blk["wb"].astype(np.float64), xs) \
+        + blk["bias"].astype(np.float64)[None, :, None]
+    check("y_spec (sampled)", ys_s, want_spec, tol)
+    check("y (sampled)", y_s, O.gelu(z), tol)
+    plan.close()
+    sp.close()

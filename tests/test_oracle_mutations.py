@@ -108,3 +108,20 @@ def test_pin_catches_mutation(monkeypatch, name, bad, check):
     monkeypatch.setattr(O, name, bad)
     with pytest.raises((AssertionError, ValueError)):
         check(O)
+
+
+def _inverse_points_no_gamma(yhat, shape, modes, points):
+    import numpy as _np
+    d = len(shape)
+    pts = _np.asarray(points)
+    sets = [O.retained_indices(shape[j], modes[j], last=(j == d - 1)) for j in range(d)]
+    grids = _np.meshgrid(*sets, indexing="ij")
+    phase = sum(2 * _np.pi * _np.outer(grids[j].ravel(), pts[:, j]) / shape[j] for j in range(d))
+    yk = yhat.reshape(yhat.shape[0], yhat.shape[1], -1)
+    return _np.real(_np.tensordot(yk, _np.exp(1j * phase), axes=([2], [0]))) / _np.prod(shape)
+
+
+def test_point_inverse_pin_catches_missing_gamma(monkeypatch):
+    monkeypatch.setattr(O, "inverse_at_points", _inverse_points_no_gamma)
+    with pytest.raises(AssertionError):
+        P.check_inverse_at_points(O)
