@@ -149,10 +149,30 @@ def roofline(wl, runner, kern, steps):
     avg_s = r["avg_us"] / 1e6
     # the dominant kernels stream fields: their floor is the HBM time of their bytes
     ach = r["alg_bytes"] / avg_s / 1e9
+    traffic = measured_traffic(wl, dom)
     out = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-           "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+           "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
            "alg_bytes_per_launch": r["alg_bytes"], "avg_launch_us": round(r["avg_us"], 2)}
     return out, rows
+
+
+def measured_traffic(wl, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the counter's reading for a plain copy of known
+    size), or None when there is none for this workload or the kernel's source has changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"counters_{wl.name}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))["kernels"][kernel]
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+    except (KeyError, OSError, ValueError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+        return None
+    return round(rec["fetch_bytes"] + rec["write_bytes"])
 
 
 def cpu_baseline(wl, sample_batch):

@@ -21,6 +21,7 @@
 // The last-axis table is read through L2 (shared by every wave); Wb slices sit in registers.
 #include "fno_internal.h"
 #include "mfma.h"
+#include "pointwise.h"
 
 #include <math.h>
 
@@ -46,16 +47,6 @@ struct EpiArgs {
   int block;           // bypass/bias/GELU present (else spectral only)
   int gelu;
 };
-
-__device__ __forceinline__ float gelu_fast(float z) {
-  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
-}
-
-__device__ __forceinline__ float gelu_grad_fast(float z) {
-  const float cdf = 0.5f * (1.0f + erff(z * 0.70710678118654752f));
-  const float pdf = __expf(-0.5f * z * z) * 0.39894228040143268f;
-  return cdf + z * pdf;
-}
 
 __device__ __forceinline__ float comp(const float4& v, int j) {
   return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
@@ -92,38 +83,71 @@ __device__ __forceinline__ void stage_line(const EpiArgs& a, const float2* Trow0
   }
 }
 
+// Fragments of the last-axis table for one point group of this wave: A operand rows
+// pb0 + 16 (tbase + j) + m, all K-steps (kpad <= 64).  Loaded one group ahead.
+template <int TMW, bool BF>
+struct GtFrag;
+template <int TMW>
+struct GtFrag<TMW, true> {
+  bf16x8 v[TMW][2];  // K-steps of 32
+};
+template <int TMW>
+struct GtFrag<TMW, false> {
+  float4 v[TMW][4];  // K-groups of 16
+};
+
+template <int TMW, bool BF>
+__device__ __forceinline__ void load_gt(const EpiArgs& a, int pb0, int tbase, int m, int q,
+                                        GtFrag<TMW, BF>& f) {
+#pragma unroll
+  for (int j = 0; j < TMW; ++j) {
+    const int64_t row = (int64_t)(pb0 + 16 * (tbase + j) + m) * a.kpad;
+    if constexpr (BF) {
+      const uint16_t* gt = static_cast<const uint16_t*>(a.gt) + row;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        f.v[j][s] = bf16x8{};
+        if (32 * s < a.kpad) f.v[j][s] = *reinterpret_cast<const bf16x8*>(gt + 32 * s + 8 * q);
+      }
+    } else {
+      const float* gt = static_cast<const float*>(a.gt) + row;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f.v[j][g] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (16 * g < a.kpad) f.v[j][g] = *reinterpret_cast<const float4*>(gt + 16 * g + 4 * q);
+      }
+    }
+  }
+}
+
 // Spectral product of one point group for this wave: acc[j] += GT[points of M-tile t] x
 // tl[channel tile ct]^T, with t = tbase + j.  M-tile t, row m <-> point 16 t + m of the group.
 template <int C, int TMW, bool BF>
 __device__ __forceinline__ void spectral_coop(const EpiArgs& a, const unsigned char* tl,
-                                              int pb0, int ct, int tbase, int m, int q,
+                                              const GtFrag<TMW, BF>& f, int ct, int m, int q,
                                               f32x4 (&acc)[TMW]) {
   const int kst = a.kpad + (BF ? 8 : 4);
-  if (BF) {
-    const uint16_t* gt = static_cast<const uint16_t*>(a.gt);
+  if constexpr (BF) {
     const uint16_t* tb = reinterpret_cast<const uint16_t*>(tl) + (16 * ct + m) * kst;
-    for (int s = 0; s < a.kpad / 32; ++s) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (32 * s >= a.kpad) break;
       const bf16x8 B = *reinterpret_cast<const bf16x8*>(tb + 32 * s + 8 * q);
 #pragma unroll
-      for (int j = 0; j < TMW; ++j) {
-        const int p = pb0 + 16 * (tbase + j) + m;
-        const bf16x8 A = *reinterpret_cast<const bf16x8*>(gt + (int64_t)p * a.kpad + 32 * s + 8 * q);
-        acc[j] = mfma_bf16(A, B, acc[j]);
-      }
+      for (int j = 0; j < TMW; ++j) acc[j] = mfma_bf16(f.v[j][s], B, acc[j]);
     }
   } else {
-    const float* gt = static_cast<const float*>(a.gt);
     const float* tb = reinterpret_cast<const float*>(tl) + (16 * ct + m) * kst;
-    for (int g = 0; g < a.kpad / 16; ++g) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if (16 * g >= a.kpad) break;
       const float4 B4 = *reinterpret_cast<const float4*>(tb + 16 * g + 4 * q);
 #pragma unroll
       for (int j = 0; j < TMW; ++j) {
-        const int p = pb0 + 16 * (tbase + j) + m;
-        const float4 A4 = *reinterpret_cast<const float4*>(gt + (int64_t)p * a.kpad + 16 * g + 4 * q);
-        acc[j] = mfma_f32(A4.x, B4.x, acc[j]);
-        acc[j] = mfma_f32(A4.y, B4.y, acc[j]);
-        acc[j] = mfma_f32(A4.z, B4.z, acc[j]);
-        acc[j] = mfma_f32(A4.w, B4.w, acc[j]);
+        acc[j] = mfma_f32(f.v[j][g].x, B4.x, acc[j]);
+        acc[j] = mfma_f32(f.v[j][g].y, B4.y, acc[j]);
+        acc[j] = mfma_f32(f.v[j][g].z, B4.z, acc[j]);
+        acc[j] = mfma_f32(f.v[j][g].w, B4.w, acc[j]);
       }
     }
   }
@@ -157,7 +181,7 @@ __global__ void __launch_bounds__(256) k_epi_fwd_fast(EpiArgs a) {
   constexpr int TMW = NT;
   constexpr int NPT = NT;  // float4 of the x tile per thread
   __shared__ __attribute__((aligned(16))) float s_x[CP * XS];
-  __shared__ __attribute__((aligned(16))) unsigned char s_tl[CP * (kMaxKpad + 8) * 4];
+  __shared__ __attribute__((aligned(16))) unsigned char s_tl[CP * (kMaxKpad + 8) * (BF ? 2 : 4)];
   __shared__ float s_bias[CP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, q = lane >> 4;
@@ -186,7 +210,11 @@ __global__ void __launch_bounds__(256) k_epi_fwd_fast(EpiArgs a) {
                                                   4 * c4);
     }
   };
-  if (a.block && g_begin < g_end) load_x(g_begin);
+  GtFrag<TMW, BF> gtf;
+  if (g_begin < g_end) {
+    if (a.block) load_x(g_begin);
+    load_gt<TMW, BF>(a, group_pos(a, g_begin).pb0, tbase, m, q, gtf);
+  }
   int64_t cur_line = -1;
   for (int64_t pg = g_begin; pg < g_end; ++pg) {
     const GroupPos gp = group_pos(a, pg);
@@ -208,7 +236,9 @@ __global__ void __launch_bounds__(256) k_epi_fwd_fast(EpiArgs a) {
     f32x4 acc[TMW];
 #pragma unroll
     for (int j = 0; j < TMW; ++j) acc[j] = zero4();
-    spectral_coop<C, TMW, BF>(a, s_tl, gp.pb0, ct, tbase, m, q, acc);
+    spectral_coop<C, TMW, BF>(a, s_tl, gtf, ct, m, q, acc);
+    // next group's table fragments: in flight during the bypass, the stores and the staging
+    if (pg + 1 < g_end) load_gt<TMW, BF>(a, group_pos(a, pg + 1).pb0, tbase, m, q, gtf);
     if (a.block) {
 #pragma unroll
       for (int kb = 0; kb < C / 4; ++kb)
@@ -226,10 +256,10 @@ __global__ void __launch_bounds__(256) k_epi_fwd_fast(EpiArgs a) {
         float4 v = make_float4(acc[j][0] + bo, acc[j][1] + bo, acc[j][2] + bo, acc[j][3] + bo);
         if (a.z) *reinterpret_cast<float4*>(a.z + off) = v;
         if (a.block && a.gelu) {
-          v.x = gelu_fast(v.x);
-          v.y = gelu_fast(v.y);
-          v.z = gelu_fast(v.z);
-          v.w = gelu_fast(v.w);
+          v.x = gelu_as(v.x);
+          v.y = gelu_as(v.y);
+          v.z = gelu_as(v.z);
+          v.w = gelu_as(v.w);
         }
         *reinterpret_cast<float4*>(a.y + off) = v;
       }
@@ -273,7 +303,7 @@ __global__ void __launch_bounds__(256) k_epi_bwd_fast(EpiArgs a) {
   constexpr int DT = (NT == 4) ? 4 : 1;  // dWb tiles per wave
   __shared__ __attribute__((aligned(16))) float s_gz[CP * XS];
   __shared__ __attribute__((aligned(16))) float s_x[CP * XS];
-  __shared__ __attribute__((aligned(16))) unsigned char s_tl[CP * (kMaxKpad + 8) * 4];
+  __shared__ __attribute__((aligned(16))) unsigned char s_tl[CP * (kMaxKpad + 8) * (BF ? 2 : 4)];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, q = lane >> 4;
   const int ct = wave % NT, tbase = (wave / NT) * TMW;
@@ -297,7 +327,11 @@ __global__ void __launch_bounds__(256) k_epi_bwd_fast(EpiArgs a) {
   const int64_t g_begin = (int64_t)blockIdx.x * a.pg_per_wg;
   const int64_t g_end = min(a.npg, g_begin + a.pg_per_wg);
   float4 pg_y[NPT], pz[NPT], px[NPT];
-  if (g_begin < g_end) load_bwd_tiles<C, NPT>(a, g_begin, tid, need_x, pg_y, pz, px);
+  GtFrag<TMW, BF> gtf;
+  if (g_begin < g_end) {
+    load_bwd_tiles<C, NPT>(a, g_begin, tid, need_x, pg_y, pz, px);
+    if (want_gx) load_gt<TMW, BF>(a, group_pos(a, g_begin).pb0, tbase, m, q, gtf);
+  }
   int64_t cur_line = -1;
   for (int64_t pg = g_begin; pg < g_end; ++pg) {
     const GroupPos gp = group_pos(a, pg);
@@ -313,10 +347,10 @@ __global__ void __launch_bounds__(256) k_epi_bwd_fast(EpiArgs a) {
       const int c = e >> 4, c4 = e & 15;
       float4 g = pg_y[u];
       if (a.gelu) {
-        g.x *= gelu_grad_fast(pz[u].x);
-        g.y *= gelu_grad_fast(pz[u].y);
-        g.z *= gelu_grad_fast(pz[u].z);
-        g.w *= gelu_grad_fast(pz[u].w);
+        g.x *= gelu_grad_as(pz[u].x);
+        g.y *= gelu_grad_as(pz[u].y);
+        g.z *= gelu_grad_as(pz[u].z);
+        g.w *= gelu_grad_as(pz[u].w);
       }
       *reinterpret_cast<float4*>(s_gz + c * XS + 4 * c4) = g;
       *reinterpret_cast<float4*>(s_x + c * XS + 4 * c4) = px[u];
@@ -327,13 +361,14 @@ __global__ void __launch_bounds__(256) k_epi_bwd_fast(EpiArgs a) {
       f32x4 acc[TMW];
 #pragma unroll
       for (int j = 0; j < TMW; ++j) acc[j] = zero4();
-      spectral_coop<C, TMW, BF>(a, s_tl, gp.pb0, ct, tbase, m, q, acc);
+      spectral_coop<C, TMW, BF>(a, s_tl, gtf, ct, m, q, acc);
+      if (pg + 1 < g_end) load_gt<TMW, BF>(a, group_pos(a, pg + 1).pb0, tbase, m, q, gtf);
       const int i = 16 * ct + m;
       if (TANH) {
 #pragma unroll
         for (int j = 0; j < TMW; ++j) {
           const float4 xv = *reinterpret_cast<const float4*>(s_x + i * XS + 16 * (tbase + j) + 4 * q);
-          const float t0 = tanhf(xv.x), t1 = tanhf(xv.y), t2 = tanhf(xv.z), t3 = tanhf(xv.w);
+          const float t0 = tanh_fast(xv.x), t1 = tanh_fast(xv.y), t2 = tanh_fast(xv.z), t3 = tanh_fast(xv.w);
           acc[j][0] *= 1.f - t0 * t0;
           acc[j][1] *= 1.f - t1 * t1;
           acc[j][2] *= 1.f - t2 * t2;

@@ -17,6 +17,7 @@
 // its partial spectrum; chunks are summed by the next kernel in a fixed order.
 #include "fno_internal.h"
 #include "mfma.h"
+#include "pointwise.h"
 
 #include <math.h>
 
@@ -36,24 +37,10 @@ struct PlaneArgs {
   float2* out;           // [nch][planes][2ma][mb]
 };
 
-__device__ __forceinline__ float tanh_fast(float v) {
-  // tanh(|v|) = (1 - e) / (1 + e), e = exp(-2|v|): no cancellation for large |v|, and the
-  // result is rounded to bfloat16 afterwards on the path that uses it
-  const float e = __expf(-2.0f * fabsf(v));
-  const float t = (1.0f - e) / (1.0f + e);
-  return copysignf(t, v);
-}
-
-__device__ __forceinline__ float gelu_grad_plane(float z) {
-  const float cdf = 0.5f * (1.0f + erff(z * 0.70710678118654752f));
-  const float pdf = __expf(-0.5f * z * z) * 0.39894228040143268f;
-  return cdf + z * pdf;
-}
-
 template <int PIN>
 __device__ __forceinline__ float prologue(float v, float w) {
   if (PIN == PLANE_TANH) return tanh_fast(v);
-  if (PIN == PLANE_GELU_GRAD) return v * gelu_grad_plane(w);
+  if (PIN == PLANE_GELU_GRAD) return v * gelu_grad_as(w);
   return v;
 }
 
