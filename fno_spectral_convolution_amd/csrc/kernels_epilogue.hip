@@ -33,7 +33,9 @@ struct EpiArgs {
   int Nb, mb, kpad;    // contiguous axis, its retained bins, padded 2*mb
   int64_t lines;       // P / Nb
   int64_t npg;         // point groups over the whole batch
-  int64_t pg_per_wg;   // contiguous point groups handled by one work-group
+  int64_t pg_per_wg;   // contiguous point groups handled by one work-group (backward)
+  int lpw;             // forward: consecutive lines of one batch entry per work-group
+  int gpl_log2;        // log2 of the point groups per line (Nb / 64)
   const float* x;
   const float2* T;     // [B][C][lines][mb]
   const float* wb;     // [C][C] (o, i)
@@ -62,10 +64,10 @@ template <int C, bool BF>
 __device__ __forceinline__ void stage_line(const EpiArgs& a, const float2* Trow0,
                                            unsigned char* tl, int tid) {
   constexpr int CP = (C + 15) / 16 * 16;
-  const int kst = a.kpad + (BF ? 8 : 4);
+  constexpr int kst = kMaxKpad + (BF ? 8 : 4);
   const int64_t cstride = a.lines * a.mb;
   const int kf_end = 2 * a.mb;
-  const int g4 = a.kpad / 4;
+  constexpr int g4 = kMaxKpad / 4;  // columns kf_end .. kMaxKpad - 1 are written as zeros
   for (int e = tid; e < CP * g4; e += 256) {
     const int c = e / g4, k4 = 4 * (e - c * g4);
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -96,26 +98,22 @@ struct GtFrag<TMW, false> {
   float4 v[TMW][4];  // K-groups of 16
 };
 
-template <int TMW, bool BF>
+template <int TMW, bool BF, bool IL = false>
 __device__ __forceinline__ void load_gt(const EpiArgs& a, int pb0, int tbase, int m, int q,
                                         GtFrag<TMW, BF>& f) {
 #pragma unroll
   for (int j = 0; j < TMW; ++j) {
-    const int64_t row = (int64_t)(pb0 + 16 * (tbase + j) + m) * a.kpad;
+    // row m of M-tile t: point 4 m + t (interleaved) or 16 t + m of the group
+    const int pt = IL ? 4 * m + tbase + j : 16 * (tbase + j) + m;
+    const int64_t row = (int64_t)(pb0 + pt) * a.kpad;
     if constexpr (BF) {
       const uint16_t* gt = static_cast<const uint16_t*>(a.gt) + row;
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        f.v[j][s] = bf16x8{};
-        if (32 * s < a.kpad) f.v[j][s] = *reinterpret_cast<const bf16x8*>(gt + 32 * s + 8 * q);
-      }
+      for (int s = 0; s < 2; ++s) f.v[j][s] = *reinterpret_cast<const bf16x8*>(gt + 32 * s + 8 * q);
     } else {
       const float* gt = static_cast<const float*>(a.gt) + row;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f.v[j][g] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (16 * g < a.kpad) f.v[j][g] = *reinterpret_cast<const float4*>(gt + 16 * g + 4 * q);
-      }
+      for (int g = 0; g < 4; ++g) f.v[j][g] = *reinterpret_cast<const float4*>(gt + 16 * g + 4 * q);
     }
   }
 }
@@ -126,7 +124,7 @@ template <int C, int TMW, bool BF>
 __device__ __forceinline__ void spectral_coop(const EpiArgs& a, const unsigned char* tl,
                                               const GtFrag<TMW, BF>& f, int ct, int m, int q,
                                               f32x4 (&acc)[TMW]) {
-  const int kst = a.kpad + (BF ? 8 : 4);
+  constexpr int kst = kMaxKpad + (BF ? 8 : 4);
   if constexpr (BF) {
     const uint16_t* tb = reinterpret_cast<const uint16_t*>(tl) + (16 * ct + m) * kst;
 #pragma unroll
@@ -171,102 +169,166 @@ __device__ __forceinline__ GroupPos group_pos(const EpiArgs& a, int64_t pg) {
   return r;
 }
 
+// 1, 2 or 4 adjacent floats from / to LDS in one access (the pointer is aligned to the run)
+template <int N>
+__device__ __forceinline__ void load_lds_run(float (&v)[N], const float* p) {
+  if constexpr (N == 4) {
+    const float4 t = *reinterpret_cast<const float4*>(p);
+    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+  } else if constexpr (N == 2) {
+    const float2 t = *reinterpret_cast<const float2*>(p);
+    v[0] = t.x; v[1] = t.y;
+  } else {
+    v[0] = *p;
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void store_lds_run(float* p, const float (&v)[N]) {
+  if constexpr (N == 4) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  } else if constexpr (N == 2) {
+    *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+  } else {
+    *p = v[0];
+  }
+}
+
+// Row loads of a [C][64] tile: thread t takes float4 t + 256 u, i.e. channel (t >> 4) + 16 u,
+// points 4 (t & 15) .. + 3, from base (already offset to this thread's first row and point).
+template <int C, int NPT>
+__device__ __forceinline__ void load_rows(float4 (&v)[NPT], const float* base, int64_t ustride,
+                                          int tid) {
+#pragma unroll
+  for (int u = 0; u < NPT; ++u) {
+    if constexpr ((16 * C) % 256 == 0) {
+      v[u] = *reinterpret_cast<const float4*>(base + u * ustride);
+    } else {
+      if (tid + 256 * u < 16 * C) v[u] = *reinterpret_cast<const float4*>(base + u * ustride);
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------------------
-// Forward.  The 4 waves split the (channel tile x point M-tile) output tiles of a group:
-// wave w owns channel tile ct = w % NT and M-tiles tbase .. tbase + NT - 1.
-template <int C, bool BF>
-__global__ void __launch_bounds__(256) k_epi_fwd_fast(EpiArgs a) {
+// Forward.  A work-group owns lpw consecutive lines of one batch entry: a contiguous range of
+// points, walked in 64-point groups.  The spectrum rows of a line are staged in LDS when the
+// line starts; the group loop itself is straight-line code, so the compiler can keep the
+// prefetches in flight across it: the x rows of group f + 1 are loaded while group f is
+// computed, then the table fragments of group f + 1 (issued in the order they are consumed;
+// the last group re-loads itself instead of branching).  The 4 waves split the output tiles
+// (wave w: channel tile w % NT, M-tiles tbase ..).  Row m of M-tile t is point 4 m + t of the
+// group, so one lane's A operands of its TMW tiles are adjacent in the [channel][point] LDS
+// tile (one LDS read feeds TMW products).  The z tile goes through LDS and the stores are
+// row-contiguous: 16 threads write one channel's 64 points.
+// MODE: 0 spectral part only, 1 block (bypass, bias, optional GELU), 2 block + z save.
+template <int C, bool BF, int MODE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C == 64 ? 3 : 4)))
+k_epi_fwd_line(EpiArgs a) {
   constexpr int CP = (C + 15) / 16 * 16;
   constexpr int NT = CP / 16;
   constexpr int TMW = NT;
-  constexpr int NPT = NT;  // float4 of the x tile per thread
-  __shared__ __attribute__((aligned(16))) float s_x[CP * XS];
+  constexpr int NPT = NT;  // float4 of a [CP][64] tile per thread
+  constexpr bool BLK = MODE >= 1;
+  constexpr bool ZS = MODE == 2;
+  __shared__ __attribute__((aligned(16))) float s_x[BLK ? CP * XS : 4];
+  __shared__ __attribute__((aligned(16))) float s_o[CP * XS];
   __shared__ __attribute__((aligned(16))) unsigned char s_tl[CP * (kMaxKpad + 8) * (BF ? 2 : 4)];
   __shared__ float s_bias[CP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, q = lane >> 4;
   const int ct = wave % NT, tbase = (wave / NT) * TMW;
+  const int64_t wg_per_b = a.lines / a.lpw;
+  const int b = (int)(blockIdx.x / wg_per_b);
+  const int64_t l0 = (int64_t)(blockIdx.x - (int64_t)b * wg_per_b) * a.lpw;
+  const int gpl = 1 << a.gpl_log2;
+  const int nf = a.lpw << a.gpl_log2;
   // Wb^T slice: B operand of K-step kb, lane (n = m, q): Wb[16 ct + m][4 kb + q]
-  float wbr[C / 4];
-  {
+  float wbr[BLK ? C / 4 : 1];
+  if (BLK) {
     const int o = 16 * ct + m;
 #pragma unroll
-    for (int kb = 0; kb < C / 4; ++kb)
-      wbr[kb] = (a.block && o < C) ? a.wb[o * C + 4 * kb + q] : 0.f;
-  }
-  for (int o = tid; o < CP; o += 256) s_bias[o] = (a.block && o < C && a.bias) ? a.bias[o] : 0.f;
-  const int64_t g_begin = (int64_t)blockIdx.x * a.pg_per_wg;
-  const int64_t g_end = min(a.npg, g_begin + a.pg_per_wg);
-  float4 pre[NPT];
-  auto load_x = [&](int64_t pg) {
-    const GroupPos gp = group_pos(a, pg);
+    for (int kb = 0; kb < C / 4; ++kb) wbr[kb] = 0.f;
+    if (o < C) {
 #pragma unroll
-    for (int u = 0; u < NPT; ++u) {
-      const int e = tid + 256 * u;
-      const int c = e >> 4, c4 = e & 15;
-      pre[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (c < C)
-        pre[u] = *reinterpret_cast<const float4*>(a.x + ((int64_t)gp.b * C + c) * a.P + gp.p0 +
-                                                  4 * c4);
+      for (int kb = 0; kb < C / 4; ++kb) wbr[kb] = a.wb[o * C + 4 * kb + q];
     }
-  };
-  GtFrag<TMW, BF> gtf;
-  if (g_begin < g_end) {
-    if (a.block) load_x(g_begin);
-    load_gt<TMW, BF>(a, group_pos(a, g_begin).pb0, tbase, m, q, gtf);
   }
-  int64_t cur_line = -1;
-  for (int64_t pg = g_begin; pg < g_end; ++pg) {
-    const GroupPos gp = group_pos(a, pg);
-    __syncthreads();  // previous group's readers are done
-    if (gp.gline != cur_line) {
-      const float2* Trow0 = a.T + ((int64_t)gp.b * C * a.lines + (gp.gline - (int64_t)gp.b * a.lines)) * a.mb;
-      stage_line<C, BF>(a, Trow0, s_tl, tid);
-      cur_line = gp.gline;
-    }
-    if (a.block) {
+  for (int o = tid; o < CP; o += 256) s_bias[o] = (BLK && o < C && a.bias) ? a.bias[o] : 0.f;
+  // this thread's rows of the x / y / z tiles: channel e >> 4, points 4 (e & 15) .. + 3
+  const int64_t pbase = l0 * a.Nb;
+  const int64_t rowoff = ((int64_t)b * C + (tid >> 4)) * a.P + pbase + 4 * (tid & 15);
+  const int64_t ustride = 16 * a.P;  // 256 threads further = 16 channels down
+  float4 pre[NPT];
+#pragma unroll
+  for (int u = 0; u < NPT; ++u) pre[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+  GtFrag<TMW, BF> gtf;
+  if (BLK) load_rows<C, NPT>(pre, a.x + rowoff, ustride, tid);
+  load_gt<TMW, BF, true>(a, 0, tbase, m, q, gtf);
+  for (int lf = 0; lf < a.lpw; ++lf) {
+    // every reader of the previous line's spectrum is past that line's last barrier
+    const float2* Trow0 = a.T + ((int64_t)b * C * a.lines + l0 + lf) * a.mb;
+    stage_line<C, BF>(a, Trow0, s_tl, tid);
+    for (int g = 0; g < gpl; ++g) {
+      const int f = (lf << a.gpl_log2) + g;
+      const int fn = min(f + 1, nf - 1);
+      if (BLK) {
+#pragma unroll
+        for (int u = 0; u < NPT; ++u) {
+          const int e = tid + 256 * u;
+          if ((16 * C) % 256 == 0 || e < 16 * C)
+            *reinterpret_cast<float4*>(s_x + (e >> 4) * XS + 4 * (e & 15)) = pre[u];
+        }
+        load_rows<C, NPT>(pre, a.x + rowoff + 64 * fn, ustride, tid);
+      }
+      __syncthreads();  // x tile and spectrum rows visible; previous z tile consumed
+      f32x4 acc[TMW];
+#pragma unroll
+      for (int j = 0; j < TMW; ++j) acc[j] = zero4();
+      spectral_coop<C, TMW, BF>(a, s_tl, gtf, ct, m, q, acc);
+      load_gt<TMW, BF, true>(a, (fn & (gpl - 1)) * PG, tbase, m, q, gtf);
+      if (BLK) {
+#pragma unroll
+        for (int kb = 0; kb < C / 4; ++kb) {
+          float av[TMW];
+          load_lds_run<TMW>(av, s_x + (4 * kb + q) * XS + 4 * m + tbase);
+#pragma unroll
+          for (int j = 0; j < TMW; ++j) acc[j] = mfma_f32(av[j], wbr[kb], acc[j]);
+        }
+      }
+      // lane (n = m, q), tile tbase + j, register r: channel 16 ct + m, point 16 q + 4 r + tbase + j
+      {
+        const int o = 16 * ct + m;
+        const float bo = s_bias[o];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v[TMW];
+#pragma unroll
+          for (int j = 0; j < TMW; ++j) v[j] = acc[j][r] + bo;
+          store_lds_run<TMW>(s_o + o * XS + 16 * q + 4 * r + tbase, v);
+        }
+      }
+      __syncthreads();  // z tile complete; x tile free
 #pragma unroll
       for (int u = 0; u < NPT; ++u) {
         const int e = tid + 256 * u;
-        *reinterpret_cast<float4*>(s_x + (e >> 4) * XS + 4 * (e & 15)) = pre[u];
-      }
-      if (pg + 1 < g_end) load_x(pg + 1);
-    }
-    __syncthreads();
-    f32x4 acc[TMW];
-#pragma unroll
-    for (int j = 0; j < TMW; ++j) acc[j] = zero4();
-    spectral_coop<C, TMW, BF>(a, s_tl, gtf, ct, m, q, acc);
-    // next group's table fragments: in flight during the bypass, the stores and the staging
-    if (pg + 1 < g_end) load_gt<TMW, BF>(a, group_pos(a, pg + 1).pb0, tbase, m, q, gtf);
-    if (a.block) {
-#pragma unroll
-      for (int kb = 0; kb < C / 4; ++kb)
-#pragma unroll
-        for (int j = 0; j < TMW; ++j)
-          acc[j] = mfma_f32(s_x[(4 * kb + q) * XS + 16 * (tbase + j) + m], wbr[kb], acc[j]);
-    }
-    // lane (n = m, q): channel 16 ct + m, points 16 t + 4 q + r
-    const int o = 16 * ct + m;
-    if (o < C) {
-      const float bo = s_bias[o];
-#pragma unroll
-      for (int j = 0; j < TMW; ++j) {
-        const int64_t off = ((int64_t)gp.b * C + o) * a.P + gp.p0 + 16 * (tbase + j) + 4 * q;
-        float4 v = make_float4(acc[j][0] + bo, acc[j][1] + bo, acc[j][2] + bo, acc[j][3] + bo);
-        if (a.z) *reinterpret_cast<float4*>(a.z + off) = v;
-        if (a.block && a.gelu) {
-          v.x = gelu_as(v.x);
-          v.y = gelu_as(v.y);
-          v.z = gelu_as(v.z);
-          v.w = gelu_as(v.w);
+        if ((16 * C) % 256 == 0 || e < 16 * C) {
+          float4 v = *reinterpret_cast<const float4*>(s_o + (e >> 4) * XS + 4 * (e & 15));
+          const int64_t off = rowoff + u * ustride + 64 * f;
+          if (ZS) *reinterpret_cast<float4*>(a.z + off) = v;
+          if (BLK && a.gelu) {
+            v.x = gelu_as(v.x);
+            v.y = gelu_as(v.y);
+            v.z = gelu_as(v.z);
+            v.w = gelu_as(v.w);
+          }
+          *reinterpret_cast<float4*>(a.y + off) = v;
         }
-        *reinterpret_cast<float4*>(a.y + off) = v;
       }
     }
   }
 }
 
+// ------------------------------------------------------------------------------------------
 // Backward prefetch of one group: g_y, z and x rows of every channel (thread-strided float4s)
 template <int C, int NPT>
 __device__ __forceinline__ void load_bwd_tiles(const EpiArgs& a, int64_t pg, int tid, bool need_x,
@@ -450,11 +512,19 @@ __global__ void __launch_bounds__(256) k_epi_bwd_fast(EpiArgs a) {
 
 // ------------------------------------------------------------------------------------------
 template <int C>
-static hipError_t launch_fwd_c(const EpiArgs& a, bool bf, int wgs, hipStream_t s) {
-  if (bf)
-    hipLaunchKernelGGL((k_epi_fwd_fast<C, true>), dim3(wgs), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_epi_fwd_fast<C, false>), dim3(wgs), dim3(256), 0, s, a);
+static hipError_t launch_fwd_c(const EpiArgs& a, bool bf, int mode, int wgs, hipStream_t s) {
+#define FNO_EPI_FWD(BFV, MV) \
+  hipLaunchKernelGGL((k_epi_fwd_line<C, BFV, MV>), dim3(wgs), dim3(256), 0, s, a)
+  if (bf) {
+    if (mode == 0) FNO_EPI_FWD(true, 0);
+    else if (mode == 1) FNO_EPI_FWD(true, 1);
+    else FNO_EPI_FWD(true, 2);
+  } else {
+    if (mode == 0) FNO_EPI_FWD(false, 0);
+    else if (mode == 1) FNO_EPI_FWD(false, 1);
+    else FNO_EPI_FWD(false, 2);
+  }
+#undef FNO_EPI_FWD
   return hipGetLastError();
 }
 
@@ -480,6 +550,8 @@ bool epilogue_fast_ok(const fno_plan* p, int mode, bool fwd) {
   if (mode == EPI_BLOCK && g.Cin != g.Cout) return false;
   if (!(C == 16 || C == 20 || C == 32 || C == 64)) return false;
   if (g.Nb % 64 != 0 || g.mb % 2 != 0 || p->kpad > kMaxKpad) return false;
+  const int gpl = g.Nb / 64;  // point groups per line: a power of two (shift / mask indexing)
+  if ((gpl & (gpl - 1)) != 0) return false;
   return true;
 }
 
@@ -505,12 +577,32 @@ static EpiArgs make_args(const fno_plan* p, int C, int pg_points, int wgs_cap, i
   return a;
 }
 
+// Lines per forward work-group: the largest power of two dividing the lines of a batch entry
+// that still leaves at least kFwdMinWgs work-groups.
+constexpr int64_t kFwdMinWgs = 2048;
+
+static int fwd_lines_per_wg(int64_t lines, int64_t batch) {
+  int lpw = 1;
+  while (lines % (2 * lpw) == 0 && batch * lines / (2 * lpw) >= kFwdMinWgs) lpw *= 2;
+  return lpw;
+}
+
 hipError_t launch_epilogue_fwd_fast(const fno_plan* p, int mode, const float2* T, const float* x,
                                     const float* wb, const float* bias, float* y, float* zsave,
                                     hipStream_t s) {
   const Geom& g = p->g;
-  int wgs = 0;
-  EpiArgs a = make_args(p, g.Cout, PG, 1024, &wgs);
+  EpiArgs a{};
+  a.B = g.B;
+  a.C = g.Cout;
+  a.P = g.P;
+  a.Nb = g.Nb;
+  a.mb = g.mb;
+  a.kpad = p->kpad;
+  a.lines = g.P / g.Nb;
+  a.lpw = fwd_lines_per_wg(a.lines, g.B);
+  int gl = 0;
+  while ((PG << gl) < g.Nb) ++gl;
+  a.gpl_log2 = gl;
   a.x = x;
   a.T = T;
   a.wb = wb;
@@ -518,13 +610,16 @@ hipError_t launch_epilogue_fwd_fast(const fno_plan* p, int mode, const float2* T
   a.gt = g.bf16 ? (const void*)p->t.gt_fwd_bf : (const void*)p->t.gt_fwd;
   a.y = y;
   a.z = zsave;
-  a.block = mode == EPI_BLOCK;
   a.gelu = (p->desc.flags & FNO_FLAG_GELU) != 0;
+  const int kmode = mode != EPI_BLOCK ? 0 : (zsave ? 2 : 1);
+  a.block = kmode != 0;
+  const int64_t wgs = (int64_t)g.B * a.lines / a.lpw;
+  if (wgs > 0x7fffffff) return hipErrorInvalidValue;
   switch (g.Cout) {
-    case 16: return launch_fwd_c<16>(a, g.bf16, wgs, s);
-    case 20: return launch_fwd_c<20>(a, g.bf16, wgs, s);
-    case 32: return launch_fwd_c<32>(a, g.bf16, wgs, s);
-    default: return launch_fwd_c<64>(a, g.bf16, wgs, s);
+    case 16: return launch_fwd_c<16>(a, g.bf16, kmode, (int)wgs, s);
+    case 20: return launch_fwd_c<20>(a, g.bf16, kmode, (int)wgs, s);
+    case 32: return launch_fwd_c<32>(a, g.bf16, kmode, (int)wgs, s);
+    default: return launch_fwd_c<64>(a, g.bf16, kmode, (int)wgs, s);
   }
 }
 

@@ -242,7 +242,9 @@ fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out) {
     rootbf_off[j] = toff;
     toff += align_up(sizeof(float2) * g.N[j]);
   }
-  const size_t gt_elems = (size_t)g.Nb * p->kpad;
+  // the epilogues read table fragments K = 64 wide whatever kpad is: the zero tail keeps the
+  // last row's over-read in bounds (its products meet zero spectrum columns)
+  const size_t gt_elems = (size_t)g.Nb * p->kpad + 64;
   const size_t gt_fwd_off = toff;
   toff += align_up(sizeof(float) * gt_elems);
   const size_t gt_unit_off = toff;
