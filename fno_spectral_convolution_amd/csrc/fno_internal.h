@@ -118,6 +118,11 @@ hipError_t launch_epilogue_bwd(const fno_plan* p, int mode, const float2* Tg, co
                                const float* wb, const float* gy, const float* z,
                                float* grad_x, float* red_part, hipStream_t s);
 bool epilogue_fast_ok(const fno_plan* p, int mode, bool fwd);
+// the backward epilogue takes the matrix-core kernel (which writes epilogue_bwd_fast_groups
+// partial rows) only when grad_x is produced; otherwise the generic kernel (nred rows)
+inline bool epilogue_bwd_fast(const fno_plan* p, int mode, const float* grad_x) {
+  return grad_x != nullptr && epilogue_fast_ok(p, mode, false);
+}
 int epilogue_bwd_fast_groups(const fno_plan* p);
 hipError_t launch_epilogue_fwd_fast(const fno_plan* p, int mode, const float2* T, const float* x,
                                     const float* wb, const float* bias, float* y, float* zsave,
@@ -133,7 +138,7 @@ bool outer_fast_ok(const fno_plan* p, int axis, bool inv);
 hipError_t launch_outer_mfma(const fno_plan* p, int axis, int chans, bool inv, const float2* in,
                              float2* out, hipStream_t s);
 hipError_t launch_bypass_grad_finish(const fno_plan* p, const float* red_part, float* dwb,
-                                     float* dbias, hipStream_t s);
+                                     float* dbias, const float* grad_x, hipStream_t s);
 hipError_t launch_pointwise(int64_t batch, int64_t npts, int cin, int hidden, int cout,
                             const float* x, const float* w1, const float* b1, const float* w2,
                             const float* b2, float* y, hipStream_t s);

@@ -32,9 +32,7 @@ struct EpiArgs {
   int64_t P;           // points per field
   int Nb, mb, kpad;    // contiguous axis, its retained bins, padded 2*mb
   int64_t lines;       // P / Nb
-  int64_t npg;         // point groups over the whole batch
-  int64_t pg_per_wg;   // contiguous point groups handled by one work-group (backward)
-  int lpw;             // forward: consecutive lines of one batch entry per work-group
+  int lpw;             // consecutive lines of one batch entry per work-group
   int gpl_log2;        // log2 of the point groups per line (Nb / 64)
   const float* x;
   const float2* T;     // [B][C][lines][mb]
@@ -149,24 +147,6 @@ __device__ __forceinline__ void spectral_coop(const EpiArgs& a, const unsigned c
       }
     }
   }
-}
-
-// Point-group bookkeeping shared by both epilogues
-struct GroupPos {
-  int b;
-  int64_t p0, gline;  // first point, global line index b * lines + line
-  int pb0;            // position of p0 inside its line
-};
-
-__device__ __forceinline__ GroupPos group_pos(const EpiArgs& a, int64_t pg) {
-  const int64_t pg_per_b = a.P / PG;
-  GroupPos r;
-  r.b = (int)(pg / pg_per_b);
-  r.p0 = (pg - (int64_t)r.b * pg_per_b) * PG;
-  const int64_t line = r.p0 / a.Nb;
-  r.pb0 = (int)(r.p0 - line * a.Nb);
-  r.gline = (int64_t)r.b * a.lines + line;
-  return r;
 }
 
 // 1, 2 or 4 adjacent floats from / to LDS in one access (the pointer is aligned to the run)
@@ -329,55 +309,49 @@ k_epi_fwd_line(EpiArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Backward prefetch of one group: g_y, z and x rows of every channel (thread-strided float4s)
-template <int C, int NPT>
-__device__ __forceinline__ void load_bwd_tiles(const EpiArgs& a, int64_t pg, int tid, bool need_x,
-                                               float4 (&gy)[NPT], float4 (&zz)[NPT],
-                                               float4 (&xx)[NPT]) {
-  const GroupPos lp = group_pos(a, pg);
-  // explicit branches: a conditional between a global load and a local zero would otherwise
-  // be compiled as a select of addresses (a private copy of the zero and flat loads)
-#pragma unroll
-  for (int u = 0; u < NPT; ++u) {
-    const int e = tid + 256 * u;
-    const int c = e >> 4, c4 = e & 15;
-    const int64_t off = ((int64_t)lp.b * C + c) * a.P + lp.p0 + 4 * c4;
-    const bool in = c < C;
-    gy[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-    zz[u] = gy[u];
-    xx[u] = gy[u];
-    if (a.block && in) gy[u] = *reinterpret_cast<const float4*>(a.gy + off);
-    if (a.block && a.gelu && in) zz[u] = *reinterpret_cast<const float4*>(a.zin + off);
-    if (need_x && in) xx[u] = *reinterpret_cast<const float4*>(a.x + off);
-  }
-}
-
-// ------------------------------------------------------------------------------------------
-// Backward.  Same tile split for grad_x; the bypass-weight gradient tiles are split too:
-// NT = 4: wave w owns dWb rows 16 w .. (all columns); NT = 2: tile (w >> 1, w & 1);
-// NT = 1: every wave sums a quarter of the points of the single tile.
-template <int C, bool BF, bool TANH>
-__global__ void __launch_bounds__(256) k_epi_bwd_fast(EpiArgs a) {
+// Backward.  Same line ownership and straight-line group pipeline as the forward: the g_y, z
+// and x rows of group f + 1 and its table fragments are in flight while group f is computed.
+//   grad_x tile : spectral product with the unit-scale table, times s(x) = 1 - tanh^2 on the
+//                 tanh path, plus Wb^T g_z (A operand g_z in the interleaved point mapping);
+//                 stored through LDS with row-contiguous float4 stores
+//   dWb, dbias  : dWb[o][i] += sum_p g_z[o][p] x[i][p] (16x16x4 f32, K = points), reduced over
+//                 the work-group in a fixed order into one partial row per work-group
+// Wave w's dWb tiles: NT = 4: o-tile w, all 4 i-tiles; NT = 2: o-tile w >> 1, i-tile w & 1;
+// NT = 1: the single tile over the 16 points 16 w .. 16 w + 15 of each group.
+// MODE: 1 spectral part only (grad_x = s(x) * spectral), 3 block, 7 block with GELU' (z read).
+template <int C, bool BF, bool TANH, int MODE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C == 64 ? 2 : 3)))
+k_epi_bwd_line(EpiArgs a) {
   constexpr int CP = (C + 15) / 16 * 16;
   constexpr int NT = CP / 16;
   constexpr int TMW = NT;
   constexpr int NPT = NT;
+  constexpr bool BLK = (MODE & 2) != 0;
+  constexpr bool GL = (MODE & 4) != 0;
+  constexpr bool NX = BLK || TANH;  // x rows needed
   constexpr int DT = (NT == 4) ? 4 : 1;  // dWb tiles per wave
-  __shared__ __attribute__((aligned(16))) float s_gz[CP * XS];
-  __shared__ __attribute__((aligned(16))) float s_x[CP * XS];
+  __shared__ __attribute__((aligned(16))) float s_gz[BLK ? CP * XS : 4];
+  __shared__ __attribute__((aligned(16))) float s_x[NX ? CP * XS : 4];
+  __shared__ __attribute__((aligned(16))) float s_o[CP * XS];
   __shared__ __attribute__((aligned(16))) unsigned char s_tl[CP * (kMaxKpad + 8) * (BF ? 2 : 4)];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, q = lane >> 4;
   const int ct = wave % NT, tbase = (wave / NT) * TMW;
-  const bool want_gx = a.y != nullptr;
-  const bool need_x = a.block || TANH;
-  // GEMM1 B operand, K-step kb, lane (n = m, q): Wb[o = 4 kb + q][i = 16 ct + m]
-  float wbr[C / 4];
-  {
+  const int64_t wg_per_b = a.lines / a.lpw;
+  const int b = (int)(blockIdx.x / wg_per_b);
+  const int64_t l0 = (int64_t)(blockIdx.x - (int64_t)b * wg_per_b) * a.lpw;
+  const int gpl = 1 << a.gpl_log2;
+  const int nf = a.lpw << a.gpl_log2;
+  // bypass B operand, K-step kb, lane (n = m, q): Wb[o = 4 kb + q][i = 16 ct + m]
+  float wbr[BLK ? C / 4 : 1];
+  if (BLK) {
     const int i = 16 * ct + m;
 #pragma unroll
-    for (int kb = 0; kb < C / 4; ++kb)
-      wbr[kb] = (a.block && i < C) ? a.wb[(4 * kb + q) * C + i] : 0.f;
+    for (int kb = 0; kb < C / 4; ++kb) wbr[kb] = 0.f;
+    if (i < C) {
+#pragma unroll
+      for (int kb = 0; kb < C / 4; ++kb) wbr[kb] = a.wb[(4 * kb + q) * C + i];
+    }
   }
   const int mo = (NT == 4) ? wave : (NT == 2 ? (wave >> 1) : 0);
   const int ni0 = (NT == 2) ? (wave & 1) : 0;
@@ -386,96 +360,118 @@ __global__ void __launch_bounds__(256) k_epi_bwd_fast(EpiArgs a) {
 #pragma unroll
   for (int u = 0; u < DT; ++u) dwb[u] = zero4();
   float dbl = 0.f;
-  const int64_t g_begin = (int64_t)blockIdx.x * a.pg_per_wg;
-  const int64_t g_end = min(a.npg, g_begin + a.pg_per_wg);
+  const int64_t pbase = l0 * a.Nb;
+  const int64_t rowoff = ((int64_t)b * C + (tid >> 4)) * a.P + pbase + 4 * (tid & 15);
+  const int64_t ustride = 16 * a.P;
   float4 pg_y[NPT], pz[NPT], px[NPT];
-  GtFrag<TMW, BF> gtf;
-  if (g_begin < g_end) {
-    load_bwd_tiles<C, NPT>(a, g_begin, tid, need_x, pg_y, pz, px);
-    if (want_gx) load_gt<TMW, BF>(a, group_pos(a, g_begin).pb0, tbase, m, q, gtf);
-  }
-  int64_t cur_line = -1;
-  for (int64_t pg = g_begin; pg < g_end; ++pg) {
-    const GroupPos gp = group_pos(a, pg);
-    __syncthreads();
-    if (want_gx && gp.gline != cur_line) {
-      const float2* Trow0 = a.T + ((int64_t)gp.b * C * a.lines + (gp.gline - (int64_t)gp.b * a.lines)) * a.mb;
-      stage_line<C, BF>(a, Trow0, s_tl, tid);
-      cur_line = gp.gline;
-    }
 #pragma unroll
-    for (int u = 0; u < NPT; ++u) {
-      const int e = tid + 256 * u;
-      const int c = e >> 4, c4 = e & 15;
-      float4 g = pg_y[u];
-      if (a.gelu) {
-        g.x *= gelu_grad_as(pz[u].x);
-        g.y *= gelu_grad_as(pz[u].y);
-        g.z *= gelu_grad_as(pz[u].z);
-        g.w *= gelu_grad_as(pz[u].w);
+  for (int u = 0; u < NPT; ++u) {
+    pg_y[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    pz[u] = pg_y[u];
+    px[u] = pg_y[u];
+  }
+  GtFrag<TMW, BF> gtf;
+  if (BLK) load_rows<C, NPT>(pg_y, a.gy + rowoff, ustride, tid);
+  if (GL) load_rows<C, NPT>(pz, a.zin + rowoff, ustride, tid);
+  if (NX) load_rows<C, NPT>(px, a.x + rowoff, ustride, tid);
+  load_gt<TMW, BF, true>(a, 0, tbase, m, q, gtf);
+  for (int lf = 0; lf < a.lpw; ++lf) {
+    // every reader of the previous line's spectrum is past that line's last barrier
+    const float2* Trow0 = a.T + ((int64_t)b * C * a.lines + l0 + lf) * a.mb;
+    stage_line<C, BF>(a, Trow0, s_tl, tid);
+    for (int g = 0; g < gpl; ++g) {
+      const int f = (lf << a.gpl_log2) + g;
+      const int fn = min(f + 1, nf - 1);
+#pragma unroll
+      for (int u = 0; u < NPT; ++u) {
+        const int e = tid + 256 * u;
+        if ((16 * C) % 256 == 0 || e < 16 * C) {
+          const int lo = (e >> 4) * XS + 4 * (e & 15);
+          if (BLK) {
+            float4 gz = pg_y[u];
+            if (GL) {
+              gz.x *= gelu_grad_as(pz[u].x);
+              gz.y *= gelu_grad_as(pz[u].y);
+              gz.z *= gelu_grad_as(pz[u].z);
+              gz.w *= gelu_grad_as(pz[u].w);
+            }
+            *reinterpret_cast<float4*>(s_gz + lo) = gz;
+          }
+          if (NX) *reinterpret_cast<float4*>(s_x + lo) = px[u];
+        }
       }
-      *reinterpret_cast<float4*>(s_gz + c * XS + 4 * c4) = g;
-      *reinterpret_cast<float4*>(s_x + c * XS + 4 * c4) = px[u];
-    }
-    if (pg + 1 < g_end) load_bwd_tiles<C, NPT>(a, pg + 1, tid, need_x, pg_y, pz, px);
-    __syncthreads();
-    if (want_gx) {
+      if (BLK) load_rows<C, NPT>(pg_y, a.gy + rowoff + 64 * fn, ustride, tid);
+      if (GL) load_rows<C, NPT>(pz, a.zin + rowoff + 64 * fn, ustride, tid);
+      if (NX) load_rows<C, NPT>(px, a.x + rowoff + 64 * fn, ustride, tid);
+      __syncthreads();  // g_z / x tiles and spectrum rows visible; previous grad tile consumed
       f32x4 acc[TMW];
 #pragma unroll
       for (int j = 0; j < TMW; ++j) acc[j] = zero4();
       spectral_coop<C, TMW, BF>(a, s_tl, gtf, ct, m, q, acc);
-      if (pg + 1 < g_end) load_gt<TMW, BF>(a, group_pos(a, pg + 1).pb0, tbase, m, q, gtf);
+      load_gt<TMW, BF, true>(a, (fn & (gpl - 1)) * PG, tbase, m, q, gtf);
       const int i = 16 * ct + m;
       if (TANH) {
+        // lane (n = m, q), tile tbase + j, register r: channel i, point 16 q + 4 r + tbase + j
 #pragma unroll
-        for (int j = 0; j < TMW; ++j) {
-          const float4 xv = *reinterpret_cast<const float4*>(s_x + i * XS + 16 * (tbase + j) + 4 * q);
-          const float t0 = tanh_fast(xv.x), t1 = tanh_fast(xv.y), t2 = tanh_fast(xv.z), t3 = tanh_fast(xv.w);
-          acc[j][0] *= 1.f - t0 * t0;
-          acc[j][1] *= 1.f - t1 * t1;
-          acc[j][2] *= 1.f - t2 * t2;
-          acc[j][3] *= 1.f - t3 * t3;
+        for (int r = 0; r < 4; ++r) {
+          float xv[TMW];
+          load_lds_run<TMW>(xv, s_x + i * XS + 16 * q + 4 * r + tbase);
+#pragma unroll
+          for (int j = 0; j < TMW; ++j) {
+            const float t = tanh_fast(xv[j]);
+            acc[j][r] *= 1.f - t * t;
+          }
         }
       }
-      if (a.block) {
+      if (BLK) {
 #pragma unroll
-        for (int kb = 0; kb < C / 4; ++kb)
+        for (int kb = 0; kb < C / 4; ++kb) {
+          float av[TMW];
+          load_lds_run<TMW>(av, s_gz + (4 * kb + q) * XS + 4 * m + tbase);
 #pragma unroll
-          for (int j = 0; j < TMW; ++j)
-            acc[j] = mfma_f32(s_gz[(4 * kb + q) * XS + 16 * (tbase + j) + m], wbr[kb], acc[j]);
-      }
-      if (i < C) {
-#pragma unroll
-        for (int j = 0; j < TMW; ++j) {
-          const int64_t off = ((int64_t)gp.b * C + i) * a.P + gp.p0 + 16 * (tbase + j) + 4 * q;
-          *reinterpret_cast<float4*>(a.y + off) =
-              make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+          for (int j = 0; j < TMW; ++j) acc[j] = mfma_f32(av[j], wbr[kb], acc[j]);
         }
       }
-    }
-    if (a.block) {
-      // dWb[o][i] += sum_points g_z[o][p] x[i][p]; k-slot q of MFMA jj <-> point 16 g + 4 q + jj
-      const int g_lo = (NT == 1) ? wave : 0;
-      const int g_hi = (NT == 1) ? wave + 1 : PG / 16;
-      for (int g = g_lo; g < g_hi; ++g) {
-        const float4 av = *reinterpret_cast<const float4*>(s_gz + (16 * mo + m) * XS + 16 * g + 4 * q);
-        if (count_db) dbl += (av.x + av.y) + (av.z + av.w);
 #pragma unroll
-        for (int u = 0; u < DT; ++u) {
-          const int ni = (NT == 4) ? u : ni0;
-          const float4 bv = *reinterpret_cast<const float4*>(s_x + (16 * ni + m) * XS + 16 * g + 4 * q);
-          dwb[u] = mfma_f32(av.x, bv.x, dwb[u]);
-          dwb[u] = mfma_f32(av.y, bv.y, dwb[u]);
-          dwb[u] = mfma_f32(av.z, bv.z, dwb[u]);
-          dwb[u] = mfma_f32(av.w, bv.w, dwb[u]);
+      for (int r = 0; r < 4; ++r) {
+        float v[TMW];
+#pragma unroll
+        for (int j = 0; j < TMW; ++j) v[j] = acc[j][r];
+        store_lds_run<TMW>(s_o + i * XS + 16 * q + 4 * r + tbase, v);
+      }
+      if (BLK) {
+        // dWb[o][i] += sum_points g_z[o][p] x[i][p]; k-slot q of MFMA jj <-> point 16 h + 4 q + jj
+        const int h_lo = (NT == 1) ? wave : 0;
+        const int h_hi = (NT == 1) ? wave + 1 : PG / 16;
+        for (int h = h_lo; h < h_hi; ++h) {
+          const float4 av = *reinterpret_cast<const float4*>(s_gz + (16 * mo + m) * XS + 16 * h + 4 * q);
+          if (count_db) dbl += (av.x + av.y) + (av.z + av.w);
+#pragma unroll
+          for (int u = 0; u < DT; ++u) {
+            const int ni = (NT == 4) ? u : ni0;
+            const float4 bv = *reinterpret_cast<const float4*>(s_x + (16 * ni + m) * XS + 16 * h + 4 * q);
+            dwb[u] = mfma_f32(av.x, bv.x, dwb[u]);
+            dwb[u] = mfma_f32(av.y, bv.y, dwb[u]);
+            dwb[u] = mfma_f32(av.z, bv.z, dwb[u]);
+            dwb[u] = mfma_f32(av.w, bv.w, dwb[u]);
+          }
+        }
+      }
+      __syncthreads();  // grad tile complete; g_z / x tiles free
+#pragma unroll
+      for (int u = 0; u < NPT; ++u) {
+        const int e = tid + 256 * u;
+        if ((16 * C) % 256 == 0 || e < 16 * C) {
+          const float4 v = *reinterpret_cast<const float4*>(s_o + (e >> 4) * XS + 4 * (e & 15));
+          *reinterpret_cast<float4*>(a.y + rowoff + u * ustride + 64 * f) = v;
         }
       }
     }
   }
-  if (!a.block || !a.part) return;
+  if (!BLK || !a.part) return;
   // Deterministic work-group reduction (fixed wave order) into LDS, then one partial row.
-  float* s_red = s_gz;             // [C][CP] dWb
-  float* s_db = s_x;               // [4 waves][4 q][CP] dbias partials
+  float* s_red = s_gz;  // [C][CP] dWb
+  float* s_db = s_x;    // [4 waves][4 q][CP] dbias partials
   __syncthreads();
   for (int e = tid; e < C * CP; e += 256) s_red[e] = 0.f;
   for (int e = tid; e < 16 * CP; e += 256) s_db[e] = 0.f;
@@ -487,8 +483,8 @@ __global__ void __launch_bounds__(256) k_epi_bwd_fast(EpiArgs a) {
         const int ni = (NT == 4) ? u : ni0;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int o = 16 * mo + 4 * q + r, i = 16 * ni + m;
-          if (o < C) s_red[o * CP + i] += dwb[u][r];
+          const int o = 16 * mo + 4 * q + r, ii = 16 * ni + m;
+          if (o < C) s_red[o * CP + ii] += dwb[u][r];
         }
       }
       s_db[(w * 4 + q) * CP + 16 * mo + m] += dbl;
@@ -499,8 +495,8 @@ __global__ void __launch_bounds__(256) k_epi_bwd_fast(EpiArgs a) {
   for (int e = tid; e < C * C + C; e += 256) {
     float v;
     if (e < C * C) {
-      const int o = e / C, i = e - o * C;
-      v = s_red[o * CP + i];
+      const int o = e / C, ii = e - o * C;
+      v = s_red[o * CP + ii];
     } else {
       const int o = e - C * C;
       v = 0.f;
@@ -529,18 +525,28 @@ static hipError_t launch_fwd_c(const EpiArgs& a, bool bf, int mode, int wgs, hip
 }
 
 template <int C>
-static hipError_t launch_bwd_c(const EpiArgs& a, bool bf, bool tanh_pre, int wgs, hipStream_t s) {
+static hipError_t launch_bwd_c(const EpiArgs& a, bool bf, bool tanh_pre, int mode, int wgs,
+                               hipStream_t s) {
+#define FNO_EPI_BWD(BFV, TV, MV) \
+  hipLaunchKernelGGL((k_epi_bwd_line<C, BFV, TV, MV>), dim3(wgs), dim3(256), 0, s, a)
+#define FNO_EPI_BWD_M(BFV, TV)    \
+  do {                            \
+    if (mode == 1)                \
+      FNO_EPI_BWD(BFV, TV, 1);    \
+    else if (mode == 3)           \
+      FNO_EPI_BWD(BFV, TV, 3);    \
+    else                          \
+      FNO_EPI_BWD(BFV, TV, 7);    \
+  } while (0)
   if (bf) {
-    if (tanh_pre)
-      hipLaunchKernelGGL((k_epi_bwd_fast<C, true, true>), dim3(wgs), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((k_epi_bwd_fast<C, true, false>), dim3(wgs), dim3(256), 0, s, a);
+    if (tanh_pre) FNO_EPI_BWD_M(true, true);
+    else FNO_EPI_BWD_M(true, false);
   } else {
-    if (tanh_pre)
-      hipLaunchKernelGGL((k_epi_bwd_fast<C, false, true>), dim3(wgs), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((k_epi_bwd_fast<C, false, false>), dim3(wgs), dim3(256), 0, s, a);
+    if (tanh_pre) FNO_EPI_BWD_M(false, true);
+    else FNO_EPI_BWD_M(false, false);
   }
+#undef FNO_EPI_BWD_M
+#undef FNO_EPI_BWD
   return hipGetLastError();
 }
 
@@ -553,28 +559,6 @@ bool epilogue_fast_ok(const fno_plan* p, int mode, bool fwd) {
   const int gpl = g.Nb / 64;  // point groups per line: a power of two (shift / mask indexing)
   if ((gpl & (gpl - 1)) != 0) return false;
   return true;
-}
-
-static EpiArgs make_args(const fno_plan* p, int C, int pg_points, int wgs_cap, int* wgs) {
-  const Geom& g = p->g;
-  EpiArgs a{};
-  a.B = g.B;
-  a.C = C;
-  a.P = g.P;
-  a.Nb = g.Nb;
-  a.mb = g.mb;
-  a.kpad = p->kpad;
-  a.lines = g.P / g.Nb;
-  a.npg = (int64_t)g.B * (g.P / pg_points);
-  int64_t w = (a.npg + 3) / 4;
-  if (w > wgs_cap) w = wgs_cap;
-  if (w < 1) w = 1;
-  a.pg_per_wg = (a.npg + w - 1) / w;
-  int64_t per_line = g.Nb / pg_points;  // keep whole lines in one work-group
-  if (per_line < 1) per_line = 1;
-  a.pg_per_wg = (a.pg_per_wg + per_line - 1) / per_line * per_line;
-  *wgs = (int)((a.npg + a.pg_per_wg - 1) / a.pg_per_wg);
-  return a;
 }
 
 // Lines per forward work-group: the largest power of two dividing the lines of a batch entry
@@ -623,11 +607,20 @@ hipError_t launch_epilogue_fwd_fast(const fno_plan* p, int mode, const float2* T
   }
 }
 
+// Lines per backward work-group: each work-group writes one row of bypass-gradient partials,
+// so it owns enough lines to keep the partials small (at least kBwdMinWgs work-groups still).
+constexpr int64_t kBwdMinWgs = 1024;
+
+static int bwd_lines_per_wg(int64_t lines, int64_t batch) {
+  int lpw = 1;
+  while (lines % (2 * lpw) == 0 && batch * lines / (2 * lpw) >= kBwdMinWgs) lpw *= 2;
+  return lpw;
+}
+
 int epilogue_bwd_fast_groups(const fno_plan* p) {
   if (!epilogue_fast_ok(p, EPI_BLOCK, false)) return 0;
-  int wgs = 0;
-  (void)make_args(p, p->g.Cin, PG, 1024, &wgs);
-  return wgs;
+  const int64_t lines = p->g.P / p->g.Nb;
+  return (int)((int64_t)p->g.B * lines / bwd_lines_per_wg(lines, p->g.B));
 }
 
 hipError_t launch_epilogue_bwd_fast(const fno_plan* p, int mode, const float2* Tg,
@@ -635,8 +628,18 @@ hipError_t launch_epilogue_bwd_fast(const fno_plan* p, int mode, const float2* T
                                     const float* z, float* grad_x, float* red_part,
                                     hipStream_t s) {
   const Geom& g = p->g;
-  int wgs = 0;
-  EpiArgs a = make_args(p, g.Cin, PG, 1024, &wgs);
+  EpiArgs a{};
+  a.B = g.B;
+  a.C = g.Cin;
+  a.P = g.P;
+  a.Nb = g.Nb;
+  a.mb = g.mb;
+  a.kpad = p->kpad;
+  a.lines = g.P / g.Nb;
+  a.lpw = bwd_lines_per_wg(a.lines, g.B);
+  int gl = 0;
+  while ((PG << gl) < g.Nb) ++gl;
+  a.gpl_log2 = gl;
   a.x = x;
   a.T = Tg;
   a.wb = wb;
@@ -646,13 +649,16 @@ hipError_t launch_epilogue_bwd_fast(const fno_plan* p, int mode, const float2* T
   a.zin = z;
   a.part = red_part;
   a.block = mode == EPI_BLOCK;
-  a.gelu = (p->desc.flags & FNO_FLAG_GELU) != 0;
+  a.gelu = z != nullptr;
   const bool tanh_pre = (p->desc.flags & FNO_FLAG_TANH_PREACT) != 0;
+  const int kmode = mode != EPI_BLOCK ? 1 : (z ? 7 : 3);
+  const int64_t wgs = (int64_t)g.B * a.lines / a.lpw;
+  if (wgs > 0x7fffffff) return hipErrorInvalidValue;
   switch (g.Cin) {
-    case 16: return launch_bwd_c<16>(a, g.bf16, tanh_pre, wgs, s);
-    case 20: return launch_bwd_c<20>(a, g.bf16, tanh_pre, wgs, s);
-    case 32: return launch_bwd_c<32>(a, g.bf16, tanh_pre, wgs, s);
-    default: return launch_bwd_c<64>(a, g.bf16, tanh_pre, wgs, s);
+    case 16: return launch_bwd_c<16>(a, g.bf16, tanh_pre, kmode, (int)wgs, s);
+    case 20: return launch_bwd_c<20>(a, g.bf16, tanh_pre, kmode, (int)wgs, s);
+    case 32: return launch_bwd_c<32>(a, g.bf16, tanh_pre, kmode, (int)wgs, s);
+    default: return launch_bwd_c<64>(a, g.bf16, tanh_pre, kmode, (int)wgs, s);
   }
 }
 

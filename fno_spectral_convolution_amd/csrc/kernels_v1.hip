@@ -439,7 +439,7 @@ k_epilogue_bwd(Geom g, int mode, bool gelu, bool tanh_pre, const float2* __restr
 hipError_t launch_epilogue_bwd(const fno_plan* p, int mode, const float2* Tg, const float* x,
                                const float* wb, const float* gy, const float* z,
                                float* grad_x, float* red_part, hipStream_t s) {
-  if (epilogue_fast_ok(p, mode, false))
+  if (epilogue_bwd_fast(p, mode, grad_x))
     return launch_epilogue_bwd_fast(p, mode, Tg, x, wb, gy, z, grad_x, red_part, s);
   const Geom& g = p->g;
   const int64_t tiles = (g.P + kEbThreads - 1) / kEbThreads;
@@ -492,10 +492,10 @@ k_bypass_finish(const float* __restrict__ part, int nparts, int cout, int cin,
 }
 
 hipError_t launch_bypass_grad_finish(const fno_plan* p, const float* red_part, float* dwb,
-                                     float* dbias, hipStream_t s) {
+                                     float* dbias, const float* grad_x, hipStream_t s) {
   const Geom& g = p->g;
   const int npair = g.Cout * g.Cin + g.Cout;
-  const int nparts = epilogue_fast_ok(p, EPI_BLOCK, false) ? epilogue_bwd_fast_groups(p) : p->nred;
+  const int nparts = epilogue_bwd_fast(p, EPI_BLOCK, grad_x) ? epilogue_bwd_fast_groups(p) : p->nred;
   hipLaunchKernelGGL(k_bypass_finish, dim3((npair + 63) / 64), dim3(256), 0, s, red_part,
                      nparts, g.Cout, g.Cin, dwb, dbias);
   return hipGetLastError();

@@ -780,7 +780,7 @@ fno_status fno_block_bwd(const fno_plan* p, const float* x, const float* w, cons
     }
     LAUNCH("epilogue_bwd", s, fno::launch_epilogue_bwd(p, fno::EPI_BLOCK, Tg, x, wb, gy, z, grad_x, red, s));
     if (red)
-      LAUNCH("bypass_grad_finish", s, fno::launch_bypass_grad_finish(p, red, grad_wb, grad_bias, s));
+      LAUNCH("bypass_grad_finish", s, fno::launch_bypass_grad_finish(p, red, grad_wb, grad_bias, grad_x, s));
   }
   return FNO_OK;
 }
