@@ -1,175 +1,270 @@
-// Per-mode complex channel mix of the FNO block and its two gradients:
+// Per-mode complex channel mix of the FNO block and its two gradients, on the matrix cores:
 //   forward   yhat[b,o,t] = sum_i xhat[b,i,t] W[c(t),i,o,kappa(t)]
-//   input     ghx[b,i,t]  = sum_o ghat[b,o,t] conj(W[c(t),i,o,kappa(t)])
-//   weight    dW[c,i,o,k] = sum_b conj(xhat[b,i,t]) ghat[b,o,t]
-// with ghat scaled by gamma(k_last)/Ntot (the adjoint of the inverse transform).  The mix
-// streams W once and is bound by that HBM read (B complex products per weight), so it runs
-// on the vector ALUs: each thread owns one mode and kMixOB channels, keeps a batch tile of
-// accumulators in registers and reads consecutive modes of W (and of the spectra) with its
-// neighbours, so every load is coalesced.  On the mixed path every operand is rounded to
-// bfloat16 before the product (the half-precision contraction of the mixed-precision
-// neural-operator page, "Tiivistelmä"); accumulation is float32.
+//   input     ghx[b,i,t]  = sum_o g[b,o,t] conj(W[c(t),i,o,kappa(t)])
+//   weight    dW[c,i,o,k] = sum_b conj(xhat[b,i,t]) g[b,o,t]
+// with g = ghat scaled by gamma(k_last)/Ntot (the adjoint of the inverse transform).  This is
+// the per-mode contraction of the FNO spectral layer (model-parallel FNO page, "Proposed
+// method"); on the mixed path every operand is rounded to bfloat16 and products accumulate in
+// float32 (mixed-precision neural-operator page, "Tiivistelmä").
+//
+// Each mode's complex product is one real GEMM with the real and imaginary parts stacked:
+//   rows  = 2 x 8 (re / im part x 8 batch entries, or x 8 input channels for dW)
+//   K     = 2 x (contracted channels or batch entries), pairs (re, im)
+//   cols  = 16 output (or input) channels
+// e.g. forward: A[b][2i] = xr, A[b][2i+1] = -xi, A[8+b][2i] = xi, A[8+b][2i+1] = xr,
+//               B[2i][o] = wr, B[2i+1][o] = wi   ->   D[b][o] = Re y, D[8+b][o] = Im y.
+// A work-group owns 16 consecutive modes (their weights are 128-byte runs of W) and one
+// 16-column tile; it streams K-chunks through LDS in fragment order (16 B per lane per
+// fragment), prefetching the next chunk into registers.  bf16 path: 16x16x32 MFMA, chunk K =
+// 32; fp32 path: 16x16x4 MFMA, chunk K = 16 (k-slot q of step s <-> k = 4 q + s).  Results
+// pass through LDS so the stores are 128-byte runs of modes as well.  The mix streams W once
+// and is bound by that read (or, for dW, by its write).
 #include "fno_internal.h"
+#include "mfma.h"
 
 namespace fno {
 
-constexpr int kMixOB = 4;  // output channels per thread
-constexpr int kMixBT = 8;  // batch entries per pass
+constexpr int kMT = 16;                 // modes per work-group
+constexpr int kRowB = 64;               // bytes per LDS fragment row (32 bf16 or 16 f32)
+constexpr int kTB = 16 * kRowB + 16;    // bytes per mode of a [16 rows][K chunk] LDS tile
+constexpr int kOutTB = 8 * 16 * 8 + 16;  // bytes per mode of the [8][16] complex output tile
 
-__device__ __forceinline__ float mround(float v, bool bf) {
-  if (!bf) return v;
-  uint32_t u = __float_as_uint(v);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return __uint_as_float(u & 0xffff0000u);
-}
-
-__device__ __forceinline__ float mix_adj_scale(const Geom& g, int64_t t) {
+__device__ __forceinline__ float mix_scale(const Geom& g, int64_t t) {
   const int kb = (int)(t % g.mb);
   const bool one = (kb == 0) || (2 * kb == g.Nb);
   return (one ? 1.0f : 2.0f) * g.inv_ntot;
 }
 
-__global__ void __launch_bounds__(256)
-k_mix_fwd_blk(Geom g, const int32_t* __restrict__ mode_woff, const float2* __restrict__ xhat,
-              const float2* __restrict__ w, float2* __restrict__ yhat) {
+// (v0, v1) into K slots (k, k + 1) of row r of mode tile t
+template <bool BF>
+__device__ __forceinline__ void put_pair(unsigned char* tile, int t, int r, int k, float v0,
+                                         float v1) {
+  unsigned char* p = tile + t * kTB + r * kRowB + k * (BF ? 2 : 4);
+  if constexpr (BF) {
+    *reinterpret_cast<uint32_t*>(p) = (uint32_t)bf16_bits(v0) | ((uint32_t)bf16_bits(v1) << 16);
+  } else {
+    *reinterpret_cast<float2*>(p) = make_float2(v0, v1);
+  }
+}
+
+// acc += A_t x B_t over one LDS chunk (lane (m, q) reads 16 B of row m of both tiles)
+template <bool BF>
+__device__ __forceinline__ f32x4 chunk_product(const unsigned char* ta, const unsigned char* tb,
+                                               int t, int m, int q, f32x4 acc) {
+  const int off = t * kTB + m * kRowB + 16 * q;
+  if constexpr (BF) {
+    const bf16x8 av = *reinterpret_cast<const bf16x8*>(ta + off);
+    const bf16x8 bv = *reinterpret_cast<const bf16x8*>(tb + off);
+    return mfma_bf16(av, bv, acc);
+  } else {
+    const float4 av = *reinterpret_cast<const float4*>(ta + off);
+    const float4 bv = *reinterpret_cast<const float4*>(tb + off);
+    acc = mfma_f32(av.x, bv.x, acc);
+    acc = mfma_f32(av.y, bv.y, acc);
+    acc = mfma_f32(av.z, bv.z, acc);
+    return mfma_f32(av.w, bv.w, acc);
+  }
+}
+
+// D fragment of mode tile t (rows 4 q + r: part (4q+r) / 8, entry (4q+r) % 8; column m) into
+// the complex output tile [t][entry][column]
+__device__ __forceinline__ void put_out(unsigned char* out, int t, int m, int q, const f32x4& d) {
+  float* base = reinterpret_cast<float*>(out + t * kOutTB) + (q >> 1);  // re or im half
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int e = 4 * (q & 1) + r;
+    base[2 * (e * 16 + m)] = d[r];
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Forward (DX = false) and input gradient (DX = true).  Grid: (mode groups, 16-column tiles of
+// the output channels, 8-entry batch tiles).  Contracted channels: Cin (forward) or Cout.
+template <bool BF, bool DX>
+__global__ void __launch_bounds__(256) k_mix_mfma(Geom g, const int32_t* __restrict__ mode_woff,
+                                                  const float2* __restrict__ spec,
+                                                  const float2* __restrict__ w,
+                                                  float2* __restrict__ out) {
+  constexpr int IC = BF ? 16 : 8;  // contracted channels per chunk (K = 2 IC)
+  constexpr int NW = 16 * IC / 16;  // weight complex values per thread per chunk (16 modes x IC x 16 cols / 256)
+  constexpr int NS = 8 * IC / 16;   // spectrum values per thread per chunk (16 modes x 8 x IC / 256)
+  __shared__ __attribute__((aligned(16))) unsigned char s_a[kMT * kTB];
+  __shared__ __attribute__((aligned(16))) unsigned char s_b[kMT * kTB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, q = lane >> 4;
   const int64_t K = g.K;
-  const int nob = (g.Cout + kMixOB - 1) / kMixOB;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)nob * K) return;
-  const int ob = (int)(idx / K);
-  const int64_t t = idx - (int64_t)ob * K;
-  const int o0 = ob * kMixOB;
-  const bool bf = g.bf16;
-  const int64_t wb0 = mode_woff[t] + (int64_t)o0 * g.Mprod;
-  const int64_t wsi = (int64_t)g.Cout * g.Mprod;
-  for (int b0 = 0; b0 < g.B; b0 += kMixBT) {
-    const int nb = min(kMixBT, g.B - b0);
-    float2 acc[kMixOB][kMixBT];
+  const int ncon = DX ? g.Cout : g.Cin;  // contracted
+  const int nout = DX ? g.Cin : g.Cout;  // columns
+  const int64_t t0 = (int64_t)blockIdx.x * kMT;
+  const int n0 = blockIdx.y * 16;
+  const int b0 = blockIdx.z * 8;
+  // every load of this thread is for mode t0 + (tid & 15); offsets fit in 32 bits (fields and
+  // weights are limited to 2^31 elements)
+  const int tl = tid & 15;
+  const int tm = (int)min(t0 + tl, K - 1);
+  const int Ki = (int)K;
+  const float sc = DX ? mix_scale(g, tm) : 1.0f;
+  // weight u of this thread: contracted channel c0 + u, column n0 + (tid >> 4)
+  const int wsi = g.Cout * (int)g.Mprod;  // W stride of the input channel
+  const int ncol = min(n0 + (tid >> 4), nout - 1);
+  const int wbase = mode_woff[tm] + (DX ? ncol * wsi : ncol * (int)g.Mprod);
+  const int wstep = DX ? (int)g.Mprod : wsi;
+  float2 pw[NW], ps[NS];
+  auto load_chunk = [&](int c0) {
 #pragma unroll
-    for (int j = 0; j < kMixOB; ++j)
+    for (int u = 0; u < NW; ++u) pw[u] = w[wbase + min(c0 + u, ncon - 1) * wstep];
 #pragma unroll
-      for (int b = 0; b < kMixBT; ++b) acc[j][b] = make_float2(0.f, 0.f);
-    for (int ci = 0; ci < g.Cin; ++ci) {
-      float2 wv[kMixOB];
+    for (int u = 0; u < NS; ++u) {
+      const int pr = (tid >> 4) + 16 * u;
+      const int b = min(b0 + pr / IC, g.B - 1), cc = min(c0 + pr % IC, ncon - 1);
+      ps[u] = spec[(b * ncon + cc) * Ki + tm];
+    }
+  };
+  f32x4 acc[4];
 #pragma unroll
-      for (int j = 0; j < kMixOB; ++j) {
-        float2 v = make_float2(0.f, 0.f);
-        if (o0 + j < g.Cout) v = w[wb0 + ci * wsi + (int64_t)j * g.Mprod];
-        wv[j] = make_float2(mround(v.x, bf), mround(v.y, bf));
-      }
+  for (int j = 0; j < 4; ++j) acc[j] = zero4();
+  load_chunk(0);
+  for (int c0 = 0; c0 < ncon; c0 += IC) {
+    __syncthreads();  // previous chunk's fragments consumed
 #pragma unroll
-      for (int b = 0; b < kMixBT; ++b) {
-        if (b >= nb) break;
-        const float2 xv = xhat[((int64_t)(b0 + b) * g.Cin + ci) * K + t];
-        const float xr = mround(xv.x, bf), xi = mround(xv.y, bf);
-#pragma unroll
-        for (int j = 0; j < kMixOB; ++j) {
-          acc[j][b].x += xr * wv[j].x - xi * wv[j].y;
-          acc[j][b].y += xr * wv[j].y + xi * wv[j].x;
-        }
-      }
+    for (int u = 0; u < NW; ++u) {
+      const int pr = (tid >> 4) + 16 * u;
+      const int kc = pr / 16, n = pr % 16;
+      const bool ok = c0 + kc < ncon && n0 + n < nout;
+      // B[2 kc][n] = wr, B[2 kc + 1][n] = wi (conj(W) is taken by the A layout of DX)
+      put_pair<BF>(s_b, tl, n, 2 * kc, ok ? pw[u].x : 0.f, ok ? pw[u].y : 0.f);
     }
 #pragma unroll
-    for (int j = 0; j < kMixOB; ++j) {
-      if (o0 + j >= g.Cout) break;
+    for (int u = 0; u < NS; ++u) {
+      const int pr = (tid >> 4) + 16 * u;
+      const int bb = pr / IC, kc = pr % IC;
+      const bool ok = c0 + kc < ncon && b0 + bb < g.B;
+      const float vr = ok ? ps[u].x * sc : 0.f, vi = ok ? ps[u].y * sc : 0.f;
+      if (DX) {  // (gr + i gi) conj(w): rows b: (gr, gi); rows 8 + b: (gi, -gr)
+        put_pair<BF>(s_a, tl, bb, 2 * kc, vr, vi);
+        put_pair<BF>(s_a, tl, 8 + bb, 2 * kc, vi, -vr);
+      } else {   // (xr + i xi) w: rows b: (xr, -xi); rows 8 + b: (xi, xr)
+        put_pair<BF>(s_a, tl, bb, 2 * kc, vr, -vi);
+        put_pair<BF>(s_a, tl, 8 + bb, 2 * kc, vi, vr);
+      }
+    }
+    load_chunk(min(c0 + IC, ncon - 1));
+    __syncthreads();
 #pragma unroll
-      for (int b = 0; b < kMixBT; ++b) {
-        if (b >= nb) break;
-        yhat[((int64_t)(b0 + b) * g.Cout + o0 + j) * K + t] = acc[j][b];
+    for (int j = 0; j < 4; ++j) acc[j] = chunk_product<BF>(s_a, s_b, 4 * wave + j, m, q, acc[j]);
+  }
+  __syncthreads();
+  unsigned char* s_out = s_a;  // [16 modes][8 entries][16 columns] complex
+#pragma unroll
+  for (int j = 0; j < 4; ++j) put_out(s_out, 4 * wave + j, m, q, acc[j]);
+  __syncthreads();
+  // out[b][n][t]: thread -> mode tl, (entry, column) pairs (tid >> 4) + 16 u
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int pr = (tid >> 4) + 16 * u;
+    const int bb = pr / 16, n = pr % 16;
+    const int64_t t = t0 + tl;
+    if (t < K && b0 + bb < g.B && n0 + n < nout) {
+      const float2 v =
+          *reinterpret_cast<const float2*>(s_out + tl * kOutTB + (bb * 16 + n) * 8);
+      out[((int64_t)(b0 + bb) * nout + n0 + n) * K + t] = v;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Weight gradient.  Grid: (mode groups, 8-channel tiles of Cin, 16-column tiles of Cout).
+// Rows 0..7: Re, rows 8..15: Im of the 8 input channels; K = (batch entry, re / im).
+template <bool BF>
+__global__ void __launch_bounds__(256) k_mix_mfma_dw(Geom g, const int32_t* __restrict__ mode_woff,
+                                                     const float2* __restrict__ xhat,
+                                                     const float2* __restrict__ ghat,
+                                                     float2* __restrict__ dw) {
+  constexpr int BC = BF ? 16 : 8;  // batch entries per chunk (K = 2 BC)
+  constexpr int NX = 8 * BC / 16;   // x values per thread per chunk (16 modes x 8 ch x BC / 256)
+  constexpr int NG = 16 * BC / 16;  // g values per thread per chunk (16 modes x 16 ch x BC / 256)
+  __shared__ __attribute__((aligned(16))) unsigned char s_a[kMT * kTB];
+  __shared__ __attribute__((aligned(16))) unsigned char s_b[kMT * kTB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, q = lane >> 4;
+  const int64_t K = g.K;
+  const int64_t t0 = (int64_t)blockIdx.x * kMT;
+  const int i0 = blockIdx.y * 8;
+  const int o0 = blockIdx.z * 16;
+  const int tl = tid & 15;
+  const int tm = (int)min(t0 + tl, K - 1);
+  const int Ki = (int)K;
+  const float sc = mix_scale(g, tm);
+  float2 px[NX], pg[NG];
+  // x value u: batch c0 + pr / 8, channel i0 + pr % 8; g value u: batch c0 + u, channel
+  // o0 + (tid >> 4)   (pr = (tid >> 4) + 16 u)
+  const int ocol = min(o0 + (tid >> 4), g.Cout - 1);
+  auto load_chunk = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < NX; ++u) {
+      const int pr = (tid >> 4) + 16 * u;
+      const int b = min(c0 + pr / 8, g.B - 1), i = min(i0 + pr % 8, g.Cin - 1);
+      px[u] = xhat[(b * g.Cin + i) * Ki + tm];
+    }
+#pragma unroll
+    for (int u = 0; u < NG; ++u) {
+      const int b = min(c0 + u, g.B - 1);
+      pg[u] = ghat[(b * g.Cout + ocol) * Ki + tm];
+    }
+  };
+  f32x4 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = zero4();
+  load_chunk(0);
+  for (int c0 = 0; c0 < g.B; c0 += BC) {
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < NX; ++u) {
+      const int pr = (tid >> 4) + 16 * u;
+      const int bb = pr / 8, ii = pr % 8;
+      const bool ok = c0 + bb < g.B && i0 + ii < g.Cin;
+      const float xr = ok ? px[u].x : 0.f, xi = ok ? px[u].y : 0.f;
+      // conj(x) g: rows i: (xr, xi); rows 8 + i: (-xi, xr)
+      put_pair<BF>(s_a, tl, ii, 2 * bb, xr, xi);
+      put_pair<BF>(s_a, tl, 8 + ii, 2 * bb, -xi, xr);
+    }
+#pragma unroll
+    for (int u = 0; u < NG; ++u) {
+      const int pr = (tid >> 4) + 16 * u;
+      const int bb = pr / 16, oo = pr % 16;
+      const bool ok = c0 + bb < g.B && o0 + oo < g.Cout;
+      put_pair<BF>(s_b, tl, oo, 2 * bb, ok ? pg[u].x * sc : 0.f, ok ? pg[u].y * sc : 0.f);
+    }
+    load_chunk(min(c0 + BC, g.B - 1));
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = chunk_product<BF>(s_a, s_b, 4 * wave + j, m, q, acc[j]);
+  }
+  __syncthreads();
+  unsigned char* s_out = s_a;  // [16 modes][8 input channels][16 output channels] complex
+#pragma unroll
+  for (int j = 0; j < 4; ++j) put_out(s_out, 4 * wave + j, m, q, acc[j]);
+  __syncthreads();
+  const int64_t t = t0 + tl;
+  if (t < K) {
+    const int64_t wmode = mode_woff[t];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int pr = (tid >> 4) + 16 * u;
+      const int ii = pr / 16, oo = pr % 16;
+      if (i0 + ii < g.Cin && o0 + oo < g.Cout) {
+        const float2 v =
+            *reinterpret_cast<const float2*>(s_out + tl * kOutTB + (ii * 16 + oo) * 8);
+        dw[wmode + ((int64_t)(i0 + ii) * g.Cout + o0 + oo) * g.Mprod] = v;
       }
     }
   }
 }
 
-__global__ void __launch_bounds__(256)
-k_mix_bwd_dx_blk(Geom g, const int32_t* __restrict__ mode_woff, const float2* __restrict__ ghat,
-                 const float2* __restrict__ w, float2* __restrict__ ghx) {
-  const int64_t K = g.K;
-  const int nib = (g.Cin + kMixOB - 1) / kMixOB;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)nib * K) return;
-  const int ib = (int)(idx / K);
-  const int64_t t = idx - (int64_t)ib * K;
-  const int i0 = ib * kMixOB;
-  const bool bf = g.bf16;
-  const float sc = mix_adj_scale(g, t);
-  const int64_t wb0 = mode_woff[t] + (int64_t)i0 * g.Cout * g.Mprod;
-  const int64_t wsi = (int64_t)g.Cout * g.Mprod;
-  for (int b0 = 0; b0 < g.B; b0 += kMixBT) {
-    const int nb = min(kMixBT, g.B - b0);
-    float2 acc[kMixOB][kMixBT];
-#pragma unroll
-    for (int j = 0; j < kMixOB; ++j)
-#pragma unroll
-      for (int b = 0; b < kMixBT; ++b) acc[j][b] = make_float2(0.f, 0.f);
-    for (int o = 0; o < g.Cout; ++o) {
-      float2 wv[kMixOB];
-#pragma unroll
-      for (int j = 0; j < kMixOB; ++j) {
-        float2 v = make_float2(0.f, 0.f);
-        if (i0 + j < g.Cin) v = w[wb0 + (int64_t)j * wsi + (int64_t)o * g.Mprod];
-        wv[j] = make_float2(mround(v.x, bf), mround(v.y, bf));
-      }
-#pragma unroll
-      for (int b = 0; b < kMixBT; ++b) {
-        if (b >= nb) break;
-        const float2 gv = ghat[((int64_t)(b0 + b) * g.Cout + o) * K + t];
-        const float gr = mround(gv.x * sc, bf), gi = mround(gv.y * sc, bf);
-#pragma unroll
-        for (int j = 0; j < kMixOB; ++j) {  // (gr + i gi) conj(w)
-          acc[j][b].x += gr * wv[j].x + gi * wv[j].y;
-          acc[j][b].y += gi * wv[j].x - gr * wv[j].y;
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < kMixOB; ++j) {
-      if (i0 + j >= g.Cin) break;
-#pragma unroll
-      for (int b = 0; b < kMixBT; ++b) {
-        if (b >= nb) break;
-        ghx[((int64_t)(b0 + b) * g.Cin + i0 + j) * K + t] = acc[j][b];
-      }
-    }
-  }
-}
-
-// One thread per (mode, input channel, block of kMixOB output channels).
-__global__ void __launch_bounds__(256)
-k_mix_bwd_dw_blk(Geom g, const int32_t* __restrict__ mode_woff, const float2* __restrict__ xhat,
-                 const float2* __restrict__ ghat, float2* __restrict__ dw) {
-  const int64_t K = g.K;
-  const int nob = (g.Cout + kMixOB - 1) / kMixOB;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)g.Cin * nob * K) return;
-  const int64_t t = idx % K;
-  const int64_t r = idx / K;
-  const int ob = (int)(r % nob);
-  const int ci = (int)(r / nob);
-  const int o0 = ob * kMixOB;
-  const bool bf = g.bf16;
-  const float sc = mix_adj_scale(g, t);
-  float2 acc[kMixOB];
-#pragma unroll
-  for (int j = 0; j < kMixOB; ++j) acc[j] = make_float2(0.f, 0.f);
-  for (int b = 0; b < g.B; ++b) {
-    const float2 xv = xhat[((int64_t)b * g.Cin + ci) * K + t];
-    const float xr = mround(xv.x, bf), xi = mround(xv.y, bf);
-#pragma unroll
-    for (int j = 0; j < kMixOB; ++j) {
-      if (o0 + j >= g.Cout) break;
-      const float2 gv = ghat[((int64_t)b * g.Cout + o0 + j) * K + t];
-      const float gr = mround(gv.x * sc, bf), gi = mround(gv.y * sc, bf);
-      acc[j].x += xr * gr + xi * gi;  // conj(x) g
-      acc[j].y += xr * gi - xi * gr;
-    }
-  }
-  const int64_t wbase = mode_woff[t] + ((int64_t)ci * g.Cout + o0) * g.Mprod;
-#pragma unroll
-  for (int j = 0; j < kMixOB; ++j) {
-    if (o0 + j >= g.Cout) break;
-    dw[wbase + (int64_t)j * g.Mprod] = acc[j];
-  }
+// ------------------------------------------------------------------------------------------
+static dim3 mix_grid(const Geom& g, int cols) {
+  return dim3((unsigned)((g.K + kMT - 1) / kMT), (unsigned)((cols + 15) / 16),
+              (unsigned)((g.B + 7) / 8));
 }
 
 hipError_t launch_mix_fwd(const fno_plan* p, const float2* xhat, int nparts,
@@ -177,27 +272,38 @@ hipError_t launch_mix_fwd(const fno_plan* p, const float2* xhat, int nparts,
   (void)nparts;
   (void)part_stride;
   const Geom& g = p->g;
-  const int64_t total = (int64_t)((g.Cout + kMixOB - 1) / kMixOB) * g.K;
-  hipLaunchKernelGGL(k_mix_fwd_blk, dim3((unsigned)((total + 63) / 64)), dim3(64), 0, s, g,
-                     p->t.mode_woff, xhat, w, yhat);
+  if (g.bf16)
+    hipLaunchKernelGGL((k_mix_mfma<true, false>), mix_grid(g, g.Cout), dim3(256), 0, s, g,
+                       p->t.mode_woff, xhat, w, yhat);
+  else
+    hipLaunchKernelGGL((k_mix_mfma<false, false>), mix_grid(g, g.Cout), dim3(256), 0, s, g,
+                       p->t.mode_woff, xhat, w, yhat);
   return hipGetLastError();
 }
 
 hipError_t launch_mix_bwd_dx(const fno_plan* p, const float2* ghat, const float2* w,
                              float2* ghx, hipStream_t s) {
   const Geom& g = p->g;
-  const int64_t total = (int64_t)((g.Cin + kMixOB - 1) / kMixOB) * g.K;
-  hipLaunchKernelGGL(k_mix_bwd_dx_blk, dim3((unsigned)((total + 63) / 64)), dim3(64), 0, s, g,
-                     p->t.mode_woff, ghat, w, ghx);
+  if (g.bf16)
+    hipLaunchKernelGGL((k_mix_mfma<true, true>), mix_grid(g, g.Cin), dim3(256), 0, s, g,
+                       p->t.mode_woff, ghat, w, ghx);
+  else
+    hipLaunchKernelGGL((k_mix_mfma<false, true>), mix_grid(g, g.Cin), dim3(256), 0, s, g,
+                       p->t.mode_woff, ghat, w, ghx);
   return hipGetLastError();
 }
 
 hipError_t launch_mix_bwd_dw(const fno_plan* p, const float2* xhat, const float2* ghat,
                              float2* dw, hipStream_t s) {
   const Geom& g = p->g;
-  const int64_t total = (int64_t)g.Cin * ((g.Cout + kMixOB - 1) / kMixOB) * g.K;
-  hipLaunchKernelGGL(k_mix_bwd_dw_blk, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
-                     g, p->t.mode_woff, xhat, ghat, dw);
+  const dim3 grid((unsigned)((g.K + kMT - 1) / kMT), (unsigned)((g.Cin + 7) / 8),
+                  (unsigned)((g.Cout + 15) / 16));
+  if (g.bf16)
+    hipLaunchKernelGGL((k_mix_mfma_dw<true>), grid, dim3(256), 0, s, g, p->t.mode_woff, xhat,
+                       ghat, dw);
+  else
+    hipLaunchKernelGGL((k_mix_mfma_dw<false>), grid, dim3(256), 0, s, g, p->t.mode_woff, xhat,
+                       ghat, dw);
   return hipGetLastError();
 }
 
