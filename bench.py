@@ -175,7 +175,7 @@ def measured_traffic(wl, kernel):
     return round(rec["fetch_bytes"] + rec["write_bytes"])
 
 
-def cpu_baseline(wl, sample_batch):
+def cpu_baseline(wl, sample_batch, min_seconds=10.0, max_reps=12):
     """The fp64 oracle, as it stands, on a bounded sample: one block's forward + backward for
     `sample_batch` batch entries of the workload (full grid and width)."""
     import numpy as np
@@ -193,19 +193,24 @@ def cpu_baseline(wl, sample_batch):
     x = g.standard_normal(shape).astype(np.float32)
     gy = g.standard_normal(shape).astype(np.float32) * 1e-3
     blk = inputs.block_params(wl, 1)[0]
+    what = "fwd+bwd" if wl.train else "fwd"
+    reps = 0
     t0 = time.perf_counter()
-    if wl.train:
-        O.block_bwd(x, blk["w"], blk["wb"], blk["bias"], wl.modes, gy, tanh=wl.mixed)
-        what = "fwd+bwd"
-    else:
-        O.block_fwd(x, blk["w"], blk["wb"], blk["bias"], wl.modes, tanh=wl.mixed)
-        what = "fwd"
-    dt = time.perf_counter() - t0
-    units = sb * wl.width * wl.points
+    # repeat the sample until about min_seconds of host work (bounded by max_reps)
+    while True:
+        if wl.train:
+            O.block_bwd(x, blk["w"], blk["wb"], blk["bias"], wl.modes, gy, tanh=wl.mixed)
+        else:
+            O.block_fwd(x, blk["w"], blk["wb"], blk["bias"], wl.modes, tanh=wl.mixed)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or reps >= max_reps:
+            break
+    units = reps * sb * wl.width * wl.points
     return {"value": units / dt, "unit": "grid-pts·ch/s", "cores": threads, "kind": "oracle",
             "sample": f"one block {what} (fp64 numpy oracle), batch {sb} of {wl.batch}, "
-                      f"width {wl.width}, grid {list(wl.grid)}, modes {list(wl.modes)}: "
-                      f"{dt:.2f} s",
+                      f"width {wl.width}, grid {list(wl.grid)}, modes {list(wl.modes)}, "
+                      f"repeated {reps}x: {dt:.2f} s",
             "seconds": round(dt, 3), "host_cpus": os.cpu_count()}
 
 
