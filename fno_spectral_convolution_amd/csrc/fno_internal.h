@@ -46,6 +46,7 @@ struct Tables {
   // f2 [4 ma][Na] (rows < 2 ma: cos, rows >= 2 ma: sin of 2 pi ka(s) row / Na)
   const float* t1;
   const uint16_t* t1_bf;
+  const uint16_t* t1t_bf;     // bf16 t1 transposed: [jpad][Nb]
   const float* f2;
   const uint16_t* f2_bf;      // bfloat16 of f2
   const uint16_t* f2_bf_lo;   // bfloat16 of (f2 - f2_bf): f2_bf + f2_bf_lo ~ f2 to 2^-16

@@ -20,6 +20,7 @@
 #include "pointwise.h"
 
 #include <math.h>
+#include <type_traits>
 
 namespace fno {
 
@@ -34,6 +35,7 @@ struct PlaneArgs {
   const void* t1;        // [Nb][jpad] f32, or bf16 bits
   const void* f2;        // [4ma][Na] f32, or bf16 bits (hi)
   const uint16_t* f2lo;  // bf16 residual of f2 (bf16 path)
+  const uint16_t* t1t;   // bf16 t1 transposed, [jpad][Nb]
   float2* out;           // [nch][planes][2ma][mb]
 };
 
@@ -52,8 +54,8 @@ __device__ __forceinline__ float cmp4(const float4& v, int j) {
 // Combine X2 (cos rows 0..2ma-1, sin rows 2ma..4ma-1, interleaved re/im columns) held in LDS
 // into the complex partial spectrum of this chunk.
 __device__ __forceinline__ void combine_store(const float* s_x2, int jpad, int ma, int mb,
-                                              float2* dst, int tid) {
-  for (int e = tid; e < 2 * ma * mb; e += 256) {
+                                              float2* dst, int tid, int nthreads = 256) {
+  for (int e = tid; e < 2 * ma * mb; e += nthreads) {
     const int sr = e / mb, k = e - sr * mb;
     const float* c = s_x2 + sr * jpad + 2 * k;
     const float* sn = s_x2 + (2 * ma + sr) * jpad + 2 * k;
@@ -348,6 +350,176 @@ __global__ void __launch_bounds__(256) k_plane_f32(PlaneArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
+// bf16 operands, 4 column tiles (jpad = 64), 512 threads.  The contiguous-axis table sits in
+// LDS, shared by the 8 waves, instead of in registers; this leaves room for twice the rows in
+// flight per CU.  Each sub-round stages 32 rows (double-buffered LDS tile, one barrier per
+// sub-round); wave w computes column tile w % 4 of M-tile w / 4.  Every 64 rows the outer-
+// axis product runs, its tiles (F2 M-tile, column tile) spread over the 8 waves.  The loop is
+// straight-line: rows past the chunk are loaded from a clamped row and staged as zeros, and
+// the F2 fragments of a stage are loaded at its start.
+template <int PIN, int NB>
+__global__ void __launch_bounds__(512) k_plane_bf16_lds(PlaneArgs a) {
+  constexpr int NTJ = 4;
+  constexpr int JP = 16 * NTJ;
+  constexpr int SUB = 32;               // rows per sub-round (2 M-tiles)
+  constexpr int SPS = 64 / SUB;         // sub-rounds per 64-row stage
+  constexpr int XS = NB + 8;            // bf16 row stride of the table and row tiles
+  constexpr int RS = 64 + 8;            // Rt row stride (bf16)
+  constexpr int KS = NB / 32;           // K-steps of the first product
+  constexpr int LPR = NB / 4;           // float4 per row
+  constexpr int NLD = SUB * LPR / 512;  // float4 per thread per sub-round and input
+  constexpr int NT2 = NTJ;              // second product: wave w owns F2 row tile w, all column tiles
+  static_assert(SUB * LPR % 512 == 0, "sub-round must split evenly");
+  static_assert(SPS == 2, "the loops below handle a 64-row stage as two sub-rounds");
+  constexpr std::integral_constant<bool, true> kTrue{};
+  constexpr std::integral_constant<bool, false> kFalse{};
+  constexpr int T1_B = JP * XS * 2, X_B = SUB * XS * 2, RT_B = JP * RS * 2;
+  constexpr int LOOP_B = T1_B + 2 * X_B + RT_B;
+  constexpr int END_B = 4 * kPlaneMaxModes * JP * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char s_raw[LOOP_B > END_B ? LOOP_B : END_B];
+  uint16_t* s_t1 = reinterpret_cast<uint16_t*>(s_raw);
+  uint16_t* s_xb = reinterpret_cast<uint16_t*>(s_raw + T1_B);  // two [SUB][XS] tiles
+  uint16_t* s_rt = reinterpret_cast<uint16_t*>(s_raw + T1_B + 2 * X_B);
+  float* s_x2 = reinterpret_cast<float*>(s_raw);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, q = lane >> 4;
+  const int jt = wave % NTJ, mt = wave / NTJ;
+  const int IT = a.ma / 4;  // 16-row tiles of F2 (4 ma rows)
+  const int64_t plane = blockIdx.x;
+  const int chunk = blockIdx.y;
+  const int r_begin = chunk * a.rows_per_chunk;
+  const int r_end = min(a.Na, r_begin + a.rows_per_chunk);
+  const int nsub = (r_end - r_begin + 63) / 64 * SPS;
+
+  // table -> LDS, [JP][XS] (row j = output column, K along the row)
+  for (int e = tid; e < JP * NB / 8; e += 512) {
+    const int j = e / (NB / 8), c8 = e % (NB / 8);
+    *reinterpret_cast<uint4*>(s_t1 + j * XS + 8 * c8) =
+        *reinterpret_cast<const uint4*>(a.t1t + (int64_t)j * NB + 8 * c8);
+  }
+  const float* base0 = a.in0 + plane * (int64_t)a.Na * NB;
+  const float* base1 = (PIN == PLANE_GELU_GRAD) ? a.in1 + plane * (int64_t)a.Na * NB : base0;
+  // thread's float4 u of sub-round n: row SUB n + (tid + 512 u) / LPR, column 4 ((tid + 512 u) % LPR)
+  const uint16_t* f2 = static_cast<const uint16_t*>(a.f2);
+  f32x4 x2[NT2];
+#pragma unroll
+  for (int k = 0; k < NT2; ++k) x2[k] = zero4();
+  bf16x8 fh[2], fl[2];  // this wave's F2 row tile, both K-steps of a stage (hi, lo)
+  auto load_sub = [&](int n, float4 (&d0)[NLD], float4 (&d1)[NLD]) {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int e = tid + 512 * u;
+      const int row = min(r_begin + SUB * n + e / LPR, r_end - 1);
+      const int64_t off = (int64_t)row * NB + 4 * (e % LPR);
+      d0[u] = *reinterpret_cast<const float4*>(base0 + off);
+      if (PIN == PLANE_GELU_GRAD) d1[u] = *reinterpret_cast<const float4*>(base1 + off);
+    }
+  };
+  // stage sub-round n's rows (tanh / GELU' prologue, bf16); rows past the chunk are zero.
+  // Even sub-rounds (the first of a 64-row stage) also load the stage's F2 fragments; the
+  // choice is a compile-time tag so that the loop has no branch around memory operations.
+  auto stage = [&](auto first_tag, int n, const float4 (&c0)[NLD], const float4 (&c1)[NLD]) {
+    uint16_t* s_x = s_xb + (n & 1) * (SUB * XS);
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int e = tid + 512 * u;
+      const int r = e / LPR, c4 = e % LPR;
+      const bool live = r_begin + SUB * n + r < r_end;
+      const float4 v = c0[u], w = c1[u];
+      // a bit mask, not a branch: divergent control flow here would make the compiler wait
+      // for every load in flight at the top of the loop
+      const uint32_t keep = live ? 0xffffffffu : 0u;
+      const float o0 = __uint_as_float(__float_as_uint(prologue<PIN>(v.x, w.x)) & keep);
+      const float o1 = __uint_as_float(__float_as_uint(prologue<PIN>(v.y, w.y)) & keep);
+      const float o2 = __uint_as_float(__float_as_uint(prologue<PIN>(v.z, w.z)) & keep);
+      const float o3 = __uint_as_float(__float_as_uint(prologue<PIN>(v.w, w.w)) & keep);
+      uint2 packed;
+      packed.x = (uint32_t)bf16_bits(o0) | ((uint32_t)bf16_bits(o1) << 16);
+      packed.y = (uint32_t)bf16_bits(o2) | ((uint32_t)bf16_bits(o3) << 16);
+      *reinterpret_cast<uint2*>(s_x + r * XS + 4 * c4) = packed;
+    }
+    if constexpr (decltype(first_tag)::value) {
+      // F2 fragments of this stage (columns r0 .. r0 + 63; a block past the rows only meets
+      // zero rows of R, so its column is clamped into the table)
+      const int r0 = r_begin + 64 * (n / SPS);
+      const int it = min(wave, IT - 1);  // waves past IT repeat the last tile (dropped)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int col = min(r0 + 32 * ks + 8 * q, a.Na - 8);
+        const int64_t fo = (int64_t)(16 * it + m) * a.Na + col;
+        fh[ks] = *reinterpret_cast<const bf16x8*>(f2 + fo);
+        fl[ks] = *reinterpret_cast<const bf16x8*>(a.f2lo + fo);
+      }
+    }
+  };
+  // products of sub-round n (after its rows are staged and the next loads are issued).  The
+  // next sub-round writes the other row buffer and, after its barrier, Rt: every wave reaches
+  // that barrier only after finishing this sub-round's reads.
+  auto compute = [&](auto last_tag, int n) {
+    constexpr int sr = decltype(last_tag)::value ? 1 : 0;
+    const uint16_t* s_x = s_xb + (n & 1) * (SUB * XS);
+    __syncthreads();  // row tile visible
+    f32x4 d = zero4();
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(s_x + (16 * mt + m) * XS + 32 * s2 + 8 * q);
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(s_t1 + (16 * jt + m) * XS + 32 * s2 + 8 * q);
+      d = mfma_bf16(av, bv, d);
+    }
+    // D rows 16 mt + 4 q + r (stage row SUB sr + ..), column 16 jt + m  ->  Rt[column][row]
+    uint2 pk;
+    pk.x = (uint32_t)bf16_bits(d[0]) | ((uint32_t)bf16_bits(d[1]) << 16);
+    pk.y = (uint32_t)bf16_bits(d[2]) | ((uint32_t)bf16_bits(d[3]) << 16);
+    *reinterpret_cast<uint2*>(s_rt + (16 * jt + m) * RS + SUB * sr + 16 * mt + 4 * q) = pk;
+    if constexpr (decltype(last_tag)::value) {
+      __syncthreads();  // Rt of the 64-row stage complete
+      // every wave runs its products (a wave past IT repeats the last F2 tile and its result
+      // is dropped at the end), so no branch separates the F2 loads from their use
+#pragma unroll
+      for (int v = 0; v < NT2; ++v) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(s_rt + (16 * v + m) * RS + 32 * ks + 8 * q);
+          x2[v] = mfma_bf16(fh[ks], bv, x2[v]);
+          x2[v] = mfma_bf16(fl[ks], bv, x2[v]);
+        }
+      }
+    }
+  };
+  // Two register sets alternate: each is staged and then reloaded two sub-rounds ahead, so
+  // one sub-round's rows are always in flight while another is staged (nsub is even: whole
+  // 64-row stages of 32-row sub-rounds).  The scheduling barrier keeps set A's loads ahead
+  // of set B's, the order in which the loop waits for them.
+  float4 a0[NLD], a1[NLD], b0[NLD], b1[NLD];
+#pragma unroll
+  for (int u = 0; u < NLD; ++u) {
+    a1[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    b1[u] = a1[u];
+  }
+  load_sub(0, a0, a1);
+  __builtin_amdgcn_sched_barrier(0);
+  load_sub(min(1, nsub - 1), b0, b1);
+  for (int n = 0; n < nsub; n += 2) {
+    stage(kTrue, n, a0, a1);
+    load_sub(min(n + 2, nsub - 1), a0, a1);
+    compute(kFalse, n);
+    stage(kFalse, n + 1, b0, b1);
+    load_sub(min(n + 3, nsub - 1), b0, b1);
+    compute(kTrue, n + 1);
+  }
+  __syncthreads();  // the loop buffers are reused for X2
+  if (wave < IT) {
+#pragma unroll
+    for (int v = 0; v < NT2; ++v)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_x2[(16 * wave + 4 * q + r) * JP + 16 * v + m] = x2[v][r];
+  }
+  __syncthreads();
+  combine_store(s_x2, JP, a.ma, a.mb,
+                a.out + ((int64_t)chunk * a.planes + plane) * (2 * a.ma * a.mb), tid, 512);
+}
+
+// ------------------------------------------------------------------------------------------
 bool plane_fast_ok(const fno_plan* p) {
   const Geom& g = p->g;
   const int jpad = p->jpad;
@@ -365,7 +537,9 @@ bool plane_fast_ok(const fno_plan* p) {
 
 template <int PIN, int NB, int NTJ>
 static void launch_plane_t(const fno_plan* p, const PlaneArgs& a, dim3 grid, hipStream_t s) {
-  if (p->g.bf16)
+  if (p->g.bf16 && NTJ == 4)
+    hipLaunchKernelGGL((k_plane_bf16_lds<PIN, NB>), grid, dim3(512), 0, s, a);
+  else if (p->g.bf16)
     hipLaunchKernelGGL((k_plane_bf16<PIN, NB, NTJ>), grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((k_plane_f32<PIN, NB, NTJ>), grid, dim3(256), 0, s, a);
@@ -405,6 +579,7 @@ hipError_t launch_plane_fwd_fast(const fno_plan* p, int plane_in, int chans, con
   a.t1 = g.bf16 ? (const void*)p->t.t1_bf : (const void*)p->t.t1;
   a.f2 = g.bf16 ? (const void*)p->t.f2_bf : (const void*)p->t.f2;
   a.f2lo = p->t.f2_bf_lo;
+  a.t1t = p->t.t1t_bf;
   a.out = out;
   dim3 grid((unsigned)a.planes, (unsigned)p->nch);
   switch (plane_in) {

@@ -259,6 +259,8 @@ fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out) {
   toff += align_up(sizeof(float) * t1_elems);
   const size_t t1_bf_off = toff;
   toff += align_up(sizeof(uint16_t) * t1_elems);
+  const size_t t1t_bf_off = toff;  // the same table transposed, [jpad][Nb]
+  toff += align_up(sizeof(uint16_t) * t1_elems);
   const size_t f2_off = toff;
   toff += align_up(sizeof(float) * f2_elems);
   const size_t f2_bf_off = toff;
@@ -331,6 +333,7 @@ fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out) {
     // forward plane tables
     float* t1 = reinterpret_cast<float*>(host.data() + t1_off);
     uint16_t* t1b = reinterpret_cast<uint16_t*>(host.data() + t1_bf_off);
+    uint16_t* t1bt = reinterpret_cast<uint16_t*>(host.data() + t1t_bf_off);
     for (int c = 0; c < g.Nb; ++c)
       for (int k = 0; k < p->jpad / 2; ++k) {
         double cv = 0.0, sv = 0.0;
@@ -344,6 +347,8 @@ fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out) {
         t1[e + 1] = (float)sv;
         t1b[e] = bf16_bits_host(cv);
         t1b[e + 1] = bf16_bits_host(sv);
+        t1bt[(size_t)(2 * k) * g.Nb + c] = bf16_bits_host(cv);
+        t1bt[(size_t)(2 * k + 1) * g.Nb + c] = bf16_bits_host(sv);
       }
     float* f2 = reinterpret_cast<float*>(host.data() + f2_off);
     uint16_t* f2b = reinterpret_cast<uint16_t*>(host.data() + f2_bf_off);
@@ -439,6 +444,7 @@ fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out) {
   p->t.gt_unit_bf = reinterpret_cast<const uint16_t*>(base + gt_unit_bf_off);
   p->t.t1 = reinterpret_cast<const float*>(base + t1_off);
   p->t.t1_bf = reinterpret_cast<const uint16_t*>(base + t1_bf_off);
+  p->t.t1t_bf = reinterpret_cast<const uint16_t*>(base + t1t_bf_off);
   p->t.f2 = reinterpret_cast<const float*>(base + f2_off);
   p->t.f2_bf = reinterpret_cast<const uint16_t*>(base + f2_bf_off);
   p->t.f2_bf_lo = reinterpret_cast<const uint16_t*>(base + f2_bf_lo_off);

@@ -22,7 +22,7 @@ __device__ __forceinline__ NormalParts normal_parts(float z) {
   const float a1 = 0.254829592f, a2 = -0.284496736f, a3 = 1.421413741f, a4 = -1.453152027f,
               a5 = 1.061405429f;
   const float x = fabsf(z) * 0.70710678118654752f;
-  const float t = 1.0f / (1.0f + p * x);
+  const float t = __builtin_amdgcn_rcpf(1.0f + p * x);  // 1 ulp reciprocal
   const float e = __expf(-x * x);  // = exp(-z^2 / 2)
   const float poly = t * (a1 + t * (a2 + t * (a3 + t * (a4 + t * a5))));
   const float tail = 0.5f * poly * e;  // = Phi(-|z|)
@@ -41,10 +41,11 @@ __device__ __forceinline__ float gelu_grad_as(float z) {
 
 // tanh(v) = sign(v) (1 - e) / (1 + e), e = exp(-2|v|): no cancellation for large |v|; the
 // absolute error near 0 is a few float32 ulps of 1, far below the bfloat16 rounding applied
-// to the pre-activated field and the 1e-2 tolerance of that path.
+// to the pre-activated field and the 1e-2 tolerance of that path.  Divisions use the
+// hardware reciprocal (1 ulp), which keeps both functions within a few float32 ulps.
 __device__ __forceinline__ float tanh_fast(float v) {
   const float e = __expf(-2.0f * fabsf(v));
-  return copysignf((1.0f - e) / (1.0f + e), v);
+  return copysignf((1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e), v);
 }
 
 }  // namespace fno
