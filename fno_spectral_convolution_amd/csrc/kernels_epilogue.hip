@@ -74,8 +74,8 @@ __device__ __forceinline__ void stage_line(const EpiArgs& a, const float2* Trow0
           reinterpret_cast<const float*>(Trow0 + (int64_t)c * cstride) + k4);
     if (BF) {
       uint2 pk;
-      pk.x = (uint32_t)bf16_bits(v.x) | ((uint32_t)bf16_bits(v.y) << 16);
-      pk.y = (uint32_t)bf16_bits(v.z) | ((uint32_t)bf16_bits(v.w) << 16);
+      pk.x = pack_bf16x2(v.x, v.y);
+      pk.y = pack_bf16x2(v.z, v.w);
       *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(tl) + c * kst + k4) = pk;
     } else {
       *reinterpret_cast<float4*>(reinterpret_cast<float*>(tl) + c * kst + k4) = v;

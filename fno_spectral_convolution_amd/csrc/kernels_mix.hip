@@ -41,7 +41,7 @@ __device__ __forceinline__ void put_pair(unsigned char* tile, int t, int r, int 
                                          float v1) {
   unsigned char* p = tile + t * kTB + r * kRowB + k * (BF ? 2 : 4);
   if constexpr (BF) {
-    *reinterpret_cast<uint32_t*>(p) = (uint32_t)bf16_bits(v0) | ((uint32_t)bf16_bits(v1) << 16);
+    *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(v0, v1);
   } else {
     *reinterpret_cast<float2*>(p) = make_float2(v0, v1);
   }

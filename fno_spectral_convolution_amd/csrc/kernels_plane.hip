@@ -131,10 +131,8 @@ __global__ void __launch_bounds__(256) k_plane_bf16(PlaneArgs a) {
       const int r = e / LPR, c4 = e % LPR;
       const float4 v = pre0[u], w = pre1[u];
       uint2 packed;
-      packed.x = (uint32_t)bf16_bits(prologue<PIN>(v.x, w.x)) |
-                 ((uint32_t)bf16_bits(prologue<PIN>(v.y, w.y)) << 16);
-      packed.y = (uint32_t)bf16_bits(prologue<PIN>(v.z, w.z)) |
-                 ((uint32_t)bf16_bits(prologue<PIN>(v.w, w.w)) << 16);
+      packed.x = pack_bf16x2(prologue<PIN>(v.x, w.x), prologue<PIN>(v.y, w.y));
+      packed.y = pack_bf16x2(prologue<PIN>(v.z, w.z), prologue<PIN>(v.w, w.w));
       *reinterpret_cast<uint2*>(s_x + r * XS + 4 * c4) = packed;
     }
   };
@@ -157,8 +155,8 @@ __global__ void __launch_bounds__(256) k_plane_bf16(PlaneArgs a) {
       }
       // D rows 16 mt + 4 q + r, column 16 jt + m  ->  Rt[column][stage row]
       uint2 pk;
-      pk.x = (uint32_t)bf16_bits(d[0]) | ((uint32_t)bf16_bits(d[1]) << 16);
-      pk.y = (uint32_t)bf16_bits(d[2]) | ((uint32_t)bf16_bits(d[3]) << 16);
+      pk.x = pack_bf16x2(d[0], d[1]);
+      pk.y = pack_bf16x2(d[2], d[3]);
       *reinterpret_cast<uint2*>(s_rt + (16 * jt + m) * RS + sub + 16 * mt + 4 * q) = pk;
     }
     __syncthreads();
@@ -434,8 +432,8 @@ __global__ void __launch_bounds__(512) k_plane_bf16_lds(PlaneArgs a) {
       const float o2 = __uint_as_float(__float_as_uint(prologue<PIN>(v.z, w.z)) & keep);
       const float o3 = __uint_as_float(__float_as_uint(prologue<PIN>(v.w, w.w)) & keep);
       uint2 packed;
-      packed.x = (uint32_t)bf16_bits(o0) | ((uint32_t)bf16_bits(o1) << 16);
-      packed.y = (uint32_t)bf16_bits(o2) | ((uint32_t)bf16_bits(o3) << 16);
+      packed.x = pack_bf16x2(o0, o1);
+      packed.y = pack_bf16x2(o2, o3);
       *reinterpret_cast<uint2*>(s_x + r * XS + 4 * c4) = packed;
     }
     if constexpr (decltype(first_tag)::value) {
@@ -468,8 +466,8 @@ __global__ void __launch_bounds__(512) k_plane_bf16_lds(PlaneArgs a) {
     }
     // D rows 16 mt + 4 q + r (stage row SUB sr + ..), column 16 jt + m  ->  Rt[column][row]
     uint2 pk;
-    pk.x = (uint32_t)bf16_bits(d[0]) | ((uint32_t)bf16_bits(d[1]) << 16);
-    pk.y = (uint32_t)bf16_bits(d[2]) | ((uint32_t)bf16_bits(d[3]) << 16);
+    pk.x = pack_bf16x2(d[0], d[1]);
+    pk.y = pack_bf16x2(d[2], d[3]);
     *reinterpret_cast<uint2*>(s_rt + (16 * jt + m) * RS + SUB * sr + 16 * mt + 4 * q) = pk;
     if constexpr (decltype(last_tag)::value) {
       __syncthreads();  // Rt of the 64-row stage complete

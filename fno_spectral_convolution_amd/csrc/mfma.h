@@ -29,6 +29,16 @@ __device__ __forceinline__ uint16_t bf16_bits(float v) {
   return (uint16_t)(u >> 16);
 }
 
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+
+// two floats -> packed bfloat16 pair (lo = a, hi = b), round-to-nearest-even; one
+// v_cvt_pk_bf16_f32 on gfx950
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2_v v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_v));
+}
+
 __device__ __forceinline__ bf16x8 to_bf16x8(float4 a, float4 b) {
   bf16x8 r;
   r[0] = (__bf16)a.x;
