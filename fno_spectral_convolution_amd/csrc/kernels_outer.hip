@@ -8,6 +8,8 @@
 // so K = 2 Lin.  The twiddle matrix A = [Mr | Mi] ([Lout_pad][2 Lin_pad], zero padded) is
 // built on the host in float64 and read through L2; a work-group stages its column tile of
 // the input, transposed and with the swapped copy, in LDS and its waves split the M-tiles.
+// Column n of N-tile t is column NT n + t of the work-group's tile, so a lane holds NT
+// adjacent output columns of a row and 16 lanes store 16 NT adjacent floats at once.
 #include "fno_internal.h"
 #include "mfma.h"
 
@@ -34,6 +36,8 @@ __global__ void __launch_bounds__(256) k_outer_mfma(OuterArgs a) {
   const int64_t c0 = (int64_t)blockIdx.y * CT;
   const float* src = a.in + pre * a.Lin * a.post2;
   // Bt[c][k]: k < Lin_pad -> X[k][c0 + c]; k >= Lin_pad -> Xs[k - Lin_pad][c0 + c]
+  // staged row of column c (local): 16 (c % NT) + c / NT
+  auto brow = [](int c) { return 16 * (c % NT) + c / NT; };
   for (int e = tid; e < a.Lin_pad * CT; e += 256) {
     const int li = e / CT, c = e - li * CT;
     const int64_t col = c0 + c;
@@ -43,12 +47,12 @@ __global__ void __launch_bounds__(256) k_outer_mfma(OuterArgs a) {
     const float vs = (c & 1) ? -v : v;  // Xs[li][c^1]
     if (BF) {
       uint16_t* bt = reinterpret_cast<uint16_t*>(s_raw);
-      bt[c * KS + li] = bf16_bits(v);
-      bt[cp * KS + a.Lin_pad + li] = bf16_bits(vs);
+      bt[brow(c) * KS + li] = bf16_bits(v);
+      bt[brow(cp) * KS + a.Lin_pad + li] = bf16_bits(vs);
     } else {
       float* bt = reinterpret_cast<float*>(s_raw);
-      bt[c * KS + li] = v;
-      bt[cp * KS + a.Lin_pad + li] = vs;
+      bt[brow(c) * KS + li] = v;
+      bt[brow(cp) * KS + a.Lin_pad + li] = vs;
     }
   }
   __syncthreads();
@@ -87,15 +91,25 @@ __global__ void __launch_bounds__(256) k_outer_mfma(OuterArgs a) {
         }
       }
     }
-    // lane (n = m, q): rows 16 mt + 4 q + r, column c0 + 16 nt + m
+    // lane (n = m, q): rows 16 mt + 4 q + r, columns c0 + NT m + nt (nt = 0 .. NT-1)
+    const int64_t col = c0 + NT * m;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int p = 16 * mt + 4 * q + r;
       if (p >= a.Lout) continue;
+      float* d = dst + (int64_t)p * a.post2 + col;
+      if (col + NT <= a.post2 && (a.post2 % NT) == 0) {
+        if constexpr (NT == 4) {
+          *reinterpret_cast<float4*>(d) = make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
+        } else if constexpr (NT == 2) {
+          *reinterpret_cast<float2*>(d) = make_float2(acc[0][r], acc[1][r]);
+        } else {
+          d[0] = acc[0][r];
+        }
+      } else {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int64_t col = c0 + 16 * nt + m;
-        if (col < a.post2) dst[(int64_t)p * a.post2 + col] = acc[nt][r];
+        for (int nt = 0; nt < NT; ++nt)
+          if (col + nt < a.post2) d[nt] = acc[nt][r];
       }
     }
   }
