@@ -458,31 +458,32 @@ hipError_t launch_epilogue_bwd(const fno_plan* p, int mode, const float2* Tg, co
   return hipGetLastError();
 }
 
-// Sum of the per-work-group bypass-gradient partials.  A group of 256 threads owns 64
-// consecutive entries; thread slice k (0..3) sums partials k, k+4, ... with 4 loads in
-// flight, and the slices are added in the fixed order 0, 1, 2, 3 (deterministic).
+// Sum of the per-work-group bypass-gradient partials.  A group of 256 threads owns 8
+// consecutive entries; thread slice k (0..31) sums partials k, k+32, ... with 8 loads in
+// flight, and the 32 slice sums are added in the fixed order 0, 1, .., 31 (deterministic).
+constexpr int kFinE = 8, kFinS = 32;
+
 __global__ void __launch_bounds__(256)
 k_bypass_finish(const float* __restrict__ part, int nparts, int cout, int cin,
                 float* __restrict__ dwb, float* __restrict__ dbias) {
-  __shared__ float s_sum[4][64];
+  __shared__ float s_sum[kFinS][kFinE];
   const int npair = cout * cin + cout;
-  const int el = threadIdx.x & 63, slice = threadIdx.x >> 6;
-  const int e = blockIdx.x * 64 + el;
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  const int el = threadIdx.x % kFinE, slice = threadIdx.x / kFinE;
+  const int e = blockIdx.x * kFinE + el;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (e < npair) {
     int q = slice;
-    for (; q + 12 < nparts; q += 16) {
-      a0 += part[(int64_t)q * npair + e];
-      a1 += part[(int64_t)(q + 4) * npair + e];
-      a2 += part[(int64_t)(q + 8) * npair + e];
-      a3 += part[(int64_t)(q + 12) * npair + e];
+    for (; q + 7 * kFinS < nparts; q += 8 * kFinS) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] += part[(int64_t)(q + j * kFinS) * npair + e];
     }
-    for (; q < nparts; q += 4) a0 += part[(int64_t)q * npair + e];
+    for (; q < nparts; q += kFinS) acc[0] += part[(int64_t)q * npair + e];
   }
-  s_sum[slice][el] = (a0 + a1) + (a2 + a3);
+  s_sum[slice][el] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
   __syncthreads();
   if (slice == 0 && e < npair) {
-    const float v = ((s_sum[0][el] + s_sum[1][el]) + s_sum[2][el]) + s_sum[3][el];
+    float v = 0.f;
+    for (int k = 0; k < kFinS; ++k) v += s_sum[k][el];
     if (e < cout * cin) {
       if (dwb) dwb[e] = v;
     } else if (dbias) {
@@ -496,7 +497,7 @@ hipError_t launch_bypass_grad_finish(const fno_plan* p, const float* red_part, f
   const Geom& g = p->g;
   const int npair = g.Cout * g.Cin + g.Cout;
   const int nparts = epilogue_bwd_fast(p, EPI_BLOCK, grad_x) ? epilogue_bwd_fast_groups(p) : p->nred;
-  hipLaunchKernelGGL(k_bypass_finish, dim3((npair + 63) / 64), dim3(256), 0, s, red_part,
+  hipLaunchKernelGGL(k_bypass_finish, dim3((npair + kFinE - 1) / kFinE), dim3(256), 0, s, red_part,
                      nparts, g.Cout, g.Cin, dwb, dbias);
   return hipGetLastError();
 }
