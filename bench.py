@@ -1,6 +1,6 @@
 """Benchmark: FNO spectral-conv throughput on one MI355X through libfno.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--no-cpu-baseline]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload train2d_512] [--no-cpu-baseline]
 
 A step is one pass of the workload's whole hot path over one batch of synthetic input
 already resident in HBM.  The default workload is the 2D FNO training step: 4 spectral
@@ -35,7 +35,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c3")
+    ap.add_argument("--workload", default="train2d_512")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-batch", type=int, default=3)
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -159,18 +159,20 @@ def roofline(wl, runner, kern, steps):
 def measured_traffic(wl, kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
     (FETCH_SIZE + WRITE_SIZE, each scaled by the counter's reading for a plain copy of known
-    size), or None when there is none for this workload or the kernel's source has changed
-    since the counters were taken."""
+    size), or None when there is none for this workload or the kernel's source (or a header it
+    includes) has changed since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"counters_{wl.name}.json")
     if not os.path.exists(path):
         return None
     try:
         rec = json.load(open(path))["kernels"][kernel]
-        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+        h = hashlib.sha256()
+        for f in rec["sources"]:  # the kernel's source file and the headers it includes
+            h.update(open(os.path.join(ROOT, f), "rb").read())
     except (KeyError, OSError, ValueError):
         return None
-    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+    if h.hexdigest() != rec["sources_sha256"]:
         return None
     return round(rec["fetch_bytes"] + rec["write_bytes"])
 

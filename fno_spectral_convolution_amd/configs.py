@@ -22,8 +22,8 @@ class Workload:
     blocks: int                   # number of spectral blocks
     mixed: bool                   # tanh pre-activation + bf16 spectral operands
     train: bool                   # forward + MSE + backward (else forward only)
-    lift_in: Optional[int] = None     # pointwise lift input channels (C2)
-    proj_hidden: Optional[int] = None  # projection hidden width (C2)
+    lift_in: Optional[int] = None     # pointwise lift input channels (2D stack)
+    proj_hidden: Optional[int] = None  # projection hidden width (2D stack)
     proj_out: Optional[int] = None
     zero_bias: bool = False
     input_kind: str = "grf"       # grf | normal | grf_coords | grf_layered
@@ -47,20 +47,20 @@ class Workload:
 
 
 WORKLOADS = {
-    "c1": Workload("c1", 1, 4, 20, (64, 64), (12, 12), 1, False, False,
+    "layer2d_64": Workload("layer2d_64", 1, 4, 20, (64, 64), (12, 12), 1, False, False,
                    zero_bias=True, input_kind="normal",
                    notes="2D single spectral layer, forward only, fp32"),
-    "c2": Workload("c2", 2, 16, 32, (256, 256), (16, 16), 4, False, False,
+    "stack2d_256": Workload("stack2d_256", 2, 16, 32, (256, 256), (16, 16), 4, False, False,
                    lift_in=3, proj_hidden=128, proj_out=1, input_kind="grf_coords",
                    notes="2D FNO stack forward, fp32, lift 3->32, projection 32->128->1"),
-    "c3": Workload("c3", 3, 8, 64, (512, 512), (32, 32), 4, True, True,
+    "train2d_512": Workload("train2d_512", 3, 8, 64, (512, 512), (32, 32), 4, True, True,
                    notes="2D FNO training step, tanh + bf16 spectral path, fwd+bwd, MSE"),
-    "c4": Workload("c4", 4, 2, 20, (128, 128, 128), (16, 16, 16), 4, False, True,
+    "train3d_128": Workload("train3d_128", 4, 2, 20, (128, 128, 128), (16, 16, 16), 4, False, True,
                    input_kind="grf_layered",
                    notes="3D FNO stack fwd+bwd, fp32, layered permeability channel"),
-    "c5": Workload("c5", 5, 1, 20, (128, 128, 128, 20), (12, 12, 12, 8), 4, False, False,
+    "st4d_128x20": Workload("st4d_128x20", 5, 1, 20, (128, 128, 128, 20), (12, 12, 12, 8), 4, False, False,
                    notes="4D space-time block stack forward, fp32"),
-    "c5h": Workload("c5h", 5, 1, 20, (128, 128, 128, 20), (12, 12, 12, 8), 4, True, False,
+    "st4d_128x20_bf16": Workload("st4d_128x20_bf16", 5, 1, 20, (128, 128, 128, 20), (12, 12, 12, 8), 4, True, False,
                     notes="4D space-time block stack forward, tanh + bf16"),
 }
 

@@ -2,9 +2,9 @@
 
 Inputs are the workloads' own seeded fields (Gaussian random fields, coordinate and layered
 permeability channels) and block parameters.  Where the oracle can evaluate the whole field in
-seconds it does (C1; C3 and C4 one block forward + backward over the full batch; C2 the whole
-stack on sampled batch entries, which the stack never mixes).  For the 4D space-time share
-(C5, 3.4 GB per field) the oracle computes the full retained spectrum and then the block output
+seconds it does (the 2D single layer; the 2D and 3D training workloads one block forward +
+backward over the full batch; the 2D stack on sampled batch entries, which the stack never
+mixes).  For the 4D space-time share (3.4 GB per field) the oracle computes the full retained spectrum and then the block output
 directly at sampled grid points.  The spectral path is also compared on its own (y_spec and the
 spectral part of grad_x), since at these weight scales the bypass dominates the block output.
 """
@@ -37,7 +37,7 @@ _FIELDS = {}
 
 
 def _field(wl):
-    """The workload's seeded input field, generated once per module (C5 and C5h share it)."""
+    """The workload's seeded input field, generated once per module (the fp32 and bf16 4D workloads share it)."""
     key = (wl.cfg_id, wl.batch, wl.width, tuple(wl.grid), wl.input_kind)
     if key not in _FIELDS:
         _FIELDS.clear()
@@ -90,24 +90,24 @@ def _block_case(L, name, grad_scale):
     sp.close()
 
 
-def test_c1_block_full(L):
-    _block_case(L, "c1", 1.0)
+def test_layer2d_64_block_full(L):
+    _block_case(L, "layer2d_64", 1.0)
 
 
-def test_c3_block_full(L):
-    _block_case(L, "c3", 1e-3)
+def test_train2d_512_block_full(L):
+    _block_case(L, "train2d_512", 1e-3)
 
 
-def test_c4_block_full(L):
-    _block_case(L, "c4", 1e-3)
+def test_train3d_128_block_full(L):
+    _block_case(L, "train3d_128", 1e-3)
 
 
-def test_c2_stack_sampled_batches(L):
-    """The full C2 stack (lift, 4 blocks, projection) on the GPU, as bench.py runs it; the
+def test_stack2d_256_sampled_batches(L):
+    """The full 2D stack (lift, 4 blocks, projection) on the GPU, as bench.py runs it; the
     oracle evaluates the same stack for batch entries 0 and 15."""
     from fno_spectral_convolution_amd.stack import StackRunner
-    wl = configs.get("c2")
-    announce("workload stack c2")
+    wl = configs.get("stack2d_256")
+    announce("workload stack stack2d_256")
     runner = StackRunner(wl, device="cuda")
     out = _host(runner.step())
     _torch().cuda.synchronize()
@@ -118,8 +118,8 @@ def test_c2_stack_sampled_batches(L):
         check(f"stack output batch {b}", out[b:b + 1], want, TOL_F32)
 
 
-@pytest.mark.parametrize("name", ["c5", "c5h"])
-def test_c5_block_sampled_points(L, name):
+@pytest.mark.parametrize("name", ["st4d_128x20", "st4d_128x20_bf16"])
+def test_st4d_128x20_block_sampled_points(L, name):
     """4D space-time share [1, 20, 128^3 x 20]: y and y_spec at 512 sampled grid points."""
     wl = configs.get(name)
     tol = TOL_MIXED if wl.mixed else TOL_F32
