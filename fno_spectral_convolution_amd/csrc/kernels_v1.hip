@@ -503,59 +503,6 @@ hipError_t launch_bypass_grad_finish(const fno_plan* p, const float* red_part, f
 }
 
 // ------------------------------------------------------------------------------------------
-// Pointwise lift / projection.  One thread per point; inputs staged in LDS.
-constexpr int kPwThreads = 256;
-
-__global__ void __launch_bounds__(kPwThreads)
-k_pointwise(int64_t npts, int cin, int hidden, int cout, const float* __restrict__ x,
-            const float* __restrict__ w1, const float* __restrict__ b1,
-            const float* __restrict__ w2, const float* __restrict__ b2, float* __restrict__ y) {
-  extern __shared__ float smem[];
-  float* s_x = smem;  // [cin][256]
-  const int tid = threadIdx.x;
-  const int b = blockIdx.y;
-  const int64_t p = (int64_t)blockIdx.x * kPwThreads + tid;
-  for (int ci = 0; ci < cin; ++ci)
-    s_x[ci * kPwThreads + tid] = (p < npts) ? x[((int64_t)b * cin + ci) * npts + p] : 0.f;
-  __syncthreads();
-  if (p >= npts) return;
-  const float* xv = s_x + tid;
-  if (hidden == 0) {
-    for (int o = 0; o < cout; ++o) {
-      float a = b1 ? b1[o] : 0.f;
-      for (int ci = 0; ci < cin; ++ci) a += w1[o * cin + ci] * xv[ci * kPwThreads];
-      y[((int64_t)b * cout + o) * npts + p] = a;
-    }
-    return;
-  }
-  for (int o0 = 0; o0 < cout; o0 += 8) {
-    float acc[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = (o0 + q < cout && b2) ? b2[o0 + q] : 0.f;
-    for (int h = 0; h < hidden; ++h) {
-      float a = b1 ? b1[h] : 0.f;
-      for (int ci = 0; ci < cin; ++ci) a += w1[h * cin + ci] * xv[ci * kPwThreads];
-      const float act = gelu_f(a);
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if (o0 + q < cout) acc[q] += w2[(o0 + q) * hidden + h] * act;
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      if (o0 + q < cout) y[((int64_t)b * cout + o0 + q) * npts + p] = acc[q];
-  }
-}
-
-hipError_t launch_pointwise(int64_t batch, int64_t npts, int cin, int hidden, int cout,
-                            const float* x, const float* w1, const float* b1, const float* w2,
-                            const float* b2, float* y, hipStream_t s) {
-  dim3 grid((unsigned)((npts + kPwThreads - 1) / kPwThreads), (unsigned)batch);
-  hipLaunchKernelGGL(k_pointwise, grid, dim3(kPwThreads), sizeof(float) * cin * kPwThreads, s,
-                     npts, cin, hidden, cout, x, w1, b1, w2, b2, y);
-  return hipGetLastError();
-}
-
-// ------------------------------------------------------------------------------------------
 // MSE: g = 2 (y - t) / n; per-group partial sums in double, then one fixed-order finish.
 __global__ void k_mse_part(int64_t n, const float* __restrict__ y, const float* __restrict__ t,
                            float* __restrict__ g, double* __restrict__ part) {

@@ -172,6 +172,22 @@ def test_pointwise_and_mse(L):
     assert abs(float(_host(loss)[0]) - lref) <= 1e-6 * lref
 
 
+def test_pointwise_widest(L):
+    """The widest pointwise layers the boundary accepts (64 -> 256 -> 128), ragged point count."""
+    announce("pointwise widest")
+    g = np.random.default_rng(6)
+    x = g.standard_normal((2, 64, 70)).astype(np.float32)
+    w1 = (g.standard_normal((256, 64)) / 8).astype(np.float32)
+    b1 = g.standard_normal(256).astype(np.float32)
+    w2 = (g.standard_normal((128, 256)) / 16).astype(np.float32)
+    b2 = g.standard_normal(128).astype(np.float32)
+    proj = L.pointwise(_dev(x), _dev(w1), _dev(b1), _dev(w2), _dev(b2))
+    lift = L.pointwise(_dev(x), _dev(w2[:, :64].copy()), _dev(b2))
+    _torch().cuda.synchronize()
+    check("projection", _host(proj), O.projection_fwd(x, w1, b1, w2, b2), TOL_F32)
+    check("lift", _host(lift), O.pointwise_linear(x, w2[:, :64], b2), TOL_F32)
+
+
 def test_bad_workspace_is_an_error(L):
     announce("workspace-too-small")
     torch = _torch()
