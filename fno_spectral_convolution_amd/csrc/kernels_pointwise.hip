@@ -17,17 +17,42 @@ namespace fno {
 constexpr int kPwP = 64;        // points per work-group
 constexpr int kPwS = kPwP + 4;  // LDS row stride (floats)
 
-// D[M][64] += W[M rows][K] . S[K][64] for this wave's M-tiles; W row-major with row stride ldw.
-// Fragment of M-tile mt, N-tile nt: lane (m, q), register r <-> row 16 mt + 4 q + r, column
-// 16 nt + m.  K-step ks uses k = 4 ks + q.
+// D[M][64] += W[M rows][K] . S[K][64] over N-tiles nt0 .. nt0 + NN - 1 of M-tile mt; W
+// row-major with row stride ldw.  Fragment of M-tile mt, N-tile nt: lane (m, q), register r
+// <-> row 16 mt + 4 q + r, column 16 nt + m.  K-step ks uses k = 4 ks + q.
+// bias[i] for i < n, else 0 (bias may be null: a uniform branch); unconditional clamped load
+__device__ __forceinline__ float masked_bias(const float* __restrict__ bias, int i, int n) {
+  if (!bias) return 0.f;
+  const float v = bias[min(i, n - 1)];
+  return __uint_as_float(__float_as_uint(v) & (i < n ? 0xffffffffu : 0u));
+}
+
+template <int NN>
 __device__ __forceinline__ void pw_tile(const float* __restrict__ w, int ldw, int M, int K,
-                                        const float* s_in, int mt, int m, int q, f32x4 (&acc)[4]) {
+                                        const float* s_in, int mt, int nt0, int m, int q,
+                                        f32x4 (&acc)[NN]) {
   const int row = 16 * mt + m;
-  for (int ks = 0; ks < (K + 3) / 4; ++ks) {
-    const int k = 4 * ks + q;
-    const float a = (row < M && k < K) ? w[row * ldw + k] : 0.f;
+  const bool row_ok = row < M;
+  const float* wr = w + min(row, M - 1) * ldw;
+  // groups of 4 K-steps: the 4 weight loads (through L2) go out together.  Loads are
+  // unconditional (clamped index) and masked, so none of them can be moved into a branch;
+  // K-steps past K read zero rows of s_in (it holds 16-row multiples).
+  for (int ks0 = 0; ks0 < (K + 15) / 16 * 4; ks0 += 4) {
+    float a[4];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[nt] = mfma_f32(a, s_in[k * kPwS + 16 * nt + m], acc[nt]);
+    for (int j = 0; j < 4; ++j) {
+      const int k = 4 * (ks0 + j) + q;
+      const float wv = wr[min(k, K - 1)];
+      const uint32_t keep = (row_ok && k < K) ? 0xffffffffu : 0u;
+      a[j] = __uint_as_float(__float_as_uint(wv) & keep);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = 4 * (ks0 + j) + q;
+#pragma unroll
+      for (int jj = 0; jj < NN; ++jj)
+        acc[jj] = mfma_f32(a[j], s_in[k * kPwS + 16 * (nt0 + jj) + m], acc[jj]);
+    }
   }
 }
 
@@ -37,11 +62,11 @@ k_pointwise_mfma(int64_t npts, int cin, int hidden, int cout, const float* __res
                  const float* __restrict__ w2, const float* __restrict__ b2,
                  float* __restrict__ y) {
   extern __shared__ __attribute__((aligned(16))) float s_pw[];
-  const int cin_p = (cin + 3) / 4 * 4;
+  const int cin_p = (cin + 15) / 16 * 16;
   const int mid = hidden > 0 ? hidden : cout;   // rows of the first product
   const int mid_p = (mid + 15) / 16 * 16;
   const int cout_p = (cout + 15) / 16 * 16;
-  float* s_x = s_pw;                             // [cin_p][kPwS]
+  float* s_x = s_pw;                             // [cin_p][kPwS], cin_p = 16-row multiple
   float* s_h = s_x + cin_p * kPwS;               // [mid_p][kPwS]  (hidden tile or output)
   float* s_y = hidden > 0 ? s_h + mid_p * kPwS : s_h;  // [cout_p][kPwS]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -49,44 +74,68 @@ k_pointwise_mfma(int64_t npts, int cin, int hidden, int cout, const float* __res
   const int b = blockIdx.y;
   const int64_t p0 = (int64_t)blockIdx.x * kPwP;
   const int np = (int)min((int64_t)kPwP, npts - p0);
-  // x tile: rows >= cin and points past the end are zero
-  for (int e = tid; e < cin_p * kPwP; e += 256) {
-    const int c = e / kPwP, pp = e % kPwP;
-    float v = 0.f;
-    if (c < cin && pp < np) v = x[((int64_t)b * cin + c) * npts + p0 + pp];
-    s_x[c * kPwS + pp] = v;
+  // x tile: rows >= cin and points past the end are zero.  Full tiles use float4 loads, four
+  // per thread issued together (row c, points 4 f .. 4 f + 3 for item c * 16 + f).
+  if (np == kPwP && (npts % 4) == 0) {
+    const float* xb = x + (int64_t)b * cin * npts + p0;
+    for (int e0 = tid; e0 < cin_p * (kPwP / 4); e0 += 4 * 256) {
+      float4 v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = e0 + 256 * j;
+        const int c = min(e / (kPwP / 4), cin - 1), f = e % (kPwP / 4);
+        v[j] = *reinterpret_cast<const float4*>(xb + (int64_t)c * npts + 4 * f);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = e0 + 256 * j;
+        const int c = e / (kPwP / 4), f = e % (kPwP / 4);
+        if (c < cin_p) {
+          const bool live = c < cin;
+          *reinterpret_cast<float4*>(s_x + c * kPwS + 4 * f) =
+              live ? v[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+    }
+  } else {
+    for (int e = tid; e < cin_p * kPwP; e += 256) {
+      const int c = e / kPwP, pp = e % kPwP;
+      float v = 0.f;
+      if (c < cin && pp < np) v = x[((int64_t)b * cin + c) * npts + p0 + pp];
+      s_x[c * kPwS + pp] = v;
+    }
   }
   __syncthreads();
   for (int mt = wave; mt < mid_p / 16; mt += 4) {
     f32x4 acc[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) acc[nt] = zero4();
-    pw_tile(w1, cin, mid, cin, s_x, mt, m, q, acc);
+    pw_tile<4>(w1, cin, mid, cin, s_x, mt, 0, m, q, acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int h = 16 * mt + 4 * q + r;
-      const float bh = (b1 && h < mid) ? b1[h] : 0.f;
+      const float bh = masked_bias(b1, h, mid);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        float v = acc[nt][r] + bh;
-        if (hidden > 0) v = (h < mid) ? gelu_as(v) : 0.f;
-        s_h[h * kPwS + 16 * nt + m] = v;
+        const float v = acc[nt][r] + bh;
+        const float gv = gelu_as(v);
+        s_h[h * kPwS + 16 * nt + m] = hidden > 0 ? (h < mid ? gv : 0.f) : v;
       }
     }
   }
   __syncthreads();
   if (hidden > 0) {
-    for (int mt = wave; mt < cout_p / 16; mt += 4) {
-      f32x4 acc[4];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[nt] = zero4();
-      pw_tile(w2, hidden, cout, hidden, s_h, mt, m, q, acc);
+    // (M-tile, N-tile) pairs round-robin over the waves: a narrow output (one M-tile) still
+    // keeps all four waves busy
+    for (int u = wave; u < (cout_p / 16) * 4; u += 4) {
+      const int mt = u / 4, nt = u % 4;
+      f32x4 acc[1] = {zero4()};
+      pw_tile<1>(w2, hidden, cout, hidden, s_h, mt, nt, m, q, acc);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int o = 16 * mt + 4 * q + r;
-        const float bo = (b2 && o < cout) ? b2[o] : 0.f;
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) s_y[o * kPwS + 16 * nt + m] = acc[nt][r] + bo;
+        const float bo = masked_bias(b2, o, cout);
+        s_y[o * kPwS + 16 * nt + m] = acc[0][r] + bo;
       }
     }
     __syncthreads();
@@ -110,7 +159,7 @@ k_pointwise_mfma(int64_t npts, int cin, int hidden, int cout, const float* __res
 hipError_t launch_pointwise(int64_t batch, int64_t npts, int cin, int hidden, int cout,
                             const float* x, const float* w1, const float* b1, const float* w2,
                             const float* b2, float* y, hipStream_t s) {
-  const int cin_p = (cin + 3) / 4 * 4;
+  const int cin_p = (cin + 15) / 16 * 16;
   const int mid = hidden > 0 ? hidden : cout;
   const int mid_p = (mid + 15) / 16 * 16;
   const int cout_p = (cout + 15) / 16 * 16;
