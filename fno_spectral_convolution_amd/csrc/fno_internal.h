@@ -98,6 +98,10 @@ enum PlaneIn { PLANE_X = 0, PLANE_TANH = 1, PLANE_GELU_GRAD = 2 };
 
 hipError_t launch_plane_fwd(const fno_plan* p, int plane_in, int chans, const float* in0,
                             const float* in1, float2* out, hipStream_t s);
+// short contiguous axis (Nb <= 32): one wave per plane, unchunked output (nch == 1)
+bool plane_small_ok(const fno_plan* p);
+hipError_t launch_plane_small(const fno_plan* p, int plane_in, int chans, const float* in0,
+                              const float* in1, float2* out, hipStream_t s);
 hipError_t launch_outer_fwd(const fno_plan* p, int axis, int chans, const float2* in,
                             int nparts, int64_t part_stride, float2* out, hipStream_t s);
 hipError_t launch_outer_inv(const fno_plan* p, int axis, int chans, const float2* in,

@@ -1,0 +1,251 @@
+// Forward transform of [Na][Nb] planes whose contiguous axis is short (Nb <= 32, e.g. the
+// 20-point time axis of a space-time field): the truncated real DFT of the contiguous axis
+// followed by the truncated DFT of the row axis, for the retained modes only (the FNO spectral
+// transform from its linear-algebra form -- model-parallel FNO page, "Proposed method"):
+//   R[row][j]  = sum_c x'[row][c] T1[c][j]               (j < 16 NTJ: cos / -sin columns)
+//   X2[i][j]   = sum_row F2[i][row] R[row][j]            (F2: cos rows, then sin rows)
+//   X[s][k]    = (X2[s][2k] + X2[2ma+s][2k+1]) + i (X2[s][2k+1] - X2[2ma+s][2k])
+//
+// One wave owns one plane at a time (no barriers between waves) and walks planes with a
+// stride of the whole grid, loading the next plane while it computes the current one.
+//   first product : M = rows (16 MT), K = 32 (columns c = 8 q + slot, masked past Nb), one
+//                   16x16x32 bf16 MFMA per tile (mixed path) or 8 16x16x4 f32 MFMAs; each
+//                   lane loads its own A operand, two float4 of its row, straight from HBM.
+//   second product: 16x16x4 f32 MFMAs whose K order is chosen so that K-step s, k-slot q is
+//                   row 16 (s / 4) + 4 q + s % 4: exactly the first product's D fragment held
+//                   by the same lane, so R never leaves the registers.  F2 sits in LDS.
+//   combine       : X2 goes to a per-wave LDS tile and is folded into the complex spectrum.
+// On the mixed path the pre-activated input, T1 and R are rounded to bfloat16 (the
+// half-precision transform of the mixed-precision neural-operator page, "Tiivistelmä"); F2
+// stays float32, which is at least as precise as the hi + lo bfloat16 pair used elsewhere.
+#include "fno_internal.h"
+#include "mfma.h"
+#include "pointwise.h"
+
+namespace fno {
+
+struct SmallPlaneArgs {
+  int Na, Nb, ma, mb;
+  int64_t planes;
+  const float* in0;
+  const float* in1;
+  const float* t1;       // [Nb][jpad] f32
+  const uint16_t* t1bf;  // [Nb][jpad] bf16 bits
+  const float* f2;       // [4 ma][Na] f32
+  float2* out;           // [planes][2 ma][mb]
+};
+
+template <int PIN>
+__device__ __forceinline__ float small_prologue(float v, float w) {
+  if (PIN == PLANE_TANH) return tanh_fast(v);
+  if (PIN == PLANE_GELU_GRAD) return v * gelu_grad_as(w);
+  return v;
+}
+
+__device__ __forceinline__ float round_bf16(float v) {
+  return __uint_as_float((uint32_t)bf16_bits(v) << 16);
+}
+
+// MT = Na / 16 row tiles, NTJ = jpad / 16 column tiles
+template <int PIN, bool BF, int MT, int NTJ>
+__global__ void __launch_bounds__(256) k_plane_small(SmallPlaneArgs a) {
+  constexpr int JP = 16 * NTJ;
+  constexpr bool TWO = PIN == PLANE_GELU_GRAD;
+  extern __shared__ __attribute__((aligned(16))) float s_sp[];
+  const int Na = 16 * MT;
+  const int F2S = Na + 4;                    // F2 row stride (floats)
+  const int ROWS2 = 4 * a.ma;                // F2 rows
+  const int MT2 = ROWS2 / 16;                // F2 row tiles (ma % 4 == 0)
+  float* s_f2 = s_sp;                        // [4 ma][F2S]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, q = lane >> 4;
+  float* s_w = s_f2 + ROWS2 * F2S + wave * (ROWS2 * JP);  // this wave's X2 tile [4 ma][JP]
+  for (int e = tid; e < ROWS2 * Na; e += 256) {
+    const int i = e / Na, r = e - i * Na;
+    s_f2[i * F2S + r] = a.f2[e];
+  }
+  // T1 fragments: B[k = 8 q + slot][n = 16 nt + m]; zero past Nb
+  float t1r[NTJ][8];
+  bf16x8 t1b[NTJ];
+#pragma unroll
+  for (int nt = 0; nt < NTJ; ++nt)
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int c = 8 * q + s;
+      const int cc = min(c, a.Nb - 1);
+      const float v = BF ? __uint_as_float((uint32_t)a.t1bf[cc * JP + 16 * nt + m] << 16)
+                         : a.t1[cc * JP + 16 * nt + m];
+      t1r[nt][s] = c < a.Nb ? v : 0.f;
+      t1b[nt][s] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(t1r[nt][s]) >> 16));
+    }
+  __syncthreads();
+  const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  // this lane's row of tile t is 16 t + m; its columns 8 q .. 8 q + 7 (two float4; columns
+  // past Nb are read from a clamped address and masked; Nb % 4 == 0 keeps float4 alignment)
+  const int c0 = min(8 * q, a.Nb - 4), c1 = min(8 * q + 4, a.Nb - 4);
+  const bool live0 = 8 * q < a.Nb, live1 = 8 * q + 4 < a.Nb;
+  float4 p0[MT][2], p1[TWO ? MT : 1][2];
+  auto load_plane = [&](int64_t pl) {
+    const float* b0 = a.in0 + pl * (int64_t)Na * a.Nb;
+    const float* b1 = TWO ? a.in1 + pl * (int64_t)Na * a.Nb : b0;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const int ro = (16 * t + m) * a.Nb;
+      p0[t][0] = *reinterpret_cast<const float4*>(b0 + ro + c0);
+      p0[t][1] = *reinterpret_cast<const float4*>(b0 + ro + c1);
+      if constexpr (TWO) {
+        p1[t][0] = *reinterpret_cast<const float4*>(b1 + ro + c0);
+        p1[t][1] = *reinterpret_cast<const float4*>(b1 + ro + c1);
+      }
+    }
+  };
+  int64_t pl = min(gw, a.planes - 1);
+  load_plane(pl);
+  for (int64_t it = gw; it < a.planes; it += nw) {
+    // first product, tile by tile straight from the load registers: operands pre-activated
+    // and masked; R tiles (t, nt), lane (m, q) register r = R[16 t + 4 q + r][16 nt + m]
+    f32x4 d[MT][NTJ];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const float4 u0 = p0[t][0], u1 = p0[t][1];
+      const float4 w0 = TWO ? p1[t][0] : u0, w1 = TWO ? p1[t][1] : u1;
+      const float raw[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+      const float rw[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      float xv[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const bool live = s < 4 ? live0 : live1;
+        float v = small_prologue<PIN>(raw[s], rw[s]);
+        if (BF) v = round_bf16(v);
+        xv[s] = __uint_as_float(__float_as_uint(v) & (live ? 0xffffffffu : 0u));
+      }
+#pragma unroll
+      for (int nt = 0; nt < NTJ; ++nt) {
+        f32x4 acc = zero4();
+        if constexpr (BF) {
+          bf16x8 av;
+#pragma unroll
+          for (int s = 0; s < 8; ++s)
+            av[s] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(xv[s]) >> 16));
+          acc = mfma_bf16(av, t1b[nt], acc);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[r] = round_bf16(acc[r]);
+        } else {
+#pragma unroll
+          for (int s = 0; s < 8; ++s) acc = mfma_f32(xv[s], t1r[nt][s], acc);
+        }
+        d[t][nt] = acc;
+      }
+    }
+    // the next plane's rows go out now, in flight during the second product and the combine
+    const int64_t nxt = min(it + nw, a.planes - 1);
+    load_plane(nxt);
+    // second product: K-step 4 t + r, k-slot q <-> row 16 t + 4 q + r
+    for (int mt2 = 0; mt2 < MT2; ++mt2) {
+      f32x4 x2[NTJ];
+#pragma unroll
+      for (int nt = 0; nt < NTJ; ++nt) x2[nt] = zero4();
+      const float* fr = s_f2 + (16 * mt2 + m) * F2S + 4 * q;
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const float4 f = *reinterpret_cast<const float4*>(fr + 16 * t);
+#pragma unroll
+        for (int nt = 0; nt < NTJ; ++nt) {
+          x2[nt] = mfma_f32(f.x, d[t][nt][0], x2[nt]);
+          x2[nt] = mfma_f32(f.y, d[t][nt][1], x2[nt]);
+          x2[nt] = mfma_f32(f.z, d[t][nt][2], x2[nt]);
+          x2[nt] = mfma_f32(f.w, d[t][nt][3], x2[nt]);
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < NTJ; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s_w[(16 * mt2 + 4 * q + r) * JP + 16 * nt + m] = x2[nt][r];
+    }
+    // combine into the complex spectrum [2 ma][mb] (same wave: LDS ops complete in order)
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's X2 writes are done
+    __builtin_amdgcn_wave_barrier();
+    float2* dst = a.out + it * (int64_t)(2 * a.ma * a.mb);
+    for (int e = lane; e < 2 * a.ma * a.mb; e += 64) {
+      const int s = e / a.mb, k = e - s * a.mb;
+      const float* c = s_w + s * JP + 2 * k;
+      const float* sn = s_w + (2 * a.ma + s) * JP + 2 * k;
+      dst[e] = make_float2(c[0] + sn[1], c[1] - sn[0]);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // reads of s_w done before the next plane rewrites it
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// The small-plane transform applies when the contiguous axis is short and the row axis fits
+// the register-resident first product.
+bool plane_small_ok(const fno_plan* p) {
+  const Geom& g = p->g;
+  if (g.Nb > 32 || g.Nb % 4 != 0) return false;
+  if (!(g.Na == 16 || g.Na == 32 || g.Na == 64 || g.Na == 128)) return false;
+  if (!(p->jpad == 16 || p->jpad == 32)) return false;
+  if (g.ma % 4 != 0 || 4 * g.ma > 128) return false;
+  return true;
+}
+
+template <int PIN, bool BF, int MT>
+static void launch_small_t(const fno_plan* p, const SmallPlaneArgs& a, hipStream_t s) {
+  const int jp = p->jpad;
+  const size_t lds = sizeof(float) * (4 * a.ma * (a.Na + 4) + 4 * (4 * a.ma) * jp);
+  const int64_t want = (a.planes + 3) / 4;
+  const unsigned grid = (unsigned)(want < 2048 ? want : 2048);
+  if (lds > 65536) {  // wide row spectra need more than the default dynamic LDS limit
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_plane_small<PIN, BF, MT, 1>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_plane_small<PIN, BF, MT, 2>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  }
+  if (jp == 16)
+    hipLaunchKernelGGL((k_plane_small<PIN, BF, MT, 1>), dim3(grid), dim3(256), lds, s, a);
+  else
+    hipLaunchKernelGGL((k_plane_small<PIN, BF, MT, 2>), dim3(grid), dim3(256), lds, s, a);
+}
+
+template <int PIN, bool BF>
+static void launch_small_mt(const fno_plan* p, const SmallPlaneArgs& a, hipStream_t s) {
+  switch (a.Na) {
+    case 16: launch_small_t<PIN, BF, 1>(p, a, s); break;
+    case 32: launch_small_t<PIN, BF, 2>(p, a, s); break;
+    case 64: launch_small_t<PIN, BF, 4>(p, a, s); break;
+    default: launch_small_t<PIN, BF, 8>(p, a, s); break;
+  }
+}
+
+template <int PIN>
+static void launch_small_pin(const fno_plan* p, const SmallPlaneArgs& a, hipStream_t s) {
+  if (p->g.bf16)
+    launch_small_mt<PIN, true>(p, a, s);
+  else
+    launch_small_mt<PIN, false>(p, a, s);
+}
+
+hipError_t launch_plane_small(const fno_plan* p, int plane_in, int chans, const float* in0,
+                              const float* in1, float2* out, hipStream_t s) {
+  const Geom& g = p->g;
+  SmallPlaneArgs a{};
+  a.Na = g.Na;
+  a.Nb = g.Nb;
+  a.ma = g.ma;
+  a.mb = g.mb;
+  a.planes = (int64_t)g.B * chans * g.O;
+  a.in0 = in0;
+  a.in1 = in1;
+  a.t1 = p->t.t1;
+  a.t1bf = p->t.t1_bf;
+  a.f2 = p->t.f2;
+  a.out = out;
+  switch (plane_in) {
+    case PLANE_X: launch_small_pin<PLANE_X>(p, a, s); break;
+    case PLANE_TANH: launch_small_pin<PLANE_TANH>(p, a, s); break;
+    default: launch_small_pin<PLANE_GELU_GRAD>(p, a, s); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fno

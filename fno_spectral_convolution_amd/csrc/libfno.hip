@@ -187,6 +187,7 @@ fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out) {
     int rows = (int)((g.Na + want - 1) / want);
     rows = (rows + 63) / 64 * 64;
     if (rows > g.Na) rows = g.Na;
+    if (fno::plane_small_ok(p)) rows = g.Na;  // the short-row kernel never chunks
     p->plane_rows = rows;
     p->nch = (g.Na + rows - 1) / rows;
   }
