@@ -99,6 +99,9 @@ def kernel_model(wl, plan):
         "mix_bwd_dx": (wbytes + 2 * spec, mixf),
         "mix_bwd_dw": (wbytes + 2 * spec, mixf),
         "epilogue_fwd": (4 * U + 4 * U + (4 * U if wl.train else 0) + T, dft_last + bypass),
+        # short rows: the epilogue also inverts axis a, from the [2ma][mb] spectrum per plane
+        "epilogue_rows_fwd": (4 * U + 4 * U + (4 * U if wl.train else 0) + plane_spec,
+                              dft_last + dft_a + bypass),
         "epilogue_bwd": (16 * U + T, dft_last + 2 * bypass),
         "mse": (12 * U, 3 * U),
     }

@@ -123,6 +123,13 @@ hipError_t launch_epilogue_bwd(const fno_plan* p, int mode, const float2* Tg, co
                                const float* wb, const float* gy, const float* z,
                                float* grad_x, float* red_part, hipStream_t s);
 bool epilogue_fast_ok(const fno_plan* p, int mode, bool fwd);
+// Short contiguous axis: the forward epilogue fused with the inverse of axis a; T is the
+// spectrum after the inverse of the outer axes 0..d-3 only, [B][Cout][O][2ma][mb].
+bool epilogue_rows_ok(const fno_plan* p, int mode, const float* x, const float* y,
+                      const float* zsave);
+hipError_t launch_epilogue_rows(const fno_plan* p, int mode, const float2* T, const float* x,
+                                const float* wb, const float* bias, float* y, float* zsave,
+                                hipStream_t s);
 // the backward epilogue takes the matrix-core kernel (which writes epilogue_bwd_fast_groups
 // partial rows) only when grad_x is produced; otherwise the generic kernel (nred rows)
 inline bool epilogue_bwd_fast(const fno_plan* p, int mode, const float* grad_x) {

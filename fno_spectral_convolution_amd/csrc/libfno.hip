@@ -621,15 +621,15 @@ fno_status forward_transform(const fno_plan* p, int plane_in, int chans, const f
   return FNO_OK;
 }
 
-// Inverse transform of the outer axes 0..d-2 of a spectrum [B][chans][K] into
-// T [B][chans][lines][mb]; returns the buffer holding T.
+// Inverse transform of the outer axes 0..naxes-1 of a spectrum [B][chans][K]: all of
+// 0..d-2 (naxes = d-1) gives T [B][chans][lines][mb]; returns the buffer holding the result
+// (src itself when naxes = 0).
 fno_status inverse_outer(const fno_plan* p, int chans, const float2* src, void* ws,
-                         hipStream_t s, const float2** T) {
-  const fno::Geom& g = p->g;
+                         hipStream_t s, const float2** T, int naxes) {
   float2* ping = at<float2>(ws, p->ws.spec_a);
   float2* pong = at<float2>(ws, p->ws.spec_b);
   const float2* cur = src;
-  for (int j = 0; j <= g.d - 2; ++j) {
+  for (int j = 0; j < naxes; ++j) {
     float2* nxt = (cur == ping) ? pong : ping;
     LAUNCH("outer_inv", s, fno::launch_outer_inv(p, j, chans, cur, nxt, s));
     cur = nxt;
@@ -671,7 +671,13 @@ fno_status fno_spectral_conv_fwd(const fno_plan* p, const float* x, const float*
   float2* yhat = at<float2>(ws, p->ws.yhat);
   LAUNCH("mix_fwd", s, fno::launch_mix_fwd(p, xhat, 1, 0, reinterpret_cast<const float2*>(w), yhat, s));
   const float2* T = nullptr;
-  st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T);
+  if (fno::epilogue_rows_ok(p, fno::EPI_SPECTRAL, x, y_spec, nullptr)) {
+    st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T, p->g.d - 2);
+    if (st != FNO_OK) return st;
+    LAUNCH("epilogue_rows_spec_fwd", s, fno::launch_epilogue_rows(p, fno::EPI_SPECTRAL, T, x, nullptr, nullptr, y_spec, nullptr, s));
+    return FNO_OK;
+  }
+  st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T, p->g.d - 1);
   if (st != FNO_OK) return st;
   LAUNCH("epilogue_spec_fwd", s, fno::launch_epilogue_fwd(p, fno::EPI_SPECTRAL, T, x, nullptr, nullptr, y_spec, nullptr,
                                   s));
@@ -697,10 +703,16 @@ fno_status fno_block_fwd(const fno_plan* p, const float* x, const float* w, cons
   float2* yhat = at<float2>(ws, p->ws.yhat);
   LAUNCH("mix_fwd", s, fno::launch_mix_fwd(p, xhat, 1, 0, reinterpret_cast<const float2*>(w), yhat, s));
   const float2* T = nullptr;
-  st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T);
-  if (st != FNO_OK) return st;
   float* zsave = (save && (p->desc.flags & FNO_FLAG_GELU)) ? at<float>(save, p->save_off_z)
                                                             : nullptr;
+  if (fno::epilogue_rows_ok(p, fno::EPI_BLOCK, x, y, zsave)) {
+    st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T, p->g.d - 2);
+    if (st != FNO_OK) return st;
+    LAUNCH("epilogue_rows_fwd", s, fno::launch_epilogue_rows(p, fno::EPI_BLOCK, T, x, wb, bias, y, zsave, s));
+    return FNO_OK;
+  }
+  st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T, p->g.d - 1);
+  if (st != FNO_OK) return st;
   LAUNCH("epilogue_fwd", s, fno::launch_epilogue_fwd(p, fno::EPI_BLOCK, T, x, wb, bias, y, zsave, s));
   return FNO_OK;
 }
@@ -739,7 +751,7 @@ fno_status fno_spectral_conv_bwd(const fno_plan* p, const float* x, const float*
     float2* ghx = at<float2>(ws, p->ws.xhat);
     LAUNCH("mix_bwd_dx", s, fno::launch_mix_bwd_dx(p, ghat, reinterpret_cast<const float2*>(w), ghx, s));
     const float2* Tg = nullptr;
-    st = inverse_outer(p, g.Cin, ghx, ws, s, &Tg);
+    st = inverse_outer(p, g.Cin, ghx, ws, s, &Tg, g.d - 1);
     if (st != FNO_OK) return st;
     LAUNCH("epilogue_spec_bwd", s, fno::launch_epilogue_bwd(p, fno::EPI_SPECTRAL, Tg, x, nullptr, nullptr, nullptr,
                                     grad_x, nullptr, s));
@@ -782,7 +794,7 @@ fno_status fno_block_bwd(const fno_plan* p, const float* x, const float* w, cons
     if (grad_x) {
       float2* ghx = at<float2>(ws, p->ws.xhat);
       LAUNCH("mix_bwd_dx", s, fno::launch_mix_bwd_dx(p, ghat, reinterpret_cast<const float2*>(w), ghx, s));
-      st = inverse_outer(p, g.Cin, ghx, ws, s, &Tg);
+      st = inverse_outer(p, g.Cin, ghx, ws, s, &Tg, g.d - 1);
       if (st != FNO_OK) return st;
     }
     LAUNCH("epilogue_bwd", s, fno::launch_epilogue_bwd(p, fno::EPI_BLOCK, Tg, x, wb, gy, z, grad_x, red, s));

@@ -40,6 +40,10 @@ CASES = [
     ("3d_short_t20_jp32", 2, 5, 3, (6, 32, 20), (3, 8, 10)),
     ("3d_short_na128", 1, 2, 3, (4, 128, 12), (2, 12, 6)),
     ("2d_short_max", 2, 3, 2, (128, 32), (32, 16)),
+    # shapes taken by the fused row-axis epilogue (rows a multiple of 16, ma <= 12, mb <= 8)
+    ("2d_rows_c20", 2, 20, 20, (32, 20), (8, 8)),
+    ("3d_rows_c9_17", 2, 9, 17, (4, 48, 24), (2, 8, 7)),
+    ("2d_rows_nb32", 1, 12, 5, (64, 32), (12, 8)),
 ]
 
 
