@@ -83,6 +83,52 @@ __device__ __forceinline__ void stage_line(const EpiArgs& a, const float2* Trow0
   }
 }
 
+// The same staging split in two, so that a line's spectrum rows can be loaded while the
+// previous line is computed: float4 e = tid + 256 i is channel e / 16, columns 4 (e % 16) ..;
+// outside the spectrum (channel >= C or column >= 2 mb) a clamped address is loaded and zeros
+// are written.
+template <int C>
+struct LineT {
+  static constexpr int CP = (C + 15) / 16 * 16;
+  static constexpr int N = (CP * (kMaxKpad / 4) + 255) / 256;
+  float4 v[N];
+};
+
+template <int C>
+__device__ __forceinline__ void load_line(const EpiArgs& a, const float2* Trow0, LineT<C>& t,
+                                          int tid) {
+  const int64_t cstride = a.lines * a.mb;
+#pragma unroll
+  for (int i = 0; i < LineT<C>::N; ++i) {
+    const int e = tid + 256 * i;
+    const int c = min(e >> 4, C - 1), k4 = min(4 * (e & 15), 2 * a.mb - 4);
+    t.v[i] = *reinterpret_cast<const float4*>(
+        reinterpret_cast<const float*>(Trow0 + (int64_t)c * cstride) + k4);
+  }
+}
+
+template <int C, bool BF>
+__device__ __forceinline__ void write_line(const EpiArgs& a, const LineT<C>& t,
+                                           unsigned char* tl, int tid) {
+  constexpr int kst = kMaxKpad + (BF ? 8 : 4);
+#pragma unroll
+  for (int i = 0; i < LineT<C>::N; ++i) {
+    const int e = tid + 256 * i;
+    if (e >= LineT<C>::CP * (kMaxKpad / 4)) break;
+    const int c = e >> 4, k4 = 4 * (e & 15);
+    const bool live = c < C && k4 < 2 * a.mb;
+    const float4 v = live ? t.v[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (BF) {
+      uint2 pk;
+      pk.x = pack_bf16x2(v.x, v.y);
+      pk.y = pack_bf16x2(v.z, v.w);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(tl) + c * kst + k4) = pk;
+    } else {
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(tl) + c * kst + k4) = v;
+    }
+  }
+}
+
 // Fragments of the last-axis table for one point group of this wave: A operand rows
 // pb0 + 16 (tbase + j) + m, all K-steps (kpad <= 64).  Loaded one group ahead.
 template <int TMW, bool BF>
@@ -96,13 +142,14 @@ struct GtFrag<TMW, false> {
   float4 v[TMW][4];  // K-groups of 16
 };
 
-template <int TMW, bool BF, bool IL = false>
+template <int TMW, bool BF, bool IL = false, int MT = 4>
 __device__ __forceinline__ void load_gt(const EpiArgs& a, int pb0, int tbase, int m, int q,
                                         GtFrag<TMW, BF>& f) {
 #pragma unroll
   for (int j = 0; j < TMW; ++j) {
-    // row m of M-tile t: point 4 m + t (interleaved) or 16 t + m of the group
-    const int pt = IL ? 4 * m + tbase + j : 16 * (tbase + j) + m;
+    // row m of M-tile t: point MT m + t (interleaved over the MT tiles of the step) or
+    // 16 t + m of the group
+    const int pt = IL ? MT * m + tbase + j : 16 * (tbase + j) + m;
     const int64_t row = (int64_t)(pb0 + pt) * a.kpad;
     if constexpr (BF) {
       const uint16_t* gt = static_cast<const uint16_t*>(a.gt) + row;
@@ -174,135 +221,199 @@ __device__ __forceinline__ void store_lds_run(float* p, const float (&v)[N]) {
   }
 }
 
-// Row loads of a [C][64] tile: thread t takes float4 t + 256 u, i.e. channel (t >> 4) + 16 u,
-// points 4 (t & 15) .. + 3, from base (already offset to this thread's first row and point).
-template <int C, int NPT>
+// Row loads of a [C][64 G] tile (NF4 = 16 G C float4): thread t takes float4 t + 256 u, i.e.
+// channel t / (16 G) + u (256 / 16 G), points 4 (t % 16 G) .. + 3, from base (already offset to
+// this thread's first row and point).
+template <int NF4, int NPT>
 __device__ __forceinline__ void load_rows(float4 (&v)[NPT], const float* base, int64_t ustride,
                                           int tid) {
 #pragma unroll
   for (int u = 0; u < NPT; ++u) {
-    if constexpr ((16 * C) % 256 == 0) {
+    if constexpr (NF4 % 256 == 0) {
       v[u] = *reinterpret_cast<const float4*>(base + u * ustride);
     } else {
-      if (tid + 256 * u < 16 * C) v[u] = *reinterpret_cast<const float4*>(base + u * ustride);
+      if (tid + 256 * u < NF4) v[u] = *reinterpret_cast<const float4*>(base + u * ustride);
     }
   }
 }
 
 // ------------------------------------------------------------------------------------------
 // Forward.  A work-group owns lpw consecutive lines of one batch entry: a contiguous range of
-// points, walked in 64-point groups.  The spectrum rows of a line are staged in LDS when the
-// line starts; the group loop itself is straight-line code, so the compiler can keep the
-// prefetches in flight across it: the x rows of group f + 1 are loaded while group f is
-// computed, then the table fragments of group f + 1 (issued in the order they are consumed;
-// the last group re-loads itself instead of branching).  The 4 waves split the output tiles
-// (wave w: channel tile w % NT, M-tiles tbase ..).  Row m of M-tile t is point 4 m + t of the
-// group, so one lane's A operands of its TMW tiles are adjacent in the [channel][point] LDS
-// tile (one LDS read feeds TMW products).  The z tile goes through LDS and the stores are
-// row-contiguous: 16 threads write one channel's 64 points.
+// points, walked in steps of G 64-point groups (G = 2 for narrow fields).  The spectrum rows of
+// a line are staged in LDS when the line starts (narrow fields: loaded one line ahead); the
+// step loop itself is straight-line code, so the compiler can keep the prefetches in flight
+// across it: the x rows of step f + 1 are loaded while step f is computed, then the table
+// fragments of step f + 1 (the last step re-loads itself instead of branching).  Wave w owns
+// the M-tiles (16 points each) w G .. w G + G - 1 of the step for every channel tile, so each
+// table fragment is loaded once per work-group and each x operand feeds NT products.  Row m of
+// M-tile t is point MT m + t of the step (MT = 4 G tiles), so a lane's A operands of its G
+// tiles are adjacent in the [channel][point] LDS tile.  The z tile goes through LDS and the
+// stores are row-contiguous: 16 G threads write one channel's 64 G points.
 // MODE: 0 spectral part only, 1 block (bypass, bias, optional GELU), 2 block + z save.
-template <int C, bool BF, int MODE>
+template <int C, bool BF, int MODE, int G>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C == 64 ? 3 : 4)))
 k_epi_fwd_line(EpiArgs a) {
   constexpr int CP = (C + 15) / 16 * 16;
   constexpr int NT = CP / 16;
-  constexpr int TMW = NT;
-  constexpr int NPT = NT;  // float4 of a [CP][64] tile per thread
+  constexpr int PI = PG * G;        // points per step
+  constexpr int XSG = PI + 4;       // LDS row stride (floats)
+  constexpr int MT = 4 * G;         // M-tiles per step; wave w owns tiles w G .. w G + G - 1
+  constexpr int FPC = 16 * G;       // float4 per channel row of a step
+  constexpr int NF4 = FPC * C;      // float4 of an x / z tile
+  constexpr int NPT = (NF4 + 255) / 256;
   constexpr bool BLK = MODE >= 1;
   constexpr bool ZS = MODE == 2;
-  __shared__ __attribute__((aligned(16))) float s_x[BLK ? CP * XS : 4];
-  __shared__ __attribute__((aligned(16))) float s_o[CP * XS];
+  static_assert(G == 1 || G == 2, "LDS runs of 1 or 2 floats");
+  __shared__ __attribute__((aligned(16))) float s_x[BLK ? CP * XSG : 4];
+  __shared__ __attribute__((aligned(16))) float s_o[CP * XSG];
   __shared__ __attribute__((aligned(16))) unsigned char s_tl[CP * (kMaxKpad + 8) * (BF ? 2 : 4)];
   __shared__ float s_bias[CP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, q = lane >> 4;
-  const int ct = wave % NT, tbase = (wave / NT) * TMW;
+  const int tbase = wave * G;
   const int64_t wg_per_b = a.lines / a.lpw;
   const int b = (int)(blockIdx.x / wg_per_b);
   const int64_t l0 = (int64_t)(blockIdx.x - (int64_t)b * wg_per_b) * a.lpw;
-  const int gpl = 1 << a.gpl_log2;
+  const int gpl = 1 << a.gpl_log2;  // steps per line
   const int nf = a.lpw << a.gpl_log2;
-  // Wb^T slice: B operand of K-step kb, lane (n = m, q): Wb[16 ct + m][4 kb + q]
-  float wbr[BLK ? C / 4 : 1];
+  // Wb^T slices: B operand of channel tile ct, K-step kb, lane (n = m, q): Wb[16 ct + m][4 kb + q]
+  float wbr[BLK ? NT : 1][BLK ? C / 4 : 1];
   if (BLK) {
-    const int o = 16 * ct + m;
 #pragma unroll
-    for (int kb = 0; kb < C / 4; ++kb) wbr[kb] = 0.f;
-    if (o < C) {
+    for (int ct = 0; ct < NT; ++ct) {
+      const int o = 16 * ct + m;
 #pragma unroll
-      for (int kb = 0; kb < C / 4; ++kb) wbr[kb] = a.wb[o * C + 4 * kb + q];
+      for (int kb = 0; kb < C / 4; ++kb) {
+        const float w = a.wb[min(o, C - 1) * C + 4 * kb + q];
+        wbr[ct][kb] = o < C ? w : 0.f;
+      }
     }
   }
   for (int o = tid; o < CP; o += 256) s_bias[o] = (BLK && o < C && a.bias) ? a.bias[o] : 0.f;
-  // this thread's rows of the x / y / z tiles: channel e >> 4, points 4 (e & 15) .. + 3
+  // float4 e = tid + 256 u of a tile: channel e / FPC, points 4 (e % FPC) .. + 3.  Past the
+  // tile (e >= NF4) a thread loads and stores a copy of the last float4 (identical data) and
+  // writes its x into the padding rows C .. CP - 1, which nothing reads: no branch anywhere.
+  static_assert(256 * NPT <= FPC * CP, "tail float4 land in the padding rows");
   const int64_t pbase = l0 * a.Nb;
-  const int64_t rowoff = ((int64_t)b * C + (tid >> 4)) * a.P + pbase + 4 * (tid & 15);
-  const int64_t ustride = 16 * a.P;  // 256 threads further = 16 channels down
+  int64_t goff[NPT];
+  int xl[NPT], ol[NPT];
+#pragma unroll
+  for (int u = 0; u < NPT; ++u) {
+    const int e = tid + 256 * u, ec = min(e, NF4 - 1);
+    goff[u] = ((int64_t)b * C + ec / FPC) * a.P + pbase + 4 * (ec % FPC);
+    xl[u] = (e / FPC) * XSG + 4 * (e % FPC);
+    ol[u] = (ec / FPC) * XSG + 4 * (ec % FPC);
+  }
   float4 pre[NPT];
 #pragma unroll
   for (int u = 0; u < NPT; ++u) pre[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-  GtFrag<TMW, BF> gtf;
-  if (BLK) load_rows<C, NPT>(pre, a.x + rowoff, ustride, tid);
-  load_gt<TMW, BF, true>(a, 0, tbase, m, q, gtf);
+  GtFrag<G, BF> gtf;
+  if (BLK) {
+#pragma unroll
+    for (int u = 0; u < NPT; ++u) pre[u] = *reinterpret_cast<const float4*>(a.x + goff[u]);
+  }
+  load_gt<G, BF, true, MT>(a, 0, tbase, m, q, gtf);
+  // narrow fields have few steps per line: the next line's spectrum rows stream in while
+  // this one is computed (the last line re-loads itself); wide ones stage each line directly
+  constexpr bool LPF = C < 64;
+  const float2* Tb = a.T + ((int64_t)b * C * a.lines + l0) * a.mb;
+  LineT<LPF ? C : 16> tln;
+  if constexpr (LPF) load_line<C>(a, Tb, tln, tid);
+  constexpr int kst = kMaxKpad + (BF ? 8 : 4);
   for (int lf = 0; lf < a.lpw; ++lf) {
     // every reader of the previous line's spectrum is past that line's last barrier
-    const float2* Trow0 = a.T + ((int64_t)b * C * a.lines + l0 + lf) * a.mb;
-    stage_line<C, BF>(a, Trow0, s_tl, tid);
+    if constexpr (LPF) {
+      write_line<C, BF>(a, tln, s_tl, tid);
+      load_line<C>(a, Tb + (int64_t)min(lf + 1, a.lpw - 1) * a.mb, tln, tid);
+    } else {
+      stage_line<C, BF>(a, Tb + (int64_t)lf * a.mb, s_tl, tid);
+    }
     for (int g = 0; g < gpl; ++g) {
       const int f = (lf << a.gpl_log2) + g;
       const int fn = min(f + 1, nf - 1);
       if (BLK) {
 #pragma unroll
-        for (int u = 0; u < NPT; ++u) {
-          const int e = tid + 256 * u;
-          if ((16 * C) % 256 == 0 || e < 16 * C)
-            *reinterpret_cast<float4*>(s_x + (e >> 4) * XS + 4 * (e & 15)) = pre[u];
-        }
-        load_rows<C, NPT>(pre, a.x + rowoff + 64 * fn, ustride, tid);
+        for (int u = 0; u < NPT; ++u) *reinterpret_cast<float4*>(s_x + xl[u]) = pre[u];
+#pragma unroll
+        for (int u = 0; u < NPT; ++u)
+          pre[u] = *reinterpret_cast<const float4*>(a.x + goff[u] + PI * fn);
       }
       __syncthreads();  // x tile and spectrum rows visible; previous z tile consumed
-      f32x4 acc[TMW];
+      f32x4 acc[G][NT];
 #pragma unroll
-      for (int j = 0; j < TMW; ++j) acc[j] = zero4();
-      spectral_coop<C, TMW, BF>(a, s_tl, gtf, ct, m, q, acc);
-      load_gt<TMW, BF, true>(a, (fn & (gpl - 1)) * PG, tbase, m, q, gtf);
+      for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) acc[j][ct] = zero4();
+      // spectral part: A = table rows of this wave's tiles, B = spectrum row of channel 16 ct + m
+      if constexpr (BF) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          if (32 * s2 >= a.kpad) break;
+#pragma unroll
+          for (int ct = 0; ct < NT; ++ct) {
+            const bf16x8 B = *reinterpret_cast<const bf16x8*>(
+                reinterpret_cast<const uint16_t*>(s_tl) + (16 * ct + m) * kst + 32 * s2 + 8 * q);
+#pragma unroll
+            for (int j = 0; j < G; ++j) acc[j][ct] = mfma_bf16(gtf.v[j][s2], B, acc[j][ct]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          if (16 * g4 >= a.kpad) break;
+#pragma unroll
+          for (int ct = 0; ct < NT; ++ct) {
+            const float4 B4 = *reinterpret_cast<const float4*>(
+                reinterpret_cast<const float*>(s_tl) + (16 * ct + m) * kst + 16 * g4 + 4 * q);
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+              acc[j][ct] = mfma_f32(gtf.v[j][g4].x, B4.x, acc[j][ct]);
+              acc[j][ct] = mfma_f32(gtf.v[j][g4].y, B4.y, acc[j][ct]);
+              acc[j][ct] = mfma_f32(gtf.v[j][g4].z, B4.z, acc[j][ct]);
+              acc[j][ct] = mfma_f32(gtf.v[j][g4].w, B4.w, acc[j][ct]);
+            }
+          }
+        }
+      }
+      load_gt<G, BF, true, MT>(a, (fn & (gpl - 1)) * PI, tbase, m, q, gtf);
       if (BLK) {
 #pragma unroll
         for (int kb = 0; kb < C / 4; ++kb) {
-          float av[TMW];
-          load_lds_run<TMW>(av, s_x + (4 * kb + q) * XS + 4 * m + tbase);
+          float av[G];
+          load_lds_run<G>(av, s_x + (4 * kb + q) * XSG + MT * m + tbase);
 #pragma unroll
-          for (int j = 0; j < TMW; ++j) acc[j] = mfma_f32(av[j], wbr[kb], acc[j]);
+          for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+            for (int j = 0; j < G; ++j) acc[j][ct] = mfma_f32(av[j], wbr[ct][kb], acc[j][ct]);
         }
       }
-      // lane (n = m, q), tile tbase + j, register r: channel 16 ct + m, point 16 q + 4 r + tbase + j
-      {
+      // lane (n = m, q), tile tbase + j, register r: channel 16 ct + m, point
+      // MT (4 q + r) + tbase + j
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) {
         const int o = 16 * ct + m;
         const float bo = s_bias[o];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float v[TMW];
+          float v[G];
 #pragma unroll
-          for (int j = 0; j < TMW; ++j) v[j] = acc[j][r] + bo;
-          store_lds_run<TMW>(s_o + o * XS + 16 * q + 4 * r + tbase, v);
+          for (int j = 0; j < G; ++j) v[j] = acc[j][ct][r] + bo;
+          store_lds_run<G>(s_o + o * XSG + MT * (4 * q + r) + tbase, v);
         }
       }
       __syncthreads();  // z tile complete; x tile free
 #pragma unroll
       for (int u = 0; u < NPT; ++u) {
-        const int e = tid + 256 * u;
-        if ((16 * C) % 256 == 0 || e < 16 * C) {
-          float4 v = *reinterpret_cast<const float4*>(s_o + (e >> 4) * XS + 4 * (e & 15));
-          const int64_t off = rowoff + u * ustride + 64 * f;
-          if (ZS) *reinterpret_cast<float4*>(a.z + off) = v;
-          if (BLK && a.gelu) {
-            v.x = gelu_as(v.x);
-            v.y = gelu_as(v.y);
-            v.z = gelu_as(v.z);
-            v.w = gelu_as(v.w);
-          }
-          *reinterpret_cast<float4*>(a.y + off) = v;
+        float4 v = *reinterpret_cast<const float4*>(s_o + ol[u]);
+        const int64_t off = goff[u] + PI * f;
+        if (ZS) *reinterpret_cast<float4*>(a.z + off) = v;
+        if (BLK && a.gelu) {
+          v.x = gelu_as(v.x);
+          v.y = gelu_as(v.y);
+          v.z = gelu_as(v.z);
+          v.w = gelu_as(v.w);
         }
+        *reinterpret_cast<float4*>(a.y + off) = v;
       }
     }
   }
@@ -371,9 +482,9 @@ k_epi_bwd_line(EpiArgs a) {
     px[u] = pg_y[u];
   }
   GtFrag<TMW, BF> gtf;
-  if (BLK) load_rows<C, NPT>(pg_y, a.gy + rowoff, ustride, tid);
-  if (GL) load_rows<C, NPT>(pz, a.zin + rowoff, ustride, tid);
-  if (NX) load_rows<C, NPT>(px, a.x + rowoff, ustride, tid);
+  if (BLK) load_rows<16 * C, NPT>(pg_y, a.gy + rowoff, ustride, tid);
+  if (GL) load_rows<16 * C, NPT>(pz, a.zin + rowoff, ustride, tid);
+  if (NX) load_rows<16 * C, NPT>(px, a.x + rowoff, ustride, tid);
   load_gt<TMW, BF, true>(a, 0, tbase, m, q, gtf);
   for (int lf = 0; lf < a.lpw; ++lf) {
     // every reader of the previous line's spectrum is past that line's last barrier
@@ -400,9 +511,9 @@ k_epi_bwd_line(EpiArgs a) {
           if (NX) *reinterpret_cast<float4*>(s_x + lo) = px[u];
         }
       }
-      if (BLK) load_rows<C, NPT>(pg_y, a.gy + rowoff + 64 * fn, ustride, tid);
-      if (GL) load_rows<C, NPT>(pz, a.zin + rowoff + 64 * fn, ustride, tid);
-      if (NX) load_rows<C, NPT>(px, a.x + rowoff + 64 * fn, ustride, tid);
+      if (BLK) load_rows<16 * C, NPT>(pg_y, a.gy + rowoff + 64 * fn, ustride, tid);
+      if (GL) load_rows<16 * C, NPT>(pz, a.zin + rowoff + 64 * fn, ustride, tid);
+      if (NX) load_rows<16 * C, NPT>(px, a.x + rowoff + 64 * fn, ustride, tid);
       __syncthreads();  // g_z / x tiles and spectrum rows visible; previous grad tile consumed
       f32x4 acc[TMW];
 #pragma unroll
@@ -507,10 +618,10 @@ k_epi_bwd_line(EpiArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-template <int C>
+template <int C, int G>
 static hipError_t launch_fwd_c(const EpiArgs& a, bool bf, int mode, int wgs, hipStream_t s) {
 #define FNO_EPI_FWD(BFV, MV) \
-  hipLaunchKernelGGL((k_epi_fwd_line<C, BFV, MV>), dim3(wgs), dim3(256), 0, s, a)
+  hipLaunchKernelGGL((k_epi_fwd_line<C, BFV, MV, G>), dim3(wgs), dim3(256), 0, s, a)
   if (bf) {
     if (mode == 0) FNO_EPI_FWD(true, 0);
     else if (mode == 1) FNO_EPI_FWD(true, 1);
@@ -584,8 +695,10 @@ hipError_t launch_epilogue_fwd_fast(const fno_plan* p, int mode, const float2* T
   a.kpad = p->kpad;
   a.lines = g.P / g.Nb;
   a.lpw = fwd_lines_per_wg(a.lines, g.B);
+  // narrow fields take two 64-point groups per step when a line holds them
+  const int G = (g.Cout <= 32 && g.Nb >= 2 * PG) ? 2 : 1;
   int gl = 0;
-  while ((PG << gl) < g.Nb) ++gl;
+  while ((PG * G << gl) < g.Nb) ++gl;
   a.gpl_log2 = gl;
   a.x = x;
   a.T = T;
@@ -599,11 +712,18 @@ hipError_t launch_epilogue_fwd_fast(const fno_plan* p, int mode, const float2* T
   a.block = kmode != 0;
   const int64_t wgs = (int64_t)g.B * a.lines / a.lpw;
   if (wgs > 0x7fffffff) return hipErrorInvalidValue;
+  if (G == 2) {
+    switch (g.Cout) {
+      case 16: return launch_fwd_c<16, 2>(a, g.bf16, kmode, (int)wgs, s);
+      case 20: return launch_fwd_c<20, 2>(a, g.bf16, kmode, (int)wgs, s);
+      default: return launch_fwd_c<32, 2>(a, g.bf16, kmode, (int)wgs, s);
+    }
+  }
   switch (g.Cout) {
-    case 16: return launch_fwd_c<16>(a, g.bf16, kmode, (int)wgs, s);
-    case 20: return launch_fwd_c<20>(a, g.bf16, kmode, (int)wgs, s);
-    case 32: return launch_fwd_c<32>(a, g.bf16, kmode, (int)wgs, s);
-    default: return launch_fwd_c<64>(a, g.bf16, kmode, (int)wgs, s);
+    case 16: return launch_fwd_c<16, 1>(a, g.bf16, kmode, (int)wgs, s);
+    case 20: return launch_fwd_c<20, 1>(a, g.bf16, kmode, (int)wgs, s);
+    case 32: return launch_fwd_c<32, 1>(a, g.bf16, kmode, (int)wgs, s);
+    default: return launch_fwd_c<64, 1>(a, g.bf16, kmode, (int)wgs, s);
   }
 }
 
