@@ -420,48 +420,57 @@ k_epi_fwd_line(EpiArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Backward.  Same line ownership and straight-line group pipeline as the forward: the g_y, z
-// and x rows of group f + 1 and its table fragments are in flight while group f is computed.
+// Backward.  Same line ownership and straight-line step pipeline as the forward (steps of G
+// 64-point groups, wave w owning M-tiles w G .. w G + G - 1 for every channel tile): the g_y, z
+// and x rows of step f + 1 and its table fragments are in flight while step f is computed.
 //   grad_x tile : spectral product with the unit-scale table, times s(x) = 1 - tanh^2 on the
 //                 tanh path, plus Wb^T g_z (A operand g_z in the interleaved point mapping);
 //                 stored through LDS with row-contiguous float4 stores
 //   dWb, dbias  : dWb[o][i] += sum_p g_z[o][p] x[i][p] (16x16x4 f32, K = points), reduced over
 //                 the work-group in a fixed order into one partial row per work-group
 // Wave w's dWb tiles: NT = 4: o-tile w, all 4 i-tiles; NT = 2: o-tile w >> 1, i-tile w & 1;
-// NT = 1: the single tile over the 16 points 16 w .. 16 w + 15 of each group.
+// NT = 1: the single tile over its quarter of the step's points.
 // MODE: 1 spectral part only (grad_x = s(x) * spectral), 3 block, 7 block with GELU' (z read).
-template <int C, bool BF, bool TANH, int MODE>
+template <int C, bool BF, bool TANH, int MODE, int G>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C == 64 ? 2 : 3)))
 k_epi_bwd_line(EpiArgs a) {
   constexpr int CP = (C + 15) / 16 * 16;
   constexpr int NT = CP / 16;
-  constexpr int TMW = NT;
-  constexpr int NPT = NT;
+  constexpr int PI = PG * G;        // points per step
+  constexpr int XSG = PI + 4;       // LDS row stride (floats)
+  constexpr int MT = 4 * G;         // M-tiles per step
+  constexpr int FPC = 16 * G;       // float4 per channel row of a step
+  constexpr int NF4 = FPC * C;
+  constexpr int NPT = (NF4 + 255) / 256;
   constexpr bool BLK = (MODE & 2) != 0;
   constexpr bool GL = (MODE & 4) != 0;
   constexpr bool NX = BLK || TANH;  // x rows needed
   constexpr int DT = (NT == 4) ? 4 : 1;  // dWb tiles per wave
-  __shared__ __attribute__((aligned(16))) float s_gz[BLK ? CP * XS : 4];
-  __shared__ __attribute__((aligned(16))) float s_x[NX ? CP * XS : 4];
-  __shared__ __attribute__((aligned(16))) float s_o[CP * XS];
+  static_assert(G == 1 || G == 2, "LDS runs of 1 or 2 floats");
+  static_assert(256 * NPT <= FPC * CP, "tail float4 land in the padding rows");
+  __shared__ __attribute__((aligned(16))) float s_gz[BLK ? CP * XSG : 4];
+  __shared__ __attribute__((aligned(16))) float s_x[NX ? CP * XSG : 4];
+  __shared__ __attribute__((aligned(16))) float s_o[CP * XSG];
   __shared__ __attribute__((aligned(16))) unsigned char s_tl[CP * (kMaxKpad + 8) * (BF ? 2 : 4)];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, q = lane >> 4;
-  const int ct = wave % NT, tbase = (wave / NT) * TMW;
+  const int tbase = wave * G;
   const int64_t wg_per_b = a.lines / a.lpw;
   const int b = (int)(blockIdx.x / wg_per_b);
   const int64_t l0 = (int64_t)(blockIdx.x - (int64_t)b * wg_per_b) * a.lpw;
   const int gpl = 1 << a.gpl_log2;
   const int nf = a.lpw << a.gpl_log2;
-  // bypass B operand, K-step kb, lane (n = m, q): Wb[o = 4 kb + q][i = 16 ct + m]
-  float wbr[BLK ? C / 4 : 1];
+  // bypass B operand of channel tile ct, K-step kb, lane (n = m, q): Wb[o = 4 kb + q][i = 16 ct + m]
+  float wbr[BLK ? NT : 1][BLK ? C / 4 : 1];
   if (BLK) {
-    const int i = 16 * ct + m;
 #pragma unroll
-    for (int kb = 0; kb < C / 4; ++kb) wbr[kb] = 0.f;
-    if (i < C) {
+    for (int ct = 0; ct < NT; ++ct) {
+      const int i = 16 * ct + m;
 #pragma unroll
-      for (int kb = 0; kb < C / 4; ++kb) wbr[kb] = a.wb[(4 * kb + q) * C + i];
+      for (int kb = 0; kb < C / 4; ++kb) {
+        const float w = a.wb[(4 * kb + q) * C + min(i, C - 1)];
+        wbr[ct][kb] = i < C ? w : 0.f;
+      }
     }
   }
   const int mo = (NT == 4) ? wave : (NT == 2 ? (wave >> 1) : 0);
@@ -471,9 +480,18 @@ k_epi_bwd_line(EpiArgs a) {
 #pragma unroll
   for (int u = 0; u < DT; ++u) dwb[u] = zero4();
   float dbl = 0.f;
+  // float4 e = tid + 256 u of a tile: channel e / FPC, points 4 (e % FPC) .. + 3 (tails as in
+  // the forward: clamped copies, padding rows)
   const int64_t pbase = l0 * a.Nb;
-  const int64_t rowoff = ((int64_t)b * C + (tid >> 4)) * a.P + pbase + 4 * (tid & 15);
-  const int64_t ustride = 16 * a.P;
+  int64_t goff[NPT];
+  int xl[NPT], ol[NPT];
+#pragma unroll
+  for (int u = 0; u < NPT; ++u) {
+    const int e = tid + 256 * u, ec = min(e, NF4 - 1);
+    goff[u] = ((int64_t)b * C + ec / FPC) * a.P + pbase + 4 * (ec % FPC);
+    xl[u] = (e / FPC) * XSG + 4 * (e % FPC);
+    ol[u] = (ec / FPC) * XSG + 4 * (ec % FPC);
+  }
   float4 pg_y[NPT], pz[NPT], px[NPT];
 #pragma unroll
   for (int u = 0; u < NPT; ++u) {
@@ -481,86 +499,135 @@ k_epi_bwd_line(EpiArgs a) {
     pz[u] = pg_y[u];
     px[u] = pg_y[u];
   }
-  GtFrag<TMW, BF> gtf;
-  if (BLK) load_rows<16 * C, NPT>(pg_y, a.gy + rowoff, ustride, tid);
-  if (GL) load_rows<16 * C, NPT>(pz, a.zin + rowoff, ustride, tid);
-  if (NX) load_rows<16 * C, NPT>(px, a.x + rowoff, ustride, tid);
-  load_gt<TMW, BF, true>(a, 0, tbase, m, q, gtf);
+  GtFrag<G, BF> gtf;
+#pragma unroll
+  for (int u = 0; u < NPT; ++u) {
+    if (BLK) pg_y[u] = *reinterpret_cast<const float4*>(a.gy + goff[u]);
+    if (GL) pz[u] = *reinterpret_cast<const float4*>(a.zin + goff[u]);
+    if (NX) px[u] = *reinterpret_cast<const float4*>(a.x + goff[u]);
+  }
+  load_gt<G, BF, true, MT>(a, 0, tbase, m, q, gtf);
+  constexpr bool LPF = C < 64;
+  const float2* Tb = a.T + ((int64_t)b * C * a.lines + l0) * a.mb;
+  LineT<LPF ? C : 16> tln;
+  if constexpr (LPF) load_line<C>(a, Tb, tln, tid);
+  constexpr int kst = kMaxKpad + (BF ? 8 : 4);
   for (int lf = 0; lf < a.lpw; ++lf) {
     // every reader of the previous line's spectrum is past that line's last barrier
-    const float2* Trow0 = a.T + ((int64_t)b * C * a.lines + l0 + lf) * a.mb;
-    stage_line<C, BF>(a, Trow0, s_tl, tid);
+    if constexpr (LPF) {
+      write_line<C, BF>(a, tln, s_tl, tid);
+      load_line<C>(a, Tb + (int64_t)min(lf + 1, a.lpw - 1) * a.mb, tln, tid);
+    } else {
+      stage_line<C, BF>(a, Tb + (int64_t)lf * a.mb, s_tl, tid);
+    }
     for (int g = 0; g < gpl; ++g) {
       const int f = (lf << a.gpl_log2) + g;
       const int fn = min(f + 1, nf - 1);
 #pragma unroll
       for (int u = 0; u < NPT; ++u) {
-        const int e = tid + 256 * u;
-        if ((16 * C) % 256 == 0 || e < 16 * C) {
-          const int lo = (e >> 4) * XS + 4 * (e & 15);
-          if (BLK) {
-            float4 gz = pg_y[u];
-            if (GL) {
-              gz.x *= gelu_grad_as(pz[u].x);
-              gz.y *= gelu_grad_as(pz[u].y);
-              gz.z *= gelu_grad_as(pz[u].z);
-              gz.w *= gelu_grad_as(pz[u].w);
-            }
-            *reinterpret_cast<float4*>(s_gz + lo) = gz;
+        if (BLK) {
+          float4 gz = pg_y[u];
+          if (GL) {
+            gz.x *= gelu_grad_as(pz[u].x);
+            gz.y *= gelu_grad_as(pz[u].y);
+            gz.z *= gelu_grad_as(pz[u].z);
+            gz.w *= gelu_grad_as(pz[u].w);
           }
-          if (NX) *reinterpret_cast<float4*>(s_x + lo) = px[u];
+          *reinterpret_cast<float4*>(s_gz + xl[u]) = gz;
+        }
+        if (NX) *reinterpret_cast<float4*>(s_x + xl[u]) = px[u];
+      }
+#pragma unroll
+      for (int u = 0; u < NPT; ++u) {
+        if (BLK) pg_y[u] = *reinterpret_cast<const float4*>(a.gy + goff[u] + PI * fn);
+        if (GL) pz[u] = *reinterpret_cast<const float4*>(a.zin + goff[u] + PI * fn);
+        if (NX) px[u] = *reinterpret_cast<const float4*>(a.x + goff[u] + PI * fn);
+      }
+      __syncthreads();  // g_z / x tiles and spectrum rows visible; previous grad tile consumed
+      f32x4 acc[G][NT];
+#pragma unroll
+      for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) acc[j][ct] = zero4();
+      if constexpr (BF) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          if (32 * s2 >= a.kpad) break;
+#pragma unroll
+          for (int ct = 0; ct < NT; ++ct) {
+            const bf16x8 B = *reinterpret_cast<const bf16x8*>(
+                reinterpret_cast<const uint16_t*>(s_tl) + (16 * ct + m) * kst + 32 * s2 + 8 * q);
+#pragma unroll
+            for (int j = 0; j < G; ++j) acc[j][ct] = mfma_bf16(gtf.v[j][s2], B, acc[j][ct]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          if (16 * g4 >= a.kpad) break;
+#pragma unroll
+          for (int ct = 0; ct < NT; ++ct) {
+            const float4 B4 = *reinterpret_cast<const float4*>(
+                reinterpret_cast<const float*>(s_tl) + (16 * ct + m) * kst + 16 * g4 + 4 * q);
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+              acc[j][ct] = mfma_f32(gtf.v[j][g4].x, B4.x, acc[j][ct]);
+              acc[j][ct] = mfma_f32(gtf.v[j][g4].y, B4.y, acc[j][ct]);
+              acc[j][ct] = mfma_f32(gtf.v[j][g4].z, B4.z, acc[j][ct]);
+              acc[j][ct] = mfma_f32(gtf.v[j][g4].w, B4.w, acc[j][ct]);
+            }
+          }
         }
       }
-      if (BLK) load_rows<16 * C, NPT>(pg_y, a.gy + rowoff + 64 * fn, ustride, tid);
-      if (GL) load_rows<16 * C, NPT>(pz, a.zin + rowoff + 64 * fn, ustride, tid);
-      if (NX) load_rows<16 * C, NPT>(px, a.x + rowoff + 64 * fn, ustride, tid);
-      __syncthreads();  // g_z / x tiles and spectrum rows visible; previous grad tile consumed
-      f32x4 acc[TMW];
-#pragma unroll
-      for (int j = 0; j < TMW; ++j) acc[j] = zero4();
-      spectral_coop<C, TMW, BF>(a, s_tl, gtf, ct, m, q, acc);
-      load_gt<TMW, BF, true>(a, (fn & (gpl - 1)) * PG, tbase, m, q, gtf);
-      const int i = 16 * ct + m;
+      load_gt<G, BF, true, MT>(a, (fn & (gpl - 1)) * PI, tbase, m, q, gtf);
       if (TANH) {
-        // lane (n = m, q), tile tbase + j, register r: channel i, point 16 q + 4 r + tbase + j
+        // lane (n = m, q), tile tbase + j, register r: channel 16 ct + m, point
+        // MT (4 q + r) + tbase + j
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float xv[TMW];
-          load_lds_run<TMW>(xv, s_x + i * XS + 16 * q + 4 * r + tbase);
+        for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
-          for (int j = 0; j < TMW; ++j) {
-            const float t = tanh_fast(xv[j]);
-            acc[j][r] *= 1.f - t * t;
+          for (int r = 0; r < 4; ++r) {
+            float xv[G];
+            load_lds_run<G>(xv, s_x + (16 * ct + m) * XSG + MT * (4 * q + r) + tbase);
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+              const float t = tanh_fast(xv[j]);
+              acc[j][ct][r] *= 1.f - t * t;
+            }
           }
-        }
       }
       if (BLK) {
 #pragma unroll
         for (int kb = 0; kb < C / 4; ++kb) {
-          float av[TMW];
-          load_lds_run<TMW>(av, s_gz + (4 * kb + q) * XS + 4 * m + tbase);
+          float av[G];
+          load_lds_run<G>(av, s_gz + (4 * kb + q) * XSG + MT * m + tbase);
 #pragma unroll
-          for (int j = 0; j < TMW; ++j) acc[j] = mfma_f32(av[j], wbr[kb], acc[j]);
+          for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+            for (int j = 0; j < G; ++j) acc[j][ct] = mfma_f32(av[j], wbr[ct][kb], acc[j][ct]);
         }
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v[TMW];
+      for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
-        for (int j = 0; j < TMW; ++j) v[j] = acc[j][r];
-        store_lds_run<TMW>(s_o + i * XS + 16 * q + 4 * r + tbase, v);
-      }
+        for (int r = 0; r < 4; ++r) {
+          float v[G];
+#pragma unroll
+          for (int j = 0; j < G; ++j) v[j] = acc[j][ct][r];
+          store_lds_run<G>(s_o + (16 * ct + m) * XSG + MT * (4 * q + r) + tbase, v);
+        }
       if (BLK) {
         // dWb[o][i] += sum_points g_z[o][p] x[i][p]; k-slot q of MFMA jj <-> point 16 h + 4 q + jj
-        const int h_lo = (NT == 1) ? wave : 0;
-        const int h_hi = (NT == 1) ? wave + 1 : PG / 16;
+        constexpr int NH = PI / 16;  // 16-point chunks of the step
+        const int h_lo = (NT == 1) ? wave * (NH / 4) : 0;
+        const int h_hi = (NT == 1) ? (wave + 1) * (NH / 4) : NH;
         for (int h = h_lo; h < h_hi; ++h) {
-          const float4 av = *reinterpret_cast<const float4*>(s_gz + (16 * mo + m) * XS + 16 * h + 4 * q);
+          const float4 av = *reinterpret_cast<const float4*>(s_gz + (16 * mo + m) * XSG + 16 * h + 4 * q);
           if (count_db) dbl += (av.x + av.y) + (av.z + av.w);
 #pragma unroll
           for (int u = 0; u < DT; ++u) {
             const int ni = (NT == 4) ? u : ni0;
-            const float4 bv = *reinterpret_cast<const float4*>(s_x + (16 * ni + m) * XS + 16 * h + 4 * q);
+            const float4 bv = *reinterpret_cast<const float4*>(s_x + (16 * ni + m) * XSG + 16 * h + 4 * q);
             dwb[u] = mfma_f32(av.x, bv.x, dwb[u]);
             dwb[u] = mfma_f32(av.y, bv.y, dwb[u]);
             dwb[u] = mfma_f32(av.z, bv.z, dwb[u]);
@@ -571,11 +638,8 @@ k_epi_bwd_line(EpiArgs a) {
       __syncthreads();  // grad tile complete; g_z / x tiles free
 #pragma unroll
       for (int u = 0; u < NPT; ++u) {
-        const int e = tid + 256 * u;
-        if ((16 * C) % 256 == 0 || e < 16 * C) {
-          const float4 v = *reinterpret_cast<const float4*>(s_o + (e >> 4) * XS + 4 * (e & 15));
-          *reinterpret_cast<float4*>(a.y + rowoff + u * ustride + 64 * f) = v;
-        }
+        const float4 v = *reinterpret_cast<const float4*>(s_o + ol[u]);
+        *reinterpret_cast<float4*>(a.y + goff[u] + PI * f) = v;
       }
     }
   }
@@ -635,11 +699,11 @@ static hipError_t launch_fwd_c(const EpiArgs& a, bool bf, int mode, int wgs, hip
   return hipGetLastError();
 }
 
-template <int C>
+template <int C, int G>
 static hipError_t launch_bwd_c(const EpiArgs& a, bool bf, bool tanh_pre, int mode, int wgs,
                                hipStream_t s) {
 #define FNO_EPI_BWD(BFV, TV, MV) \
-  hipLaunchKernelGGL((k_epi_bwd_line<C, BFV, TV, MV>), dim3(wgs), dim3(256), 0, s, a)
+  hipLaunchKernelGGL((k_epi_bwd_line<C, BFV, TV, MV, G>), dim3(wgs), dim3(256), 0, s, a)
 #define FNO_EPI_BWD_M(BFV, TV)    \
   do {                            \
     if (mode == 1)                \
@@ -757,6 +821,8 @@ hipError_t launch_epilogue_bwd_fast(const fno_plan* p, int mode, const float2* T
   a.kpad = p->kpad;
   a.lines = g.P / g.Nb;
   a.lpw = bwd_lines_per_wg(a.lines, g.B);
+  // one 64-point group per step: with three input tiles in flight, larger steps cost more in
+  // occupancy than they save in barriers (measured on the 128^3 width-20 backward)
   int gl = 0;
   while ((PG << gl) < g.Nb) ++gl;
   a.gpl_log2 = gl;
@@ -775,10 +841,10 @@ hipError_t launch_epilogue_bwd_fast(const fno_plan* p, int mode, const float2* T
   const int64_t wgs = (int64_t)g.B * a.lines / a.lpw;
   if (wgs > 0x7fffffff) return hipErrorInvalidValue;
   switch (g.Cin) {
-    case 16: return launch_bwd_c<16>(a, g.bf16, tanh_pre, kmode, (int)wgs, s);
-    case 20: return launch_bwd_c<20>(a, g.bf16, tanh_pre, kmode, (int)wgs, s);
-    case 32: return launch_bwd_c<32>(a, g.bf16, tanh_pre, kmode, (int)wgs, s);
-    default: return launch_bwd_c<64>(a, g.bf16, tanh_pre, kmode, (int)wgs, s);
+    case 16: return launch_bwd_c<16, 1>(a, g.bf16, tanh_pre, kmode, (int)wgs, s);
+    case 20: return launch_bwd_c<20, 1>(a, g.bf16, tanh_pre, kmode, (int)wgs, s);
+    case 32: return launch_bwd_c<32, 1>(a, g.bf16, tanh_pre, kmode, (int)wgs, s);
+    default: return launch_bwd_c<64, 1>(a, g.bf16, tanh_pre, kmode, (int)wgs, s);
   }
 }
 
