@@ -70,6 +70,8 @@ __device__ __forceinline__ void copy16_to_lds(const float* src, float* lds_wave_
 }
 
 constexpr int kWaitVm0 = 0x0F70;   // s_waitcnt vmcnt(0)
+// s_waitcnt vmcnt(n) for n < 16 (expcnt and lgkmcnt left free)
+constexpr int wait_vm(int n) { return 0x0F70 | (n & 15); }
 
 __device__ __forceinline__ uint32_t lds_addr(const float* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float*)p;
@@ -257,9 +259,18 @@ k_epi_rows(RowsEpiArgs a) {
   load_rowtab(0);
   const int64_t ybase = (int64_t)b * a.Cout * chs + (int64_t)o * plane;
 
+  // global stores per thread in a chunk's store pass; vector-memory operations retire in issue
+  // order, so waiting until at most that many are outstanding leaves the previous chunk's
+  // stores in flight while guaranteeing this chunk's x copy and row table
+  constexpr int kStores = (MODE == 2 ? 2 : 1) * kErXPT;
+  static_assert(kStores < 16, "vmcnt field");
+  // fp32: set-up loads done before the loop, so that the loop's own waits are those of its
+  // steady state (the compiler merges the first iteration's state with the later ones); the
+  // bf16 variants spill registers with it and keep the merged waits
+  if constexpr (!BF) __builtin_amdgcn_s_waitcnt(kWaitVm0);
   for (int c = 0; c < nchunk; ++c) {
     // x chunk c in s_x, the row table of chunk c in registers; s_y free (previous stores read)
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __builtin_amdgcn_s_waitcnt(wait_vm(kStores));
     __syncthreads();
     if constexpr (BLK) {
       // bypass: D[co][point] = sum_ci Wb[co][ci] x[ci][point] + bias[co]
@@ -283,8 +294,10 @@ k_epi_rows(RowsEpiArgs a) {
         }
       }
       __syncthreads();
-      // s_x has been read: the next chunk's x streams in during the spectral part
-      if (c + 1 < nchunk) load_x(c + 1);
+      // s_x has been read: the next chunk's x streams in during the spectral part (the last
+      // chunk copies itself again, unread: a branch here would make the compiler drain every
+      // load before the spectral products)
+      load_x(min(c + 1, nchunk - 1));
     }
     // spectral part, one output channel at a time
 #pragma unroll
