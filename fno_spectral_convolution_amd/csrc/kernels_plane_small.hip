@@ -13,11 +13,12 @@
 //                   lane loads its own A operand, two float4 of its row, straight from HBM.
 //   second product: 16x16x4 f32 MFMAs whose K order is chosen so that K-step s, k-slot q is
 //                   row 16 (s / 4) + 4 q + s % 4: exactly the first product's D fragment held
-//                   by the same lane, so R never leaves the registers.  F2 sits in LDS.
+//                   by the same lane, so R never leaves the registers.  F2 sits in LDS.  On the
+//                   mixed path: 16x16x32 bf16 MFMAs taking two row tiles' fragments per K-step,
+//                   F2 as its bf16 hi + lo pair (two products).
 //   combine       : X2 goes to a per-wave LDS tile and is folded into the complex spectrum.
 // On the mixed path the pre-activated input, T1 and R are rounded to bfloat16 (the
-// half-precision transform of the mixed-precision neural-operator page, "Tiivistelmä"); F2
-// stays float32, which is at least as precise as the hi + lo bfloat16 pair used elsewhere.
+// half-precision transform of the mixed-precision neural-operator page, "Tiivistelmä").
 #include "fno_internal.h"
 #include "mfma.h"
 #include "pointwise.h"
@@ -32,6 +33,8 @@ struct SmallPlaneArgs {
   const float* t1;       // [Nb][jpad] f32
   const uint16_t* t1bf;  // [Nb][jpad] bf16 bits
   const float* f2;       // [4 ma][Na] f32
+  const uint16_t* f2bf;  // [4 ma][Na] bf16 bits of f2, and of its residual
+  const uint16_t* f2lo;
   float2* out;           // [planes][2 ma][mb]
 };
 
@@ -53,16 +56,26 @@ __global__ void __launch_bounds__(256) k_plane_small(SmallPlaneArgs a) {
   constexpr bool TWO = PIN == PLANE_GELU_GRAD;
   extern __shared__ __attribute__((aligned(16))) float s_sp[];
   const int Na = 16 * MT;
-  const int F2S = Na + 4;                    // F2 row stride (floats)
+  const int F2S = Na + 4;                    // F2 row stride (floats; f32 path)
+  const int F2H = Na + 8;                    // F2 row stride (bf16 elements; bf16 path)
   const int ROWS2 = 4 * a.ma;                // F2 rows
   const int MT2 = ROWS2 / 16;                // F2 row tiles (ma % 4 == 0)
-  float* s_f2 = s_sp;                        // [4 ma][F2S]
+  // F2 in LDS: f32 [4 ma][F2S], or the bf16 pair hi [4 ma][F2H], lo [4 ma][F2H]
+  float* s_f2 = s_sp;
+  uint16_t* s_f2h = reinterpret_cast<uint16_t*>(s_sp);
+  uint16_t* s_f2l = s_f2h + ROWS2 * F2H;
+  const int f2_floats = BF ? ROWS2 * F2H : ROWS2 * F2S;  // the same bytes either way
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, q = lane >> 4;
-  float* s_w = s_f2 + ROWS2 * F2S + wave * (ROWS2 * JP);  // this wave's X2 tile [4 ma][JP]
+  float* s_w = s_sp + f2_floats + wave * (ROWS2 * JP);  // this wave's X2 tile [4 ma][JP]
   for (int e = tid; e < ROWS2 * Na; e += 256) {
     const int i = e / Na, r = e - i * Na;
-    s_f2[i * F2S + r] = a.f2[e];
+    if (BF) {
+      s_f2h[i * F2H + r] = a.f2bf[e];
+      s_f2l[i * F2H + r] = a.f2lo[e];
+    } else {
+      s_f2[i * F2S + r] = a.f2[e];
+    }
   }
   // T1 fragments: B[k = 8 q + slot][n = 16 nt + m]; zero past Nb
   float t1r[NTJ][8];
@@ -141,21 +154,52 @@ __global__ void __launch_bounds__(256) k_plane_small(SmallPlaneArgs a) {
     // the next plane's rows go out now, in flight during the second product and the combine
     const int64_t nxt = min(it + nw, a.planes - 1);
     load_plane(nxt);
-    // second product: K-step 4 t + r, k-slot q <-> row 16 t + 4 q + r
     for (int mt2 = 0; mt2 < MT2; ++mt2) {
       f32x4 x2[NTJ];
 #pragma unroll
       for (int nt = 0; nt < NTJ; ++nt) x2[nt] = zero4();
-      const float* fr = s_f2 + (16 * mt2 + m) * F2S + 4 * q;
+      if constexpr (!BF) {
+        // second product: K-step 4 t + r, k-slot q <-> row 16 t + 4 q + r
+        const float* fr = s_f2 + (16 * mt2 + m) * F2S + 4 * q;
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const float4 f = *reinterpret_cast<const float4*>(fr + 16 * t);
+        for (int t = 0; t < MT; ++t) {
+          const float4 f = *reinterpret_cast<const float4*>(fr + 16 * t);
 #pragma unroll
-        for (int nt = 0; nt < NTJ; ++nt) {
-          x2[nt] = mfma_f32(f.x, d[t][nt][0], x2[nt]);
-          x2[nt] = mfma_f32(f.y, d[t][nt][1], x2[nt]);
-          x2[nt] = mfma_f32(f.z, d[t][nt][2], x2[nt]);
-          x2[nt] = mfma_f32(f.w, d[t][nt][3], x2[nt]);
+          for (int nt = 0; nt < NTJ; ++nt) {
+            x2[nt] = mfma_f32(f.x, d[t][nt][0], x2[nt]);
+            x2[nt] = mfma_f32(f.y, d[t][nt][1], x2[nt]);
+            x2[nt] = mfma_f32(f.z, d[t][nt][2], x2[nt]);
+            x2[nt] = mfma_f32(f.w, d[t][nt][3], x2[nt]);
+          }
+        }
+      } else {
+        // second product on bf16 MFMAs (R is already rounded to bf16; F2 as its hi + lo
+        // pair): K-step p, slot (q, e) <-> row 16 (2 p + e / 4) + 4 q + e % 4, so the B
+        // operand is this lane's fragments of row tiles 2 p and 2 p + 1
+        const uint16_t* fh = s_f2h + (16 * mt2 + m) * F2H + 4 * q;
+        const uint16_t* fl = s_f2l + (16 * mt2 + m) * F2H + 4 * q;
+#pragma unroll
+        for (int pp = 0; pp < (MT + 1) / 2; ++pp) {
+          const int t0 = 2 * pp, t1 = min(2 * pp + 1, MT - 1);
+          const uint2 h0 = *reinterpret_cast<const uint2*>(fh + 32 * pp);
+          const uint2 l0 = *reinterpret_cast<const uint2*>(fl + 32 * pp);
+          uint2 h1 = make_uint2(0u, 0u), l1 = make_uint2(0u, 0u);
+          if (2 * pp + 1 < MT) {  // compile-time after unrolling
+            h1 = *reinterpret_cast<const uint2*>(fh + 32 * pp + 16);
+            l1 = *reinterpret_cast<const uint2*>(fl + 32 * pp + 16);
+          }
+          const bf16x8 ah = __builtin_bit_cast(bf16x8, make_uint4(h0.x, h0.y, h1.x, h1.y));
+          const bf16x8 al = __builtin_bit_cast(bf16x8, make_uint4(l0.x, l0.y, l1.x, l1.y));
+#pragma unroll
+          for (int nt = 0; nt < NTJ; ++nt) {
+            const uint32_t b0 = pack_bf16x2(d[t0][nt][0], d[t0][nt][1]);
+            const uint32_t b1 = pack_bf16x2(d[t0][nt][2], d[t0][nt][3]);
+            const uint32_t b2 = 2 * pp + 1 < MT ? pack_bf16x2(d[t1][nt][0], d[t1][nt][1]) : 0u;
+            const uint32_t b3 = 2 * pp + 1 < MT ? pack_bf16x2(d[t1][nt][2], d[t1][nt][3]) : 0u;
+            const bf16x8 bv = __builtin_bit_cast(bf16x8, make_uint4(b0, b1, b2, b3));
+            x2[nt] = mfma_bf16(ah, bv, x2[nt]);
+            x2[nt] = mfma_bf16(al, bv, x2[nt]);
+          }
         }
       }
 #pragma unroll
@@ -192,7 +236,7 @@ bool plane_small_ok(const fno_plan* p) {
 template <int PIN, bool BF, int MT>
 static void launch_small_t(const fno_plan* p, const SmallPlaneArgs& a, hipStream_t s) {
   const int jp = p->jpad;
-  const size_t lds = sizeof(float) * (4 * a.ma * (a.Na + 4) + 4 * (4 * a.ma) * jp);
+  const size_t lds = sizeof(float) * (4 * a.ma * (a.Na + (BF ? 8 : 4)) + 4 * (4 * a.ma) * jp);
   const int64_t want = (a.planes + 3) / 4;
   const unsigned grid = (unsigned)(want < 2048 ? want : 2048);
   if (lds > 65536) {  // wide row spectra need more than the default dynamic LDS limit
@@ -239,6 +283,8 @@ hipError_t launch_plane_small(const fno_plan* p, int plane_in, int chans, const 
   a.t1 = p->t.t1;
   a.t1bf = p->t.t1_bf;
   a.f2 = p->t.f2;
+  a.f2bf = p->t.f2_bf;
+  a.f2lo = p->t.f2_bf_lo;
   a.out = out;
   switch (plane_in) {
     case PLANE_X: launch_small_pin<PLANE_X>(p, a, s); break;
