@@ -115,6 +115,149 @@ __global__ void __launch_bounds__(256) k_outer_mfma(OuterArgs a) {
   }
 }
 
+// Forward transform of an outer axis when few rows are kept (Lout <= 64): the product
+// out[o][c] = sum_k Mr[o][k] X[k][c] + Mi[o][k] Xs[k][c] has a short M and a long K, so a
+// work-group owns a block of CB = 64 NTW columns of one slab and streams the slab's rows through
+// LDS in 16-row chunks (float4 rows, prefetched one chunk ahead in registers) while every output
+// tile stays in registers: wave w owns N-tiles w NTW .. w NTW + NTW - 1 for all MT row tiles.
+// K-step ks, k-slot q is row k0 + 4 q + ks, so a lane's table operands for a chunk are one float4
+// per table half and row tile.  Xs needs no copy: it is X at the partner column c ^ 1, negated
+// for even c (a lane constant).  fp32 operands.
+template <int MT, int NTW>
+__global__ void __launch_bounds__(256) k_outer_fwd_stream(OuterArgs a) {
+  constexpr int CB = 64 * NTW;   // columns per work-group
+  constexpr int CBS = CB + 4;    // LDS row stride: the four k-slot groups on distinct banks
+  constexpr int F4R = CB / 4;    // float4 per chunk row
+  __shared__ __attribute__((aligned(16))) float s_x[16 * CBS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, q = lane >> 4;
+  const int64_t pre = blockIdx.y;
+  const int c0 = blockIdx.x * CB;
+  const float* src = a.in + pre * a.Lin * a.post2;
+  float* dst = a.out + pre * a.Lout * a.post2;
+  const int K2 = 2 * a.Lin_pad;  // table row stride
+  const float* A = static_cast<const float*>(a.A);
+  // chunk element i of this thread: float4 e = tid + 256 i -> row e / F4R, columns 4 (e % F4R)
+  int xrow[NTW], xcol[NTW];
+  bool xcol_ok[NTW];
+#pragma unroll
+  for (int i = 0; i < NTW; ++i) {
+    const int e = tid + 256 * i;
+    xrow[i] = e / F4R;
+    const int col = c0 + 4 * (e % F4R);
+    xcol_ok[i] = col < a.post2;
+    xcol[i] = min(col, a.post2 - 4);
+  }
+  auto load_chunk = [&](int k0, float4 (&v)[NTW]) {
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) {
+      const int row = k0 + xrow[i];
+      const float4 t = *reinterpret_cast<const float4*>(src + (int64_t)min(row, a.Lin - 1) * a.post2 + xcol[i]);
+      const bool ok = row < a.Lin && xcol_ok[i];
+      v[i] = ok ? t : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto load_tab = [&](int k0, float4 (&r)[MT], float4 (&im)[MT]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const float* row = A + (int64_t)(16 * mt + m) * K2 + k0 + 4 * q;
+      r[mt] = *reinterpret_cast<const float4*>(row);
+      im[mt] = *reinterpret_cast<const float4*>(row + a.Lin_pad);
+    }
+  };
+  f32x4 acc[MT][NTW];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) acc[mt][j] = zero4();
+  float4 xv[NTW], tr[MT], ti[MT];
+  load_chunk(0, xv);
+  load_tab(0, tr, ti);
+  const float sgn = (m & 1) ? 1.f : -1.f;  // Xs[k][c] = sgn * X[k][c ^ 1]
+  const int nchunk = a.Lin_pad / 16;
+  for (int ch = 0; ch < nchunk; ++ch) {
+#pragma unroll
+    for (int i = 0; i < NTW; ++i)
+      *reinterpret_cast<float4*>(s_x + xrow[i] * CBS + 4 * ((tid + 256 * i) % F4R)) = xv[i];
+    float4 cr[MT], ci[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      cr[mt] = tr[mt];
+      ci[mt] = ti[mt];
+    }
+    // the next chunk (the last one loads itself again: no branch around the loads)
+    const int kn = 16 * min(ch + 1, nchunk - 1);
+    load_chunk(kn, xv);
+    load_tab(kn, tr, ti);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const float* xr = s_x + (4 * q + ks) * CBS + 16 * wave * NTW + m;
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        const float bx = xr[16 * j];
+        const float bs = sgn * xr[16 * j + ((m & 1) ? -1 : 1)];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const float ar = ks == 0 ? cr[mt].x : ks == 1 ? cr[mt].y : ks == 2 ? cr[mt].z : cr[mt].w;
+          const float ai = ks == 0 ? ci[mt].x : ks == 1 ? ci[mt].y : ks == 2 ? ci[mt].z : ci[mt].w;
+          acc[mt][j] = mfma_f32(ar, bx, acc[mt][j]);
+          acc[mt][j] = mfma_f32(ai, bs, acc[mt][j]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // lane (n = m, q), register r: output row 16 mt + 4 q + r, column c0 + 16 (w NTW + j) + m
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int o = 16 * mt + 4 * q + r;
+      if (o >= a.Lout) continue;
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        const int col = c0 + 16 * (wave * NTW + j) + m;
+        if (col < a.post2) dst[(int64_t)o * a.post2 + col] = acc[mt][j][r];
+      }
+    }
+}
+
+template <int MT, int NTW>
+static hipError_t launch_stream_t(dim3 grid, const OuterArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((k_outer_fwd_stream<MT, NTW>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int MT>
+static hipError_t launch_stream_mt(int ntw, dim3 grid, const OuterArgs& a, hipStream_t s) {
+  switch (ntw) {
+    case 1: return launch_stream_t<MT, 1>(grid, a, s);
+    case 2: return launch_stream_t<MT, 2>(grid, a, s);
+    case 3: return launch_stream_t<MT, 3>(grid, a, s);
+    case 4: return launch_stream_t<MT, 4>(grid, a, s);
+  }
+  if constexpr (MT <= 2) {
+    switch (ntw) {
+      case 5: return launch_stream_t<MT, 5>(grid, a, s);
+      case 6: return launch_stream_t<MT, 6>(grid, a, s);
+      case 7: return launch_stream_t<MT, 7>(grid, a, s);
+      case 8: return launch_stream_t<MT, 8>(grid, a, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+static hipError_t launch_outer_stream(int mt, int ntw, dim3 grid, const OuterArgs& a,
+                                      hipStream_t s) {
+  switch (mt) {
+    case 1: return launch_stream_mt<1>(ntw, grid, a, s);
+    case 2: return launch_stream_mt<2>(ntw, grid, a, s);
+    case 3: return launch_stream_mt<3>(ntw, grid, a, s);
+    default: return launch_stream_mt<4>(ntw, grid, a, s);
+  }
+}
+
 static int pad16(int v) { return (v + 15) / 16 * 16; }
 
 // pre/post of the transform of axis j (see the generic kernel) and the launch
@@ -141,6 +284,18 @@ hipError_t launch_outer_mfma(const fno_plan* p, int axis, int chans, bool inv, c
   } else {
     a.A = bf ? (const void*)p->t.ofwd_bf[axis] : (const void*)p->t.ofwd[axis];
     a.Alo = p->t.ofwd_bf_lo[axis];
+  }
+  if (!inv && !bf && a.Lout_pad <= 64 && a.post2 % 4 == 0 && pre <= 65535) {
+    // few kept rows, long K: stream the slab in column blocks of 64 NTW (as wide as the row
+    // needs, narrower while that leaves fewer than ~1024 work-groups)
+    const int mt = a.Lout_pad / 16;
+    const int ntw_max = mt > 2 ? 4 : 8;
+    int ntw = (int)((a.post2 + 63) / 64);
+    if (ntw > ntw_max) ntw = ntw_max;
+    while (ntw > 1 && pre * ((a.post2 + 64 * ntw - 1) / (64 * ntw)) < 1024) --ntw;
+    const int cb = 64 * ntw;
+    dim3 grid((unsigned)((a.post2 + cb - 1) / cb), (unsigned)pre);
+    return launch_outer_stream(mt, ntw, grid, a, s);
   }
   const int KS = 2 * a.Lin_pad + (bf ? 8 : 4);
   const size_t col_bytes = (size_t)KS * (bf ? 2 : 4);
