@@ -223,38 +223,162 @@ __global__ void __launch_bounds__(256) k_outer_fwd_stream(OuterArgs a) {
     }
 }
 
+// The same streaming transform on the mixed path: 32-row chunks, one 16x16x32 bf16 MFMA K-step
+// per chunk and term, the table as its bf16 hi + lo pair (two products per term).  K-slot (q, e)
+// is row k0 + 8 q + e; a lane reads the column pair (c & ~1) of each of its 8 rows as one float2,
+// which gives both X[k][c] and the partner for Xs, rounded to bf16 as operands.
 template <int MT, int NTW>
-static hipError_t launch_stream_t(dim3 grid, const OuterArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((k_outer_fwd_stream<MT, NTW>), grid, dim3(256), 0, s, a);
+__global__ void __launch_bounds__(256) k_outer_fwd_stream_bf(OuterArgs a) {
+  constexpr int CB = 64 * NTW;
+  constexpr int CBS = CB + 4;
+  constexpr int F4R = CB / 4;
+  constexpr int NL = 2 * NTW;  // float4 of a 32-row chunk per thread
+  __shared__ __attribute__((aligned(16))) float s_x[32 * CBS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, q = lane >> 4;
+  const int64_t pre = blockIdx.y;
+  const int c0 = blockIdx.x * CB;
+  const float* src = a.in + pre * a.Lin * a.post2;
+  float* dst = a.out + pre * a.Lout * a.post2;
+  const int K2 = 2 * a.Lin_pad;
+  const uint16_t* Ah = static_cast<const uint16_t*>(a.A);
+  const uint16_t* Al = a.Alo;
+  int xrow[NL], xcol[NL];
+  bool xcol_ok[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int e = tid + 256 * i;
+    xrow[i] = e / F4R;
+    const int col = c0 + 4 * (e % F4R);
+    xcol_ok[i] = col < a.post2;
+    xcol[i] = min(col, a.post2 - 4);
+  }
+  auto load_chunk = [&](int k0, float4 (&v)[NL]) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int row = k0 + xrow[i];
+      const float4 t = *reinterpret_cast<const float4*>(src + (int64_t)min(row, a.Lin - 1) * a.post2 + xcol[i]);
+      const bool ok = row < a.Lin && xcol_ok[i];
+      v[i] = ok ? t : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  // table fragments of a K-step: [row tile][Mr hi, Mr lo, Mi hi, Mi lo], columns k0 + 8 q ..
+  auto load_tab = [&](int k0, bf16x8 (&t)[MT][4]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int64_t row = (int64_t)(16 * mt + m) * K2 + min(k0 + 8 * q, a.Lin_pad - 8);
+      t[mt][0] = *reinterpret_cast<const bf16x8*>(Ah + row);
+      t[mt][1] = *reinterpret_cast<const bf16x8*>(Al + row);
+      t[mt][2] = *reinterpret_cast<const bf16x8*>(Ah + row + a.Lin_pad);
+      t[mt][3] = *reinterpret_cast<const bf16x8*>(Al + row + a.Lin_pad);
+    }
+  };
+  f32x4 acc[MT][NTW];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) acc[mt][j] = zero4();
+  float4 xv[NL];
+  bf16x8 tb[MT][4];
+  load_chunk(0, xv);
+  load_tab(0, tb);
+  const bool odd = (m & 1) != 0;
+  const int nchunk = (a.Lin_pad + 31) / 32;
+  for (int ch = 0; ch < nchunk; ++ch) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+      *reinterpret_cast<float4*>(s_x + xrow[i] * CBS + 4 * ((tid + 256 * i) % F4R)) = xv[i];
+    bf16x8 ct[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) ct[mt][h] = tb[mt][h];
+    // rows past Lin in a chunk are loaded as zeros, so the (clamped) table operands of K-slots
+    // past Lin_pad multiply zeros
+    const int kn = 32 * min(ch + 1, nchunk - 1);
+    load_chunk(kn, xv);
+    load_tab(kn, tb);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      const float* xr = s_x + 8 * q * CBS + 16 * (wave * NTW + j) + (m & ~1);
+      float xe[8], xs[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float2 pr = *reinterpret_cast<const float2*>(xr + e * CBS);
+        xe[e] = odd ? pr.y : pr.x;
+        xs[e] = odd ? pr.x : -pr.y;
+      }
+      const bf16x8 bx = __builtin_bit_cast(
+          bf16x8, make_uint4(pack_bf16x2(xe[0], xe[1]), pack_bf16x2(xe[2], xe[3]),
+                             pack_bf16x2(xe[4], xe[5]), pack_bf16x2(xe[6], xe[7])));
+      const bf16x8 bs = __builtin_bit_cast(
+          bf16x8, make_uint4(pack_bf16x2(xs[0], xs[1]), pack_bf16x2(xs[2], xs[3]),
+                             pack_bf16x2(xs[4], xs[5]), pack_bf16x2(xs[6], xs[7])));
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        acc[mt][j] = mfma_bf16(ct[mt][0], bx, acc[mt][j]);
+        acc[mt][j] = mfma_bf16(ct[mt][1], bx, acc[mt][j]);
+        acc[mt][j] = mfma_bf16(ct[mt][2], bs, acc[mt][j]);
+        acc[mt][j] = mfma_bf16(ct[mt][3], bs, acc[mt][j]);
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int o = 16 * mt + 4 * q + r;
+      if (o >= a.Lout) continue;
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        const int col = c0 + 16 * (wave * NTW + j) + m;
+        if (col < a.post2) dst[(int64_t)o * a.post2 + col] = acc[mt][j][r];
+      }
+    }
+}
+
+template <int MT, int NTW>
+static hipError_t launch_stream_t(dim3 grid, const OuterArgs& a, bool bf, hipStream_t s) {
+  if (bf) {
+    if constexpr (NTW <= 6)
+      hipLaunchKernelGGL((k_outer_fwd_stream_bf<MT, NTW>), grid, dim3(256), 0, s, a);
+    else
+      return hipErrorInvalidValue;
+  } else {
+    hipLaunchKernelGGL((k_outer_fwd_stream<MT, NTW>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
 template <int MT>
-static hipError_t launch_stream_mt(int ntw, dim3 grid, const OuterArgs& a, hipStream_t s) {
+static hipError_t launch_stream_mt(int ntw, dim3 grid, const OuterArgs& a, bool bf,
+                                   hipStream_t s) {
   switch (ntw) {
-    case 1: return launch_stream_t<MT, 1>(grid, a, s);
-    case 2: return launch_stream_t<MT, 2>(grid, a, s);
-    case 3: return launch_stream_t<MT, 3>(grid, a, s);
-    case 4: return launch_stream_t<MT, 4>(grid, a, s);
+    case 1: return launch_stream_t<MT, 1>(grid, a, bf, s);
+    case 2: return launch_stream_t<MT, 2>(grid, a, bf, s);
+    case 3: return launch_stream_t<MT, 3>(grid, a, bf, s);
+    case 4: return launch_stream_t<MT, 4>(grid, a, bf, s);
   }
   if constexpr (MT <= 2) {
     switch (ntw) {
-      case 5: return launch_stream_t<MT, 5>(grid, a, s);
-      case 6: return launch_stream_t<MT, 6>(grid, a, s);
-      case 7: return launch_stream_t<MT, 7>(grid, a, s);
-      case 8: return launch_stream_t<MT, 8>(grid, a, s);
+      case 5: return launch_stream_t<MT, 5>(grid, a, bf, s);
+      case 6: return launch_stream_t<MT, 6>(grid, a, bf, s);
+      case 7: return launch_stream_t<MT, 7>(grid, a, bf, s);
+      case 8: return launch_stream_t<MT, 8>(grid, a, bf, s);
     }
   }
   return hipErrorInvalidValue;
 }
 
-static hipError_t launch_outer_stream(int mt, int ntw, dim3 grid, const OuterArgs& a,
+static hipError_t launch_outer_stream(int mt, int ntw, dim3 grid, const OuterArgs& a, bool bf,
                                       hipStream_t s) {
   switch (mt) {
-    case 1: return launch_stream_mt<1>(ntw, grid, a, s);
-    case 2: return launch_stream_mt<2>(ntw, grid, a, s);
-    case 3: return launch_stream_mt<3>(ntw, grid, a, s);
-    default: return launch_stream_mt<4>(ntw, grid, a, s);
+    case 1: return launch_stream_mt<1>(ntw, grid, a, bf, s);
+    case 2: return launch_stream_mt<2>(ntw, grid, a, bf, s);
+    case 3: return launch_stream_mt<3>(ntw, grid, a, bf, s);
+    default: return launch_stream_mt<4>(ntw, grid, a, bf, s);
   }
 }
 
@@ -285,17 +409,17 @@ hipError_t launch_outer_mfma(const fno_plan* p, int axis, int chans, bool inv, c
     a.A = bf ? (const void*)p->t.ofwd_bf[axis] : (const void*)p->t.ofwd[axis];
     a.Alo = p->t.ofwd_bf_lo[axis];
   }
-  if (!inv && !bf && a.Lout_pad <= 64 && a.post2 % 4 == 0 && pre <= 65535) {
+  if (!inv && a.Lout_pad <= 64 && a.post2 % 4 == 0 && pre <= 65535) {
     // few kept rows, long K: stream the slab in column blocks of 64 NTW (as wide as the row
     // needs, narrower while that leaves fewer than ~1024 work-groups)
     const int mt = a.Lout_pad / 16;
-    const int ntw_max = mt > 2 ? 4 : 8;
+    const int ntw_max = mt > 2 ? 4 : (bf ? 6 : 8);
     int ntw = (int)((a.post2 + 63) / 64);
     if (ntw > ntw_max) ntw = ntw_max;
     while (ntw > 1 && pre * ((a.post2 + 64 * ntw - 1) / (64 * ntw)) < 1024) --ntw;
     const int cb = 64 * ntw;
     dim3 grid((unsigned)((a.post2 + cb - 1) / cb), (unsigned)pre);
-    return launch_outer_stream(mt, ntw, grid, a, s);
+    return launch_outer_stream(mt, ntw, grid, a, bf, s);
   }
   const int KS = 2 * a.Lin_pad + (bf ? 8 : 4);
   const size_t col_bytes = (size_t)KS * (bf ? 2 : 4);
