@@ -339,6 +339,128 @@ __global__ void __launch_bounds__(256) k_outer_fwd_stream_bf(OuterArgs a) {
     }
 }
 
+// Inverse transform of an outer axis from few kept rows (Lin <= 64) to N rows: a short K and a
+// long M.  A work-group owns a block of CB = 64 NTW columns of one slab: the kept rows of the block
+// are staged once in LDS (row-major, float4 loads), then wave w walks all output row tiles for its
+// N-tiles w NTW .. w NTW + NTW - 1 and stores each finished tile.  Operands as in the streaming
+// forward transform (fp32 16x16x4 with K-slot q <-> row 4 q + ks of a 16-row group; bf16
+// 16x16x32 with K-slot (q, e) <-> row 8 q + e, the table as its hi + lo pair).
+template <bool BF, int NTW>
+__global__ void __launch_bounds__(256) k_outer_inv_stream(OuterArgs a) {
+  constexpr int CB = 64 * NTW;
+  constexpr int CBS = CB + 4;
+  constexpr int F4R = CB / 4;
+  extern __shared__ __attribute__((aligned(16))) float s_xi[];  // [Lin_pad][CBS]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, q = lane >> 4;
+  const int64_t pre = blockIdx.y;
+  const int c0 = blockIdx.x * CB;
+  const float* src = a.in + pre * a.Lin * a.post2;
+  float* dst = a.out + pre * a.Lout * a.post2;
+  const int K2 = 2 * a.Lin_pad;
+  // stage the kept rows (rows past Lin and columns past the slab as zeros)
+  for (int e = tid; e < a.Lin_pad * F4R; e += 256) {
+    const int row = e / F4R, col = c0 + 4 * (e - row * F4R);
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (row < a.Lin && col < a.post2)
+      v = *reinterpret_cast<const float4*>(src + (int64_t)row * a.post2 + col);
+    *reinterpret_cast<float4*>(s_xi + row * CBS + 4 * (e - row * F4R)) = v;
+  }
+  __syncthreads();
+  const bool odd = (m & 1) != 0;
+  const float sgn = odd ? 1.f : -1.f;  // Xs[k][c] = sgn * X[k][c ^ 1]
+  const int colw = 16 * wave * NTW + m;
+  for (int mt = 0; mt < a.Lout_pad / 16; ++mt) {
+    f32x4 acc[NTW];
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) acc[j] = zero4();
+    const int orow = 16 * mt + m;
+    if constexpr (!BF) {
+      const float* A = static_cast<const float*>(a.A) + (int64_t)orow * K2;
+      for (int g = 0; g < a.Lin_pad / 16; ++g) {
+        const float4 ar = *reinterpret_cast<const float4*>(A + 16 * g + 4 * q);
+        const float4 ai = *reinterpret_cast<const float4*>(A + a.Lin_pad + 16 * g + 4 * q);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const float* xr = s_xi + (16 * g + 4 * q + ks) * CBS + colw;
+          const float tr = ks == 0 ? ar.x : ks == 1 ? ar.y : ks == 2 ? ar.z : ar.w;
+          const float ti = ks == 0 ? ai.x : ks == 1 ? ai.y : ks == 2 ? ai.z : ai.w;
+#pragma unroll
+          for (int j = 0; j < NTW; ++j) {
+            const float bx = xr[16 * j];
+            const float bs = sgn * xr[16 * j + (odd ? -1 : 1)];
+            acc[j] = mfma_f32(tr, bx, acc[j]);
+            acc[j] = mfma_f32(ti, bs, acc[j]);
+          }
+        }
+      }
+    } else {
+      const uint16_t* Ah = static_cast<const uint16_t*>(a.A) + (int64_t)orow * K2;
+      const uint16_t* Al = a.Alo + (int64_t)orow * K2;
+      for (int k0 = 0; k0 < a.Lin_pad; k0 += 32) {
+        // K-slots past Lin_pad (a 16-row remainder) read zero rows of the staged block: the
+        // table columns are clamped into the row
+        const int tc = min(k0 + 8 * q, a.Lin_pad - 8);
+        const uint32_t km = k0 + 8 * q < a.Lin_pad ? 0xffffffffu : 0u;  // mask, not a branch
+        auto ld = [&](const uint16_t* p) {
+          uint4 v = *reinterpret_cast<const uint4*>(p);
+          v.x &= km; v.y &= km; v.z &= km; v.w &= km;
+          return __builtin_bit_cast(bf16x8, v);
+        };
+        const bf16x8 rh = ld(Ah + tc), rl = ld(Al + tc);
+        const bf16x8 ih = ld(Ah + a.Lin_pad + tc), il = ld(Al + a.Lin_pad + tc);
+        const int xr0 = min(k0 + 8 * q, a.Lin_pad - 8);
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+          const float* xr = s_xi + xr0 * CBS + 16 * (wave * NTW + j) + (m & ~1);
+          float xe[8], xs[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float2 pr = *reinterpret_cast<const float2*>(xr + e * CBS);
+            xe[e] = odd ? pr.y : pr.x;
+            xs[e] = odd ? pr.x : -pr.y;
+          }
+          const bf16x8 bx = __builtin_bit_cast(
+              bf16x8, make_uint4(pack_bf16x2(xe[0], xe[1]), pack_bf16x2(xe[2], xe[3]),
+                                 pack_bf16x2(xe[4], xe[5]), pack_bf16x2(xe[6], xe[7])));
+          const bf16x8 bs = __builtin_bit_cast(
+              bf16x8, make_uint4(pack_bf16x2(xs[0], xs[1]), pack_bf16x2(xs[2], xs[3]),
+                                 pack_bf16x2(xs[4], xs[5]), pack_bf16x2(xs[6], xs[7])));
+          acc[j] = mfma_bf16(rh, bx, acc[j]);
+          acc[j] = mfma_bf16(rl, bx, acc[j]);
+          acc[j] = mfma_bf16(ih, bs, acc[j]);
+          acc[j] = mfma_bf16(il, bs, acc[j]);
+        }
+      }
+    }
+    // lane (n = m, q), register r: output row 16 mt + 4 q + r, column c0 + 16 (w NTW + j) + m
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int o = 16 * mt + 4 * q + r;
+      if (o >= a.Lout) continue;
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        const int col = c0 + 16 * (wave * NTW + j) + m;
+        if (col < a.post2) dst[(int64_t)o * a.post2 + col] = acc[j][r];
+      }
+    }
+  }
+}
+
+template <bool BF>
+static hipError_t launch_inv_stream(int ntw, dim3 grid, size_t lds, const OuterArgs& a,
+                                    hipStream_t s) {
+  switch (ntw) {
+    case 1: hipLaunchKernelGGL((k_outer_inv_stream<BF, 1>), grid, dim3(256), lds, s, a); break;
+    case 2: hipLaunchKernelGGL((k_outer_inv_stream<BF, 2>), grid, dim3(256), lds, s, a); break;
+    case 3: hipLaunchKernelGGL((k_outer_inv_stream<BF, 3>), grid, dim3(256), lds, s, a); break;
+    case 4: hipLaunchKernelGGL((k_outer_inv_stream<BF, 4>), grid, dim3(256), lds, s, a); break;
+    case 5: hipLaunchKernelGGL((k_outer_inv_stream<BF, 5>), grid, dim3(256), lds, s, a); break;
+    default: hipLaunchKernelGGL((k_outer_inv_stream<BF, 6>), grid, dim3(256), lds, s, a); break;
+  }
+  return hipGetLastError();
+}
+
 template <int MT, int NTW>
 static hipError_t launch_stream_t(dim3 grid, const OuterArgs& a, bool bf, hipStream_t s) {
   if (bf) {
@@ -408,6 +530,21 @@ hipError_t launch_outer_mfma(const fno_plan* p, int axis, int chans, bool inv, c
   } else {
     a.A = bf ? (const void*)p->t.ofwd_bf[axis] : (const void*)p->t.ofwd[axis];
     a.Alo = p->t.ofwd_bf_lo[axis];
+  }
+  if (inv && a.Lin_pad <= 64 && a.post2 % 4 == 0 && a.post2 >= 256 && pre >= 1024 &&
+      pre <= 65535) {
+    // few kept rows in, N rows out, many wide slabs: stage the kept rows of a column block once
+    // and walk the output row tiles (blocks as wide as the row needs, up to 6 N-tiles per wave).
+    // Narrow or few slabs keep the generic kernel, whose waves split the output rows instead.
+    int ntw = (int)((a.post2 + 63) / 64);
+    if (ntw > 6) ntw = 6;
+    while (ntw > 1 && pre * ((a.post2 + 64 * ntw - 1) / (64 * ntw)) < 1024) --ntw;
+    while (ntw > 1 && sizeof(float) * (size_t)a.Lin_pad * (64 * ntw + 4) > 65536) --ntw;
+    const int cb = 64 * ntw;
+    const size_t lds = sizeof(float) * (size_t)a.Lin_pad * (cb + 4);
+    dim3 grid((unsigned)((a.post2 + cb - 1) / cb), (unsigned)pre);
+    return bf ? launch_inv_stream<true>(ntw, grid, lds, a, s)
+              : launch_inv_stream<false>(ntw, grid, lds, a, s);
   }
   if (!inv && a.Lout_pad <= 64 && a.post2 % 4 == 0 && pre <= 65535) {
     // few kept rows, long K: stream the slab in column blocks of 64 NTW (as wide as the row
