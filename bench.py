@@ -36,6 +36,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="train2d_512")
+    ap.add_argument("--spectral-precision", choices=["f32", "bf16", "f16"], default=None,
+                    help="run the workload's plan at this spectral precision, tanh kept as the "
+                         "workload has it (e.g. f32: a mixed run after a precision-schedule "
+                         "switch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-batch", type=int, default=3)
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -108,7 +112,7 @@ def kernel_model(wl, plan):
     return model
 
 
-def bench_gpu(wl, steps, warmup):
+def bench_gpu(wl, steps, warmup, precision=None):
     import torch
 
     from fno_spectral_convolution_amd import binding as L
@@ -117,6 +121,8 @@ def bench_gpu(wl, steps, warmup):
     torch.cuda.set_device(0)
     t0 = time.perf_counter()
     runner = StackRunner(wl, device="cuda:0")
+    if precision is not None:
+        runner.set_precision(precision)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t0
     print(f"[bench] {wl.name}: inputs on device in {setup_s:.1f}s; warmup {warmup}", flush=True)
@@ -204,9 +210,9 @@ def cpu_baseline(wl, sample_batch, min_seconds=10.0, max_reps=12):
     # repeat the sample until about min_seconds of host work (bounded by max_reps)
     while True:
         if wl.train:
-            O.block_bwd(x, blk["w"], blk["wb"], blk["bias"], wl.modes, gy, tanh=wl.mixed)
+            O.block_bwd(x, blk["w"], blk["wb"], blk["bias"], wl.modes, gy, tanh=bool(wl.mixed))
         else:
-            O.block_fwd(x, blk["w"], blk["wb"], blk["bias"], wl.modes, tanh=wl.mixed)
+            O.block_fwd(x, blk["w"], blk["wb"], blk["bias"], wl.modes, tanh=bool(wl.mixed))
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds or reps >= max_reps:
@@ -230,16 +236,19 @@ def main():
         sys.exit(2)
     from fno_spectral_convolution_amd import configs
     wl = configs.get(args.workload)
-    runner, wall, kern = bench_gpu(wl, args.steps, args.warmup)
+    runner, wall, kern = bench_gpu(wl, args.steps, args.warmup, args.spectral_precision)
+    dtype = runner.precision
+    switched = dtype != configs.precision(wl)
     ms = wall / args.steps * 1e3
     value = wl.units / (wall / args.steps)
     roof, rows = roofline(wl, runner, kern, args.steps)
+    if switched:  # the committed counters were taken at the workload's own precision
+        roof["traffic"] = None
     del runner
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", flush=True)
         cpu = cpu_baseline(wl, args.cpu_sample_batch)
-    dtype = "bf16" if wl.mixed else "f32"
     rec = {
         "metric": METRIC, "value": value, "unit": "grid-pts·ch/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
@@ -247,8 +256,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: {wl.notes}", "batch": wl.batch, "width": wl.width,
                    "grid": list(wl.grid), "modes": list(wl.modes), "blocks": wl.blocks,
-                   "spectral_precision": "bf16 operands, fp32 accumulate" if wl.mixed
-                   else "fp32", "pointwise_precision": "fp32"},
+                   "spectral_precision": (f"{dtype} operands, fp32 accumulate"
+                                          if dtype != "f32" else "fp32")
+                   + (f" (switched from {configs.precision(wl)}, tanh "
+                      f"{'kept' if wl.mixed else 'off'})" if switched else ""),
+                   "pointwise_precision": "fp32"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": {k: {"launches": v["launches"], "avg_us": round(v["avg_us"], 2),

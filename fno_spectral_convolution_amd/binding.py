@@ -11,7 +11,8 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import POINTER, byref, c_char_p, c_int, c_int32, c_int64, c_size_t, c_uint32, c_void_p
+from ctypes import (POINTER, byref, c_char_p, c_float, c_int, c_int32, c_int64, c_size_t,
+                    c_uint32, c_void_p)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfno.so")
@@ -34,7 +35,8 @@ FNO_FLAG_BIAS = 4
 EXPORTS = [
     "fno_plan_validate", "fno_plan_create", "fno_plan_destroy", "fno_plan_query",
     "fno_spectral_conv_fwd", "fno_spectral_conv_bwd", "fno_block_fwd", "fno_block_bwd",
-    "fno_pointwise_fwd", "fno_mse_workspace_bytes", "fno_mse_grad", "fno_timing_enable",
+    "fno_pointwise_fwd", "fno_mse_workspace_bytes", "fno_mse_grad", "fno_mse_grad_scaled",
+    "fno_timing_enable",
     "fno_timing_reset", "fno_timing_count", "fno_timing_get", "fno_status_string",
     "fno_last_error_message",
 ]
@@ -75,6 +77,7 @@ def _load():
                                       P, P, P, P, P, P, P]),
         "fno_mse_workspace_bytes": (c_int, [c_int64, POINTER(c_size_t)]),
         "fno_mse_grad": (c_int, [c_int64, P, P, P, P, P, c_size_t, P]),
+        "fno_mse_grad_scaled": (c_int, [c_int64, P, P, P, P, c_float, P, c_size_t, P]),
         "fno_timing_enable": (c_int, [c_int]),
         "fno_timing_reset": (c_int, []),
         "fno_timing_count": (c_int, [POINTER(c_int)]),
@@ -176,6 +179,11 @@ def fno_mse_grad(n, y, t, grad, loss, ws, ws_bytes, stream):
     _check(_lib.fno_mse_grad(n, y, t, grad, loss, ws, ws_bytes, stream), "fno_mse_grad")
 
 
+def fno_mse_grad_scaled(n, y, t, grad, loss, grad_scale, ws, ws_bytes, stream):
+    _check(_lib.fno_mse_grad_scaled(n, y, t, grad, loss, grad_scale, ws, ws_bytes, stream),
+           "fno_mse_grad_scaled")
+
+
 def fno_timing_enable(enable: bool) -> None:
     _check(_lib.fno_timing_enable(1 if enable else 0), "fno_timing_enable")
 
@@ -202,6 +210,17 @@ def timing_report() -> dict:
 
 
 # ---- torch-facing convenience (allocation + pointer marshalling only) ---------------------
+def spectral_dtype(mixed):
+    """fno_dtype of a plan: False -> F32, True / "bf16" -> BF16, "f16" -> F16."""
+    if mixed is False or mixed is None:
+        return FNO_DTYPE_F32
+    if mixed is True or mixed == "bf16":
+        return FNO_DTYPE_BF16
+    if mixed == "f16":
+        return FNO_DTYPE_F16
+    raise ValueError(f"unknown spectral precision {mixed!r}")
+
+
 def _ptr(t):
     return None if t is None else t.data_ptr()
 
@@ -213,14 +232,16 @@ class Plan:
 
     def __init__(self, batch, c_in, c_out, grid, modes, mixed=False, tanh=None, gelu=True,
                  bias=True, device=None):
+        """mixed: False (fp32 spectral path), True or "bf16" (bfloat16 operands), "f16" (IEEE
+        half operands); a mixed plan takes the tanh pre-activation unless tanh says otherwise."""
         import torch
         self.torch = torch
         self.device = torch.device(device) if device is not None else torch.device("cuda")
-        tanh = mixed if tanh is None else tanh
+        tanh = bool(mixed) if tanh is None else tanh
         flags = (FNO_FLAG_TANH_PREACT if tanh else 0) | (FNO_FLAG_GELU if gelu else 0) | \
             (FNO_FLAG_BIAS if bias else 0)
         self.desc = make_desc(batch, c_in, c_out, tuple(grid), tuple(modes),
-                              FNO_DTYPE_BF16 if mixed else FNO_DTYPE_F32, flags)
+                              spectral_dtype(mixed), flags)
         self.batch, self.c_in, self.c_out = batch, c_in, c_out
         self.grid, self.modes = tuple(grid), tuple(modes)
         self.flags = flags
@@ -312,13 +333,20 @@ def pointwise(x, w1, b1=None, w2=None, b2=None, out=None):
     return y
 
 
-def mse_grad(y, t, grad=None, loss=None, ws=None):
+def mse_grad(y, t, grad=None, loss=None, ws=None, grad_scale=1.0):
+    """loss = mean((y - t)^2), grad = grad_scale * 2 (y - t) / n (grad_scale: a static loss
+    scale for IEEE-half plans)."""
     import torch
     n = y.numel()
     g = grad if grad is not None else torch.empty_like(y)
     lo = loss if loss is not None else torch.empty(1, dtype=torch.float32, device=y.device)
     nb = fno_mse_workspace_bytes(n)
     w = ws if ws is not None else torch.empty(max(nb, 16), dtype=torch.uint8, device=y.device)
-    fno_mse_grad(n, y.data_ptr(), t.data_ptr(), g.data_ptr(), lo.data_ptr(), w.data_ptr(),
-                 w.numel(), torch.cuda.current_stream(y.device).cuda_stream)
+    stream = torch.cuda.current_stream(y.device).cuda_stream
+    if grad_scale == 1.0:
+        fno_mse_grad(n, y.data_ptr(), t.data_ptr(), g.data_ptr(), lo.data_ptr(), w.data_ptr(),
+                     w.numel(), stream)
+    else:
+        fno_mse_grad_scaled(n, y.data_ptr(), t.data_ptr(), g.data_ptr(), lo.data_ptr(),
+                            float(grad_scale), w.data_ptr(), w.numel(), stream)
     return lo, g

@@ -1,4 +1,4 @@
-"""Workload registry: the five FNO workloads this library is checked and measured on.
+"""Workload registry: the FNO workloads this library is checked and measured on.
 
 Pure data.  Shapes follow the FNO of the model-parallel FNO page ("Proposed method": 4
 spectral blocks, width 20; "Main findings": 3D and 4D space-time grids) and the
@@ -20,7 +20,8 @@ class Workload:
     grid: Tuple[int, ...]         # spatial grid N_0..N_{d-1}; the last axis is contiguous
     modes: Tuple[int, ...]        # modes per corner m_0..m_{d-1}
     blocks: int                   # number of spectral blocks
-    mixed: bool                   # tanh pre-activation + bf16 spectral operands
+    mixed: object                 # False: fp32; True / "bf16" or "f16": tanh pre-activation
+                                  # + bfloat16 or IEEE-half spectral operands
     train: bool                   # forward + MSE + backward (else forward only)
     lift_in: Optional[int] = None     # pointwise lift input channels (2D stack)
     proj_hidden: Optional[int] = None  # projection hidden width (2D stack)
@@ -62,7 +63,23 @@ WORKLOADS = {
                    notes="4D space-time block stack forward, fp32"),
     "st4d_128x20_bf16": Workload("st4d_128x20_bf16", 5, 1, 20, (128, 128, 128, 20), (12, 12, 12, 8), 4, True, False,
                     notes="4D space-time block stack forward, tanh + bf16"),
+    # the IEEE-half variants of the two mixed-precision workloads
+    "train2d_512_f16": Workload("train2d_512_f16", 3, 8, 64, (512, 512), (32, 32), 4, "f16", True,
+                   notes="2D FNO training step, tanh + fp16 spectral path (static loss scale 2^16), fwd+bwd, MSE"),
+    "st4d_128x20_f16": Workload("st4d_128x20_f16", 5, 1, 20, (128, 128, 128, 20), (12, 12, 12, 8), 4, "f16", False,
+                    notes="4D space-time block stack forward, tanh + fp16"),
 }
+
+# static loss scale of the IEEE-half training step: MSE gradients of a mean over ~10^8 elements
+# are ~1e-8, below half's smallest subnormal (6e-8); scaled by 2^16 they sit near 1e-3
+F16_LOSS_SCALE = 65536.0
+
+
+def precision(wl) -> str:
+    """Spectral arithmetic of a workload: "f32", "bf16" or "f16"."""
+    if wl.mixed == "f16":
+        return "f16"
+    return "bf16" if wl.mixed else "f32"
 
 
 def get(name: str) -> Workload:

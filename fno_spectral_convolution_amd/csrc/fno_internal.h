@@ -27,7 +27,20 @@ struct Geom {
   int64_t Mprod;       // prod m_j (weights per corner per (i, o))
   int ncorner;
   float inv_ntot;      // 1 / P
-  bool bf16;           // spectral operands in bfloat16
+  bool bf16;           // spectral operands in a 16-bit format (half)
+  int half;            // 0: fp32 operands; 1: bfloat16; 2: IEEE half
+  // IEEE-half plans scale every transform table by 1/sqrt(N_j) in both directions (sc[j]), so
+  // spectra stay near unit size; 1 otherwise.  The mix's adjoint factor gamma * adj_scale is
+  // gamma / Ntot (tables unscaled) or gamma (scaled tables).
+  float sc[kMaxDims];
+  float adj_scale;
+  // IEEE-half plans also multiply the mixed spectra by a power of two near sqrt(Cin) Cout
+  // (mix_gain[0], forward) or sqrt(Cout) Cin (mix_gain[1], input gradient).  It offsets the
+  // 1/(Cin Cout) size of FNO spectral weights, so the spectra entering the inverse stay in
+  // half's normal range; the last inverse stage takes it out again (inv_gain, folded into its
+  // half table or applied in float).  Powers of two: both steps are exact.  1 otherwise.
+  float mix_gain[2];
+  float inv_gain[2];
 };
 
 // Device tables owned by a plan (all in one allocation).
@@ -40,7 +53,8 @@ struct Tables {
   // gt_fwd = g(k)/Ntot (cos, -sin)(2 pi k p / Nb); gt_unit = (cos, -sin) (adjoint scale)
   const float* gt_fwd;
   const float* gt_unit;
-  const uint16_t* gt_fwd_bf;        // the same, bfloat16 bits
+  const uint16_t* gt_fwd_bf;        // the same as 16-bit half operands (IEEE-half plans:
+                                    // 1/sqrt(Nb) and 1/mix_gain instead of 1/Ntot)
   const uint16_t* gt_unit_bf;
   // forward plane tables: t1 [Nb][jpad] (col 2k = cos, 2k+1 = -sin of 2 pi k c / Nb) and
   // f2 [4 ma][Na] (rows < 2 ma: cos, rows >= 2 ma: sin of 2 pi ka(s) row / Na)
@@ -155,6 +169,6 @@ hipError_t launch_pointwise(int64_t batch, int64_t npts, int cin, int hidden, in
                             const float* x, const float* w1, const float* b1, const float* w2,
                             const float* b2, float* y, hipStream_t s);
 hipError_t launch_mse(int64_t n, const float* y, const float* t, float* g, float* loss,
-                      double* part, int nparts, hipStream_t s);
+                      float grad_scale, double* part, int nparts, hipStream_t s);
 
 }  // namespace fno

@@ -4,8 +4,8 @@
 //   y_spec[row][c] = sum_k g(k)/Ntot Re(U[row][k] e^{+2 pi i k c / Nb})
 //   z = y_spec + Wb x + bias,  y = GELU(z)
 // (the inverse half of the FNO spectral transform and its pointwise bypass: model-parallel FNO
-// page, "Proposed method"; the half-precision variant of the mixed-precision neural-operator
-// page, "Tiivistelmä").  T = [B][Cout][O][2 ma][mb] is the spectrum after the inverse of the
+// page, "Proposed method"; the half-precision variants (bfloat16 or IEEE half operands) of the
+// mixed-precision neural-operator page, "Tiivistelmä").  T = [B][Cout][O][2 ma][mb] is the spectrum after the inverse of the
 // outer axes only, so the full-size last-axis spectrum [B][Cout][O][Na][mb] never exists.
 //
 // A work-group owns one outer position o of one batch entry (all channels, all Na rows) and
@@ -108,9 +108,13 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // MODE 0: y = y_spec;  1: y = act(y_spec + Wb x + bias);  2: the same and z saved
-template <bool BF, int MODE>
+template <int H, int MODE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 k_epi_rows(RowsEpiArgs a) {
+  constexpr bool BF = H != 0;  // half operands (bfloat16 or IEEE half)
+  using HT = HalfOf<H>;
+  using V8 = typename HT::v8;
+  using E = typename HT::elem;
   constexpr bool BLK = MODE >= 1;
   extern __shared__ __attribute__((aligned(16))) float s_er[];
   const int Nb = a.Nb;
@@ -149,7 +153,7 @@ k_epi_rows(RowsEpiArgs a) {
   const int k = m >> 1, ri = m & 1;
   const int twoma = 2 * a.ma;
   float afr[BF ? 1 : kErCPW][BF ? 1 : kErMA];
-  bf16x8 afb[BF ? kErCPW : 1][2];
+  V8 afb[BF ? kErCPW : 1][2];
 #pragma unroll
   for (int j = 0; j < kErCPW; ++j) {
     const int cor = wave + 4 * j;
@@ -182,13 +186,13 @@ k_epi_rows(RowsEpiArgs a) {
           const float fx = (ri == part) ? 1.f : 0.f;
           const float fy = (ri == part) ? 0.f : (ri ? 1.f : -1.f);
           afb[j][jj][e] =
-              (__bf16)keep_if(t.x * fx + t.y * fy, co_ok && s < twoma && tcol < a.KA && k < a.mb);
+              (E)keep_if(t.x * fx + t.y * fy, co_ok && s < twoma && tcol < a.KA && k < a.mb);
         }
     }
   }
   // second-product B fragments (G[k' = 4 q + r][c]), c = 16 ct + m
   float gfr[BF ? 1 : 2][4];
-  bf16x8 gfb[2];
+  V8 gfb[2];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     const int c = 16 * ct + m;
@@ -202,12 +206,7 @@ k_epi_rows(RowsEpiArgs a) {
     } else {
       const uint2 g2 = *reinterpret_cast<const uint2*>(a.gt_bf + cc * a.kpad + 4 * q);
       const uint32_t w0 = c < Nb ? g2.x : 0u, w1 = c < Nb ? g2.y : 0u;
-      gfb[ct][0] = __builtin_bit_cast(__bf16, (uint16_t)(w0 & 0xffffu));
-      gfb[ct][1] = __builtin_bit_cast(__bf16, (uint16_t)(w0 >> 16));
-      gfb[ct][2] = __builtin_bit_cast(__bf16, (uint16_t)(w1 & 0xffffu));
-      gfb[ct][3] = __builtin_bit_cast(__bf16, (uint16_t)(w1 >> 16));
-#pragma unroll
-      for (int e = 4; e < 8; ++e) gfb[ct][e] = __builtin_bit_cast(__bf16, (uint16_t)0);
+      gfb[ct] = __builtin_bit_cast(V8, make_uint4(w0, w1, 0u, 0u));
     }
   }
   // bypass A fragments Wb[16 mt + m][4 kb + q] and the bias of rows 16 mt + 4 q + r
@@ -234,7 +233,7 @@ k_epi_rows(RowsEpiArgs a) {
   }
   // first-product B fragments: A[row][s'] for this lane's row of chunk c
   float bfr[BF ? 1 : kErMA];
-  bf16x8 bhi[2], blo[2];
+  V8 bhi[2], blo[2];
   auto load_rowtab = [&](int c) {
     const int row = kErRows * c + m;
     if constexpr (!BF) {
@@ -251,8 +250,8 @@ k_epi_rows(RowsEpiArgs a) {
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         const int col = min(32 * jj + 8 * q, a.KA - 8);
-        bhi[jj] = *reinterpret_cast<const bf16x8*>(a.ainv_bf + row * a.KA + col);
-        blo[jj] = *reinterpret_cast<const bf16x8*>(a.ainv_lo + row * a.KA + col);
+        bhi[jj] = *reinterpret_cast<const V8*>(a.ainv_bf + row * a.KA + col);
+        blo[jj] = *reinterpret_cast<const V8*>(a.ainv_lo + row * a.KA + col);
       }
     }
   };
@@ -310,17 +309,13 @@ k_epi_rows(RowsEpiArgs a) {
       } else {
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-          u = mfma_bf16(afb[j][jj], bhi[jj], u);
-          u = mfma_bf16(afb[j][jj], blo[jj], u);
+          u = HT::mfma(afb[j][jj], bhi[jj], u);
+          u = HT::mfma(afb[j][jj], blo[jj], u);
         }
       }
-      bf16x8 ub;
-      if constexpr (BF) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ub[e] = (__bf16)u[e];
-#pragma unroll
-        for (int e = 4; e < 8; ++e) ub[e] = __builtin_bit_cast(__bf16, (uint16_t)0);
-      }
+      V8 ub;
+      if constexpr (BF)
+        ub = __builtin_bit_cast(V8, make_uint4(HT::pack2(u[0], u[1]), HT::pack2(u[2], u[3]), 0u, 0u));
       // U (A operand, K-step r slot q <-> k' = 4 q + r) times G (B operand)
       float* py = s_y + min(cor, a.Cout) * kErYC + 4 * q * kErRS + m;
 #pragma unroll
@@ -330,7 +325,7 @@ k_epi_rows(RowsEpiArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) w = mfma_f32(u[r], gfr[ct][r], w);
         } else {
-          w = mfma_bf16(ub, gfb[ct], w);
+          w = HT::mfma(ub, gfb[ct], w);
         }
         // w[r] = y_spec[chunk row 4 q + r][column 16 ct + m]
 #pragma unroll
@@ -394,17 +389,17 @@ bool epilogue_rows_ok(const fno_plan* p, int mode, const float* x, const float* 
   return al16(x) && al16(y) && al16(zsave);
 }
 
-template <bool BF, int MODE>
+template <int H, int MODE>
 static hipError_t launch_rows_t(const RowsEpiArgs& a, int B, hipStream_t s) {
   const int RP = kErRows * a.Nb;
   const int xfl = 4 * kErKB * RP > 4 * 256 * kErXPT ? 4 * kErKB * RP : 4 * 256 * kErXPT;
   const size_t lds = sizeof(float) * ((size_t)(a.Cout + 1) * kErYC + (MODE >= 1 ? xfl : 0));
   if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_epi_rows<BF, MODE>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_epi_rows<H, MODE>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k_epi_rows<BF, MODE>), dim3((unsigned)a.O, (unsigned)B), dim3(256), lds, s,
+  hipLaunchKernelGGL((k_epi_rows<H, MODE>), dim3((unsigned)a.O, (unsigned)B), dim3(256), lds, s,
                      a);
   return hipGetLastError();
 }
@@ -437,14 +432,19 @@ hipError_t launch_epilogue_rows(const fno_plan* p, int mode, const float2* T, co
   a.gt = p->t.gt_fwd;
   a.gt_bf = p->t.gt_fwd_bf;
   const int md = mode == EPI_SPECTRAL ? 0 : (zsave ? 2 : 1);
-  if (g.bf16) {
-    if (md == 0) return launch_rows_t<true, 0>(a, g.B, s);
-    if (md == 1) return launch_rows_t<true, 1>(a, g.B, s);
-    return launch_rows_t<true, 2>(a, g.B, s);
+  if (g.half == 2) {
+    if (md == 0) return launch_rows_t<2, 0>(a, g.B, s);
+    if (md == 1) return launch_rows_t<2, 1>(a, g.B, s);
+    return launch_rows_t<2, 2>(a, g.B, s);
   }
-  if (md == 0) return launch_rows_t<false, 0>(a, g.B, s);
-  if (md == 1) return launch_rows_t<false, 1>(a, g.B, s);
-  return launch_rows_t<false, 2>(a, g.B, s);
+  if (g.half == 1) {
+    if (md == 0) return launch_rows_t<1, 0>(a, g.B, s);
+    if (md == 1) return launch_rows_t<1, 1>(a, g.B, s);
+    return launch_rows_t<1, 2>(a, g.B, s);
+  }
+  if (md == 0) return launch_rows_t<0, 0>(a, g.B, s);
+  if (md == 1) return launch_rows_t<0, 1>(a, g.B, s);
+  return launch_rows_t<0, 2>(a, g.B, s);
 }
 
 }  // namespace fno

@@ -38,7 +38,7 @@ struct EpiArgs {
   const float2* T;     // [B][C][lines][mb]
   const float* wb;     // [C][C] (o, i)
   const float* bias;   // [C] or null
-  const void* gt;      // [Nb][kpad] f32 or bf16 bits
+  const void* gt;      // [Nb][kpad] f32 or half bits (the plan's format)
   float* y;            // forward output (or grad_x backward)
   float* z;            // forward z save (nullable)
   const float* gy;     // backward incoming gradient
@@ -58,9 +58,10 @@ constexpr int kMaxKpad = 64;  // 2*mb padded; larger spectra take the generic ke
 
 // Stage the spectrum rows of one line (every channel, 2*mb floats) into LDS as the B operand
 // of the spectral product: bf16 [CP][kpad + 8] or f32 [CP][kpad + 4], zero padded.
-template <int C, bool BF>
+template <int C, int H>
 __device__ __forceinline__ void stage_line(const EpiArgs& a, const float2* Trow0,
                                            unsigned char* tl, int tid) {
+  constexpr bool BF = H != 0;
   constexpr int CP = (C + 15) / 16 * 16;
   constexpr int kst = kMaxKpad + (BF ? 8 : 4);
   const int64_t cstride = a.lines * a.mb;
@@ -74,8 +75,8 @@ __device__ __forceinline__ void stage_line(const EpiArgs& a, const float2* Trow0
           reinterpret_cast<const float*>(Trow0 + (int64_t)c * cstride) + k4);
     if (BF) {
       uint2 pk;
-      pk.x = pack_bf16x2(v.x, v.y);
-      pk.y = pack_bf16x2(v.z, v.w);
+      pk.x = HalfOf<H>::pack2(v.x, v.y);
+      pk.y = HalfOf<H>::pack2(v.z, v.w);
       *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(tl) + c * kst + k4) = pk;
     } else {
       *reinterpret_cast<float4*>(reinterpret_cast<float*>(tl) + c * kst + k4) = v;
@@ -107,9 +108,10 @@ __device__ __forceinline__ void load_line(const EpiArgs& a, const float2* Trow0,
   }
 }
 
-template <int C, bool BF>
+template <int C, int H>
 __device__ __forceinline__ void write_line(const EpiArgs& a, const LineT<C>& t,
                                            unsigned char* tl, int tid) {
+  constexpr bool BF = H != 0;
   constexpr int kst = kMaxKpad + (BF ? 8 : 4);
 #pragma unroll
   for (int i = 0; i < LineT<C>::N; ++i) {
@@ -120,8 +122,8 @@ __device__ __forceinline__ void write_line(const EpiArgs& a, const LineT<C>& t,
     const float4 v = live ? t.v[i] : make_float4(0.f, 0.f, 0.f, 0.f);
     if (BF) {
       uint2 pk;
-      pk.x = pack_bf16x2(v.x, v.y);
-      pk.y = pack_bf16x2(v.z, v.w);
+      pk.x = HalfOf<H>::pack2(v.x, v.y);
+      pk.y = HalfOf<H>::pack2(v.z, v.w);
       *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(tl) + c * kst + k4) = pk;
     } else {
       *reinterpret_cast<float4*>(reinterpret_cast<float*>(tl) + c * kst + k4) = v;
@@ -131,20 +133,20 @@ __device__ __forceinline__ void write_line(const EpiArgs& a, const LineT<C>& t,
 
 // Fragments of the last-axis table for one point group of this wave: A operand rows
 // pb0 + 16 (tbase + j) + m, all K-steps (kpad <= 64).  Loaded one group ahead.
-template <int TMW, bool BF>
-struct GtFrag;
-template <int TMW>
-struct GtFrag<TMW, true> {
-  bf16x8 v[TMW][2];  // K-steps of 32
+template <int TMW, int H>
+struct GtFrag {
+  typename HalfOf<H>::v8 v[TMW][2];  // K-steps of 32
 };
 template <int TMW>
-struct GtFrag<TMW, false> {
+struct GtFrag<TMW, 0> {
   float4 v[TMW][4];  // K-groups of 16
 };
 
-template <int TMW, bool BF, bool IL = false, int MT = 4>
+template <int TMW, int H, bool IL = false, int MT = 4>
 __device__ __forceinline__ void load_gt(const EpiArgs& a, int pb0, int tbase, int m, int q,
-                                        GtFrag<TMW, BF>& f) {
+                                        GtFrag<TMW, H>& f) {
+  constexpr bool BF = H != 0;
+  using V8 = typename HalfOf<H>::v8;
 #pragma unroll
   for (int j = 0; j < TMW; ++j) {
     // row m of M-tile t: point MT m + t (interleaved over the MT tiles of the step) or
@@ -154,44 +156,11 @@ __device__ __forceinline__ void load_gt(const EpiArgs& a, int pb0, int tbase, in
     if constexpr (BF) {
       const uint16_t* gt = static_cast<const uint16_t*>(a.gt) + row;
 #pragma unroll
-      for (int s = 0; s < 2; ++s) f.v[j][s] = *reinterpret_cast<const bf16x8*>(gt + 32 * s + 8 * q);
+      for (int s = 0; s < 2; ++s) f.v[j][s] = *reinterpret_cast<const V8*>(gt + 32 * s + 8 * q);
     } else {
       const float* gt = static_cast<const float*>(a.gt) + row;
 #pragma unroll
       for (int g = 0; g < 4; ++g) f.v[j][g] = *reinterpret_cast<const float4*>(gt + 16 * g + 4 * q);
-    }
-  }
-}
-
-// Spectral product of one point group for this wave: acc[j] += GT[points of M-tile t] x
-// tl[channel tile ct]^T, with t = tbase + j.  M-tile t, row m <-> point 16 t + m of the group.
-template <int C, int TMW, bool BF>
-__device__ __forceinline__ void spectral_coop(const EpiArgs& a, const unsigned char* tl,
-                                              const GtFrag<TMW, BF>& f, int ct, int m, int q,
-                                              f32x4 (&acc)[TMW]) {
-  constexpr int kst = kMaxKpad + (BF ? 8 : 4);
-  if constexpr (BF) {
-    const uint16_t* tb = reinterpret_cast<const uint16_t*>(tl) + (16 * ct + m) * kst;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      if (32 * s >= a.kpad) break;
-      const bf16x8 B = *reinterpret_cast<const bf16x8*>(tb + 32 * s + 8 * q);
-#pragma unroll
-      for (int j = 0; j < TMW; ++j) acc[j] = mfma_bf16(f.v[j][s], B, acc[j]);
-    }
-  } else {
-    const float* tb = reinterpret_cast<const float*>(tl) + (16 * ct + m) * kst;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      if (16 * g >= a.kpad) break;
-      const float4 B4 = *reinterpret_cast<const float4*>(tb + 16 * g + 4 * q);
-#pragma unroll
-      for (int j = 0; j < TMW; ++j) {
-        acc[j] = mfma_f32(f.v[j][g].x, B4.x, acc[j]);
-        acc[j] = mfma_f32(f.v[j][g].y, B4.y, acc[j]);
-        acc[j] = mfma_f32(f.v[j][g].z, B4.z, acc[j]);
-        acc[j] = mfma_f32(f.v[j][g].w, B4.w, acc[j]);
-      }
     }
   }
 }
@@ -250,9 +219,11 @@ __device__ __forceinline__ void load_rows(float4 (&v)[NPT], const float* base, i
 // tiles are adjacent in the [channel][point] LDS tile.  The z tile goes through LDS and the
 // stores are row-contiguous: 16 G threads write one channel's 64 G points.
 // MODE: 0 spectral part only, 1 block (bypass, bias, optional GELU), 2 block + z save.
-template <int C, bool BF, int MODE, int G>
+template <int C, int H, int MODE, int G>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C == 64 ? 3 : 4)))
 k_epi_fwd_line(EpiArgs a) {
+  constexpr bool BF = H != 0;  // half operands (bfloat16 or IEEE half)
+  using V8 = typename HalfOf<H>::v8;
   constexpr int CP = (C + 15) / 16 * 16;
   constexpr int NT = CP / 16;
   constexpr int PI = PG * G;        // points per step
@@ -307,12 +278,12 @@ k_epi_fwd_line(EpiArgs a) {
   float4 pre[NPT];
 #pragma unroll
   for (int u = 0; u < NPT; ++u) pre[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-  GtFrag<G, BF> gtf;
+  GtFrag<G, H> gtf;
   if (BLK) {
 #pragma unroll
     for (int u = 0; u < NPT; ++u) pre[u] = *reinterpret_cast<const float4*>(a.x + goff[u]);
   }
-  load_gt<G, BF, true, MT>(a, 0, tbase, m, q, gtf);
+  load_gt<G, H, true, MT>(a, 0, tbase, m, q, gtf);
   // narrow fields have few steps per line: the next line's spectrum rows stream in while
   // this one is computed (the last line re-loads itself); wide ones stage each line directly
   constexpr bool LPF = C < 64;
@@ -323,10 +294,10 @@ k_epi_fwd_line(EpiArgs a) {
   for (int lf = 0; lf < a.lpw; ++lf) {
     // every reader of the previous line's spectrum is past that line's last barrier
     if constexpr (LPF) {
-      write_line<C, BF>(a, tln, s_tl, tid);
+      write_line<C, H>(a, tln, s_tl, tid);
       load_line<C>(a, Tb + (int64_t)min(lf + 1, a.lpw - 1) * a.mb, tln, tid);
     } else {
-      stage_line<C, BF>(a, Tb + (int64_t)lf * a.mb, s_tl, tid);
+      stage_line<C, H>(a, Tb + (int64_t)lf * a.mb, s_tl, tid);
     }
     for (int g = 0; g < gpl; ++g) {
       const int f = (lf << a.gpl_log2) + g;
@@ -351,10 +322,10 @@ k_epi_fwd_line(EpiArgs a) {
           if (32 * s2 >= a.kpad) break;
 #pragma unroll
           for (int ct = 0; ct < NT; ++ct) {
-            const bf16x8 B = *reinterpret_cast<const bf16x8*>(
+            const V8 B = *reinterpret_cast<const V8*>(
                 reinterpret_cast<const uint16_t*>(s_tl) + (16 * ct + m) * kst + 32 * s2 + 8 * q);
 #pragma unroll
-            for (int j = 0; j < G; ++j) acc[j][ct] = mfma_bf16(gtf.v[j][s2], B, acc[j][ct]);
+            for (int j = 0; j < G; ++j) acc[j][ct] = HalfOf<H>::mfma(gtf.v[j][s2], B, acc[j][ct]);
           }
         }
       } else {
@@ -375,7 +346,7 @@ k_epi_fwd_line(EpiArgs a) {
           }
         }
       }
-      load_gt<G, BF, true, MT>(a, (fn & (gpl - 1)) * PI, tbase, m, q, gtf);
+      load_gt<G, H, true, MT>(a, (fn & (gpl - 1)) * PI, tbase, m, q, gtf);
       if (BLK) {
 #pragma unroll
         for (int kb = 0; kb < C / 4; ++kb) {
@@ -431,9 +402,11 @@ k_epi_fwd_line(EpiArgs a) {
 // Wave w's dWb tiles: NT = 4: o-tile w, all 4 i-tiles; NT = 2: o-tile w >> 1, i-tile w & 1;
 // NT = 1: the single tile over its quarter of the step's points.
 // MODE: 1 spectral part only (grad_x = s(x) * spectral), 3 block, 7 block with GELU' (z read).
-template <int C, bool BF, bool TANH, int MODE, int G>
+template <int C, int H, bool TANH, int MODE, int G>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C == 64 ? 2 : 3)))
 k_epi_bwd_line(EpiArgs a) {
+  constexpr bool BF = H != 0;  // half operands (bfloat16 or IEEE half)
+  using V8 = typename HalfOf<H>::v8;
   constexpr int CP = (C + 15) / 16 * 16;
   constexpr int NT = CP / 16;
   constexpr int PI = PG * G;        // points per step
@@ -499,14 +472,14 @@ k_epi_bwd_line(EpiArgs a) {
     pz[u] = pg_y[u];
     px[u] = pg_y[u];
   }
-  GtFrag<G, BF> gtf;
+  GtFrag<G, H> gtf;
 #pragma unroll
   for (int u = 0; u < NPT; ++u) {
     if (BLK) pg_y[u] = *reinterpret_cast<const float4*>(a.gy + goff[u]);
     if (GL) pz[u] = *reinterpret_cast<const float4*>(a.zin + goff[u]);
     if (NX) px[u] = *reinterpret_cast<const float4*>(a.x + goff[u]);
   }
-  load_gt<G, BF, true, MT>(a, 0, tbase, m, q, gtf);
+  load_gt<G, H, true, MT>(a, 0, tbase, m, q, gtf);
   constexpr bool LPF = C < 64;
   const float2* Tb = a.T + ((int64_t)b * C * a.lines + l0) * a.mb;
   LineT<LPF ? C : 16> tln;
@@ -515,10 +488,10 @@ k_epi_bwd_line(EpiArgs a) {
   for (int lf = 0; lf < a.lpw; ++lf) {
     // every reader of the previous line's spectrum is past that line's last barrier
     if constexpr (LPF) {
-      write_line<C, BF>(a, tln, s_tl, tid);
+      write_line<C, H>(a, tln, s_tl, tid);
       load_line<C>(a, Tb + (int64_t)min(lf + 1, a.lpw - 1) * a.mb, tln, tid);
     } else {
-      stage_line<C, BF>(a, Tb + (int64_t)lf * a.mb, s_tl, tid);
+      stage_line<C, H>(a, Tb + (int64_t)lf * a.mb, s_tl, tid);
     }
     for (int g = 0; g < gpl; ++g) {
       const int f = (lf << a.gpl_log2) + g;
@@ -555,10 +528,10 @@ k_epi_bwd_line(EpiArgs a) {
           if (32 * s2 >= a.kpad) break;
 #pragma unroll
           for (int ct = 0; ct < NT; ++ct) {
-            const bf16x8 B = *reinterpret_cast<const bf16x8*>(
+            const V8 B = *reinterpret_cast<const V8*>(
                 reinterpret_cast<const uint16_t*>(s_tl) + (16 * ct + m) * kst + 32 * s2 + 8 * q);
 #pragma unroll
-            for (int j = 0; j < G; ++j) acc[j][ct] = mfma_bf16(gtf.v[j][s2], B, acc[j][ct]);
+            for (int j = 0; j < G; ++j) acc[j][ct] = HalfOf<H>::mfma(gtf.v[j][s2], B, acc[j][ct]);
           }
         }
       } else {
@@ -579,7 +552,7 @@ k_epi_bwd_line(EpiArgs a) {
           }
         }
       }
-      load_gt<G, BF, true, MT>(a, (fn & (gpl - 1)) * PI, tbase, m, q, gtf);
+      load_gt<G, H, true, MT>(a, (fn & (gpl - 1)) * PI, tbase, m, q, gtf);
       if (TANH) {
         // lane (n = m, q), tile tbase + j, register r: channel 16 ct + m, point
         // MT (4 q + r) + tbase + j
@@ -683,24 +656,25 @@ k_epi_bwd_line(EpiArgs a) {
 
 // ------------------------------------------------------------------------------------------
 template <int C, int G>
-static hipError_t launch_fwd_c(const EpiArgs& a, bool bf, int mode, int wgs, hipStream_t s) {
-#define FNO_EPI_FWD(BFV, MV) \
-  hipLaunchKernelGGL((k_epi_fwd_line<C, BFV, MV, G>), dim3(wgs), dim3(256), 0, s, a)
-  if (bf) {
-    if (mode == 0) FNO_EPI_FWD(true, 0);
-    else if (mode == 1) FNO_EPI_FWD(true, 1);
-    else FNO_EPI_FWD(true, 2);
-  } else {
-    if (mode == 0) FNO_EPI_FWD(false, 0);
-    else if (mode == 1) FNO_EPI_FWD(false, 1);
-    else FNO_EPI_FWD(false, 2);
-  }
+static hipError_t launch_fwd_c(const EpiArgs& a, int half, int mode, int wgs, hipStream_t s) {
+#define FNO_EPI_FWD(HV, MV) \
+  hipLaunchKernelGGL((k_epi_fwd_line<C, HV, MV, G>), dim3(wgs), dim3(256), 0, s, a)
+#define FNO_EPI_FWD_M(HV)                 \
+  do {                                    \
+    if (mode == 0) FNO_EPI_FWD(HV, 0);      \
+    else if (mode == 1) FNO_EPI_FWD(HV, 1); \
+    else FNO_EPI_FWD(HV, 2);                \
+  } while (0)
+  if (half == 2) FNO_EPI_FWD_M(2);
+  else if (half == 1) FNO_EPI_FWD_M(1);
+  else FNO_EPI_FWD_M(0);
+#undef FNO_EPI_FWD_M
 #undef FNO_EPI_FWD
   return hipGetLastError();
 }
 
 template <int C, int G>
-static hipError_t launch_bwd_c(const EpiArgs& a, bool bf, bool tanh_pre, int mode, int wgs,
+static hipError_t launch_bwd_c(const EpiArgs& a, int half, bool tanh_pre, int mode, int wgs,
                                hipStream_t s) {
 #define FNO_EPI_BWD(BFV, TV, MV) \
   hipLaunchKernelGGL((k_epi_bwd_line<C, BFV, TV, MV, G>), dim3(wgs), dim3(256), 0, s, a)
@@ -713,12 +687,15 @@ static hipError_t launch_bwd_c(const EpiArgs& a, bool bf, bool tanh_pre, int mod
     else                          \
       FNO_EPI_BWD(BFV, TV, 7);    \
   } while (0)
-  if (bf) {
-    if (tanh_pre) FNO_EPI_BWD_M(true, true);
-    else FNO_EPI_BWD_M(true, false);
+  if (half == 2) {
+    if (tanh_pre) FNO_EPI_BWD_M(2, true);
+    else FNO_EPI_BWD_M(2, false);
+  } else if (half == 1) {
+    if (tanh_pre) FNO_EPI_BWD_M(1, true);
+    else FNO_EPI_BWD_M(1, false);
   } else {
-    if (tanh_pre) FNO_EPI_BWD_M(false, true);
-    else FNO_EPI_BWD_M(false, false);
+    if (tanh_pre) FNO_EPI_BWD_M(0, true);
+    else FNO_EPI_BWD_M(0, false);
   }
 #undef FNO_EPI_BWD_M
 #undef FNO_EPI_BWD
@@ -778,16 +755,16 @@ hipError_t launch_epilogue_fwd_fast(const fno_plan* p, int mode, const float2* T
   if (wgs > 0x7fffffff) return hipErrorInvalidValue;
   if (G == 2) {
     switch (g.Cout) {
-      case 16: return launch_fwd_c<16, 2>(a, g.bf16, kmode, (int)wgs, s);
-      case 20: return launch_fwd_c<20, 2>(a, g.bf16, kmode, (int)wgs, s);
-      default: return launch_fwd_c<32, 2>(a, g.bf16, kmode, (int)wgs, s);
+      case 16: return launch_fwd_c<16, 2>(a, g.half, kmode, (int)wgs, s);
+      case 20: return launch_fwd_c<20, 2>(a, g.half, kmode, (int)wgs, s);
+      default: return launch_fwd_c<32, 2>(a, g.half, kmode, (int)wgs, s);
     }
   }
   switch (g.Cout) {
-    case 16: return launch_fwd_c<16, 1>(a, g.bf16, kmode, (int)wgs, s);
-    case 20: return launch_fwd_c<20, 1>(a, g.bf16, kmode, (int)wgs, s);
-    case 32: return launch_fwd_c<32, 1>(a, g.bf16, kmode, (int)wgs, s);
-    default: return launch_fwd_c<64, 1>(a, g.bf16, kmode, (int)wgs, s);
+    case 16: return launch_fwd_c<16, 1>(a, g.half, kmode, (int)wgs, s);
+    case 20: return launch_fwd_c<20, 1>(a, g.half, kmode, (int)wgs, s);
+    case 32: return launch_fwd_c<32, 1>(a, g.half, kmode, (int)wgs, s);
+    default: return launch_fwd_c<64, 1>(a, g.half, kmode, (int)wgs, s);
   }
 }
 
@@ -841,10 +818,10 @@ hipError_t launch_epilogue_bwd_fast(const fno_plan* p, int mode, const float2* T
   const int64_t wgs = (int64_t)g.B * a.lines / a.lpw;
   if (wgs > 0x7fffffff) return hipErrorInvalidValue;
   switch (g.Cin) {
-    case 16: return launch_bwd_c<16, 1>(a, g.bf16, tanh_pre, kmode, (int)wgs, s);
-    case 20: return launch_bwd_c<20, 1>(a, g.bf16, tanh_pre, kmode, (int)wgs, s);
-    case 32: return launch_bwd_c<32, 1>(a, g.bf16, tanh_pre, kmode, (int)wgs, s);
-    default: return launch_bwd_c<64, 1>(a, g.bf16, tanh_pre, kmode, (int)wgs, s);
+    case 16: return launch_bwd_c<16, 1>(a, g.half, tanh_pre, kmode, (int)wgs, s);
+    case 20: return launch_bwd_c<20, 1>(a, g.half, tanh_pre, kmode, (int)wgs, s);
+    case 32: return launch_bwd_c<32, 1>(a, g.half, tanh_pre, kmode, (int)wgs, s);
+    default: return launch_bwd_c<64, 1>(a, g.half, tanh_pre, kmode, (int)wgs, s);
   }
 }
 

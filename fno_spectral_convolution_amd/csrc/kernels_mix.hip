@@ -2,10 +2,12 @@
 //   forward   yhat[b,o,t] = sum_i xhat[b,i,t] W[c(t),i,o,kappa(t)]
 //   input     ghx[b,i,t]  = sum_o g[b,o,t] conj(W[c(t),i,o,kappa(t)])
 //   weight    dW[c,i,o,k] = sum_b conj(xhat[b,i,t]) g[b,o,t]
-// with g = ghat scaled by gamma(k_last)/Ntot (the adjoint of the inverse transform).  This is
+// with g = ghat scaled by gamma(k_last)/Ntot (the adjoint of the inverse transform; gamma alone
+// when the plan's transform tables carry 1/sqrt(N_j) in both directions).  IEEE-half plans
+// multiply yhat and ghx by a power-of-two gain that the last inverse stage divides out.  This is
 // the per-mode contraction of the FNO spectral layer (model-parallel FNO page, "Proposed
-// method"); on the mixed path every operand is rounded to bfloat16 and products accumulate in
-// float32 (mixed-precision neural-operator page, "Tiivistelmä").
+// method"); on the half paths every operand is rounded to bfloat16 or IEEE half and products
+// accumulate in float32 (mixed-precision neural-operator page, "Tiivistelmä").
 //
 // Each mode's complex product is one real GEMM with the real and imaginary parts stacked:
 //   rows  = 2 x 8 (re / im part x 8 batch entries, or x 8 input channels for dW)
@@ -32,30 +34,32 @@ constexpr int kOutTB = 8 * 16 * 8 + 16;  // bytes per mode of the [8][16] comple
 __device__ __forceinline__ float mix_scale(const Geom& g, int64_t t) {
   const int kb = (int)(t % g.mb);
   const bool one = (kb == 0) || (2 * kb == g.Nb);
-  return (one ? 1.0f : 2.0f) * g.inv_ntot;
+  return (one ? 1.0f : 2.0f) * g.adj_scale;
 }
 
 // (v0, v1) into K slots (k, k + 1) of row r of mode tile t
-template <bool BF>
+template <int H>
 __device__ __forceinline__ void put_pair(unsigned char* tile, int t, int r, int k, float v0,
                                          float v1) {
+  constexpr bool BF = H != 0;
   unsigned char* p = tile + t * kTB + r * kRowB + k * (BF ? 2 : 4);
   if constexpr (BF) {
-    *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(v0, v1);
+    *reinterpret_cast<uint32_t*>(p) = HalfOf<H>::pack2(v0, v1);
   } else {
     *reinterpret_cast<float2*>(p) = make_float2(v0, v1);
   }
 }
 
 // acc += A_t x B_t over one LDS chunk (lane (m, q) reads 16 B of row m of both tiles)
-template <bool BF>
+template <int H>
 __device__ __forceinline__ f32x4 chunk_product(const unsigned char* ta, const unsigned char* tb,
                                                int t, int m, int q, f32x4 acc) {
   const int off = t * kTB + m * kRowB + 16 * q;
-  if constexpr (BF) {
-    const bf16x8 av = *reinterpret_cast<const bf16x8*>(ta + off);
-    const bf16x8 bv = *reinterpret_cast<const bf16x8*>(tb + off);
-    return mfma_bf16(av, bv, acc);
+  if constexpr (H != 0) {
+    using V = typename HalfOf<H>::v8;
+    const V av = *reinterpret_cast<const V*>(ta + off);
+    const V bv = *reinterpret_cast<const V*>(tb + off);
+    return HalfOf<H>::mfma(av, bv, acc);
   } else {
     const float4 av = *reinterpret_cast<const float4*>(ta + off);
     const float4 bv = *reinterpret_cast<const float4*>(tb + off);
@@ -80,11 +84,12 @@ __device__ __forceinline__ void put_out(unsigned char* out, int t, int m, int q,
 // ------------------------------------------------------------------------------------------
 // Forward (DX = false) and input gradient (DX = true).  Grid: (mode groups, 16-column tiles of
 // the output channels, 8-entry batch tiles).  Contracted channels: Cin (forward) or Cout.
-template <bool BF, bool DX>
+template <int H, bool DX>
 __global__ void __launch_bounds__(256) k_mix_mfma(Geom g, const int32_t* __restrict__ mode_woff,
                                                   const float2* __restrict__ spec,
                                                   const float2* __restrict__ w,
                                                   float2* __restrict__ out) {
+  constexpr bool BF = H != 0;       // half operands (bfloat16 or IEEE half)
   constexpr int IC = BF ? 16 : 8;  // contracted channels per chunk (K = 2 IC)
   constexpr int NW = 16 * IC / 16;  // weight complex values per thread per chunk (16 modes x IC x 16 cols / 256)
   constexpr int NS = 8 * IC / 16;   // spectrum values per thread per chunk (16 modes x 8 x IC / 256)
@@ -132,7 +137,7 @@ __global__ void __launch_bounds__(256) k_mix_mfma(Geom g, const int32_t* __restr
       const int kc = pr / 16, n = pr % 16;
       const bool ok = c0 + kc < ncon && n0 + n < nout;
       // B[2 kc][n] = wr, B[2 kc + 1][n] = wi (conj(W) is taken by the A layout of DX)
-      put_pair<BF>(s_b, tl, n, 2 * kc, ok ? pw[u].x : 0.f, ok ? pw[u].y : 0.f);
+      put_pair<H>(s_b, tl, n, 2 * kc, ok ? pw[u].x : 0.f, ok ? pw[u].y : 0.f);
     }
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
@@ -141,17 +146,17 @@ __global__ void __launch_bounds__(256) k_mix_mfma(Geom g, const int32_t* __restr
       const bool ok = c0 + kc < ncon && b0 + bb < g.B;
       const float vr = ok ? ps[u].x * sc : 0.f, vi = ok ? ps[u].y * sc : 0.f;
       if (DX) {  // (gr + i gi) conj(w): rows b: (gr, gi); rows 8 + b: (gi, -gr)
-        put_pair<BF>(s_a, tl, bb, 2 * kc, vr, vi);
-        put_pair<BF>(s_a, tl, 8 + bb, 2 * kc, vi, -vr);
+        put_pair<H>(s_a, tl, bb, 2 * kc, vr, vi);
+        put_pair<H>(s_a, tl, 8 + bb, 2 * kc, vi, -vr);
       } else {   // (xr + i xi) w: rows b: (xr, -xi); rows 8 + b: (xi, xr)
-        put_pair<BF>(s_a, tl, bb, 2 * kc, vr, -vi);
-        put_pair<BF>(s_a, tl, 8 + bb, 2 * kc, vi, vr);
+        put_pair<H>(s_a, tl, bb, 2 * kc, vr, -vi);
+        put_pair<H>(s_a, tl, 8 + bb, 2 * kc, vi, vr);
       }
     }
     load_chunk(min(c0 + IC, ncon - 1));
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = chunk_product<BF>(s_a, s_b, 4 * wave + j, m, q, acc[j]);
+    for (int j = 0; j < 4; ++j) acc[j] = chunk_product<H>(s_a, s_b, 4 * wave + j, m, q, acc[j]);
   }
   __syncthreads();
   unsigned char* s_out = s_a;  // [16 modes][8 entries][16 columns] complex
@@ -165,8 +170,11 @@ __global__ void __launch_bounds__(256) k_mix_mfma(Geom g, const int32_t* __restr
     const int bb = pr / 16, n = pr % 16;
     const int64_t t = t0 + tl;
     if (t < K && b0 + bb < g.B && n0 + n < nout) {
-      const float2 v =
-          *reinterpret_cast<const float2*>(s_out + tl * kOutTB + (bb * 16 + n) * 8);
+      float2 v = *reinterpret_cast<const float2*>(s_out + tl * kOutTB + (bb * 16 + n) * 8);
+      if constexpr (H == 2) {  // IEEE half: the mix gain (a power of two)
+        v.x *= g.mix_gain[DX];
+        v.y *= g.mix_gain[DX];
+      }
       out[((int64_t)(b0 + bb) * nout + n0 + n) * K + t] = v;
     }
   }
@@ -175,11 +183,12 @@ __global__ void __launch_bounds__(256) k_mix_mfma(Geom g, const int32_t* __restr
 // ------------------------------------------------------------------------------------------
 // Weight gradient.  Grid: (mode groups, 8-channel tiles of Cin, 16-column tiles of Cout).
 // Rows 0..7: Re, rows 8..15: Im of the 8 input channels; K = (batch entry, re / im).
-template <bool BF>
+template <int H>
 __global__ void __launch_bounds__(256) k_mix_mfma_dw(Geom g, const int32_t* __restrict__ mode_woff,
                                                      const float2* __restrict__ xhat,
                                                      const float2* __restrict__ ghat,
                                                      float2* __restrict__ dw) {
+  constexpr bool BF = H != 0;
   constexpr int BC = BF ? 16 : 8;  // batch entries per chunk (K = 2 BC)
   constexpr int NX = 8 * BC / 16;   // x values per thread per chunk (16 modes x 8 ch x BC / 256)
   constexpr int NG = 16 * BC / 16;  // g values per thread per chunk (16 modes x 16 ch x BC / 256)
@@ -225,20 +234,20 @@ __global__ void __launch_bounds__(256) k_mix_mfma_dw(Geom g, const int32_t* __re
       const bool ok = c0 + bb < g.B && i0 + ii < g.Cin;
       const float xr = ok ? px[u].x : 0.f, xi = ok ? px[u].y : 0.f;
       // conj(x) g: rows i: (xr, xi); rows 8 + i: (-xi, xr)
-      put_pair<BF>(s_a, tl, ii, 2 * bb, xr, xi);
-      put_pair<BF>(s_a, tl, 8 + ii, 2 * bb, -xi, xr);
+      put_pair<H>(s_a, tl, ii, 2 * bb, xr, xi);
+      put_pair<H>(s_a, tl, 8 + ii, 2 * bb, -xi, xr);
     }
 #pragma unroll
     for (int u = 0; u < NG; ++u) {
       const int pr = (tid >> 4) + 16 * u;
       const int bb = pr / 16, oo = pr % 16;
       const bool ok = c0 + bb < g.B && o0 + oo < g.Cout;
-      put_pair<BF>(s_b, tl, oo, 2 * bb, ok ? pg[u].x * sc : 0.f, ok ? pg[u].y * sc : 0.f);
+      put_pair<H>(s_b, tl, oo, 2 * bb, ok ? pg[u].x * sc : 0.f, ok ? pg[u].y * sc : 0.f);
     }
     load_chunk(min(c0 + BC, g.B - 1));
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = chunk_product<BF>(s_a, s_b, 4 * wave + j, m, q, acc[j]);
+    for (int j = 0; j < 4; ++j) acc[j] = chunk_product<H>(s_a, s_b, 4 * wave + j, m, q, acc[j]);
   }
   __syncthreads();
   unsigned char* s_out = s_a;  // [16 modes][8 input channels][16 output channels] complex
@@ -272,11 +281,14 @@ hipError_t launch_mix_fwd(const fno_plan* p, const float2* xhat, int nparts,
   (void)nparts;
   (void)part_stride;
   const Geom& g = p->g;
-  if (g.bf16)
-    hipLaunchKernelGGL((k_mix_mfma<true, false>), mix_grid(g, g.Cout), dim3(256), 0, s, g,
+  if (g.half == 2)
+    hipLaunchKernelGGL((k_mix_mfma<2, false>), mix_grid(g, g.Cout), dim3(256), 0, s, g,
+                       p->t.mode_woff, xhat, w, yhat);
+  else if (g.half == 1)
+    hipLaunchKernelGGL((k_mix_mfma<1, false>), mix_grid(g, g.Cout), dim3(256), 0, s, g,
                        p->t.mode_woff, xhat, w, yhat);
   else
-    hipLaunchKernelGGL((k_mix_mfma<false, false>), mix_grid(g, g.Cout), dim3(256), 0, s, g,
+    hipLaunchKernelGGL((k_mix_mfma<0, false>), mix_grid(g, g.Cout), dim3(256), 0, s, g,
                        p->t.mode_woff, xhat, w, yhat);
   return hipGetLastError();
 }
@@ -284,11 +296,14 @@ hipError_t launch_mix_fwd(const fno_plan* p, const float2* xhat, int nparts,
 hipError_t launch_mix_bwd_dx(const fno_plan* p, const float2* ghat, const float2* w,
                              float2* ghx, hipStream_t s) {
   const Geom& g = p->g;
-  if (g.bf16)
-    hipLaunchKernelGGL((k_mix_mfma<true, true>), mix_grid(g, g.Cin), dim3(256), 0, s, g,
+  if (g.half == 2)
+    hipLaunchKernelGGL((k_mix_mfma<2, true>), mix_grid(g, g.Cin), dim3(256), 0, s, g,
+                       p->t.mode_woff, ghat, w, ghx);
+  else if (g.half == 1)
+    hipLaunchKernelGGL((k_mix_mfma<1, true>), mix_grid(g, g.Cin), dim3(256), 0, s, g,
                        p->t.mode_woff, ghat, w, ghx);
   else
-    hipLaunchKernelGGL((k_mix_mfma<false, true>), mix_grid(g, g.Cin), dim3(256), 0, s, g,
+    hipLaunchKernelGGL((k_mix_mfma<0, true>), mix_grid(g, g.Cin), dim3(256), 0, s, g,
                        p->t.mode_woff, ghat, w, ghx);
   return hipGetLastError();
 }
@@ -298,11 +313,14 @@ hipError_t launch_mix_bwd_dw(const fno_plan* p, const float2* xhat, const float2
   const Geom& g = p->g;
   const dim3 grid((unsigned)((g.K + kMT - 1) / kMT), (unsigned)((g.Cin + 7) / 8),
                   (unsigned)((g.Cout + 15) / 16));
-  if (g.bf16)
-    hipLaunchKernelGGL((k_mix_mfma_dw<true>), grid, dim3(256), 0, s, g, p->t.mode_woff, xhat,
+  if (g.half == 2)
+    hipLaunchKernelGGL((k_mix_mfma_dw<2>), grid, dim3(256), 0, s, g, p->t.mode_woff, xhat,
+                       ghat, dw);
+  else if (g.half == 1)
+    hipLaunchKernelGGL((k_mix_mfma_dw<1>), grid, dim3(256), 0, s, g, p->t.mode_woff, xhat,
                        ghat, dw);
   else
-    hipLaunchKernelGGL((k_mix_mfma_dw<false>), grid, dim3(256), 0, s, g, p->t.mode_woff, xhat,
+    hipLaunchKernelGGL((k_mix_mfma_dw<0>), grid, dim3(256), 0, s, g, p->t.mode_woff, xhat,
                        ghat, dw);
   return hipGetLastError();
 }

@@ -24,8 +24,10 @@ struct OuterArgs {
   const uint16_t* Alo;   // bf16 residual (bf16 path)
 };
 
-template <bool BF, int NT>
+template <int H, int NT>
 __global__ void __launch_bounds__(256) k_outer_mfma(OuterArgs a) {
+  constexpr bool BF = H != 0;  // half operands (bfloat16 or IEEE half)
+  using V8 = typename HalfOf<H>::v8;
   constexpr int CT = 16 * NT;  // columns per work-group
   extern __shared__ __attribute__((aligned(16))) unsigned char s_raw[];
   const int K = 2 * a.Lin_pad;
@@ -47,8 +49,8 @@ __global__ void __launch_bounds__(256) k_outer_mfma(OuterArgs a) {
     const float vs = (c & 1) ? -v : v;  // Xs[li][c^1]
     if (BF) {
       uint16_t* bt = reinterpret_cast<uint16_t*>(s_raw);
-      bt[brow(c) * KS + li] = bf16_bits(v);
-      bt[brow(cp) * KS + a.Lin_pad + li] = bf16_bits(vs);
+      bt[brow(c) * KS + li] = HalfOf<H>::bits(v);
+      bt[brow(cp) * KS + a.Lin_pad + li] = HalfOf<H>::bits(vs);
     } else {
       float* bt = reinterpret_cast<float*>(s_raw);
       bt[brow(c) * KS + li] = v;
@@ -67,13 +69,13 @@ __global__ void __launch_bounds__(256) k_outer_mfma(OuterArgs a) {
       const uint16_t* Al = a.Alo + (int64_t)prow * K;
       const uint16_t* bt = reinterpret_cast<const uint16_t*>(s_raw);
       for (int k0 = 0; k0 < K; k0 += 32) {
-        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(A + k0 + 8 * q);
-        const bf16x8 al = *reinterpret_cast<const bf16x8*>(Al + k0 + 8 * q);
+        const V8 ah = *reinterpret_cast<const V8*>(A + k0 + 8 * q);
+        const V8 al = *reinterpret_cast<const V8*>(Al + k0 + 8 * q);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(bt + (16 * nt + m) * KS + k0 + 8 * q);
-          acc[nt] = mfma_bf16(ah, bv, acc[nt]);
-          acc[nt] = mfma_bf16(al, bv, acc[nt]);
+          const V8 bv = *reinterpret_cast<const V8*>(bt + (16 * nt + m) * KS + k0 + 8 * q);
+          acc[nt] = HalfOf<H>::mfma(ah, bv, acc[nt]);
+          acc[nt] = HalfOf<H>::mfma(al, bv, acc[nt]);
         }
       }
     } else {
@@ -227,8 +229,10 @@ __global__ void __launch_bounds__(256) k_outer_fwd_stream(OuterArgs a) {
 // per chunk and term, the table as its bf16 hi + lo pair (two products per term).  K-slot (q, e)
 // is row k0 + 8 q + e; a lane reads the column pair (c & ~1) of each of its 8 rows as one float2,
 // which gives both X[k][c] and the partner for Xs, rounded to bf16 as operands.
-template <int MT, int NTW>
+template <int H, int MT, int NTW>
 __global__ void __launch_bounds__(256) k_outer_fwd_stream_bf(OuterArgs a) {
+  using HT = Half<H>;
+  using V8 = typename HT::v8;
   constexpr int CB = 64 * NTW;
   constexpr int CBS = CB + 4;
   constexpr int F4R = CB / 4;
@@ -263,14 +267,14 @@ __global__ void __launch_bounds__(256) k_outer_fwd_stream_bf(OuterArgs a) {
     }
   };
   // table fragments of a K-step: [row tile][Mr hi, Mr lo, Mi hi, Mi lo], columns k0 + 8 q ..
-  auto load_tab = [&](int k0, bf16x8 (&t)[MT][4]) {
+  auto load_tab = [&](int k0, V8 (&t)[MT][4]) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int64_t row = (int64_t)(16 * mt + m) * K2 + min(k0 + 8 * q, a.Lin_pad - 8);
-      t[mt][0] = *reinterpret_cast<const bf16x8*>(Ah + row);
-      t[mt][1] = *reinterpret_cast<const bf16x8*>(Al + row);
-      t[mt][2] = *reinterpret_cast<const bf16x8*>(Ah + row + a.Lin_pad);
-      t[mt][3] = *reinterpret_cast<const bf16x8*>(Al + row + a.Lin_pad);
+      t[mt][0] = *reinterpret_cast<const V8*>(Ah + row);
+      t[mt][1] = *reinterpret_cast<const V8*>(Al + row);
+      t[mt][2] = *reinterpret_cast<const V8*>(Ah + row + a.Lin_pad);
+      t[mt][3] = *reinterpret_cast<const V8*>(Al + row + a.Lin_pad);
     }
   };
   f32x4 acc[MT][NTW];
@@ -279,7 +283,7 @@ __global__ void __launch_bounds__(256) k_outer_fwd_stream_bf(OuterArgs a) {
 #pragma unroll
     for (int j = 0; j < NTW; ++j) acc[mt][j] = zero4();
   float4 xv[NL];
-  bf16x8 tb[MT][4];
+  V8 tb[MT][4];
   load_chunk(0, xv);
   load_tab(0, tb);
   const bool odd = (m & 1) != 0;
@@ -288,7 +292,7 @@ __global__ void __launch_bounds__(256) k_outer_fwd_stream_bf(OuterArgs a) {
 #pragma unroll
     for (int i = 0; i < NL; ++i)
       *reinterpret_cast<float4*>(s_x + xrow[i] * CBS + 4 * ((tid + 256 * i) % F4R)) = xv[i];
-    bf16x8 ct[MT][4];
+    V8 ct[MT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -309,18 +313,18 @@ __global__ void __launch_bounds__(256) k_outer_fwd_stream_bf(OuterArgs a) {
         xe[e] = odd ? pr.y : pr.x;
         xs[e] = odd ? pr.x : -pr.y;
       }
-      const bf16x8 bx = __builtin_bit_cast(
-          bf16x8, make_uint4(pack_bf16x2(xe[0], xe[1]), pack_bf16x2(xe[2], xe[3]),
-                             pack_bf16x2(xe[4], xe[5]), pack_bf16x2(xe[6], xe[7])));
-      const bf16x8 bs = __builtin_bit_cast(
-          bf16x8, make_uint4(pack_bf16x2(xs[0], xs[1]), pack_bf16x2(xs[2], xs[3]),
-                             pack_bf16x2(xs[4], xs[5]), pack_bf16x2(xs[6], xs[7])));
+      const V8 bx = __builtin_bit_cast(
+          V8, make_uint4(HT::pack2(xe[0], xe[1]), HT::pack2(xe[2], xe[3]),
+                         HT::pack2(xe[4], xe[5]), HT::pack2(xe[6], xe[7])));
+      const V8 bs = __builtin_bit_cast(
+          V8, make_uint4(HT::pack2(xs[0], xs[1]), HT::pack2(xs[2], xs[3]),
+                         HT::pack2(xs[4], xs[5]), HT::pack2(xs[6], xs[7])));
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        acc[mt][j] = mfma_bf16(ct[mt][0], bx, acc[mt][j]);
-        acc[mt][j] = mfma_bf16(ct[mt][1], bx, acc[mt][j]);
-        acc[mt][j] = mfma_bf16(ct[mt][2], bs, acc[mt][j]);
-        acc[mt][j] = mfma_bf16(ct[mt][3], bs, acc[mt][j]);
+        acc[mt][j] = HT::mfma(ct[mt][0], bx, acc[mt][j]);
+        acc[mt][j] = HT::mfma(ct[mt][1], bx, acc[mt][j]);
+        acc[mt][j] = HT::mfma(ct[mt][2], bs, acc[mt][j]);
+        acc[mt][j] = HT::mfma(ct[mt][3], bs, acc[mt][j]);
       }
     }
     __syncthreads();
@@ -345,8 +349,11 @@ __global__ void __launch_bounds__(256) k_outer_fwd_stream_bf(OuterArgs a) {
 // N-tiles w NTW .. w NTW + NTW - 1 and stores each finished tile.  Operands as in the streaming
 // forward transform (fp32 16x16x4 with K-slot q <-> row 4 q + ks of a 16-row group; bf16
 // 16x16x32 with K-slot (q, e) <-> row 8 q + e, the table as its hi + lo pair).
-template <bool BF, int NTW>
+template <int H, int NTW>
 __global__ void __launch_bounds__(256) k_outer_inv_stream(OuterArgs a) {
+  constexpr bool BF = H != 0;  // half operands (bfloat16 or IEEE half)
+  using HT = HalfOf<H>;
+  using V8 = typename HT::v8;
   constexpr int CB = 64 * NTW;
   constexpr int CBS = CB + 4;
   constexpr int F4R = CB / 4;
@@ -405,10 +412,10 @@ __global__ void __launch_bounds__(256) k_outer_inv_stream(OuterArgs a) {
         auto ld = [&](const uint16_t* p) {
           uint4 v = *reinterpret_cast<const uint4*>(p);
           v.x &= km; v.y &= km; v.z &= km; v.w &= km;
-          return __builtin_bit_cast(bf16x8, v);
+          return __builtin_bit_cast(V8, v);
         };
-        const bf16x8 rh = ld(Ah + tc), rl = ld(Al + tc);
-        const bf16x8 ih = ld(Ah + a.Lin_pad + tc), il = ld(Al + a.Lin_pad + tc);
+        const V8 rh = ld(Ah + tc), rl = ld(Al + tc);
+        const V8 ih = ld(Ah + a.Lin_pad + tc), il = ld(Al + a.Lin_pad + tc);
         const int xr0 = min(k0 + 8 * q, a.Lin_pad - 8);
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
@@ -420,16 +427,16 @@ __global__ void __launch_bounds__(256) k_outer_inv_stream(OuterArgs a) {
             xe[e] = odd ? pr.y : pr.x;
             xs[e] = odd ? pr.x : -pr.y;
           }
-          const bf16x8 bx = __builtin_bit_cast(
-              bf16x8, make_uint4(pack_bf16x2(xe[0], xe[1]), pack_bf16x2(xe[2], xe[3]),
-                                 pack_bf16x2(xe[4], xe[5]), pack_bf16x2(xe[6], xe[7])));
-          const bf16x8 bs = __builtin_bit_cast(
-              bf16x8, make_uint4(pack_bf16x2(xs[0], xs[1]), pack_bf16x2(xs[2], xs[3]),
-                                 pack_bf16x2(xs[4], xs[5]), pack_bf16x2(xs[6], xs[7])));
-          acc[j] = mfma_bf16(rh, bx, acc[j]);
-          acc[j] = mfma_bf16(rl, bx, acc[j]);
-          acc[j] = mfma_bf16(ih, bs, acc[j]);
-          acc[j] = mfma_bf16(il, bs, acc[j]);
+          const V8 bx = __builtin_bit_cast(
+              V8, make_uint4(HT::pack2(xe[0], xe[1]), HT::pack2(xe[2], xe[3]),
+                             HT::pack2(xe[4], xe[5]), HT::pack2(xe[6], xe[7])));
+          const V8 bs = __builtin_bit_cast(
+              V8, make_uint4(HT::pack2(xs[0], xs[1]), HT::pack2(xs[2], xs[3]),
+                             HT::pack2(xs[4], xs[5]), HT::pack2(xs[6], xs[7])));
+          acc[j] = HT::mfma(rh, bx, acc[j]);
+          acc[j] = HT::mfma(rl, bx, acc[j]);
+          acc[j] = HT::mfma(ih, bs, acc[j]);
+          acc[j] = HT::mfma(il, bs, acc[j]);
         }
       }
     }
@@ -447,27 +454,31 @@ __global__ void __launch_bounds__(256) k_outer_inv_stream(OuterArgs a) {
   }
 }
 
-template <bool BF>
+template <int H>
 static hipError_t launch_inv_stream(int ntw, dim3 grid, size_t lds, const OuterArgs& a,
                                     hipStream_t s) {
   switch (ntw) {
-    case 1: hipLaunchKernelGGL((k_outer_inv_stream<BF, 1>), grid, dim3(256), lds, s, a); break;
-    case 2: hipLaunchKernelGGL((k_outer_inv_stream<BF, 2>), grid, dim3(256), lds, s, a); break;
-    case 3: hipLaunchKernelGGL((k_outer_inv_stream<BF, 3>), grid, dim3(256), lds, s, a); break;
-    case 4: hipLaunchKernelGGL((k_outer_inv_stream<BF, 4>), grid, dim3(256), lds, s, a); break;
-    case 5: hipLaunchKernelGGL((k_outer_inv_stream<BF, 5>), grid, dim3(256), lds, s, a); break;
-    default: hipLaunchKernelGGL((k_outer_inv_stream<BF, 6>), grid, dim3(256), lds, s, a); break;
+    case 1: hipLaunchKernelGGL((k_outer_inv_stream<H, 1>), grid, dim3(256), lds, s, a); break;
+    case 2: hipLaunchKernelGGL((k_outer_inv_stream<H, 2>), grid, dim3(256), lds, s, a); break;
+    case 3: hipLaunchKernelGGL((k_outer_inv_stream<H, 3>), grid, dim3(256), lds, s, a); break;
+    case 4: hipLaunchKernelGGL((k_outer_inv_stream<H, 4>), grid, dim3(256), lds, s, a); break;
+    case 5: hipLaunchKernelGGL((k_outer_inv_stream<H, 5>), grid, dim3(256), lds, s, a); break;
+    default: hipLaunchKernelGGL((k_outer_inv_stream<H, 6>), grid, dim3(256), lds, s, a); break;
   }
   return hipGetLastError();
 }
 
 template <int MT, int NTW>
-static hipError_t launch_stream_t(dim3 grid, const OuterArgs& a, bool bf, hipStream_t s) {
-  if (bf) {
-    if constexpr (NTW <= 6)
-      hipLaunchKernelGGL((k_outer_fwd_stream_bf<MT, NTW>), grid, dim3(256), 0, s, a);
-    else
+static hipError_t launch_stream_t(dim3 grid, const OuterArgs& a, int half, hipStream_t s) {
+  if (half) {
+    if constexpr (NTW <= 6) {
+      if (half == 2)
+        hipLaunchKernelGGL((k_outer_fwd_stream_bf<2, MT, NTW>), grid, dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((k_outer_fwd_stream_bf<1, MT, NTW>), grid, dim3(256), 0, s, a);
+    } else {
       return hipErrorInvalidValue;
+    }
   } else {
     hipLaunchKernelGGL((k_outer_fwd_stream<MT, NTW>), grid, dim3(256), 0, s, a);
   }
@@ -475,7 +486,7 @@ static hipError_t launch_stream_t(dim3 grid, const OuterArgs& a, bool bf, hipStr
 }
 
 template <int MT>
-static hipError_t launch_stream_mt(int ntw, dim3 grid, const OuterArgs& a, bool bf,
+static hipError_t launch_stream_mt(int ntw, dim3 grid, const OuterArgs& a, int bf,
                                    hipStream_t s) {
   switch (ntw) {
     case 1: return launch_stream_t<MT, 1>(grid, a, bf, s);
@@ -494,7 +505,7 @@ static hipError_t launch_stream_mt(int ntw, dim3 grid, const OuterArgs& a, bool 
   return hipErrorInvalidValue;
 }
 
-static hipError_t launch_outer_stream(int mt, int ntw, dim3 grid, const OuterArgs& a, bool bf,
+static hipError_t launch_outer_stream(int mt, int ntw, dim3 grid, const OuterArgs& a, int bf,
                                       hipStream_t s) {
   switch (mt) {
     case 1: return launch_stream_mt<1>(ntw, grid, a, bf, s);
@@ -543,8 +554,9 @@ hipError_t launch_outer_mfma(const fno_plan* p, int axis, int chans, bool inv, c
     const int cb = 64 * ntw;
     const size_t lds = sizeof(float) * (size_t)a.Lin_pad * (cb + 4);
     dim3 grid((unsigned)((a.post2 + cb - 1) / cb), (unsigned)pre);
-    return bf ? launch_inv_stream<true>(ntw, grid, lds, a, s)
-              : launch_inv_stream<false>(ntw, grid, lds, a, s);
+    return g.half == 2 ? launch_inv_stream<2>(ntw, grid, lds, a, s)
+           : g.half == 1 ? launch_inv_stream<1>(ntw, grid, lds, a, s)
+                         : launch_inv_stream<0>(ntw, grid, lds, a, s);
   }
   if (!inv && a.Lout_pad <= 64 && a.post2 % 4 == 0 && pre <= 65535) {
     // few kept rows, long K: stream the slab in column blocks of 64 NTW (as wide as the row
@@ -556,7 +568,7 @@ hipError_t launch_outer_mfma(const fno_plan* p, int axis, int chans, bool inv, c
     while (ntw > 1 && pre * ((a.post2 + 64 * ntw - 1) / (64 * ntw)) < 1024) --ntw;
     const int cb = 64 * ntw;
     dim3 grid((unsigned)((a.post2 + cb - 1) / cb), (unsigned)pre);
-    return launch_outer_stream(mt, ntw, grid, a, bf, s);
+    return launch_outer_stream(mt, ntw, grid, a, g.half, s);
   }
   const int KS = 2 * a.Lin_pad + (bf ? 8 : 4);
   const size_t col_bytes = (size_t)KS * (bf ? 2 : 4);
@@ -565,14 +577,18 @@ hipError_t launch_outer_mfma(const fno_plan* p, int axis, int chans, bool inv, c
   const int ct = 16 * nt;
   const size_t lds = (size_t)ct * col_bytes;
   dim3 grid((unsigned)pre, (unsigned)((a.post2 + ct - 1) / ct));
-  if (bf) {
-    if (nt == 4) hipLaunchKernelGGL((k_outer_mfma<true, 4>), grid, dim3(256), lds, s, a);
-    else if (nt == 2) hipLaunchKernelGGL((k_outer_mfma<true, 2>), grid, dim3(256), lds, s, a);
-    else hipLaunchKernelGGL((k_outer_mfma<true, 1>), grid, dim3(256), lds, s, a);
+  if (g.half == 2) {
+    if (nt == 4) hipLaunchKernelGGL((k_outer_mfma<2, 4>), grid, dim3(256), lds, s, a);
+    else if (nt == 2) hipLaunchKernelGGL((k_outer_mfma<2, 2>), grid, dim3(256), lds, s, a);
+    else hipLaunchKernelGGL((k_outer_mfma<2, 1>), grid, dim3(256), lds, s, a);
+  } else if (bf) {
+    if (nt == 4) hipLaunchKernelGGL((k_outer_mfma<1, 4>), grid, dim3(256), lds, s, a);
+    else if (nt == 2) hipLaunchKernelGGL((k_outer_mfma<1, 2>), grid, dim3(256), lds, s, a);
+    else hipLaunchKernelGGL((k_outer_mfma<1, 1>), grid, dim3(256), lds, s, a);
   } else {
-    if (nt == 4) hipLaunchKernelGGL((k_outer_mfma<false, 4>), grid, dim3(256), lds, s, a);
-    else if (nt == 2) hipLaunchKernelGGL((k_outer_mfma<false, 2>), grid, dim3(256), lds, s, a);
-    else hipLaunchKernelGGL((k_outer_mfma<false, 1>), grid, dim3(256), lds, s, a);
+    if (nt == 4) hipLaunchKernelGGL((k_outer_mfma<0, 4>), grid, dim3(256), lds, s, a);
+    else if (nt == 2) hipLaunchKernelGGL((k_outer_mfma<0, 2>), grid, dim3(256), lds, s, a);
+    else hipLaunchKernelGGL((k_outer_mfma<0, 1>), grid, dim3(256), lds, s, a);
   }
   return hipGetLastError();
 }

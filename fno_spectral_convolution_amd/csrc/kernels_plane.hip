@@ -32,10 +32,10 @@ struct PlaneArgs {
   int rows_per_chunk;
   const float* in0;
   const float* in1;
-  const void* t1;        // [Nb][jpad] f32, or bf16 bits
-  const void* f2;        // [4ma][Na] f32, or bf16 bits (hi)
-  const uint16_t* f2lo;  // bf16 residual of f2 (bf16 path)
-  const uint16_t* t1t;   // bf16 t1 transposed, [jpad][Nb]
+  const void* t1;        // [Nb][jpad] f32, or half bits (the plan's format)
+  const void* f2;        // [4ma][Na] f32, or half bits (hi)
+  const uint16_t* f2lo;  // half residual of f2 (half paths)
+  const uint16_t* t1t;   // half t1 transposed, [jpad][Nb]
   float2* out;           // [nch][planes][2ma][mb]
 };
 
@@ -64,8 +64,11 @@ __device__ __forceinline__ void combine_store(const float* s_x2, int jpad, int m
 }
 
 // bf16 operands, fp32 accumulation.  NB = Nb (multiple of 32, <= 512), NTJ = jpad / 16.
-template <int PIN, int NB, int NTJ>
+template <int PIN, int NB, int NTJ, int H>
 __global__ void __launch_bounds__(256) k_plane_bf16(PlaneArgs a) {
+  using HT = Half<H>;  // the plan's half format (bfloat16 or IEEE half)
+  using V8 = typename HT::v8;
+  using E = typename HT::elem;
   constexpr int SUB = 16 * (4 / NTJ);   // rows per sub-round (one M-tile per wave)
   constexpr int XS = NB + 8;            // LDS row stride (bf16 elements)
   constexpr int RS = 64 + 8;            // Rt row stride (bf16 elements)
@@ -91,14 +94,14 @@ __global__ void __launch_bounds__(256) k_plane_bf16(PlaneArgs a) {
   const int r_end = min(a.Na, r_begin + a.rows_per_chunk);
 
   // this wave's slice of T1: B[k][n] = T1[32 s + 8 q + e][16 jt + m]
-  bf16x8 tb[KS];
+  V8 tb[KS];
   {
     const uint16_t* t1 = static_cast<const uint16_t*>(a.t1);
 #pragma unroll
     for (int s = 0; s < KS; ++s)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        tb[s][e] = __builtin_bit_cast(__bf16, t1[(32 * s + 8 * q + e) * JP + 16 * jt + m]);
+        tb[s][e] = __builtin_bit_cast(E, t1[(32 * s + 8 * q + e) * JP + 16 * jt + m]);
   }
   f32x4 x2[2][NTJ];  // i-tiles wave and wave + 4
 #pragma unroll
@@ -131,8 +134,8 @@ __global__ void __launch_bounds__(256) k_plane_bf16(PlaneArgs a) {
       const int r = e / LPR, c4 = e % LPR;
       const float4 v = pre0[u], w = pre1[u];
       uint2 packed;
-      packed.x = pack_bf16x2(prologue<PIN>(v.x, w.x), prologue<PIN>(v.y, w.y));
-      packed.y = pack_bf16x2(prologue<PIN>(v.z, w.z), prologue<PIN>(v.w, w.w));
+      packed.x = HT::pack2(prologue<PIN>(v.x, w.x), prologue<PIN>(v.y, w.y));
+      packed.y = HT::pack2(prologue<PIN>(v.z, w.z), prologue<PIN>(v.w, w.w));
       *reinterpret_cast<uint2*>(s_x + r * XS + 4 * c4) = packed;
     }
   };
@@ -149,14 +152,14 @@ __global__ void __launch_bounds__(256) k_plane_bf16(PlaneArgs a) {
       f32x4 d = zero4();
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const bf16x8 av =
-            *reinterpret_cast<const bf16x8*>(s_x + (16 * mt + m) * XS + 32 * s + 8 * q);
-        d = mfma_bf16(av, tb[s], d);
+        const V8 av =
+            *reinterpret_cast<const V8*>(s_x + (16 * mt + m) * XS + 32 * s + 8 * q);
+        d = HT::mfma(av, tb[s], d);
       }
       // D rows 16 mt + 4 q + r, column 16 jt + m  ->  Rt[column][stage row]
       uint2 pk;
-      pk.x = pack_bf16x2(d[0], d[1]);
-      pk.y = pack_bf16x2(d[2], d[3]);
+      pk.x = HT::pack2(d[0], d[1]);
+      pk.y = HT::pack2(d[2], d[3]);
       *reinterpret_cast<uint2*>(s_rt + (16 * jt + m) * RS + sub + 16 * mt + 4 * q) = pk;
     }
     __syncthreads();
@@ -164,31 +167,31 @@ __global__ void __launch_bounds__(256) k_plane_bf16(PlaneArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int krow = 32 * ks + 8 * q;
-      bf16x8 bv[NTJ];
+      V8 bv[NTJ];
 #pragma unroll
       for (int v = 0; v < NTJ; ++v)
-        bv[v] = *reinterpret_cast<const bf16x8*>(s_rt + (16 * v + m) * RS + krow);
+        bv[v] = *reinterpret_cast<const V8*>(s_rt + (16 * v + m) * RS + krow);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int it = wave + 4 * u;
         if (it >= IT) break;
         const int64_t fo = (int64_t)(16 * it + m) * a.Na + r0 + krow;
-        bf16x8 ah, al;
+        V8 ah, al;
         if (r0 + krow + 8 <= r_end) {
-          ah = *reinterpret_cast<const bf16x8*>(f2 + fo);
-          al = *reinterpret_cast<const bf16x8*>(a.f2lo + fo);
+          ah = *reinterpret_cast<const V8*>(f2 + fo);
+          al = *reinterpret_cast<const V8*>(a.f2lo + fo);
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const bool in = r0 + krow + e < r_end;
-            ah[e] = __builtin_bit_cast(__bf16, in ? f2[fo + e] : (uint16_t)0);
-            al[e] = __builtin_bit_cast(__bf16, in ? a.f2lo[fo + e] : (uint16_t)0);
+            ah[e] = __builtin_bit_cast(E, in ? f2[fo + e] : (uint16_t)0);
+            al[e] = __builtin_bit_cast(E, in ? a.f2lo[fo + e] : (uint16_t)0);
           }
         }
 #pragma unroll
         for (int v = 0; v < NTJ; ++v) {
-          x2[u][v] = mfma_bf16(ah, bv[v], x2[u][v]);
-          x2[u][v] = mfma_bf16(al, bv[v], x2[u][v]);
+          x2[u][v] = HT::mfma(ah, bv[v], x2[u][v]);
+          x2[u][v] = HT::mfma(al, bv[v], x2[u][v]);
         }
       }
     }
@@ -355,8 +358,10 @@ __global__ void __launch_bounds__(256) k_plane_f32(PlaneArgs a) {
 // axis product runs, its tiles (F2 M-tile, column tile) spread over the 8 waves.  The loop is
 // straight-line: rows past the chunk are loaded from a clamped row and staged as zeros, and
 // the F2 fragments of a stage are loaded at its start.
-template <int PIN, int NB>
+template <int PIN, int NB, int H>
 __global__ void __launch_bounds__(512) k_plane_bf16_lds(PlaneArgs a) {
+  using HT = Half<H>;  // the plan's half format (bfloat16 or IEEE half)
+  using V8 = typename HT::v8;
   constexpr int NTJ = 4;
   constexpr int JP = 16 * NTJ;
   constexpr int SUB = 32;               // rows per sub-round (2 M-tiles)
@@ -402,7 +407,7 @@ __global__ void __launch_bounds__(512) k_plane_bf16_lds(PlaneArgs a) {
   f32x4 x2[NT2];
 #pragma unroll
   for (int k = 0; k < NT2; ++k) x2[k] = zero4();
-  bf16x8 fh[2], fl[2];  // this wave's F2 row tile, both K-steps of a stage (hi, lo)
+  V8 fh[2], fl[2];  // this wave's F2 row tile, both K-steps of a stage (hi, lo)
   auto load_sub = [&](int n, float4 (&d0)[NLD], float4 (&d1)[NLD]) {
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
@@ -432,8 +437,8 @@ __global__ void __launch_bounds__(512) k_plane_bf16_lds(PlaneArgs a) {
       const float o2 = __uint_as_float(__float_as_uint(prologue<PIN>(v.z, w.z)) & keep);
       const float o3 = __uint_as_float(__float_as_uint(prologue<PIN>(v.w, w.w)) & keep);
       uint2 packed;
-      packed.x = pack_bf16x2(o0, o1);
-      packed.y = pack_bf16x2(o2, o3);
+      packed.x = HT::pack2(o0, o1);
+      packed.y = HT::pack2(o2, o3);
       *reinterpret_cast<uint2*>(s_x + r * XS + 4 * c4) = packed;
     }
     if constexpr (decltype(first_tag)::value) {
@@ -445,8 +450,8 @@ __global__ void __launch_bounds__(512) k_plane_bf16_lds(PlaneArgs a) {
       for (int ks = 0; ks < 2; ++ks) {
         const int col = min(r0 + 32 * ks + 8 * q, a.Na - 8);
         const int64_t fo = (int64_t)(16 * it + m) * a.Na + col;
-        fh[ks] = *reinterpret_cast<const bf16x8*>(f2 + fo);
-        fl[ks] = *reinterpret_cast<const bf16x8*>(a.f2lo + fo);
+        fh[ks] = *reinterpret_cast<const V8*>(f2 + fo);
+        fl[ks] = *reinterpret_cast<const V8*>(a.f2lo + fo);
       }
     }
   };
@@ -460,14 +465,14 @@ __global__ void __launch_bounds__(512) k_plane_bf16_lds(PlaneArgs a) {
     f32x4 d = zero4();
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) {
-      const bf16x8 av = *reinterpret_cast<const bf16x8*>(s_x + (16 * mt + m) * XS + 32 * s2 + 8 * q);
-      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(s_t1 + (16 * jt + m) * XS + 32 * s2 + 8 * q);
-      d = mfma_bf16(av, bv, d);
+      const V8 av = *reinterpret_cast<const V8*>(s_x + (16 * mt + m) * XS + 32 * s2 + 8 * q);
+      const V8 bv = *reinterpret_cast<const V8*>(s_t1 + (16 * jt + m) * XS + 32 * s2 + 8 * q);
+      d = HT::mfma(av, bv, d);
     }
     // D rows 16 mt + 4 q + r (stage row SUB sr + ..), column 16 jt + m  ->  Rt[column][row]
     uint2 pk;
-    pk.x = pack_bf16x2(d[0], d[1]);
-    pk.y = pack_bf16x2(d[2], d[3]);
+    pk.x = HT::pack2(d[0], d[1]);
+    pk.y = HT::pack2(d[2], d[3]);
     *reinterpret_cast<uint2*>(s_rt + (16 * jt + m) * RS + SUB * sr + 16 * mt + 4 * q) = pk;
     if constexpr (decltype(last_tag)::value) {
       __syncthreads();  // Rt of the 64-row stage complete
@@ -477,9 +482,9 @@ __global__ void __launch_bounds__(512) k_plane_bf16_lds(PlaneArgs a) {
       for (int v = 0; v < NT2; ++v) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(s_rt + (16 * v + m) * RS + 32 * ks + 8 * q);
-          x2[v] = mfma_bf16(fh[ks], bv, x2[v]);
-          x2[v] = mfma_bf16(fl[ks], bv, x2[v]);
+          const V8 bv = *reinterpret_cast<const V8*>(s_rt + (16 * v + m) * RS + 32 * ks + 8 * q);
+          x2[v] = HT::mfma(fh[ks], bv, x2[v]);
+          x2[v] = HT::mfma(fl[ks], bv, x2[v]);
         }
       }
     }
@@ -535,10 +540,14 @@ bool plane_fast_ok(const fno_plan* p) {
 
 template <int PIN, int NB, int NTJ>
 static void launch_plane_t(const fno_plan* p, const PlaneArgs& a, dim3 grid, hipStream_t s) {
-  if (p->g.bf16 && NTJ == 4)
-    hipLaunchKernelGGL((k_plane_bf16_lds<PIN, NB>), grid, dim3(512), 0, s, a);
+  if (p->g.half == 2 && NTJ == 4)
+    hipLaunchKernelGGL((k_plane_bf16_lds<PIN, NB, 2>), grid, dim3(512), 0, s, a);
+  else if (p->g.half == 2)
+    hipLaunchKernelGGL((k_plane_bf16<PIN, NB, NTJ, 2>), grid, dim3(256), 0, s, a);
+  else if (p->g.bf16 && NTJ == 4)
+    hipLaunchKernelGGL((k_plane_bf16_lds<PIN, NB, 1>), grid, dim3(512), 0, s, a);
   else if (p->g.bf16)
-    hipLaunchKernelGGL((k_plane_bf16<PIN, NB, NTJ>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_plane_bf16<PIN, NB, NTJ, 1>), grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((k_plane_f32<PIN, NB, NTJ>), grid, dim3(256), 0, s, a);
 }

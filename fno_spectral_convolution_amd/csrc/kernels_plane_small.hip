@@ -17,8 +17,8 @@
 //                   mixed path: 16x16x32 bf16 MFMAs taking two row tiles' fragments per K-step,
 //                   F2 as its bf16 hi + lo pair (two products).
 //   combine       : X2 goes to a per-wave LDS tile and is folded into the complex spectrum.
-// On the mixed path the pre-activated input, T1 and R are rounded to bfloat16 (the
-// half-precision transform of the mixed-precision neural-operator page, "Tiivistelmä").
+// On the half paths the pre-activated input, T1 and R are rounded to bfloat16 or IEEE half
+// (the half-precision transform of the mixed-precision neural-operator page, "Tiivistelmä").
 #include "fno_internal.h"
 #include "mfma.h"
 #include "pointwise.h"
@@ -31,9 +31,9 @@ struct SmallPlaneArgs {
   const float* in0;
   const float* in1;
   const float* t1;       // [Nb][jpad] f32
-  const uint16_t* t1bf;  // [Nb][jpad] bf16 bits
+  const uint16_t* t1bf;  // [Nb][jpad] half bits (the plan's format)
   const float* f2;       // [4 ma][Na] f32
-  const uint16_t* f2bf;  // [4 ma][Na] bf16 bits of f2, and of its residual
+  const uint16_t* f2bf;  // [4 ma][Na] half bits of f2, and of its residual
   const uint16_t* f2lo;
   float2* out;           // [planes][2 ma][mb]
 };
@@ -45,13 +45,13 @@ __device__ __forceinline__ float small_prologue(float v, float w) {
   return v;
 }
 
-__device__ __forceinline__ float round_bf16(float v) {
-  return __uint_as_float((uint32_t)bf16_bits(v) << 16);
-}
-
 // MT = Na / 16 row tiles, NTJ = jpad / 16 column tiles
-template <int PIN, bool BF, int MT, int NTJ>
+template <int PIN, int H, int MT, int NTJ>
 __global__ void __launch_bounds__(256) k_plane_small(SmallPlaneArgs a) {
+  constexpr bool BF = H != 0;  // half operands (bfloat16 or IEEE half)
+  using HT = HalfOf<H>;
+  using V8 = typename HT::v8;
+  using E = typename HT::elem;
   constexpr int JP = 16 * NTJ;
   constexpr bool TWO = PIN == PLANE_GELU_GRAD;
   extern __shared__ __attribute__((aligned(16))) float s_sp[];
@@ -79,17 +79,17 @@ __global__ void __launch_bounds__(256) k_plane_small(SmallPlaneArgs a) {
   }
   // T1 fragments: B[k = 8 q + slot][n = 16 nt + m]; zero past Nb
   float t1r[NTJ][8];
-  bf16x8 t1b[NTJ];
+  V8 t1b[NTJ];
 #pragma unroll
   for (int nt = 0; nt < NTJ; ++nt)
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int c = 8 * q + s;
       const int cc = min(c, a.Nb - 1);
-      const float v = BF ? __uint_as_float((uint32_t)a.t1bf[cc * JP + 16 * nt + m] << 16)
+      const float v = BF ? HT::value(a.t1bf[cc * JP + 16 * nt + m])
                          : a.t1[cc * JP + 16 * nt + m];
       t1r[nt][s] = c < a.Nb ? v : 0.f;
-      t1b[nt][s] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(t1r[nt][s]) >> 16));
+      t1b[nt][s] = (E)t1r[nt][s];  // exact: t1r holds a half value (or zero)
     }
   __syncthreads();
   const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
@@ -130,20 +130,19 @@ __global__ void __launch_bounds__(256) k_plane_small(SmallPlaneArgs a) {
       for (int s = 0; s < 8; ++s) {
         const bool live = s < 4 ? live0 : live1;
         float v = small_prologue<PIN>(raw[s], rw[s]);
-        if (BF) v = round_bf16(v);
+        if (BF) v = round_half<H>(v);
         xv[s] = __uint_as_float(__float_as_uint(v) & (live ? 0xffffffffu : 0u));
       }
 #pragma unroll
       for (int nt = 0; nt < NTJ; ++nt) {
         f32x4 acc = zero4();
         if constexpr (BF) {
-          bf16x8 av;
+          V8 av;
 #pragma unroll
-          for (int s = 0; s < 8; ++s)
-            av[s] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(xv[s]) >> 16));
-          acc = mfma_bf16(av, t1b[nt], acc);
+          for (int s = 0; s < 8; ++s) av[s] = (E)xv[s];  // exact: already rounded
+          acc = HT::mfma(av, t1b[nt], acc);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[r] = round_bf16(acc[r]);
+          for (int r = 0; r < 4; ++r) acc[r] = round_half<H>(acc[r]);
         } else {
 #pragma unroll
           for (int s = 0; s < 8; ++s) acc = mfma_f32(xv[s], t1r[nt][s], acc);
@@ -188,17 +187,17 @@ __global__ void __launch_bounds__(256) k_plane_small(SmallPlaneArgs a) {
             h1 = *reinterpret_cast<const uint2*>(fh + 32 * pp + 16);
             l1 = *reinterpret_cast<const uint2*>(fl + 32 * pp + 16);
           }
-          const bf16x8 ah = __builtin_bit_cast(bf16x8, make_uint4(h0.x, h0.y, h1.x, h1.y));
-          const bf16x8 al = __builtin_bit_cast(bf16x8, make_uint4(l0.x, l0.y, l1.x, l1.y));
+          const V8 ah = __builtin_bit_cast(V8, make_uint4(h0.x, h0.y, h1.x, h1.y));
+          const V8 al = __builtin_bit_cast(V8, make_uint4(l0.x, l0.y, l1.x, l1.y));
 #pragma unroll
           for (int nt = 0; nt < NTJ; ++nt) {
-            const uint32_t b0 = pack_bf16x2(d[t0][nt][0], d[t0][nt][1]);
-            const uint32_t b1 = pack_bf16x2(d[t0][nt][2], d[t0][nt][3]);
-            const uint32_t b2 = 2 * pp + 1 < MT ? pack_bf16x2(d[t1][nt][0], d[t1][nt][1]) : 0u;
-            const uint32_t b3 = 2 * pp + 1 < MT ? pack_bf16x2(d[t1][nt][2], d[t1][nt][3]) : 0u;
-            const bf16x8 bv = __builtin_bit_cast(bf16x8, make_uint4(b0, b1, b2, b3));
-            x2[nt] = mfma_bf16(ah, bv, x2[nt]);
-            x2[nt] = mfma_bf16(al, bv, x2[nt]);
+            const uint32_t b0 = HT::pack2(d[t0][nt][0], d[t0][nt][1]);
+            const uint32_t b1 = HT::pack2(d[t0][nt][2], d[t0][nt][3]);
+            const uint32_t b2 = 2 * pp + 1 < MT ? HT::pack2(d[t1][nt][0], d[t1][nt][1]) : 0u;
+            const uint32_t b3 = 2 * pp + 1 < MT ? HT::pack2(d[t1][nt][2], d[t1][nt][3]) : 0u;
+            const V8 bv = __builtin_bit_cast(V8, make_uint4(b0, b1, b2, b3));
+            x2[nt] = HT::mfma(ah, bv, x2[nt]);
+            x2[nt] = HT::mfma(al, bv, x2[nt]);
           }
         }
       }
@@ -233,40 +232,42 @@ bool plane_small_ok(const fno_plan* p) {
   return true;
 }
 
-template <int PIN, bool BF, int MT>
+template <int PIN, int H, int MT>
 static void launch_small_t(const fno_plan* p, const SmallPlaneArgs& a, hipStream_t s) {
   const int jp = p->jpad;
-  const size_t lds = sizeof(float) * (4 * a.ma * (a.Na + (BF ? 8 : 4)) + 4 * (4 * a.ma) * jp);
+  const size_t lds = sizeof(float) * (4 * a.ma * (a.Na + (H != 0 ? 8 : 4)) + 4 * (4 * a.ma) * jp);
   const int64_t want = (a.planes + 3) / 4;
   const unsigned grid = (unsigned)(want < 2048 ? want : 2048);
   if (lds > 65536) {  // wide row spectra need more than the default dynamic LDS limit
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_plane_small<PIN, BF, MT, 1>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_plane_small<PIN, H, MT, 1>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_plane_small<PIN, BF, MT, 2>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_plane_small<PIN, H, MT, 2>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   }
   if (jp == 16)
-    hipLaunchKernelGGL((k_plane_small<PIN, BF, MT, 1>), dim3(grid), dim3(256), lds, s, a);
+    hipLaunchKernelGGL((k_plane_small<PIN, H, MT, 1>), dim3(grid), dim3(256), lds, s, a);
   else
-    hipLaunchKernelGGL((k_plane_small<PIN, BF, MT, 2>), dim3(grid), dim3(256), lds, s, a);
+    hipLaunchKernelGGL((k_plane_small<PIN, H, MT, 2>), dim3(grid), dim3(256), lds, s, a);
 }
 
-template <int PIN, bool BF>
+template <int PIN, int H>
 static void launch_small_mt(const fno_plan* p, const SmallPlaneArgs& a, hipStream_t s) {
   switch (a.Na) {
-    case 16: launch_small_t<PIN, BF, 1>(p, a, s); break;
-    case 32: launch_small_t<PIN, BF, 2>(p, a, s); break;
-    case 64: launch_small_t<PIN, BF, 4>(p, a, s); break;
-    default: launch_small_t<PIN, BF, 8>(p, a, s); break;
+    case 16: launch_small_t<PIN, H, 1>(p, a, s); break;
+    case 32: launch_small_t<PIN, H, 2>(p, a, s); break;
+    case 64: launch_small_t<PIN, H, 4>(p, a, s); break;
+    default: launch_small_t<PIN, H, 8>(p, a, s); break;
   }
 }
 
 template <int PIN>
 static void launch_small_pin(const fno_plan* p, const SmallPlaneArgs& a, hipStream_t s) {
-  if (p->g.bf16)
-    launch_small_mt<PIN, true>(p, a, s);
+  if (p->g.half == 2)
+    launch_small_mt<PIN, 2>(p, a, s);
+  else if (p->g.half == 1)
+    launch_small_mt<PIN, 1>(p, a, s);
   else
-    launch_small_mt<PIN, false>(p, a, s);
+    launch_small_mt<PIN, 0>(p, a, s);
 }
 
 hipError_t launch_plane_small(const fno_plan* p, int plane_in, int chans, const float* in0,

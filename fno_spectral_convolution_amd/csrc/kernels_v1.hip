@@ -5,10 +5,11 @@
 // page, "Proposed method").  Twiddles come from per-axis root tables (cos, sin)(2 pi t / N)
 // built on the host in float64; the index k*p is reduced modulo N in integers.
 //
-// Mixed path (bf16 operands, fp32 accumulation -- mixed-precision neural-operator page,
-// "Tiivistelmä"): every operand of a transform or mix product (pre-activated input,
-// twiddle, spectrum value, weight) is rounded to bfloat16 (nearest-even) before the
-// multiply; products and sums are float32.
+// Half paths (bfloat16 or IEEE-half operands, fp32 accumulation -- mixed-precision
+// neural-operator page, "Tiivistelmä"): every operand of a transform or mix product
+// (pre-activated input, twiddle, spectrum value, weight) is rounded to the plan's format
+// (nearest-even) before the multiply; products and sums are float32.  IEEE-half plans scale each
+// transform by 1/sqrt(N_j) in both directions (Geom::sc), as their tables do.
 #include "fno_internal.h"
 
 #include <math.h>
@@ -21,7 +22,10 @@ __device__ __forceinline__ float bf16r(float v) {
   return __uint_as_float(u & 0xffff0000u);
 }
 
-__device__ __forceinline__ float opnd(float v, bool bf) { return bf ? bf16r(v) : v; }
+// an operand in the plan's arithmetic: 0 fp32, 1 bfloat16, 2 IEEE half (nearest-even)
+__device__ __forceinline__ float opnd(float v, int half) {
+  return half == 2 ? (float)(_Float16)v : (half == 1 ? bf16r(v) : v);
+}
 
 __device__ __forceinline__ float gelu_f(float z) {
   return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
@@ -57,7 +61,7 @@ k_plane_fwd(Geom g, const float2* __restrict__ root_b, const float2* __restrict_
   const int tid = threadIdx.x;
   const int64_t plane = blockIdx.x;
   const int chunk = blockIdx.y;
-  const bool bf = g.bf16;
+  const int bf = g.half;
   for (int t = tid; t < Nb; t += kPlaneThreads) s_rb[t] = root_b[t];
   for (int t = tid; t < Na; t += kPlaneThreads) s_ra[t] = root_a[t];
   const int r_begin = chunk * rows_per_chunk;
@@ -118,7 +122,10 @@ k_plane_fwd(Geom g, const float2* __restrict__ root_b, const float2* __restrict_
 #pragma unroll
   for (int q = 0; q < kPlaneMaxAcc; ++q) {
     const int o = tid + q * kPlaneThreads;
-    if (o < nout) dst[o] = acc[q];
+    if (o < nout) {
+      const float sc = g.sc[g.d - 2] * g.sc[g.d - 1];
+      dst[o] = make_float2(acc[q].x * sc, acc[q].y * sc);
+    }
   }
 }
 
@@ -182,7 +189,7 @@ hipError_t launch_reduce_parts(const float2* in, int nparts, int64_t part_stride
 template <bool INV>
 __global__ void k_outer(const float2* __restrict__ root, int N, int m, int64_t pre,
                         int64_t post, const float2* __restrict__ in, float2* __restrict__ out,
-                        bool bf) {
+                        int bf, float sc) {
   const int Lin = INV ? 2 * m : N;
   const int Lout = INV ? N : 2 * m;
   const int64_t total = pre * Lout * post;
@@ -208,7 +215,7 @@ __global__ void k_outer(const float2* __restrict__ root, int N, int m, int64_t p
       im += vi * w.x - vr * w.y;
     }
   }
-  out[i] = make_float2(re, im);
+  out[i] = make_float2(re * sc, im * sc);
 }
 
 static void outer_shape(const fno_plan* p, int axis, int chans, bool inv, int64_t* pre,
@@ -236,7 +243,7 @@ hipError_t launch_outer_fwd(const fno_plan* p, int axis, int chans, const float2
   const int64_t total = pre * 2 * g.M[axis] * post;
   const float2* root = g.bf16 ? p->t.root_bf[axis] : p->t.root[axis];
   hipLaunchKernelGGL(k_outer<false>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
-                     root, g.N[axis], g.M[axis], pre, post, in, out, g.bf16);
+                     root, g.N[axis], g.M[axis], pre, post, in, out, g.half, g.sc[axis]);
   return hipGetLastError();
 }
 
@@ -249,7 +256,7 @@ hipError_t launch_outer_inv(const fno_plan* p, int axis, int chans, const float2
   const int64_t total = pre * (int64_t)g.N[axis] * post;
   const float2* root = g.bf16 ? p->t.root_bf[axis] : p->t.root[axis];
   hipLaunchKernelGGL(k_outer<true>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
-                     root, g.N[axis], g.M[axis], pre, post, in, out, g.bf16);
+                     root, g.N[axis], g.M[axis], pre, post, in, out, g.half, g.sc[axis]);
   return hipGetLastError();
 }
 
@@ -286,7 +293,7 @@ k_epilogue_fwd(Geom g, int mode, bool gelu, const float2* __restrict__ root_b,
   const int64_t line = p / Nb;
   const int pb = (int)(p - line * Nb);
   const int64_t lines = P / Nb;
-  const bool bf = g.bf16;
+  const int bf = g.half;
   for (int o = 0; o < Cout; ++o) {
     const float2* tr = T + (((int64_t)b * Cout + o) * lines + line) * mb;
     float ys = 0.f;
@@ -299,7 +306,7 @@ k_epilogue_fwd(Geom g, int mode, bool gelu, const float2* __restrict__ root_b,
       idx += pb;
       if (idx >= Nb) idx -= Nb;
     }
-    float z = ys * g.inv_ntot;
+    float z = ys * (g.half == 2 ? g.sc[g.d - 1] * g.inv_gain[0] : g.inv_ntot);
     if (block) {
       float acc = s_bias[o];
       const float* wr = s_wb + o * Cin;
@@ -352,7 +359,7 @@ k_epilogue_bwd(Geom g, int mode, bool gelu, bool tanh_pre, const float2* __restr
   const int b = blockIdx.y;
   const int64_t P = g.P;
   const bool block = (mode == EPI_BLOCK);
-  const bool bf = g.bf16;
+  const int bf = g.half;
   for (int t = tid; t < Nb; t += kEbThreads) s_rb[t] = root_b[t];
   if (block)
     for (int t = tid; t < Cout * Cin; t += kEbThreads) s_wb[t] = wb[t];
@@ -397,6 +404,7 @@ k_epilogue_bwd(Geom g, int mode, bool gelu, bool tanh_pre, const float2* __restr
           idx += pb;
           if (idx >= Nb) idx -= Nb;
         }
+        gs *= g.sc[g.d - 1] * g.inv_gain[1];  // 1 except on IEEE-half plans
         const int64_t off = ((int64_t)b * Cin + ci) * P + p;
         if (tanh_pre) {
           const float xv = block ? s_x[ci * kEbThreads + tid] : x[off];
@@ -508,10 +516,10 @@ hipError_t launch_bypass_grad_finish(const fno_plan* p, const float* red_part, f
 // ------------------------------------------------------------------------------------------
 // MSE: g = 2 (y - t) / n; per-group partial sums in double, then one fixed-order finish.
 __global__ void k_mse_part(int64_t n, const float* __restrict__ y, const float* __restrict__ t,
-                           float* __restrict__ g, double* __restrict__ part) {
+                           float* __restrict__ g, float grad_scale, double* __restrict__ part) {
   __shared__ double s_red[256];
   const int tid = threadIdx.x;
-  const float sc = (float)(2.0 / (double)n);
+  const float sc = (float)(2.0 * (double)grad_scale / (double)n);
   double a = 0.0;
   const int64_t n4 = n / 4;
   const float4* y4 = reinterpret_cast<const float4*>(y);
@@ -553,8 +561,8 @@ __global__ void k_mse_finish(int64_t n, int nparts, const double* __restrict__ p
 }
 
 hipError_t launch_mse(int64_t n, const float* y, const float* t, float* g, float* loss,
-                      double* part, int nparts, hipStream_t s) {
-  hipLaunchKernelGGL(k_mse_part, dim3(nparts), dim3(256), 0, s, n, y, t, g, part);
+                      float grad_scale, double* part, int nparts, hipStream_t s) {
+  hipLaunchKernelGGL(k_mse_part, dim3(nparts), dim3(256), 0, s, n, y, t, g, grad_scale, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !loss) return e;
   hipLaunchKernelGGL(k_mse_finish, dim3(1), dim3(256), 0, s, n, nparts, part, loss);

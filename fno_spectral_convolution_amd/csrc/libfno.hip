@@ -10,6 +10,7 @@
 
 #include <mutex>
 #include <new>
+#include <cmath>
 #include <string>
 #include <vector>
 
@@ -68,6 +69,25 @@ double bf16_value_host(uint16_t bits) {
   return (double)f;
 }
 
+// float64 -> IEEE half bits, round to nearest even (one rounding)
+uint16_t f16_bits_host(double v) {
+  const _Float16 h = (_Float16)v;
+  uint16_t b;
+  memcpy(&b, &h, 2);
+  return b;
+}
+
+double f16_value_host(uint16_t bits) {
+  _Float16 h;
+  memcpy(&h, &bits, 2);
+  return (double)h;
+}
+
+// the plan's half format: bfloat16 or IEEE half
+uint16_t half_bits_host(double v, bool f16) { return f16 ? f16_bits_host(v) : bf16_bits_host(v); }
+double half_value_host(uint16_t b, bool f16) { return f16 ? f16_value_host(b) : bf16_value_host(b); }
+float round_half_host(float v, bool f16) { return (float)half_value_host(half_bits_host(v, f16), f16); }
+
 }  // namespace
 
 extern "C" {
@@ -112,8 +132,6 @@ fno_status fno_plan_validate(const fno_plan_desc* d) {
                   (long long)d->modes[j], (long long)mmax);
   }
   // limits of the kernels (valid FNO shapes beyond them are UNSUPPORTED)
-  if (d->spectral_dtype == FNO_DTYPE_F16)
-    return fail(FNO_ERR_UNSUPPORTED, "fp16 spectral path not implemented");
   if (d->c_in > 64 || d->c_out > 64)
     return fail(FNO_ERR_UNSUPPORTED, "channels > 64 not implemented");
   const int64_t na = d->n[nd - 2], nb = d->n[nd - 1];
@@ -174,7 +192,20 @@ fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out) {
   for (int j = 0; j < g.d - 2; ++j) g.O *= g.N[j];
   g.ncorner = 1 << (g.d - 1);
   g.inv_ntot = (float)(1.0 / (double)g.P);
-  g.bf16 = desc->spectral_dtype == FNO_DTYPE_BF16;
+  g.half = desc->spectral_dtype == FNO_DTYPE_BF16 ? 1 : (desc->spectral_dtype == FNO_DTYPE_F16 ? 2 : 0);
+  g.bf16 = g.half != 0;
+  const bool f16 = g.half == 2;
+  for (int j = 0; j < fno::kMaxDims; ++j)
+    g.sc[j] = (f16 && j < g.d) ? (float)(1.0 / sqrt((double)g.N[j])) : 1.0f;
+  g.adj_scale = f16 ? 1.0f : g.inv_ntot;
+  {
+    // the power of two nearest to v (v >= 1)
+    auto pow2_near = [](double v) { return (float)std::ldexp(1.0, (int)std::lround(std::log2(v))); };
+    g.mix_gain[0] = f16 ? pow2_near(std::sqrt((double)g.Cin) * g.Cout) : 1.0f;
+    g.mix_gain[1] = f16 ? pow2_near(std::sqrt((double)g.Cout) * g.Cin) : 1.0f;
+    g.inv_gain[0] = 1.0f / g.mix_gain[0];
+    g.inv_gain[1] = 1.0f / g.mix_gain[1];
+  }
   const int cmax = g.Cin > g.Cout ? g.Cin : g.Cout;
 
   p->kpad = (2 * g.mb + 31) / 32 * 32;
@@ -300,7 +331,7 @@ fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out) {
       const double ang = 2.0 * M_PI * (double)t / (double)g.N[j];
       const float c = (float)cos(ang), s = (float)sin(ang);
       r[t] = make_float2(c, s);
-      rb[t] = make_float2(round_bf16(c), round_bf16(s));
+      rb[t] = make_float2(round_half_host(c, f16), round_half_host(s, f16));
     }
   }
   {
@@ -309,7 +340,12 @@ fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out) {
     float* gu = reinterpret_cast<float*>(host.data() + gt_unit_off);
     uint16_t* gfb = reinterpret_cast<uint16_t*>(host.data() + gt_fwd_bf_off);
     uint16_t* gub = reinterpret_cast<uint16_t*>(host.data() + gt_unit_bf_off);
-    const double inv_ntot = 1.0 / (double)g.P;
+    // g / Ntot on unscaled plans; with 1/sqrt(N_j) tables both ways (IEEE half) the last-axis
+    // inverse keeps only its own 1/sqrt(Nb), and its half tables also divide out the mix gain
+    // (the last inverse stage of the forward and of the input gradient)
+    const double inv_ntot = f16 ? 1.0 / sqrt((double)g.Nb) : 1.0 / (double)g.P;
+    const double usc = f16 ? 1.0 / sqrt((double)g.Nb) : 1.0;
+    const double hf = g.inv_gain[0], hu = g.inv_gain[1];
     for (int pt = 0; pt < g.Nb; ++pt)
       for (int k = 0; k < p->kpad / 2; ++k) {
         double c = 0.0, sn = 0.0, gam = 0.0;
@@ -322,12 +358,12 @@ fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out) {
         const size_t e = (size_t)pt * p->kpad + 2 * k;
         gf[e] = (float)(gam * inv_ntot * c);
         gf[e + 1] = (float)(-gam * inv_ntot * sn);
-        gu[e] = (float)c;
-        gu[e + 1] = (float)(-sn);
-        gfb[e] = bf16_bits_host(gam * inv_ntot * c);
-        gfb[e + 1] = bf16_bits_host(-gam * inv_ntot * sn);
-        gub[e] = bf16_bits_host(c);
-        gub[e + 1] = bf16_bits_host(-sn);
+        gu[e] = (float)(usc * c);
+        gu[e + 1] = (float)(-usc * sn);
+        gfb[e] = half_bits_host(hf * gam * inv_ntot * c, f16);
+        gfb[e + 1] = half_bits_host(-hf * gam * inv_ntot * sn, f16);
+        gub[e] = half_bits_host(hu * usc * c, f16);
+        gub[e + 1] = half_bits_host(-hu * usc * sn, f16);
       }
   }
   {
@@ -340,16 +376,16 @@ fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out) {
         double cv = 0.0, sv = 0.0;
         if (k < g.mb) {
           const double ang = 2.0 * M_PI * (double)(((int64_t)k * c) % g.Nb) / (double)g.Nb;
-          cv = cos(ang);
-          sv = -sin(ang);
+          cv = g.sc[g.d - 1] * cos(ang);
+          sv = -g.sc[g.d - 1] * sin(ang);
         }
         const size_t e = (size_t)c * p->jpad + 2 * k;
         t1[e] = (float)cv;
         t1[e + 1] = (float)sv;
-        t1b[e] = bf16_bits_host(cv);
-        t1b[e + 1] = bf16_bits_host(sv);
-        t1bt[(size_t)(2 * k) * g.Nb + c] = bf16_bits_host(cv);
-        t1bt[(size_t)(2 * k + 1) * g.Nb + c] = bf16_bits_host(sv);
+        t1b[e] = half_bits_host(cv, f16);
+        t1b[e + 1] = half_bits_host(sv, f16);
+        t1bt[(size_t)(2 * k) * g.Nb + c] = half_bits_host(cv, f16);
+        t1bt[(size_t)(2 * k + 1) * g.Nb + c] = half_bits_host(sv, f16);
       }
     float* f2 = reinterpret_cast<float*>(host.data() + f2_off);
     uint16_t* f2b = reinterpret_cast<uint16_t*>(host.data() + f2_bf_off);
@@ -359,22 +395,25 @@ fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out) {
       const int ka = sidx < g.ma ? sidx : g.Na - 2 * g.ma + sidx;
       for (int row = 0; row < g.Na; ++row) {
         const double ang = 2.0 * M_PI * (double)(((int64_t)ka * row) % g.Na) / (double)g.Na;
-        const double v = i < 2 * g.ma ? cos(ang) : sin(ang);
+        const double v = g.sc[g.d - 2] * (i < 2 * g.ma ? cos(ang) : sin(ang));
         const size_t e = (size_t)i * g.Na + row;
         f2[e] = (float)v;
-        f2b[e] = bf16_bits_host(v);
-        f2l[e] = bf16_bits_host(v - bf16_value_host(f2b[e]));
+        f2b[e] = half_bits_host(v, f16);
+        f2l[e] = half_bits_host(v - half_value_host(f2b[e], f16), f16);
       }
     }
   }
   for (int j = 0; j <= g.d - 2; ++j) {
     const int N = g.N[j], m = g.M[j];
     const int Np = p16(N), Mp = p16(2 * m);
-    auto put = [&](size_t* off, size_t e, double v) {
+    const double scj = g.sc[j];  // 1/sqrt(N_j) on IEEE-half plans, both directions
+    auto put = [&](size_t* off, size_t e, double v0) {
+      const double v = scj * v0;
       reinterpret_cast<float*>(host.data() + off[0])[e] = (float)v;
-      const uint16_t hi = bf16_bits_host(v);
+      const uint16_t hi = half_bits_host(v, f16);
       reinterpret_cast<uint16_t*>(host.data() + off[1])[e] = hi;
-      reinterpret_cast<uint16_t*>(host.data() + off[2])[e] = bf16_bits_host(v - bf16_value_host(hi));
+      reinterpret_cast<uint16_t*>(host.data() + off[2])[e] =
+          half_bits_host(v - half_value_host(hi, f16), f16);
     };
     for (int pt = 0; pt < N; ++pt)
       for (int sidx = 0; sidx < 2 * m; ++sidx) {
@@ -836,7 +875,15 @@ fno_status fno_mse_workspace_bytes(int64_t n, size_t* bytes) {
 
 fno_status fno_mse_grad(int64_t n, const float* y, const float* t, float* grad, float* loss,
                         void* ws, size_t ws_bytes, void* stream) {
+  return fno_mse_grad_scaled(n, y, t, grad, loss, 1.0f, ws, ws_bytes, stream);
+}
+
+fno_status fno_mse_grad_scaled(int64_t n, const float* y, const float* t, float* grad,
+                               float* loss, float grad_scale, void* ws, size_t ws_bytes,
+                               void* stream) {
   if (n < 1) return fail(FNO_ERR_INVALID_ARGUMENT, "n < 1");
+  if (!(grad_scale > 0.0f) || !std::isfinite(grad_scale))
+    return fail(FNO_ERR_INVALID_ARGUMENT, "grad_scale must be finite and > 0");
   REQ(y, "y");
   REQ(t, "t");
   REQ(grad, "grad");
@@ -844,7 +891,7 @@ fno_status fno_mse_grad(int64_t n, const float* y, const float* t, float* grad, 
   const int parts = mse_parts(n);
   if (ws_bytes < sizeof(double) * (size_t)parts)
     return fail(FNO_ERR_INVALID_ARGUMENT, "workspace too small");
-  LAUNCH("mse", static_cast<hipStream_t>(stream), fno::launch_mse(n, y, t, grad, loss, static_cast<double*>(ws), parts,
+  LAUNCH("mse", static_cast<hipStream_t>(stream), fno::launch_mse(n, y, t, grad, loss, grad_scale, static_cast<double*>(ws), parts,
                          static_cast<hipStream_t>(stream)));
   return FNO_OK;
 }

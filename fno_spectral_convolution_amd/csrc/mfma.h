@@ -1,7 +1,7 @@
 // Thin wrappers over the gfx950 matrix-core builtins used by libfno, with their lane layouts.
 //
 // 16x16x4 f32  : A lane l holds A[l%16][l/16];            B holds B[l/16][l%16]
-// 16x16x32 bf16: A lane l holds A[l%16][8*(l/16) + e];    B holds B[8*(l/16) + e][l%16]
+// 16x16x32 bf16 / f16: A lane l holds A[l%16][8*(l/16) + e];    B holds B[8*(l/16) + e][l%16]
 // 16x16 result : lane l, register r holds D[4*(l/16) + r][l%16]
 // (checked on the device against a host matrix product for these exact builtins)
 #pragma once
@@ -50,6 +50,60 @@ __device__ __forceinline__ bf16x8 to_bf16x8(float4 a, float4 b) {
   r[6] = (__bf16)b.z;
   r[7] = (__bf16)b.w;
   return r;
+}
+
+// ---- half-precision operand formats ------------------------------------------------------
+// H = 1: bfloat16 (fp32's exponent range, 8-bit significand); H = 2: IEEE half (5-bit
+// exponent, 11-bit significand).  Operands travel as 16-bit patterns; an MFMA operand of 8
+// values is Half<H>::v8.  Every conversion rounds to nearest even.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+template <int H>
+struct Half;
+
+template <>
+struct Half<1> {
+  using elem = __bf16;
+  using v8 = bf16x8;
+  static __device__ __forceinline__ f32x4 mfma(v8 a, v8 b, f32x4 c) { return mfma_bf16(a, b, c); }
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2(a, b); }
+  static __device__ __forceinline__ uint16_t bits(float v) { return bf16_bits(v); }
+  static __device__ __forceinline__ float value(uint16_t h) {
+    return __uint_as_float((uint32_t)h << 16);
+  }
+};
+
+template <>
+struct Half<2> {
+  using elem = _Float16;
+  using v8 = f16x8;
+  static __device__ __forceinline__ f32x4 mfma(v8 a, v8 b, f32x4 c) { return mfma_f16(a, b, c); }
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    const f32x2_v v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_v));
+  }
+  static __device__ __forceinline__ uint16_t bits(float v) {
+    return __builtin_bit_cast(uint16_t, (_Float16)v);
+  }
+  static __device__ __forceinline__ float value(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+  }
+};
+
+// the format a kernel instantiated with H uses for its half operands (H = 0: fp32 kernels,
+// whose half branches are never taken)
+template <int H>
+using HalfOf = Half<H == 0 ? 1 : H>;
+
+// v rounded to the half format H (as a float)
+template <int H>
+__device__ __forceinline__ float round_half(float v) {
+  return HalfOf<H>::value(HalfOf<H>::bits(v));
 }
 
 __device__ __forceinline__ f32x4 zero4() {

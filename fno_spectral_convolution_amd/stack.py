@@ -5,6 +5,10 @@ the spectral blocks (GELU after each), an optional projection head, and for trai
 workloads the MSE loss against a target and the backward through every block (input,
 spectral-weight, bypass-weight and bias gradients).  Torch provides device memory and the
 stream; all arithmetic runs in libfno's kernels.
+
+``PrecisionSchedule`` with ``StackRunner.run`` moves a training run from a half-precision
+spectral path to fp32 at a chosen step (precision scheduling, mixed-precision neural-operator
+page, "Tiivistelmä").
 """
 from __future__ import annotations
 
@@ -12,6 +16,39 @@ import numpy as np
 
 from . import binding as L
 from . import inputs
+from .configs import F16_LOSS_SCALE, precision
+
+
+SPECTRAL_PRECISIONS = ("f32", "bf16", "f16")
+_PLAN_MIXED = {"f32": False, "bf16": "bf16", "f16": "f16"}
+
+
+class PrecisionSchedule:
+    """Mixed-to-full precision switch of a training run (mixed-precision neural-operator page,
+    "Tiivistelmä": precision scheduling).  Steps 0 .. switch_step - 1 run the spectral path
+    with `half` operands ("bf16" or "f16"), every later step in fp32.  The page gives only the
+    direction of the switch, so the step is the caller's.  The tanh pre-activation is part of
+    the model and stays on after the switch: only the arithmetic changes."""
+
+    def __init__(self, switch_step: int, half: str = "bf16"):
+        if half not in ("bf16", "f16"):
+            raise ValueError(f"half must be 'bf16' or 'f16', not {half!r}")
+        if isinstance(switch_step, bool) or int(switch_step) != switch_step or switch_step < 0:
+            raise ValueError(f"switch_step must be an integer >= 0, not {switch_step!r}")
+        self.switch_step = int(switch_step)
+        self.half = half
+
+    @classmethod
+    def from_fraction(cls, total_steps: int, half_fraction: float, half: str = "bf16"):
+        """The first floor(half_fraction * total_steps) steps in half precision."""
+        if total_steps < 0 or not 0.0 <= half_fraction <= 1.0:
+            raise ValueError("need total_steps >= 0 and 0 <= half_fraction <= 1")
+        return cls(int(half_fraction * total_steps), half)
+
+    def precision_at(self, step: int) -> str:
+        if step < 0:
+            raise ValueError("step must be >= 0")
+        return self.half if step < self.switch_step else "f32"
 
 
 class StackRunner:
@@ -22,7 +59,15 @@ class StackRunner:
         dev = torch.device(device)
         self.device = dev
         C = wl.width
-        self.plan = L.Plan(wl.batch, C, C, wl.grid, wl.modes, mixed=wl.mixed, device=dev)
+        # one plan per spectral precision the run has used (a plan holds only its tables and
+        # workspace); the workload's tanh pre-activation is kept by all of them
+        self._tanh = bool(wl.mixed)
+        self._plans = {}
+        self.precision = precision(wl)
+        self.plan = self._plan_for(self.precision)
+        # IEEE-half training takes a static loss scale: every gradient the step returns
+        # (weights, bypass, bias, input) comes out multiplied by grad_scale
+        self.grad_scale = F16_LOSS_SCALE if self.precision == "f16" else 1.0
         hi = host_inputs or make_host_inputs(wl)
         self.host = hi
         to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
@@ -40,6 +85,7 @@ class StackRunner:
             self.acts = [torch.empty(shape, dtype=torch.float32, device=dev)
                          for _ in range(nb + 1)]
             self.saves = [self.plan.new_save() for _ in range(nb)]
+            self._save_bytes = self.plan.save_bytes
             self.g = [torch.empty(shape, dtype=torch.float32, device=dev) for _ in range(2)]
             self.grads = [{"w": torch.empty_like(p["w"]), "wb": torch.empty_like(p["wb"]),
                            "bias": torch.empty_like(p["bias"])} for p in self.params]
@@ -54,6 +100,42 @@ class StackRunner:
             out_shape = (wl.batch, wl.proj_out) + tuple(wl.grid)
             self.out = torch.empty(out_shape, dtype=torch.float32, device=dev)
         self.plan.workspace()
+
+    def _plan_for(self, prec):
+        if prec not in self._plans:
+            wl = self.wl
+            plan = L.Plan(wl.batch, wl.width, wl.width, wl.grid, wl.modes,
+                          mixed=_PLAN_MIXED[prec], tanh=self._tanh, device=self.device)
+            plan.workspace()
+            self._plans[prec] = plan
+        return self._plans[prec]
+
+    def set_precision(self, prec):
+        """Run the following steps with spectral precision `prec` ("f32", "bf16", "f16").
+        The first switch to a precision builds its plan (host tables, one upload); the saved
+        spectra buffers grow if the new plan needs more.  Enqueued work is not affected."""
+        if prec not in SPECTRAL_PRECISIONS:
+            raise ValueError(f"spectral precision must be one of {SPECTRAL_PRECISIONS}")
+        if prec == self.precision:
+            return
+        plan = self._plan_for(prec)
+        if self.wl.train and plan.save_bytes > self._save_bytes:
+            self.saves = [plan.new_save() for _ in range(self.wl.blocks)]
+            self._save_bytes = plan.save_bytes
+        self.plan = plan
+        self.precision = prec
+        self.grad_scale = F16_LOSS_SCALE if prec == "f16" else 1.0
+
+    def run(self, schedule, steps, start=0, on_step=None):
+        """Steps start .. start + steps - 1 of a training run, each at the precision the
+        schedule gives it; on_step(step_index, output) is called after each step is enqueued."""
+        out = None
+        for i in range(start, start + steps):
+            self.set_precision(schedule.precision_at(i))
+            out = self.step()
+            if on_step is not None:
+                on_step(i, out)
+        return out
 
     def _act(self, i):
         return self.acts[i] if self.wl.train else self.acts[i % 2]
@@ -77,7 +159,8 @@ class StackRunner:
             L.pointwise(h, pr["w1"], pr["b1"], pr["w2"], pr["b2"], out=self.out)
             h = self.out
         if wl.train:
-            L.mse_grad(h, self.target, grad=self.g[0], loss=self.loss, ws=self.mse_ws)
+            L.mse_grad(h, self.target, grad=self.g[0], loss=self.loss, ws=self.mse_ws,
+                       grad_scale=self.grad_scale)
             gin = 0
             for i in reversed(range(len(self.params))):
                 p = self.params[i]

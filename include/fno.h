@@ -70,7 +70,15 @@ typedef enum fno_status {
  * BF16: bfloat16 operands (pre-activated input, transform tables, spectra, weights rounded
  *       to nearest-even on load) with float32 accumulation -- the half-precision transform
  *       and contraction of [MIXED].  The bypass, bias, GELU and every HBM activation stay
- *       float32.  */
+ *       float32.
+ * F16:  the same with IEEE half operands.  Half's 5-bit exponent is kept in range by scaling
+ *       every transform of the plan by 1/sqrt(N_j) per axis in both directions (tables built
+ *       so), and by multiplying the mixed spectra by the power of two nearest sqrt(Cin) Cout
+ *       (forward; sqrt(Cout) Cin for the input gradient), which the last inverse stage divides
+ *       out.  The gain suits spectral weights of size about 1/(Cin Cout), the usual FNO
+ *       initialisation; weights orders of magnitude larger can overflow half (inf in the
+ *       output).  Results are unchanged up to rounding.  Gradients far below half's range (a
+ *       mean over 10^8 elements) need a loss scale, see fno_mse_grad_scaled.  */
 typedef enum fno_dtype { FNO_DTYPE_F32 = 0, FNO_DTYPE_BF16 = 1, FNO_DTYPE_F16 = 2 } fno_dtype;
 
 enum {
@@ -159,6 +167,13 @@ fno_status fno_pointwise_fwd(int64_t batch, int64_t npts, int64_t c_in, int64_t 
 fno_status fno_mse_workspace_bytes(int64_t n, size_t* bytes);
 fno_status fno_mse_grad(int64_t n, const float* y, const float* t, float* grad, float* loss,
                         void* workspace, size_t workspace_bytes, void* stream);
+/* The same with grad = grad_scale * 2 (y - t) / n (the loss itself unscaled): a static loss
+ * scale, which keeps the gradients of an IEEE-half (F16) plan's backward inside half's range;
+ * every gradient the backward then returns is scaled by grad_scale as well.  grad_scale must
+ * be finite and > 0 (else INVALID_ARGUMENT). */
+fno_status fno_mse_grad_scaled(int64_t n, const float* y, const float* t, float* grad,
+                               float* loss, float grad_scale, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /* Per-kernel timing with HIP events, for measurement (off by default).  While enabled, every
  * kernel launch of libfno is bracketed by two events recorded on the stream it is launched

@@ -5,6 +5,17 @@ import numpy as np
 
 TOL_F32 = 1e-5    # relative L2, fp32 spectral path
 TOL_MIXED = 1e-2  # relative L2, tanh + bf16 spectral path
+# tanh + IEEE-half spectral path: the operand rounding error scales with the unit roundoff,
+# 2^-11 for half against 2^-8 for bfloat16, so the bfloat16 bound divided by 8.  A half path
+# that rounded its operands to bfloat16 by mistake shows errors eight times larger.
+TOL_F16 = TOL_MIXED / 8
+
+
+def tol_for(mixed) -> float:
+    """Tolerance of a spectral precision as the plans take it: False, True / "bf16", "f16"."""
+    if not mixed:
+        return TOL_F32
+    return TOL_F16 if mixed == "f16" else TOL_MIXED
 
 
 def rel_l2(got, want) -> float:

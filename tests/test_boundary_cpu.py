@@ -43,6 +43,7 @@ def _desc(**kw):
     dict(), dict(grid=(128, 128, 128), modes=(16, 16, 16)),
     dict(grid=(128, 128, 128, 20), modes=(12, 12, 12, 8), batch=1),
     dict(grid=(512, 512), modes=(32, 32), c_in=64, c_out=64, dtype=1, flags=7),
+    dict(grid=(512, 512), modes=(32, 32), c_in=64, c_out=64, dtype=2, flags=7),
     dict(grid=(8, 8), modes=(4, 5)), dict(grid=(15, 9), modes=(7, 5)),
 ])
 def test_validate_accepts(kw):
@@ -58,7 +59,6 @@ def test_validate_accepts(kw):
     (dict(c_in=0), L.FNO_ERR_INVALID_ARGUMENT),
     (dict(flags=8), L.FNO_ERR_INVALID_ARGUMENT),
     (dict(dtype=7), L.FNO_ERR_INVALID_ARGUMENT),
-    (dict(dtype=2), L.FNO_ERR_UNSUPPORTED),
     (dict(c_in=65), L.FNO_ERR_UNSUPPORTED),
     (dict(grid=(64, 8192), modes=(12, 12)), L.FNO_ERR_UNSUPPORTED),
 ])
@@ -85,6 +85,9 @@ def test_null_arguments_rejected_on_host():
         L.FNO_ERR_INVALID_ARGUMENT
     assert L._lib.fno_mse_grad(0, None, None, None, None, None, 0, None) == \
         L.FNO_ERR_INVALID_ARGUMENT
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert L._lib.fno_mse_grad_scaled(4, None, None, None, None, bad, None, 0, None) == \
+            L.FNO_ERR_INVALID_ARGUMENT
     assert L._lib.fno_pointwise_fwd(1, 1, 1, 0, 300, None, None, None, None, None, None,
                                     None) == L.FNO_ERR_UNSUPPORTED
 
@@ -102,6 +105,8 @@ def test_status_strings():
     dict(grid=(6, 8, 10, 20), modes=(2, 3, 4, 8), batch=1),
     dict(grid=(128, 128, 128, 20), modes=(12, 12, 12, 8), batch=1),
     dict(grid=(512, 512), modes=(32, 32), c_in=64, c_out=64, batch=8, dtype=1, flags=7),
+    dict(grid=(512, 512), modes=(32, 32), c_in=64, c_out=64, batch=8, dtype=2, flags=7),
+    dict(grid=(128, 128, 128, 20), modes=(12, 12, 12, 8), batch=1, dtype=2, flags=7),
     dict(grid=(16, 32), modes=(1, 1), c_in=1, c_out=1),
 ])
 def test_plan_create_host_logic(kw):

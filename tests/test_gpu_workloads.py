@@ -1,4 +1,4 @@
-"""Parity at the five workloads' full sizes, in the launch configuration bench.py times.
+"""Parity at the workloads' full sizes, in the launch configuration bench.py times.
 
 Inputs are the workloads' own seeded fields (Gaussian random fields, coordinate and layered
 permeability channels) and block parameters.  Where the oracle can evaluate the whole field in
@@ -15,7 +15,7 @@ import pytest
 
 import oracle.fno_oracle as O
 from fno_spectral_convolution_amd import configs, inputs
-from tests.gpu_helpers import TOL_F32, TOL_MIXED, announce, check
+from tests.gpu_helpers import TOL_F32, announce, check, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -59,7 +59,7 @@ def _grad_in(wl, scale):
 def _block_case(L, name, grad_scale):
     """One block of the workload at full size: forward, backward and the spectral path alone."""
     wl = configs.get(name)
-    tol = TOL_MIXED if wl.mixed else TOL_F32
+    tol = tol_for(wl.mixed)
     announce("workload block", name, wl.batch, wl.width, wl.grid, wl.modes)
     x = _field(wl)
     blk = inputs.block_params(wl, 1)[0]
@@ -72,7 +72,7 @@ def _block_case(L, name, grad_scale):
     _torch().cuda.synchronize()
     y, gx, gw, gwb, gb = _host(y), _host(g["x"]), _host(g["w"]), _host(g["wb"]), _host(g["bias"])
     del save, g
-    ref = O.block_bwd(x, blk["w"], blk["wb"], blk["bias"], wl.modes, gy, tanh=wl.mixed)
+    ref = O.block_bwd(x, blk["w"], blk["wb"], blk["bias"], wl.modes, gy, tanh=bool(wl.mixed))
     check("y", y, ref["fwd"]["y"], tol)
     check("grad_x", gx, ref["grad_x"], tol)
     check("grad_w", gw, ref["grad_w"], tol)
@@ -98,6 +98,10 @@ def test_train2d_512_block_full(L):
     _block_case(L, "train2d_512", 1e-3)
 
 
+def test_train2d_512_f16_block_full(L):
+    _block_case(L, "train2d_512_f16", 1e-3)
+
+
 def test_train3d_128_block_full(L):
     _block_case(L, "train3d_128", 1e-3)
 
@@ -118,11 +122,11 @@ def test_stack2d_256_sampled_batches(L):
         check(f"stack output batch {b}", out[b:b + 1], want, TOL_F32)
 
 
-@pytest.mark.parametrize("name", ["st4d_128x20", "st4d_128x20_bf16"])
+@pytest.mark.parametrize("name", ["st4d_128x20", "st4d_128x20_bf16", "st4d_128x20_f16"])
 def test_st4d_128x20_block_sampled_points(L, name):
     """4D space-time share [1, 20, 128^3 x 20]: y and y_spec at 512 sampled grid points."""
     wl = configs.get(name)
-    tol = TOL_MIXED if wl.mixed else TOL_F32
+    tol = tol_for(wl.mixed)
     announce("workload block sampled", name)
     torch = _torch()
     x = _field(wl)
