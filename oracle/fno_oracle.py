@@ -43,6 +43,20 @@ Backward (gradient of a complex quantity = dL/dRe + i dL/dIm):
   B5  grad_x = sum_o Wb[o,i] g_z[o] + s(x) gxs,   s = 1 - tanh(x)^2 (mixed) or 1
   B6  dWb[o,i] = sum_{b,p} g_z[o] x[i];   dbias[o] = sum_{b,p} g_z[o]
 
+Tucker-factorised weights (TFNO, one of the architectures [MIXED] "Tiivistelmä" trains in mixed
+precision; the page names it only).  The weight on the retained grid, W_full[i, o, s_0..s_{d-1}]
+(``expand_weights``' layout: s_j in 0..2m_j-1 on outer axes, 0..m_{d-1}-1 on the last), is held
+in Tucker form (core tensor times one factor matrix per mode):
+
+  T1  W_full = G x_1 U_in x_2 U_out x_3 U_0 .. x_{d+2} U_{d-1},
+      (T x_n U)[.., a, ..] = sum_r T[.., r, ..] U[a, r]   (mode-n product: index r_n -> a)
+      G complex [R_in, R_out, R_0, .., R_{d-1}], U_n complex [I_n, R_n].
+  T2  grad_G   = grad_W x_1 conj(U_in)^T x_2 conj(U_out)^T .. (every mode)
+  T3  grad_U_n[a, r] = sum over all other indices of grad_W[.., a, ..] conj(B_n[.., r, ..]),
+      B_n = G x_m U_m over every m != n
+  (W is complex-linear in each of G and the U_n, so each gradient is grad_W pulled back through
+  the conjugated Jacobian.)  The block is F1-F4 with W = fold(W_full).
+
 Layouts: fields are [B, C, N_0, .., N_{d-1}] float; ``W`` is complex
 [2^(d-1), Cin, Cout, m_0, .., m_{d-1}]; ``Wb`` is [Cout, Cin]; ``bias`` is [Cout].
 Everything is evaluated in float64 / complex128.
@@ -61,6 +75,7 @@ __all__ = [
     "gelu",
     "gelu_prime", "spectral_conv_fwd", "spectral_conv_bwd", "block_fwd", "block_bwd",
     "pointwise_linear", "projection_fwd", "mse_loss_grad", "stack_fwd", "train_step",
+    "mode_product", "tucker_to_full", "tucker_block_fwd", "tucker_block_bwd",
 ]
 
 
@@ -371,3 +386,67 @@ def train_step(x, target, blocks, modes, tanh: bool = False):
                      "grad_bias": r["grad_bias"]}
         g = r["grad_x"]
     return {"loss": loss, "y": acts[-1], "grad_x": g, "grads": grads}
+
+
+# ----------------------------------------------------------------------------- Tucker weights
+def mode_product(t: np.ndarray, u: np.ndarray, n: int) -> np.ndarray:
+    """T1's mode-n product: (T x_n U)[.., a, ..] = sum_r T[.., r, ..] U[a, r]."""
+    t = np.asarray(t, dtype=np.complex128)
+    u = np.asarray(u, dtype=np.complex128)
+    assert t.shape[n] == u.shape[1], (t.shape, u.shape, n)
+    r = np.tensordot(t, u, axes=([n], [1]))  # the new index a comes last
+    return np.moveaxis(r, -1, n)
+
+
+def tucker_to_full(core, factors) -> np.ndarray:
+    """T1: the retained-grid weight W_full [Cin, Cout, 2m_0, .., m_{d-1}] of a Tucker core and
+    its factors [U_in, U_out, U_0, .., U_{d-1}]."""
+    t = np.asarray(core, dtype=np.complex128)
+    assert t.ndim == len(factors), (t.shape, len(factors))
+    for n, u in enumerate(factors):
+        t = mode_product(t, u, n)
+    return t
+
+
+def _check_tucker_shapes(core, factors, cin, cout, modes):
+    want = [cin, cout] + [2 * m for m in modes[:-1]] + [modes[-1]]
+    assert len(factors) == len(want) == np.ndim(core)
+    for n, u in enumerate(factors):
+        assert np.shape(u) == (want[n], np.shape(core)[n]), (n, np.shape(u), want[n])
+
+
+def tucker_block_fwd(x, core, factors, wb, bias, modes, tanh: bool = False, act: bool = True):
+    """One FNO block whose spectral weight is T1's Tucker form (F1-F4 on W = fold(W_full))."""
+    x = np.asarray(x, dtype=np.float64)
+    _check_tucker_shapes(core, factors, x.shape[1], np.shape(wb)[0], modes)
+    w = fold_weights(tucker_to_full(core, factors), modes)
+    return block_fwd(x, w, wb, bias, modes, tanh=tanh, act=act)
+
+
+def tucker_block_bwd(x, core, factors, wb, bias, modes, g_y, tanh: bool = False,
+                     act: bool = True):
+    """B1-B6 with T2 / T3 for the Tucker factors.  Returns block_bwd's dict plus grad_core
+    and grad_factors (same order as ``factors``)."""
+    x = np.asarray(x, dtype=np.float64)
+    _check_tucker_shapes(core, factors, x.shape[1], np.shape(wb)[0], modes)
+    core = np.asarray(core, dtype=np.complex128)
+    factors = [np.asarray(u, dtype=np.complex128) for u in factors]
+    w = fold_weights(tucker_to_full(core, factors), modes)
+    r = block_bwd(x, w, wb, bias, modes, g_y, tanh=tanh, act=act)
+    gw = expand_weights(r["grad_w"], modes)
+    # T2: every mode contracted with the conjugated factor
+    gcore = gw
+    for n, u in enumerate(factors):
+        gcore = mode_product(gcore, np.conj(u).T, n)
+    # T3: B_n = G with every factor but the n-th applied; contract all indices except n
+    gfac = []
+    for n in range(len(factors)):
+        bn = core
+        for m, u in enumerate(factors):
+            if m != n:
+                bn = mode_product(bn, u, m)
+        axes = [a for a in range(gw.ndim) if a != n]
+        gfac.append(np.tensordot(gw, np.conj(bn), axes=(axes, axes)))
+    r["grad_core"] = gcore
+    r["grad_factors"] = gfac
+    return r

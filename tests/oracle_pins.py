@@ -405,6 +405,110 @@ def check_inverse_at_points(O):
         _close(got, want, 1e-12, f"inverse at points {grid}")
 
 
+# ------------------------------------------------------------------ T1-T3: Tucker weights
+def _crand(g, shape):
+    return g.standard_normal(shape) + 1j * g.standard_normal(shape)
+
+
+def _apply_mode(t, m, n):
+    """t with matrix m[a, r] applied on axis n, written with an explicit einsum subscript."""
+    letters = "abcdefgh"[:t.ndim]
+    out = letters[:n] + "z" + letters[n + 1:]
+    return np.einsum(f"{letters},z{letters[n]}->{out}", t, m)
+
+
+def check_tucker_identity_factors(O):
+    """Square identity factors leave the core unchanged."""
+    g = _rng(200)
+    shape = (3, 2, 4, 5)
+    core = _crand(g, shape)
+    got = O.tucker_to_full(core, [np.eye(n) for n in shape])
+    assert np.array_equal(got, core)
+
+
+def check_tucker_hosvd(O):
+    """Higher-order SVD (Kolda and Bader, "Tensor decompositions and applications"): with U_n
+    the left singular vectors of the mode-n unfolding and core = W x_n conj(U_n)^T for every n,
+    the full-rank Tucker form reconstructs W, and truncating mode n to R_n columns costs at most
+    the sum over modes of the discarded squared singular values.  The factors are unitary and
+    not symmetric, so a transposed or conjugated factor in the oracle's product fails."""
+    g = _rng(201)
+    for shape in [(3, 4, 6, 5), (2, 3, 4, 4, 3)]:
+        W = _crand(g, shape)
+        Us, svals = [], []
+        for n in range(len(shape)):
+            unf = np.moveaxis(W, n, 0).reshape(shape[n], -1)
+            U, sv, _ = np.linalg.svd(unf, full_matrices=True)
+            Us.append(U)
+            svals.append(sv)
+        core = W
+        for n, U in enumerate(Us):
+            core = _apply_mode(core, np.conj(U).T, n)
+        _close(O.tucker_to_full(core, Us), W, 1e-12, f"HOSVD round trip {shape}")
+        ranks = [max(1, n - 1) for n in shape]
+        tcore = core[tuple(slice(0, r) for r in ranks)]
+        approx = O.tucker_to_full(tcore, [U[:, :r] for U, r in zip(Us, ranks)])
+        bound = sum(float(np.sum(sv[r:] ** 2)) for sv, r in zip(svals, ranks))
+        err = float(np.sum(np.abs(W - approx) ** 2))
+        assert 0.0 < err <= bound * (1 + 1e-12), (shape, err, bound)
+
+
+def check_tucker_rank_one(O):
+    """A rank-1 Tucker form is the scaled outer product of its factor vectors."""
+    g = _rng(202)
+    dims = (3, 4, 6, 5)
+    c = complex(g.standard_normal(), g.standard_normal())
+    vecs = [_crand(g, (n,)) for n in dims]
+    want = c * vecs[0]
+    for v in vecs[1:]:
+        want = np.multiply.outer(want, v)
+    got = O.tucker_to_full(np.full((1,) * len(dims), c), [v[:, None] for v in vecs])
+    _close(got, want, 1e-13, "rank-1 Tucker")
+
+
+def check_tucker_block_finite_differences(O):
+    """fp64 central differences of L = <y, g> through a whole block (tanh, GELU, bypass) with
+    Tucker weights, for the real and imaginary parts of sampled core and factor entries, in 2D
+    and 3D."""
+    for gi, (grid, modes, ranks) in enumerate([((6, 8), (2, 3), (2, 3, 3, 2)),
+                                               ((4, 4, 6), (1, 2, 2), (2, 2, 2, 3, 1))]):
+        g = _rng(210 + gi)
+        cin, cout = 2, 3
+        dims = [cin, cout] + [2 * m for m in modes[:-1]] + [modes[-1]]
+        x = g.standard_normal((2, cin) + grid)
+        core = _crand(g, ranks) * 0.5
+        facs = [_crand(g, (n, r)) * 0.5 for n, r in zip(dims, ranks)]
+        wb = g.standard_normal((cout, cin))
+        bias = g.standard_normal(cout)
+        gy = g.standard_normal((2, cout) + grid)
+
+        def L(core_, facs_):
+            return float(np.sum(O.tucker_block_fwd(x, core_, facs_, wb, bias, modes,
+                                                   tanh=True)["y"] * gy))
+
+        r = O.tucker_block_bwd(x, core, facs, wb, bias, modes, gy, tanh=True)
+        h = 1e-6
+        targets = [("core", None)] + [("factor", n) for n in range(len(facs))]
+        for what, n in targets:
+            arr = core if n is None else facs[n]
+            ana_all = r["grad_core"] if n is None else r["grad_factors"][n]
+            for _ in range(3):
+                idx = tuple(int(g.integers(0, s_)) for s_ in arr.shape)
+                for dlt, part in ((h, np.real), (1j * h, np.imag)):
+                    ap, am = arr.copy(), arr.copy()
+                    ap[idx] += dlt
+                    am[idx] -= dlt
+                    if n is None:
+                        num = (L(ap, facs) - L(am, facs)) / (2 * h)
+                    else:
+                        fp = list(facs)
+                        fm = list(facs)
+                        fp[n], fm[n] = ap, am
+                        num = (L(core, fp) - L(core, fm)) / (2 * h)
+                    ana = part(ana_all[idx])
+                    assert abs(num - ana) < 1e-6 * max(1, abs(num)), (what, n, idx, num, ana)
+
+
 ALL_CHECKS = [
     check_inverse_at_points,
     check_spectrum_bruteforce, check_spectrum_numpy_fft, check_parseval_and_dc,
@@ -412,4 +516,6 @@ ALL_CHECKS = [
     check_single_mode_dc_plane, check_cutoff, check_linearity_equivariance_selfadjoint,
     check_gelu, check_zero_weight_block, check_adjoint_identities,
     check_block_finite_differences, check_mse_and_stack,
+    check_tucker_identity_factors, check_tucker_hosvd, check_tucker_rank_one,
+    check_tucker_block_finite_differences,
 ]

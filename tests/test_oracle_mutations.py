@@ -86,6 +86,36 @@ def _block_no_bias(x, w, wb, bias, modes, tanh=False, act=True):
     return _orig["block_fwd"](x, w, wb, None, modes, tanh=tanh, act=act)
 
 
+def _mode_product_transposed(t, u, n):
+    return _orig["mode_product"](t, np.asarray(u).T, n)
+
+
+def _mode_product_conj(t, u, n):
+    return _orig["mode_product"](t, np.conj(u), n)
+
+
+def _tucker_bwd_factor_unconj(x, core, factors, wb, bias, modes, g_y, tanh=False, act=True):
+    r = _orig["tucker_block_bwd"](x, core, factors, wb, bias, modes, g_y, tanh, act)
+    r = dict(r)
+    r["grad_factors"] = [np.conj(gf) for gf in r["grad_factors"]]
+    return r
+
+
+def _tucker_bwd_core_one_mode_short(x, core, factors, wb, bias, modes, g_y, tanh=False,
+                                    act=True):
+    r = _orig["tucker_block_bwd"](x, core, factors, wb, bias, modes, g_y, tanh, act)
+    r = dict(r)
+    # the last mode's conjugated factor left out of T2 (replaced by its plain transpose)
+    u = np.asarray(factors[-1])
+    n = len(factors) - 1
+    gw = O.expand_weights(r["grad_w"], modes)
+    gc = gw
+    for m, um in enumerate(factors):
+        gc = _orig["mode_product"](gc, (np.conj(um) if m != n else um).T, m)
+    r["grad_core"] = gc
+    return r
+
+
 MUTATIONS = [
     ("dft_matrix", _dft_sign_flipped, P.check_spectrum_bruteforce),
     ("retained_indices", _retained_off_by_one, P.check_spectrum_numpy_fft),
@@ -99,6 +129,11 @@ MUTATIONS = [
     ("spectral_conv_bwd", _bwd_no_conj, P.check_adjoint_identities),
     ("block_bwd", _block_bwd_no_tanh_prime, P.check_block_finite_differences),
     ("block_fwd", _block_no_bias, P.check_zero_weight_block),
+    ("mode_product", _mode_product_transposed, P.check_tucker_hosvd),
+    ("mode_product", _mode_product_conj, P.check_tucker_hosvd),
+    ("tucker_block_bwd", _tucker_bwd_factor_unconj, P.check_tucker_block_finite_differences),
+    ("tucker_block_bwd", _tucker_bwd_core_one_mode_short,
+     P.check_tucker_block_finite_differences),
 ]
 
 
