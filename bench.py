@@ -209,10 +209,18 @@ def cpu_baseline(wl, sample_batch, min_seconds=10.0, max_reps=12):
     t0 = time.perf_counter()
     # repeat the sample until about min_seconds of host work (bounded by max_reps)
     while True:
-        if wl.train:
-            O.block_bwd(x, blk["w"], blk["wb"], blk["bias"], wl.modes, gy, tanh=bool(wl.mixed))
+        tanh = bool(wl.mixed)
+        if "core" in blk:  # Tucker-factorised weights
+            if wl.train:
+                O.tucker_block_bwd(x, blk["core"], blk["factors"], blk["wb"], blk["bias"],
+                                   wl.modes, gy, tanh=tanh)
+            else:
+                O.tucker_block_fwd(x, blk["core"], blk["factors"], blk["wb"], blk["bias"],
+                                   wl.modes, tanh=tanh)
+        elif wl.train:
+            O.block_bwd(x, blk["w"], blk["wb"], blk["bias"], wl.modes, gy, tanh=tanh)
         else:
-            O.block_fwd(x, blk["w"], blk["wb"], blk["bias"], wl.modes, tanh=bool(wl.mixed))
+            O.block_fwd(x, blk["w"], blk["wb"], blk["bias"], wl.modes, tanh=tanh)
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds or reps >= max_reps:
@@ -239,6 +247,7 @@ def main():
     runner, wall, kern = bench_gpu(wl, args.steps, args.warmup, args.spectral_precision)
     dtype = runner.precision
     switched = dtype != configs.precision(wl)
+    tucker_order = runner.tk.order if runner.tk is not None else None
     ms = wall / args.steps * 1e3
     value = wl.units / (wall / args.steps)
     roof, rows = roofline(wl, runner, kern, args.steps)
@@ -260,7 +269,10 @@ def main():
                                           if dtype != "f32" else "fp32")
                    + (f" (switched from {configs.precision(wl)}, tanh "
                       f"{'kept' if wl.mixed else 'off'})" if switched else ""),
-                   "pointwise_precision": "fp32"},
+                   "pointwise_precision": "fp32",
+                   **({"spectral_weight": f"Tucker ranks {list(wl.tucker_ranks)}, contraction "
+                                          f"order '{tucker_order}'"}
+                      if wl.tucker_ranks else {})},
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": {k: {"launches": v["launches"], "avg_us": round(v["avg_us"], 2),

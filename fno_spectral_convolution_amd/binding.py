@@ -36,6 +36,8 @@ EXPORTS = [
     "fno_plan_validate", "fno_plan_create", "fno_plan_destroy", "fno_plan_query",
     "fno_spectral_conv_fwd", "fno_spectral_conv_bwd", "fno_block_fwd", "fno_block_bwd",
     "fno_pointwise_fwd", "fno_mse_workspace_bytes", "fno_mse_grad", "fno_mse_grad_scaled",
+    "fno_tucker_order", "fno_tucker_create", "fno_tucker_destroy", "fno_tucker_query",
+    "fno_tucker_block_fwd", "fno_tucker_block_bwd",
     "fno_timing_enable",
     "fno_timing_reset", "fno_timing_count", "fno_timing_get", "fno_status_string",
     "fno_last_error_message",
@@ -78,6 +80,16 @@ def _load():
         "fno_mse_workspace_bytes": (c_int, [c_int64, POINTER(c_size_t)]),
         "fno_mse_grad": (c_int, [c_int64, P, P, P, P, P, c_size_t, P]),
         "fno_mse_grad_scaled": (c_int, [c_int64, P, P, P, P, c_float, P, c_size_t, P]),
+        "fno_tucker_order": (c_int, [POINTER(fno_plan_desc), POINTER(c_int32), c_char_p,
+                                     c_size_t]),
+        "fno_tucker_create": (c_int, [P, POINTER(c_int32), POINTER(c_void_p)]),
+        "fno_tucker_destroy": (c_int, [P]),
+        "fno_tucker_query": (c_int, [P, POINTER(c_size_t), POINTER(c_int64), POINTER(c_int64),
+                                     c_char_p, c_size_t]),
+        "fno_tucker_block_fwd": (c_int, [P, P, P, POINTER(c_void_p), P, P, P, P, P, c_size_t,
+                                         P]),
+        "fno_tucker_block_bwd": (c_int, [P, P, P, POINTER(c_void_p), P, P, P, P, P, P,
+                                         POINTER(c_void_p), P, P, P, c_size_t, P]),
         "fno_timing_enable": (c_int, [c_int]),
         "fno_timing_reset": (c_int, []),
         "fno_timing_count": (c_int, [POINTER(c_int)]),
@@ -316,6 +328,123 @@ class Plan:
                       _ptr(save), grad_y.data_ptr(), _ptr(gx), _ptr(gw), _ptr(gwb), _ptr(gb),
                       ws.data_ptr(), self.ws_bytes, self._stream())
         return {"x": gx, "w": gw, "wb": gwb, "bias": gb}
+
+
+def _ranks_arr(ranks):
+    return (c_int32 * len(ranks))(*[int(r) for r in ranks])
+
+
+def _ptr_arr(ptrs):
+    return (c_void_p * len(ptrs))(*[p if p else None for p in ptrs])
+
+
+def fno_tucker_order(desc, ranks) -> str:
+    """The greedy contraction order of a descriptor and Tucker ranks (host only)."""
+    buf = ctypes.create_string_buffer(512)
+    _check(_lib.fno_tucker_order(byref(desc), _ranks_arr(ranks), buf, len(buf)),
+           "fno_tucker_order")
+    return buf.value.decode()
+
+
+def fno_tucker_create(plan_handle, ranks):
+    h = c_void_p()
+    _check(_lib.fno_tucker_create(plan_handle, _ranks_arr(ranks), byref(h)), "fno_tucker_create")
+    return h.value
+
+
+def fno_tucker_destroy(handle):
+    _check(_lib.fno_tucker_destroy(handle), "fno_tucker_destroy")
+
+
+def fno_tucker_query(handle, nfactors):
+    ws = c_size_t()
+    core = c_int64()
+    fac = (c_int64 * nfactors)()
+    buf = ctypes.create_string_buffer(512)
+    _check(_lib.fno_tucker_query(handle, byref(ws), byref(core), fac, buf, len(buf)),
+           "fno_tucker_query")
+    return ws.value, core.value, list(fac), buf.value.decode()
+
+
+def fno_tucker_block_fwd(h, x, core, factors, wb, bias, y, save, ws, ws_bytes, stream):
+    _check(_lib.fno_tucker_block_fwd(h, x, core, _ptr_arr(factors), wb, bias, y, save, ws,
+                                     ws_bytes, stream), "fno_tucker_block_fwd")
+
+
+def fno_tucker_block_bwd(h, x, core, factors, wb, bias, save, gy, gx, gcore, gfactors, gwb, gb,
+                         ws, ws_bytes, stream):
+    gf = _ptr_arr(gfactors) if gfactors is not None else None
+    _check(_lib.fno_tucker_block_bwd(h, x, core, _ptr_arr(factors), wb, bias, save, gy, gx,
+                                     gcore, gf, gwb, gb, ws, ws_bytes, stream),
+           "fno_tucker_block_bwd")
+
+
+class Tucker:
+    """Tucker-factorised spectral weights bound to a ``Plan``: core complex64
+    [R_in, R_out, R_0, .., R_{d-1}], factors complex64 [C_in, R_in], [C_out, R_out],
+    [2 m_j, R_j] (outer axes), [m_{d-1}, R_{d-1}]."""
+
+    def __init__(self, plan, ranks):
+        self.plan = plan
+        self.ranks = tuple(int(r) for r in ranks)
+        self.nf = len(plan.grid) + 2
+        if len(self.ranks) != self.nf:
+            raise ValueError(f"need {self.nf} ranks (in, out, one per axis)")
+        self.handle = fno_tucker_create(plan.handle, self.ranks)
+        self.ws_bytes, self.core_elems, self.factor_elems, self.order = \
+            fno_tucker_query(self.handle, self.nf)
+        self._ws = None
+
+    def close(self):
+        if getattr(self, "handle", None):
+            fno_tucker_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def factor_shapes(self):
+        p = self.plan
+        full = [p.c_in, p.c_out] + [2 * m for m in p.modes[:-1]] + [p.modes[-1]]
+        return [(n, r) for n, r in zip(full, self.ranks)]
+
+    def workspace(self):
+        if self._ws is None:
+            t = self.plan.torch
+            self._ws = t.empty(max(self.ws_bytes, 16), dtype=t.uint8, device=self.plan.device)
+        return self._ws
+
+    def block_fwd(self, x, core, factors, wb, bias=None, save=None, out=None):
+        p = self.plan
+        y = out if out is not None else p._field(p.c_out)
+        ws = self.workspace()
+        fno_tucker_block_fwd(self.handle, x.data_ptr(), core.data_ptr(),
+                             [f.data_ptr() for f in factors], wb.data_ptr(), _ptr(bias),
+                             y.data_ptr(), _ptr(save), ws.data_ptr(), self.ws_bytes,
+                             p._stream())
+        return y
+
+    def block_bwd(self, x, core, factors, wb, bias, save, grad_y, want_x=True, want_w=True,
+                  out=None):
+        """Returns dict(x, core, factors, wb, bias) of gradients (None where not asked)."""
+        p = self.plan
+        t = p.torch
+        o = dict(out or {})
+        gx = o.get("x", p._field(p.c_in) if want_x else None)
+        gcore = o.get("core", t.empty_like(core) if want_w else None)
+        gfac = o.get("factors", [t.empty_like(f) for f in factors] if want_w else None)
+        gwb = o.get("wb", t.empty_like(wb))
+        gb = o.get("bias", t.empty(p.c_out, dtype=t.float32, device=p.device))
+        ws = self.workspace()
+        fno_tucker_block_bwd(self.handle, x.data_ptr(), core.data_ptr(),
+                             [f.data_ptr() for f in factors], wb.data_ptr(), _ptr(bias),
+                             _ptr(save), grad_y.data_ptr(), _ptr(gx), _ptr(gcore),
+                             [_ptr(g) for g in gfac] if gfac is not None else None,
+                             _ptr(gwb), _ptr(gb), ws.data_ptr(), self.ws_bytes, p._stream())
+        return {"x": gx, "core": gcore, "factors": gfac, "wb": gwb, "bias": gb}
 
 
 def pointwise(x, w1, b1=None, w2=None, b2=None, out=None):

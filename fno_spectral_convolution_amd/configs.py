@@ -28,6 +28,8 @@ class Workload:
     proj_out: Optional[int] = None
     zero_bias: bool = False
     input_kind: str = "grf"       # grf | normal | grf_coords | grf_layered
+    tucker_ranks: Optional[Tuple[int, ...]] = None  # Tucker-factorised spectral weights
+                                  # (TFNO): ranks R_in, R_out, R_0..R_{d-1}
     notes: str = ""
 
     @property
@@ -68,6 +70,11 @@ WORKLOADS = {
                    notes="2D FNO training step, tanh + fp16 spectral path (static loss scale 2^16), fwd+bwd, MSE"),
     "st4d_128x20_f16": Workload("st4d_128x20_f16", 5, 1, 20, (128, 128, 128, 20), (12, 12, 12, 8), 4, "f16", False,
                     notes="4D space-time block stack forward, tanh + fp16"),
+    # TFNO: the 2D mixed-precision training step with Tucker-factorised spectral weights, every
+    # rank half its mode's extent (64 channels, 2 x 32 and 32 retained modes)
+    "train2d_512_tfno": Workload("train2d_512_tfno", 6, 8, 64, (512, 512), (32, 32), 4, True, True,
+                    tucker_ranks=(32, 32, 32, 16),
+                    notes="2D TFNO training step (Tucker ranks 32/32/32/16), tanh + bf16, fwd+bwd, MSE"),
 }
 
 # static loss scale of the IEEE-half training step: MSE gradients of a mean over ~10^8 elements

@@ -5,6 +5,9 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include <string>
+#include <vector>
+
 #include "fno.h"
 
 namespace fno {
@@ -126,6 +129,47 @@ hipError_t launch_mix_bwd_dx(const fno_plan* p, const float2* ghat, const float2
                              float2* ghx, hipStream_t s);
 hipError_t launch_mix_bwd_dw(const fno_plan* p, const float2* xhat, const float2* ghat,
                              float2* dw, hipStream_t s);
+// The same on an explicit geometry and per-mode weight offsets (woff[t] = offset of mode t
+// inside one [Cin][Cout] weight slab; input-channel stride Cout * Mprod, output stride Mprod).
+hipError_t launch_mix_fwd_g(const Geom& g, const int32_t* woff, const float2* xhat,
+                            const float2* w, float2* yhat, hipStream_t s);
+hipError_t launch_mix_bwd_dx_g(const Geom& g, const int32_t* woff, const float2* ghat,
+                               const float2* w, float2* ghx, hipStream_t s);
+hipError_t launch_mix_bwd_dw_g(const Geom& g, const int32_t* woff, const float2* xhat,
+                               const float2* ghat, float2* dw, hipStream_t s);
+
+// ---- Tucker-factorised weights (tucker.hip) ---------------------------------------------------
+constexpr int kTuckerMaxMat = 4096;          // entries of a factor matrix (at most 64 x 64)
+constexpr int64_t kTuckerPartElems = 1 << 20;  // complex partials of one factor gradient
+struct TuckerDims {
+  int d;
+  int64_t B;
+  int Cin, Cout;
+  int K[kMaxDims];       // retained extent of each mode: 2 m_j (outer axes), m_{d-1} (last)
+  int R[2 + kMaxDims];   // ranks: R_in, R_out, R_0 .. R_{d-1}
+};
+// One pairwise contraction of the Tucker network.  CORE: factor `factor` (0 in, 1 out, 2 + j
+// mode j) applied to the core's lineage; DATA_IN: U_in on the spectrum; MIX: the per-mode
+// channel mix; DATA_OUT: U_out on the mixed spectrum.  Mode products read [pre][cn][post] and
+// write [pre][an][post]; for MIX, cn / an are the contracted / output channels.
+struct TuckerStep {
+  enum Kind { CORE = 0, DATA_IN = 1, MIX = 2, DATA_OUT = 3 } kind;
+  int factor;
+  int64_t pre, post;
+  int an, cn;
+};
+std::vector<TuckerStep> tucker_greedy_order(const TuckerDims& t);
+std::string tucker_order_string(const std::vector<TuckerStep>& steps, int d);
+// out[p][a][q] = sum_c op(A)[a][c] T[p][c][q]; op(A) = A [an][cn], or A^T (A stored [cn][an])
+// when trans, conjugated when conj
+hipError_t launch_mode_product(int64_t pre, int an, int cn, int64_t post, const float2* A,
+                               bool trans, bool conj, const float2* T, float2* out,
+                               hipStream_t s);
+// out[a][c] = scale sum_{p,q} X[p][a][q] w(q) conj(Y[p][c][q]) (conjugated when conj_out),
+// w = gamma(q mod mb) * adj when gamma_w, else 1; part: kTuckerPartElems complex scratch
+hipError_t launch_gram(int64_t pre, int an, int cn, int64_t post, const float2* X,
+                       const float2* Y, bool gamma_w, int mb, int Nb, float adj, float scale,
+                       bool conj_out, float2* part, float2* out, hipStream_t s);
 hipError_t launch_reduce_parts(const float2* in, int nparts, int64_t part_stride, int64_t n,
                                float2* out, hipStream_t s);
 // Epilogue: last-axis inverse of T [B][C][lines][mb] plus the pointwise part.

@@ -276,53 +276,62 @@ static dim3 mix_grid(const Geom& g, int cols) {
               (unsigned)((g.B + 7) / 8));
 }
 
+hipError_t launch_mix_fwd_g(const Geom& g, const int32_t* woff, const float2* xhat,
+                            const float2* w, float2* yhat, hipStream_t s) {
+  if (g.half == 2)
+    hipLaunchKernelGGL((k_mix_mfma<2, false>), mix_grid(g, g.Cout), dim3(256), 0, s, g, woff,
+                       xhat, w, yhat);
+  else if (g.half == 1)
+    hipLaunchKernelGGL((k_mix_mfma<1, false>), mix_grid(g, g.Cout), dim3(256), 0, s, g, woff,
+                       xhat, w, yhat);
+  else
+    hipLaunchKernelGGL((k_mix_mfma<0, false>), mix_grid(g, g.Cout), dim3(256), 0, s, g, woff,
+                       xhat, w, yhat);
+  return hipGetLastError();
+}
+
+hipError_t launch_mix_bwd_dx_g(const Geom& g, const int32_t* woff, const float2* ghat,
+                               const float2* w, float2* ghx, hipStream_t s) {
+  if (g.half == 2)
+    hipLaunchKernelGGL((k_mix_mfma<2, true>), mix_grid(g, g.Cin), dim3(256), 0, s, g, woff,
+                       ghat, w, ghx);
+  else if (g.half == 1)
+    hipLaunchKernelGGL((k_mix_mfma<1, true>), mix_grid(g, g.Cin), dim3(256), 0, s, g, woff,
+                       ghat, w, ghx);
+  else
+    hipLaunchKernelGGL((k_mix_mfma<0, true>), mix_grid(g, g.Cin), dim3(256), 0, s, g, woff,
+                       ghat, w, ghx);
+  return hipGetLastError();
+}
+
+hipError_t launch_mix_bwd_dw_g(const Geom& g, const int32_t* woff, const float2* xhat,
+                               const float2* ghat, float2* dw, hipStream_t s) {
+  const dim3 grid((unsigned)((g.K + kMT - 1) / kMT), (unsigned)((g.Cin + 7) / 8),
+                  (unsigned)((g.Cout + 15) / 16));
+  if (g.half == 2)
+    hipLaunchKernelGGL((k_mix_mfma_dw<2>), grid, dim3(256), 0, s, g, woff, xhat, ghat, dw);
+  else if (g.half == 1)
+    hipLaunchKernelGGL((k_mix_mfma_dw<1>), grid, dim3(256), 0, s, g, woff, xhat, ghat, dw);
+  else
+    hipLaunchKernelGGL((k_mix_mfma_dw<0>), grid, dim3(256), 0, s, g, woff, xhat, ghat, dw);
+  return hipGetLastError();
+}
+
 hipError_t launch_mix_fwd(const fno_plan* p, const float2* xhat, int nparts,
                           int64_t part_stride, const float2* w, float2* yhat, hipStream_t s) {
   (void)nparts;
   (void)part_stride;
-  const Geom& g = p->g;
-  if (g.half == 2)
-    hipLaunchKernelGGL((k_mix_mfma<2, false>), mix_grid(g, g.Cout), dim3(256), 0, s, g,
-                       p->t.mode_woff, xhat, w, yhat);
-  else if (g.half == 1)
-    hipLaunchKernelGGL((k_mix_mfma<1, false>), mix_grid(g, g.Cout), dim3(256), 0, s, g,
-                       p->t.mode_woff, xhat, w, yhat);
-  else
-    hipLaunchKernelGGL((k_mix_mfma<0, false>), mix_grid(g, g.Cout), dim3(256), 0, s, g,
-                       p->t.mode_woff, xhat, w, yhat);
-  return hipGetLastError();
+  return launch_mix_fwd_g(p->g, p->t.mode_woff, xhat, w, yhat, s);
 }
 
 hipError_t launch_mix_bwd_dx(const fno_plan* p, const float2* ghat, const float2* w,
                              float2* ghx, hipStream_t s) {
-  const Geom& g = p->g;
-  if (g.half == 2)
-    hipLaunchKernelGGL((k_mix_mfma<2, true>), mix_grid(g, g.Cin), dim3(256), 0, s, g,
-                       p->t.mode_woff, ghat, w, ghx);
-  else if (g.half == 1)
-    hipLaunchKernelGGL((k_mix_mfma<1, true>), mix_grid(g, g.Cin), dim3(256), 0, s, g,
-                       p->t.mode_woff, ghat, w, ghx);
-  else
-    hipLaunchKernelGGL((k_mix_mfma<0, true>), mix_grid(g, g.Cin), dim3(256), 0, s, g,
-                       p->t.mode_woff, ghat, w, ghx);
-  return hipGetLastError();
+  return launch_mix_bwd_dx_g(p->g, p->t.mode_woff, ghat, w, ghx, s);
 }
 
 hipError_t launch_mix_bwd_dw(const fno_plan* p, const float2* xhat, const float2* ghat,
                              float2* dw, hipStream_t s) {
-  const Geom& g = p->g;
-  const dim3 grid((unsigned)((g.K + kMT - 1) / kMT), (unsigned)((g.Cin + 7) / 8),
-                  (unsigned)((g.Cout + 15) / 16));
-  if (g.half == 2)
-    hipLaunchKernelGGL((k_mix_mfma_dw<2>), grid, dim3(256), 0, s, g, p->t.mode_woff, xhat,
-                       ghat, dw);
-  else if (g.half == 1)
-    hipLaunchKernelGGL((k_mix_mfma_dw<1>), grid, dim3(256), 0, s, g, p->t.mode_woff, xhat,
-                       ghat, dw);
-  else
-    hipLaunchKernelGGL((k_mix_mfma_dw<0>), grid, dim3(256), 0, s, g, p->t.mode_woff, xhat,
-                       ghat, dw);
-  return hipGetLastError();
+  return launch_mix_bwd_dw_g(p->g, p->t.mode_woff, xhat, ghat, dw, s);
 }
 
 }  // namespace fno

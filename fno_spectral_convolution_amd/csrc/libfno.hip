@@ -689,6 +689,282 @@ int pre_mode(const fno_plan* p) {
   return (p->desc.flags & FNO_FLAG_TANH_PREACT) ? fno::PLANE_TANH : fno::PLANE_X;
 }
 
+// The spectral-weight step of a block: the dense per-mode mix, or a Tucker-factorised one.
+struct WeightMix {
+  virtual ~WeightMix() = default;
+  // xhat [B][Cin][K] -> yhat [B][Cout][K]
+  virtual fno_status fwd(const float2* xhat, float2* yhat, void* ws, hipStream_t s) const = 0;
+  // ghat [B][Cout][K] -> ghx [B][Cin][K] (when ghx is non-null) and the weight gradients
+  // (when wanted; they read xhat)
+  virtual fno_status bwd(const float2* xhat, const float2* ghat, float2* ghx, void* ws,
+                         hipStream_t s) const = 0;
+  virtual bool wants_weight_grad() const = 0;
+};
+
+struct DenseMix final : WeightMix {
+  const fno_plan* p;
+  const float2* w;
+  float2* grad_w;
+  DenseMix(const fno_plan* p_, const float* w_, float* gw_)
+      : p(p_), w(reinterpret_cast<const float2*>(w_)), grad_w(reinterpret_cast<float2*>(gw_)) {}
+  fno_status fwd(const float2* xhat, float2* yhat, void*, hipStream_t s) const override {
+    LAUNCH("mix_fwd", s, fno::launch_mix_fwd(p, xhat, 1, 0, w, yhat, s));
+    return FNO_OK;
+  }
+  fno_status bwd(const float2* xhat, const float2* ghat, float2* ghx, void*,
+                 hipStream_t s) const override {
+    if (grad_w) LAUNCH("mix_bwd_dw", s, fno::launch_mix_bwd_dw(p, xhat, ghat, grad_w, s));
+    if (ghx) LAUNCH("mix_bwd_dx", s, fno::launch_mix_bwd_dx(p, ghat, w, ghx, s));
+    return FNO_OK;
+  }
+  bool wants_weight_grad() const override { return grad_w != nullptr; }
+};
+
+// Block forward after argument checks: transform, weight step, inverse + epilogue.
+fno_status block_fwd_impl(const fno_plan* p, const float* x, const float* wb, const float* bias,
+                          float* y, void* save, void* ws, hipStream_t s, const WeightMix& mix) {
+  float2* xhat = save ? static_cast<float2*>(save) : at<float2>(ws, p->ws.xhat);
+  fno_status st = forward_transform(p, pre_mode(p), p->g.Cin, x, nullptr, xhat, ws, s);
+  if (st != FNO_OK) return st;
+  float2* yhat = at<float2>(ws, p->ws.yhat);
+  st = mix.fwd(xhat, yhat, ws, s);
+  if (st != FNO_OK) return st;
+  const float2* T = nullptr;
+  float* zsave = (save && (p->desc.flags & FNO_FLAG_GELU)) ? at<float>(save, p->save_off_z)
+                                                            : nullptr;
+  if (fno::epilogue_rows_ok(p, fno::EPI_BLOCK, x, y, zsave)) {
+    st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T, p->g.d - 2);
+    if (st != FNO_OK) return st;
+    LAUNCH("epilogue_rows_fwd", s, fno::launch_epilogue_rows(p, fno::EPI_BLOCK, T, x, wb, bias, y, zsave, s));
+    return FNO_OK;
+  }
+  st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T, p->g.d - 1);
+  if (st != FNO_OK) return st;
+  LAUNCH("epilogue_fwd", s, fno::launch_epilogue_fwd(p, fno::EPI_BLOCK, T, x, wb, bias, y, zsave, s));
+  return FNO_OK;
+}
+
+// Block backward after argument checks.
+fno_status block_bwd_impl(const fno_plan* p, const float* x, const float* wb, const void* save,
+                          const float* gy, float* grad_x, float* grad_wb, float* grad_bias,
+                          void* ws, hipStream_t s, const WeightMix& mix) {
+  const fno::Geom& g = p->g;
+  const bool gelu = (p->desc.flags & FNO_FLAG_GELU) != 0;
+  const float* z = gelu ? at<const float>(const_cast<void*>(save), p->save_off_z) : nullptr;
+  float2* ghat = at<float2>(ws, p->ws.yhat);
+  fno_status st = forward_transform(p, gelu ? fno::PLANE_GELU_GRAD : fno::PLANE_X, g.Cout, gy,
+                                    z, ghat, ws, s);
+  if (st != FNO_OK) return st;
+  float2* ghx = grad_x ? at<float2>(ws, p->ws.xhat) : nullptr;
+  if (mix.wants_weight_grad() || ghx) {
+    st = mix.bwd(static_cast<const float2*>(save), ghat, ghx, ws, s);
+    if (st != FNO_OK) return st;
+  }
+  float* red = (grad_wb || grad_bias) ? at<float>(ws, p->ws.red_part) : nullptr;
+  if (grad_x || red) {
+    const float2* Tg = nullptr;
+    if (grad_x) {
+      st = inverse_outer(p, g.Cin, ghx, ws, s, &Tg, g.d - 1);
+      if (st != FNO_OK) return st;
+    }
+    LAUNCH("epilogue_bwd", s, fno::launch_epilogue_bwd(p, fno::EPI_BLOCK, Tg, x, wb, gy, z, grad_x, red, s));
+    if (red)
+      LAUNCH("bypass_grad_finish", s, fno::launch_bypass_grad_finish(p, red, grad_wb, grad_bias, grad_x, s));
+  }
+  return FNO_OK;
+}
+
+}  // namespace
+
+// A Tucker-factorised weight bound to a plan: the greedy contraction order, the mix geometry
+// and the layout of its buffers behind the plan's own part of the workspace.
+struct fno_tucker {
+  const fno_plan* plan;
+  fno::TuckerDims dims;
+  int nf;                                   // factors: d + 2
+  std::vector<fno::TuckerStep> steps;
+  std::string order;
+  int core_steps;
+  bool in_on_data, out_on_data;
+  fno::Geom gmix;                           // the plan's geometry with the mix's channels
+  int32_t* ident_woff;                      // device [K]: t -> t
+  int64_t K;
+  int64_t core_elems;
+  int64_t factor_elems[2 + fno::kMaxDims];
+  std::vector<size_t> chain_off;            // result of each core step
+  size_t g0_off, g1_off, x1_off, t2_off, u_off, v_off, part_off, total;
+};
+
+namespace {
+
+fno_status tucker_dims(const fno_plan_desc* d, const int32_t* ranks, fno::TuckerDims* t) {
+  if (!ranks) return fail(FNO_ERR_INVALID_ARGUMENT, "ranks is NULL");
+  fno_status st = fno_plan_validate(d);
+  if (st != FNO_OK) return st;
+  t->d = d->ndim;
+  t->B = d->batch;
+  t->Cin = (int)d->c_in;
+  t->Cout = (int)d->c_out;
+  for (int j = 0; j < t->d; ++j) t->K[j] = (int)(j < t->d - 1 ? 2 * d->modes[j] : d->modes[j]);
+  const int ext[2] = {t->Cin, t->Cout};
+  for (int n = 0; n < t->d + 2; ++n) {
+    const int full = n < 2 ? ext[n] : t->K[n - 2];
+    if (ranks[n] < 1 || ranks[n] > full)
+      return fail(FNO_ERR_INVALID_ARGUMENT, "rank %d of mode %d outside 1..%d", ranks[n], n,
+                  full);
+    t->R[n] = ranks[n];
+  }
+  return FNO_OK;
+}
+
+const float2* f2c(const float* p) { return reinterpret_cast<const float2*>(p); }
+
+// The Tucker-factorised weight step (the greedy order of tucker.hip).
+struct TuckerMix final : WeightMix {
+  const fno_tucker* t;
+  const float2* core;
+  const float* const* fac;
+  float2* grad_core;
+  float* const* grad_fac;  // may be null (forward)
+  bool want_w;
+  TuckerMix(const fno_tucker* t_, const float* core_, const float* const* fac_,
+            float* gcore, float* const* gfac)
+      : t(t_), core(f2c(core_)), fac(fac_), grad_core(reinterpret_cast<float2*>(gcore)),
+        grad_fac(gfac) {
+    want_w = grad_core != nullptr;
+    for (int n = 0; gfac && n < t->nf; ++n) want_w = want_w || gfac[n] != nullptr;
+  }
+  float2* gf(int n) const { return grad_fac ? reinterpret_cast<float2*>(grad_fac[n]) : nullptr; }
+  bool wants_weight_grad() const override { return want_w; }
+
+  // the core's lineage: every core step in order; in[si] = the input of step si
+  fno_status core_chain(void* ws, hipStream_t s, std::vector<const float2*>* in,
+                        const float2** H) const {
+    const float2* cur = core;
+    int si = 0;
+    for (const fno::TuckerStep& st : t->steps) {
+      if (st.kind != fno::TuckerStep::CORE) continue;
+      float2* out = at<float2>(ws, t->chain_off[si]);
+      if (in) (*in)[si] = cur;
+      LAUNCH("tucker_mode", s, fno::launch_mode_product(st.pre, st.an, st.cn, st.post,
+                                                        f2c(fac[st.factor]), false, false, cur,
+                                                        out, s));
+      cur = out;
+      ++si;
+    }
+    *H = cur;
+    return FNO_OK;
+  }
+
+  fno_status fwd(const float2* xhat, float2* yhat, void* ws, hipStream_t s) const override {
+    const fno::TuckerDims& d = t->dims;
+    const float2* H = nullptr;
+    fno_status st = core_chain(ws, s, nullptr, &H);
+    if (st != FNO_OK) return st;
+    const float2* data = xhat;
+    if (t->in_on_data) {
+      float2* x1 = at<float2>(ws, t->x1_off);
+      LAUNCH("tucker_mode", s, fno::launch_mode_product(d.B, d.R[0], d.Cin, t->K, f2c(fac[0]),
+                                                        true, false, xhat, x1, s));
+      data = x1;
+    }
+    float2* mixed = t->out_on_data ? at<float2>(ws, t->t2_off) : yhat;
+    LAUNCH("tucker_mix_fwd", s, fno::launch_mix_fwd_g(t->gmix, t->ident_woff, data, H, mixed, s));
+    if (t->out_on_data)
+      LAUNCH("tucker_mode", s, fno::launch_mode_product(d.B, d.Cout, d.R[1], t->K, f2c(fac[1]),
+                                                        false, false, mixed, yhat, s));
+    return FNO_OK;
+  }
+
+  fno_status bwd(const float2* xhat, const float2* ghat, float2* ghx, void* ws,
+                 hipStream_t s) const override {
+    const fno::TuckerDims& d = t->dims;
+    const fno::Geom& g = t->plan->g;
+    float2* part = at<float2>(ws, t->part_off);
+    std::vector<const float2*> chain_in(t->core_steps, nullptr);
+    const float2* H = nullptr;
+    fno_status st = core_chain(ws, s, &chain_in, &H);
+    if (st != FNO_OK) return st;
+    // u = ghat with U_out's conjugate applied (when U_out acts on the data side)
+    const float2* u = ghat;
+    if (t->out_on_data) {
+      float2* ub = at<float2>(ws, t->u_off);
+      LAUNCH("tucker_mode", s, fno::launch_mode_product(d.B, d.R[1], d.Cout, t->K, f2c(fac[1]),
+                                                        true, true, ghat, ub, s));
+      u = ub;
+    }
+    float2* gH = at<float2>(ws, t->g0_off);
+    if (want_w) {
+      const float2* data = xhat;
+      if (t->in_on_data) {
+        float2* x1 = at<float2>(ws, t->x1_off);
+        LAUNCH("tucker_mode", s, fno::launch_mode_product(d.B, d.R[0], d.Cin, t->K,
+                                                          f2c(fac[0]), true, false, xhat, x1, s));
+        data = x1;
+      }
+      // gradient of the core-side tensor the mix reads
+      LAUNCH("tucker_mix_dw", s, fno::launch_mix_bwd_dw_g(t->gmix, t->ident_woff, data, u, gH, s));
+      if (t->out_on_data && gf(1)) {
+        float2* t2 = at<float2>(ws, t->t2_off);
+        LAUNCH("tucker_mix_fwd", s, fno::launch_mix_fwd_g(t->gmix, t->ident_woff, data, H, t2, s));
+        LAUNCH("tucker_gram", s, fno::launch_gram(d.B, d.Cout, d.R[1], t->K, ghat, t2, true,
+                                                  g.mb, g.Nb, g.adj_scale, g.inv_gain[0], false,
+                                                  part, gf(1), s));
+      }
+    }
+    // v = the mix's adjoint of u; the input gradient spectrum, or it before U_in
+    const bool need_v = ghx || (t->in_on_data && gf(0));
+    if (need_v) {
+      float2* v = t->in_on_data ? at<float2>(ws, t->v_off) : ghx;
+      LAUNCH("tucker_mix_dx", s, fno::launch_mix_bwd_dx_g(t->gmix, t->ident_woff, u, H, v, s));
+      if (t->in_on_data) {
+        if (ghx)
+          LAUNCH("tucker_mode", s, fno::launch_mode_product(d.B, d.Cin, d.R[0], t->K,
+                                                            f2c(fac[0]), false, true, v, ghx, s));
+        if (gf(0))
+          LAUNCH("tucker_gram", s, fno::launch_gram(d.B, d.Cin, d.R[0], t->K, xhat, v, false,
+                                                    g.mb, g.Nb, 1.0f, g.inv_gain[1], true,
+                                                    part, gf(0), s));
+      }
+    }
+    if (!want_w) return FNO_OK;
+    // the core's lineage in reverse: factor gradients, then the gradient of each step's input
+    float2* cur = gH;
+    float2* other = at<float2>(ws, t->g1_off);
+    int si = t->core_steps - 1;
+    for (int k = (int)t->steps.size() - 1; k >= 0; --k) {
+      const fno::TuckerStep& stp = t->steps[k];
+      if (stp.kind != fno::TuckerStep::CORE) continue;
+      if (gf(stp.factor))
+        LAUNCH("tucker_gram", s, fno::launch_gram(stp.pre, stp.an, stp.cn, stp.post, cur,
+                                                  chain_in[si], false, g.mb, g.Nb, 1.0f, 1.0f,
+                                                  false, part, gf(stp.factor), s));
+      float2* dst = si == 0 ? grad_core : other;
+      if (dst)
+        LAUNCH("tucker_mode", s, fno::launch_mode_product(stp.pre, stp.cn, stp.an, stp.post,
+                                                          f2c(fac[stp.factor]), true, true, cur,
+                                                          dst, s));
+      other = cur;
+      cur = dst;
+      --si;
+    }
+    return FNO_OK;
+  }
+};
+
+fno_status check_tucker_args(const fno_tucker* t, const float* core, const float* const* fac,
+                             void* ws, size_t ws_bytes) {
+  if (!t) return fail(FNO_ERR_INVALID_ARGUMENT, "tucker is NULL");
+  REQ(core, "core");
+  if (!fac) return fail(FNO_ERR_INVALID_ARGUMENT, "factors is NULL");
+  for (int n = 0; n < t->nf; ++n) REQ(fac[n], "factor");
+  REQ(ws, "workspace");
+  if (ws_bytes < t->total)
+    return fail(FNO_ERR_INVALID_ARGUMENT, "workspace %zu bytes < required %zu", ws_bytes,
+                t->total);
+  return FNO_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -735,25 +1011,8 @@ fno_status fno_block_fwd(const fno_plan* p, const float* x, const float* w, cons
   OPT(save, "save");
   fno_status st = check_ws(p, ws, ws_bytes);
   if (st != FNO_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  float2* xhat = save ? static_cast<float2*>(save) : at<float2>(ws, p->ws.xhat);
-  st = forward_transform(p, pre_mode(p), p->g.Cin, x, nullptr, xhat, ws, s);
-  if (st != FNO_OK) return st;
-  float2* yhat = at<float2>(ws, p->ws.yhat);
-  LAUNCH("mix_fwd", s, fno::launch_mix_fwd(p, xhat, 1, 0, reinterpret_cast<const float2*>(w), yhat, s));
-  const float2* T = nullptr;
-  float* zsave = (save && (p->desc.flags & FNO_FLAG_GELU)) ? at<float>(save, p->save_off_z)
-                                                            : nullptr;
-  if (fno::epilogue_rows_ok(p, fno::EPI_BLOCK, x, y, zsave)) {
-    st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T, p->g.d - 2);
-    if (st != FNO_OK) return st;
-    LAUNCH("epilogue_rows_fwd", s, fno::launch_epilogue_rows(p, fno::EPI_BLOCK, T, x, wb, bias, y, zsave, s));
-    return FNO_OK;
-  }
-  st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T, p->g.d - 1);
-  if (st != FNO_OK) return st;
-  LAUNCH("epilogue_fwd", s, fno::launch_epilogue_fwd(p, fno::EPI_BLOCK, T, x, wb, bias, y, zsave, s));
-  return FNO_OK;
+  return block_fwd_impl(p, x, wb, bias, y, save, ws, static_cast<hipStream_t>(stream),
+                        DenseMix(p, w, nullptr));
 }
 
 fno_status fno_spectral_conv_bwd(const fno_plan* p, const float* x, const float* w,
@@ -817,30 +1076,161 @@ fno_status fno_block_bwd(const fno_plan* p, const float* x, const float* w, cons
   OPT(grad_bias, "grad_bias");
   fno_status st = check_ws(p, ws, ws_bytes);
   if (st != FNO_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const fno::Geom& g = p->g;
-  const float* z = gelu ? at<const float>(const_cast<void*>(save), p->save_off_z) : nullptr;
-  float2* ghat = at<float2>(ws, p->ws.yhat);
-  st = forward_transform(p, gelu ? fno::PLANE_GELU_GRAD : fno::PLANE_X, g.Cout, gy, z, ghat,
-                         ws, s);
+  return block_bwd_impl(p, x, wb, save, gy, grad_x, grad_wb, grad_bias, ws,
+                        static_cast<hipStream_t>(stream), DenseMix(p, w, grad_w));
+}
+
+fno_status fno_tucker_order(const fno_plan_desc* desc, const int32_t* ranks, char* buf,
+                            size_t len) {
+  fno::TuckerDims d;
+  fno_status st = tucker_dims(desc, ranks, &d);
   if (st != FNO_OK) return st;
-  if (grad_w)
-    LAUNCH("mix_bwd_dw", s, fno::launch_mix_bwd_dw(p, static_cast<const float2*>(save), ghat,
-                                  reinterpret_cast<float2*>(grad_w), s));
-  float* red = (grad_wb || grad_bias) ? at<float>(ws, p->ws.red_part) : nullptr;
-  if (grad_x || red) {
-    const float2* Tg = nullptr;
-    if (grad_x) {
-      float2* ghx = at<float2>(ws, p->ws.xhat);
-      LAUNCH("mix_bwd_dx", s, fno::launch_mix_bwd_dx(p, ghat, reinterpret_cast<const float2*>(w), ghx, s));
-      st = inverse_outer(p, g.Cin, ghx, ws, s, &Tg, g.d - 1);
-      if (st != FNO_OK) return st;
+  const std::string o = fno::tucker_order_string(fno::tucker_greedy_order(d), d.d);
+  if (!buf || len < o.size() + 1)
+    return fail(FNO_ERR_INVALID_ARGUMENT, "buffer of %zu bytes < %zu", len, o.size() + 1);
+  memcpy(buf, o.c_str(), o.size() + 1);
+  return FNO_OK;
+}
+
+fno_status fno_tucker_create(const fno_plan* p, const int32_t* ranks, fno_tucker** out) {
+  if (!p || !out) return fail(FNO_ERR_INVALID_ARGUMENT, "plan or out is NULL");
+  *out = nullptr;
+  fno::TuckerDims d;
+  fno_status st = tucker_dims(&p->desc, ranks, &d);
+  if (st != FNO_OK) return st;
+  fno_tucker* t = new (std::nothrow) fno_tucker();
+  if (!t) return fail(FNO_ERR_OUT_OF_MEMORY, "host allocation");
+  t->plan = p;
+  t->dims = d;
+  t->nf = d.d + 2;
+  t->steps = fno::tucker_greedy_order(d);
+  t->order = fno::tucker_order_string(t->steps, d.d);
+  t->K = p->g.K;
+  t->core_elems = 1;
+  for (int n = 0; n < t->nf; ++n) t->core_elems *= d.R[n];
+  const int ext[2] = {d.Cin, d.Cout};
+  for (int n = 0; n < t->nf; ++n)
+    t->factor_elems[n] = (int64_t)(n < 2 ? ext[n] : d.K[n - 2]) * d.R[n];
+  // workspace: the plan's part, then the Tucker buffers
+  size_t off = align_up(p->ws.total);
+  auto take = [&](int64_t complex_elems) {
+    const size_t o = off;
+    off += align_up(sizeof(float2) * (size_t)complex_elems);
+    return o;
+  };
+  int64_t gmax = t->core_elems;
+  t->core_steps = 0;
+  t->in_on_data = t->out_on_data = false;
+  for (const fno::TuckerStep& stp : t->steps) {
+    if (stp.kind == fno::TuckerStep::CORE) {
+      const int64_t e = stp.pre * stp.an * stp.post;
+      t->chain_off.push_back(take(e));
+      gmax = e > gmax ? e : gmax;
+      ++t->core_steps;
+    } else if (stp.kind == fno::TuckerStep::DATA_IN) {
+      t->in_on_data = true;
+    } else if (stp.kind == fno::TuckerStep::DATA_OUT) {
+      t->out_on_data = true;
+    } else {
+      t->gmix = p->g;
+      t->gmix.Cin = stp.cn;
+      t->gmix.Cout = stp.an;
+      t->gmix.Mprod = p->g.K;
     }
-    LAUNCH("epilogue_bwd", s, fno::launch_epilogue_bwd(p, fno::EPI_BLOCK, Tg, x, wb, gy, z, grad_x, red, s));
-    if (red)
-      LAUNCH("bypass_grad_finish", s, fno::launch_bypass_grad_finish(p, red, grad_wb, grad_bias, grad_x, s));
+  }
+  t->g0_off = take(gmax);
+  t->g1_off = take(gmax);
+  const int64_t dR = (int64_t)d.B * t->K;
+  t->x1_off = take(t->in_on_data ? dR * d.R[0] : 0);
+  t->v_off = take(t->in_on_data ? dR * d.R[0] : 0);
+  t->t2_off = take(t->out_on_data ? dR * d.R[1] : 0);
+  t->u_off = take(t->out_on_data ? dR * d.R[1] : 0);
+  t->part_off = take(fno::kTuckerPartElems);
+  t->total = off;
+  // identity mode offsets: the core-side tensor [c_in][c_out][K] holds mode t at t
+  std::vector<int32_t> ident((size_t)t->K);
+  for (int64_t k = 0; k < t->K; ++k) ident[(size_t)k] = (int32_t)k;
+  t->ident_woff = nullptr;
+  hipError_t e = hipSetDevice(p->device);
+  if (e == hipSuccess) e = hipMalloc(&t->ident_woff, sizeof(int32_t) * ident.size());
+  if (e == hipSuccess)
+    e = hipMemcpy(t->ident_woff, ident.data(), sizeof(int32_t) * ident.size(),
+                  hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    if (t->ident_woff) (void)hipFree(t->ident_woff);
+    delete t;
+    return hip_fail(e, "fno_tucker_create");
+  }
+  *out = t;
+  return FNO_OK;
+}
+
+fno_status fno_tucker_destroy(fno_tucker* t) {
+  if (!t) return FNO_OK;
+  hipError_t e = hipSuccess;
+  if (t->ident_woff) e = hipFree(t->ident_woff);
+  delete t;
+  return e == hipSuccess ? FNO_OK : hip_fail(e, "fno_tucker_destroy");
+}
+
+fno_status fno_tucker_query(const fno_tucker* t, size_t* ws_bytes, int64_t* core_elems,
+                            int64_t* factor_elems, char* order, size_t order_len) {
+  if (!t) return fail(FNO_ERR_INVALID_ARGUMENT, "tucker is NULL");
+  if (ws_bytes) *ws_bytes = t->total;
+  if (core_elems) *core_elems = t->core_elems;
+  if (factor_elems)
+    for (int n = 0; n < t->nf; ++n) factor_elems[n] = t->factor_elems[n];
+  if (order) {
+    if (order_len < t->order.size() + 1)
+      return fail(FNO_ERR_INVALID_ARGUMENT, "order buffer of %zu bytes < %zu", order_len,
+                  t->order.size() + 1);
+    memcpy(order, t->order.c_str(), t->order.size() + 1);
   }
   return FNO_OK;
+}
+
+fno_status fno_tucker_block_fwd(const fno_tucker* t, const float* x, const float* core,
+                                const float* const* factors, const float* wb, const float* bias,
+                                float* y, void* save, void* ws, size_t ws_bytes, void* stream) {
+  fno_status st = check_tucker_args(t, core, factors, ws, ws_bytes);
+  if (st != FNO_OK) return st;
+  const fno_plan* p = t->plan;
+  REQ(x, "x");
+  REQ(wb, "w_bypass");
+  REQ(y, "y");
+  if (p->desc.flags & FNO_FLAG_BIAS) REQ(bias, "bias");
+  OPT(save, "save");
+  return block_fwd_impl(p, x, wb, bias, y, save, ws, static_cast<hipStream_t>(stream),
+                        TuckerMix(t, core, factors, nullptr, nullptr));
+}
+
+fno_status fno_tucker_block_bwd(const fno_tucker* t, const float* x, const float* core,
+                                const float* const* factors, const float* wb, const float* bias,
+                                const void* save, const float* gy, float* grad_x,
+                                float* grad_core, float* const* grad_factors, float* grad_wb,
+                                float* grad_bias, void* ws, size_t ws_bytes, void* stream) {
+  (void)bias;
+  fno_status st = check_tucker_args(t, core, factors, ws, ws_bytes);
+  if (st != FNO_OK) return st;
+  const fno_plan* p = t->plan;
+  REQ(x, "x");
+  REQ(wb, "w_bypass");
+  REQ(gy, "grad_y");
+  OPT(grad_x, "grad_x");
+  OPT(grad_core, "grad_core");
+  OPT(grad_wb, "grad_w_bypass");
+  OPT(grad_bias, "grad_bias");
+  bool want_w = grad_core != nullptr;
+  for (int n = 0; grad_factors && n < t->nf; ++n) {
+    OPT(grad_factors[n], "grad_factor");
+    want_w = want_w || grad_factors[n] != nullptr;
+  }
+  const bool gelu = (p->desc.flags & FNO_FLAG_GELU) != 0;
+  if (gelu || want_w) REQ(save, "save");
+  OPT(save, "save");
+  return block_bwd_impl(p, x, wb, save, gy, grad_x, grad_wb, grad_bias, ws,
+                        static_cast<hipStream_t>(stream),
+                        TuckerMix(t, core, factors, grad_core, grad_factors));
 }
 
 fno_status fno_pointwise_fwd(int64_t batch, int64_t npts, int64_t cin, int64_t hidden,

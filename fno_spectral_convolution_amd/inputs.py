@@ -7,7 +7,7 @@ the other through it.  Every array is generated on the host in float64 from
 so the GPU and the oracle receive byte-identical values.
 
 Streams: 0 input field, 1 spectral weights, 2 bypass weights, 3 bias, 4 target field,
-5 lift/projection weights, 6 permeability layers.
+5 lift/projection weights, 6 permeability layers, 7 Tucker core and factors.
 
 The pages' datasets (CO2 plume simulations, the mixed-precision study's PDE datasets) are
 not available; these fields stand in for them with the same shapes:
@@ -22,8 +22,8 @@ from __future__ import annotations
 import numpy as np
 import scipy.fft as _sfft
 
-STREAM_INPUT, STREAM_W, STREAM_WB, STREAM_BIAS, STREAM_TARGET, STREAM_PROJ, STREAM_LAYERS = \
-    range(7)
+(STREAM_INPUT, STREAM_W, STREAM_WB, STREAM_BIAS, STREAM_TARGET, STREAM_PROJ, STREAM_LAYERS,
+ STREAM_TUCKER) = range(8)
 
 
 def rng(cfg_id: int, stream: int, index: int = 0) -> np.random.Generator:
@@ -134,11 +134,37 @@ def bias(w, block: int = 0, cin=None, cout=None) -> np.ndarray:
     return rng(w.cfg_id, STREAM_BIAS, block).uniform(-lim, lim, cout).astype(np.float32)
 
 
+def tucker_params(w, block: int = 0, cin=None, cout=None, modes=None, ranks=None):
+    """Tucker core [R_in, R_out, R_0..] and factors [C_in, R_in], [C_out, R_out], [2 m_j, R_j],
+    [m_{d-1}, R_{d-1}] as complex64: factor entries complex normal with variance 1/extent (unit
+    expected column norm), core entries complex normal times 1/(C_in C_out)."""
+    cin = cin or w.width
+    cout = cout or w.width
+    modes = tuple(modes or w.modes)
+    ranks = tuple(ranks or w.tucker_ranks)
+    ext = [cin, cout] + [2 * m for m in modes[:-1]] + [modes[-1]]
+    g = rng(w.cfg_id, STREAM_TUCKER, block)
+    factors = []
+    for n, r in zip(ext, ranks):
+        u = (g.standard_normal((n, r)) + 1j * g.standard_normal((n, r))) / np.sqrt(2.0 * n)
+        factors.append(u.astype(np.complex64))
+    core = (g.standard_normal(ranks) + 1j * g.standard_normal(ranks)) / (cin * cout)
+    return core.astype(np.complex64), factors
+
+
 def block_params(w, n_blocks=None):
-    """Per-block parameter dicts (w, wb, bias) for ``n_blocks`` blocks."""
+    """Per-block parameter dicts for ``n_blocks`` blocks: (w, wb, bias), or (core, factors,
+    wb, bias) for workloads with Tucker-factorised spectral weights."""
     n = w.blocks if n_blocks is None else n_blocks
-    return [{"w": spectral_weights(w, i), "wb": bypass_weights(w, i), "bias": bias(w, i)}
-            for i in range(n)]
+    out = []
+    for i in range(n):
+        blk = {"wb": bypass_weights(w, i), "bias": bias(w, i)}
+        if getattr(w, "tucker_ranks", None):
+            blk["core"], blk["factors"] = tucker_params(w, i)
+        else:
+            blk["w"] = spectral_weights(w, i)
+        out.append(blk)
+    return out
 
 
 def lift_proj_params(w):

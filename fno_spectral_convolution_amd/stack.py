@@ -3,7 +3,8 @@
 ``StackRunner(workload).step()`` runs one pass of a workload: an optional pointwise lift,
 the spectral blocks (GELU after each), an optional projection head, and for training
 workloads the MSE loss against a target and the backward through every block (input,
-spectral-weight, bypass-weight and bias gradients).  Torch provides device memory and the
+spectral-weight, bypass-weight and bias gradients).  Workloads with Tucker ranks hold each
+block's spectral weight as a Tucker core and factors (TFNO) and run the Tucker entry points.  Torch provides device memory and the
 stream; all arithmetic runs in libfno's kernels.
 
 ``PrecisionSchedule`` with ``StackRunner.run`` moves a training run from a half-precision
@@ -63,14 +64,21 @@ class StackRunner:
         # workspace); the workload's tanh pre-activation is kept by all of them
         self._tanh = bool(wl.mixed)
         self._plans = {}
+        self._tuckers = {}
+        self.tucker = bool(wl.tucker_ranks)
         self.precision = precision(wl)
         self.plan = self._plan_for(self.precision)
+        self.tk = self._tuckers.get(self.precision)
         # IEEE-half training takes a static loss scale: every gradient the step returns
         # (weights, bypass, bias, input) comes out multiplied by grad_scale
         self.grad_scale = F16_LOSS_SCALE if self.precision == "f16" else 1.0
         hi = host_inputs or make_host_inputs(wl)
         self.host = hi
-        to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+        def to(a):
+            if isinstance(a, list):
+                return [to(v) for v in a]
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
         self.params = [{k: to(v) for k, v in blk.items()} for blk in hi["blocks"]]
         self.x_in = to(hi["x"])
         self.target = to(hi["target"]) if wl.train else None
@@ -87,8 +95,15 @@ class StackRunner:
             self.saves = [self.plan.new_save() for _ in range(nb)]
             self._save_bytes = self.plan.save_bytes
             self.g = [torch.empty(shape, dtype=torch.float32, device=dev) for _ in range(2)]
-            self.grads = [{"w": torch.empty_like(p["w"]), "wb": torch.empty_like(p["wb"]),
-                           "bias": torch.empty_like(p["bias"])} for p in self.params]
+            self.grads = []
+            for p in self.params:
+                gr = {"wb": torch.empty_like(p["wb"]), "bias": torch.empty_like(p["bias"])}
+                if self.tucker:
+                    gr["core"] = torch.empty_like(p["core"])
+                    gr["factors"] = [torch.empty_like(u) for u in p["factors"]]
+                else:
+                    gr["w"] = torch.empty_like(p["w"])
+                self.grads.append(gr)
             self.loss = torch.empty(1, dtype=torch.float32, device=dev)
             self.mse_ws = torch.empty(max(L.fno_mse_workspace_bytes(self.acts[-1].numel()), 16),
                                       dtype=torch.uint8, device=dev)
@@ -106,7 +121,12 @@ class StackRunner:
             wl = self.wl
             plan = L.Plan(wl.batch, wl.width, wl.width, wl.grid, wl.modes,
                           mixed=_PLAN_MIXED[prec], tanh=self._tanh, device=self.device)
-            plan.workspace()
+            if wl.tucker_ranks:
+                tk = L.Tucker(plan, wl.tucker_ranks)
+                tk.workspace()
+                self._tuckers[prec] = tk
+            else:
+                plan.workspace()
             self._plans[prec] = plan
         return self._plans[prec]
 
@@ -123,6 +143,7 @@ class StackRunner:
             self.saves = [plan.new_save() for _ in range(self.wl.blocks)]
             self._save_bytes = plan.save_bytes
         self.plan = plan
+        self.tk = self._tuckers.get(prec)
         self.precision = prec
         self.grad_scale = F16_LOSS_SCALE if prec == "f16" else 1.0
 
@@ -152,7 +173,11 @@ class StackRunner:
         h = src0
         for i, p in enumerate(self.params):
             dst = self._act(i + 1)
-            self.plan.block_fwd(h, p["w"], p["wb"], p["bias"], save=self.saves[i], out=dst)
+            if self.tucker:
+                self.tk.block_fwd(h, p["core"], p["factors"], p["wb"], p["bias"],
+                                  save=self.saves[i], out=dst)
+            else:
+                self.plan.block_fwd(h, p["w"], p["wb"], p["bias"], save=self.saves[i], out=dst)
             h = dst
         if self.lp is not None:
             pr = self.lp["proj"]
@@ -166,8 +191,13 @@ class StackRunner:
                 p = self.params[i]
                 x_i = src0 if i == 0 else self.acts[i]
                 gout = 1 - gin
-                self.plan.block_bwd(x_i, p["w"], p["wb"], p["bias"], self.saves[i], self.g[gin],
-                                    out={"x": self.g[gout], **self.grads[i]})
+                if self.tucker:
+                    self.tk.block_bwd(x_i, p["core"], p["factors"], p["wb"], p["bias"],
+                                      self.saves[i], self.g[gin],
+                                      out={"x": self.g[gout], **self.grads[i]})
+                else:
+                    self.plan.block_bwd(x_i, p["w"], p["wb"], p["bias"], self.saves[i],
+                                        self.g[gin], out={"x": self.g[gout], **self.grads[i]})
                 gin = gout
             self.grad_x = self.g[gin]
         return h

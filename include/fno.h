@@ -152,6 +152,63 @@ fno_status fno_block_bwd(const fno_plan* plan, const float* x, const float* w,
                          float* grad_w_bypass, float* grad_bias, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* ---- Tucker-factorised spectral weights (TFNO) ----------------------------------------------
+ * TFNO is one of the architectures trained in mixed precision on the mixed-precision
+ * neural-operator page ("Tiivistelmä"), together with a greedy algorithm ordering the block's
+ * half-precision tensor contractions.  The weight on the retained grid,
+ *   W[i, o, s_0, .., s_{d-1}]   (s_j < 2 m_j on outer axes, low modes first; s_{d-1} < m_{d-1}),
+ * is a Tucker form: W = G x_1 U_in x_2 U_out x_3 U_0 .. x_{d+2} U_{d-1}, where the mode-n
+ * product replaces a core index r by a: (T x_n U)[.., a, ..] = sum_r T[.., r, ..] U[a, r].
+ * Device layouts (interleaved complex64, row-major): core G [R_in][R_out][R_0]..[R_{d-1}],
+ * U_in [C_in][R_in], U_out [C_out][R_out], U_j [2 m_j][R_j] (j < d-1), U_{d-1} [m_{d-1}][R_{d-1}].
+ * A dense weight w of fno_block_fwd equals W with corner c taking s_j in the high half of
+ * axis j exactly when bit j of c is set.
+ * The block computes the mix without forming W where that is smaller: a greedy order takes,
+ * of the contractions available (a factor applied to the core, U_in applied to the spectrum,
+ * the per-mode channel mix once the core carries every mode, U_out applied to the mixed
+ * spectrum), the one with the smallest result first (ties: fewer flops).  The mix runs in the
+ * plan's spectral precision; the factor products in float32.  ranks: d + 2 values R_in, R_out,
+ * R_0 .. R_{d-1}, each in 1 .. its mode's extent (else INVALID_ARGUMENT). */
+typedef struct fno_tucker fno_tucker;
+
+/* Host only (no HIP call): the greedy contraction order for a descriptor and ranks, as a
+ * space-separated list of steps, e.g. "G*U1 G*U0 X*Uin mix Y*Uout" (G*Un: factor n of the
+ * modes applied to the core; G*Uin / G*Uout: a channel factor applied to the core; X*Uin:
+ * U_in on the spectrum; mix; Y*Uout: U_out on the mixed spectrum).  buf receives it with its
+ * terminating NUL (INVALID_ARGUMENT when len is too small). */
+fno_status fno_tucker_order(const fno_plan_desc* desc, const int32_t* ranks, char* buf,
+                            size_t len);
+
+/* Bind Tucker ranks to a plan (which must outlive the result): the order above, the workspace
+ * layout, and one small device table (K int32).  *out receives the object. */
+fno_status fno_tucker_create(const fno_plan* plan, const int32_t* ranks, fno_tucker** out);
+fno_status fno_tucker_destroy(fno_tucker* tucker);  /* NULL accepted */
+
+/* Workspace bytes of the Tucker calls (they replace the plan's own workspace size), complex
+ * elements of the core and of each of the d + 2 factors, and the contraction order (as
+ * fno_tucker_order).  Any output pointer may be NULL. */
+fno_status fno_tucker_query(const fno_tucker* tucker, size_t* workspace_bytes,
+                            int64_t* core_elems, int64_t* factor_elems, char* order,
+                            size_t order_len);
+
+/* fno_block_fwd with the Tucker weight (core + factors: a host array of d + 2 device
+ * pointers, in the order U_in, U_out, U_0 .. U_{d-1}).  The save buffer is the plan's. */
+fno_status fno_tucker_block_fwd(const fno_tucker* tucker, const float* x, const float* core,
+                                const float* const* factors, const float* w_bypass,
+                                const float* bias, float* y, void* save, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* fno_block_bwd with the Tucker weight: grad_core (the core's layout) and grad_factors (a host
+ * array of d + 2 device pointers, each nullable; the array itself may be NULL) replace grad_w.
+ * The gradient convention is W's (dL/dRe + i dL/dIm); save is required when FNO_FLAG_GELU is
+ * set or any weight gradient is asked for. */
+fno_status fno_tucker_block_bwd(const fno_tucker* tucker, const float* x, const float* core,
+                                const float* const* factors, const float* w_bypass,
+                                const float* bias, const void* save, const float* grad_y,
+                                float* grad_x, float* grad_core, float* const* grad_factors,
+                                float* grad_w_bypass, float* grad_bias, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Pointwise layers used to lift into and project out of the block stack.
  * hidden == 0: y = w1 x + b1            (w1 [c_out][c_in], b1 [c_out])
  * hidden  > 0: y = w2 GELU(w1 x + b1) + b2 (w1 [hidden][c_in], w2 [c_out][hidden])

@@ -1,0 +1,125 @@
+"""Tucker-factorised (TFNO) block through the C-ABI against the fp64 oracle.
+
+Each case runs fno_tucker_block_fwd / _bwd and compares y, grad_x, grad_core, every factor
+gradient, grad_w_bypass and grad_bias with the oracle's tucker_block_fwd / _bwd (relative L2,
+the tolerances of the plain block: 1e-5 fp32, 1e-2 tanh + bf16, 1.25e-3 tanh + IEEE half).
+The shapes take both forms of the greedy order: factors applied to the spectrum around a
+rank-sized mix, and every factor applied to the core (the dense weight formed) when the batch
+is large; also rank 1, C_in != C_out, 3D and a 4D grid with a 20-point last axis.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle.fno_oracle as O
+from fno_spectral_convolution_amd import inputs
+from tests.gpu_helpers import announce, check, tol_for
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # name, batch, cin, cout, grid, modes, ranks, expected fragment of the order
+    ("2d_half_ranks", 2, 16, 16, (24, 64), (5, 12), (8, 8, 6, 6), "X*Uin"),
+    ("2d_core_side", 64, 4, 4, (16, 32), (4, 8), (4, 4, 8, 8), "G*Uin"),
+    ("2d_rank_one", 3, 5, 7, (16, 20), (3, 6), (1, 1, 1, 1), None),
+    ("2d_ragged", 2, 6, 3, (15, 9), (7, 5), (4, 2, 9, 3), None),
+    ("3d", 2, 6, 5, (8, 12, 16), (2, 3, 5), (3, 4, 2, 3, 4), None),
+    ("4d_t20", 1, 3, 4, (4, 6, 8, 20), (2, 2, 3, 8), (2, 3, 2, 3, 4, 5), None),
+    ("2d_wide", 2, 64, 64, (32, 64), (8, 16), (32, 32, 8, 8), "X*Uin"),
+]
+PRECISIONS = [("f32", False), ("mixed", True), ("f16", "f16")]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(a):
+    return _torch().from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def _host(t):
+    return t.detach().cpu().numpy()
+
+
+def _tucker_params(seed, cin, cout, modes, ranks):
+    """Seeded core and factors: unit-column factors and a core of size 1/(C_in C_out)."""
+    g = np.random.default_rng(np.random.SeedSequence([3000, seed]))
+    ext = [cin, cout] + [2 * m for m in modes[:-1]] + [modes[-1]]
+    facs = []
+    for n, r in zip(ext, ranks):
+        u = (g.standard_normal((n, r)) + 1j * g.standard_normal((n, r))) / np.sqrt(2.0 * n)
+        facs.append(u.astype(np.complex64))
+    core = ((g.standard_normal(ranks) + 1j * g.standard_normal(ranks))
+            / (cin * cout)).astype(np.complex64)
+    return core, facs
+
+
+@pytest.fixture(scope="module")
+def L():
+    from fno_spectral_convolution_amd import binding
+    return binding
+
+
+@pytest.mark.parametrize("prec", PRECISIONS, ids=[p[0] for p in PRECISIONS])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_tucker_block_fwd_bwd(L, case, prec):
+    name, batch, cin, cout, grid, modes, ranks, frag = case
+    pname, mixed = prec
+    seed = zlib.crc32(name.encode()) % 1000
+    x, _, wb, b = inputs.small_case(seed, batch, cin, cout, grid, modes)
+    gy = inputs.normal_like(seed, (batch, cout) + grid)
+    core, facs = _tucker_params(seed, cin, cout, modes, ranks)
+    plan = L.Plan(batch, cin, cout, grid, modes, mixed=mixed)
+    tk = L.Tucker(plan, ranks)
+    announce("tucker", name, pname, tk.order)
+    if frag is not None:
+        assert frag in tk.order.split(), tk.order
+    tol = tol_for(mixed)
+    tx, twb, tb, tg, tcore = (_dev(a) for a in (x, wb, b, gy, core))
+    tfac = [_dev(u) for u in facs]
+    save = plan.new_save()
+    y = tk.block_fwd(tx, tcore, tfac, twb, tb, save=save)
+    gr = tk.block_bwd(tx, tcore, tfac, twb, tb, save, tg)
+    _torch().cuda.synchronize()
+    ref = O.tucker_block_bwd(x, core, facs, wb, b, modes, gy, tanh=bool(mixed))
+    check("y", _host(y), ref["fwd"]["y"], tol)
+    check("grad_x", _host(gr["x"]), ref["grad_x"], tol)
+    check("grad_core", _host(gr["core"]), ref["grad_core"], tol)
+    for n, (got, want) in enumerate(zip(gr["factors"], ref["grad_factors"])):
+        check(f"grad_factor {n}", _host(got), want, tol)
+    check("grad_wb", _host(gr["wb"]), ref["grad_wb"], tol)
+    check("grad_bias", _host(gr["bias"]), ref["grad_bias"], tol)
+    tk.close()
+    plan.close()
+
+
+def test_tucker_partial_outputs_and_determinism(L):
+    """grad_x alone (no weight gradients, no save read for them), weight gradients alone, and
+    a second call giving bit-identical results."""
+    name, batch, cin, cout, grid, modes, ranks, _ = CASES[0]
+    announce("tucker partial", name)
+    x, _, wb, b = inputs.small_case(7, batch, cin, cout, grid, modes)
+    gy = inputs.normal_like(7, (batch, cout) + grid)
+    core, facs = _tucker_params(7, cin, cout, modes, ranks)
+    plan = L.Plan(batch, cin, cout, grid, modes)
+    tk = L.Tucker(plan, ranks)
+    tx, twb, tb, tg, tcore = (_dev(a) for a in (x, wb, b, gy, core))
+    tfac = [_dev(u) for u in facs]
+    save = plan.new_save()
+    tk.block_fwd(tx, tcore, tfac, twb, tb, save=save)
+    full = tk.block_bwd(tx, tcore, tfac, twb, tb, save, tg)
+    only_x = tk.block_bwd(tx, tcore, tfac, twb, tb, save, tg, want_w=False)
+    only_w = tk.block_bwd(tx, tcore, tfac, twb, tb, save, tg, want_x=False)
+    again = tk.block_bwd(tx, tcore, tfac, twb, tb, save, tg)
+    _torch().cuda.synchronize()
+    assert np.array_equal(_host(full["x"]), _host(only_x["x"]))
+    assert np.array_equal(_host(full["core"]), _host(only_w["core"]))
+    for a, c in zip(full["factors"], only_w["factors"]):
+        assert np.array_equal(_host(a), _host(c))
+    for k in ("x", "core", "wb", "bias"):
+        assert np.array_equal(_host(full[k]), _host(again[k]))
+    tk.close()
+    plan.close()

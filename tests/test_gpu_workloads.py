@@ -90,6 +90,43 @@ def _block_case(L, name, grad_scale):
     sp.close()
 
 
+def _tucker_block_case(L, name, grad_scale):
+    """One Tucker-factorised block of the workload at full size, forward and backward."""
+    wl = configs.get(name)
+    tol = tol_for(wl.mixed)
+    x = _field(wl)
+    blk = inputs.block_params(wl, 1)[0]
+    gy = _grad_in(wl, grad_scale)
+    plan = L.Plan(wl.batch, wl.width, wl.width, wl.grid, wl.modes, mixed=wl.mixed)
+    tk = L.Tucker(plan, wl.tucker_ranks)
+    announce("workload tucker block", name, wl.batch, wl.width, wl.grid, wl.modes,
+             wl.tucker_ranks, tk.order)
+    tx, twb, tb, tg, tcore = (_dev(a) for a in (x, blk["wb"], blk["bias"], gy, blk["core"]))
+    tfac = [_dev(u) for u in blk["factors"]]
+    save = plan.new_save()
+    y = tk.block_fwd(tx, tcore, tfac, twb, tb, save=save)
+    g = tk.block_bwd(tx, tcore, tfac, twb, tb, save, tg)
+    _torch().cuda.synchronize()
+    got = {"y": _host(y), "grad_x": _host(g["x"]), "grad_core": _host(g["core"]),
+           "grad_wb": _host(g["wb"]), "grad_bias": _host(g["bias"]),
+           "grad_factors": [_host(u) for u in g["factors"]]}
+    del save, g
+    ref = O.tucker_block_bwd(x, blk["core"], blk["factors"], blk["wb"], blk["bias"], wl.modes,
+                             gy, tanh=bool(wl.mixed))
+    check("y", got["y"], ref["fwd"]["y"], tol)
+    check("y error against |y_spec|", got["y"] - ref["fwd"]["y"] + ref["fwd"]["y_spec"],
+          ref["fwd"]["y_spec"],
+          tol)
+    check("grad_x", got["grad_x"], ref["grad_x"], tol)
+    check("grad_core", got["grad_core"], ref["grad_core"], tol)
+    for n, (a, b) in enumerate(zip(got["grad_factors"], ref["grad_factors"])):
+        check(f"grad_factor {n}", a, b, tol)
+    check("grad_wb", got["grad_wb"], ref["grad_wb"], tol)
+    check("grad_bias", got["grad_bias"], ref["grad_bias"], tol)
+    tk.close()
+    plan.close()
+
+
 def test_layer2d_64_block_full(L):
     _block_case(L, "layer2d_64", 1.0)
 
@@ -100,6 +137,10 @@ def test_train2d_512_block_full(L):
 
 def test_train2d_512_f16_block_full(L):
     _block_case(L, "train2d_512_f16", 1e-3)
+
+
+def test_train2d_512_tfno_block_full(L):
+    _tucker_block_case(L, "train2d_512_tfno", 1e-3)
 
 
 def test_train3d_128_block_full(L):
