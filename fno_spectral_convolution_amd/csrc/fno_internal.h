@@ -28,6 +28,8 @@ struct Geom {
   int64_t P;           // points per field = prod N_j
   int64_t K;           // retained modes per (batch, channel) = prod_{j<d-1} 2 m_j * m_b
   int64_t Mprod;       // prod m_j (weights per corner per (i, o))
+  int w_si, w_so;      // mix weight strides of the input / output channel (Cout Mprod, Mprod
+                       // in W's corner layout)
   int ncorner;
   float inv_ntot;      // 1 / P
   bool bf16;           // spectral operands in a 16-bit format (half)

@@ -110,10 +110,9 @@ __global__ void __launch_bounds__(256) k_mix_mfma(Geom g, const int32_t* __restr
   const int Ki = (int)K;
   const float sc = DX ? mix_scale(g, tm) : 1.0f;
   // weight u of this thread: contracted channel c0 + u, column n0 + (tid >> 4)
-  const int wsi = g.Cout * (int)g.Mprod;  // W stride of the input channel
   const int ncol = min(n0 + (tid >> 4), nout - 1);
-  const int wbase = mode_woff[tm] + (DX ? ncol * wsi : ncol * (int)g.Mprod);
-  const int wstep = DX ? (int)g.Mprod : wsi;
+  const int wbase = mode_woff[tm] + ncol * (DX ? g.w_si : g.w_so);
+  const int wstep = DX ? g.w_so : g.w_si;
   float2 pw[NW], ps[NS];
   auto load_chunk = [&](int c0) {
 #pragma unroll
@@ -264,7 +263,7 @@ __global__ void __launch_bounds__(256) k_mix_mfma_dw(Geom g, const int32_t* __re
       if (i0 + ii < g.Cin && o0 + oo < g.Cout) {
         const float2 v =
             *reinterpret_cast<const float2*>(s_out + tl * kOutTB + (ii * 16 + oo) * 8);
-        dw[wmode + ((int64_t)(i0 + ii) * g.Cout + o0 + oo) * g.Mprod] = v;
+        dw[wmode + (int64_t)(i0 + ii) * g.w_si + (int64_t)(o0 + oo) * g.w_so] = v;
       }
     }
   }

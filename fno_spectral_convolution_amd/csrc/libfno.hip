@@ -184,6 +184,8 @@ fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out) {
     g.Mprod *= g.M[j];
     g.K *= (j == g.d - 1) ? g.M[j] : 2 * g.M[j];
   }
+  g.w_si = (int)(g.Cout * g.Mprod);
+  g.w_so = (int)g.Mprod;
   g.Na = g.N[g.d - 2];
   g.Nb = g.N[g.d - 1];
   g.ma = g.M[g.d - 2];
@@ -787,7 +789,11 @@ struct fno_tucker {
   int core_steps;
   bool in_on_data, out_on_data;
   fno::Geom gmix;                           // the plan's geometry with the mix's channels
-  int32_t* ident_woff;                      // device [K]: t -> t
+  // U_in / U_out on the spectrum as fp32 mix launches with one weight for every mode:
+  // g_in (C_in -> R_in; adjoint R_in -> C_in), g_out (R_out -> C_out; adjoint C_out -> R_out)
+  fno::Geom g_in, g_out;
+  int32_t* ident_woff;                      // device [2 K]: [0, K) t -> t, then K zeros
+  const int32_t* zero_woff;
   int64_t K;
   int64_t core_elems;
   int64_t factor_elems[2 + fno::kMaxDims];
@@ -846,7 +852,7 @@ struct TuckerMix final : WeightMix {
       if (st.kind != fno::TuckerStep::CORE) continue;
       float2* out = at<float2>(ws, t->chain_off[si]);
       if (in) (*in)[si] = cur;
-      LAUNCH("tucker_mode", s, fno::launch_mode_product(st.pre, st.an, st.cn, st.post,
+      LAUNCH("tucker_core", s, fno::launch_mode_product(st.pre, st.an, st.cn, st.post,
                                                         f2c(fac[st.factor]), false, false, cur,
                                                         out, s));
       cur = out;
@@ -857,22 +863,21 @@ struct TuckerMix final : WeightMix {
   }
 
   fno_status fwd(const float2* xhat, float2* yhat, void* ws, hipStream_t s) const override {
-    const fno::TuckerDims& d = t->dims;
     const float2* H = nullptr;
     fno_status st = core_chain(ws, s, nullptr, &H);
     if (st != FNO_OK) return st;
     const float2* data = xhat;
     if (t->in_on_data) {
       float2* x1 = at<float2>(ws, t->x1_off);
-      LAUNCH("tucker_mode", s, fno::launch_mode_product(d.B, d.R[0], d.Cin, t->K, f2c(fac[0]),
-                                                        true, false, xhat, x1, s));
+      LAUNCH("tucker_data", s, fno::launch_mix_fwd_g(t->g_in, t->zero_woff, xhat, f2c(fac[0]),
+                                                     x1, s));
       data = x1;
     }
     float2* mixed = t->out_on_data ? at<float2>(ws, t->t2_off) : yhat;
     LAUNCH("tucker_mix_fwd", s, fno::launch_mix_fwd_g(t->gmix, t->ident_woff, data, H, mixed, s));
     if (t->out_on_data)
-      LAUNCH("tucker_mode", s, fno::launch_mode_product(d.B, d.Cout, d.R[1], t->K, f2c(fac[1]),
-                                                        false, false, mixed, yhat, s));
+      LAUNCH("tucker_data", s, fno::launch_mix_fwd_g(t->g_out, t->zero_woff, mixed, f2c(fac[1]),
+                                                     yhat, s));
     return FNO_OK;
   }
 
@@ -889,8 +894,8 @@ struct TuckerMix final : WeightMix {
     const float2* u = ghat;
     if (t->out_on_data) {
       float2* ub = at<float2>(ws, t->u_off);
-      LAUNCH("tucker_mode", s, fno::launch_mode_product(d.B, d.R[1], d.Cout, t->K, f2c(fac[1]),
-                                                        true, true, ghat, ub, s));
+      LAUNCH("tucker_data", s, fno::launch_mix_bwd_dx_g(t->g_out, t->zero_woff, ghat,
+                                                        f2c(fac[1]), ub, s));
       u = ub;
     }
     float2* gH = at<float2>(ws, t->g0_off);
@@ -898,8 +903,8 @@ struct TuckerMix final : WeightMix {
       const float2* data = xhat;
       if (t->in_on_data) {
         float2* x1 = at<float2>(ws, t->x1_off);
-        LAUNCH("tucker_mode", s, fno::launch_mode_product(d.B, d.R[0], d.Cin, t->K,
-                                                          f2c(fac[0]), true, false, xhat, x1, s));
+        LAUNCH("tucker_data", s, fno::launch_mix_fwd_g(t->g_in, t->zero_woff, xhat, f2c(fac[0]),
+                                                       x1, s));
         data = x1;
       }
       // gradient of the core-side tensor the mix reads
@@ -907,7 +912,7 @@ struct TuckerMix final : WeightMix {
       if (t->out_on_data && gf(1)) {
         float2* t2 = at<float2>(ws, t->t2_off);
         LAUNCH("tucker_mix_fwd", s, fno::launch_mix_fwd_g(t->gmix, t->ident_woff, data, H, t2, s));
-        LAUNCH("tucker_gram", s, fno::launch_gram(d.B, d.Cout, d.R[1], t->K, ghat, t2, true,
+        LAUNCH("tucker_gram_data", s, fno::launch_gram(d.B, d.Cout, d.R[1], t->K, ghat, t2, true,
                                                   g.mb, g.Nb, g.adj_scale, g.inv_gain[0], false,
                                                   part, gf(1), s));
       }
@@ -919,10 +924,10 @@ struct TuckerMix final : WeightMix {
       LAUNCH("tucker_mix_dx", s, fno::launch_mix_bwd_dx_g(t->gmix, t->ident_woff, u, H, v, s));
       if (t->in_on_data) {
         if (ghx)
-          LAUNCH("tucker_mode", s, fno::launch_mode_product(d.B, d.Cin, d.R[0], t->K,
-                                                            f2c(fac[0]), false, true, v, ghx, s));
+          LAUNCH("tucker_data", s, fno::launch_mix_bwd_dx_g(t->g_in, t->zero_woff, v,
+                                                            f2c(fac[0]), ghx, s));
         if (gf(0))
-          LAUNCH("tucker_gram", s, fno::launch_gram(d.B, d.Cin, d.R[0], t->K, xhat, v, false,
+          LAUNCH("tucker_gram_data", s, fno::launch_gram(d.B, d.Cin, d.R[0], t->K, xhat, v, false,
                                                     g.mb, g.Nb, 1.0f, g.inv_gain[1], true,
                                                     part, gf(0), s));
       }
@@ -936,12 +941,12 @@ struct TuckerMix final : WeightMix {
       const fno::TuckerStep& stp = t->steps[k];
       if (stp.kind != fno::TuckerStep::CORE) continue;
       if (gf(stp.factor))
-        LAUNCH("tucker_gram", s, fno::launch_gram(stp.pre, stp.an, stp.cn, stp.post, cur,
+        LAUNCH("tucker_gram_core", s, fno::launch_gram(stp.pre, stp.an, stp.cn, stp.post, cur,
                                                   chain_in[si], false, g.mb, g.Nb, 1.0f, 1.0f,
                                                   false, part, gf(stp.factor), s));
       float2* dst = si == 0 ? grad_core : other;
       if (dst)
-        LAUNCH("tucker_mode", s, fno::launch_mode_product(stp.pre, stp.cn, stp.an, stp.post,
+        LAUNCH("tucker_core_adj", s, fno::launch_mode_product(stp.pre, stp.cn, stp.an, stp.post,
                                                           f2c(fac[stp.factor]), true, true, cur,
                                                           dst, s));
       other = cur;
@@ -1136,6 +1141,8 @@ fno_status fno_tucker_create(const fno_plan* p, const int32_t* ranks, fno_tucker
       t->gmix.Cin = stp.cn;
       t->gmix.Cout = stp.an;
       t->gmix.Mprod = p->g.K;
+      t->gmix.w_si = (int)(stp.an * p->g.K);
+      t->gmix.w_so = (int)p->g.K;
     }
   }
   t->g0_off = take(gmax);
@@ -1147,9 +1154,25 @@ fno_status fno_tucker_create(const fno_plan* p, const int32_t* ranks, fno_tucker
   t->u_off = take(t->out_on_data ? dR * d.R[1] : 0);
   t->part_off = take(fno::kTuckerPartElems);
   t->total = off;
-  // identity mode offsets: the core-side tensor [c_in][c_out][K] holds mode t at t
-  std::vector<int32_t> ident((size_t)t->K);
+  // identity mode offsets (the core-side tensor [c_in][c_out][K] holds mode t at t), then
+  // zero offsets (a factor matrix, the same for every mode)
+  std::vector<int32_t> ident((size_t)(2 * t->K), 0);
   for (int64_t k = 0; k < t->K; ++k) ident[(size_t)k] = (int32_t)k;
+  auto factor_geom = [&](int cin, int cout, int w_si, int w_so) {
+    fno::Geom g = p->g;
+    g.Cin = cin;
+    g.Cout = cout;
+    g.w_si = w_si;
+    g.w_so = w_so;
+    g.half = 0;  // factor products in float32
+    g.bf16 = false;
+    g.mb = 1;    // no half-spectrum weight and no adjoint scale on these launches
+    g.adj_scale = 1.0f;
+    g.mix_gain[0] = g.mix_gain[1] = g.inv_gain[0] = g.inv_gain[1] = 1.0f;
+    return g;
+  };
+  t->g_in = factor_geom(d.Cin, d.R[0], d.R[0], 1);     // W[i][ri] = U_in[i][ri]
+  t->g_out = factor_geom(d.R[1], d.Cout, 1, d.R[1]);   // W[ro][o] = U_out[o][ro]
   t->ident_woff = nullptr;
   hipError_t e = hipSetDevice(p->device);
   if (e == hipSuccess) e = hipMalloc(&t->ident_woff, sizeof(int32_t) * ident.size());
@@ -1161,6 +1184,7 @@ fno_status fno_tucker_create(const fno_plan* p, const int32_t* ranks, fno_tucker
     delete t;
     return hip_fail(e, "fno_tucker_create");
   }
+  t->zero_woff = t->ident_woff + t->K;
   *out = t;
   return FNO_OK;
 }

@@ -214,11 +214,60 @@ k_mode_product(int64_t pre, int an, int cn, int64_t post, const float2* __restri
     if (a0 + j < an) op[(int64_t)(a0 + j) * post] = make_float2(ar[j], ai[j]);
 }
 
+// Short rows (post < kMpShortPost, e.g. the last mode of the core): one thread per output
+// element in output order, so stores are contiguous; threads of one (p, q) read the same
+// T values.  op(A) (at most 64 x 64) sits in LDS.
+constexpr int kMpShortPost = 16;
+
+__global__ void __launch_bounds__(256)
+k_mode_product_short(int64_t pre, int an, int cn, int post, const float2* __restrict__ A,
+                     int trans, int conj, const float2* __restrict__ T,
+                     float2* __restrict__ out) {
+  __shared__ float2 s_a[64 * 64];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < an * cn; e += 256) {
+    const int a = e / cn, c = e % cn;
+    float2 v = trans ? A[(int64_t)c * an + a] : A[e];
+    if (conj) v.y = -v.y;
+    s_a[e] = v;
+  }
+  __syncthreads();
+  const int64_t e = (int64_t)blockIdx.x * 256 + tid;
+  if (e >= pre * an * post) return;
+  const int q = (int)(e % post);
+  const int64_t pa = e / post;
+  const int a = (int)(pa % an);
+  const int64_t p = pa / an;
+  const float2* tp = T + p * cn * post + q;
+  float ar = 0.f, ai = 0.f;
+  for (int c0 = 0; c0 < cn; c0 += kMpC) {
+    float2 tv[kMpC];
+#pragma unroll
+    for (int u = 0; u < kMpC; ++u) tv[u] = tp[(int64_t)min(c0 + u, cn - 1) * post];
+#pragma unroll
+    for (int u = 0; u < kMpC; ++u) {
+      const bool ok = c0 + u < cn;
+      const float tr = ok ? tv[u].x : 0.f, ti = ok ? tv[u].y : 0.f;
+      const float2 m = s_a[a * cn + min(c0 + u, cn - 1)];
+      ar += m.x * tr - m.y * ti;
+      ai += m.x * ti + m.y * tr;
+    }
+  }
+  out[e] = make_float2(ar, ai);
+}
+
 hipError_t launch_mode_product(int64_t pre, int an, int cn, int64_t post, const float2* A,
                                bool trans, bool conj, const float2* T, float2* out,
                                hipStream_t s) {
   if (an < 1 || cn < 1 || an > 64 || cn > 64 || pre < 1 || post < 1)
     return hipErrorInvalidValue;
+  if (post < kMpShortPost) {
+    const int64_t nblk = (pre * an * post + 255) / 256;
+    if (nblk > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_mode_product_short, dim3((unsigned)nblk), dim3(256), 0, s, pre, an, cn,
+                       (int)post, A, trans ? 1 : 0, conj ? 1 : 0, T, out);
+    return hipGetLastError();
+  }
   const int64_t blocks = (pre * post + 255) / 256;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks, (unsigned)((an + kMpRows - 1) / kMpRows));
@@ -232,70 +281,72 @@ hipError_t launch_mode_product(int64_t pre, int an, int cn, int64_t post, const 
 // X [pre][an][post], Y [pre][cn][post]; w(q) = gamma(q mod mb) * adj (the inverse transform's
 // half-spectrum weight, when gamma_w) or 1.  Stage 1: work-group g sums the (p, q) range
 // [g chunk, (g + 1) chunk) in tiles of kGramT staged in LDS (all of a tile's loads go out
-// before any is stored); thread t owns the 4 x 4 outputs a = 4 (t / 16) + i, c = 4 (t % 16) + j,
-// so each LDS read serves four products.  Stage 2 adds the partials of each output in a fixed
-// order (deterministic) and applies scale / conj.
+// before any is stored); thread t owns a TA x TC block of outputs, sized so that the threads
+// cover an x cn with as few idle as possible, and each LDS read serves TC (or TA) products.
+// Stage 2 adds the partials of each output in a fixed order (deterministic) and applies
+// scale / conj.
 constexpr int kGramT = 32;
 constexpr int kGramLd = (2 * 64 * kGramT) / 256;  // tile values loaded per thread (at most)
 
+template <int TA, int TC>
 __global__ void __launch_bounds__(256)
-k_gram_part(int64_t pre, int an, int cn, int64_t post, const float2* __restrict__ X,
-            const float2* __restrict__ Y, int gamma_w, int mb, int Nb, float adj, int64_t chunk,
+k_gram_part(int pre, int an, int cn, int post, const float2* __restrict__ X,
+            const float2* __restrict__ Y, int gamma_w, int mb, int Nb, float adj, int chunk,
             float2* __restrict__ part) {
   __shared__ float2 s_x[64][kGramT + 1];
   __shared__ float2 s_y[64][kGramT + 1];
   const int tid = threadIdx.x;
-  const int64_t D = pre * post;
-  const int64_t lo = (int64_t)blockIdx.x * chunk;
-  const int64_t hi = min(D, lo + chunk);
-  const int ab = tid >> 4, cb = tid & 15;
+  const int D = pre * post;
+  const int lo = blockIdx.x * chunk;
+  const int hi = min(D, lo + chunk);
+  const int ncb = (cn + TC - 1) / TC;
+  const int ab = tid / ncb, cb = tid % ncb;
+  const bool active = ab * TA < an;
   const int rows = an + cn;
-  float ar[4][4], ai[4][4];
+  // tile element t of this thread is fixed (256 u is a multiple of kGramT); its rows are
+  // r0 + 8 u
+  const int t = tid & (kGramT - 1);
+  const int r0 = tid / kGramT;
+  float ar[TA][TC], ai[TA][TC];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TA; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ar[i][j] = ai[i][j] = 0.f;
-  for (int64_t base = lo; base < hi; base += kGramT) {
+    for (int j = 0; j < TC; ++j) ar[i][j] = ai[i][j] = 0.f;
+  for (int base = lo; base < hi; base += kGramT) {
+    const int idx = min(base + t, hi - 1);
+    const int pp = idx / post, qq = idx - pp * post;
+    float wq = base + t < hi ? 1.f : 0.f;
+    if (gamma_w) {
+      const int kb = qq % mb;
+      wq *= ((kb == 0 || 2 * kb == Nb) ? 1.f : 2.f) * adj;
+    }
+    const float2* xs = X + (int64_t)pp * an * post + qq;
+    const float2* ys = Y + (int64_t)pp * cn * post + qq;
     float2 v[kGramLd];
 #pragma unroll
     for (int u = 0; u < kGramLd; ++u) {
-      const int e = tid + 256 * u;
-      const int row = min(e / kGramT, rows - 1), t = e % kGramT;
-      const int64_t idx = min(base + t, hi - 1);
-      const int64_t pp = idx / post, qq = idx % post;
-      const float2* src = row < an ? X + (pp * an + row) * post + qq
-                                   : Y + (pp * cn + (row - an)) * post + qq;
-      v[u] = *src;
+      const int row = min(r0 + (256 / kGramT) * u, rows - 1);
+      v[u] = row < an ? xs[(int64_t)row * post] : ys[(int64_t)(row - an) * post];
     }
     __syncthreads();  // the previous tile's products are done
 #pragma unroll
     for (int u = 0; u < kGramLd; ++u) {
-      const int e = tid + 256 * u;
-      const int row = e / kGramT, t = e % kGramT;
-      if (row < rows) {
-        const int64_t idx = base + t;
-        float wq = idx < hi ? 1.f : 0.f;
-        if (gamma_w && row < an) {
-          const int kb = (int)((idx % post) % mb);
-          wq *= ((kb == 0 || 2 * kb == Nb) ? 1.f : 2.f) * adj;
-        }
-        const float2 val = make_float2(v[u].x * wq, v[u].y * wq);
-        if (row < an) s_x[row][t] = val;
-        else s_y[row - an][t] = val;
-      }
+      const int row = r0 + (256 / kGramT) * u;
+      if (row < an) s_x[row][t] = make_float2(v[u].x * wq, v[u].y * wq);
+      else if (row < rows) s_y[row - an][t] = v[u];
     }
     __syncthreads();
-    if (4 * ab < an && 4 * cb < cn) {
-      for (int t = 0; t < kGramT; ++t) {
-        float2 xv[4], yv[4];
+    if (active) {
+      for (int k = 0; k < kGramT; ++k) {
+        float2 xv[TA], yv[TC];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xv[i] = s_x[min(4 * ab + i, 63)][t];
+        for (int i = 0; i < TA; ++i) xv[i] = s_x[min(TA * ab + i, 63)][k];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) yv[j] = s_y[min(4 * cb + j, 63)][t];
+        for (int j = 0; j < TC; ++j) yv[j] = s_y[min(TC * cb + j, 63)][k];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < TA; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
+          for (int j = 0; j < TC; ++j) {
             ar[i][j] += xv[i].x * yv[j].x + xv[i].y * yv[j].y;  // x conj(y)
             ai[i][j] += xv[i].y * yv[j].x - xv[i].x * yv[j].y;
           }
@@ -304,44 +355,48 @@ k_gram_part(int64_t pre, int an, int cn, int64_t post, const float2* __restrict_
   }
   const int nout = an * cn;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TA; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int a = 4 * ab + i, c = 4 * cb + j;
-      if (a < an && c < cn)
+    for (int j = 0; j < TC; ++j) {
+      const int a = TA * ab + i, c = TC * cb + j;
+      if (active && a < an && c < cn)
         part[(int64_t)blockIdx.x * nout + a * cn + c] = make_float2(ar[i][j], ai[i][j]);
     }
 }
 
-// 64 outputs per work-group; its 4 waves add every 4th partial (8 loads in flight per
-// thread), then the 4 sums are combined in wave order.
+// 16 outputs per work-group; 16 thread groups each add every 16th partial (8 loads in flight
+// per thread), then the 16 sums are combined in group order.
+constexpr int kFinOut = 16;
+constexpr int kFinGroups = 256 / kFinOut;
+
 __global__ void __launch_bounds__(256)
 k_gram_finish(int nparts, int nout, const float2* __restrict__ part, float scale, int conj_out,
               float2* __restrict__ out) {
-  __shared__ float2 s_sum[4][64];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int e = blockIdx.x * 64 + lane;
+  __shared__ float2 s_sum[kFinGroups][kFinOut];
+  const int o = threadIdx.x % kFinOut, w = threadIdx.x / kFinOut;
+  const int e = blockIdx.x * kFinOut + o;
   const int ec = min(e, nout - 1);
   float r = 0.f, i = 0.f;
-  for (int g0 = w; g0 < nparts; g0 += 4 * 8) {
+  for (int g0 = w; g0 < nparts; g0 += kFinGroups * 8) {
     float2 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)min(g0 + 4 * u, nparts - 1) * nout + ec];
+    for (int u = 0; u < 8; ++u)
+      v[u] = part[(int64_t)min(g0 + kFinGroups * u, nparts - 1) * nout + ec];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const bool ok = g0 + 4 * u < nparts;
+      const bool ok = g0 + kFinGroups * u < nparts;
       r += ok ? v[u].x : 0.f;
       i += ok ? v[u].y : 0.f;
     }
   }
-  s_sum[w][lane] = make_float2(r, i);
+  s_sum[w][o] = make_float2(r, i);
   __syncthreads();
   if (w == 0 && e < nout) {
     float sr = 0.f, si = 0.f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      sr += s_sum[k][lane].x;
-      si += s_sum[k][lane].y;
+    for (int k = 0; k < kFinGroups; ++k) {
+      sr += s_sum[k][o].x;
+      si += s_sum[k][o].y;
     }
     out[e] = make_float2(scale * sr, (conj_out ? -scale : scale) * si);
   }
@@ -349,7 +404,7 @@ k_gram_finish(int nparts, int nout, const float2* __restrict__ part, float scale
 
 int gram_parts(int64_t pre, int64_t post, int an, int cn) {
   const int64_t D = pre * post;
-  int64_t parts = (D + 4 * kGramT - 1) / (4 * kGramT);  // about four tiles per work-group
+  int64_t parts = (D + 2 * kGramT - 1) / (2 * kGramT);  // about two tiles per work-group
   const int64_t cap = kTuckerPartElems / ((int64_t)an * cn);
   if (parts > cap) parts = cap;
   if (parts > 2048) parts = 2048;
@@ -360,20 +415,38 @@ int gram_parts(int64_t pre, int64_t post, int an, int cn) {
 hipError_t launch_gram(int64_t pre, int an, int cn, int64_t post, const float2* X,
                        const float2* Y, bool gamma_w, int mb, int Nb, float adj, float scale,
                        bool conj_out, float2* part, float2* out, hipStream_t s) {
-  if (an < 1 || cn < 1 || an > 64 || cn > 64 || pre < 1 || post < 1)
+  if (an < 1 || cn < 1 || an > 64 || cn > 64 || pre < 1 || post < 1 ||
+      pre * post > 0x7fffffff || pre * (an > cn ? an : cn) * post > 0x7fffffff)
     return hipErrorInvalidValue;
   const int parts = gram_parts(pre, post, an, cn);
   const int64_t D = pre * post;
   int64_t chunk = (D + parts - 1) / parts;
   chunk = (chunk + kGramT - 1) / kGramT * kGramT;
   const int nparts = (int)((D + chunk - 1) / chunk);
-  hipLaunchKernelGGL(k_gram_part, dim3((unsigned)nparts), dim3(256), 0, s, pre, an, cn, post,
-                     X, Y, gamma_w ? 1 : 0, mb, Nb, adj, chunk, part);
+  // the smallest per-thread output block whose thread grid fits 256 threads
+  auto fits = [&](int ta, int tc) { return ((an + ta - 1) / ta) * ((cn + tc - 1) / tc) <= 256; };
+  const dim3 grid((unsigned)nparts), blk(256);
+  const int ip = (int)pre, iq = (int)post, ic = (int)chunk, gw = gamma_w ? 1 : 0;
+  if (fits(1, 1))
+    hipLaunchKernelGGL((k_gram_part<1, 1>), grid, blk, 0, s, ip, an, cn, iq, X, Y, gw, mb, Nb,
+                       adj, ic, part);
+  else if (fits(2, 1))
+    hipLaunchKernelGGL((k_gram_part<2, 1>), grid, blk, 0, s, ip, an, cn, iq, X, Y, gw, mb, Nb,
+                       adj, ic, part);
+  else if (fits(2, 2))
+    hipLaunchKernelGGL((k_gram_part<2, 2>), grid, blk, 0, s, ip, an, cn, iq, X, Y, gw, mb, Nb,
+                       adj, ic, part);
+  else if (fits(4, 2))
+    hipLaunchKernelGGL((k_gram_part<4, 2>), grid, blk, 0, s, ip, an, cn, iq, X, Y, gw, mb, Nb,
+                       adj, ic, part);
+  else
+    hipLaunchKernelGGL((k_gram_part<4, 4>), grid, blk, 0, s, ip, an, cn, iq, X, Y, gw, mb, Nb,
+                       adj, ic, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nout = an * cn;
-  hipLaunchKernelGGL(k_gram_finish, dim3((unsigned)((nout + 63) / 64)), dim3(256), 0, s, nparts,
-                     nout, part, scale, conj_out ? 1 : 0, out);
+  hipLaunchKernelGGL(k_gram_finish, dim3((unsigned)((nout + kFinOut - 1) / kFinOut)), dim3(256),
+                     0, s, nparts, nout, part, scale, conj_out ? 1 : 0, out);
   return hipGetLastError();
 }
 
