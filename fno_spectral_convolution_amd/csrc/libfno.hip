@@ -212,10 +212,12 @@ fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out) {
 
   p->kpad = (2 * g.mb + 31) / 32 * 32;
   p->jpad = (2 * g.mb + 15) / 16 * 16;
-  // plane-transform chunking along axis a: about 1024 work-groups, chunks of 64-row multiples
+  // plane-transform chunking along axis a: at least 512 work-groups (two per CU), chunks of
+  // 64-row multiples; fewer, longer chunks amortise each work-group's table load and final
+  // combine, and a single chunk needs no partial-sum pass
   {
     const int64_t planes = (int64_t)g.B * cmax * g.O;
-    int64_t want = (1024 + planes - 1) / planes;
+    int64_t want = (512 + planes - 1) / planes;
     if (want < 1) want = 1;
     int rows = (int)((g.Na + want - 1) / want);
     rows = (rows + 63) / 64 * 64;

@@ -35,6 +35,10 @@ CASES = [
     ("2d_mc_c64", 2, 64, 64, (64, 512), (8, 32)),
     ("3d_mc_c20", 1, 20, 20, (10, 12, 64), (3, 4, 8)),
     ("4d_mc_c16", 1, 16, 16, (4, 6, 8, 64), (2, 2, 3, 6)),
+    # few planes and long outer axes: the plane transform splits each plane into row chunks
+    # and adds their partial spectra
+    ("2d_chunked_nb64", 1, 4, 4, (256, 64), (8, 8)),
+    ("2d_chunked_nb512", 1, 2, 2, (256, 512), (16, 32)),
     # shapes taken by the short-row plane kernel (contiguous axis <= 32, a multiple of 4)
     ("4d_short_t20", 1, 3, 4, (4, 6, 16, 20), (2, 2, 4, 8)),
     ("3d_short_t20_jp32", 2, 5, 3, (6, 32, 20), (3, 8, 10)),
