@@ -38,7 +38,7 @@ EXPORTS = [
     "fno_pointwise_fwd", "fno_mse_workspace_bytes", "fno_mse_grad", "fno_mse_grad_scaled",
     "fno_tucker_order", "fno_tucker_create", "fno_tucker_destroy", "fno_tucker_query",
     "fno_tucker_block_fwd", "fno_tucker_block_bwd",
-    "fno_timing_enable",
+    "fno_timing_enable", "fno_timing_select",
     "fno_timing_reset", "fno_timing_count", "fno_timing_get", "fno_status_string",
     "fno_last_error_message",
 ]
@@ -91,6 +91,7 @@ def _load():
         "fno_tucker_block_bwd": (c_int, [P, P, P, POINTER(c_void_p), P, P, P, P, P, P,
                                          POINTER(c_void_p), P, P, P, c_size_t, P]),
         "fno_timing_enable": (c_int, [c_int]),
+        "fno_timing_select": (c_int, [c_char_p]),
         "fno_timing_reset": (c_int, []),
         "fno_timing_count": (c_int, [POINTER(c_int)]),
         "fno_timing_get": (c_int, [c_int, POINTER(c_char_p), POINTER(c_int64),
@@ -198,6 +199,11 @@ def fno_mse_grad_scaled(n, y, t, grad, loss, grad_scale, ws, ws_bytes, stream):
 
 def fno_timing_enable(enable: bool) -> None:
     _check(_lib.fno_timing_enable(1 if enable else 0), "fno_timing_enable")
+
+
+def fno_timing_select(name=None) -> None:
+    """Time only the launches of kernel `name` (None: every launch)."""
+    _check(_lib.fno_timing_select(name.encode() if name else None), "fno_timing_select")
 
 
 def fno_timing_reset() -> None:

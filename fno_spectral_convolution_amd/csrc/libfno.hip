@@ -551,6 +551,7 @@ namespace {
 struct TimingState {
   std::mutex mu;
   bool on = false;
+  std::string only;  // when not empty: time only the launches of this name
   struct Pending {
     const char* name;
     hipEvent_t a, b;
@@ -585,7 +586,7 @@ hipError_t timed_launch(const char* name, hipStream_t s, F&& launch) {
   hipEvent_t a = nullptr, b = nullptr;
   {
     std::lock_guard<std::mutex> lk(T.mu);
-    if (!T.on) return launch();
+    if (!T.on || (!T.only.empty() && T.only != name)) return launch();
     a = timing_event(T);
     b = timing_event(T);
   }
@@ -1316,6 +1317,13 @@ fno_status fno_timing_enable(int enable) {
   TimingState& T = timing_state();
   std::lock_guard<std::mutex> lk(T.mu);
   T.on = enable != 0;
+  return FNO_OK;
+}
+
+fno_status fno_timing_select(const char* name) {
+  TimingState& T = timing_state();
+  std::lock_guard<std::mutex> lk(T.mu);
+  T.only = name ? name : "";
   return FNO_OK;
 }
 

@@ -239,6 +239,9 @@ fno_status fno_mse_grad_scaled(int64_t n, const float* y, const float* t, float*
  * names; fno_timing_get returns name, launch count and summed duration (ms) of entry
  * `index`.  The name pointer stays valid until the next fno_timing_reset.  Process-wide. */
 fno_status fno_timing_enable(int enable);
+/* Restrict the timer to the launches of one kernel name (NULL or "" = every launch), so that a
+ * measurement can time one kernel while the others run without events.  Process-wide. */
+fno_status fno_timing_select(const char* name);
 fno_status fno_timing_reset(void);
 fno_status fno_timing_count(int* count);
 fno_status fno_timing_get(int index, const char** name, int64_t* launches, double* total_ms);
