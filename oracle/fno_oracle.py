@@ -57,6 +57,12 @@ in Tucker form (core tensor times one factor matrix per mode):
   (W is complex-linear in each of G and the U_n, so each gradient is grad_W pulled back through
   the conjugated Jacobian.)  The block is F1-F4 with W = fold(W_full).
 
+Input activation (a layout of the same network, not another network): a block may take a
+pre-activation x and apply GELU to it first, so that the previous block need not store both
+its z and y = GELU(z).  Then every use of x above uses GELU(x) and
+
+  B7  grad_x = GELU'(x) * (grad_x of the block on GELU(x))
+
 Layouts: fields are [B, C, N_0, .., N_{d-1}] float; ``W`` is complex
 [2^(d-1), Cin, Cout, m_0, .., m_{d-1}]; ``Wb`` is [Cout, Cin]; ``bias`` is [Cout].
 Everything is evaluated in float64 / complex128.
@@ -269,9 +275,11 @@ def _pointwise(wmat: np.ndarray, f: np.ndarray) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------- spectral conv
-def spectral_conv_fwd(x, w, modes, tanh: bool = False):
+def spectral_conv_fwd(x, w, modes, tanh: bool = False, input_gelu: bool = False):
     """F1-F3 only (no bypass, bias or activation).  Returns dict(y_spec, xhat, yhat)."""
     x = np.asarray(x, dtype=np.float64)
+    if input_gelu:
+        x = gelu(x)
     xp = np.tanh(x) if tanh else x
     xhat = spectrum(xp, modes)
     yhat = channel_mix(xhat, w, modes)
@@ -279,12 +287,17 @@ def spectral_conv_fwd(x, w, modes, tanh: bool = False):
     return {"y_spec": y_spec, "xhat": xhat, "yhat": yhat}
 
 
-def spectral_conv_bwd(x, w, modes, g_yspec, tanh: bool = False):
-    """Adjoint of ``spectral_conv_fwd`` (B2-B4, times tanh' on the mixed path).
+def spectral_conv_bwd(x, w, modes, g_yspec, tanh: bool = False, input_gelu: bool = False):
+    """Adjoint of ``spectral_conv_fwd`` (B2-B4, times tanh' on the mixed path; B7 with an
+    input activation).
 
     Returns dict(grad_x, grad_w) with grad_w in W's corner layout.
     """
     x = np.asarray(x, dtype=np.float64)
+    if input_gelu:
+        r = spectral_conv_bwd(gelu(x), w, modes, g_yspec, tanh=tanh)
+        r["grad_x"] = gelu_prime(x) * r["grad_x"]
+        return r
     g = np.asarray(g_yspec, dtype=np.float64)
     xp = np.tanh(x) if tanh else x
     xhat = spectrum(xp, modes)
@@ -299,9 +312,13 @@ def spectral_conv_bwd(x, w, modes, g_yspec, tanh: bool = False):
 
 
 # ----------------------------------------------------------------------------- block
-def block_fwd(x, w, wb, bias, modes, tanh: bool = False, act: bool = True):
-    """F1-F4: one FNO block.  Returns dict(y, z, y_spec, xhat, yhat)."""
+def block_fwd(x, w, wb, bias, modes, tanh: bool = False, act: bool = True,
+              input_gelu: bool = False):
+    """F1-F4: one FNO block (input GELU(x) when input_gelu).  Returns dict(y, z, y_spec,
+    xhat, yhat)."""
     x = np.asarray(x, dtype=np.float64)
+    if input_gelu:
+        x = gelu(x)
     out = spectral_conv_fwd(x, w, modes, tanh=tanh)
     z = out["y_spec"] + _pointwise(wb, x)
     if bias is not None:
@@ -311,9 +328,16 @@ def block_fwd(x, w, wb, bias, modes, tanh: bool = False, act: bool = True):
     return out
 
 
-def block_bwd(x, w, wb, bias, modes, g_y, tanh: bool = False, act: bool = True):
-    """B1-B6 for one block.  Returns dict(grad_x, grad_w, grad_wb, grad_bias, g_z, gx_spec)."""
+def block_bwd(x, w, wb, bias, modes, g_y, tanh: bool = False, act: bool = True,
+              input_gelu: bool = False):
+    """B1-B6 for one block (B7 with an input activation).  Returns dict(grad_x, grad_w,
+    grad_wb, grad_bias, g_z, gx_spec)."""
     x = np.asarray(x, dtype=np.float64)
+    if input_gelu:
+        r = block_bwd(gelu(x), w, wb, bias, modes, g_y, tanh=tanh, act=act)
+        r["grad_x"] = gelu_prime(x) * r["grad_x"]
+        r["gx_spec"] = gelu_prime(x) * r["gx_spec"]
+        return r
     g_y = np.asarray(g_y, dtype=np.float64)
     fwd = block_fwd(x, w, wb, bias, modes, tanh=tanh, act=act)
     g_z = g_y * gelu_prime(fwd["z"]) if act else g_y

@@ -405,6 +405,46 @@ def check_inverse_at_points(O):
         _close(got, want, 1e-12, f"inverse at points {grid}")
 
 
+def check_input_activation(O):
+    """A block on a pre-activation x with input_gelu is the same block on GELU(x) (forward),
+    and its grad_x obeys the chain rule (fp64 central differences through the whole block,
+    tanh path, with and without the output GELU)."""
+    g = _rng(300)
+    grid, modes = (6, 8), (2, 3)
+    cin, cout = 2, 3
+    x = g.standard_normal((2, cin) + grid)
+    w = _rand_w(g, 2, cin, cout, modes) * 0.5
+    wb = g.standard_normal((cout, cin))
+    bias = g.standard_normal(cout)
+    gy = g.standard_normal((2, cout) + grid)
+    xg = O.gelu(x)
+    for act in (True, False):
+        a = O.block_fwd(x, w, wb, bias, modes, tanh=True, act=act, input_gelu=True)["y"]
+        b = O.block_fwd(xg, w, wb, bias, modes, tanh=True, act=act)["y"]
+        assert np.array_equal(a, b)
+        r = O.block_bwd(x, w, wb, bias, modes, gy, tanh=True, act=act, input_gelu=True)
+        h = 1e-6
+        for _ in range(6):
+            idx = tuple(int(g.integers(0, s_)) for s_ in x.shape)
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            L = lambda xx: float(np.sum(O.block_fwd(xx, w, wb, bias, modes, tanh=True,  # noqa: E731
+                                                    act=act, input_gelu=True)["y"] * gy))
+            num = (L(xp) - L(xm)) / (2 * h)
+            assert abs(num - r["grad_x"][idx]) < 1e-6 * max(1, abs(num)), (act, idx, num)
+        sp = O.spectral_conv_bwd(x, w, modes, gy, tanh=True, input_gelu=True)
+        for _ in range(3):
+            idx = tuple(int(g.integers(0, s_)) for s_ in x.shape)
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            Ls = lambda xx: float(np.sum(O.spectral_conv_fwd(xx, w, modes, tanh=True,  # noqa: E731
+                                                             input_gelu=True)["y_spec"] * gy))
+            num = (Ls(xp) - Ls(xm)) / (2 * h)
+            assert abs(num - sp["grad_x"][idx]) < 1e-6 * max(1, abs(num)), ("spec", idx, num)
+
+
 # ------------------------------------------------------------------ T1-T3: Tucker weights
 def _crand(g, shape):
     return g.standard_normal(shape) + 1j * g.standard_normal(shape)
@@ -516,6 +556,7 @@ ALL_CHECKS = [
     check_single_mode_dc_plane, check_cutoff, check_linearity_equivariance_selfadjoint,
     check_gelu, check_zero_weight_block, check_adjoint_identities,
     check_block_finite_differences, check_mse_and_stack,
+    check_input_activation,
     check_tucker_identity_factors, check_tucker_hosvd, check_tucker_rank_one,
     check_tucker_block_finite_differences,
 ]

@@ -116,6 +116,13 @@ def _tucker_bwd_core_one_mode_short(x, core, factors, wb, bias, modes, g_y, tanh
     return r
 
 
+def _block_bwd_input_gelu_no_prime(x, w, wb, bias, modes, g_y, tanh=False, act=True,
+                                   input_gelu=False):
+    if not input_gelu:
+        return _orig["block_bwd"](x, w, wb, bias, modes, g_y, tanh=tanh, act=act)
+    return _orig["block_bwd"](O.gelu(x), w, wb, bias, modes, g_y, tanh=tanh, act=act)
+
+
 MUTATIONS = [
     ("dft_matrix", _dft_sign_flipped, P.check_spectrum_bruteforce),
     ("retained_indices", _retained_off_by_one, P.check_spectrum_numpy_fft),
@@ -129,6 +136,7 @@ MUTATIONS = [
     ("spectral_conv_bwd", _bwd_no_conj, P.check_adjoint_identities),
     ("block_bwd", _block_bwd_no_tanh_prime, P.check_block_finite_differences),
     ("block_fwd", _block_no_bias, P.check_zero_weight_block),
+    ("block_bwd", _block_bwd_input_gelu_no_prime, P.check_input_activation),
     ("mode_product", _mode_product_transposed, P.check_tucker_hosvd),
     ("mode_product", _mode_product_conj, P.check_tucker_hosvd),
     ("tucker_block_bwd", _tucker_bwd_factor_unconj, P.check_tucker_block_finite_differences),
