@@ -98,15 +98,21 @@ def kernel_model(wl, plan):
     model = {
         "plane_fwd": (4 * U + plane_spec, dft_last + dft_a),
         "plane_fwd_tanh": (4 * U + plane_spec, dft_last + dft_a),
+        "plane_fwd_gelu": (4 * U + plane_spec, dft_last + dft_a),
+        "plane_fwd_tanh_gelu": (4 * U + plane_spec, dft_last + dft_a),
         "plane_fwd_gelugrad": (8 * U + plane_spec, dft_last + dft_a),
         "mix_fwd": (wbytes + 2 * spec, mixf),
         "mix_bwd_dx": (wbytes + 2 * spec, mixf),
         "mix_bwd_dw": (wbytes + 2 * spec, mixf),
-        "epilogue_fwd": (4 * U + 4 * U + (4 * U if wl.train else 0) + T, dft_last + bypass),
+        # x in, y out (+ z saved for the backward)
+        "epilogue_fwd": (8 * U + T, dft_last + bypass),
+        "epilogue_fwd_zsave": (12 * U + T, dft_last + bypass),
         # short rows: the epilogue also inverts axis a, from the [2ma][mb] spectrum per plane
-        "epilogue_rows_fwd": (4 * U + 4 * U + (4 * U if wl.train else 0) + plane_spec,
-                              dft_last + dft_a + bypass),
-        "epilogue_bwd": (16 * U + T, dft_last + 2 * bypass),
+        "epilogue_rows_fwd": (8 * U + plane_spec, dft_last + dft_a + bypass),
+        "epilogue_rows_fwd_zsave": (12 * U + plane_spec, dft_last + dft_a + bypass),
+        # g and x in, grad_x out (+ z in for GELU' when the block applies the output GELU)
+        "epilogue_bwd": (12 * U + T, dft_last + 2 * bypass),
+        "epilogue_bwd_gelu": (16 * U + T, dft_last + 2 * bypass),
         "mse": (12 * U, 3 * U),
     }
     return model

@@ -31,6 +31,7 @@ FNO_DTYPE_F16 = 2
 FNO_FLAG_TANH_PREACT = 1
 FNO_FLAG_GELU = 2
 FNO_FLAG_BIAS = 4
+FNO_FLAG_INPUT_GELU = 8
 
 EXPORTS = [
     "fno_plan_validate", "fno_plan_create", "fno_plan_destroy", "fno_plan_query",
@@ -249,15 +250,16 @@ class Plan:
     [Cout, Cin], bias float32 [Cout]."""
 
     def __init__(self, batch, c_in, c_out, grid, modes, mixed=False, tanh=None, gelu=True,
-                 bias=True, device=None):
+                 bias=True, device=None, input_gelu=False):
         """mixed: False (fp32 spectral path), True or "bf16" (bfloat16 operands), "f16" (IEEE
-        half operands); a mixed plan takes the tanh pre-activation unless tanh says otherwise."""
+        half operands); a mixed plan takes the tanh pre-activation unless tanh says otherwise.
+        input_gelu: x is a pre-activation and the block's input is GELU(x)."""
         import torch
         self.torch = torch
         self.device = torch.device(device) if device is not None else torch.device("cuda")
         tanh = bool(mixed) if tanh is None else tanh
         flags = (FNO_FLAG_TANH_PREACT if tanh else 0) | (FNO_FLAG_GELU if gelu else 0) | \
-            (FNO_FLAG_BIAS if bias else 0)
+            (FNO_FLAG_BIAS if bias else 0) | (FNO_FLAG_INPUT_GELU if input_gelu else 0)
         self.desc = make_desc(batch, c_in, c_out, tuple(grid), tuple(modes),
                               spectral_dtype(mixed), flags)
         self.batch, self.c_in, self.c_out = batch, c_in, c_out

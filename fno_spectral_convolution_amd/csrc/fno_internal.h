@@ -113,7 +113,13 @@ namespace fno {
 
 // ---- launchers (kernels_*.hip) -------------------------------------------------------------
 // Prologue of the plane transform: how a field value becomes a transform operand.
-enum PlaneIn { PLANE_X = 0, PLANE_TANH = 1, PLANE_GELU_GRAD = 2 };
+enum PlaneIn {
+  PLANE_X = 0,
+  PLANE_TANH = 1,        // tanh(x)
+  PLANE_GELU_GRAD = 2,   // g * GELU'(z)
+  PLANE_GELU = 3,        // GELU(x): a block whose input is a pre-activation
+  PLANE_TANH_GELU = 4    // tanh(GELU(x))
+};
 
 hipError_t launch_plane_fwd(const fno_plan* p, int plane_in, int chans, const float* in0,
                             const float* in1, float2* out, hipStream_t s);

@@ -379,6 +379,8 @@ bool epilogue_rows_ok(const fno_plan* p, int mode, const float* x, const float* 
   if (g.ma > kErMA || g.ma % 4 != 0 || g.mb > 8) return false;
   if (g.Cout > 4 * kErCPW || g.Cout * g.Nb > 64 * kErXPT) return false;
   if (mode != EPI_SPECTRAL && (g.Cin > 4 * kErKB || g.Cin * g.Nb > 64 * kErXPT)) return false;
+  // the bypass here reads x as the block's input; a pre-activation input takes the line kernels
+  if (mode != EPI_SPECTRAL && (p->desc.flags & FNO_FLAG_INPUT_GELU)) return false;
   if (g.B > 65535) return false;
   // 32-bit offsets within one batch entry's field
   const int64_t chs = g.O * (int64_t)g.Na * g.Nb;

@@ -218,7 +218,8 @@ __device__ __forceinline__ void load_rows(float4 (&v)[NPT], const float* base, i
 // M-tile t is point MT m + t of the step (MT = 4 G tiles), so a lane's A operands of its G
 // tiles are adjacent in the [channel][point] LDS tile.  The z tile goes through LDS and the
 // stores are row-contiguous: 16 G threads write one channel's 64 G points.
-// MODE: 0 spectral part only, 1 block (bypass, bias, optional GELU), 2 block + z save.
+// MODE: 0 spectral part only, 1 block (bypass, bias, optional GELU), 2 block + z save; plus 8
+// when x is a pre-activation (the bypass takes GELU(x), applied as the x tile is staged).
 template <int C, int H, int MODE, int G>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C == 64 ? 3 : 4)))
 k_epi_fwd_line(EpiArgs a) {
@@ -232,8 +233,9 @@ k_epi_fwd_line(EpiArgs a) {
   constexpr int FPC = 16 * G;       // float4 per channel row of a step
   constexpr int NF4 = FPC * C;      // float4 of an x / z tile
   constexpr int NPT = (NF4 + 255) / 256;
-  constexpr bool BLK = MODE >= 1;
-  constexpr bool ZS = MODE == 2;
+  constexpr bool BLK = (MODE & 3) >= 1;
+  constexpr bool ZS = (MODE & 3) == 2;
+  constexpr bool IG = (MODE & 8) != 0;
   static_assert(G == 1 || G == 2, "LDS runs of 1 or 2 floats");
   __shared__ __attribute__((aligned(16))) float s_x[BLK ? CP * XSG : 4];
   __shared__ __attribute__((aligned(16))) float s_o[CP * XSG];
@@ -304,7 +306,16 @@ k_epi_fwd_line(EpiArgs a) {
       const int fn = min(f + 1, nf - 1);
       if (BLK) {
 #pragma unroll
-        for (int u = 0; u < NPT; ++u) *reinterpret_cast<float4*>(s_x + xl[u]) = pre[u];
+        for (int u = 0; u < NPT; ++u) {
+          float4 xv = pre[u];
+          if constexpr (IG) {
+            xv.x = gelu_as(xv.x);
+            xv.y = gelu_as(xv.y);
+            xv.z = gelu_as(xv.z);
+            xv.w = gelu_as(xv.w);
+          }
+          *reinterpret_cast<float4*>(s_x + xl[u]) = xv;
+        }
 #pragma unroll
         for (int u = 0; u < NPT; ++u)
           pre[u] = *reinterpret_cast<const float4*>(a.x + goff[u] + PI * fn);
@@ -401,7 +412,9 @@ k_epi_fwd_line(EpiArgs a) {
 //                 the work-group in a fixed order into one partial row per work-group
 // Wave w's dWb tiles: NT = 4: o-tile w, all 4 i-tiles; NT = 2: o-tile w >> 1, i-tile w & 1;
 // NT = 1: the single tile over its quarter of the step's points.
-// MODE: 1 spectral part only (grad_x = s(x) * spectral), 3 block, 7 block with GELU' (z read).
+// MODE: 1 spectral part only (grad_x = s(x) * spectral), 3 block, 7 block with GELU' (z read);
+// plus 8 when x is a pre-activation: the x tile holds the block's input GELU(x) (for dWb and
+// the tanh factor), a second tile GELU'(x), which multiplies the grad tile as it is stored.
 template <int C, int H, bool TANH, int MODE, int G>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C == 64 ? 2 : 3)))
 k_epi_bwd_line(EpiArgs a) {
@@ -417,13 +430,15 @@ k_epi_bwd_line(EpiArgs a) {
   constexpr int NPT = (NF4 + 255) / 256;
   constexpr bool BLK = (MODE & 2) != 0;
   constexpr bool GL = (MODE & 4) != 0;
-  constexpr bool NX = BLK || TANH;  // x rows needed
+  constexpr bool IG = (MODE & 8) != 0;
+  constexpr bool NX = BLK || TANH || IG;  // x rows needed
   constexpr int DT = (NT == 4) ? 4 : 1;  // dWb tiles per wave
   static_assert(G == 1 || G == 2, "LDS runs of 1 or 2 floats");
   static_assert(256 * NPT <= FPC * CP, "tail float4 land in the padding rows");
   __shared__ __attribute__((aligned(16))) float s_gz[BLK ? CP * XSG : 4];
   __shared__ __attribute__((aligned(16))) float s_x[NX ? CP * XSG : 4];
   __shared__ __attribute__((aligned(16))) float s_o[CP * XSG];
+  __shared__ __attribute__((aligned(16))) float s_gp[IG ? CP * XSG : 4];
   __shared__ __attribute__((aligned(16))) unsigned char s_tl[CP * (kMaxKpad + 8) * (BF ? 2 : 4)];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, q = lane >> 4;
@@ -508,7 +523,17 @@ k_epi_bwd_line(EpiArgs a) {
           }
           *reinterpret_cast<float4*>(s_gz + xl[u]) = gz;
         }
-        if (NX) *reinterpret_cast<float4*>(s_x + xl[u]) = px[u];
+        if constexpr (IG) {
+          float4 xin, gp;
+          gelu_and_grad(px[u].x, xin.x, gp.x);
+          gelu_and_grad(px[u].y, xin.y, gp.y);
+          gelu_and_grad(px[u].z, xin.z, gp.z);
+          gelu_and_grad(px[u].w, xin.w, gp.w);
+          *reinterpret_cast<float4*>(s_x + xl[u]) = xin;
+          *reinterpret_cast<float4*>(s_gp + xl[u]) = gp;
+        } else if (NX) {
+          *reinterpret_cast<float4*>(s_x + xl[u]) = px[u];
+        }
       }
 #pragma unroll
       for (int u = 0; u < NPT; ++u) {
@@ -611,7 +636,14 @@ k_epi_bwd_line(EpiArgs a) {
       __syncthreads();  // grad tile complete; g_z / x tiles free
 #pragma unroll
       for (int u = 0; u < NPT; ++u) {
-        const float4 v = *reinterpret_cast<const float4*>(s_o + ol[u]);
+        float4 v = *reinterpret_cast<const float4*>(s_o + ol[u]);
+        if constexpr (IG) {
+          const float4 gp = *reinterpret_cast<const float4*>(s_gp + ol[u]);
+          v.x *= gp.x;
+          v.y *= gp.y;
+          v.z *= gp.z;
+          v.w *= gp.w;
+        }
         *reinterpret_cast<float4*>(a.y + goff[u] + PI * f) = v;
       }
     }
@@ -659,11 +691,13 @@ template <int C, int G>
 static hipError_t launch_fwd_c(const EpiArgs& a, int half, int mode, int wgs, hipStream_t s) {
 #define FNO_EPI_FWD(HV, MV) \
   hipLaunchKernelGGL((k_epi_fwd_line<C, HV, MV, G>), dim3(wgs), dim3(256), 0, s, a)
-#define FNO_EPI_FWD_M(HV)                 \
-  do {                                    \
-    if (mode == 0) FNO_EPI_FWD(HV, 0);      \
-    else if (mode == 1) FNO_EPI_FWD(HV, 1); \
-    else FNO_EPI_FWD(HV, 2);                \
+#define FNO_EPI_FWD_M(HV)                   \
+  do {                                      \
+    if (mode == 0) FNO_EPI_FWD(HV, 0);        \
+    else if (mode == 1) FNO_EPI_FWD(HV, 1);   \
+    else if (mode == 2) FNO_EPI_FWD(HV, 2);   \
+    else if (mode == 9) FNO_EPI_FWD(HV, 9);   \
+    else FNO_EPI_FWD(HV, 10);                 \
   } while (0)
   if (half == 2) FNO_EPI_FWD_M(2);
   else if (half == 1) FNO_EPI_FWD_M(1);
@@ -678,14 +712,14 @@ static hipError_t launch_bwd_c(const EpiArgs& a, int half, bool tanh_pre, int mo
                                hipStream_t s) {
 #define FNO_EPI_BWD(BFV, TV, MV) \
   hipLaunchKernelGGL((k_epi_bwd_line<C, BFV, TV, MV, G>), dim3(wgs), dim3(256), 0, s, a)
-#define FNO_EPI_BWD_M(BFV, TV)    \
-  do {                            \
-    if (mode == 1)                \
-      FNO_EPI_BWD(BFV, TV, 1);    \
-    else if (mode == 3)           \
-      FNO_EPI_BWD(BFV, TV, 3);    \
-    else                          \
-      FNO_EPI_BWD(BFV, TV, 7);    \
+#define FNO_EPI_BWD_M(BFV, TV)                  \
+  do {                                          \
+    if (mode == 1) FNO_EPI_BWD(BFV, TV, 1);       \
+    else if (mode == 3) FNO_EPI_BWD(BFV, TV, 3);  \
+    else if (mode == 7) FNO_EPI_BWD(BFV, TV, 7);  \
+    else if (mode == 9) FNO_EPI_BWD(BFV, TV, 9);  \
+    else if (mode == 11) FNO_EPI_BWD(BFV, TV, 11); \
+    else FNO_EPI_BWD(BFV, TV, 15);                \
   } while (0)
   if (half == 2) {
     if (tanh_pre) FNO_EPI_BWD_M(2, true);
@@ -749,7 +783,8 @@ hipError_t launch_epilogue_fwd_fast(const fno_plan* p, int mode, const float2* T
   a.y = y;
   a.z = zsave;
   a.gelu = (p->desc.flags & FNO_FLAG_GELU) != 0;
-  const int kmode = mode != EPI_BLOCK ? 0 : (zsave ? 2 : 1);
+  const bool ig = (p->desc.flags & FNO_FLAG_INPUT_GELU) != 0;
+  const int kmode = mode != EPI_BLOCK ? 0 : ((zsave ? 2 : 1) | (ig ? 8 : 0));
   a.block = kmode != 0;
   const int64_t wgs = (int64_t)g.B * a.lines / a.lpw;
   if (wgs > 0x7fffffff) return hipErrorInvalidValue;
@@ -814,7 +849,8 @@ hipError_t launch_epilogue_bwd_fast(const fno_plan* p, int mode, const float2* T
   a.block = mode == EPI_BLOCK;
   a.gelu = z != nullptr;
   const bool tanh_pre = (p->desc.flags & FNO_FLAG_TANH_PREACT) != 0;
-  const int kmode = mode != EPI_BLOCK ? 1 : (z ? 7 : 3);
+  const int kmode = (mode != EPI_BLOCK ? 1 : (z ? 7 : 3)) |
+                    ((p->desc.flags & FNO_FLAG_INPUT_GELU) ? 8 : 0);
   const int64_t wgs = (int64_t)g.B * a.lines / a.lpw;
   if (wgs > 0x7fffffff) return hipErrorInvalidValue;
   switch (g.Cin) {

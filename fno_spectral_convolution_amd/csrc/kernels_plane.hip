@@ -43,6 +43,8 @@ template <int PIN>
 __device__ __forceinline__ float prologue(float v, float w) {
   if (PIN == PLANE_TANH) return tanh_fast(v);
   if (PIN == PLANE_GELU_GRAD) return v * gelu_grad_as(w);
+  if (PIN == PLANE_GELU) return gelu_as(v);
+  if (PIN == PLANE_TANH_GELU) return tanh_fast(gelu_as(v));
   return v;
 }
 
@@ -592,6 +594,8 @@ hipError_t launch_plane_fwd_fast(const fno_plan* p, int plane_in, int chans, con
   switch (plane_in) {
     case PLANE_X: launch_plane_pin<PLANE_X>(p, a, grid, s); break;
     case PLANE_TANH: launch_plane_pin<PLANE_TANH>(p, a, grid, s); break;
+    case PLANE_GELU: launch_plane_pin<PLANE_GELU>(p, a, grid, s); break;
+    case PLANE_TANH_GELU: launch_plane_pin<PLANE_TANH_GELU>(p, a, grid, s); break;
     default: launch_plane_pin<PLANE_GELU_GRAD>(p, a, grid, s); break;
   }
   return hipGetLastError();

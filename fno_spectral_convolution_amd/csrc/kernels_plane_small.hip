@@ -42,6 +42,8 @@ template <int PIN>
 __device__ __forceinline__ float small_prologue(float v, float w) {
   if (PIN == PLANE_TANH) return tanh_fast(v);
   if (PIN == PLANE_GELU_GRAD) return v * gelu_grad_as(w);
+  if (PIN == PLANE_GELU) return gelu_as(v);
+  if (PIN == PLANE_TANH_GELU) return tanh_fast(gelu_as(v));
   return v;
 }
 
@@ -290,6 +292,8 @@ hipError_t launch_plane_small(const fno_plan* p, int plane_in, int chans, const 
   switch (plane_in) {
     case PLANE_X: launch_small_pin<PLANE_X>(p, a, s); break;
     case PLANE_TANH: launch_small_pin<PLANE_TANH>(p, a, s); break;
+    case PLANE_GELU: launch_small_pin<PLANE_GELU>(p, a, s); break;
+    case PLANE_TANH_GELU: launch_small_pin<PLANE_TANH_GELU>(p, a, s); break;
     default: launch_small_pin<PLANE_GELU_GRAD>(p, a, s); break;
   }
   return hipGetLastError();

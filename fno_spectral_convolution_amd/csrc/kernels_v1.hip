@@ -77,7 +77,8 @@ k_plane_fwd(Geom g, const float2* __restrict__ root_b, const float2* __restrict_
     for (int e = tid; e < nr * Nb; e += kPlaneThreads) {
       const int64_t off = base + (int64_t)r0 * Nb + e;
       float v = in0[off];
-      if (PIN == PLANE_TANH) v = tanhf(v);
+      if (PIN == PLANE_GELU || PIN == PLANE_TANH_GELU) v = gelu_f(v);
+      if (PIN == PLANE_TANH || PIN == PLANE_TANH_GELU) v = tanhf(v);
       if (PIN == PLANE_GELU_GRAD) v = v * gelu_grad_f(in1[off]);
       s_x[e] = opnd(v, bf);
     }
@@ -151,6 +152,14 @@ hipError_t launch_plane_fwd(const fno_plan* p, int plane_in, int chans, const fl
     case PLANE_TANH:
       hipLaunchKernelGGL(k_plane_fwd<PLANE_TANH>, grid, dim3(kPlaneThreads), lds, s, g, rb, ra,
                          in0, in1, out, planes, rows);
+      break;
+    case PLANE_GELU:
+      hipLaunchKernelGGL(k_plane_fwd<PLANE_GELU>, grid, dim3(kPlaneThreads), lds, s, g, rb, ra,
+                         in0, in1, out, planes, rows);
+      break;
+    case PLANE_TANH_GELU:
+      hipLaunchKernelGGL(k_plane_fwd<PLANE_TANH_GELU>, grid, dim3(kPlaneThreads), lds, s, g, rb,
+                         ra, in0, in1, out, planes, rows);
       break;
     default:
       hipLaunchKernelGGL(k_plane_fwd<PLANE_GELU_GRAD>, grid, dim3(kPlaneThreads), lds, s, g, rb,
@@ -266,7 +275,7 @@ hipError_t launch_outer_inv(const fno_plan* p, int axis, int chans, const float2
 constexpr int kEpiThreads = 128;
 
 __global__ void __launch_bounds__(kEpiThreads)
-k_epilogue_fwd(Geom g, int mode, bool gelu, const float2* __restrict__ root_b,
+k_epilogue_fwd(Geom g, int mode, bool gelu, bool ig, const float2* __restrict__ root_b,
                const float2* __restrict__ T, const float* __restrict__ x,
                const float* __restrict__ wb, const float* __restrict__ bias,
                float* __restrict__ y, float* __restrict__ zsave) {
@@ -285,8 +294,10 @@ k_epilogue_fwd(Geom g, int mode, bool gelu, const float2* __restrict__ root_b,
   if (block) {
     for (int t = tid; t < Cout * Cin; t += kEpiThreads) s_wb[t] = wb[t];
     for (int t = tid; t < Cout; t += kEpiThreads) s_bias[t] = bias ? bias[t] : 0.f;
-    for (int ci = 0; ci < Cin; ++ci)
-      s_x[ci * kEpiThreads + tid] = (p < P) ? x[((int64_t)b * Cin + ci) * P + p] : 0.f;
+    for (int ci = 0; ci < Cin; ++ci) {
+      const float xv = (p < P) ? x[((int64_t)b * Cin + ci) * P + p] : 0.f;
+      s_x[ci * kEpiThreads + tid] = ig ? gelu_f(xv) : xv;  // the block's input
+    }
   }
   __syncthreads();
   if (p >= P) return;
@@ -330,8 +341,9 @@ hipError_t launch_epilogue_fwd(const fno_plan* p, int mode, const float2* T, con
                                       (mode == EPI_BLOCK ? (size_t)g.Cin * kEpiThreads : 0));
   dim3 grid((unsigned)((g.P + kEpiThreads - 1) / kEpiThreads), (unsigned)g.B);
   const bool gelu = (p->desc.flags & FNO_FLAG_GELU) != 0;
+  const bool ig = (p->desc.flags & FNO_FLAG_INPUT_GELU) != 0;
   const float2* rb = g.bf16 ? p->t.root_bf[g.d - 1] : p->t.root[g.d - 1];
-  hipLaunchKernelGGL(k_epilogue_fwd, grid, dim3(kEpiThreads), lds, s, g, mode, gelu, rb, T, x,
+  hipLaunchKernelGGL(k_epilogue_fwd, grid, dim3(kEpiThreads), lds, s, g, mode, gelu, ig, rb, T, x,
                      wb, (p->desc.flags & FNO_FLAG_BIAS) ? bias : nullptr, y, zsave);
   return hipGetLastError();
 }
@@ -344,7 +356,8 @@ constexpr int kEbThreads = 64;
 constexpr int kEbPairs = (64 * 64 + 64 + kEbThreads - 1) / kEbThreads;
 
 __global__ void __launch_bounds__(kEbThreads)
-k_epilogue_bwd(Geom g, int mode, bool gelu, bool tanh_pre, const float2* __restrict__ root_b,
+k_epilogue_bwd(Geom g, int mode, bool gelu, bool tanh_pre, bool ig,
+               const float2* __restrict__ root_b,
                const float2* __restrict__ Tg, const float* __restrict__ x,
                const float* __restrict__ wb, const float* __restrict__ gy,
                const float* __restrict__ z, float* __restrict__ grad_x,
@@ -386,8 +399,10 @@ k_epilogue_bwd(Geom g, int mode, bool gelu, bool tanh_pre, const float2* __restr
         }
         s_gz[o * kEbThreads + tid] = v;
       }
-      for (int ci = 0; ci < Cin; ++ci)
-        s_x[ci * kEbThreads + tid] = live ? x[((int64_t)b * Cin + ci) * P + p] : 0.f;
+      for (int ci = 0; ci < Cin; ++ci) {
+        const float xv = live ? x[((int64_t)b * Cin + ci) * P + p] : 0.f;
+        s_x[ci * kEbThreads + tid] = ig ? gelu_f(xv) : xv;  // the block's input
+      }
     }
     __syncthreads();
     if (live && grad_x) {
@@ -407,7 +422,7 @@ k_epilogue_bwd(Geom g, int mode, bool gelu, bool tanh_pre, const float2* __restr
         gs *= g.sc[g.d - 1] * g.inv_gain[1];  // 1 except on IEEE-half plans
         const int64_t off = ((int64_t)b * Cin + ci) * P + p;
         if (tanh_pre) {
-          const float xv = block ? s_x[ci * kEbThreads + tid] : x[off];
+          const float xv = block ? s_x[ci * kEbThreads + tid] : (ig ? gelu_f(x[off]) : x[off]);
           const float th = tanhf(xv);
           gs *= (1.f - th * th);
         }
@@ -416,6 +431,7 @@ k_epilogue_bwd(Geom g, int mode, bool gelu, bool tanh_pre, const float2* __restr
           for (int o = 0; o < Cout; ++o) acc += s_wb[o * Cin + ci] * s_gz[o * kEbThreads + tid];
           gs += acc;
         }
+        if (ig) gs *= gelu_grad_f(x[off]);  // the input was GELU(x)
         grad_x[off] = gs;
       }
     }
@@ -462,9 +478,10 @@ hipError_t launch_epilogue_bwd(const fno_plan* p, int mode, const float2* Tg, co
                                                          : 0));
   const bool gelu = (p->desc.flags & FNO_FLAG_GELU) != 0;
   const bool tanh_pre = (p->desc.flags & FNO_FLAG_TANH_PREACT) != 0;
+  const bool ig = (p->desc.flags & FNO_FLAG_INPUT_GELU) != 0;
   const float2* rb = g.bf16 ? p->t.root_bf[g.d - 1] : p->t.root[g.d - 1];
   hipLaunchKernelGGL(k_epilogue_bwd, dim3((unsigned)groups, (unsigned)g.B), dim3(kEbThreads),
-                     lds, s, g, mode, gelu, tanh_pre, rb, Tg, x, wb, gy, z, grad_x, red_part,
+                     lds, s, g, mode, gelu, tanh_pre, ig, rb, Tg, x, wb, gy, z, grad_x, red_part,
                      tpg);
   return hipGetLastError();
 }

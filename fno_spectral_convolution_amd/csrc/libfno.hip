@@ -111,7 +111,8 @@ fno_status fno_plan_validate(const fno_plan_desc* d) {
   if (d->ndim < 2 || d->ndim > 4)
     return fail(FNO_ERR_INVALID_ARGUMENT, "ndim %d not in {2,3,4}", d->ndim);
   if (d->reserved != 0) return fail(FNO_ERR_INVALID_ARGUMENT, "reserved field must be 0");
-  if (d->flags & ~(uint32_t)(FNO_FLAG_TANH_PREACT | FNO_FLAG_GELU | FNO_FLAG_BIAS))
+  if (d->flags & ~(uint32_t)(FNO_FLAG_TANH_PREACT | FNO_FLAG_GELU | FNO_FLAG_BIAS |
+                             FNO_FLAG_INPUT_GELU))
     return fail(FNO_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", d->flags);
   if (d->spectral_dtype != FNO_DTYPE_F32 && d->spectral_dtype != FNO_DTYPE_BF16 &&
       d->spectral_dtype != FNO_DTYPE_F16)
@@ -629,6 +630,8 @@ hipError_t timing_collect(TimingState& T) {
 const char* plane_name(int plane_in) {
   switch (plane_in) {
     case fno::PLANE_TANH: return "plane_fwd_tanh";
+    case fno::PLANE_GELU: return "plane_fwd_gelu";
+    case fno::PLANE_TANH_GELU: return "plane_fwd_tanh_gelu";
     case fno::PLANE_GELU_GRAD: return "plane_fwd_gelugrad";
     default: return "plane_fwd";
   }
@@ -691,7 +694,9 @@ fno_status check_ws(const fno_plan* p, void* ws, size_t ws_bytes) {
 }
 
 int pre_mode(const fno_plan* p) {
-  return (p->desc.flags & FNO_FLAG_TANH_PREACT) ? fno::PLANE_TANH : fno::PLANE_X;
+  const bool t = (p->desc.flags & FNO_FLAG_TANH_PREACT) != 0;
+  if (p->desc.flags & FNO_FLAG_INPUT_GELU) return t ? fno::PLANE_TANH_GELU : fno::PLANE_GELU;
+  return t ? fno::PLANE_TANH : fno::PLANE_X;
 }
 
 // The spectral-weight step of a block: the dense per-mode mix, or a Tucker-factorised one.
@@ -740,12 +745,15 @@ fno_status block_fwd_impl(const fno_plan* p, const float* x, const float* wb, co
   if (fno::epilogue_rows_ok(p, fno::EPI_BLOCK, x, y, zsave)) {
     st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T, p->g.d - 2);
     if (st != FNO_OK) return st;
-    LAUNCH("epilogue_rows_fwd", s, fno::launch_epilogue_rows(p, fno::EPI_BLOCK, T, x, wb, bias, y, zsave, s));
+    // timer names tell launches that also save z apart (their bytes differ)
+    LAUNCH(zsave ? "epilogue_rows_fwd_zsave" : "epilogue_rows_fwd", s,
+           fno::launch_epilogue_rows(p, fno::EPI_BLOCK, T, x, wb, bias, y, zsave, s));
     return FNO_OK;
   }
   st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T, p->g.d - 1);
   if (st != FNO_OK) return st;
-  LAUNCH("epilogue_fwd", s, fno::launch_epilogue_fwd(p, fno::EPI_BLOCK, T, x, wb, bias, y, zsave, s));
+  LAUNCH(zsave ? "epilogue_fwd_zsave" : "epilogue_fwd", s,
+         fno::launch_epilogue_fwd(p, fno::EPI_BLOCK, T, x, wb, bias, y, zsave, s));
   return FNO_OK;
 }
 
@@ -772,7 +780,9 @@ fno_status block_bwd_impl(const fno_plan* p, const float* x, const float* wb, co
       st = inverse_outer(p, g.Cin, ghx, ws, s, &Tg, g.d - 1);
       if (st != FNO_OK) return st;
     }
-    LAUNCH("epilogue_bwd", s, fno::launch_epilogue_bwd(p, fno::EPI_BLOCK, Tg, x, wb, gy, z, grad_x, red, s));
+    // with the output GELU the epilogue also reads z (another field)
+    LAUNCH(z ? "epilogue_bwd_gelu" : "epilogue_bwd", s,
+           fno::launch_epilogue_bwd(p, fno::EPI_BLOCK, Tg, x, wb, gy, z, grad_x, red, s));
     if (red)
       LAUNCH("bypass_grad_finish", s, fno::launch_bypass_grad_finish(p, red, grad_wb, grad_bias, grad_x, s));
   }

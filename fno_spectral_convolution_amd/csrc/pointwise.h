@@ -39,6 +39,13 @@ __device__ __forceinline__ float gelu_grad_as(float z) {
   return n.cdf + z * n.pdf;
 }
 
+// GELU(z) and GELU'(z) from one evaluation of Phi and phi
+__device__ __forceinline__ void gelu_and_grad(float z, float& g, float& gp) {
+  const NormalParts n = normal_parts(z);
+  g = z * n.cdf;
+  gp = n.cdf + z * n.pdf;
+}
+
 // tanh(v) = 1 - 2 / (e^{2v} + 1): five instructions (exp, reciprocal); saturates to +-1 for
 // large |v| (e = inf or 0).  Near 0 the absolute error is a few float32 ulps of 1, far below
 // the bfloat16 rounding applied to the pre-activated field and the 1e-2 tolerance of that

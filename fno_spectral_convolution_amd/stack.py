@@ -60,15 +60,14 @@ class StackRunner:
         dev = torch.device(device)
         self.device = dev
         C = wl.width
-        # one plan per spectral precision the run has used (a plan holds only its tables and
-        # workspace); the workload's tanh pre-activation is kept by all of them
+        # one plan per spectral precision the run has used and block role (a plan holds only
+        # its tables and workspace); the workload's tanh pre-activation is kept by all of them
         self._tanh = bool(wl.mixed)
         self._plans = {}
         self._tuckers = {}
         self.tucker = bool(wl.tucker_ranks)
         self.precision = precision(wl)
-        self.plan = self._plan_for(self.precision)
-        self.tk = self._tuckers.get(self.precision)
+        self._use_precision(self.precision)
         # IEEE-half training takes a static loss scale: every gradient the step returns
         # (weights, bypass, bias, input) comes out multiplied by grad_scale
         self.grad_scale = F16_LOSS_SCALE if self.precision == "f16" else 1.0
@@ -92,8 +91,8 @@ class StackRunner:
         if wl.train:
             self.acts = [torch.empty(shape, dtype=torch.float32, device=dev)
                          for _ in range(nb + 1)]
-            self.saves = [self.plan.new_save() for _ in range(nb)]
-            self._save_bytes = self.plan.save_bytes
+            self.saves = [self.block_plans[i].new_save() for i in range(nb)]
+            self._save_bytes = [self.block_plans[i].save_bytes for i in range(nb)]
             self.g = [torch.empty(shape, dtype=torch.float32, device=dev) for _ in range(2)]
             self.grads = []
             for p in self.params:
@@ -114,21 +113,38 @@ class StackRunner:
         if self.lp is not None:
             out_shape = (wl.batch, wl.proj_out) + tuple(wl.grid)
             self.out = torch.empty(out_shape, dtype=torch.float32, device=dev)
-        self.plan.workspace()
+    def role(self, i):
+        """(input GELU, output GELU) of block i.  A training stack moves the GELU between two
+        blocks to the start of the later one: each inner block then keeps only its
+        pre-activation z, and its backward reads z and the incoming gradient once instead of
+        twice.  The network, its outputs and its gradients are those of the plain stack."""
+        nb = self.wl.blocks
+        if not self.wl.train or nb == 1:
+            return (False, True)
+        return (i > 0, i == nb - 1)
 
-    def _plan_for(self, prec):
-        if prec not in self._plans:
+    def _plan_for(self, prec, role=(False, True)):
+        key = (prec, role)
+        if key not in self._plans:
             wl = self.wl
             plan = L.Plan(wl.batch, wl.width, wl.width, wl.grid, wl.modes,
-                          mixed=_PLAN_MIXED[prec], tanh=self._tanh, device=self.device)
+                          mixed=_PLAN_MIXED[prec], tanh=self._tanh, gelu=role[1],
+                          input_gelu=role[0], device=self.device)
             if wl.tucker_ranks:
                 tk = L.Tucker(plan, wl.tucker_ranks)
                 tk.workspace()
-                self._tuckers[prec] = tk
+                self._tuckers[key] = tk
             else:
                 plan.workspace()
-            self._plans[prec] = plan
-        return self._plans[prec]
+            self._plans[key] = plan
+        return self._plans[key]
+
+    def _use_precision(self, prec):
+        nb = self.wl.blocks
+        self.block_plans = [self._plan_for(prec, self.role(i)) for i in range(nb)]
+        self.block_tuckers = [self._tuckers.get((prec, self.role(i))) for i in range(nb)]
+        self.plan = self.block_plans[-1]
+        self.tk = self.block_tuckers[-1]
 
     def set_precision(self, prec):
         """Run the following steps with spectral precision `prec` ("f32", "bf16", "f16").
@@ -138,12 +154,12 @@ class StackRunner:
             raise ValueError(f"spectral precision must be one of {SPECTRAL_PRECISIONS}")
         if prec == self.precision:
             return
-        plan = self._plan_for(prec)
-        if self.wl.train and plan.save_bytes > self._save_bytes:
-            self.saves = [plan.new_save() for _ in range(self.wl.blocks)]
-            self._save_bytes = plan.save_bytes
-        self.plan = plan
-        self.tk = self._tuckers.get(prec)
+        self._use_precision(prec)
+        if self.wl.train:
+            for i, plan in enumerate(self.block_plans):
+                if plan.save_bytes > self._save_bytes[i]:
+                    self.saves[i] = plan.new_save()
+                    self._save_bytes[i] = plan.save_bytes
         self.precision = prec
         self.grad_scale = F16_LOSS_SCALE if prec == "f16" else 1.0
 
@@ -174,10 +190,11 @@ class StackRunner:
         for i, p in enumerate(self.params):
             dst = self._act(i + 1)
             if self.tucker:
-                self.tk.block_fwd(h, p["core"], p["factors"], p["wb"], p["bias"],
-                                  save=self.saves[i], out=dst)
+                self.block_tuckers[i].block_fwd(h, p["core"], p["factors"], p["wb"], p["bias"],
+                                                save=self.saves[i], out=dst)
             else:
-                self.plan.block_fwd(h, p["w"], p["wb"], p["bias"], save=self.saves[i], out=dst)
+                self.block_plans[i].block_fwd(h, p["w"], p["wb"], p["bias"], save=self.saves[i],
+                                              out=dst)
             h = dst
         if self.lp is not None:
             pr = self.lp["proj"]
@@ -192,12 +209,13 @@ class StackRunner:
                 x_i = src0 if i == 0 else self.acts[i]
                 gout = 1 - gin
                 if self.tucker:
-                    self.tk.block_bwd(x_i, p["core"], p["factors"], p["wb"], p["bias"],
-                                      self.saves[i], self.g[gin],
-                                      out={"x": self.g[gout], **self.grads[i]})
+                    self.block_tuckers[i].block_bwd(x_i, p["core"], p["factors"], p["wb"],
+                                                    p["bias"], self.saves[i], self.g[gin],
+                                                    out={"x": self.g[gout], **self.grads[i]})
                 else:
-                    self.plan.block_bwd(x_i, p["w"], p["wb"], p["bias"], self.saves[i],
-                                        self.g[gin], out={"x": self.g[gout], **self.grads[i]})
+                    self.block_plans[i].block_bwd(x_i, p["w"], p["wb"], p["bias"], self.saves[i],
+                                                  self.g[gin],
+                                                  out={"x": self.g[gout], **self.grads[i]})
                 gin = gout
             self.grad_x = self.g[gin]
         return h

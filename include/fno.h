@@ -84,7 +84,10 @@ typedef enum fno_dtype { FNO_DTYPE_F32 = 0, FNO_DTYPE_BF16 = 1, FNO_DTYPE_F16 = 
 enum {
   FNO_FLAG_TANH_PREACT = 1u, /* x' = tanh(x) feeds the spectral path only [MIXED] */
   FNO_FLAG_GELU = 2u,        /* block output y = GELU(z); without it y = z            */
-  FNO_FLAG_BIAS = 4u         /* bias pointer is read; without it bias is taken as 0    */
+  FNO_FLAG_BIAS = 4u,        /* bias pointer is read; without it bias is taken as 0    */
+  FNO_FLAG_INPUT_GELU = 8u   /* x is a pre-activation: the block's input is GELU(x), and
+                                grad_x carries GELU'(x).  Lets a stack keep only each block's z
+                                (the previous block runs without FNO_FLAG_GELU)           */
 };
 
 typedef struct fno_plan_desc {

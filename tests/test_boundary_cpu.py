@@ -44,6 +44,7 @@ def _desc(**kw):
     dict(grid=(128, 128, 128, 20), modes=(12, 12, 12, 8), batch=1),
     dict(grid=(512, 512), modes=(32, 32), c_in=64, c_out=64, dtype=1, flags=7),
     dict(grid=(512, 512), modes=(32, 32), c_in=64, c_out=64, dtype=2, flags=7),
+    dict(grid=(512, 512), modes=(32, 32), c_in=64, c_out=64, dtype=1, flags=15),
     dict(grid=(8, 8), modes=(4, 5)), dict(grid=(15, 9), modes=(7, 5)),
 ])
 def test_validate_accepts(kw):
@@ -57,7 +58,7 @@ def test_validate_accepts(kw):
     (dict(modes=(0, 12)), L.FNO_ERR_INVALID_ARGUMENT),
     (dict(batch=0), L.FNO_ERR_INVALID_ARGUMENT),
     (dict(c_in=0), L.FNO_ERR_INVALID_ARGUMENT),
-    (dict(flags=8), L.FNO_ERR_INVALID_ARGUMENT),
+    (dict(flags=16), L.FNO_ERR_INVALID_ARGUMENT),
     (dict(dtype=7), L.FNO_ERR_INVALID_ARGUMENT),
     (dict(c_in=65), L.FNO_ERR_UNSUPPORTED),
     (dict(grid=(64, 8192), modes=(12, 12)), L.FNO_ERR_UNSUPPORTED),

@@ -232,3 +232,62 @@ def test_bad_workspace_is_an_error(L):
                                 plan.workspace().data_ptr(), plan.ws_bytes, 0)
     assert ei.value.status == L.FNO_ERR_INVALID_ARGUMENT
     plan.close()
+
+
+# shapes for the pre-activation input: each line-epilogue width, the generic kernels, a short
+# contiguous axis (line kernels decline, generic epilogue), 3D and 4D
+IG_CASES = [c for c in CASES if c[0] in (
+    "2d_ragged", "2d_c1shape", "2d_mc_c16", "2d_mc_c32", "2d_mc_c64", "3d_mc_c20",
+    "4d_short_t20", "2d_rows_c20", "2d_odd_maxmodes", "4d_t20")]
+
+
+@pytest.mark.parametrize("act", [True, False], ids=["gelu_out", "z_out"])
+@pytest.mark.parametrize("prec", PRECISIONS[:3], ids=[p[0] for p in PRECISIONS[:3]])
+@pytest.mark.parametrize("case", IG_CASES, ids=[c[0] for c in IG_CASES])
+def test_block_input_gelu(L, case, prec, act):
+    """A block whose input is a pre-activation (FNO_FLAG_INPUT_GELU): forward, backward."""
+    name, batch, cin, cout, grid, modes = case
+    pname, mixed, tanh = prec
+    announce("block input_gelu", name, pname, act)
+    seed = 900 + zlib.crc32(name.encode()) % 1000
+    x, w, wb, b = inputs.small_case(seed, batch, cin, cout, grid, modes)
+    gy = inputs.normal_like(seed, (batch, cout) + grid)
+    tol = tol_for(mixed)
+    plan = L.Plan(batch, cin, cout, grid, modes, mixed=mixed, tanh=tanh, gelu=act,
+                  input_gelu=True)
+    tx, tw, twb, tb, tg = (_dev(a) for a in (x, w, wb, b, gy))
+    save = plan.new_save()
+    y = plan.block_fwd(tx, tw, twb, tb, save=save)
+    g = plan.block_bwd(tx, tw, twb, tb, save, tg)
+    _torch().cuda.synchronize()
+    ref = O.block_bwd(x, w, wb, b, modes, gy, tanh=tanh, act=act, input_gelu=True)
+    check("y", _host(y), ref["fwd"]["y"], tol)
+    check("grad_x", _host(g["x"]), ref["grad_x"], tol)
+    check("grad_w", _host(g["w"]), ref["grad_w"], tol)
+    check("grad_wb", _host(g["wb"]), ref["grad_wb"], tol)
+    check("grad_bias", _host(g["bias"]), ref["grad_bias"], tol)
+    plan.close()
+
+
+@pytest.mark.parametrize("prec", PRECISIONS[:2], ids=[p[0] for p in PRECISIONS[:2]])
+@pytest.mark.parametrize("case", IG_CASES[:6], ids=[c[0] for c in IG_CASES[:6]])
+def test_spectral_conv_input_gelu(L, case, prec):
+    name, batch, cin, cout, grid, modes = case
+    pname, mixed, tanh = prec
+    announce("spectral input_gelu", name, pname)
+    seed = 1900 + zlib.crc32(name.encode()) % 1000
+    x, w, _, _ = inputs.small_case(seed, batch, cin, cout, grid, modes)
+    gy = inputs.normal_like(seed, (batch, cout) + grid)
+    tol = tol_for(mixed)
+    plan = L.Plan(batch, cin, cout, grid, modes, mixed=mixed, tanh=tanh, gelu=False, bias=False,
+                  input_gelu=True)
+    tx, tw, tg = (_dev(a) for a in (x, w, gy))
+    ys = plan.spectral_conv_fwd(tx, tw)
+    gx, gw = plan.spectral_conv_bwd(tx, tw, tg)
+    _torch().cuda.synchronize()
+    fwd = O.spectral_conv_fwd(x, w, modes, tanh=tanh, input_gelu=True)
+    bwd = O.spectral_conv_bwd(x, w, modes, gy, tanh=tanh, input_gelu=True)
+    check("y_spec", _host(ys), fwd["y_spec"], tol)
+    check("grad_x", _host(gx), bwd["grad_x"], tol)
+    check("grad_w", _host(gw), bwd["grad_w"], tol)
+    plan.close()
