@@ -1,7 +1,7 @@
 """Precision scheduling on the GPU (mixed-precision neural-operator page, "Tiivistelmä":
-training moves from mixed to full precision): a two-block 2D training stack runs four steps
-through StackRunner.run, two with half operands, two in fp32 with the tanh pre-activation
-kept.  Every step's loss, output and gradients are compared with the oracle's training step
+training moves from mixed to full precision): a two-block 2D training stack (dense or
+Tucker-factorised weights) runs four steps through StackRunner.run, two with half operands,
+two in fp32 with the tanh pre-activation kept.  Every step's loss, output and gradients are compared with the oracle's training step
 (tanh on) at the tolerance of the precision the step ran in; steps of one precision must agree
 bit for bit (no weight update runs between them)."""
 import numpy as np
@@ -22,24 +22,53 @@ def _host(t):
     return t.detach().cpu().numpy().copy()
 
 
+def _tucker_train_ref(hi, modes):
+    """The oracle's training step of a stack of Tucker blocks (GELU after every block, MSE)."""
+    acts = [np.asarray(hi["x"], dtype=np.float64)]
+    for blk in hi["blocks"]:
+        acts.append(O.tucker_block_fwd(acts[-1], blk["core"], blk["factors"], blk["wb"],
+                                       blk["bias"], modes, tanh=True)["y"])
+    loss, g = O.mse_loss_grad(acts[-1], hi["target"])
+    grads = [None] * len(hi["blocks"])
+    for i in reversed(range(len(hi["blocks"]))):
+        blk = hi["blocks"][i]
+        r = O.tucker_block_bwd(acts[i], blk["core"], blk["factors"], blk["wb"], blk["bias"],
+                               modes, g, tanh=True)
+        grads[i] = {"grad_core": r["grad_core"], "grad_factors": r["grad_factors"],
+                    "grad_wb": r["grad_wb"], "grad_bias": r["grad_bias"]}
+        g = r["grad_x"]
+    return {"loss": loss, "y": acts[-1], "grad_x": g, "grads": grads}
+
+
+@pytest.mark.parametrize("weights", ["dense", "tucker"])
 @pytest.mark.parametrize("half", ["bf16", "f16"])
-def test_precision_schedule_training_run(half):
+def test_precision_schedule_training_run(half, weights):
     import torch
     from fno_spectral_convolution_amd.stack import PrecisionSchedule, StackRunner
-    announce("schedule", half)
-    wl = configs.Workload(mixed=True if half == "bf16" else "f16", **_WL)
+    announce("schedule", half, weights)
+    extra = {"tucker_ranks": (8, 8, 6, 6)} if weights == "tucker" else {}
+    wl = configs.Workload(mixed=True if half == "bf16" else "f16", **_WL, **extra)
     runner = StackRunner(wl, device="cuda")
     hi = runner.host
-    ref = O.train_step(hi["x"], hi["target"], hi["blocks"], wl.modes, tanh=True)
+    if weights == "tucker":
+        ref = _tucker_train_ref(hi, wl.modes)
+    else:
+        ref = O.train_step(hi["x"], hi["target"], hi["blocks"], wl.modes, tanh=True)
+    wkeys = ("core", "wb", "bias") if weights == "tucker" else ("w", "wb", "bias")
     seen = []
 
     def on_step(i, out):
         torch.cuda.synchronize()
         s = runner.grad_scale
+        grads = []
+        for g in runner.grads:
+            d = {k: _host(g[k]) / s for k in wkeys}
+            if weights == "tucker":
+                d["factors"] = [_host(u) / s for u in g["factors"]]
+            grads.append(d)
         seen.append({"precision": runner.precision, "scale": s, "y": _host(out),
                      "loss": float(_host(runner.loss)[0]), "grad_x": _host(runner.grad_x) / s,
-                     "grads": [{k: _host(g[k]) / s for k in ("w", "wb", "bias")}
-                               for g in runner.grads]})
+                     "grads": grads})
 
     runner.run(PrecisionSchedule(2, half), 4, on_step=on_step)
     assert [r["precision"] for r in seen] == [half, half, "f32", "f32"]
@@ -51,12 +80,17 @@ def test_precision_schedule_training_run(half):
         assert abs(r["loss"] - ref["loss"]) <= tol * ref["loss"], (r["loss"], ref["loss"])
         check("grad_x", r["grad_x"], ref["grad_x"], tol)
         for b, (g, gr) in enumerate(zip(r["grads"], ref["grads"])):
-            check(f"block {b} grad_w", g["w"], gr["grad_w"], tol)
+            if weights == "tucker":
+                check(f"block {b} grad_core", g["core"], gr["grad_core"], tol)
+                for n, (u, ur) in enumerate(zip(g["factors"], gr["grad_factors"])):
+                    check(f"block {b} grad_factor {n}", u, ur, tol)
+            else:
+                check(f"block {b} grad_w", g["w"], gr["grad_w"], tol)
             check(f"block {b} grad_wb", g["wb"], gr["grad_wb"], tol)
             check(f"block {b} grad_bias", g["bias"], gr["grad_bias"], tol)
     for a, b in ((seen[0], seen[1]), (seen[2], seen[3])):
         assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["grad_x"], b["grad_x"])
         for ga, gb in zip(a["grads"], b["grads"]):
-            assert all(np.array_equal(ga[k], gb[k]) for k in ga)
+            assert all(np.array_equal(ga[k], gb[k]) for k in wkeys)
     # the fp32 steps after the switch differ from the half steps before it
     assert not np.array_equal(seen[1]["y"], seen[2]["y"])
