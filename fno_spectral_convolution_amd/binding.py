@@ -38,7 +38,8 @@ EXPORTS = [
     "fno_spectral_conv_fwd", "fno_spectral_conv_bwd", "fno_block_fwd", "fno_block_bwd",
     "fno_pointwise_fwd", "fno_mse_workspace_bytes", "fno_mse_grad", "fno_mse_grad_scaled",
     "fno_tucker_order", "fno_tucker_create", "fno_tucker_destroy", "fno_tucker_query",
-    "fno_tucker_block_fwd", "fno_tucker_block_bwd",
+    "fno_tucker_block_fwd", "fno_tucker_block_bwd", "fno_tucker_spectral_conv_fwd",
+    "fno_tucker_spectral_conv_bwd",
     "fno_timing_enable", "fno_timing_select",
     "fno_timing_reset", "fno_timing_count", "fno_timing_get", "fno_status_string",
     "fno_last_error_message",
@@ -91,6 +92,10 @@ def _load():
                                          P]),
         "fno_tucker_block_bwd": (c_int, [P, P, P, POINTER(c_void_p), P, P, P, P, P, P,
                                          POINTER(c_void_p), P, P, P, c_size_t, P]),
+        "fno_tucker_spectral_conv_fwd": (c_int, [P, P, P, POINTER(c_void_p), P, P, P, c_size_t,
+                                                 P]),
+        "fno_tucker_spectral_conv_bwd": (c_int, [P, P, P, POINTER(c_void_p), P, P, P, P,
+                                                 POINTER(c_void_p), P, c_size_t, P]),
         "fno_timing_enable": (c_int, [c_int]),
         "fno_timing_select": (c_int, [c_char_p]),
         "fno_timing_reset": (c_int, []),
@@ -387,6 +392,19 @@ def fno_tucker_block_bwd(h, x, core, factors, wb, bias, save, gy, gx, gcore, gfa
            "fno_tucker_block_bwd")
 
 
+def fno_tucker_spectral_conv_fwd(h, x, core, factors, y, save, ws, ws_bytes, stream):
+    _check(_lib.fno_tucker_spectral_conv_fwd(h, x, core, _ptr_arr(factors), y, save, ws,
+                                             ws_bytes, stream), "fno_tucker_spectral_conv_fwd")
+
+
+def fno_tucker_spectral_conv_bwd(h, x, core, factors, save, gys, gx, gcore, gfactors, ws,
+                                 ws_bytes, stream):
+    gf = _ptr_arr(gfactors) if gfactors is not None else None
+    _check(_lib.fno_tucker_spectral_conv_bwd(h, x, core, _ptr_arr(factors), save, gys, gx, gcore,
+                                             gf, ws, ws_bytes, stream),
+           "fno_tucker_spectral_conv_bwd")
+
+
 class Tucker:
     """Tucker-factorised spectral weights bound to a ``Plan``: core complex64
     [R_in, R_out, R_0, .., R_{d-1}], factors complex64 [C_in, R_in], [C_out, R_out],
@@ -434,6 +452,31 @@ class Tucker:
                              y.data_ptr(), _ptr(save), ws.data_ptr(), self.ws_bytes,
                              p._stream())
         return y
+
+    def spectral_conv_fwd(self, x, core, factors, save=None, out=None):
+        p = self.plan
+        y = out if out is not None else p._field(p.c_out)
+        ws = self.workspace()
+        fno_tucker_spectral_conv_fwd(self.handle, x.data_ptr(), core.data_ptr(),
+                                     [f.data_ptr() for f in factors], y.data_ptr(), _ptr(save),
+                                     ws.data_ptr(), self.ws_bytes, p._stream())
+        return y
+
+    def spectral_conv_bwd(self, x, core, factors, grad_y_spec, save=None, want_x=True,
+                          want_w=True):
+        """Returns (grad_x, grad_core, grad_factors) (None where not asked)."""
+        p = self.plan
+        t = p.torch
+        gx = p._field(p.c_in) if want_x else None
+        gcore = t.empty_like(core) if want_w else None
+        gfac = [t.empty_like(f) for f in factors] if want_w else None
+        ws = self.workspace()
+        fno_tucker_spectral_conv_bwd(self.handle, x.data_ptr(), core.data_ptr(),
+                                     [f.data_ptr() for f in factors], _ptr(save),
+                                     grad_y_spec.data_ptr(), _ptr(gx), _ptr(gcore),
+                                     [_ptr(g) for g in gfac] if gfac is not None else None,
+                                     ws.data_ptr(), self.ws_bytes, p._stream())
+        return gx, gcore, gfac
 
     def block_bwd(self, x, core, factors, wb, bias, save, grad_y, want_x=True, want_w=True,
                   out=None):

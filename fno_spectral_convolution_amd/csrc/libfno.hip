@@ -789,6 +789,60 @@ fno_status block_bwd_impl(const fno_plan* p, const float* x, const float* wb, co
   return FNO_OK;
 }
 
+// Spectral convolution alone (no bypass, bias or GELU) after argument checks.
+fno_status spectral_fwd_impl(const fno_plan* p, const float* x, float* y_spec, void* save,
+                             void* ws, hipStream_t s, const WeightMix& mix) {
+  float2* xhat = save ? static_cast<float2*>(save) : at<float2>(ws, p->ws.xhat);
+  fno_status st = forward_transform(p, pre_mode(p), p->g.Cin, x, nullptr, xhat, ws, s);
+  if (st != FNO_OK) return st;
+  float2* yhat = at<float2>(ws, p->ws.yhat);
+  st = mix.fwd(xhat, yhat, ws, s);
+  if (st != FNO_OK) return st;
+  const float2* T = nullptr;
+  if (fno::epilogue_rows_ok(p, fno::EPI_SPECTRAL, x, y_spec, nullptr)) {
+    st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T, p->g.d - 2);
+    if (st != FNO_OK) return st;
+    LAUNCH("epilogue_rows_spec_fwd", s, fno::launch_epilogue_rows(p, fno::EPI_SPECTRAL, T, x, nullptr, nullptr, y_spec, nullptr, s));
+    return FNO_OK;
+  }
+  st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T, p->g.d - 1);
+  if (st != FNO_OK) return st;
+  LAUNCH("epilogue_spec_fwd", s, fno::launch_epilogue_fwd(p, fno::EPI_SPECTRAL, T, x, nullptr, nullptr, y_spec, nullptr,
+                                  s));
+  return FNO_OK;
+}
+
+// Its backward: the weight gradients read the retained spectrum (from save, else recomputed).
+fno_status spectral_bwd_impl(const fno_plan* p, const float* x, const void* save,
+                             const float* gys, float* grad_x, void* ws, hipStream_t s,
+                             const WeightMix& mix) {
+  const fno::Geom& g = p->g;
+  float2* ghat = at<float2>(ws, p->ws.yhat);
+  const float2* xhat = static_cast<const float2*>(save);
+  fno_status st;
+  if (mix.wants_weight_grad() && !xhat) {
+    float2* xh = at<float2>(ws, p->ws.xhat);
+    st = forward_transform(p, pre_mode(p), g.Cin, x, nullptr, xh, ws, s);
+    if (st != FNO_OK) return st;
+    xhat = xh;
+  }
+  st = forward_transform(p, fno::PLANE_X, g.Cout, gys, nullptr, ghat, ws, s);
+  if (st != FNO_OK) return st;
+  float2* ghx = grad_x ? at<float2>(ws, p->ws.xhat) : nullptr;
+  if (mix.wants_weight_grad() || ghx) {
+    st = mix.bwd(xhat, ghat, ghx, ws, s);
+    if (st != FNO_OK) return st;
+  }
+  if (grad_x) {
+    const float2* Tg = nullptr;
+    st = inverse_outer(p, g.Cin, ghx, ws, s, &Tg, g.d - 1);
+    if (st != FNO_OK) return st;
+    LAUNCH("epilogue_spec_bwd", s, fno::launch_epilogue_bwd(p, fno::EPI_SPECTRAL, Tg, x, nullptr, nullptr, nullptr,
+                                    grad_x, nullptr, s));
+  }
+  return FNO_OK;
+}
+
 }  // namespace
 
 // A Tucker-factorised weight bound to a plan: the greedy contraction order, the mix geometry
@@ -936,13 +990,14 @@ struct TuckerMix final : WeightMix {
       float2* v = t->in_on_data ? at<float2>(ws, t->v_off) : ghx;
       LAUNCH("tucker_mix_dx", s, fno::launch_mix_bwd_dx_g(t->gmix, t->ident_woff, u, H, v, s));
       if (t->in_on_data) {
-        if (ghx)
-          LAUNCH("tucker_data", s, fno::launch_mix_bwd_dx_g(t->g_in, t->zero_woff, v,
-                                                            f2c(fac[0]), ghx, s));
+        // the U_in gradient reads xhat, so it goes before ghx (which may reuse xhat's slot)
         if (gf(0))
           LAUNCH("tucker_gram_data", s, fno::launch_gram(d.B, d.Cin, d.R[0], t->K, xhat, v, false,
                                                     g.mb, g.Nb, 1.0f, g.inv_gain[1], true,
                                                     part, gf(0), s));
+        if (ghx)
+          LAUNCH("tucker_data", s, fno::launch_mix_bwd_dx_g(t->g_in, t->zero_woff, v,
+                                                            f2c(fac[0]), ghx, s));
       }
     }
     if (!want_w) return FNO_OK;
@@ -997,24 +1052,8 @@ fno_status fno_spectral_conv_fwd(const fno_plan* p, const float* x, const float*
   OPT(save, "save");
   fno_status st = check_ws(p, ws, ws_bytes);
   if (st != FNO_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  float2* xhat = save ? static_cast<float2*>(save) : at<float2>(ws, p->ws.xhat);
-  st = forward_transform(p, pre_mode(p), p->g.Cin, x, nullptr, xhat, ws, s);
-  if (st != FNO_OK) return st;
-  float2* yhat = at<float2>(ws, p->ws.yhat);
-  LAUNCH("mix_fwd", s, fno::launch_mix_fwd(p, xhat, 1, 0, reinterpret_cast<const float2*>(w), yhat, s));
-  const float2* T = nullptr;
-  if (fno::epilogue_rows_ok(p, fno::EPI_SPECTRAL, x, y_spec, nullptr)) {
-    st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T, p->g.d - 2);
-    if (st != FNO_OK) return st;
-    LAUNCH("epilogue_rows_spec_fwd", s, fno::launch_epilogue_rows(p, fno::EPI_SPECTRAL, T, x, nullptr, nullptr, y_spec, nullptr, s));
-    return FNO_OK;
-  }
-  st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T, p->g.d - 1);
-  if (st != FNO_OK) return st;
-  LAUNCH("epilogue_spec_fwd", s, fno::launch_epilogue_fwd(p, fno::EPI_SPECTRAL, T, x, nullptr, nullptr, y_spec, nullptr,
-                                  s));
-  return FNO_OK;
+  return spectral_fwd_impl(p, x, y_spec, save, ws, static_cast<hipStream_t>(stream),
+                           DenseMix(p, w, nullptr));
 }
 
 fno_status fno_block_fwd(const fno_plan* p, const float* x, const float* w, const float* wb,
@@ -1045,34 +1084,8 @@ fno_status fno_spectral_conv_bwd(const fno_plan* p, const float* x, const float*
   OPT(grad_w, "grad_w");
   fno_status st = check_ws(p, ws, ws_bytes);
   if (st != FNO_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const fno::Geom& g = p->g;
-  float2* ghat = at<float2>(ws, p->ws.yhat);
-  if (grad_w) {
-    const float2* xhat = static_cast<const float2*>(save);
-    if (!xhat) {
-      float2* xh = at<float2>(ws, p->ws.xhat);
-      st = forward_transform(p, pre_mode(p), g.Cin, x, nullptr, xh, ws, s);
-      if (st != FNO_OK) return st;
-      xhat = xh;
-    }
-    st = forward_transform(p, fno::PLANE_X, g.Cout, gys, nullptr, ghat, ws, s);
-    if (st != FNO_OK) return st;
-    LAUNCH("mix_bwd_dw", s, fno::launch_mix_bwd_dw(p, xhat, ghat, reinterpret_cast<float2*>(grad_w), s));
-  } else {
-    st = forward_transform(p, fno::PLANE_X, g.Cout, gys, nullptr, ghat, ws, s);
-    if (st != FNO_OK) return st;
-  }
-  if (grad_x) {
-    float2* ghx = at<float2>(ws, p->ws.xhat);
-    LAUNCH("mix_bwd_dx", s, fno::launch_mix_bwd_dx(p, ghat, reinterpret_cast<const float2*>(w), ghx, s));
-    const float2* Tg = nullptr;
-    st = inverse_outer(p, g.Cin, ghx, ws, s, &Tg, g.d - 1);
-    if (st != FNO_OK) return st;
-    LAUNCH("epilogue_spec_bwd", s, fno::launch_epilogue_bwd(p, fno::EPI_SPECTRAL, Tg, x, nullptr, nullptr, nullptr,
-                                    grad_x, nullptr, s));
-  }
-  return FNO_OK;
+  return spectral_bwd_impl(p, x, save, gys, grad_x, ws, static_cast<hipStream_t>(stream),
+                           DenseMix(p, w, grad_w));
 }
 
 fno_status fno_block_bwd(const fno_plan* p, const float* x, const float* w, const float* wb,
@@ -1268,6 +1281,35 @@ fno_status fno_tucker_block_bwd(const fno_tucker* t, const float* x, const float
   return block_bwd_impl(p, x, wb, save, gy, grad_x, grad_wb, grad_bias, ws,
                         static_cast<hipStream_t>(stream),
                         TuckerMix(t, core, factors, grad_core, grad_factors));
+}
+
+fno_status fno_tucker_spectral_conv_fwd(const fno_tucker* t, const float* x, const float* core,
+                                        const float* const* factors, float* y_spec, void* save,
+                                        void* ws, size_t ws_bytes, void* stream) {
+  fno_status st = check_tucker_args(t, core, factors, ws, ws_bytes);
+  if (st != FNO_OK) return st;
+  REQ(x, "x");
+  REQ(y_spec, "y_spec");
+  OPT(save, "save");
+  return spectral_fwd_impl(t->plan, x, y_spec, save, ws, static_cast<hipStream_t>(stream),
+                           TuckerMix(t, core, factors, nullptr, nullptr));
+}
+
+fno_status fno_tucker_spectral_conv_bwd(const fno_tucker* t, const float* x, const float* core,
+                                        const float* const* factors, const void* save,
+                                        const float* gys, float* grad_x, float* grad_core,
+                                        float* const* grad_factors, void* ws, size_t ws_bytes,
+                                        void* stream) {
+  fno_status st = check_tucker_args(t, core, factors, ws, ws_bytes);
+  if (st != FNO_OK) return st;
+  REQ(x, "x");
+  REQ(gys, "grad_y_spec");
+  OPT(save, "save");
+  OPT(grad_x, "grad_x");
+  OPT(grad_core, "grad_core");
+  for (int n = 0; grad_factors && n < t->nf; ++n) OPT(grad_factors[n], "grad_factor");
+  return spectral_bwd_impl(t->plan, x, save, gys, grad_x, ws, static_cast<hipStream_t>(stream),
+                           TuckerMix(t, core, factors, grad_core, grad_factors));
 }
 
 fno_status fno_pointwise_fwd(int64_t batch, int64_t npts, int64_t cin, int64_t hidden,

@@ -201,6 +201,19 @@ fno_status fno_tucker_block_fwd(const fno_tucker* tucker, const float* x, const 
                                 const float* bias, float* y, void* save, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* fno_spectral_conv_fwd / _bwd with the Tucker weight (the spectral convolution alone; save is
+ * optional as there: without it the backward recomputes the spectrum). */
+fno_status fno_tucker_spectral_conv_fwd(const fno_tucker* tucker, const float* x,
+                                        const float* core, const float* const* factors,
+                                        float* y_spec, void* save, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+fno_status fno_tucker_spectral_conv_bwd(const fno_tucker* tucker, const float* x,
+                                        const float* core, const float* const* factors,
+                                        const void* save, const float* grad_y_spec,
+                                        float* grad_x, float* grad_core,
+                                        float* const* grad_factors, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
 /* fno_block_bwd with the Tucker weight: grad_core (the core's layout) and grad_factors (a host
  * array of d + 2 device pointers, each nullable; the array itself may be NULL) replace grad_w.
  * The gradient convention is W's (dL/dRe + i dL/dIm); save is required when FNO_FLAG_GELU is

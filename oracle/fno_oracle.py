@@ -81,7 +81,8 @@ __all__ = [
     "gelu",
     "gelu_prime", "spectral_conv_fwd", "spectral_conv_bwd", "block_fwd", "block_bwd",
     "pointwise_linear", "projection_fwd", "mse_loss_grad", "stack_fwd", "train_step",
-    "mode_product", "tucker_to_full", "tucker_block_fwd", "tucker_block_bwd",
+    "mode_product", "tucker_to_full", "tucker_block_fwd", "tucker_block_bwd", "tucker_grads",
+    "tucker_spectral_conv_fwd", "tucker_spectral_conv_bwd",
 ]
 
 
@@ -457,7 +458,15 @@ def tucker_block_bwd(x, core, factors, wb, bias, modes, g_y, tanh: bool = False,
     factors = [np.asarray(u, dtype=np.complex128) for u in factors]
     w = fold_weights(tucker_to_full(core, factors), modes)
     r = block_bwd(x, w, wb, bias, modes, g_y, tanh=tanh, act=act)
-    gw = expand_weights(r["grad_w"], modes)
+    r["grad_core"], r["grad_factors"] = tucker_grads(core, factors,
+                                                     expand_weights(r["grad_w"], modes))
+    return r
+
+
+def tucker_grads(core, factors, gw):
+    """T2 and T3: the core and factor gradients from the retained-grid weight gradient gw."""
+    core = np.asarray(core, dtype=np.complex128)
+    factors = [np.asarray(u, dtype=np.complex128) for u in factors]
     # T2: every mode contracted with the conjugated factor
     gcore = gw
     for n, u in enumerate(factors):
@@ -471,6 +480,23 @@ def tucker_block_bwd(x, core, factors, wb, bias, modes, g_y, tanh: bool = False,
                 bn = mode_product(bn, u, m)
         axes = [a for a in range(gw.ndim) if a != n]
         gfac.append(np.tensordot(gw, np.conj(bn), axes=(axes, axes)))
-    r["grad_core"] = gcore
-    r["grad_factors"] = gfac
+    return gcore, gfac
+
+
+def tucker_spectral_conv_fwd(x, core, factors, modes, tanh: bool = False):
+    """F1-F3 with T1's Tucker weight."""
+    x = np.asarray(x, dtype=np.float64)
+    _check_tucker_shapes(core, factors, x.shape[1], np.shape(factors[1])[0], modes)
+    return spectral_conv_fwd(x, fold_weights(tucker_to_full(core, factors), modes), modes,
+                             tanh=tanh)
+
+
+def tucker_spectral_conv_bwd(x, core, factors, modes, g_yspec, tanh: bool = False):
+    """The adjoint of tucker_spectral_conv_fwd: grad_x, grad_core, grad_factors (T2 / T3)."""
+    x = np.asarray(x, dtype=np.float64)
+    _check_tucker_shapes(core, factors, x.shape[1], np.shape(factors[1])[0], modes)
+    r = spectral_conv_bwd(x, fold_weights(tucker_to_full(core, factors), modes), modes, g_yspec,
+                          tanh=tanh)
+    r["grad_core"], r["grad_factors"] = tucker_grads(core, factors,
+                                                     expand_weights(r["grad_w"], modes))
     return r

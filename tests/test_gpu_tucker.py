@@ -123,3 +123,36 @@ def test_tucker_partial_outputs_and_determinism(L):
         assert np.array_equal(_host(full[k]), _host(again[k]))
     tk.close()
     plan.close()
+
+
+@pytest.mark.parametrize("use_save", [True, False], ids=["save", "recompute"])
+@pytest.mark.parametrize("prec", PRECISIONS[:2], ids=[p[0] for p in PRECISIONS[:2]])
+@pytest.mark.parametrize("case", CASES[:5], ids=[c[0] for c in CASES[:5]])
+def test_tucker_spectral_conv(L, case, prec, use_save):
+    """The spectral convolution alone with Tucker weights (no bypass to mask its errors), with
+    the spectrum saved by the forward or recomputed by the backward."""
+    name, batch, cin, cout, grid, modes, ranks, _ = case
+    pname, mixed = prec
+    seed = 400 + zlib.crc32(name.encode()) % 1000
+    x, _, _, _ = inputs.small_case(seed, batch, cin, cout, grid, modes)
+    gy = inputs.normal_like(seed, (batch, cout) + grid)
+    core, facs = _tucker_params(seed, cin, cout, modes, ranks)
+    plan = L.Plan(batch, cin, cout, grid, modes, mixed=mixed, gelu=False, bias=False)
+    tk = L.Tucker(plan, ranks)
+    announce("tucker spectral", name, pname, use_save, tk.order)
+    tol = tol_for(mixed)
+    tx, tg, tcore = (_dev(a) for a in (x, gy, core))
+    tfac = [_dev(u) for u in facs]
+    save = plan.new_save() if use_save else None
+    ys = tk.spectral_conv_fwd(tx, tcore, tfac, save=save)
+    gx, gcore, gfac = tk.spectral_conv_bwd(tx, tcore, tfac, tg, save=save)
+    _torch().cuda.synchronize()
+    fwd = O.tucker_spectral_conv_fwd(x, core, facs, modes, tanh=bool(mixed))
+    bwd = O.tucker_spectral_conv_bwd(x, core, facs, modes, gy, tanh=bool(mixed))
+    check("y_spec", _host(ys), fwd["y_spec"], tol)
+    check("grad_x", _host(gx), bwd["grad_x"], tol)
+    check("grad_core", _host(gcore), bwd["grad_core"], tol)
+    for n, want in enumerate(bwd["grad_factors"]):
+        check(f"grad_factor {n}", _host(gfac[n]), want, tol)
+    tk.close()
+    plan.close()
