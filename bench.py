@@ -114,6 +114,10 @@ def kernel_model(wl, plan):
         "epilogue_bwd": (12 * U + T, dft_last + 2 * bypass),
         "epilogue_bwd_gelu": (16 * U + T, dft_last + 2 * bypass),
         "mse": (12 * U, 3 * U),
+        # the last block's forward fused with the loss: x and the target in, grad_z out
+        "epilogue_fwd_mse": (12 * U + T, dft_last + bypass),
+        # the same where the line epilogue does not apply: z and the target in, grad_z out
+        "mse_preact": (12 * U, 3 * U),
     }
     return model
 

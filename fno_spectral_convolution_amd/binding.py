@@ -36,10 +36,10 @@ FNO_FLAG_INPUT_GELU = 8
 EXPORTS = [
     "fno_plan_validate", "fno_plan_create", "fno_plan_destroy", "fno_plan_query",
     "fno_spectral_conv_fwd", "fno_spectral_conv_bwd", "fno_block_fwd", "fno_block_bwd",
-    "fno_pointwise_fwd", "fno_mse_workspace_bytes", "fno_mse_grad", "fno_mse_grad_scaled",
+    "fno_block_fwd_mse", "fno_block_bwd_preact", "fno_pointwise_fwd", "fno_mse_workspace_bytes", "fno_mse_grad", "fno_mse_grad_scaled",
     "fno_tucker_order", "fno_tucker_create", "fno_tucker_destroy", "fno_tucker_query",
     "fno_tucker_block_fwd", "fno_tucker_block_bwd", "fno_tucker_spectral_conv_fwd",
-    "fno_tucker_spectral_conv_bwd",
+    "fno_tucker_spectral_conv_bwd", "fno_tucker_block_fwd_mse", "fno_tucker_block_bwd_preact",
     "fno_timing_enable", "fno_timing_select",
     "fno_timing_reset", "fno_timing_count", "fno_timing_get", "fno_status_string",
     "fno_last_error_message",
@@ -77,6 +77,8 @@ def _load():
         "fno_spectral_conv_bwd": (c_int, [P, P, P, P, P, P, P, P, c_size_t, P]),
         "fno_block_fwd": (c_int, [P, P, P, P, P, P, P, P, c_size_t, P]),
         "fno_block_bwd": (c_int, [P, P, P, P, P, P, P, P, P, P, P, P, c_size_t, P]),
+        "fno_block_fwd_mse": (c_int, [P, P, P, P, P, P, c_float, P, P, P, P, c_size_t, P]),
+        "fno_block_bwd_preact": (c_int, [P, P, P, P, P, P, P, P, P, P, P, P, c_size_t, P]),
         "fno_pointwise_fwd": (c_int, [c_int64, c_int64, c_int64, c_int64, c_int64,
                                       P, P, P, P, P, P, P]),
         "fno_mse_workspace_bytes": (c_int, [c_int64, POINTER(c_size_t)]),
@@ -96,6 +98,10 @@ def _load():
                                                  P]),
         "fno_tucker_spectral_conv_bwd": (c_int, [P, P, P, POINTER(c_void_p), P, P, P, P,
                                                  POINTER(c_void_p), P, c_size_t, P]),
+        "fno_tucker_block_fwd_mse": (c_int, [P, P, P, POINTER(c_void_p), P, P, P, c_float, P,
+                                             P, P, P, c_size_t, P]),
+        "fno_tucker_block_bwd_preact": (c_int, [P, P, P, POINTER(c_void_p), P, P, P, P, P, P,
+                                                POINTER(c_void_p), P, P, P, c_size_t, P]),
         "fno_timing_enable": (c_int, [c_int]),
         "fno_timing_select": (c_int, [c_char_p]),
         "fno_timing_reset": (c_int, []),
@@ -181,6 +187,19 @@ def fno_block_bwd(plan, x, w, w_bypass, bias, save, grad_y, grad_x, grad_w, grad
                   grad_bias, ws, ws_bytes, stream):
     _check(_lib.fno_block_bwd(plan, x, w, w_bypass, bias, save, grad_y, grad_x, grad_w,
                               grad_w_bypass, grad_bias, ws, ws_bytes, stream), "fno_block_bwd")
+
+
+def fno_block_fwd_mse(plan, x, w, w_bypass, bias, target, grad_scale, grad_z, loss, save, ws,
+                      ws_bytes, stream):
+    _check(_lib.fno_block_fwd_mse(plan, x, w, w_bypass, bias, target, grad_scale, grad_z, loss,
+                                  save, ws, ws_bytes, stream), "fno_block_fwd_mse")
+
+
+def fno_block_bwd_preact(plan, x, w, w_bypass, bias, save, grad_z, grad_x, grad_w,
+                         grad_w_bypass, grad_bias, ws, ws_bytes, stream):
+    _check(_lib.fno_block_bwd_preact(plan, x, w, w_bypass, bias, save, grad_z, grad_x, grad_w,
+                                     grad_w_bypass, grad_bias, ws, ws_bytes, stream),
+           "fno_block_bwd_preact")
 
 
 def fno_pointwise_fwd(batch, npts, c_in, hidden, c_out, x, w1, b1, w2, b2, y, stream):
@@ -342,6 +361,34 @@ class Plan:
                       ws.data_ptr(), self.ws_bytes, self._stream())
         return {"x": gx, "w": gw, "wb": gwb, "bias": gb}
 
+    def block_fwd_mse(self, x, w, wb, bias, target, grad_scale=1.0, save=None, grad_z=None,
+                      loss=None):
+        """Block forward fused with the MSE loss; returns (grad_z, loss) (device tensors)."""
+        t = self.torch
+        gz = grad_z if grad_z is not None else self._field(self.c_out)
+        ls = loss if loss is not None else t.empty(1, dtype=t.float32, device=self.device)
+        ws = self.workspace()
+        fno_block_fwd_mse(self.handle, x.data_ptr(), w.data_ptr(), wb.data_ptr(), _ptr(bias),
+                          target.data_ptr(), float(grad_scale), gz.data_ptr(), ls.data_ptr(),
+                          _ptr(save), ws.data_ptr(), self.ws_bytes, self._stream())
+        return gz, ls
+
+    def block_bwd_preact(self, x, w, wb, bias, save, grad_z, want=("x", "w", "wb", "bias"),
+                         out=None):
+        """Block backward from the gradient at the pre-activation (block_bwd's outputs)."""
+        t = self.torch
+        o = dict(out or {})
+        gx = o.get("x", self._field(self.c_in) if "x" in want else None)
+        gw = o.get("w", t.empty_like(w) if "w" in want else None)
+        gwb = o.get("wb", t.empty_like(wb) if "wb" in want else None)
+        gb = o.get("bias", t.empty(self.c_out, dtype=t.float32, device=self.device)
+                   if "bias" in want else None)
+        ws = self.workspace()
+        fno_block_bwd_preact(self.handle, x.data_ptr(), w.data_ptr(), wb.data_ptr(), _ptr(bias),
+                             _ptr(save), grad_z.data_ptr(), _ptr(gx), _ptr(gw), _ptr(gwb),
+                             _ptr(gb), ws.data_ptr(), self.ws_bytes, self._stream())
+        return {"x": gx, "w": gw, "wb": gwb, "bias": gb}
+
 
 def _ranks_arr(ranks):
     return (c_int32 * len(ranks))(*[int(r) for r in ranks])
@@ -390,6 +437,21 @@ def fno_tucker_block_bwd(h, x, core, factors, wb, bias, save, gy, gx, gcore, gfa
     _check(_lib.fno_tucker_block_bwd(h, x, core, _ptr_arr(factors), wb, bias, save, gy, gx,
                                      gcore, gf, gwb, gb, ws, ws_bytes, stream),
            "fno_tucker_block_bwd")
+
+
+def fno_tucker_block_fwd_mse(h, x, core, factors, wb, bias, target, grad_scale, grad_z, loss,
+                             save, ws, ws_bytes, stream):
+    _check(_lib.fno_tucker_block_fwd_mse(h, x, core, _ptr_arr(factors), wb, bias, target,
+                                         grad_scale, grad_z, loss, save, ws, ws_bytes, stream),
+           "fno_tucker_block_fwd_mse")
+
+
+def fno_tucker_block_bwd_preact(h, x, core, factors, wb, bias, save, gz, gx, gcore, gfactors,
+                                gwb, gb, ws, ws_bytes, stream):
+    gf = _ptr_arr(gfactors) if gfactors is not None else None
+    _check(_lib.fno_tucker_block_bwd_preact(h, x, core, _ptr_arr(factors), wb, bias, save, gz,
+                                            gx, gcore, gf, gwb, gb, ws, ws_bytes, stream),
+           "fno_tucker_block_bwd_preact")
 
 
 def fno_tucker_spectral_conv_fwd(h, x, core, factors, y, save, ws, ws_bytes, stream):
@@ -495,6 +557,41 @@ class Tucker:
                              _ptr(save), grad_y.data_ptr(), _ptr(gx), _ptr(gcore),
                              [_ptr(g) for g in gfac] if gfac is not None else None,
                              _ptr(gwb), _ptr(gb), ws.data_ptr(), self.ws_bytes, p._stream())
+        return {"x": gx, "core": gcore, "factors": gfac, "wb": gwb, "bias": gb}
+
+    def block_fwd_mse(self, x, core, factors, wb, bias, target, grad_scale=1.0, save=None,
+                      grad_z=None, loss=None):
+        """block_fwd fused with the MSE loss; returns (grad_z, loss) (device tensors)."""
+        p = self.plan
+        t = p.torch
+        gz = grad_z if grad_z is not None else p._field(p.c_out)
+        ls = loss if loss is not None else t.empty(1, dtype=t.float32, device=p.device)
+        ws = self.workspace()
+        fno_tucker_block_fwd_mse(self.handle, x.data_ptr(), core.data_ptr(),
+                                 [f.data_ptr() for f in factors], wb.data_ptr(), _ptr(bias),
+                                 target.data_ptr(), float(grad_scale), gz.data_ptr(),
+                                 ls.data_ptr(), _ptr(save), ws.data_ptr(), self.ws_bytes,
+                                 p._stream())
+        return gz, ls
+
+    def block_bwd_preact(self, x, core, factors, wb, bias, save, grad_z, want_x=True,
+                         want_w=True, out=None):
+        """block_bwd from the gradient at the pre-activation (block_bwd's outputs)."""
+        p = self.plan
+        t = p.torch
+        o = dict(out or {})
+        gx = o.get("x", p._field(p.c_in) if want_x else None)
+        gcore = o.get("core", t.empty_like(core) if want_w else None)
+        gfac = o.get("factors", [t.empty_like(f) for f in factors] if want_w else None)
+        gwb = o.get("wb", t.empty_like(wb))
+        gb = o.get("bias", t.empty(p.c_out, dtype=t.float32, device=p.device))
+        ws = self.workspace()
+        fno_tucker_block_bwd_preact(self.handle, x.data_ptr(), core.data_ptr(),
+                                    [f.data_ptr() for f in factors], wb.data_ptr(), _ptr(bias),
+                                    _ptr(save), grad_z.data_ptr(), _ptr(gx), _ptr(gcore),
+                                    [_ptr(g) for g in gfac] if gfac is not None else None,
+                                    _ptr(gwb), _ptr(gb), ws.data_ptr(), self.ws_bytes,
+                                    p._stream())
         return {"x": gx, "core": gcore, "factors": gfac, "wb": gwb, "bias": gb}
 
 

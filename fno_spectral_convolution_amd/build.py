@@ -1,14 +1,18 @@
 """Build libfno.so in-tree with hipcc for gfx950.
 
 Usage: python -m fno_spectral_convolution_amd.build   (or call build()).
+Each HIP source compiles to an object of its own (in parallel, up to FNO_BUILD_JOBS or the
+CPU count, at most 8), then one hipcc line links the shared library.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import glob
 import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -17,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfno.so")
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU instructions stay off in every HIP translation unit
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
@@ -35,19 +39,45 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source of libfno into one shared library (always recompiles)."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, "-I", CSRC] + sources() + ["-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(line for line in (res.stdout + res.stderr).splitlines()
                     if "packed-fp32-ops" not in line)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
-    if verbose and out.strip():
-        print(out)
+    return res.returncode, out
+
+
+def _jobs() -> int:
+    env = os.environ.get("FNO_BUILD_JOBS")
+    if env:
+        return max(1, int(env))
+    return max(1, min(8, os.cpu_count() or 1))
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source of libfno into one shared library (always recompiles)."""
+    cc = hipcc()
+    tmp = LIB + ".tmp"
+    with tempfile.TemporaryDirectory(prefix="libfno_build_") as obj_dir:
+        cmds = []
+        for src in sources():
+            obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
+            cmds.append([cc] + HIPCC_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj])
+        with concurrent.futures.ThreadPoolExecutor(max_workers=_jobs()) as pool:
+            results = list(pool.map(_run, cmds))
+        for cmd, (rc, out) in zip(cmds, results):
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            if rc != 0:
+                raise RuntimeError(f"hipcc failed ({rc}) on {cmd[-3]}:\n{out}")
+            if verbose and out.strip():
+                print(out)
+        link = [cc, "--offload-arch=gfx950", "-fPIC", "-shared"] + [c[-1] for c in cmds] + \
+            ["-o", tmp]
+        if verbose:
+            print(" ".join(link), flush=True)
+        rc, out = _run(link)
+        if rc != 0:
+            raise RuntimeError(f"hipcc link failed ({rc}):\n{out}")
     os.replace(tmp, LIB)
     return LIB
 

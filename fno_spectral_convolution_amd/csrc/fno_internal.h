@@ -87,6 +87,7 @@ struct Workspace {
   size_t xhat;         // [B][Cin][K] complex (when the caller gives no save buffer)
   size_t yhat;         // [B][Cout][K] complex
   size_t red_part;     // bypass-gradient partials [nred][Cout*Cin + Cout] float
+  size_t loss_part;    // loss partial sums of the fused forward, [loss_parts] double
   size_t total;
 };
 
@@ -181,7 +182,8 @@ hipError_t launch_gram(int64_t pre, int an, int cn, int64_t post, const float2* 
 hipError_t launch_reduce_parts(const float2* in, int nparts, int64_t part_stride, int64_t n,
                                float2* out, hipStream_t s);
 // Epilogue: last-axis inverse of T [B][C][lines][mb] plus the pointwise part.
-enum EpiMode { EPI_SPECTRAL = 0, EPI_BLOCK = 1 };
+// EPI_BLOCK_PREACT: the block without its output GELU (y receives the pre-activation z).
+enum EpiMode { EPI_SPECTRAL = 0, EPI_BLOCK = 1, EPI_BLOCK_PREACT = 2 };
 hipError_t launch_epilogue_fwd(const fno_plan* p, int mode, const float2* T, const float* x,
                                const float* wb, const float* bias, float* y, float* zsave,
                                hipStream_t s);
@@ -202,6 +204,13 @@ inline bool epilogue_bwd_fast(const fno_plan* p, int mode, const float* grad_x) 
   return grad_x != nullptr && epilogue_fast_ok(p, mode, false);
 }
 int epilogue_bwd_fast_groups(const fno_plan* p);
+// The block's forward epilogue fused with the MSE loss (matrix-core kernel only): writes
+// gz = msc (y - t) GELU'(z) (msc = grad_scale 2 / n; GELU' = 1 without the output GELU) and
+// one partial sum of (y - t)^2 per work-group into lpart (epilogue_fwd_fast_groups of them).
+int epilogue_fwd_fast_groups(const fno_plan* p);
+hipError_t launch_epilogue_fwd_mse(const fno_plan* p, const float2* T, const float* x,
+                                   const float* wb, const float* bias, const float* tgt,
+                                   float msc, float* gz, double* lpart, hipStream_t s);
 hipError_t launch_epilogue_fwd_fast(const fno_plan* p, int mode, const float2* T, const float* x,
                                     const float* wb, const float* bias, float* y, float* zsave,
                                     hipStream_t s);
@@ -222,5 +231,13 @@ hipError_t launch_pointwise(int64_t batch, int64_t npts, int cin, int hidden, in
                             const float* b2, float* y, hipStream_t s);
 hipError_t launch_mse(int64_t n, const float* y, const float* t, float* g, float* loss,
                       float grad_scale, double* part, int nparts, hipStream_t s);
+// In place on gz, which holds z [B][C][P]: y = GELU(z) (or z), gz = sc (y - t) GELU'(z) (or
+// sc (y - t)) with sc = grad_scale 2 / n; partial sums of (y - t)^2 into part[nparts].
+hipError_t launch_mse_preact(int64_t n, const float* t, float* gz, bool gelu, float grad_scale,
+                             double* part, int nparts, hipStream_t s);
+// loss = sum of part[0..nparts) / n, in a fixed order
+hipError_t launch_mse_finish(int64_t n, int nparts, const double* part, float* loss,
+                             hipStream_t s);
+constexpr int kMseParts = 1024;  // work-groups of the stand-alone loss kernels
 
 }  // namespace fno

@@ -421,7 +421,7 @@ hipError_t launch_epilogue_rows(const fno_plan* p, int mode, const float2* T, co
   a.KA = 2 * a.SO;
   a.kpad = p->kpad;
   a.O = (int)g.O;
-  a.gelu = (p->desc.flags & FNO_FLAG_GELU) ? 1 : 0;
+  a.gelu = (mode == EPI_BLOCK && (p->desc.flags & FNO_FLAG_GELU)) ? 1 : 0;
   a.T = T;
   a.x = x;
   a.wb = wb;

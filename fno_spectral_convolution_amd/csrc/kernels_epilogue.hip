@@ -44,6 +44,8 @@ struct EpiArgs {
   const float* gy;     // backward incoming gradient
   const float* zin;    // backward saved z
   float* part;         // backward per-group partials [grid][C*C + C]
+  double* lpart;       // forward with the fused loss: per-group sums of (y - t)^2 [grid]
+  float msc;           // its gradient scale (grad_scale 2 / n); the target is gy
   int block;           // bypass/bias/GELU present (else spectral only)
   int gelu;
 };
@@ -219,7 +221,10 @@ __device__ __forceinline__ void load_rows(float4 (&v)[NPT], const float* base, i
 // tiles are adjacent in the [channel][point] LDS tile.  The z tile goes through LDS and the
 // stores are row-contiguous: 16 G threads write one channel's 64 G points.
 // MODE: 0 spectral part only, 1 block (bypass, bias, optional GELU), 2 block + z save; plus 8
-// when x is a pre-activation (the bypass takes GELU(x), applied as the x tile is staged).
+// when x is a pre-activation (the bypass takes GELU(x), applied as the x tile is staged); plus
+// 16 (with 1) for the fused MSE loss: the target rows of a step are loaded at its start and
+// the store phase writes msc (y - t) GELU'(z) in place of y, and adds (y - t)^2 to a per-thread
+// sum, reduced over the work-group in a fixed order into one partial at the end.
 template <int C, int H, int MODE, int G>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C == 64 ? 3 : 4)))
 k_epi_fwd_line(EpiArgs a) {
@@ -236,9 +241,12 @@ k_epi_fwd_line(EpiArgs a) {
   constexpr bool BLK = (MODE & 3) >= 1;
   constexpr bool ZS = (MODE & 3) == 2;
   constexpr bool IG = (MODE & 8) != 0;
+  constexpr bool MS = (MODE & 16) != 0;
   static_assert(G == 1 || G == 2, "LDS runs of 1 or 2 floats");
+  static_assert(!MS || (MODE & 3) == 1, "the fused loss replaces y and takes no z save");
   __shared__ __attribute__((aligned(16))) float s_x[BLK ? CP * XSG : 4];
   __shared__ __attribute__((aligned(16))) float s_o[CP * XSG];
+  __shared__ double s_loss[MS ? 4 : 1];
   __shared__ __attribute__((aligned(16))) unsigned char s_tl[CP * (kMaxKpad + 8) * (BF ? 2 : 4)];
   __shared__ float s_bias[CP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -280,6 +288,9 @@ k_epi_fwd_line(EpiArgs a) {
   float4 pre[NPT];
 #pragma unroll
   for (int u = 0; u < NPT; ++u) pre[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+  // fused loss: target rows of the current step; the copies past the tile add nothing
+  float4 ptg[MS ? NPT : 1];
+  double lsum = 0.0;
   GtFrag<G, H> gtf;
   if (BLK) {
 #pragma unroll
@@ -315,6 +326,13 @@ k_epi_fwd_line(EpiArgs a) {
             xv.w = gelu_as(xv.w);
           }
           *reinterpret_cast<float4*>(s_x + xl[u]) = xv;
+        }
+        // this step's target rows go out before the next step's x rows: the store phase
+        // waits only for them
+        if constexpr (MS) {
+#pragma unroll
+          for (int u = 0; u < NPT; ++u)
+            ptg[u] = *reinterpret_cast<const float4*>(a.gy + goff[u] + PI * f);
         }
 #pragma unroll
         for (int u = 0; u < NPT; ++u)
@@ -388,6 +406,27 @@ k_epi_fwd_line(EpiArgs a) {
       for (int u = 0; u < NPT; ++u) {
         float4 v = *reinterpret_cast<const float4*>(s_o + ol[u]);
         const int64_t off = goff[u] + PI * f;
+        if constexpr (MS) {
+          float4 yv = v, gp = make_float4(1.f, 1.f, 1.f, 1.f);
+          if (a.gelu) {
+            gelu_and_grad(v.x, yv.x, gp.x);
+            gelu_and_grad(v.y, yv.y, gp.y);
+            gelu_and_grad(v.z, yv.z, gp.z);
+            gelu_and_grad(v.w, yv.w, gp.w);
+          }
+          const float4 d = make_float4(yv.x - ptg[u].x, yv.y - ptg[u].y, yv.z - ptg[u].z,
+                                       yv.w - ptg[u].w);
+          const double sq = (double)(d.x * d.x + d.y * d.y) + (double)(d.z * d.z + d.w * d.w);
+          if constexpr (256 * NPT == NF4) {
+            lsum += sq;
+          } else {
+            lsum += (tid + 256 * u < NF4) ? sq : 0.0;
+          }
+          *reinterpret_cast<float4*>(a.y + off) =
+              make_float4(a.msc * d.x * gp.x, a.msc * d.y * gp.y, a.msc * d.z * gp.z,
+                          a.msc * d.w * gp.w);
+          continue;
+        }
         if (ZS) *reinterpret_cast<float4*>(a.z + off) = v;
         if (BLK && a.gelu) {
           v.x = gelu_as(v.x);
@@ -398,6 +437,14 @@ k_epi_fwd_line(EpiArgs a) {
         *reinterpret_cast<float4*>(a.y + off) = v;
       }
     }
+  }
+  if constexpr (MS) {
+    // fixed order: xor butterflies within each wave, then the four waves in turn
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
+    if (lane == 0) s_loss[wave] = lsum;
+    __syncthreads();
+    if (tid == 0) a.lpart[blockIdx.x] = ((s_loss[0] + s_loss[1]) + s_loss[2]) + s_loss[3];
   }
 }
 
@@ -697,7 +744,9 @@ static hipError_t launch_fwd_c(const EpiArgs& a, int half, int mode, int wgs, hi
     else if (mode == 1) FNO_EPI_FWD(HV, 1);   \
     else if (mode == 2) FNO_EPI_FWD(HV, 2);   \
     else if (mode == 9) FNO_EPI_FWD(HV, 9);   \
-    else FNO_EPI_FWD(HV, 10);                 \
+    else if (mode == 10) FNO_EPI_FWD(HV, 10); \
+    else if (mode == 17) FNO_EPI_FWD(HV, 17); \
+    else FNO_EPI_FWD(HV, 25);                 \
   } while (0)
   if (half == 2) FNO_EPI_FWD_M(2);
   else if (half == 1) FNO_EPI_FWD_M(1);
@@ -739,7 +788,7 @@ static hipError_t launch_bwd_c(const EpiArgs& a, int half, bool tanh_pre, int mo
 bool epilogue_fast_ok(const fno_plan* p, int mode, bool fwd) {
   const Geom& g = p->g;
   const int C = fwd ? g.Cout : g.Cin;
-  if (mode == EPI_BLOCK && g.Cin != g.Cout) return false;
+  if (mode != EPI_SPECTRAL && g.Cin != g.Cout) return false;
   if (!(C == 16 || C == 20 || C == 32 || C == 64)) return false;
   if (g.Nb % 64 != 0 || g.mb % 2 != 0 || p->kpad > kMaxKpad) return false;
   const int gpl = g.Nb / 64;  // point groups per line: a power of two (shift / mask indexing)
@@ -757,9 +806,8 @@ static int fwd_lines_per_wg(int64_t lines, int64_t batch) {
   return lpw;
 }
 
-hipError_t launch_epilogue_fwd_fast(const fno_plan* p, int mode, const float2* T, const float* x,
-                                    const float* wb, const float* bias, float* y, float* zsave,
-                                    hipStream_t s) {
+// Arguments of the forward line kernel; kmode bits as the kernel's MODE (without its width).
+static EpiArgs fwd_args(const fno_plan* p, int* G, int64_t* wgs) {
   const Geom& g = p->g;
   EpiArgs a{};
   a.B = g.B;
@@ -771,22 +819,18 @@ hipError_t launch_epilogue_fwd_fast(const fno_plan* p, int mode, const float2* T
   a.lines = g.P / g.Nb;
   a.lpw = fwd_lines_per_wg(a.lines, g.B);
   // narrow fields take two 64-point groups per step when a line holds them
-  const int G = (g.Cout <= 32 && g.Nb >= 2 * PG) ? 2 : 1;
+  *G = (g.Cout <= 32 && g.Nb >= 2 * PG) ? 2 : 1;
   int gl = 0;
-  while ((PG * G << gl) < g.Nb) ++gl;
+  while ((PG * *G << gl) < g.Nb) ++gl;
   a.gpl_log2 = gl;
-  a.x = x;
-  a.T = T;
-  a.wb = wb;
-  a.bias = (p->desc.flags & FNO_FLAG_BIAS) ? bias : nullptr;
   a.gt = g.bf16 ? (const void*)p->t.gt_fwd_bf : (const void*)p->t.gt_fwd;
-  a.y = y;
-  a.z = zsave;
-  a.gelu = (p->desc.flags & FNO_FLAG_GELU) != 0;
-  const bool ig = (p->desc.flags & FNO_FLAG_INPUT_GELU) != 0;
-  const int kmode = mode != EPI_BLOCK ? 0 : ((zsave ? 2 : 1) | (ig ? 8 : 0));
-  a.block = kmode != 0;
-  const int64_t wgs = (int64_t)g.B * a.lines / a.lpw;
+  *wgs = (int64_t)g.B * a.lines / a.lpw;
+  return a;
+}
+
+static hipError_t launch_fwd_any(const fno_plan* p, const EpiArgs& a, int G, int kmode,
+                                 int64_t wgs, hipStream_t s) {
+  const Geom& g = p->g;
   if (wgs > 0x7fffffff) return hipErrorInvalidValue;
   if (G == 2) {
     switch (g.Cout) {
@@ -801,6 +845,54 @@ hipError_t launch_epilogue_fwd_fast(const fno_plan* p, int mode, const float2* T
     case 32: return launch_fwd_c<32, 1>(a, g.half, kmode, (int)wgs, s);
     default: return launch_fwd_c<64, 1>(a, g.half, kmode, (int)wgs, s);
   }
+}
+
+int epilogue_fwd_fast_groups(const fno_plan* p) {
+  if (!epilogue_fast_ok(p, EPI_BLOCK, true)) return 0;
+  int G = 1;
+  int64_t wgs = 0;
+  (void)fwd_args(p, &G, &wgs);
+  return wgs > 0x7fffffff ? 0 : (int)wgs;
+}
+
+hipError_t launch_epilogue_fwd_fast(const fno_plan* p, int mode, const float2* T, const float* x,
+                                    const float* wb, const float* bias, float* y, float* zsave,
+                                    hipStream_t s) {
+  int G = 1;
+  int64_t wgs = 0;
+  EpiArgs a = fwd_args(p, &G, &wgs);
+  a.x = x;
+  a.T = T;
+  a.wb = wb;
+  a.bias = (p->desc.flags & FNO_FLAG_BIAS) ? bias : nullptr;
+  a.y = y;
+  a.z = zsave;
+  a.gelu = mode == EPI_BLOCK && (p->desc.flags & FNO_FLAG_GELU) != 0;
+  const bool ig = (p->desc.flags & FNO_FLAG_INPUT_GELU) != 0;
+  const int kmode = mode == EPI_SPECTRAL ? 0 : ((zsave ? 2 : 1) | (ig ? 8 : 0));
+  a.block = kmode != 0;
+  return launch_fwd_any(p, a, G, kmode, wgs, s);
+}
+
+hipError_t launch_epilogue_fwd_mse(const fno_plan* p, const float2* T, const float* x,
+                                   const float* wb, const float* bias, const float* tgt,
+                                   float msc, float* gz, double* lpart, hipStream_t s) {
+  int G = 1;
+  int64_t wgs = 0;
+  EpiArgs a = fwd_args(p, &G, &wgs);
+  a.x = x;
+  a.T = T;
+  a.wb = wb;
+  a.bias = (p->desc.flags & FNO_FLAG_BIAS) ? bias : nullptr;
+  a.y = gz;
+  a.gy = tgt;
+  a.msc = msc;
+  a.lpart = lpart;
+  a.gelu = (p->desc.flags & FNO_FLAG_GELU) != 0;
+  const bool ig = (p->desc.flags & FNO_FLAG_INPUT_GELU) != 0;
+  const int kmode = 1 | 16 | (ig ? 8 : 0);
+  a.block = 1;
+  return launch_fwd_any(p, a, G, kmode, wgs, s);
 }
 
 // Lines per backward work-group: each work-group writes one row of bypass-gradient partials,

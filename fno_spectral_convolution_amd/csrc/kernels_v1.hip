@@ -336,11 +336,12 @@ hipError_t launch_epilogue_fwd(const fno_plan* p, int mode, const float2* T, con
   if (epilogue_fast_ok(p, mode, true))
     return launch_epilogue_fwd_fast(p, mode, T, x, wb, bias, y, zsave, s);
   const Geom& g = p->g;
+  const bool gelu = mode == EPI_BLOCK && (p->desc.flags & FNO_FLAG_GELU) != 0;
+  if (mode == EPI_BLOCK_PREACT) mode = EPI_BLOCK;  // the same kernel, without the GELU
   const size_t lds = sizeof(float2) * g.Nb +
                      sizeof(float) * ((size_t)g.Cout * g.Cin + g.Cout +
                                       (mode == EPI_BLOCK ? (size_t)g.Cin * kEpiThreads : 0));
   dim3 grid((unsigned)((g.P + kEpiThreads - 1) / kEpiThreads), (unsigned)g.B);
-  const bool gelu = (p->desc.flags & FNO_FLAG_GELU) != 0;
   const bool ig = (p->desc.flags & FNO_FLAG_INPUT_GELU) != 0;
   const float2* rb = g.bf16 ? p->t.root_bf[g.d - 1] : p->t.root[g.d - 1];
   hipLaunchKernelGGL(k_epilogue_fwd, grid, dim3(kEpiThreads), lds, s, g, mode, gelu, ig, rb, T, x,
@@ -476,7 +477,7 @@ hipError_t launch_epilogue_bwd(const fno_plan* p, int mode, const float2* Tg, co
                      sizeof(float) * ((size_t)g.Cout * g.Cin +
                                       (mode == EPI_BLOCK ? (size_t)(g.Cout + g.Cin) * kEbThreads
                                                          : 0));
-  const bool gelu = (p->desc.flags & FNO_FLAG_GELU) != 0;
+  const bool gelu = z != nullptr;  // the caller passes z exactly when GELU' applies
   const bool tanh_pre = (p->desc.flags & FNO_FLAG_TANH_PREACT) != 0;
   const bool ig = (p->desc.flags & FNO_FLAG_INPUT_GELU) != 0;
   const float2* rb = g.bf16 ? p->t.root_bf[g.d - 1] : p->t.root[g.d - 1];
@@ -582,6 +583,47 @@ hipError_t launch_mse(int64_t n, const float* y, const float* t, float* g, float
   hipLaunchKernelGGL(k_mse_part, dim3(nparts), dim3(256), 0, s, n, y, t, g, grad_scale, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !loss) return e;
+  hipLaunchKernelGGL(k_mse_finish, dim3(1), dim3(256), 0, s, n, nparts, part, loss);
+  return hipGetLastError();
+}
+
+// The loss through the output GELU: gz holds z on entry; y = GELU(z) (or z), and
+// gz = sc (y - t) GELU'(z) on exit, the gradient of grad_scale * mean((y - t)^2) at z.
+__global__ void k_mse_preact_part(int64_t n, const float* __restrict__ t, float* __restrict__ gz,
+                                  bool gelu, float grad_scale, double* __restrict__ part) {
+  __shared__ double s_red[256];
+  const int tid = threadIdx.x;
+  const float sc = (float)(2.0 * (double)grad_scale / (double)n);
+  double a = 0.0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + tid; i < n; i += (int64_t)gridDim.x * 256) {
+    const float z = gz[i];
+    float y = z, gp = 1.f;
+    if (gelu) {
+      y = gelu_f(z);
+      gp = gelu_grad_f(z);
+    }
+    const float d = y - t[i];
+    gz[i] = sc * d * gp;
+    a += (double)d * (double)d;
+  }
+  s_red[tid] = a;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) s_red[tid] += s_red[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) part[blockIdx.x] = s_red[0];
+}
+
+hipError_t launch_mse_preact(int64_t n, const float* t, float* gz, bool gelu, float grad_scale,
+                             double* part, int nparts, hipStream_t s) {
+  hipLaunchKernelGGL(k_mse_preact_part, dim3(nparts), dim3(256), 0, s, n, t, gz, gelu,
+                     grad_scale, part);
+  return hipGetLastError();
+}
+
+hipError_t launch_mse_finish(int64_t n, int nparts, const double* part, float* loss,
+                             hipStream_t s) {
   hipLaunchKernelGGL(k_mse_finish, dim3(1), dim3(256), 0, s, n, nparts, part, loss);
   return hipGetLastError();
 }

@@ -263,6 +263,11 @@ fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out) {
     const int nparts = nfast > p->nred ? nfast : p->nred;
     off += align_up(sizeof(float) * (size_t)nparts * (g.Cout * g.Cin + g.Cout));
   }
+  w.loss_part = off;
+  {
+    const int nfast = fno::epilogue_fwd_fast_groups(p);
+    off += align_up(sizeof(double) * (size_t)(nfast > fno::kMseParts ? nfast : fno::kMseParts));
+  }
   w.total = off;
   p->save_off_z = align_up(sizeof(float2) * (size_t)g.B * g.Cin * g.K);
   p->save_bytes = p->save_off_z +
@@ -730,6 +735,28 @@ struct DenseMix final : WeightMix {
   bool wants_weight_grad() const override { return grad_w != nullptr; }
 };
 
+// The inverse of the outer axes and the forward epilogue of a block (mode EPI_BLOCK, or
+// EPI_BLOCK_PREACT for z without the output GELU) from the mixed spectrum yhat.
+fno_status block_epilogue_fwd(const fno_plan* p, int mode, const float2* yhat, const float* x,
+                              const float* wb, const float* bias, float* y, float* zsave,
+                              void* ws, hipStream_t s) {
+  const float2* T = nullptr;
+  fno_status st;
+  if (fno::epilogue_rows_ok(p, mode, x, y, zsave)) {
+    st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T, p->g.d - 2);
+    if (st != FNO_OK) return st;
+    // timer names tell launches that also save z apart (their bytes differ)
+    LAUNCH(zsave ? "epilogue_rows_fwd_zsave" : "epilogue_rows_fwd", s,
+           fno::launch_epilogue_rows(p, mode, T, x, wb, bias, y, zsave, s));
+    return FNO_OK;
+  }
+  st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T, p->g.d - 1);
+  if (st != FNO_OK) return st;
+  LAUNCH(zsave ? "epilogue_fwd_zsave" : "epilogue_fwd", s,
+         fno::launch_epilogue_fwd(p, mode, T, x, wb, bias, y, zsave, s));
+  return FNO_OK;
+}
+
 // Block forward after argument checks: transform, weight step, inverse + epilogue.
 fno_status block_fwd_impl(const fno_plan* p, const float* x, const float* wb, const float* bias,
                           float* y, void* save, void* ws, hipStream_t s, const WeightMix& mix) {
@@ -739,30 +766,55 @@ fno_status block_fwd_impl(const fno_plan* p, const float* x, const float* wb, co
   float2* yhat = at<float2>(ws, p->ws.yhat);
   st = mix.fwd(xhat, yhat, ws, s);
   if (st != FNO_OK) return st;
-  const float2* T = nullptr;
   float* zsave = (save && (p->desc.flags & FNO_FLAG_GELU)) ? at<float>(save, p->save_off_z)
                                                             : nullptr;
-  if (fno::epilogue_rows_ok(p, fno::EPI_BLOCK, x, y, zsave)) {
-    st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T, p->g.d - 2);
-    if (st != FNO_OK) return st;
-    // timer names tell launches that also save z apart (their bytes differ)
-    LAUNCH(zsave ? "epilogue_rows_fwd_zsave" : "epilogue_rows_fwd", s,
-           fno::launch_epilogue_rows(p, fno::EPI_BLOCK, T, x, wb, bias, y, zsave, s));
-    return FNO_OK;
-  }
-  st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T, p->g.d - 1);
+  return block_epilogue_fwd(p, fno::EPI_BLOCK, yhat, x, wb, bias, y, zsave, ws, s);
+}
+
+// Block forward fused with the MSE loss against `tgt`: grad_z = grad_scale 2 (y - t) / n
+// GELU'(z) and, when `loss` is given, loss = mean((y - t)^2).  The matrix-core epilogue does
+// it in one pass over the field; the other epilogues write z into grad_z and a pointwise pass
+// turns it into the gradient in place.
+fno_status block_fwd_mse_impl(const fno_plan* p, const float* x, const float* wb,
+                              const float* bias, const float* tgt, float grad_scale,
+                              float* grad_z, float* loss, void* save, void* ws, hipStream_t s,
+                              const WeightMix& mix) {
+  const fno::Geom& g = p->g;
+  float2* xhat = save ? static_cast<float2*>(save) : at<float2>(ws, p->ws.xhat);
+  fno_status st = forward_transform(p, pre_mode(p), g.Cin, x, nullptr, xhat, ws, s);
   if (st != FNO_OK) return st;
-  LAUNCH(zsave ? "epilogue_fwd_zsave" : "epilogue_fwd", s,
-         fno::launch_epilogue_fwd(p, fno::EPI_BLOCK, T, x, wb, bias, y, zsave, s));
+  float2* yhat = at<float2>(ws, p->ws.yhat);
+  st = mix.fwd(xhat, yhat, ws, s);
+  if (st != FNO_OK) return st;
+  const int64_t n = (int64_t)g.B * g.Cout * g.P;
+  double* lpart = at<double>(ws, p->ws.loss_part);
+  int nparts = fno::kMseParts;
+  if (fno::epilogue_fast_ok(p, fno::EPI_BLOCK, true)) {
+    const float2* T = nullptr;
+    st = inverse_outer(p, g.Cout, yhat, ws, s, &T, g.d - 1);
+    if (st != FNO_OK) return st;
+    const float msc = (float)(2.0 * (double)grad_scale / (double)n);
+    LAUNCH("epilogue_fwd_mse", s,
+           fno::launch_epilogue_fwd_mse(p, T, x, wb, bias, tgt, msc, grad_z, lpart, s));
+    nparts = fno::epilogue_fwd_fast_groups(p);
+  } else {
+    st = block_epilogue_fwd(p, fno::EPI_BLOCK_PREACT, yhat, x, wb, bias, grad_z, nullptr, ws, s);
+    if (st != FNO_OK) return st;
+    const bool gelu = (p->desc.flags & FNO_FLAG_GELU) != 0;
+    LAUNCH("mse_preact", s,
+           fno::launch_mse_preact(n, tgt, grad_z, gelu, grad_scale, lpart, nparts, s));
+  }
+  if (loss) LAUNCH("mse_finish", s, fno::launch_mse_finish(n, nparts, lpart, loss, s));
   return FNO_OK;
 }
 
-// Block backward after argument checks.
+// Block backward after argument checks.  With `preact`, gy is the gradient at the
+// pre-activation z (the output GELU's derivative already applied) and z is not read.
 fno_status block_bwd_impl(const fno_plan* p, const float* x, const float* wb, const void* save,
                           const float* gy, float* grad_x, float* grad_wb, float* grad_bias,
-                          void* ws, hipStream_t s, const WeightMix& mix) {
+                          void* ws, hipStream_t s, const WeightMix& mix, bool preact = false) {
   const fno::Geom& g = p->g;
-  const bool gelu = (p->desc.flags & FNO_FLAG_GELU) != 0;
+  const bool gelu = (p->desc.flags & FNO_FLAG_GELU) != 0 && !preact;
   const float* z = gelu ? at<const float>(const_cast<void*>(save), p->save_off_z) : nullptr;
   float2* ghat = at<float2>(ws, p->ws.yhat);
   fno_status st = forward_transform(p, gelu ? fno::PLANE_GELU_GRAD : fno::PLANE_X, g.Cout, gy,
@@ -1111,6 +1163,50 @@ fno_status fno_block_bwd(const fno_plan* p, const float* x, const float* w, cons
                         static_cast<hipStream_t>(stream), DenseMix(p, w, grad_w));
 }
 
+fno_status fno_block_fwd_mse(const fno_plan* p, const float* x, const float* w, const float* wb,
+                             const float* bias, const float* target, float grad_scale,
+                             float* grad_z, float* loss, void* save, void* ws, size_t ws_bytes,
+                             void* stream) {
+  if (!p) return fail(FNO_ERR_INVALID_ARGUMENT, "plan is NULL");
+  REQ(x, "x");
+  REQ(w, "w");
+  REQ(wb, "w_bypass");
+  if (p->desc.flags & FNO_FLAG_BIAS) REQ(bias, "bias");
+  REQ(target, "target");
+  REQ(grad_z, "grad_z");
+  OPT(loss, "loss");
+  OPT(save, "save");
+  if (!(grad_scale > 0.0f) || !std::isfinite(grad_scale))
+    return fail(FNO_ERR_INVALID_ARGUMENT, "grad_scale must be finite and > 0");
+  fno_status st = check_ws(p, ws, ws_bytes);
+  if (st != FNO_OK) return st;
+  return block_fwd_mse_impl(p, x, wb, bias, target, grad_scale, grad_z, loss, save, ws,
+                            static_cast<hipStream_t>(stream), DenseMix(p, w, nullptr));
+}
+
+fno_status fno_block_bwd_preact(const fno_plan* p, const float* x, const float* w,
+                                const float* wb, const float* bias, const void* save,
+                                const float* grad_z, float* grad_x, float* grad_w,
+                                float* grad_wb, float* grad_bias, void* ws, size_t ws_bytes,
+                                void* stream) {
+  (void)bias;
+  if (!p) return fail(FNO_ERR_INVALID_ARGUMENT, "plan is NULL");
+  REQ(x, "x");
+  REQ(w, "w");
+  REQ(wb, "w_bypass");
+  REQ(grad_z, "grad_z");
+  if (grad_w) REQ(save, "save");
+  OPT(save, "save");
+  OPT(grad_x, "grad_x");
+  OPT(grad_w, "grad_w");
+  OPT(grad_wb, "grad_w_bypass");
+  OPT(grad_bias, "grad_bias");
+  fno_status st = check_ws(p, ws, ws_bytes);
+  if (st != FNO_OK) return st;
+  return block_bwd_impl(p, x, wb, save, grad_z, grad_x, grad_wb, grad_bias, ws,
+                        static_cast<hipStream_t>(stream), DenseMix(p, w, grad_w), true);
+}
+
 fno_status fno_tucker_order(const fno_plan_desc* desc, const int32_t* ranks, char* buf,
                             size_t len) {
   fno::TuckerDims d;
@@ -1283,6 +1379,58 @@ fno_status fno_tucker_block_bwd(const fno_tucker* t, const float* x, const float
                         TuckerMix(t, core, factors, grad_core, grad_factors));
 }
 
+fno_status fno_tucker_block_fwd_mse(const fno_tucker* t, const float* x, const float* core,
+                                    const float* const* factors, const float* wb,
+                                    const float* bias, const float* target, float grad_scale,
+                                    float* grad_z, float* loss, void* save, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  fno_status st = check_tucker_args(t, core, factors, ws, ws_bytes);
+  if (st != FNO_OK) return st;
+  const fno_plan* p = t->plan;
+  REQ(x, "x");
+  REQ(wb, "w_bypass");
+  if (p->desc.flags & FNO_FLAG_BIAS) REQ(bias, "bias");
+  REQ(target, "target");
+  REQ(grad_z, "grad_z");
+  OPT(loss, "loss");
+  OPT(save, "save");
+  if (!(grad_scale > 0.0f) || !std::isfinite(grad_scale))
+    return fail(FNO_ERR_INVALID_ARGUMENT, "grad_scale must be finite and > 0");
+  return block_fwd_mse_impl(p, x, wb, bias, target, grad_scale, grad_z, loss, save, ws,
+                            static_cast<hipStream_t>(stream),
+                            TuckerMix(t, core, factors, nullptr, nullptr));
+}
+
+fno_status fno_tucker_block_bwd_preact(const fno_tucker* t, const float* x, const float* core,
+                                       const float* const* factors, const float* wb,
+                                       const float* bias, const void* save,
+                                       const float* grad_z, float* grad_x, float* grad_core,
+                                       float* const* grad_factors, float* grad_wb,
+                                       float* grad_bias, void* ws, size_t ws_bytes,
+                                       void* stream) {
+  (void)bias;
+  fno_status st = check_tucker_args(t, core, factors, ws, ws_bytes);
+  if (st != FNO_OK) return st;
+  const fno_plan* p = t->plan;
+  REQ(x, "x");
+  REQ(wb, "w_bypass");
+  REQ(grad_z, "grad_z");
+  OPT(grad_x, "grad_x");
+  OPT(grad_core, "grad_core");
+  OPT(grad_wb, "grad_w_bypass");
+  OPT(grad_bias, "grad_bias");
+  bool want_w = grad_core != nullptr;
+  for (int n = 0; grad_factors && n < t->nf; ++n) {
+    OPT(grad_factors[n], "grad_factor");
+    want_w = want_w || grad_factors[n] != nullptr;
+  }
+  if (want_w) REQ(save, "save");
+  OPT(save, "save");
+  return block_bwd_impl(p, x, wb, save, grad_z, grad_x, grad_wb, grad_bias, ws,
+                        static_cast<hipStream_t>(stream),
+                        TuckerMix(t, core, factors, grad_core, grad_factors), true);
+}
+
 fno_status fno_tucker_spectral_conv_fwd(const fno_tucker* t, const float* x, const float* core,
                                         const float* const* factors, float* y_spec, void* save,
                                         void* ws, size_t ws_bytes, void* stream) {
@@ -1333,7 +1481,7 @@ fno_status fno_pointwise_fwd(int64_t batch, int64_t npts, int64_t cin, int64_t h
 
 static int mse_parts(int64_t n) {
   int64_t g = (n + 255) / 256;
-  return (int)(g < 1024 ? (g < 1 ? 1 : g) : 1024);
+  return (int)(g < fno::kMseParts ? (g < 1 ? 1 : g) : fno::kMseParts);
 }
 
 fno_status fno_mse_workspace_bytes(int64_t n, size_t* bytes) {

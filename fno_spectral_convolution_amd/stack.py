@@ -53,7 +53,13 @@ class PrecisionSchedule:
 
 
 class StackRunner:
-    def __init__(self, wl, device="cuda", host_inputs=None):
+    """fuse_loss (training stacks without a projection head): the last block's forward
+    computes the loss and the gradient at its pre-activation in one pass (fno_block_fwd_mse)
+    and its backward starts from that gradient (fno_block_bwd_preact), so the output field y
+    is never written; step() then returns None.  With fuse_loss=False the step writes y and
+    runs the stand-alone loss kernel between the two passes."""
+
+    def __init__(self, wl, device="cuda", host_inputs=None, fuse_loss=True):
         import torch
         self.torch = torch
         self.wl = wl
@@ -88,6 +94,7 @@ class StackRunner:
                        "proj": {k: to(v) for k, v in lp["proj"].items()}}
         shape = (wl.batch, C) + tuple(wl.grid)
         nb = wl.blocks
+        self.fuse_loss = bool(fuse_loss and wl.train and self.lp is None)
         if wl.train:
             self.acts = [torch.empty(shape, dtype=torch.float32, device=dev)
                          for _ in range(nb + 1)]
@@ -178,7 +185,8 @@ class StackRunner:
         return self.acts[i] if self.wl.train else self.acts[i % 2]
 
     def step(self):
-        """One pass of the workload; returns the output field (and enqueues the backward)."""
+        """One pass of the workload; returns the output field (None when the loss is fused
+        into the last block) and enqueues the backward of a training workload."""
         wl = self.wl
         if self.lp is not None:
             lift = self.lp["lift"]
@@ -187,8 +195,21 @@ class StackRunner:
         else:
             src0 = self.x_in
         h = src0
+        nb = len(self.params)
         for i, p in enumerate(self.params):
             dst = self._act(i + 1)
+            if self.fuse_loss and i == nb - 1:
+                # loss and the gradient at the last pre-activation, into g[0]; y is not stored
+                if self.tucker:
+                    self.block_tuckers[i].block_fwd_mse(
+                        h, p["core"], p["factors"], p["wb"], p["bias"], self.target,
+                        self.grad_scale, save=self.saves[i], grad_z=self.g[0], loss=self.loss)
+                else:
+                    self.block_plans[i].block_fwd_mse(
+                        h, p["w"], p["wb"], p["bias"], self.target, self.grad_scale,
+                        save=self.saves[i], grad_z=self.g[0], loss=self.loss)
+                h = None
+                break
             if self.tucker:
                 self.block_tuckers[i].block_fwd(h, p["core"], p["factors"], p["wb"], p["bias"],
                                                 save=self.saves[i], out=dst)
@@ -201,14 +222,24 @@ class StackRunner:
             L.pointwise(h, pr["w1"], pr["b1"], pr["w2"], pr["b2"], out=self.out)
             h = self.out
         if wl.train:
-            L.mse_grad(h, self.target, grad=self.g[0], loss=self.loss, ws=self.mse_ws,
-                       grad_scale=self.grad_scale)
+            if not self.fuse_loss:
+                L.mse_grad(h, self.target, grad=self.g[0], loss=self.loss, ws=self.mse_ws,
+                           grad_scale=self.grad_scale)
             gin = 0
             for i in reversed(range(len(self.params))):
                 p = self.params[i]
                 x_i = src0 if i == 0 else self.acts[i]
                 gout = 1 - gin
-                if self.tucker:
+                if self.fuse_loss and i == nb - 1:
+                    if self.tucker:
+                        self.block_tuckers[i].block_bwd_preact(
+                            x_i, p["core"], p["factors"], p["wb"], p["bias"], self.saves[i],
+                            self.g[gin], out={"x": self.g[gout], **self.grads[i]})
+                    else:
+                        self.block_plans[i].block_bwd_preact(
+                            x_i, p["w"], p["wb"], p["bias"], self.saves[i], self.g[gin],
+                            out={"x": self.g[gout], **self.grads[i]})
+                elif self.tucker:
                     self.block_tuckers[i].block_bwd(x_i, p["core"], p["factors"], p["wb"],
                                                     p["bias"], self.saves[i], self.g[gin],
                                                     out={"x": self.g[gout], **self.grads[i]})

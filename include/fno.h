@@ -155,6 +155,32 @@ fno_status fno_block_bwd(const fno_plan* plan, const float* x, const float* w,
                          float* grad_w_bypass, float* grad_bias, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* The last block of a training step fused with the mean-squared-error loss against `target`
+ * (same shape as y): with z = y_spec + Wb x + bias and y = GELU(z) (y = z without
+ * FNO_FLAG_GELU), writes
+ *   grad_z = grad_scale * 2 (y - target) / n * GELU'(z)   (n = batch * C_out * prod N),
+ * the gradient of grad_scale * mean((y - target)^2) with respect to z, and, when `loss` (a
+ * device float) is non-NULL, loss = mean((y - target)^2) (unscaled; fixed-order reduction).
+ * y itself is not written.  It equals fno_block_fwd, then fno_mse_grad_scaled on y, then the
+ * output GELU's chain rule, in one pass over the field when the plan's matrix-core epilogue
+ * applies (else the epilogue writes z into grad_z and a pointwise pass rewrites it).
+ * `save` (nullable) receives the retained spectrum only: the pre-activation is not needed
+ * afterwards, since fno_block_bwd_preact takes grad_z.  grad_scale must be finite and > 0. */
+fno_status fno_block_fwd_mse(const fno_plan* plan, const float* x, const float* w,
+                             const float* w_bypass, const float* bias, const float* target,
+                             float grad_scale, float* grad_z, float* loss, void* save,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Block backward from the gradient at the pre-activation z (the output GELU's derivative
+ * already applied, as fno_block_fwd_mse returns it): fno_block_bwd without the GELU' step, so
+ * z is never read.  `save` is one filled by fno_block_fwd or fno_block_fwd_mse with the same
+ * inputs (its spectrum is read); it is required only for grad_w (else NULL recomputes). */
+fno_status fno_block_bwd_preact(const fno_plan* plan, const float* x, const float* w,
+                                const float* w_bypass, const float* bias, const void* save,
+                                const float* grad_z, float* grad_x, float* grad_w,
+                                float* grad_w_bypass, float* grad_bias, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* ---- Tucker-factorised spectral weights (TFNO) ----------------------------------------------
  * TFNO is one of the architectures trained in mixed precision on the mixed-precision
  * neural-operator page ("Tiivistelmä"), together with a greedy algorithm ordering the block's
@@ -224,6 +250,21 @@ fno_status fno_tucker_block_bwd(const fno_tucker* tucker, const float* x, const 
                                 float* grad_x, float* grad_core, float* const* grad_factors,
                                 float* grad_w_bypass, float* grad_bias, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/* fno_block_fwd_mse / fno_block_bwd_preact with the Tucker weight (arguments as in
+ * fno_tucker_block_fwd / _bwd; save is required for any weight gradient). */
+fno_status fno_tucker_block_fwd_mse(const fno_tucker* tucker, const float* x, const float* core,
+                                    const float* const* factors, const float* w_bypass,
+                                    const float* bias, const float* target, float grad_scale,
+                                    float* grad_z, float* loss, void* save, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+fno_status fno_tucker_block_bwd_preact(const fno_tucker* tucker, const float* x,
+                                       const float* core, const float* const* factors,
+                                       const float* w_bypass, const float* bias,
+                                       const void* save, const float* grad_z, float* grad_x,
+                                       float* grad_core, float* const* grad_factors,
+                                       float* grad_w_bypass, float* grad_bias, void* workspace,
+                                       size_t workspace_bytes, void* stream);
 
 /* Pointwise layers used to lift into and project out of the block stack.
  * hidden == 0: y = w1 x + b1            (w1 [c_out][c_in], b1 [c_out])

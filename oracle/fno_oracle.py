@@ -376,6 +376,24 @@ def mse_loss_grad(y, t):
     return float(np.mean(diff * diff)), 2.0 * diff / diff.size
 
 
+def block_fwd_mse(x, w, wb, bias, modes, target, grad_scale: float = 1.0, tanh: bool = False,
+                  act: bool = True, input_gelu: bool = False):
+    """The last block of a training step followed by the loss (F1-F4, then A12), reported at
+    the block's pre-activation: loss = mean((y - t)^2) and grad_z = grad_scale * dloss/dz,
+    i.e. the loss gradient 2 (y - t) / numel through the output GELU's derivative (B1).
+    Returns dict(loss, grad_z, fwd)."""
+    fwd = block_fwd(x, w, wb, bias, modes, tanh=tanh, act=act, input_gelu=input_gelu)
+    loss, g_y = mse_loss_grad(fwd["y"], target)
+    g_z = g_y * gelu_prime(fwd["z"]) if act else g_y
+    return {"loss": loss, "grad_z": grad_scale * g_z, "fwd": fwd}
+
+
+def block_bwd_preact(x, w, wb, bias, modes, g_z, tanh: bool = False, input_gelu: bool = False):
+    """B2-B6 (and B7) of one block from the gradient at its pre-activation z: block_bwd with
+    the output GELU's derivative already applied."""
+    return block_bwd(x, w, wb, bias, modes, g_z, tanh=tanh, act=False, input_gelu=input_gelu)
+
+
 # ----------------------------------------------------------------------------- stacks
 def stack_fwd(x, blocks, modes, tanh: bool = False, lift=None, proj=None):
     """Lift (optional) -> FNO blocks (GELU after each) -> projection (optional).

@@ -385,6 +385,66 @@ def check_mse_and_stack(O):
         assert abs(num - res["grad_x"][idx]) < 1e-6 * max(1e-3, abs(num)), ("stack dx", num)
 
 
+def check_fused_loss(O):
+    """The last block fused with the loss: grad_z by central differences of the loss in z
+    (the output GELU between them), and the pre-activation backward's grad_x, grad_Wb and
+    grad_bias by central differences of loss(block(x)) (input GELU on and off); grad_scale
+    only scales the gradient."""
+    h = 1e-6
+    for gi, (grid, modes, tanh, ig) in enumerate([((6, 8), (2, 3), True, False),
+                                                  ((4, 4, 6), (1, 2, 2), False, True)]):
+        g = _rng(160 + gi)
+        d = len(grid)
+        c = 2
+        x = g.standard_normal((2, c) + grid)
+        w = _rand_w(g, d, c, c, modes) * 0.4
+        wb = g.standard_normal((c, c))
+        bias = g.standard_normal(c)
+        tgt = g.standard_normal((2, c) + grid)
+        r = O.block_fwd_mse(x, w, wb, bias, modes, tgt, tanh=tanh, input_gelu=ig)
+        z = r["fwd"]["z"]
+        loss_z = lambda z_: float(np.mean((O.gelu(z_) - tgt) ** 2))  # noqa: E731
+        assert abs(r["loss"] - loss_z(z)) < 1e-12 * max(1.0, r["loss"])
+        for _ in range(5):
+            idx = tuple(int(g.integers(0, s)) for s in z.shape)
+            zp = z.copy()
+            zm = z.copy()
+            zp[idx] += h
+            zm[idx] -= h
+            num = (loss_z(zp) - loss_z(zm)) / (2 * h)
+            assert abs(num - r["grad_z"][idx]) < 1e-6 * max(1e-3, abs(num)), \
+                ("grad_z", idx, num, r["grad_z"][idx])
+        r8 = O.block_fwd_mse(x, w, wb, bias, modes, tgt, grad_scale=8.0, tanh=tanh,
+                             input_gelu=ig)
+        _close(r8["grad_z"], 8.0 * r["grad_z"], 1e-15, "grad_scale")
+        b = O.block_bwd_preact(x, w, wb, bias, modes, r["grad_z"], tanh=tanh, input_gelu=ig)
+        L = lambda x_, wb_, b_: O.block_fwd_mse(  # noqa: E731
+            x_, w, wb_, b_, modes, tgt, tanh=tanh, input_gelu=ig)["loss"]
+        for _ in range(5):
+            idx = tuple(int(g.integers(0, s)) for s in x.shape)
+            xp = x.copy()
+            xm = x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            num = (L(xp, wb, bias) - L(xm, wb, bias)) / (2 * h)
+            assert abs(num - b["grad_x"][idx]) < 1e-6 * max(1e-3, abs(num)), ("dx", idx, num)
+        for _ in range(3):
+            idx = (int(g.integers(0, c)), int(g.integers(0, c)))
+            p = wb.copy()
+            m = wb.copy()
+            p[idx] += h
+            m[idx] -= h
+            num = (L(x, p, bias) - L(x, m, bias)) / (2 * h)
+            assert abs(num - b["grad_wb"][idx]) < 1e-6 * max(1e-3, abs(num)), ("dWb", idx)
+        for o in range(c):
+            p = bias.copy()
+            m = bias.copy()
+            p[o] += h
+            m[o] -= h
+            num = (L(x, wb, p) - L(x, wb, m)) / (2 * h)
+            assert abs(num - b["grad_bias"][o]) < 1e-6 * max(1e-3, abs(num)), ("dbias", o)
+
+
 def check_inverse_at_points(O):
     """The point-wise inverse agrees with numpy's irfftn of the zero-padded spectrum at
     every sampled point (2D, 3D, 4D)."""
@@ -556,7 +616,7 @@ ALL_CHECKS = [
     check_single_mode_dc_plane, check_cutoff, check_linearity_equivariance_selfadjoint,
     check_gelu, check_zero_weight_block, check_adjoint_identities,
     check_block_finite_differences, check_mse_and_stack,
-    check_input_activation,
+    check_input_activation, check_fused_loss,
     check_tucker_identity_factors, check_tucker_hosvd, check_tucker_rank_one,
     check_tucker_block_finite_differences,
 ]

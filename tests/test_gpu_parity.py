@@ -291,3 +291,55 @@ def test_spectral_conv_input_gelu(L, case, prec):
     check("grad_x", _host(gx), bwd["grad_x"], tol)
     check("grad_w", _host(gw), bwd["grad_w"], tol)
     plan.close()
+
+
+def _fused_loss_case(L, case, prec, ig, act, seed0):
+    """fno_block_fwd_mse then fno_block_bwd_preact against the oracle's loss, grad_z and the
+    block backward from it; f16 plans take the static loss scale 2^16."""
+    name, batch, cin, cout, grid, modes = case
+    pname, mixed, tanh = prec
+    announce("block fused loss", name, pname, "input_gelu" if ig else "", "gelu" if act else "z")
+    seed = seed0 + zlib.crc32(name.encode()) % 1000
+    x, w, wb, b = inputs.small_case(seed, batch, cin, cout, grid, modes)
+    tgt = inputs.normal_like(seed + 1, (batch, cout) + grid)
+    scale = 65536.0 if mixed == "f16" else 1.0
+    tol = tol_for(mixed)
+    plan = L.Plan(batch, cin, cout, grid, modes, mixed=mixed, tanh=tanh, gelu=act,
+                  input_gelu=ig)
+    tx, tw, twb, tb, tt = (_dev(a) for a in (x, w, wb, b, tgt))
+    save = plan.new_save()
+    gz, loss = plan.block_fwd_mse(tx, tw, twb, tb, tt, grad_scale=scale, save=save)
+    g = plan.block_bwd_preact(tx, tw, twb, tb, save, gz)
+    # from the oracle's grad_z, without a save (the spectrum recomputed; grad_x only)
+    ref = O.block_fwd_mse(x, w, wb, b, modes, tgt, tanh=tanh, act=act, input_gelu=ig)
+    g2 = plan.block_bwd_preact(tx, tw, twb, tb, None,
+                               _dev((ref["grad_z"] * scale).astype(np.float32)),
+                               want=("x",))
+    _torch().cuda.synchronize()
+    refb = O.block_bwd_preact(x, w, wb, b, modes, ref["grad_z"], tanh=tanh, input_gelu=ig)
+    check("grad_z", _host(gz) / scale, ref["grad_z"], tol)
+    got_loss = float(_host(loss)[0])
+    print(f"    loss: {got_loss:.7e} (oracle {ref['loss']:.7e})", flush=True)
+    assert abs(got_loss - ref["loss"]) <= tol * ref["loss"], (got_loss, ref["loss"])
+    check("grad_x", _host(g["x"]) / scale, refb["grad_x"], tol)
+    check("grad_w", _host(g["w"]) / scale, refb["grad_w"], tol)
+    check("grad_wb", _host(g["wb"]) / scale, refb["grad_wb"], tol)
+    check("grad_bias", _host(g["bias"]) / scale, refb["grad_bias"], tol)
+    check("grad_x (recomputed spectrum)", _host(g2["x"]) / scale, refb["grad_x"], tol)
+    plan.close()
+
+
+@pytest.mark.parametrize("prec", PRECISIONS[:3], ids=[p[0] for p in PRECISIONS[:3]])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_block_fused_loss(L, case, prec):
+    """The last block fused with the MSE loss (the matrix-core epilogue where it applies, the
+    generic and row-axis epilogues plus a pointwise pass elsewhere)."""
+    _fused_loss_case(L, case, prec, False, True, 2900)
+
+
+@pytest.mark.parametrize("ig,act", [(True, True), (True, False), (False, False)],
+                         ids=["input_gelu", "input_gelu_z_out", "z_out"])
+@pytest.mark.parametrize("prec", PRECISIONS[:2], ids=[p[0] for p in PRECISIONS[:2]])
+@pytest.mark.parametrize("case", IG_CASES, ids=[c[0] for c in IG_CASES])
+def test_block_fused_loss_activations(L, case, prec, ig, act):
+    _fused_loss_case(L, case, prec, ig, act, 3900)

@@ -1,9 +1,11 @@
 """Precision scheduling on the GPU (mixed-precision neural-operator page, "Tiivistelmä":
 training moves from mixed to full precision): a two-block 2D training stack (dense or
 Tucker-factorised weights) runs four steps through StackRunner.run, two with half operands,
-two in fp32 with the tanh pre-activation kept.  Every step's loss, output and gradients are compared with the oracle's training step
-(tanh on) at the tolerance of the precision the step ran in; steps of one precision must agree
-bit for bit (no weight update runs between them)."""
+two in fp32 with the tanh pre-activation kept, once with the loss fused into the last block
+and once with the stand-alone loss kernel.  Every step's loss, gradients and (with the loss
+kernel) output are compared with the oracle's training step (tanh on) at the tolerance of the
+precision the step ran in; steps of one precision must agree bit for bit (no weight update runs
+between them)."""
 import numpy as np
 import pytest
 
@@ -40,15 +42,17 @@ def _tucker_train_ref(hi, modes):
     return {"loss": loss, "y": acts[-1], "grad_x": g, "grads": grads}
 
 
+@pytest.mark.parametrize("fuse", [True, False], ids=["fused_loss", "loss_kernel"])
 @pytest.mark.parametrize("weights", ["dense", "tucker"])
 @pytest.mark.parametrize("half", ["bf16", "f16"])
-def test_precision_schedule_training_run(half, weights):
+def test_precision_schedule_training_run(half, weights, fuse):
     import torch
     from fno_spectral_convolution_amd.stack import PrecisionSchedule, StackRunner
-    announce("schedule", half, weights)
+    announce("schedule", half, weights, "fused loss" if fuse else "loss kernel")
     extra = {"tucker_ranks": (8, 8, 6, 6)} if weights == "tucker" else {}
     wl = configs.Workload(mixed=True if half == "bf16" else "f16", **_WL, **extra)
-    runner = StackRunner(wl, device="cuda")
+    runner = StackRunner(wl, device="cuda", fuse_loss=fuse)
+    assert runner.fuse_loss == fuse
     hi = runner.host
     if weights == "tucker":
         ref = _tucker_train_ref(hi, wl.modes)
@@ -66,7 +70,10 @@ def test_precision_schedule_training_run(half, weights):
             if weights == "tucker":
                 d["factors"] = [_host(u) / s for u in g["factors"]]
             grads.append(d)
-        seen.append({"precision": runner.precision, "scale": s, "y": _host(out),
+        # the fused loss never writes the output field
+        assert (out is None) == fuse
+        seen.append({"precision": runner.precision, "scale": s,
+                     "y": None if out is None else _host(out),
                      "loss": float(_host(runner.loss)[0]), "grad_x": _host(runner.grad_x) / s,
                      "grads": grads})
 
@@ -76,7 +83,8 @@ def test_precision_schedule_training_run(half, weights):
     for i, r in enumerate(seen):
         tol = tol_for(False if r["precision"] == "f32" else ("f16" if half == "f16" else True))
         print(f"  step {i} ({r['precision']})", flush=True)
-        check("y", r["y"], ref["y"], tol)
+        if not fuse:
+            check("y", r["y"], ref["y"], tol)
         assert abs(r["loss"] - ref["loss"]) <= tol * ref["loss"], (r["loss"], ref["loss"])
         check("grad_x", r["grad_x"], ref["grad_x"], tol)
         for b, (g, gr) in enumerate(zip(r["grads"], ref["grads"])):
@@ -89,8 +97,10 @@ def test_precision_schedule_training_run(half, weights):
             check(f"block {b} grad_wb", g["wb"], gr["grad_wb"], tol)
             check(f"block {b} grad_bias", g["bias"], gr["grad_bias"], tol)
     for a, b in ((seen[0], seen[1]), (seen[2], seen[3])):
-        assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["grad_x"], b["grad_x"])
+        assert a["loss"] == b["loss"] and np.array_equal(a["grad_x"], b["grad_x"])
+        if not fuse:
+            assert np.array_equal(a["y"], b["y"])
         for ga, gb in zip(a["grads"], b["grads"]):
             assert all(np.array_equal(ga[k], gb[k]) for k in wkeys)
     # the fp32 steps after the switch differ from the half steps before it
-    assert not np.array_equal(seen[1]["y"], seen[2]["y"])
+    assert not np.array_equal(seen[1]["grad_x"], seen[2]["grad_x"])

@@ -156,3 +156,43 @@ def test_tucker_spectral_conv(L, case, prec, use_save):
         check(f"grad_factor {n}", _host(gfac[n]), want, tol)
     tk.close()
     plan.close()
+
+
+@pytest.mark.parametrize("prec", PRECISIONS, ids=[p[0] for p in PRECISIONS])
+@pytest.mark.parametrize("case", CASES[:5] + CASES[6:], ids=[c[0] for c in CASES[:5] + CASES[6:]])
+def test_tucker_fused_loss(L, case, prec):
+    """fno_tucker_block_fwd_mse then fno_tucker_block_bwd_preact against the oracle's loss,
+    grad_z and the Tucker block backward from it (f16: static loss scale 2^16)."""
+    name, batch, cin, cout, grid, modes, ranks, _ = case
+    pname, mixed = prec
+    seed = 40 + zlib.crc32(name.encode()) % 1000
+    x, _, wb, b = inputs.small_case(seed, batch, cin, cout, grid, modes)
+    tgt = inputs.normal_like(seed + 1, (batch, cout) + grid)
+    core, facs = _tucker_params(seed, cin, cout, modes, ranks)
+    scale = 65536.0 if mixed == "f16" else 1.0
+    plan = L.Plan(batch, cin, cout, grid, modes, mixed=mixed, input_gelu=True)
+    tk = L.Tucker(plan, ranks)
+    announce("tucker fused loss", name, pname, tk.order)
+    tol = tol_for(mixed)
+    tx, twb, tb, tt, tcore = (_dev(a) for a in (x, wb, b, tgt, core))
+    tfac = [_dev(u) for u in facs]
+    save = plan.new_save()
+    gz, loss = tk.block_fwd_mse(tx, tcore, tfac, twb, tb, tt, grad_scale=scale, save=save)
+    gr = tk.block_bwd_preact(tx, tcore, tfac, twb, tb, save, gz)
+    _torch().cuda.synchronize()
+    w = O.fold_weights(O.tucker_to_full(core, facs), modes)
+    ref = O.block_fwd_mse(x, w, wb, b, modes, tgt, tanh=bool(mixed), input_gelu=True)
+    refb = O.block_bwd_preact(x, w, wb, b, modes, ref["grad_z"], tanh=bool(mixed),
+                              input_gelu=True)
+    gcore, gfac = O.tucker_grads(core, facs, O.expand_weights(refb["grad_w"], modes))
+    check("grad_z", _host(gz) / scale, ref["grad_z"], tol)
+    got_loss = float(_host(loss)[0])
+    assert abs(got_loss - ref["loss"]) <= tol * ref["loss"], (got_loss, ref["loss"])
+    check("grad_x", _host(gr["x"]) / scale, refb["grad_x"], tol)
+    check("grad_core", _host(gr["core"]) / scale, gcore, tol)
+    for n, (got, want) in enumerate(zip(gr["factors"], gfac)):
+        check(f"grad_factor {n}", _host(got) / scale, want, tol)
+    check("grad_wb", _host(gr["wb"]) / scale, refb["grad_wb"], tol)
+    check("grad_bias", _host(gr["bias"]) / scale, refb["grad_bias"], tol)
+    tk.close()
+    plan.close()

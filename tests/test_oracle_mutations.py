@@ -123,7 +123,28 @@ def _block_bwd_input_gelu_no_prime(x, w, wb, bias, modes, g_y, tanh=False, act=T
     return _orig["block_bwd"](O.gelu(x), w, wb, bias, modes, g_y, tanh=tanh, act=act)
 
 
+def _fused_loss_no_gelu_prime(x, w, wb, bias, modes, target, grad_scale=1.0, tanh=False,
+                              act=True, input_gelu=False):
+    # the loss gradient handed on as if y were z (the output GELU's derivative dropped)
+    r = _orig["block_fwd_mse"](x, w, wb, bias, modes, target, grad_scale, tanh, False,
+                               input_gelu)
+    fwd = _orig["block_fwd"](x, w, wb, bias, modes, tanh=tanh, act=act, input_gelu=input_gelu)
+    r = dict(r)
+    r["loss"] = float(np.mean((fwd["y"] - np.asarray(target, dtype=np.float64)) ** 2))
+    r["grad_z"] = grad_scale * 2.0 * (fwd["y"] - target) / fwd["y"].size
+    r["fwd"] = fwd
+    return r
+
+
+def _preact_bwd_gelu_twice(x, w, wb, bias, modes, g_z, tanh=False, input_gelu=False):
+    # the output GELU's derivative applied again on top of the pre-activation gradient
+    return _orig["block_bwd"](x, w, wb, bias, modes, g_z, tanh=tanh, act=True,
+                              input_gelu=input_gelu)
+
+
 MUTATIONS = [
+    ("block_fwd_mse", _fused_loss_no_gelu_prime, P.check_fused_loss),
+    ("block_bwd_preact", _preact_bwd_gelu_twice, P.check_fused_loss),
     ("dft_matrix", _dft_sign_flipped, P.check_spectrum_bruteforce),
     ("retained_indices", _retained_off_by_one, P.check_spectrum_numpy_fft),
     ("gamma_weights", _gamma_all_two, P.check_roundtrip_identity),
