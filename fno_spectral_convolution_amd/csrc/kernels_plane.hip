@@ -44,7 +44,7 @@ __device__ __forceinline__ float prologue(float v, float w) {
   if (PIN == PLANE_TANH) return tanh_fast(v);
   if (PIN == PLANE_GELU_GRAD) return v * gelu_grad_as(w);
   if (PIN == PLANE_GELU) return gelu_as(v);
-  if (PIN == PLANE_TANH_GELU) return tanh_fast(gelu_as(v));
+  if (PIN == PLANE_TANH_GELU) return tanh_gelu(v);
   return v;
 }
 

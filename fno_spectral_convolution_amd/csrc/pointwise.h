@@ -4,46 +4,57 @@
 // Phi is evaluated from the complementary error function with the rational approximation of
 // Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26 (Hastings):
 //   erfc(x) ~ (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),  t = 1/(1 + p x), x >= 0,
-// with absolute error <= 1.5e-7.  Working with erfc for the tail side avoids the 1 - erf
-// cancellation, and exp(-x^2) with x = |z|/sqrt 2 is also e^{-z^2/2}, so phi(z) shares it.
+// with absolute error <= 1.5e-7, and exp(-x^2) with x = |z|/sqrt 2 is also e^{-z^2/2}, so
+// phi(z) shares it.  erf = 1 - erfc carries that absolute error near 0, where GELU multiplies
+// it by |z| / 2 (and Phi, GELU' keep it absolute, as the erfc form did).  The exponential is
+// the hardware base-2 exponential (v_exp_f32) of a pre-scaled argument; it flushes to 0 below
+// 2^-126, where erfc is far below float resolution of erf anyway.
 #pragma once
 
 #include <hip/hip_runtime.h>
 
 namespace fno {
 
-struct NormalParts {
-  float cdf;  // Phi(z)
-  float pdf;  // phi(z)
+// erf(|z|/sqrt 2) = 1 - erfc(|z|/sqrt 2) and phi's exponential e = exp(-z^2 / 2), with the
+// constants folded: t = 1 / (1 + (p / sqrt 2)|z|) and e = 2^(-(log2 e / 2) z^2).  Then
+//   GELU(z)  = z Phi(z) = (z + |z| erf(|z|/sqrt 2)) / 2      (either sign of z),
+//   Phi(z)   = (1 + sign(z) erf(|z|/sqrt 2)) / 2,  GELU'(z) = Phi(z) + z e / sqrt(2 pi).
+// The absolute error of erf here is that of the approximant (<= 1.5e-7) plus rounding; GELU's is
+// that times |z| / 2.
+struct NormalErf {
+  float erf_abs;  // erf(|z| / sqrt 2)
+  float e;        // exp(-z^2 / 2)
 };
 
-__device__ __forceinline__ NormalParts normal_parts(float z) {
-  const float p = 0.3275911f;
+__device__ __forceinline__ NormalErf normal_erf(float z) {
+  const float p = 0.3275911f * 0.70710678118654752f;
   const float a1 = 0.254829592f, a2 = -0.284496736f, a3 = 1.421413741f, a4 = -1.453152027f,
               a5 = 1.061405429f;
-  const float x = fabsf(z) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(1.0f + p * x);  // 1 ulp reciprocal
-  const float e = __expf(-x * x);  // = exp(-z^2 / 2)
-  const float poly = t * (a1 + t * (a2 + t * (a3 + t * (a4 + t * a5))));
-  const float tail = 0.5f * poly * e;  // = Phi(-|z|)
-  NormalParts r;
-  r.cdf = z >= 0.f ? 1.0f - tail : tail;
-  r.pdf = e * 0.39894228040143268f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(p, fabsf(z), 1.0f));  // 1 ulp reciprocal
+  const float e = __builtin_amdgcn_exp2f((z * z) * -0.72134752044448170f);
+  const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, a5, a4), a3), a2), a1);
+  NormalErf r;
+  r.erf_abs = fmaf(-poly, e, 1.0f);
+  r.e = e;
   return r;
 }
 
-__device__ __forceinline__ float gelu_as(float z) { return z * normal_parts(z).cdf; }
-
-__device__ __forceinline__ float gelu_grad_as(float z) {
-  const NormalParts n = normal_parts(z);
-  return n.cdf + z * n.pdf;
+__device__ __forceinline__ float gelu_as(float z) {
+  return 0.5f * fmaf(fabsf(z), normal_erf(z).erf_abs, z);
 }
 
-// GELU(z) and GELU'(z) from one evaluation of Phi and phi
+__device__ __forceinline__ float gelu_grad_as(float z) {
+  const NormalErf n = normal_erf(z);
+  const float cdf = fmaf(0.5f, copysignf(n.erf_abs, z), 0.5f);
+  return fmaf(z * 0.39894228040143268f, n.e, cdf);
+}
+
+// GELU(z) and GELU'(z) from one evaluation of erf and the density
 __device__ __forceinline__ void gelu_and_grad(float z, float& g, float& gp) {
-  const NormalParts n = normal_parts(z);
-  g = z * n.cdf;
-  gp = n.cdf + z * n.pdf;
+  const NormalErf n = normal_erf(z);
+  g = 0.5f * fmaf(fabsf(z), n.erf_abs, z);
+  const float cdf = fmaf(0.5f, copysignf(n.erf_abs, z), 0.5f);
+  gp = fmaf(z * 0.39894228040143268f, n.e, cdf);
 }
 
 // tanh(v) = 1 - 2 / (e^{2v} + 1): five instructions (exp, reciprocal); saturates to +-1 for
@@ -51,8 +62,15 @@ __device__ __forceinline__ void gelu_and_grad(float z, float& g, float& gp) {
 // the bfloat16 rounding applied to the pre-activated field and the 1e-2 tolerance of that
 // path.  Divisions use the hardware reciprocal (1 ulp).
 __device__ __forceinline__ float tanh_fast(float v) {
-  const float e = __expf(2.0f * v);
-  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+  const float e = __builtin_amdgcn_exp2f(v * 2.8853900817779268f);  // e^{2v}
+  return fmaf(-2.0f, __builtin_amdgcn_rcpf(e + 1.0f), 1.0f);
+}
+
+// tanh(GELU(z)): e^{2 GELU(z)} = 2^{log2(e) (z + |z| erf(|z|/sqrt 2))}, one scale for both
+__device__ __forceinline__ float tanh_gelu(float z) {
+  const float u = fmaf(fabsf(z), normal_erf(z).erf_abs, z);  // 2 GELU(z)
+  const float e = __builtin_amdgcn_exp2f(u * 1.4426950408889634f);
+  return fmaf(-2.0f, __builtin_amdgcn_rcpf(e + 1.0f), 1.0f);
 }
 
 }  // namespace fno
