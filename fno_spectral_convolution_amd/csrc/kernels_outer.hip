@@ -22,6 +22,8 @@ struct OuterArgs {
   float* out;            // [pre][Lout][post2]
   const void* A;         // [Lout_pad][2 Lin_pad] f32, or bf16 bits (hi)
   const uint16_t* Alo;   // bf16 residual (bf16 path)
+  int64_t pre;           // slabs
+  int msplit, mt_per;    // k_outer_mfma: work-groups per slab, output row tiles of each
 };
 
 template <int H, int NT>
@@ -34,32 +36,64 @@ __global__ void __launch_bounds__(256) k_outer_mfma(OuterArgs a) {
   const int KS = K + (BF ? 8 : 4);  // row stride of Bt (elements)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, q = lane >> 4;
-  const int64_t pre = blockIdx.x;
+  // With msplit > 1 the output row tiles of a slab are split over msplit work-groups, which
+  // the numbering keeps on one XCD (work-group x runs on XCD x % 8) so that they share the
+  // slab's input in its L2: x = 8 msplit grp + 8 ms + i is slab 8 grp + i, part ms.
+  int64_t pre = blockIdx.x;
+  int ms = 0;
+  if (a.msplit > 1) {
+    const int64_t x = blockIdx.x;
+    const int64_t grp = x / (8 * a.msplit);
+    const int r = (int)(x - grp * 8 * a.msplit);
+    ms = r / 8;
+    pre = grp * 8 + (r & 7);
+    if (pre >= a.pre) return;  // the whole work-group: past the last slab
+  }
+  const int mt_begin = ms * a.mt_per;
+  const int mt_end = min(a.Lout_pad / 16, mt_begin + a.mt_per);
   const int64_t c0 = (int64_t)blockIdx.y * CT;
   const float* src = a.in + pre * a.Lin * a.post2;
   // Bt[c][k]: k < Lin_pad -> X[k][c0 + c]; k >= Lin_pad -> Xs[k - Lin_pad][c0 + c]
   // staged row of column c (local): 16 (c % NT) + c / NT
   auto brow = [](int c) { return 16 * (c % NT) + c / NT; };
-  for (int e = tid; e < a.Lin_pad * CT; e += 256) {
-    const int li = e / CT, c = e - li * CT;
-    const int64_t col = c0 + c;
-    float v = 0.f;
-    if (li < a.Lin && col < a.post2) v = src[(int64_t)li * a.post2 + col];
-    const int cp = c ^ 1;
-    const float vs = (c & 1) ? -v : v;  // Xs[li][c^1]
-    if (BF) {
-      uint16_t* bt = reinterpret_cast<uint16_t*>(s_raw);
-      bt[brow(c) * KS + li] = HalfOf<H>::bits(v);
-      bt[brow(cp) * KS + a.Lin_pad + li] = HalfOf<H>::bits(vs);
-    } else {
-      float* bt = reinterpret_cast<float*>(s_raw);
-      bt[brow(c) * KS + li] = v;
-      bt[brow(cp) * KS + a.Lin_pad + li] = vs;
+  // 8 loads per thread in flight at a time: clamped addresses and a mask, no branch around
+  // the loads (which would make each wait for the one before it)
+  constexpr int SU = 8;
+  const int nel = a.Lin_pad * CT;
+  for (int e0 = 0; e0 < nel; e0 += 256 * SU) {
+    float v[SU];
+#pragma unroll
+    for (int u = 0; u < SU; ++u) {
+      const int e = e0 + tid + 256 * u;
+      const int li = e / CT, c = e - li * CT;
+      const int64_t col = c0 + c;
+      const bool ok = e < nel && li < a.Lin && col < a.post2;
+      const int64_t off = (int64_t)min(li, a.Lin - 1) * a.post2 + min(col, a.post2 - 1);
+      const float x = src[off];
+      v[u] = ok ? x : 0.f;
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the LDS writes
+#pragma unroll
+    for (int u = 0; u < SU; ++u) {
+      const int e = e0 + tid + 256 * u;
+      if (e >= nel) continue;
+      const int li = e / CT, c = e - li * CT;
+      const int cp = c ^ 1;
+      const float vs = (c & 1) ? -v[u] : v[u];  // Xs[li][c^1]
+      if (BF) {
+        uint16_t* bt = reinterpret_cast<uint16_t*>(s_raw);
+        bt[brow(c) * KS + li] = HalfOf<H>::bits(v[u]);
+        bt[brow(cp) * KS + a.Lin_pad + li] = HalfOf<H>::bits(vs);
+      } else {
+        float* bt = reinterpret_cast<float*>(s_raw);
+        bt[brow(c) * KS + li] = v[u];
+        bt[brow(cp) * KS + a.Lin_pad + li] = vs;
+      }
     }
   }
   __syncthreads();
   float* dst = a.out + pre * a.Lout * a.post2;
-  for (int mt = wave; mt < a.Lout_pad / 16; mt += 4) {
+  for (int mt = mt_begin + wave; mt < mt_end; mt += 4) {
     f32x4 acc[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[nt] = zero4();
@@ -576,7 +610,17 @@ hipError_t launch_outer_mfma(const fno_plan* p, int axis, int chans, bool inv, c
   while (nt > 1 && (size_t)16 * nt * col_bytes > 64 * 1024) nt /= 2;
   const int ct = 16 * nt;
   const size_t lds = (size_t)ct * col_bytes;
-  dim3 grid((unsigned)pre, (unsigned)((a.post2 + ct - 1) / ct));
+  const int64_t ctiles = (a.post2 + ct - 1) / ct;
+  // few slabs: split each slab's output row tiles over up to msplit work-groups (at least
+  // four tiles, one per wave, each) until about 2048 work-groups are in flight
+  const int mtiles = a.Lout_pad / 16;
+  a.pre = pre;
+  a.msplit = 1;
+  while (2 * a.msplit * 4 <= mtiles && pre * ctiles * a.msplit < 2048) a.msplit *= 2;
+  a.mt_per = (mtiles + a.msplit - 1) / a.msplit;
+  const int64_t gx = a.msplit == 1 ? pre : (pre + 7) / 8 * 8 * a.msplit;
+  if (gx > 0x7fffffff || ctiles > 65535) return hipErrorInvalidValue;
+  dim3 grid((unsigned)gx, (unsigned)ctiles);
   if (g.half == 2) {
     if (nt == 4) hipLaunchKernelGGL((k_outer_mfma<2, 4>), grid, dim3(256), lds, s, a);
     else if (nt == 2) hipLaunchKernelGGL((k_outer_mfma<2, 2>), grid, dim3(256), lds, s, a);
