@@ -147,6 +147,41 @@ def test_train3d_128_block_full(L):
     _block_case(L, "train3d_128", 1e-3)
 
 
+@pytest.mark.parametrize("name", ["train2d_512", "train3d_128"])
+def test_last_block_fused_loss_full(L, name):
+    """The last block of the training stack at full size, as the step runs it: input GELU,
+    output GELU, the loss against the workload's target fused into the forward epilogue
+    (fno_block_fwd_mse) and the backward from the pre-activation gradient
+    (fno_block_bwd_preact), against the oracle's loss, grad_z and block backward."""
+    wl = configs.get(name)
+    tol = tol_for(wl.mixed)
+    announce("workload fused loss", name, wl.batch, wl.width, wl.grid, wl.modes)
+    x = _field(wl)
+    tgt = inputs.field(wl, inputs.STREAM_TARGET)
+    blk = inputs.block_params(wl, 1)[0]
+    plan = L.Plan(wl.batch, wl.width, wl.width, wl.grid, wl.modes, mixed=wl.mixed,
+                  input_gelu=True)
+    tx, tw, twb, tb, tt = (_dev(a) for a in (x, blk["w"], blk["wb"], blk["bias"], tgt))
+    save = plan.new_save()
+    gz, loss = plan.block_fwd_mse(tx, tw, twb, tb, tt, save=save)
+    g = plan.block_bwd_preact(tx, tw, twb, tb, save, gz)
+    _torch().cuda.synchronize()
+    got = {"grad_z": _host(gz), "loss": float(_host(loss)[0]), "grad_x": _host(g["x"]),
+           "grad_w": _host(g["w"]), "grad_wb": _host(g["wb"]), "grad_bias": _host(g["bias"])}
+    del save, g, gz, tt
+    ref = O.block_fwd_mse(x, blk["w"], blk["wb"], blk["bias"], wl.modes, tgt,
+                          tanh=bool(wl.mixed), input_gelu=True)
+    print(f"    loss: {got['loss']:.7e} (oracle {ref['loss']:.7e})", flush=True)
+    assert abs(got["loss"] - ref["loss"]) <= tol * ref["loss"], (got["loss"], ref["loss"])
+    check("grad_z", got["grad_z"], ref["grad_z"], tol)
+    refb = O.block_bwd_preact(x, blk["w"], blk["wb"], blk["bias"], wl.modes, ref["grad_z"],
+                              tanh=bool(wl.mixed), input_gelu=True)
+    del ref
+    for k in ("grad_x", "grad_w", "grad_wb", "grad_bias"):
+        check(k, got[k], refb[k], tol)
+    plan.close()
+
+
 def test_stack2d_256_sampled_batches(L):
     """The full 2D stack (lift, 4 blocks, projection) on the GPU, as bench.py runs it; the
     oracle evaluates the same stack for batch entries 0 and 15."""
