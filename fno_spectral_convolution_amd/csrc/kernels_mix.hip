@@ -180,7 +180,9 @@ __global__ void __launch_bounds__(256) k_mix_mfma(Geom g, const int32_t* __restr
 }
 
 // ------------------------------------------------------------------------------------------
-// Weight gradient.  Grid: (mode groups, 8-channel tiles of Cin, 16-column tiles of Cout).
+// Weight gradient.  Grid: (mode groups, gridDim.y parts of the 8-channel tiles of Cin, 16-column
+// tiles of Cout): a work-group walks the Cin tiles y, y + gridDim.y, ..., and the first batch
+// chunk of the next tile is loaded while the current one is computed and stored.
 // Rows 0..7: Re, rows 8..15: Im of the 8 input channels; K = (batch entry, re / im).
 template <int H>
 __global__ void __launch_bounds__(256) k_mix_mfma_dw(Geom g, const int32_t* __restrict__ mode_woff,
@@ -197,17 +199,18 @@ __global__ void __launch_bounds__(256) k_mix_mfma_dw(Geom g, const int32_t* __re
   const int m = lane & 15, q = lane >> 4;
   const int64_t K = g.K;
   const int64_t t0 = (int64_t)blockIdx.x * kMT;
-  const int i0 = blockIdx.y * 8;
+  const int istride = gridDim.y * 8;
   const int o0 = blockIdx.z * 16;
   const int tl = tid & 15;
   const int tm = (int)min(t0 + tl, K - 1);
   const int Ki = (int)K;
   const float sc = mix_scale(g, tm);
+  const int64_t wmode = mode_woff[tm];
   float2 px[NX], pg[NG];
   // x value u: batch c0 + pr / 8, channel i0 + pr % 8; g value u: batch c0 + u, channel
   // o0 + (tid >> 4)   (pr = (tid >> 4) + 16 u)
   const int ocol = min(o0 + (tid >> 4), g.Cout - 1);
-  auto load_chunk = [&](int c0) {
+  auto load_chunk = [&](int i0, int c0) {
 #pragma unroll
     for (int u = 0; u < NX; ++u) {
       const int pr = (tid >> 4) + 16 * u;
@@ -220,50 +223,54 @@ __global__ void __launch_bounds__(256) k_mix_mfma_dw(Geom g, const int32_t* __re
       pg[u] = ghat[(b * g.Cout + ocol) * Ki + tm];
     }
   };
-  f32x4 acc[4];
+  load_chunk(blockIdx.y * 8, 0);
+  for (int i0 = blockIdx.y * 8; i0 < g.Cin; i0 += istride) {
+    f32x4 acc[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) acc[j] = zero4();
-  load_chunk(0);
-  for (int c0 = 0; c0 < g.B; c0 += BC) {
-    __syncthreads();
+    for (int j = 0; j < 4; ++j) acc[j] = zero4();
+    for (int c0 = 0; c0 < g.B; c0 += BC) {
+      __syncthreads();  // the previous chunk's fragments and output tile are consumed
 #pragma unroll
-    for (int u = 0; u < NX; ++u) {
-      const int pr = (tid >> 4) + 16 * u;
-      const int bb = pr / 8, ii = pr % 8;
-      const bool ok = c0 + bb < g.B && i0 + ii < g.Cin;
-      const float xr = ok ? px[u].x : 0.f, xi = ok ? px[u].y : 0.f;
-      // conj(x) g: rows i: (xr, xi); rows 8 + i: (-xi, xr)
-      put_pair<H>(s_a, tl, ii, 2 * bb, xr, xi);
-      put_pair<H>(s_a, tl, 8 + ii, 2 * bb, -xi, xr);
+      for (int u = 0; u < NX; ++u) {
+        const int pr = (tid >> 4) + 16 * u;
+        const int bb = pr / 8, ii = pr % 8;
+        const bool ok = c0 + bb < g.B && i0 + ii < g.Cin;
+        const float xr = ok ? px[u].x : 0.f, xi = ok ? px[u].y : 0.f;
+        // conj(x) g: rows i: (xr, xi); rows 8 + i: (-xi, xr)
+        put_pair<H>(s_a, tl, ii, 2 * bb, xr, xi);
+        put_pair<H>(s_a, tl, 8 + ii, 2 * bb, -xi, xr);
+      }
+#pragma unroll
+      for (int u = 0; u < NG; ++u) {
+        const int pr = (tid >> 4) + 16 * u;
+        const int bb = pr / 16, oo = pr % 16;
+        const bool ok = c0 + bb < g.B && o0 + oo < g.Cout;
+        put_pair<H>(s_b, tl, oo, 2 * bb, ok ? pg[u].x * sc : 0.f, ok ? pg[u].y * sc : 0.f);
+      }
+      // the next chunk: this tile's next batch chunk, else the next tile's first (clamped
+      // copies past the end)
+      const bool more = c0 + BC < g.B;
+      load_chunk(more ? i0 : min(i0 + istride, g.Cin - 1), more ? c0 + BC : 0);
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = chunk_product<H>(s_a, s_b, 4 * wave + j, m, q, acc[j]);
     }
-#pragma unroll
-    for (int u = 0; u < NG; ++u) {
-      const int pr = (tid >> 4) + 16 * u;
-      const int bb = pr / 16, oo = pr % 16;
-      const bool ok = c0 + bb < g.B && o0 + oo < g.Cout;
-      put_pair<H>(s_b, tl, oo, 2 * bb, ok ? pg[u].x * sc : 0.f, ok ? pg[u].y * sc : 0.f);
-    }
-    load_chunk(min(c0 + BC, g.B - 1));
     __syncthreads();
+    unsigned char* s_out = s_a;  // [16 modes][8 input channels][16 output channels] complex
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = chunk_product<H>(s_a, s_b, 4 * wave + j, m, q, acc[j]);
-  }
-  __syncthreads();
-  unsigned char* s_out = s_a;  // [16 modes][8 input channels][16 output channels] complex
+    for (int j = 0; j < 4; ++j) put_out(s_out, 4 * wave + j, m, q, acc[j]);
+    __syncthreads();
+    const int64_t t = t0 + tl;
+    if (t < K) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) put_out(s_out, 4 * wave + j, m, q, acc[j]);
-  __syncthreads();
-  const int64_t t = t0 + tl;
-  if (t < K) {
-    const int64_t wmode = mode_woff[t];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int pr = (tid >> 4) + 16 * u;
-      const int ii = pr / 16, oo = pr % 16;
-      if (i0 + ii < g.Cin && o0 + oo < g.Cout) {
-        const float2 v =
-            *reinterpret_cast<const float2*>(s_out + tl * kOutTB + (ii * 16 + oo) * 8);
-        dw[wmode + (int64_t)(i0 + ii) * g.w_si + (int64_t)(o0 + oo) * g.w_so] = v;
+      for (int u = 0; u < 8; ++u) {
+        const int pr = (tid >> 4) + 16 * u;
+        const int ii = pr / 16, oo = pr % 16;
+        if (i0 + ii < g.Cin && o0 + oo < g.Cout) {
+          const float2 v =
+              *reinterpret_cast<const float2*>(s_out + tl * kOutTB + (ii * 16 + oo) * 8);
+          dw[wmode + (int64_t)(i0 + ii) * g.w_si + (int64_t)(o0 + oo) * g.w_so] = v;
+        }
       }
     }
   }
@@ -305,8 +312,12 @@ hipError_t launch_mix_bwd_dx_g(const Geom& g, const int32_t* woff, const float2*
 
 hipError_t launch_mix_bwd_dw_g(const Geom& g, const int32_t* woff, const float2* xhat,
                                const float2* ghat, float2* dw, hipStream_t s) {
-  const dim3 grid((unsigned)((g.K + kMT - 1) / kMT), (unsigned)((g.Cin + 7) / 8),
-                  (unsigned)((g.Cout + 15) / 16));
+  // Cin tiles per work-group: about 1024 work-groups in all, at most every tile in one
+  const int64_t mg = (g.K + kMT - 1) / kMT, ot = (g.Cout + 15) / 16, itiles = (g.Cin + 7) / 8;
+  int64_t parts = (1024 + mg * ot - 1) / (mg * ot);
+  if (parts > itiles) parts = itiles;
+  if (parts < 1) parts = 1;
+  const dim3 grid((unsigned)mg, (unsigned)parts, (unsigned)ot);
   if (g.half == 2)
     hipLaunchKernelGGL((k_mix_mfma_dw<2>), grid, dim3(256), 0, s, g, woff, xhat, ghat, dw);
   else if (g.half == 1)
