@@ -38,6 +38,7 @@ EXPORTS = [
     "fno_spectral_conv_fwd", "fno_spectral_conv_bwd", "fno_block_fwd", "fno_block_bwd",
     "fno_block_fwd_mse", "fno_block_bwd_preact", "fno_pointwise_fwd", "fno_mse_workspace_bytes", "fno_mse_grad", "fno_mse_grad_scaled",
     "fno_tucker_order", "fno_tucker_create", "fno_tucker_destroy", "fno_tucker_query",
+    "fno_tucker_keep_intermediates", "fno_tucker_save_bytes",
     "fno_tucker_block_fwd", "fno_tucker_block_bwd", "fno_tucker_spectral_conv_fwd",
     "fno_tucker_spectral_conv_bwd", "fno_tucker_block_fwd_mse", "fno_tucker_block_bwd_preact",
     "fno_timing_enable", "fno_timing_select",
@@ -88,6 +89,8 @@ def _load():
                                      c_size_t]),
         "fno_tucker_create": (c_int, [P, POINTER(c_int32), POINTER(c_void_p)]),
         "fno_tucker_destroy": (c_int, [P]),
+        "fno_tucker_keep_intermediates": (c_int, [P, c_int]),
+        "fno_tucker_save_bytes": (c_int, [P, POINTER(c_size_t)]),
         "fno_tucker_query": (c_int, [P, POINTER(c_size_t), POINTER(c_int64), POINTER(c_int64),
                                      c_char_p, c_size_t]),
         "fno_tucker_block_fwd": (c_int, [P, P, P, POINTER(c_void_p), P, P, P, P, P, c_size_t,
@@ -504,6 +507,22 @@ class Tucker:
             t = self.plan.torch
             self._ws = t.empty(max(self.ws_bytes, 16), dtype=t.uint8, device=self.plan.device)
         return self._ws
+
+    def keep_intermediates(self, keep=True):
+        """Keep the forward's weight-step intermediates in the save buffer for the backward
+        (save buffers then come from new_save())."""
+        _check(_lib.fno_tucker_keep_intermediates(self.handle, 1 if keep else 0),
+               "fno_tucker_keep_intermediates")
+
+    @property
+    def save_bytes(self):
+        b = c_size_t()
+        _check(_lib.fno_tucker_save_bytes(self.handle, byref(b)), "fno_tucker_save_bytes")
+        return b.value
+
+    def new_save(self):
+        t = self.plan.torch
+        return t.empty(max(self.save_bytes, 16), dtype=t.uint8, device=self.plan.device)
 
     def block_fwd(self, x, core, factors, wb, bias=None, save=None, out=None):
         p = self.plan

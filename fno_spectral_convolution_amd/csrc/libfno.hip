@@ -918,6 +918,12 @@ struct fno_tucker {
   int64_t factor_elems[2 + fno::kMaxDims];
   std::vector<size_t> chain_off;            // result of each core step
   size_t g0_off, g1_off, x1_off, t2_off, u_off, v_off, part_off, total;
+  // with `keep`, the save buffer continues after the plan's part with the forward's weight-step
+  // intermediates (each core step's result, U_in xhat, the mix output before U_out), which the
+  // backward then reads instead of recomputing
+  bool keep = false;
+  std::vector<size_t> keep_chain_off;
+  size_t keep_x1_off = 0, keep_t2_off = 0, keep_total = 0;
 };
 
 namespace {
@@ -952,28 +958,37 @@ struct TuckerMix final : WeightMix {
   float2* grad_core;
   float* const* grad_fac;  // may be null (forward)
   bool want_w;
+  unsigned char* kept;     // the save buffer when it carries the kept intermediates, else null
   TuckerMix(const fno_tucker* t_, const float* core_, const float* const* fac_,
-            float* gcore, float* const* gfac)
+            float* gcore, float* const* gfac, const void* save = nullptr)
       : t(t_), core(f2c(core_)), fac(fac_), grad_core(reinterpret_cast<float2*>(gcore)),
         grad_fac(gfac) {
     want_w = grad_core != nullptr;
     for (int n = 0; gfac && n < t->nf; ++n) want_w = want_w || gfac[n] != nullptr;
+    kept = (t->keep && save) ? static_cast<unsigned char*>(const_cast<void*>(save)) : nullptr;
+  }
+  // the buffer of core step si's result: the save buffer's slot when kept
+  float2* chain_buf(void* ws, int si) const {
+    return kept ? reinterpret_cast<float2*>(kept + t->keep_chain_off[si])
+                : at<float2>(ws, t->chain_off[si]);
   }
   float2* gf(int n) const { return grad_fac ? reinterpret_cast<float2*>(grad_fac[n]) : nullptr; }
   bool wants_weight_grad() const override { return want_w; }
 
   // the core's lineage: every core step in order; in[si] = the input of step si
+  // compute: run the products (else the kept results of the forward are only pointed at)
   fno_status core_chain(void* ws, hipStream_t s, std::vector<const float2*>* in,
-                        const float2** H) const {
+                        const float2** H, bool compute = true) const {
     const float2* cur = core;
     int si = 0;
     for (const fno::TuckerStep& st : t->steps) {
       if (st.kind != fno::TuckerStep::CORE) continue;
-      float2* out = at<float2>(ws, t->chain_off[si]);
+      float2* out = chain_buf(ws, si);
       if (in) (*in)[si] = cur;
-      LAUNCH("tucker_core", s, fno::launch_mode_product(st.pre, st.an, st.cn, st.post,
-                                                        f2c(fac[st.factor]), false, false, cur,
-                                                        out, s));
+      if (compute)
+        LAUNCH("tucker_core", s, fno::launch_mode_product(st.pre, st.an, st.cn, st.post,
+                                                          f2c(fac[st.factor]), false, false,
+                                                          cur, out, s));
       cur = out;
       ++si;
     }
@@ -987,12 +1002,15 @@ struct TuckerMix final : WeightMix {
     if (st != FNO_OK) return st;
     const float2* data = xhat;
     if (t->in_on_data) {
-      float2* x1 = at<float2>(ws, t->x1_off);
+      float2* x1 = kept ? reinterpret_cast<float2*>(kept + t->keep_x1_off)
+                        : at<float2>(ws, t->x1_off);
       LAUNCH("tucker_data", s, fno::launch_mix_fwd_g(t->g_in, t->zero_woff, xhat, f2c(fac[0]),
                                                      x1, s));
       data = x1;
     }
-    float2* mixed = t->out_on_data ? at<float2>(ws, t->t2_off) : yhat;
+    float2* mixed = !t->out_on_data ? yhat
+                    : kept          ? reinterpret_cast<float2*>(kept + t->keep_t2_off)
+                                    : at<float2>(ws, t->t2_off);
     LAUNCH("tucker_mix_fwd", s, fno::launch_mix_fwd_g(t->gmix, t->ident_woff, data, H, mixed, s));
     if (t->out_on_data)
       LAUNCH("tucker_data", s, fno::launch_mix_fwd_g(t->g_out, t->zero_woff, mixed, f2c(fac[1]),
@@ -1007,7 +1025,7 @@ struct TuckerMix final : WeightMix {
     float2* part = at<float2>(ws, t->part_off);
     std::vector<const float2*> chain_in(t->core_steps, nullptr);
     const float2* H = nullptr;
-    fno_status st = core_chain(ws, s, &chain_in, &H);
+    fno_status st = core_chain(ws, s, &chain_in, &H, kept == nullptr);
     if (st != FNO_OK) return st;
     // u = ghat with U_out's conjugate applied (when U_out acts on the data side)
     const float2* u = ghat;
@@ -1020,7 +1038,9 @@ struct TuckerMix final : WeightMix {
     float2* gH = at<float2>(ws, t->g0_off);
     if (want_w) {
       const float2* data = xhat;
-      if (t->in_on_data) {
+      if (t->in_on_data && kept) {
+        data = reinterpret_cast<const float2*>(kept + t->keep_x1_off);
+      } else if (t->in_on_data) {
         float2* x1 = at<float2>(ws, t->x1_off);
         LAUNCH("tucker_data", s, fno::launch_mix_fwd_g(t->g_in, t->zero_woff, xhat, f2c(fac[0]),
                                                        x1, s));
@@ -1029,8 +1049,11 @@ struct TuckerMix final : WeightMix {
       // gradient of the core-side tensor the mix reads
       LAUNCH("tucker_mix_dw", s, fno::launch_mix_bwd_dw_g(t->gmix, t->ident_woff, data, u, gH, s));
       if (t->out_on_data && gf(1)) {
-        float2* t2 = at<float2>(ws, t->t2_off);
-        LAUNCH("tucker_mix_fwd", s, fno::launch_mix_fwd_g(t->gmix, t->ident_woff, data, H, t2, s));
+        float2* t2 = kept ? reinterpret_cast<float2*>(kept + t->keep_t2_off)
+                          : at<float2>(ws, t->t2_off);
+        if (!kept)
+          LAUNCH("tucker_mix_fwd", s,
+                 fno::launch_mix_fwd_g(t->gmix, t->ident_woff, data, H, t2, s));
         LAUNCH("tucker_gram_data", s, fno::launch_gram(d.B, d.Cout, d.R[1], t->K, ghat, t2, true,
                                                   g.mb, g.Nb, g.adj_scale, g.inv_gain[0], false,
                                                   part, gf(1), s));
@@ -1276,6 +1299,20 @@ fno_status fno_tucker_create(const fno_plan* p, const int32_t* ranks, fno_tucker
   t->u_off = take(t->out_on_data ? dR * d.R[1] : 0);
   t->part_off = take(fno::kTuckerPartElems);
   t->total = off;
+  {
+    size_t koff = align_up(p->save_bytes);
+    auto keep_take = [&](int64_t complex_elems) {
+      const size_t o = koff;
+      koff += align_up(sizeof(float2) * (size_t)complex_elems);
+      return o;
+    };
+    for (const fno::TuckerStep& stp : t->steps)
+      if (stp.kind == fno::TuckerStep::CORE)
+        t->keep_chain_off.push_back(keep_take(stp.pre * stp.an * stp.post));
+    t->keep_x1_off = keep_take(t->in_on_data ? dR * d.R[0] : 0);
+    t->keep_t2_off = keep_take(t->out_on_data ? dR * d.R[1] : 0);
+    t->keep_total = koff;
+  }
   // identity mode offsets (the core-side tensor [c_in][c_out][K] holds mode t at t), then
   // zero offsets (a factor matrix, the same for every mode)
   std::vector<int32_t> ident((size_t)(2 * t->K), 0);
@@ -1319,6 +1356,18 @@ fno_status fno_tucker_destroy(fno_tucker* t) {
   return e == hipSuccess ? FNO_OK : hip_fail(e, "fno_tucker_destroy");
 }
 
+fno_status fno_tucker_keep_intermediates(fno_tucker* t, int keep) {
+  if (!t) return fail(FNO_ERR_INVALID_ARGUMENT, "tucker is NULL");
+  t->keep = keep != 0;
+  return FNO_OK;
+}
+
+fno_status fno_tucker_save_bytes(const fno_tucker* t, size_t* bytes) {
+  if (!t || !bytes) return fail(FNO_ERR_INVALID_ARGUMENT, "tucker or bytes is NULL");
+  *bytes = t->keep ? t->keep_total : t->plan->save_bytes;
+  return FNO_OK;
+}
+
 fno_status fno_tucker_query(const fno_tucker* t, size_t* ws_bytes, int64_t* core_elems,
                             int64_t* factor_elems, char* order, size_t order_len) {
   if (!t) return fail(FNO_ERR_INVALID_ARGUMENT, "tucker is NULL");
@@ -1347,7 +1396,7 @@ fno_status fno_tucker_block_fwd(const fno_tucker* t, const float* x, const float
   if (p->desc.flags & FNO_FLAG_BIAS) REQ(bias, "bias");
   OPT(save, "save");
   return block_fwd_impl(p, x, wb, bias, y, save, ws, static_cast<hipStream_t>(stream),
-                        TuckerMix(t, core, factors, nullptr, nullptr));
+                        TuckerMix(t, core, factors, nullptr, nullptr, save));
 }
 
 fno_status fno_tucker_block_bwd(const fno_tucker* t, const float* x, const float* core,
@@ -1376,7 +1425,7 @@ fno_status fno_tucker_block_bwd(const fno_tucker* t, const float* x, const float
   OPT(save, "save");
   return block_bwd_impl(p, x, wb, save, gy, grad_x, grad_wb, grad_bias, ws,
                         static_cast<hipStream_t>(stream),
-                        TuckerMix(t, core, factors, grad_core, grad_factors));
+                        TuckerMix(t, core, factors, grad_core, grad_factors, save));
 }
 
 fno_status fno_tucker_block_fwd_mse(const fno_tucker* t, const float* x, const float* core,
@@ -1398,7 +1447,7 @@ fno_status fno_tucker_block_fwd_mse(const fno_tucker* t, const float* x, const f
     return fail(FNO_ERR_INVALID_ARGUMENT, "grad_scale must be finite and > 0");
   return block_fwd_mse_impl(p, x, wb, bias, target, grad_scale, grad_z, loss, save, ws,
                             static_cast<hipStream_t>(stream),
-                            TuckerMix(t, core, factors, nullptr, nullptr));
+                            TuckerMix(t, core, factors, nullptr, nullptr, save));
 }
 
 fno_status fno_tucker_block_bwd_preact(const fno_tucker* t, const float* x, const float* core,
@@ -1428,7 +1477,7 @@ fno_status fno_tucker_block_bwd_preact(const fno_tucker* t, const float* x, cons
   OPT(save, "save");
   return block_bwd_impl(p, x, wb, save, grad_z, grad_x, grad_wb, grad_bias, ws,
                         static_cast<hipStream_t>(stream),
-                        TuckerMix(t, core, factors, grad_core, grad_factors), true);
+                        TuckerMix(t, core, factors, grad_core, grad_factors, save), true);
 }
 
 fno_status fno_tucker_spectral_conv_fwd(const fno_tucker* t, const float* x, const float* core,
@@ -1440,7 +1489,7 @@ fno_status fno_tucker_spectral_conv_fwd(const fno_tucker* t, const float* x, con
   REQ(y_spec, "y_spec");
   OPT(save, "save");
   return spectral_fwd_impl(t->plan, x, y_spec, save, ws, static_cast<hipStream_t>(stream),
-                           TuckerMix(t, core, factors, nullptr, nullptr));
+                           TuckerMix(t, core, factors, nullptr, nullptr, save));
 }
 
 fno_status fno_tucker_spectral_conv_bwd(const fno_tucker* t, const float* x, const float* core,
@@ -1457,7 +1506,7 @@ fno_status fno_tucker_spectral_conv_bwd(const fno_tucker* t, const float* x, con
   OPT(grad_core, "grad_core");
   for (int n = 0; grad_factors && n < t->nf; ++n) OPT(grad_factors[n], "grad_factor");
   return spectral_bwd_impl(t->plan, x, save, gys, grad_x, ws, static_cast<hipStream_t>(stream),
-                           TuckerMix(t, core, factors, grad_core, grad_factors));
+                           TuckerMix(t, core, factors, grad_core, grad_factors, save));
 }
 
 fno_status fno_pointwise_fwd(int64_t batch, int64_t npts, int64_t cin, int64_t hidden,

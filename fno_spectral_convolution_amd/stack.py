@@ -98,8 +98,8 @@ class StackRunner:
         if wl.train:
             self.acts = [torch.empty(shape, dtype=torch.float32, device=dev)
                          for _ in range(nb + 1)]
-            self.saves = [self.block_plans[i].new_save() for i in range(nb)]
-            self._save_bytes = [self.block_plans[i].save_bytes for i in range(nb)]
+            self.saves = [self._saver(i).new_save() for i in range(nb)]
+            self._save_bytes = [self._saver(i).save_bytes for i in range(nb)]
             self.g = [torch.empty(shape, dtype=torch.float32, device=dev) for _ in range(2)]
             self.grads = []
             for p in self.params:
@@ -140,6 +140,8 @@ class StackRunner:
             if wl.tucker_ranks:
                 tk = L.Tucker(plan, wl.tucker_ranks)
                 tk.workspace()
+                if wl.train:  # the backward reads the forward's weight-step intermediates
+                    tk.keep_intermediates(True)
                 self._tuckers[key] = tk
             else:
                 plan.workspace()
@@ -163,10 +165,11 @@ class StackRunner:
             return
         self._use_precision(prec)
         if self.wl.train:
-            for i, plan in enumerate(self.block_plans):
-                if plan.save_bytes > self._save_bytes[i]:
-                    self.saves[i] = plan.new_save()
-                    self._save_bytes[i] = plan.save_bytes
+            for i in range(len(self.block_plans)):
+                sv = self._saver(i)
+                if sv.save_bytes > self._save_bytes[i]:
+                    self.saves[i] = sv.new_save()
+                    self._save_bytes[i] = sv.save_bytes
         self.precision = prec
         self.grad_scale = F16_LOSS_SCALE if prec == "f16" else 1.0
 
@@ -180,6 +183,11 @@ class StackRunner:
             if on_step is not None:
                 on_step(i, out)
         return out
+
+    def _saver(self, i):
+        """What sizes block i's save buffer: its Tucker weight (with the kept intermediates)
+        or its plan."""
+        return self.block_tuckers[i] if self.tucker else self.block_plans[i]
 
     def _act(self, i):
         return self.acts[i] if self.wl.train else self.acts[i % 2]

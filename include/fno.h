@@ -220,8 +220,18 @@ fno_status fno_tucker_query(const fno_tucker* tucker, size_t* workspace_bytes,
                             int64_t* core_elems, int64_t* factor_elems, char* order,
                             size_t order_len);
 
+/* Keep the weight step's intermediates for the backward (keep != 0; off after create): every
+ * Tucker call then takes save buffers of fno_tucker_save_bytes bytes, the plan's save followed
+ * by the forward's core-chain results, U_in applied to the spectrum and the mix output before
+ * U_out, which the backward reads instead of recomputing (its results are the same bits).  Off,
+ * save buffers are the plan's and the backward recomputes them.  A backward must see the same
+ * setting as the forward that filled its save buffer. */
+fno_status fno_tucker_keep_intermediates(fno_tucker* tucker, int keep);
+fno_status fno_tucker_save_bytes(const fno_tucker* tucker, size_t* bytes);
+
 /* fno_block_fwd with the Tucker weight (core + factors: a host array of d + 2 device
- * pointers, in the order U_in, U_out, U_0 .. U_{d-1}).  The save buffer is the plan's. */
+ * pointers, in the order U_in, U_out, U_0 .. U_{d-1}).  The save buffer is the plan's
+ * (fno_tucker_save_bytes with kept intermediates). */
 fno_status fno_tucker_block_fwd(const fno_tucker* tucker, const float* x, const float* core,
                                 const float* const* factors, const float* w_bypass,
                                 const float* bias, float* y, void* save, void* workspace,

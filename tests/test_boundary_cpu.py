@@ -91,6 +91,8 @@ def test_null_arguments_rejected_on_host():
             L.FNO_ERR_INVALID_ARGUMENT
     assert L._lib.fno_pointwise_fwd(1, 1, 1, 0, 300, None, None, None, None, None, None,
                                     None) == L.FNO_ERR_UNSUPPORTED
+    assert L._lib.fno_tucker_keep_intermediates(None, 1) == L.FNO_ERR_INVALID_ARGUMENT
+    assert L._lib.fno_tucker_save_bytes(None, None) == L.FNO_ERR_INVALID_ARGUMENT
     assert L._lib.fno_block_fwd_mse(None, None, None, None, None, None, 1.0, None, None, None,
                                     None, 0, None) == L.FNO_ERR_INVALID_ARGUMENT
     assert L._lib.fno_block_bwd_preact(None, None, None, None, None, None, None, None, None,

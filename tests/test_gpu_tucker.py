@@ -196,3 +196,47 @@ def test_tucker_fused_loss(L, case, prec):
     check("grad_bias", _host(gr["bias"]) / scale, refb["grad_bias"], tol)
     tk.close()
     plan.close()
+
+
+@pytest.mark.parametrize("prec", PRECISIONS[:2], ids=[p[0] for p in PRECISIONS[:2]])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_tucker_kept_intermediates(L, case, prec):
+    """fno_tucker_keep_intermediates: the backward reads the forward's core-chain results,
+    U_in xhat and the mix output from the save buffer instead of recomputing them; every output
+    is the same bits as without, for the plain and the loss-fused block."""
+    name, batch, cin, cout, grid, modes, ranks, _ = case
+    pname, mixed = prec
+    seed = 70 + zlib.crc32(name.encode()) % 1000
+    x, _, wb, b = inputs.small_case(seed, batch, cin, cout, grid, modes)
+    gy = inputs.normal_like(seed, (batch, cout) + grid)
+    core, facs = _tucker_params(seed, cin, cout, modes, ranks)
+    plan = L.Plan(batch, cin, cout, grid, modes, mixed=mixed)
+    tk = L.Tucker(plan, ranks)
+    announce("tucker kept", name, pname, tk.order)
+    tx, twb, tb, tg, tcore = (_dev(a) for a in (x, wb, b, gy, core))
+    tfac = [_dev(u) for u in facs]
+
+    def run():
+        save = tk.new_save()
+        y = tk.block_fwd(tx, tcore, tfac, twb, tb, save=save)
+        g = tk.block_bwd(tx, tcore, tfac, twb, tb, save, tg)
+        gz, loss = tk.block_fwd_mse(tx, tcore, tfac, twb, tb, tg, save=save)
+        gp = tk.block_bwd_preact(tx, tcore, tfac, twb, tb, save, gz)
+        _torch().cuda.synchronize()
+        out = {"y": _host(y), "gz": _host(gz), "loss": _host(loss)}
+        for tag, d in (("bwd", g), ("pre", gp)):
+            for k in ("x", "core", "wb", "bias"):
+                out[f"{tag}_{k}"] = _host(d[k])
+            for n, u in enumerate(d["factors"]):
+                out[f"{tag}_factor{n}"] = _host(u)
+        return out
+
+    plain_bytes = tk.save_bytes
+    plain = run()
+    tk.keep_intermediates(True)
+    assert tk.save_bytes > plain_bytes
+    kept = run()
+    for k in plain:
+        assert np.array_equal(plain[k], kept[k]), k
+    tk.close()
+    plan.close()
