@@ -88,7 +88,9 @@ def kernel_model(wl, plan):
     spec = B * C * K * 8
     wbytes = ncorner * C * C * Mprod * 8
     lines = P // Nb
-    T = B * C * lines * mb * 8
+    # the spectrum after the outer inverses: complex float32, or the half format on half plans
+    # of width 64 (the width-64 line epilogues take it so)
+    T = B * C * lines * mb * (4 if (wl.mixed and C == 64) else 8)
     O = P // (Na * Nb)
     plane_spec = B * C * O * 2 * ma * mb * 8
     dft_last = 4 * mb * U                      # real row -> mb complex bins (and back)

@@ -208,22 +208,28 @@ int epilogue_bwd_fast_groups(const fno_plan* p);
 // gz = msc (y - t) GELU'(z) (msc = grad_scale 2 / n; GELU' = 1 without the output GELU) and
 // one partial sum of (y - t)^2 per work-group into lpart (epilogue_fwd_fast_groups of them).
 int epilogue_fwd_fast_groups(const fno_plan* p);
-hipError_t launch_epilogue_fwd_mse(const fno_plan* p, const float2* T, const float* x,
+hipError_t launch_epilogue_fwd_mse(const fno_plan* p, const void* T, const float* x,
                                    const float* wb, const float* bias, const float* tgt,
-                                   float msc, float* gz, double* lpart, hipStream_t s);
-hipError_t launch_epilogue_fwd_fast(const fno_plan* p, int mode, const float2* T, const float* x,
+                                   float msc, float* gz, double* lpart, hipStream_t s,
+                                   bool t_half = false);
+// t_half: T is in the plan's half format (width 64, half operands; launch_outer_mfma_half)
+hipError_t launch_epilogue_fwd_fast(const fno_plan* p, int mode, const void* T, const float* x,
                                     const float* wb, const float* bias, float* y, float* zsave,
-                                    hipStream_t s);
-hipError_t launch_epilogue_bwd_fast(const fno_plan* p, int mode, const float2* Tg,
+                                    hipStream_t s, bool t_half = false);
+hipError_t launch_epilogue_bwd_fast(const fno_plan* p, int mode, const void* Tg,
                                     const float* x, const float* wb, const float* gy,
                                     const float* z, float* grad_x, float* red_part,
-                                    hipStream_t s);
+                                    hipStream_t s, bool t_half = false);
 bool plane_fast_ok(const fno_plan* p);
 hipError_t launch_plane_fwd_fast(const fno_plan* p, int plane_in, int chans, const float* in0,
                                  const float* in1, float2* out, hipStream_t s);
 bool outer_fast_ok(const fno_plan* p, int axis, bool inv);
 hipError_t launch_outer_mfma(const fno_plan* p, int axis, int chans, bool inv, const float2* in,
                              float2* out, hipStream_t s);
+// The inverse of outer axis `axis` written in the plan's half format (half plans, outer_fast_ok):
+// the rounding the matrix-core line epilogues apply to T when they stage it.
+hipError_t launch_outer_mfma_half(const fno_plan* p, int axis, int chans, const float2* in,
+                                  uint16_t* out, hipStream_t s);
 hipError_t launch_bypass_grad_finish(const fno_plan* p, const float* red_part, float* dwb,
                                      float* dbias, const float* grad_x, hipStream_t s);
 hipError_t launch_pointwise(int64_t batch, int64_t npts, int cin, int hidden, int cout,

@@ -24,6 +24,7 @@
 #include "pointwise.h"
 
 #include <math.h>
+#include <type_traits>
 
 namespace fno {
 
@@ -35,7 +36,7 @@ struct EpiArgs {
   int lpw;             // consecutive lines of one batch entry per work-group
   int gpl_log2;        // log2 of the point groups per line (Nb / 64)
   const float* x;
-  const float2* T;     // [B][C][lines][mb]
+  const void* T;       // [B][C][lines][mb] complex: float32, or the plan's half format (TH)
   const float* wb;     // [C][C] (o, i)
   const float* bias;   // [C] or null
   const void* gt;      // [Nb][kpad] f32 or half bits (the plan's format)
@@ -60,9 +61,11 @@ constexpr int kMaxKpad = 64;  // 2*mb padded; larger spectra take the generic ke
 
 // Stage the spectrum rows of one line (every channel, 2*mb floats) into LDS as the B operand
 // of the spectral product: bf16 [CP][kpad + 8] or f32 [CP][kpad + 4], zero padded.
-template <int C, int H>
-__device__ __forceinline__ void stage_line(const EpiArgs& a, const float2* Trow0,
-                                           unsigned char* tl, int tid) {
+// T0: complex index of channel 0's row of the line; TH: T holds the half format already (the
+// outer inverse rounded it as this staging would), so its bits are copied.
+template <int C, int H, bool TH>
+__device__ __forceinline__ void stage_line(const EpiArgs& a, int64_t T0, unsigned char* tl,
+                                           int tid) {
   constexpr bool BF = H != 0;
   constexpr int CP = (C + 15) / 16 * 16;
   constexpr int kst = kMaxKpad + (BF ? 8 : 4);
@@ -71,10 +74,17 @@ __device__ __forceinline__ void stage_line(const EpiArgs& a, const float2* Trow0
   constexpr int g4 = kMaxKpad / 4;  // columns kf_end .. kMaxKpad - 1 are written as zeros
   for (int e = tid; e < CP * g4; e += 256) {
     const int c = e / g4, k4 = 4 * (e - c * g4);
+    const int64_t off = 2 * (T0 + (int64_t)c * cstride) + k4;  // float (or half) units
+    if constexpr (TH) {
+      uint2 raw = make_uint2(0u, 0u);
+      if (c < C && k4 < kf_end) raw = *reinterpret_cast<const uint2*>(
+                                    static_cast<const uint16_t*>(a.T) + off);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(tl) + c * kst + k4) = raw;
+      continue;
+    }
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (c < C && k4 < kf_end)
-      v = *reinterpret_cast<const float4*>(
-          reinterpret_cast<const float*>(Trow0 + (int64_t)c * cstride) + k4);
+      v = *reinterpret_cast<const float4*>(static_cast<const float*>(a.T) + off);
     if (BF) {
       uint2 pk;
       pk.x = HalfOf<H>::pack2(v.x, v.y);
@@ -90,37 +100,45 @@ __device__ __forceinline__ void stage_line(const EpiArgs& a, const float2* Trow0
 // previous line is computed: float4 e = tid + 256 i is channel e / 16, columns 4 (e % 16) ..;
 // outside the spectrum (channel >= C or column >= 2 mb) a clamped address is loaded and zeros
 // are written.
-template <int C>
+template <int C, bool TH>
 struct LineT {
   static constexpr int CP = (C + 15) / 16 * 16;
   static constexpr int N = (CP * (kMaxKpad / 4) + 255) / 256;
-  float4 v[N];
+  std::conditional_t<TH, uint2, float4> v[N];  // 4 columns: half bits, or float32
 };
 
-template <int C>
-__device__ __forceinline__ void load_line(const EpiArgs& a, const float2* Trow0, LineT<C>& t,
+template <int C, bool TH>
+__device__ __forceinline__ void load_line(const EpiArgs& a, int64_t T0, LineT<C, TH>& t,
                                           int tid) {
   const int64_t cstride = a.lines * a.mb;
 #pragma unroll
-  for (int i = 0; i < LineT<C>::N; ++i) {
+  for (int i = 0; i < LineT<C, TH>::N; ++i) {
     const int e = tid + 256 * i;
     const int c = min(e >> 4, C - 1), k4 = min(4 * (e & 15), 2 * a.mb - 4);
-    t.v[i] = *reinterpret_cast<const float4*>(
-        reinterpret_cast<const float*>(Trow0 + (int64_t)c * cstride) + k4);
+    const int64_t off = 2 * (T0 + (int64_t)c * cstride) + k4;
+    if constexpr (TH)
+      t.v[i] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.T) + off);
+    else
+      t.v[i] = *reinterpret_cast<const float4*>(static_cast<const float*>(a.T) + off);
   }
 }
 
-template <int C, int H>
-__device__ __forceinline__ void write_line(const EpiArgs& a, const LineT<C>& t,
+template <int C, int H, bool TH>
+__device__ __forceinline__ void write_line(const EpiArgs& a, const LineT<C, TH>& t,
                                            unsigned char* tl, int tid) {
   constexpr bool BF = H != 0;
   constexpr int kst = kMaxKpad + (BF ? 8 : 4);
 #pragma unroll
-  for (int i = 0; i < LineT<C>::N; ++i) {
+  for (int i = 0; i < LineT<C, TH>::N; ++i) {
     const int e = tid + 256 * i;
-    if (e >= LineT<C>::CP * (kMaxKpad / 4)) break;
+    if (e >= LineT<C, TH>::CP * (kMaxKpad / 4)) break;
     const int c = e >> 4, k4 = 4 * (e & 15);
     const bool live = c < C && k4 < 2 * a.mb;
+    if constexpr (TH) {
+      const uint2 raw = live ? t.v[i] : make_uint2(0u, 0u);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(tl) + c * kst + k4) = raw;
+      continue;
+    } else {
     const float4 v = live ? t.v[i] : make_float4(0.f, 0.f, 0.f, 0.f);
     if (BF) {
       uint2 pk;
@@ -129,6 +147,7 @@ __device__ __forceinline__ void write_line(const EpiArgs& a, const LineT<C>& t,
       *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(tl) + c * kst + k4) = pk;
     } else {
       *reinterpret_cast<float4*>(reinterpret_cast<float*>(tl) + c * kst + k4) = v;
+    }
     }
   }
 }
@@ -225,7 +244,7 @@ __device__ __forceinline__ void load_rows(float4 (&v)[NPT], const float* base, i
 // 16 (with 1) for the fused MSE loss: the target rows of a step are loaded at its start and
 // the store phase writes msc (y - t) GELU'(z) in place of y, and adds (y - t)^2 to a per-thread
 // sum, reduced over the work-group in a fixed order into one partial at the end.
-template <int C, int H, int MODE, int G>
+template <int C, int H, int MODE, int G, bool TH>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C == 64 ? 3 : 4)))
 k_epi_fwd_line(EpiArgs a) {
   constexpr bool BF = H != 0;  // half operands (bfloat16 or IEEE half)
@@ -300,17 +319,17 @@ k_epi_fwd_line(EpiArgs a) {
   // narrow fields have few steps per line: the next line's spectrum rows stream in while
   // this one is computed (the last line re-loads itself); wide ones stage each line directly
   constexpr bool LPF = C < 64;
-  const float2* Tb = a.T + ((int64_t)b * C * a.lines + l0) * a.mb;
-  LineT<LPF ? C : 16> tln;
-  if constexpr (LPF) load_line<C>(a, Tb, tln, tid);
+  const int64_t Tb = ((int64_t)b * C * a.lines + l0) * a.mb;  // complex index of this range
+  LineT<LPF ? C : 16, TH> tln;
+  if constexpr (LPF) load_line<C, TH>(a, Tb, tln, tid);
   constexpr int kst = kMaxKpad + (BF ? 8 : 4);
   for (int lf = 0; lf < a.lpw; ++lf) {
     // every reader of the previous line's spectrum is past that line's last barrier
     if constexpr (LPF) {
-      write_line<C, H>(a, tln, s_tl, tid);
-      load_line<C>(a, Tb + (int64_t)min(lf + 1, a.lpw - 1) * a.mb, tln, tid);
+      write_line<C, H, TH>(a, tln, s_tl, tid);
+      load_line<C, TH>(a, Tb + (int64_t)min(lf + 1, a.lpw - 1) * a.mb, tln, tid);
     } else {
-      stage_line<C, H>(a, Tb + (int64_t)lf * a.mb, s_tl, tid);
+      stage_line<C, H, TH>(a, Tb + (int64_t)lf * a.mb, s_tl, tid);
     }
     for (int g = 0; g < gpl; ++g) {
       const int f = (lf << a.gpl_log2) + g;
@@ -462,7 +481,7 @@ k_epi_fwd_line(EpiArgs a) {
 // MODE: 1 spectral part only (grad_x = s(x) * spectral), 3 block, 7 block with GELU' (z read);
 // plus 8 when x is a pre-activation: the x tile holds the block's input GELU(x) (for dWb and
 // the tanh factor), a second tile GELU'(x), which multiplies the grad tile as it is stored.
-template <int C, int H, bool TANH, int MODE, int G>
+template <int C, int H, bool TANH, int MODE, int G, bool TH>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C == 64 ? 2 : 3)))
 k_epi_bwd_line(EpiArgs a) {
   constexpr bool BF = H != 0;  // half operands (bfloat16 or IEEE half)
@@ -543,17 +562,17 @@ k_epi_bwd_line(EpiArgs a) {
   }
   load_gt<G, H, true, MT>(a, 0, tbase, m, q, gtf);
   constexpr bool LPF = C < 64;
-  const float2* Tb = a.T + ((int64_t)b * C * a.lines + l0) * a.mb;
-  LineT<LPF ? C : 16> tln;
-  if constexpr (LPF) load_line<C>(a, Tb, tln, tid);
+  const int64_t Tb = ((int64_t)b * C * a.lines + l0) * a.mb;  // complex index of this range
+  LineT<LPF ? C : 16, TH> tln;
+  if constexpr (LPF) load_line<C, TH>(a, Tb, tln, tid);
   constexpr int kst = kMaxKpad + (BF ? 8 : 4);
   for (int lf = 0; lf < a.lpw; ++lf) {
     // every reader of the previous line's spectrum is past that line's last barrier
     if constexpr (LPF) {
-      write_line<C, H>(a, tln, s_tl, tid);
-      load_line<C>(a, Tb + (int64_t)min(lf + 1, a.lpw - 1) * a.mb, tln, tid);
+      write_line<C, H, TH>(a, tln, s_tl, tid);
+      load_line<C, TH>(a, Tb + (int64_t)min(lf + 1, a.lpw - 1) * a.mb, tln, tid);
     } else {
-      stage_line<C, H>(a, Tb + (int64_t)lf * a.mb, s_tl, tid);
+      stage_line<C, H, TH>(a, Tb + (int64_t)lf * a.mb, s_tl, tid);
     }
     for (int g = 0; g < gpl; ++g) {
       const int f = (lf << a.gpl_log2) + g;
@@ -734,10 +753,34 @@ k_epi_bwd_line(EpiArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
+// th: T arrives in the half format (width 64 with half operands only)
 template <int C, int G>
-static hipError_t launch_fwd_c(const EpiArgs& a, int half, int mode, int wgs, hipStream_t s) {
+static hipError_t launch_fwd_c(const EpiArgs& a, int half, int mode, int wgs, hipStream_t s,
+                               bool th = false) {
+  if constexpr (C == 64 && G == 1) {
+    if (th && half != 0) {
 #define FNO_EPI_FWD(HV, MV) \
-  hipLaunchKernelGGL((k_epi_fwd_line<C, HV, MV, G>), dim3(wgs), dim3(256), 0, s, a)
+  hipLaunchKernelGGL((k_epi_fwd_line<C, HV, MV, G, true>), dim3(wgs), dim3(256), 0, s, a)
+#define FNO_EPI_FWD_M(HV)                   \
+  do {                                      \
+    if (mode == 0) FNO_EPI_FWD(HV, 0);        \
+    else if (mode == 1) FNO_EPI_FWD(HV, 1);   \
+    else if (mode == 2) FNO_EPI_FWD(HV, 2);   \
+    else if (mode == 9) FNO_EPI_FWD(HV, 9);   \
+    else if (mode == 10) FNO_EPI_FWD(HV, 10); \
+    else if (mode == 17) FNO_EPI_FWD(HV, 17); \
+    else FNO_EPI_FWD(HV, 25);                 \
+  } while (0)
+      if (half == 2) FNO_EPI_FWD_M(2);
+      else FNO_EPI_FWD_M(1);
+#undef FNO_EPI_FWD_M
+#undef FNO_EPI_FWD
+      return hipGetLastError();
+    }
+  }
+  if (th) return hipErrorInvalidValue;
+#define FNO_EPI_FWD(HV, MV) \
+  hipLaunchKernelGGL((k_epi_fwd_line<C, HV, MV, G, false>), dim3(wgs), dim3(256), 0, s, a)
 #define FNO_EPI_FWD_M(HV)                   \
   do {                                      \
     if (mode == 0) FNO_EPI_FWD(HV, 0);        \
@@ -758,9 +801,35 @@ static hipError_t launch_fwd_c(const EpiArgs& a, int half, int mode, int wgs, hi
 
 template <int C, int G>
 static hipError_t launch_bwd_c(const EpiArgs& a, int half, bool tanh_pre, int mode, int wgs,
-                               hipStream_t s) {
+                               hipStream_t s, bool th = false) {
+  if constexpr (C == 64 && G == 1) {
+    if (th && half != 0) {
 #define FNO_EPI_BWD(BFV, TV, MV) \
-  hipLaunchKernelGGL((k_epi_bwd_line<C, BFV, TV, MV, G>), dim3(wgs), dim3(256), 0, s, a)
+  hipLaunchKernelGGL((k_epi_bwd_line<C, BFV, TV, MV, G, true>), dim3(wgs), dim3(256), 0, s, a)
+#define FNO_EPI_BWD_M(BFV, TV)                   \
+  do {                                           \
+    if (mode == 1) FNO_EPI_BWD(BFV, TV, 1);        \
+    else if (mode == 3) FNO_EPI_BWD(BFV, TV, 3);   \
+    else if (mode == 7) FNO_EPI_BWD(BFV, TV, 7);   \
+    else if (mode == 9) FNO_EPI_BWD(BFV, TV, 9);   \
+    else if (mode == 11) FNO_EPI_BWD(BFV, TV, 11); \
+    else FNO_EPI_BWD(BFV, TV, 15);                 \
+  } while (0)
+      if (half == 2) {
+        if (tanh_pre) FNO_EPI_BWD_M(2, true);
+        else FNO_EPI_BWD_M(2, false);
+      } else {
+        if (tanh_pre) FNO_EPI_BWD_M(1, true);
+        else FNO_EPI_BWD_M(1, false);
+      }
+#undef FNO_EPI_BWD_M
+#undef FNO_EPI_BWD
+      return hipGetLastError();
+    }
+  }
+  if (th) return hipErrorInvalidValue;
+#define FNO_EPI_BWD(BFV, TV, MV) \
+  hipLaunchKernelGGL((k_epi_bwd_line<C, BFV, TV, MV, G, false>), dim3(wgs), dim3(256), 0, s, a)
 #define FNO_EPI_BWD_M(BFV, TV)                  \
   do {                                          \
     if (mode == 1) FNO_EPI_BWD(BFV, TV, 1);       \
@@ -829,21 +898,23 @@ static EpiArgs fwd_args(const fno_plan* p, int* G, int64_t* wgs) {
 }
 
 static hipError_t launch_fwd_any(const fno_plan* p, const EpiArgs& a, int G, int kmode,
-                                 int64_t wgs, hipStream_t s) {
+                                 int64_t wgs, hipStream_t s, bool th = false) {
   const Geom& g = p->g;
   if (wgs > 0x7fffffff) return hipErrorInvalidValue;
   if (G == 2) {
     switch (g.Cout) {
-      case 16: return launch_fwd_c<16, 2>(a, g.half, kmode, (int)wgs, s);
+      case 16: if (th) return hipErrorInvalidValue;
+             return launch_fwd_c<16, 2>(a, g.half, kmode, (int)wgs, s);
       case 20: return launch_fwd_c<20, 2>(a, g.half, kmode, (int)wgs, s);
       default: return launch_fwd_c<32, 2>(a, g.half, kmode, (int)wgs, s);
     }
   }
   switch (g.Cout) {
-    case 16: return launch_fwd_c<16, 1>(a, g.half, kmode, (int)wgs, s);
+    case 16: if (th) return hipErrorInvalidValue;
+             return launch_fwd_c<16, 1>(a, g.half, kmode, (int)wgs, s);
     case 20: return launch_fwd_c<20, 1>(a, g.half, kmode, (int)wgs, s);
     case 32: return launch_fwd_c<32, 1>(a, g.half, kmode, (int)wgs, s);
-    default: return launch_fwd_c<64, 1>(a, g.half, kmode, (int)wgs, s);
+    default: return launch_fwd_c<64, 1>(a, g.half, kmode, (int)wgs, s, th);
   }
 }
 
@@ -855,9 +926,9 @@ int epilogue_fwd_fast_groups(const fno_plan* p) {
   return wgs > 0x7fffffff ? 0 : (int)wgs;
 }
 
-hipError_t launch_epilogue_fwd_fast(const fno_plan* p, int mode, const float2* T, const float* x,
+hipError_t launch_epilogue_fwd_fast(const fno_plan* p, int mode, const void* T, const float* x,
                                     const float* wb, const float* bias, float* y, float* zsave,
-                                    hipStream_t s) {
+                                    hipStream_t s, bool t_half) {
   int G = 1;
   int64_t wgs = 0;
   EpiArgs a = fwd_args(p, &G, &wgs);
@@ -871,12 +942,13 @@ hipError_t launch_epilogue_fwd_fast(const fno_plan* p, int mode, const float2* T
   const bool ig = (p->desc.flags & FNO_FLAG_INPUT_GELU) != 0;
   const int kmode = mode == EPI_SPECTRAL ? 0 : ((zsave ? 2 : 1) | (ig ? 8 : 0));
   a.block = kmode != 0;
-  return launch_fwd_any(p, a, G, kmode, wgs, s);
+  return launch_fwd_any(p, a, G, kmode, wgs, s, t_half);
 }
 
-hipError_t launch_epilogue_fwd_mse(const fno_plan* p, const float2* T, const float* x,
+hipError_t launch_epilogue_fwd_mse(const fno_plan* p, const void* T, const float* x,
                                    const float* wb, const float* bias, const float* tgt,
-                                   float msc, float* gz, double* lpart, hipStream_t s) {
+                                   float msc, float* gz, double* lpart, hipStream_t s,
+                                   bool t_half) {
   int G = 1;
   int64_t wgs = 0;
   EpiArgs a = fwd_args(p, &G, &wgs);
@@ -892,7 +964,7 @@ hipError_t launch_epilogue_fwd_mse(const fno_plan* p, const float2* T, const flo
   const bool ig = (p->desc.flags & FNO_FLAG_INPUT_GELU) != 0;
   const int kmode = 1 | 16 | (ig ? 8 : 0);
   a.block = 1;
-  return launch_fwd_any(p, a, G, kmode, wgs, s);
+  return launch_fwd_any(p, a, G, kmode, wgs, s, t_half);
 }
 
 // Lines per backward work-group: each work-group writes one row of bypass-gradient partials,
@@ -911,10 +983,10 @@ int epilogue_bwd_fast_groups(const fno_plan* p) {
   return (int)((int64_t)p->g.B * lines / bwd_lines_per_wg(lines, p->g.B));
 }
 
-hipError_t launch_epilogue_bwd_fast(const fno_plan* p, int mode, const float2* Tg,
+hipError_t launch_epilogue_bwd_fast(const fno_plan* p, int mode, const void* Tg,
                                     const float* x, const float* wb, const float* gy,
                                     const float* z, float* grad_x, float* red_part,
-                                    hipStream_t s) {
+                                    hipStream_t s, bool t_half) {
   const Geom& g = p->g;
   EpiArgs a{};
   a.B = g.B;
@@ -946,10 +1018,13 @@ hipError_t launch_epilogue_bwd_fast(const fno_plan* p, int mode, const float2* T
   const int64_t wgs = (int64_t)g.B * a.lines / a.lpw;
   if (wgs > 0x7fffffff) return hipErrorInvalidValue;
   switch (g.Cin) {
-    case 16: return launch_bwd_c<16, 1>(a, g.half, tanh_pre, kmode, (int)wgs, s);
-    case 20: return launch_bwd_c<20, 1>(a, g.half, tanh_pre, kmode, (int)wgs, s);
-    case 32: return launch_bwd_c<32, 1>(a, g.half, tanh_pre, kmode, (int)wgs, s);
-    default: return launch_bwd_c<64, 1>(a, g.half, tanh_pre, kmode, (int)wgs, s);
+    case 16: if (t_half) return hipErrorInvalidValue;
+             return launch_bwd_c<16, 1>(a, g.half, tanh_pre, kmode, (int)wgs, s);
+    case 20: if (t_half) return hipErrorInvalidValue;
+             return launch_bwd_c<20, 1>(a, g.half, tanh_pre, kmode, (int)wgs, s);
+    case 32: if (t_half) return hipErrorInvalidValue;
+             return launch_bwd_c<32, 1>(a, g.half, tanh_pre, kmode, (int)wgs, s);
+    default: return launch_bwd_c<64, 1>(a, g.half, tanh_pre, kmode, (int)wgs, s, t_half);
   }
 }
 

@@ -24,6 +24,7 @@ struct OuterArgs {
   const uint16_t* Alo;   // bf16 residual (bf16 path)
   int64_t pre;           // slabs
   int msplit, mt_per;    // k_outer_mfma: work-groups per slab, output row tiles of each
+  uint16_t* outh;        // k_outer_mfma: the output in the plan's half format instead, or null
 };
 
 template <int H, int NT>
@@ -129,6 +130,27 @@ __global__ void __launch_bounds__(256) k_outer_mfma(OuterArgs a) {
     }
     // lane (n = m, q): rows 16 mt + 4 q + r, columns c0 + NT m + nt (nt = 0 .. NT-1)
     const int64_t col = c0 + NT * m;
+    if constexpr (BF && NT == 4) {
+      if (a.outh) {
+        // rounded to the half format here (nearest even), as its consumer would round it
+        uint16_t* dh = a.outh + pre * a.Lout * a.post2;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int p = 16 * mt + 4 * q + r;
+          if (p >= a.Lout) continue;
+          uint16_t* d = dh + (int64_t)p * a.post2 + col;
+          if (col + 4 <= a.post2 && (a.post2 % 4) == 0) {
+            *reinterpret_cast<uint2*>(d) = make_uint2(HalfOf<H>::pack2(acc[0][r], acc[1][r]),
+                                                      HalfOf<H>::pack2(acc[2][r], acc[3][r]));
+          } else {
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+              if (col + nt < a.post2) d[nt] = HalfOf<H>::bits(acc[nt][r]);
+          }
+        }
+        continue;
+      }
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int p = 16 * mt + 4 * q + r;
@@ -551,6 +573,9 @@ static hipError_t launch_outer_stream(int mt, int ntw, dim3 grid, const OuterArg
 
 static int pad16(int v) { return (v + 15) / 16 * 16; }
 
+static hipError_t launch_outer_generic(const fno_plan* p, OuterArgs a, int64_t pre,
+                                       hipStream_t s);
+
 // pre/post of the transform of axis j (see the generic kernel) and the launch
 hipError_t launch_outer_mfma(const fno_plan* p, int axis, int chans, bool inv, const float2* in,
                              float2* out, hipStream_t s) {
@@ -604,10 +629,20 @@ hipError_t launch_outer_mfma(const fno_plan* p, int axis, int chans, bool inv, c
     dim3 grid((unsigned)((a.post2 + cb - 1) / cb), (unsigned)pre);
     return launch_outer_stream(mt, ntw, grid, a, g.half, s);
   }
+  return launch_outer_generic(p, a, pre, s);
+}
+
+// k_outer_mfma for the arguments of launch_outer_mfma: column tiles of 64, 32 or 16, and the
+// output rows of few slabs split over up to msplit work-groups
+static hipError_t launch_outer_generic(const fno_plan* p, OuterArgs a, int64_t pre,
+                                       hipStream_t s) {
+  const Geom& g = p->g;
+  const bool bf = g.bf16;
   const int KS = 2 * a.Lin_pad + (bf ? 8 : 4);
   const size_t col_bytes = (size_t)KS * (bf ? 2 : 4);
   int nt = a.post2 >= 64 ? 4 : (a.post2 >= 32 ? 2 : 1);
   while (nt > 1 && (size_t)16 * nt * col_bytes > 64 * 1024) nt /= 2;
+  if (a.outh && nt != 4) return hipErrorInvalidValue;  // the half output needs 4-column lanes
   const int ct = 16 * nt;
   const size_t lds = (size_t)ct * col_bytes;
   const int64_t ctiles = (a.post2 + ct - 1) / ct;
@@ -635,6 +670,30 @@ hipError_t launch_outer_mfma(const fno_plan* p, int axis, int chans, bool inv, c
     else hipLaunchKernelGGL((k_outer_mfma<0, 1>), grid, dim3(256), lds, s, a);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_outer_mfma_half(const fno_plan* p, int axis, int chans, const float2* in,
+                                  uint16_t* out, hipStream_t s) {
+  const Geom& g = p->g;
+  if (!g.bf16) return hipErrorInvalidValue;
+  int64_t pre = (int64_t)g.B * chans;
+  for (int i = 0; i < axis; ++i) pre *= g.N[i];
+  int64_t post = g.mb;
+  for (int i = axis + 1; i <= g.d - 2; ++i) post *= 2 * g.M[i];
+  OuterArgs a{};
+  const int N = g.N[axis], m2 = 2 * g.M[axis];
+  a.Lin = m2;
+  a.Lout = N;
+  a.Lin_pad = pad16(a.Lin);
+  a.Lout_pad = pad16(a.Lout);
+  a.post2 = 2 * post;
+  a.in = reinterpret_cast<const float*>(in);
+  a.out = nullptr;
+  a.outh = out;
+  a.A = (const void*)p->t.oinv_bf[axis];
+  a.Alo = p->t.oinv_bf_lo[axis];
+  if (a.post2 < 64) return hipErrorInvalidValue;
+  return launch_outer_generic(p, a, pre, s);
 }
 
 bool outer_fast_ok(const fno_plan* p, int axis, bool inv) {

@@ -676,18 +676,32 @@ fno_status forward_transform(const fno_plan* p, int plane_in, int chans, const f
 // Inverse transform of the outer axes 0..naxes-1 of a spectrum [B][chans][K]: all of
 // 0..d-2 (naxes = d-1) gives T [B][chans][lines][mb]; returns the buffer holding the result
 // (src itself when naxes = 0).
+// half_last: the last axis's result in the plan's half format (see half_T).
 fno_status inverse_outer(const fno_plan* p, int chans, const float2* src, void* ws,
-                         hipStream_t s, const float2** T, int naxes) {
+                         hipStream_t s, const float2** T, int naxes, bool half_last = false) {
   float2* ping = at<float2>(ws, p->ws.spec_a);
   float2* pong = at<float2>(ws, p->ws.spec_b);
   const float2* cur = src;
   for (int j = 0; j < naxes; ++j) {
     float2* nxt = (cur == ping) ? pong : ping;
-    LAUNCH("outer_inv", s, fno::launch_outer_inv(p, j, chans, cur, nxt, s));
+    if (half_last && j == naxes - 1)
+      LAUNCH("outer_inv", s, fno::launch_outer_mfma_half(p, j, chans, cur,
+                                                         reinterpret_cast<uint16_t*>(nxt), s));
+    else
+      LAUNCH("outer_inv", s, fno::launch_outer_inv(p, j, chans, cur, nxt, s));
     cur = nxt;
   }
   *T = cur;
   return FNO_OK;
+}
+
+// T (the spectrum after the outer inverses) goes to the width-64 matrix-core line epilogue of a
+// half plan in that plan's half format: the epilogue rounds T to it when it stages a line, so
+// the outer inverse rounds it instead (the same bits) and T's bytes halve.
+bool half_T(const fno_plan* p, int chans) {
+  const fno::Geom& g = p->g;
+  return g.bf16 && chans == 64 && g.d >= 2 && fno::outer_fast_ok(p, g.d - 2, true) &&
+         2 * g.mb >= 64;
 }
 
 fno_status check_ws(const fno_plan* p, void* ws, size_t ws_bytes) {
@@ -750,10 +764,16 @@ fno_status block_epilogue_fwd(const fno_plan* p, int mode, const float2* yhat, c
            fno::launch_epilogue_rows(p, mode, T, x, wb, bias, y, zsave, s));
     return FNO_OK;
   }
-  st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T, p->g.d - 1);
+  const bool fast = fno::epilogue_fast_ok(p, mode, true);
+  const bool th = fast && half_T(p, p->g.Cout);
+  st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T, p->g.d - 1, th);
   if (st != FNO_OK) return st;
-  LAUNCH(zsave ? "epilogue_fwd_zsave" : "epilogue_fwd", s,
-         fno::launch_epilogue_fwd(p, mode, T, x, wb, bias, y, zsave, s));
+  if (fast)
+    LAUNCH(zsave ? "epilogue_fwd_zsave" : "epilogue_fwd", s,
+           fno::launch_epilogue_fwd_fast(p, mode, T, x, wb, bias, y, zsave, s, th));
+  else
+    LAUNCH(zsave ? "epilogue_fwd_zsave" : "epilogue_fwd", s,
+           fno::launch_epilogue_fwd(p, mode, T, x, wb, bias, y, zsave, s));
   return FNO_OK;
 }
 
@@ -791,11 +811,12 @@ fno_status block_fwd_mse_impl(const fno_plan* p, const float* x, const float* wb
   int nparts = fno::kMseParts;
   if (fno::epilogue_fast_ok(p, fno::EPI_BLOCK, true)) {
     const float2* T = nullptr;
-    st = inverse_outer(p, g.Cout, yhat, ws, s, &T, g.d - 1);
+    const bool th = half_T(p, g.Cout);
+    st = inverse_outer(p, g.Cout, yhat, ws, s, &T, g.d - 1, th);
     if (st != FNO_OK) return st;
     const float msc = (float)(2.0 * (double)grad_scale / (double)n);
     LAUNCH("epilogue_fwd_mse", s,
-           fno::launch_epilogue_fwd_mse(p, T, x, wb, bias, tgt, msc, grad_z, lpart, s));
+           fno::launch_epilogue_fwd_mse(p, T, x, wb, bias, tgt, msc, grad_z, lpart, s, th));
     nparts = fno::epilogue_fwd_fast_groups(p);
   } else {
     st = block_epilogue_fwd(p, fno::EPI_BLOCK_PREACT, yhat, x, wb, bias, grad_z, nullptr, ws, s);
@@ -828,13 +849,20 @@ fno_status block_bwd_impl(const fno_plan* p, const float* x, const float* wb, co
   float* red = (grad_wb || grad_bias) ? at<float>(ws, p->ws.red_part) : nullptr;
   if (grad_x || red) {
     const float2* Tg = nullptr;
+    const bool fast = fno::epilogue_bwd_fast(p, fno::EPI_BLOCK, grad_x);
+    const bool th = fast && half_T(p, g.Cin);
     if (grad_x) {
-      st = inverse_outer(p, g.Cin, ghx, ws, s, &Tg, g.d - 1);
+      st = inverse_outer(p, g.Cin, ghx, ws, s, &Tg, g.d - 1, th);
       if (st != FNO_OK) return st;
     }
     // with the output GELU the epilogue also reads z (another field)
-    LAUNCH(z ? "epilogue_bwd_gelu" : "epilogue_bwd", s,
-           fno::launch_epilogue_bwd(p, fno::EPI_BLOCK, Tg, x, wb, gy, z, grad_x, red, s));
+    if (fast)
+      LAUNCH(z ? "epilogue_bwd_gelu" : "epilogue_bwd", s,
+             fno::launch_epilogue_bwd_fast(p, fno::EPI_BLOCK, Tg, x, wb, gy, z, grad_x, red, s,
+                                           th));
+    else
+      LAUNCH(z ? "epilogue_bwd_gelu" : "epilogue_bwd", s,
+             fno::launch_epilogue_bwd(p, fno::EPI_BLOCK, Tg, x, wb, gy, z, grad_x, red, s));
     if (red)
       LAUNCH("bypass_grad_finish", s, fno::launch_bypass_grad_finish(p, red, grad_wb, grad_bias, grad_x, s));
   }
