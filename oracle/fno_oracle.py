@@ -79,7 +79,8 @@ __all__ = [
     "retained_indices", "dft_matrix", "gamma_weights", "spectrum", "expand_weights",
     "fold_weights", "channel_mix", "inverse_spectrum", "inverse_at_points", "adjoint_inverse",
     "gelu",
-    "gelu_prime", "spectral_conv_fwd", "spectral_conv_bwd", "block_fwd", "block_bwd",
+    "gelu_prime", "spectral_conv_fwd", "spectral_conv_bwd", "block_fwd", "block_at_points",
+    "block_bwd",
     "pointwise_linear", "projection_fwd", "mse_loss_grad", "stack_fwd", "train_step",
     "mode_product", "tucker_to_full", "tucker_block_fwd", "tucker_block_bwd", "tucker_grads",
     "tucker_spectral_conv_fwd", "tucker_spectral_conv_bwd",
@@ -327,6 +328,29 @@ def block_fwd(x, w, wb, bias, modes, tanh: bool = False, act: bool = True,
     out["z"] = z
     out["y"] = gelu(z) if act else z
     return out
+
+
+def block_at_points(x, w, wb, bias, modes, points, tanh: bool = False, act: bool = True,
+                    input_gelu: bool = False):
+    """F1-F4 evaluated only at given grid points: the spectrum of the whole field (F1, F2),
+    then F3 by ``inverse_at_points`` and the bypass, bias and GELU of F4 at those points alone.
+
+    For fields too large to invert whole (the 4D space-time share).  ``points`` is an int
+    array [P, d]; returns dict(y_spec, z, y), each [B, Cout, P].
+    """
+    x = gelu(x) if input_gelu else np.asarray(x)
+    grid = x.shape[2:]
+    xp = np.tanh(np.asarray(x, dtype=np.float64)) if tanh else x
+    yhat = channel_mix(spectrum(xp, modes), w, modes)
+    del xp
+    pts = np.asarray(points, dtype=np.int64)
+    y_spec = inverse_at_points(yhat, grid, modes, pts)
+    flat = np.ravel_multi_index(tuple(pts.T), grid)
+    xs = x.reshape(x.shape[0], x.shape[1], -1)[:, :, flat].astype(np.float64)
+    z = y_spec + _pointwise(wb, xs)
+    if bias is not None:
+        z = z + _bcast(bias, 3)
+    return {"y_spec": y_spec, "z": z, "y": gelu(z) if act else z}
 
 
 def block_bwd(x, w, wb, bias, modes, g_y, tanh: bool = False, act: bool = True,

@@ -609,6 +609,59 @@ def check_tucker_block_finite_differences(O):
                     assert abs(num - ana) < 1e-6 * max(1, abs(num)), (what, n, idx, num, ana)
 
 
+
+def check_pointwise_lift_projection(O):
+    """The lift (1x1 linear layer with bias) and the projection head (Linear, GELU, Linear)
+    evaluated point by point with explicit loops and math.erf."""
+    g = _rng(170)
+    b, cin, hid, cout = 2, 3, 5, 2
+    grid = (3, 4)
+    x = g.standard_normal((b, cin) + grid)
+    w1 = g.standard_normal((hid, cin))
+    b1 = g.standard_normal(hid)
+    w2 = g.standard_normal((cout, hid))
+    b2 = g.standard_normal(cout)
+    lift = O.pointwise_linear(x, w1, b1)
+    proj = O.projection_fwd(x, w1, b1, w2, b2)
+    for bi in range(b):
+        for p0 in range(grid[0]):
+            for p1 in range(grid[1]):
+                h = []
+                for k in range(hid):
+                    a = b1[k] + sum(w1[k, i] * x[bi, i, p0, p1] for i in range(cin))
+                    assert abs(lift[bi, k, p0, p1] - a) < 1e-13 * max(1.0, abs(a)), ("lift", k)
+                    h.append(0.5 * a * (1.0 + math.erf(a / math.sqrt(2.0))))
+                for o in range(cout):
+                    want = b2[o] + sum(w2[o, k] * h[k] for k in range(hid))
+                    got = proj[bi, o, p0, p1]
+                    assert abs(got - want) < 1e-13 * max(1.0, abs(want)), ("projection", o)
+    assert np.array_equal(O.pointwise_linear(x, w1, None),
+                          O.pointwise_linear(x, w1, np.zeros(hid)))
+
+
+def check_block_at_points(O):
+    """The point-wise block (spectrum, mix, point-wise inverse, bypass, bias, GELU at sampled
+    points only) equals the whole-field block at those points: 2D, 3D and 4D, with and without
+    tanh and input GELU."""
+    cases = [((8, 10), (3, 4), False, False), ((6, 8, 10), (2, 3, 4), True, False),
+             ((4, 6, 4, 8), (2, 2, 1, 3), False, True)]
+    for gi, (grid, modes, tanh, ig) in enumerate(cases):
+        g = _rng(180 + gi)
+        d = len(grid)
+        cin, cout = 3, 2
+        x = g.standard_normal((2, cin) + grid)
+        w = _rand_w(g, d, cin, cout, modes)
+        wb = g.standard_normal((cout, cin))
+        bias = g.standard_normal(cout)
+        full = O.block_fwd(x, w, wb, bias, modes, tanh=tanh, input_gelu=ig)
+        pts = np.stack([g.integers(0, n, 11) for n in grid], axis=1)
+        got = O.block_at_points(x, w, wb, bias, modes, pts, tanh=tanh, input_gelu=ig)
+        for key in ("y_spec", "z", "y"):
+            want = np.stack([full[key][(slice(None), slice(None)) + tuple(p)] for p in pts],
+                            axis=-1)
+            _close(got[key], want, 1e-12, f"block at points {grid} {key}")
+
+
 ALL_CHECKS = [
     check_inverse_at_points,
     check_spectrum_bruteforce, check_spectrum_numpy_fft, check_parseval_and_dc,
@@ -619,4 +672,5 @@ ALL_CHECKS = [
     check_input_activation, check_fused_loss,
     check_tucker_identity_factors, check_tucker_hosvd, check_tucker_rank_one,
     check_tucker_block_finite_differences,
+    check_pointwise_lift_projection, check_block_at_points,
 ]

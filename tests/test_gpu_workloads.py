@@ -223,15 +223,10 @@ def test_st4d_128x20_block_sampled_points(L, name):
     ys_s = _host(ys.reshape(wl.batch, wl.width, -1)[:, :, idx])
     del ys, tx
     torch.cuda.synchronize()
-    xp = np.tanh(x.astype(np.float64)) if wl.mixed else x
-    xhat = O.spectrum(xp, wl.modes)
-    del xp
-    yhat = O.channel_mix(xhat, blk["w"], wl.modes)
-    want_spec = O.inverse_at_points(yhat, wl.grid, wl.modes, pts)
-    xs = x.reshape(wl.batch, wl.width, -1)[:, :, flat].astype(np.float64)
-    z = want_spec + np.einsum("oi,bip->bop", blk["wb"].astype(np.float64), xs) \
-        + blk["bias"].astype(np.float64)[None, :, None]
+    want = O.block_at_points(x, blk["w"], blk["wb"], blk["bias"], wl.modes, pts,
+                             tanh=bool(wl.mixed))
+    want_spec = want["y_spec"]
     check("y_spec (sampled)", ys_s, want_spec, tol)
-    check("y (sampled)", y_s, O.gelu(z), tol)
+    check("y (sampled)", y_s, want["y"], tol)
     plan.close()
     sp.close()

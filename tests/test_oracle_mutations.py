@@ -142,7 +142,54 @@ def _preact_bwd_gelu_twice(x, w, wb, bias, modes, g_z, tanh=False, input_gelu=Fa
                               input_gelu=input_gelu)
 
 
+def _lift_no_bias(x, wmat, bias):
+    return _orig["pointwise_linear"](x, wmat, None)
+
+
+def _projection_gelu_after_second(x, w1, b1, w2, b2):
+    h = _orig["pointwise_linear"](x, w1, b1)
+    return O.gelu(_orig["pointwise_linear"](h, w2, b2))
+
+
+def _block_points_common(x, w, wb, bias, modes, points, tanh, act, input_gelu, bypass_src,
+                         flip_points):
+    x = np.asarray(x, dtype=np.float64)
+    if input_gelu:
+        x = O.gelu(x)
+    grid = x.shape[2:]
+    xp = np.tanh(x) if tanh else x
+    yhat = O.channel_mix(O.spectrum(xp, modes), w, modes)
+    pts = np.asarray(points, dtype=np.int64)
+    y_spec = O.inverse_at_points(yhat, grid, modes, pts)
+    if flip_points:
+        flat = np.ravel_multi_index(tuple(pts[:, ::-1].T), grid[::-1])
+    else:
+        flat = np.ravel_multi_index(tuple(pts.T), grid)
+    src = xp if bypass_src == "preact" else x
+    xs = src.reshape(x.shape[0], x.shape[1], -1)[:, :, flat]
+    z = y_spec + np.einsum("oi,bip->bop", wb, xs) + np.asarray(bias)[None, :, None]
+    return {"y_spec": y_spec, "z": z, "y": O.gelu(z) if act else z}
+
+
+def _block_points_bypass_on_tanh(x, w, wb, bias, modes, points, tanh=False, act=True,
+                                 input_gelu=False):
+    # the bypass fed the tanh pre-activated field instead of the block's input
+    return _block_points_common(x, w, wb, bias, modes, points, tanh, act, input_gelu,
+                                "preact", False)
+
+
+def _block_points_index_order(x, w, wb, bias, modes, points, tanh=False, act=True,
+                              input_gelu=False):
+    # the bypass gathers x with the point coordinates in reversed axis order
+    return _block_points_common(x, w, wb, bias, modes, points, tanh, act, input_gelu, "x",
+                                True)
+
+
 MUTATIONS = [
+    ("pointwise_linear", _lift_no_bias, P.check_pointwise_lift_projection),
+    ("projection_fwd", _projection_gelu_after_second, P.check_pointwise_lift_projection),
+    ("block_at_points", _block_points_bypass_on_tanh, P.check_block_at_points),
+    ("block_at_points", _block_points_index_order, P.check_block_at_points),
     ("block_fwd_mse", _fused_loss_no_gelu_prime, P.check_fused_loss),
     ("block_bwd_preact", _preact_bwd_gelu_twice, P.check_fused_loss),
     ("dft_matrix", _dft_sign_flipped, P.check_spectrum_bruteforce),
