@@ -352,12 +352,14 @@ class Plan:
 
     def block_bwd(self, x, w, wb, bias, save, grad_y, want=("x", "w", "wb", "bias"), out=None):
         t = self.torch
-        o = dict(out or {})
-        gx = o.get("x", self._field(self.c_in) if "x" in want else None)
-        gw = o.get("w", t.empty_like(w) if "w" in want else None)
-        gwb = o.get("wb", t.empty_like(wb) if "wb" in want else None)
-        gb = o.get("bias", t.empty(self.c_out, dtype=t.float32, device=self.device)
-                   if "bias" in want else None)
+        o = out or {}
+        # an output is allocated only when the caller passes none for it
+        gx = o["x"] if "x" in o else (self._field(self.c_in) if "x" in want else None)
+        gw = o["w"] if "w" in o else (t.empty_like(w) if "w" in want else None)
+        gwb = o["wb"] if "wb" in o else (t.empty_like(wb) if "wb" in want else None)
+        gb = o["bias"] if "bias" in o else (
+            t.empty(self.c_out, dtype=t.float32, device=self.device) if "bias" in want
+            else None)
         ws = self.workspace()
         fno_block_bwd(self.handle, x.data_ptr(), w.data_ptr(), wb.data_ptr(), _ptr(bias),
                       _ptr(save), grad_y.data_ptr(), _ptr(gx), _ptr(gw), _ptr(gwb), _ptr(gb),
@@ -380,12 +382,14 @@ class Plan:
                          out=None):
         """Block backward from the gradient at the pre-activation (block_bwd's outputs)."""
         t = self.torch
-        o = dict(out or {})
-        gx = o.get("x", self._field(self.c_in) if "x" in want else None)
-        gw = o.get("w", t.empty_like(w) if "w" in want else None)
-        gwb = o.get("wb", t.empty_like(wb) if "wb" in want else None)
-        gb = o.get("bias", t.empty(self.c_out, dtype=t.float32, device=self.device)
-                   if "bias" in want else None)
+        o = out or {}
+        # an output is allocated only when the caller passes none for it
+        gx = o["x"] if "x" in o else (self._field(self.c_in) if "x" in want else None)
+        gw = o["w"] if "w" in o else (t.empty_like(w) if "w" in want else None)
+        gwb = o["wb"] if "wb" in o else (t.empty_like(wb) if "wb" in want else None)
+        gb = o["bias"] if "bias" in o else (
+            t.empty(self.c_out, dtype=t.float32, device=self.device) if "bias" in want
+            else None)
         ws = self.workspace()
         fno_block_bwd_preact(self.handle, x.data_ptr(), w.data_ptr(), wb.data_ptr(), _ptr(bias),
                              _ptr(save), grad_z.data_ptr(), _ptr(gx), _ptr(gw), _ptr(gwb),
@@ -564,12 +568,14 @@ class Tucker:
         """Returns dict(x, core, factors, wb, bias) of gradients (None where not asked)."""
         p = self.plan
         t = p.torch
-        o = dict(out or {})
-        gx = o.get("x", p._field(p.c_in) if want_x else None)
-        gcore = o.get("core", t.empty_like(core) if want_w else None)
-        gfac = o.get("factors", [t.empty_like(f) for f in factors] if want_w else None)
-        gwb = o.get("wb", t.empty_like(wb))
-        gb = o.get("bias", t.empty(p.c_out, dtype=t.float32, device=p.device))
+        o = out or {}
+        # an output is allocated only when the caller passes none for it
+        gx = o["x"] if "x" in o else (p._field(p.c_in) if want_x else None)
+        gcore = o["core"] if "core" in o else (t.empty_like(core) if want_w else None)
+        gfac = o["factors"] if "factors" in o else (
+            [t.empty_like(f) for f in factors] if want_w else None)
+        gwb = o["wb"] if "wb" in o else t.empty_like(wb)
+        gb = o["bias"] if "bias" in o else t.empty(p.c_out, dtype=t.float32, device=p.device)
         ws = self.workspace()
         fno_tucker_block_bwd(self.handle, x.data_ptr(), core.data_ptr(),
                              [f.data_ptr() for f in factors], wb.data_ptr(), _ptr(bias),
@@ -598,12 +604,14 @@ class Tucker:
         """block_bwd from the gradient at the pre-activation (block_bwd's outputs)."""
         p = self.plan
         t = p.torch
-        o = dict(out or {})
-        gx = o.get("x", p._field(p.c_in) if want_x else None)
-        gcore = o.get("core", t.empty_like(core) if want_w else None)
-        gfac = o.get("factors", [t.empty_like(f) for f in factors] if want_w else None)
-        gwb = o.get("wb", t.empty_like(wb))
-        gb = o.get("bias", t.empty(p.c_out, dtype=t.float32, device=p.device))
+        o = out or {}
+        # an output is allocated only when the caller passes none for it
+        gx = o["x"] if "x" in o else (p._field(p.c_in) if want_x else None)
+        gcore = o["core"] if "core" in o else (t.empty_like(core) if want_w else None)
+        gfac = o["factors"] if "factors" in o else (
+            [t.empty_like(f) for f in factors] if want_w else None)
+        gwb = o["wb"] if "wb" in o else t.empty_like(wb)
+        gb = o["bias"] if "bias" in o else t.empty(p.c_out, dtype=t.float32, device=p.device)
         ws = self.workspace()
         fno_tucker_block_bwd_preact(self.handle, x.data_ptr(), core.data_ptr(),
                                     [f.data_ptr() for f in factors], wb.data_ptr(), _ptr(bias),

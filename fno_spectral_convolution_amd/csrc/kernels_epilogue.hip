@@ -276,16 +276,35 @@ k_epi_fwd_line(EpiArgs a) {
   const int64_t l0 = (int64_t)(blockIdx.x - (int64_t)b * wg_per_b) * a.lpw;
   const int gpl = 1 << a.gpl_log2;  // steps per line
   const int nf = a.lpw << a.gpl_log2;
+  // S3: on half plans with a multiple of 32 channels the bypass runs as three bf16 products
+  // of hi / lo split operands (float32 accumulation), K-steps of 32 channels
+  constexpr bool S3 = BF && (C % 32 == 0);
+  constexpr int KS = S3 ? C / 32 : 1;
   // Wb^T slices: B operand of channel tile ct, K-step kb, lane (n = m, q): Wb[16 ct + m][4 kb + q]
-  float wbr[BLK ? NT : 1][BLK ? C / 4 : 1];
+  float wbr[BLK && !S3 ? NT : 1][BLK && !S3 ? C / 4 : 1];
+  // S3: K-step s, lane (n = m, q) holds Wb[16 ct + m][32 s + 8 q + e], e = 0..7, split
+  bf16x8 wbh[BLK && S3 ? NT : 1][KS], wbl[BLK && S3 ? NT : 1][KS];
   if (BLK) {
+    if constexpr (S3) {
 #pragma unroll
-    for (int ct = 0; ct < NT; ++ct) {
-      const int o = 16 * ct + m;
+      for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
-      for (int kb = 0; kb < C / 4; ++kb) {
-        const float w = a.wb[min(o, C - 1) * C + 4 * kb + q];
-        wbr[ct][kb] = o < C ? w : 0.f;
+        for (int s = 0; s < KS; ++s) {
+          const float* row = a.wb + (16 * ct + m) * C + 32 * s + 8 * q;
+          const float4 w0 = *reinterpret_cast<const float4*>(row);
+          const float4 w1 = *reinterpret_cast<const float4*>(row + 4);
+          const float v[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+          split_bf16x8(v, wbh[ct][s], wbl[ct][s]);
+        }
+    } else {
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) {
+        const int o = 16 * ct + m;
+#pragma unroll
+        for (int kb = 0; kb < C / 4; ++kb) {
+          const float w = a.wb[min(o, C - 1) * C + 4 * kb + q];
+          wbr[ct][kb] = o < C ? w : 0.f;
+        }
       }
     }
   }
@@ -396,14 +415,36 @@ k_epi_fwd_line(EpiArgs a) {
       }
       load_gt<G, H, true, MT>(a, (fn & (gpl - 1)) * PI, tbase, m, q, gtf);
       if (BLK) {
+        if constexpr (S3) {
+          // A: lane (m, q) holds x[32 s + 8 q + e][point MT m + tbase + j], split
 #pragma unroll
-        for (int kb = 0; kb < C / 4; ++kb) {
-          float av[G];
-          load_lds_run<G>(av, s_x + (4 * kb + q) * XSG + MT * m + tbase);
+          for (int s = 0; s < KS; ++s) {
+            float xv[8][G];
 #pragma unroll
-          for (int ct = 0; ct < NT; ++ct)
+            for (int e = 0; e < 8; ++e)
+              load_lds_run<G>(xv[e], s_x + (32 * s + 8 * q + e) * XSG + MT * m + tbase);
 #pragma unroll
-            for (int j = 0; j < G; ++j) acc[j][ct] = mfma_f32(av[j], wbr[ct][kb], acc[j][ct]);
+            for (int j = 0; j < G; ++j) {
+              float v[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) v[e] = xv[e][j];
+              bf16x8 ah, al;
+              split_bf16x8(v, ah, al);
+#pragma unroll
+              for (int ct = 0; ct < NT; ++ct)
+                acc[j][ct] = mfma_split3(ah, al, wbh[ct][s], wbl[ct][s], acc[j][ct]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < C / 4; ++kb) {
+            float av[G];
+            load_lds_run<G>(av, s_x + (4 * kb + q) * XSG + MT * m + tbase);
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+              for (int j = 0; j < G; ++j) acc[j][ct] = mfma_f32(av[j], wbr[ct][kb], acc[j][ct]);
+          }
         }
       }
       // lane (n = m, q), tile tbase + j, register r: channel 16 ct + m, point
@@ -514,26 +555,55 @@ k_epi_bwd_line(EpiArgs a) {
   const int64_t l0 = (int64_t)(blockIdx.x - (int64_t)b * wg_per_b) * a.lpw;
   const int gpl = 1 << a.gpl_log2;
   const int nf = a.lpw << a.gpl_log2;
+  // S3: on half plans with a multiple of 32 channels the bypass and dWb products run as three
+  // bf16 products of hi / lo split operands (float32 accumulation), K-steps of 32
+  constexpr bool S3 = BF && (C % 32 == 0);
+  constexpr int KS = S3 ? C / 32 : 1;
   // bypass B operand of channel tile ct, K-step kb, lane (n = m, q): Wb[o = 4 kb + q][i = 16 ct + m]
-  float wbr[BLK ? NT : 1][BLK ? C / 4 : 1];
+  float wbr[BLK && !S3 ? NT : 1][BLK && !S3 ? C / 4 : 1];
+  // S3: K-step s, lane (n = m, q) holds Wb[o = 32 s + 8 q + e][i = 16 ct + m], e = 0..7, split
+  bf16x8 wbh[BLK && S3 ? NT : 1][KS], wbl[BLK && S3 ? NT : 1][KS];
   if (BLK) {
+    if constexpr (S3) {
 #pragma unroll
-    for (int ct = 0; ct < NT; ++ct) {
-      const int i = 16 * ct + m;
+      for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
-      for (int kb = 0; kb < C / 4; ++kb) {
-        const float w = a.wb[(4 * kb + q) * C + min(i, C - 1)];
-        wbr[ct][kb] = i < C ? w : 0.f;
+        for (int s = 0; s < KS; ++s) {
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = a.wb[(32 * s + 8 * q + e) * C + 16 * ct + m];
+          split_bf16x8(v, wbh[ct][s], wbl[ct][s]);
+        }
+    } else {
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) {
+        const int i = 16 * ct + m;
+#pragma unroll
+        for (int kb = 0; kb < C / 4; ++kb) {
+          const float w = a.wb[(4 * kb + q) * C + min(i, C - 1)];
+          wbr[ct][kb] = i < C ? w : 0.f;
+        }
       }
     }
   }
-  const int mo = (NT == 4) ? wave : (NT == 2 ? (wave >> 1) : 0);
-  const int ni0 = (NT == 2) ? (wave & 1) : 0;
-  const bool count_db = (NT != 2) || ((wave & 1) == 0);
+  // dWb tiles of this wave: S3 with NT = 4: o-tiles 2 (w >> 1) + oo, i-tiles 2 (w & 1) + ii
+  // (oo, ii < 2); otherwise as described above
+  constexpr int OT = (S3 && NT == 4) ? 2 : 1;
+  const int mo = S3 ? (NT == 4 ? 2 * (wave >> 1) : (wave >> 1))
+                    : ((NT == 4) ? wave : (NT == 2 ? (wave >> 1) : 0));
+  const int ni0 = S3 ? (NT == 4 ? 2 * (wave & 1) : (wave & 1)) : ((NT == 2) ? (wave & 1) : 0);
+  const bool count_db = (!S3 && NT != 2) || ((wave & 1) == 0);
   f32x4 dwb[DT];
 #pragma unroll
   for (int u = 0; u < DT; ++u) dwb[u] = zero4();
-  float dbl = 0.f;
+  f32x4 dw3[S3 ? OT : 1][S3 ? OT : 1];
+#pragma unroll
+  for (int oo = 0; oo < (S3 ? OT : 1); ++oo)
+#pragma unroll
+    for (int ii = 0; ii < (S3 ? OT : 1); ++ii) dw3[oo][ii] = zero4();
+  float dbl = 0.f, dbl3[OT];
+#pragma unroll
+  for (int oo = 0; oo < OT; ++oo) dbl3[oo] = 0.f;
   // float4 e = tid + 256 u of a tile: channel e / FPC, points 4 (e % FPC) .. + 3 (tails as in
   // the forward: clamped copies, padding rows)
   const int64_t pbase = l0 * a.Nb;
@@ -661,14 +731,36 @@ k_epi_bwd_line(EpiArgs a) {
           }
       }
       if (BLK) {
+        if constexpr (S3) {
+          // A: lane (m, q) holds g_z[o = 32 s + 8 q + e][point MT m + tbase + j], split
 #pragma unroll
-        for (int kb = 0; kb < C / 4; ++kb) {
-          float av[G];
-          load_lds_run<G>(av, s_gz + (4 * kb + q) * XSG + MT * m + tbase);
+          for (int s = 0; s < KS; ++s) {
+            float gv[8][G];
 #pragma unroll
-          for (int ct = 0; ct < NT; ++ct)
+            for (int e = 0; e < 8; ++e)
+              load_lds_run<G>(gv[e], s_gz + (32 * s + 8 * q + e) * XSG + MT * m + tbase);
 #pragma unroll
-            for (int j = 0; j < G; ++j) acc[j][ct] = mfma_f32(av[j], wbr[ct][kb], acc[j][ct]);
+            for (int j = 0; j < G; ++j) {
+              float v[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) v[e] = gv[e][j];
+              bf16x8 ah, al;
+              split_bf16x8(v, ah, al);
+#pragma unroll
+              for (int ct = 0; ct < NT; ++ct)
+                acc[j][ct] = mfma_split3(ah, al, wbh[ct][s], wbl[ct][s], acc[j][ct]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < C / 4; ++kb) {
+            float av[G];
+            load_lds_run<G>(av, s_gz + (4 * kb + q) * XSG + MT * m + tbase);
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+              for (int j = 0; j < G; ++j) acc[j][ct] = mfma_f32(av[j], wbr[ct][kb], acc[j][ct]);
+          }
         }
       }
 #pragma unroll
@@ -680,7 +772,35 @@ k_epi_bwd_line(EpiArgs a) {
           for (int j = 0; j < G; ++j) v[j] = acc[j][ct][r];
           store_lds_run<G>(s_o + (16 * ct + m) * XSG + MT * (4 * q + r) + tbase, v);
         }
-      if (BLK) {
+      if (BLK && S3) {
+        // dWb[o][i] += sum_points g_z[o][p] x[i][p] over 32-point chunks h: A lane (m, q) holds
+        // g_z[16 mo' + m][32 h + 8 q + e], B lane (m, q) holds x[16 ni' + m][32 h + 8 q + e]
+#pragma unroll
+        for (int h = 0; h < PI / 32; ++h) {
+          bf16x8 gh[OT], gl[OT];
+#pragma unroll
+          for (int oo = 0; oo < OT; ++oo) {
+            const float* r = s_gz + (16 * (mo + oo) + m) * XSG + 32 * h + 8 * q;
+            const float4 a0 = *reinterpret_cast<const float4*>(r);
+            const float4 a1 = *reinterpret_cast<const float4*>(r + 4);
+            if (count_db) dbl3[oo] += ((a0.x + a0.y) + (a0.z + a0.w)) + ((a1.x + a1.y) + (a1.z + a1.w));
+            const float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            split_bf16x8(v, gh[oo], gl[oo]);
+          }
+#pragma unroll
+          for (int ii = 0; ii < OT; ++ii) {
+            const float* r = s_x + (16 * (ni0 + ii) + m) * XSG + 32 * h + 8 * q;
+            const float4 b0 = *reinterpret_cast<const float4*>(r);
+            const float4 b1 = *reinterpret_cast<const float4*>(r + 4);
+            const float v[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+            bf16x8 xh, xl8;
+            split_bf16x8(v, xh, xl8);
+#pragma unroll
+            for (int oo = 0; oo < OT; ++oo)
+              dw3[oo][ii] = mfma_split3(gh[oo], gl[oo], xh, xl8, dw3[oo][ii]);
+          }
+        }
+      } else if (BLK) {
         // dWb[o][i] += sum_points g_z[o][p] x[i][p]; k-slot q of MFMA jj <-> point 16 h + 4 q + jj
         constexpr int NH = PI / 16;  // 16-point chunks of the step
         const int h_lo = (NT == 1) ? wave * (NH / 4) : 0;
@@ -724,16 +844,28 @@ k_epi_bwd_line(EpiArgs a) {
   __syncthreads();
   for (int w = 0; w < 4; ++w) {
     if (wave == w) {
+      if constexpr (S3) {
 #pragma unroll
-      for (int u = 0; u < DT; ++u) {
-        const int ni = (NT == 4) ? u : ni0;
+        for (int oo = 0; oo < OT; ++oo) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int o = 16 * mo + 4 * q + r, ii = 16 * ni + m;
-          if (o < C) s_red[o * CP + ii] += dwb[u][r];
+          for (int ii = 0; ii < OT; ++ii)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              s_red[(16 * (mo + oo) + 4 * q + r) * CP + 16 * (ni0 + ii) + m] += dw3[oo][ii][r];
+          s_db[(w * 4 + q) * CP + 16 * (mo + oo) + m] += dbl3[oo];
         }
+      } else {
+#pragma unroll
+        for (int u = 0; u < DT; ++u) {
+          const int ni = (NT == 4) ? u : ni0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int o = 16 * mo + 4 * q + r, ii = 16 * ni + m;
+            if (o < C) s_red[o * CP + ii] += dwb[u][r];
+          }
+        }
+        s_db[(w * 4 + q) * CP + 16 * mo + m] += dbl;
       }
-      s_db[(w * 4 + q) * CP + 16 * mo + m] += dbl;
     }
     __syncthreads();
   }

@@ -52,6 +52,31 @@ __device__ __forceinline__ bf16x8 to_bf16x8(float4 a, float4 b) {
   return r;
 }
 
+// Eight floats as a bfloat16 pair hi + lo: hi = bf16(v) and lo = bf16(v - hi), both rounded to
+// nearest even.  v - hi is exact in float32 and |v - hi| <= 2^-9 |v|, so |v - (hi + lo)| <=
+// 2^-18 |v|.  Three bf16 products hi*hi + hi*lo + lo*hi (exact in the float32 accumulator)
+// then equal a*b up to about 3 * 2^-18 |a b|: the dropped lo*lo term and the two lo roundings.
+__device__ __forceinline__ void split_bf16x8(const float (&v)[8], bf16x8& hi, bf16x8& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    h[k] = pack_bf16x2(v[2 * k], v[2 * k + 1]);
+    const float h0 = __uint_as_float(h[k] << 16);
+    const float h1 = __uint_as_float(h[k] & 0xffff0000u);
+    l[k] = pack_bf16x2(v[2 * k] - h0, v[2 * k + 1] - h1);
+  }
+  hi = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
+  lo = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
+}
+
+// acc += a * b for split operands (three bf16 products, the small ones first)
+__device__ __forceinline__ f32x4 mfma_split3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl,
+                                             f32x4 acc) {
+  acc = mfma_bf16(ah, bl, acc);
+  acc = mfma_bf16(al, bh, acc);
+  return mfma_bf16(ah, bh, acc);
+}
+
 // ---- half-precision operand formats ------------------------------------------------------
 // H = 1: bfloat16 (fp32's exponent range, 8-bit significand); H = 2: IEEE half (5-bit
 // exponent, 11-bit significand).  Operands travel as 16-bit patterns; an MFMA operand of 8
