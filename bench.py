@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -26,7 +27,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-PEAK_TFLOPS = {"f32_mfma": 157.3, "bf16_mfma": 2516.6, "f32_valu": 78.6}
+MFMA_F32_TFLOPS = 157.3        # dense fp32 matrix cores (= fp32 vector peak)
+MFMA_HALF_TFLOPS = 2516.6      # dense bf16 / fp16 matrix cores
 METRIC = "FNO spectral-conv fwd+bwd grid-pts·ch/s per MI355X; % HBM/MFMA roofline"
 
 
@@ -64,13 +66,101 @@ def copy_calibration(nbytes: int, reps: int = 3):
                       "GBps_rw": 8 * n / dt / 1e9}), flush=True)
 
 
-def kernel_model(wl, plan):
-    """Algorithmic bytes and flops per launch of each libfno kernel for this workload.
+def _fft_flops(n: int) -> float:
+    """Flops of one real FFT row of n points, the usual 2.5 n log2 n estimate."""
+    return 2.5 * n * math.log2(n)
+
+
+def _outer_lines(wl, j: int) -> int:
+    """Lines of the truncated DFT along outer axis j: the transforms run innermost outer axis
+    first, so axes before j are still whole and axes after j already truncated."""
+    N, m, d = wl.grid, wl.modes, wl.ndim
+    lines = wl.batch * wl.width * m[-1]
+    for i in range(d - 1):
+        if i < j:
+            lines *= N[i]
+        elif i > j:
+            lines *= 2 * m[i]
+    return lines
+
+
+def _weight_bytes(wl) -> int:
+    """Bytes of one block's spectral weight: the dense corners, or the Tucker core + factors."""
+    C, m, d = wl.width, wl.modes, wl.ndim
+    if wl.tucker_ranks:
+        r = list(wl.tucker_ranks)
+        ext = [C, C] + [2 * v for v in m[:-1]] + [m[-1]]
+        core = 1
+        for v in r:
+            core *= v
+        return 8 * (core + sum(e * v for e, v in zip(ext, r)))
+    mp = 1
+    for v in m:
+        mp *= v
+    return 8 * (1 << (d - 1)) * C * C * mp
+
+
+def method_work(wl):
+    """The method's compulsory HBM bytes and flops of one step of the workload.
+
+    Bytes: per block, the input and output fields, W and Wb once (forward: 8 B per element +
+    |W|); a training step adds the incoming gradient, the input again, grad_x, W again and dW
+    (20 B per element + 3 |W|), and the loss target once; lift and projection read and write
+    their fields.  Flops: a real FFT of the contiguous axis (2.5 N log2 N per row) and truncated
+    DFTs along the outer axes (8 N 2m per line) in each direction, the per-mode mix (8 B C^2 K),
+    in the spectral dtype; the 1x1 bypass (2 C^2 per point, 3x with the backward), lift and
+    projection in float32."""
+    B, C, P, nb = wl.batch, wl.width, wl.points, wl.blocks
+    U = B * C * P
+    N, m, d = wl.grid, wl.modes, wl.ndim
+    K = m[-1]
+    for j in range(d - 1):
+        K *= 2 * m[j]
+    per_dir = U / N[-1] * _fft_flops(N[-1]) + sum(
+        8 * N[j] * 2 * m[j] * _outer_lines(wl, j) for j in range(d - 1))
+    mix = 8 * B * C * C * K
+    bypass = 2 * C * C * P * B
+    wbytes = _weight_bytes(wl)
+    wb_bytes = 4 * C * C + 4 * C
+    if wl.train:
+        nbytes = nb * (20 * U + 3 * wbytes + 3 * wb_bytes) + 4 * U
+        spec = nb * (4 * per_dir + 3 * mix)
+        pw = nb * 3 * bypass
+    else:
+        nbytes = nb * (8 * U + wbytes + wb_bytes)
+        spec = nb * (2 * per_dir + mix)
+        pw = nb * bypass
+    if wl.lift_in:
+        nbytes += 4 * B * P * (wl.lift_in + C) + 4 * B * P * (C + wl.proj_out)
+        pw += 2 * B * P * (wl.lift_in * C + C * wl.proj_hidden + wl.proj_hidden * wl.proj_out)
+    return {"bytes": nbytes, "flops_spectral": spec, "flops_pointwise": pw}
+
+
+def step_roofline(wl, prec, ms_per_step):
+    """Both floors of one step: HBM time of the compulsory bytes at 8 TB/s, and matrix-core
+    time of the method's flops (spectral flops at the peak of the spectral dtype, pointwise
+    flops at the float32 peak); t_roof is the larger, frac = t_roof / measured step time."""
+    w = method_work(wl)
+    t_hbm = w["bytes"] / (HBM_PEAK_GBS * 1e9)
+    peak_spec = MFMA_F32_TFLOPS if prec == "f32" else MFMA_HALF_TFLOPS
+    t_flop = w["flops_spectral"] / (peak_spec * 1e12) + w["flops_pointwise"] / (
+        MFMA_F32_TFLOPS * 1e12)
+    t_roof = max(t_hbm, t_flop)
+    return {"alg_bytes": w["bytes"], "alg_flops_spectral": w["flops_spectral"],
+            "alg_flops_pointwise": w["flops_pointwise"], "t_hbm_us": round(t_hbm * 1e6, 1),
+            "t_flop_us": round(t_flop * 1e6, 1), "t_roof_us": round(t_roof * 1e6, 1),
+            "bound": "hbm" if t_hbm >= t_flop else "mfma",
+            "frac": round(t_roof / (ms_per_step * 1e-3), 4)}
+
+
+def kernel_model(wl, prec):
+    """Algorithmic bytes and flops per launch of each libfno kernel for this workload:
+    name -> (bytes, spectral flops, pointwise flops, pointwise on the bf16 matrix cores).
 
     Bytes: every input and output buffer of the kernel once (fields, spectra, weights).
-    Flops: the truncated-DFT / mix / bypass arithmetic as the method defines it (direct
-    sums over the retained modes)."""
-    g = plan
+    Flops: the method's, as in method_work (FFT count for the contiguous axis, dense truncated
+    DFTs along outer axes, the mix, the bypass).  On half plans with a multiple of 32 channels
+    the line epilogues run the bypass products as three bf16 products of split operands."""
     B, C = wl.batch, wl.width
     P = wl.points
     d = wl.ndim
@@ -81,53 +171,66 @@ def kernel_model(wl, plan):
     K = mb
     for j in range(d - 1):
         K *= 2 * m[j]
-    Mprod = 1
-    for v in m:
-        Mprod *= v
     ncorner = 1 << (d - 1)
+    half = prec != "f32"
     spec = B * C * K * 8
-    wbytes = ncorner * C * C * Mprod * 8
+    wbytes = _weight_bytes(wl) if not wl.tucker_ranks else 0
+    mprod = 1
+    for v in m:
+        mprod *= v
+    wdense = 8 * ncorner * C * C * mprod
     lines = P // Nb
     # the spectrum after the outer inverses: complex float32, or the half format on half plans
     # of width 64 (the width-64 line epilogues take it so)
-    T = B * C * lines * mb * (4 if (wl.mixed and C == 64) else 8)
+    T = B * C * lines * mb * (4 if (half and C == 64) else 8)
     O = P // (Na * Nb)
     plane_spec = B * C * O * 2 * ma * mb * 8
-    dft_last = 4 * mb * U                      # real row -> mb complex bins (and back)
-    dft_a = 8 * (2 * ma) * mb * Na * B * C * O  # one complex truncated DFT along axis a
+    fft_last = U / Nb * _fft_flops(Nb)            # real row <-> retained bins, per direction
+    dft_a = 8 * Na * 2 * ma * _outer_lines(wl, d - 2)
     bypass = 2 * C * C * P * B
     mixf = 8 * B * C * C * K
+    split = half and C % 32 == 0
     model = {
-        "plane_fwd": (4 * U + plane_spec, dft_last + dft_a),
-        "plane_fwd_tanh": (4 * U + plane_spec, dft_last + dft_a),
-        "plane_fwd_gelu": (4 * U + plane_spec, dft_last + dft_a),
-        "plane_fwd_tanh_gelu": (4 * U + plane_spec, dft_last + dft_a),
-        "plane_fwd_gelugrad": (8 * U + plane_spec, dft_last + dft_a),
-        "mix_fwd": (wbytes + 2 * spec, mixf),
-        "mix_bwd_dx": (wbytes + 2 * spec, mixf),
-        "mix_bwd_dw": (wbytes + 2 * spec, mixf),
+        "plane_fwd": (4 * U + plane_spec, fft_last + dft_a, 0, False),
+        "plane_fwd_tanh": (4 * U + plane_spec, fft_last + dft_a, 0, False),
+        "plane_fwd_gelu": (4 * U + plane_spec, fft_last + dft_a, 0, False),
+        "plane_fwd_tanh_gelu": (4 * U + plane_spec, fft_last + dft_a, 0, False),
+        "plane_fwd_gelugrad": (8 * U + plane_spec, fft_last + dft_a, 0, False),
+        "mix_fwd": (max(wbytes, wdense) + 2 * spec, mixf, 0, False),
+        "mix_bwd_dx": (max(wbytes, wdense) + 2 * spec, mixf, 0, False),
+        "mix_bwd_dw": (max(wbytes, wdense) + 2 * spec, mixf, 0, False),
         # x in, y out (+ z saved for the backward)
-        "epilogue_fwd": (8 * U + T, dft_last + bypass),
-        "epilogue_fwd_zsave": (12 * U + T, dft_last + bypass),
+        "epilogue_fwd": (8 * U + T, fft_last, bypass, split),
+        "epilogue_fwd_zsave": (12 * U + T, fft_last, bypass, split),
         # short rows: the epilogue also inverts axis a, from the [2ma][mb] spectrum per plane
-        "epilogue_rows_fwd": (8 * U + plane_spec, dft_last + dft_a + bypass),
-        "epilogue_rows_fwd_zsave": (12 * U + plane_spec, dft_last + dft_a + bypass),
+        "epilogue_rows_fwd": (8 * U + plane_spec, fft_last + dft_a, bypass, False),
+        "epilogue_rows_fwd_zsave": (12 * U + plane_spec, fft_last + dft_a, bypass, False),
         # g and x in, grad_x out (+ z in for GELU' when the block applies the output GELU)
-        "epilogue_bwd": (12 * U + T, dft_last + 2 * bypass),
-        "epilogue_bwd_gelu": (16 * U + T, dft_last + 2 * bypass),
-        "mse": (12 * U, 3 * U),
+        "epilogue_bwd": (12 * U + T, fft_last, 2 * bypass, split),
+        "epilogue_bwd_gelu": (16 * U + T, fft_last, 2 * bypass, split),
+        "mse": (12 * U, 0, 3 * U, False),
         # the last block's forward fused with the loss: x and the target in, grad_z out
-        "epilogue_fwd_mse": (12 * U + T, dft_last + bypass),
+        "epilogue_fwd_mse": (12 * U + T, fft_last, bypass, split),
         # the same where the line epilogue does not apply: z and the target in, grad_z out
-        "mse_preact": (12 * U, 3 * U),
+        "mse_preact": (12 * U, 0, 3 * U, False),
     }
     return model
+
+
+def kernel_floor(model_row, prec):
+    """(t_hbm, t_flop) of one launch: bytes at 8 TB/s; spectral flops at the spectral dtype's
+    matrix-core peak; pointwise flops at the float32 peak, or as three bf16 products each at the
+    bf16 peak where the kernel splits its operands."""
+    b, fs, fp, split = model_row
+    peak_spec = MFMA_F32_TFLOPS if prec == "f32" else MFMA_HALF_TFLOPS
+    peak_pw = MFMA_HALF_TFLOPS / 3 if split else MFMA_F32_TFLOPS
+    return b / (HBM_PEAK_GBS * 1e9), fs / (peak_spec * 1e12) + fp / (peak_pw * 1e12)
 
 
 def dominant_kernel(wl, kern):
     """The kernel with the most time among those the byte model covers (kern: timer report);
     without a report, the one with the most algorithmic bytes per step."""
-    model = kernel_model(wl, None)
+    model = kernel_model(wl, configs_precision(wl))
     if kern:
         cands = [n for n in kern if model.get(n, (None,))[0]]
         if cands:
@@ -192,29 +295,45 @@ def bench_gpu(wl, steps, warmup, precision=None):
     return runner, wall, dom, kern_dom, kern_all
 
 
-def roofline(wl, runner, dom, kern_dom, kern_all):
-    """Roofline of the dominant kernel from its events in the timed region; the per-kernel
-    rows from the breakdown steps."""
-    model = kernel_model(wl, runner.plan)
+def configs_precision(wl):
+    from fno_spectral_convolution_amd import configs
+    return configs.precision(wl)
+
+
+def roofline(wl, prec, dom, kern_dom, kern_all):
+    """Roofline of the dominant kernel from its events in the timed region (bound: the larger of
+    its HBM and matrix-core floors); the per-kernel rows from the breakdown steps."""
+    model = kernel_model(wl, prec)
 
     def row(name, launches, total_ms, share):
         avg_s = total_ms / 1e3 / max(launches, 1)
-        b, f = model.get(name, (None, None))
+        mr = model.get(name)
+        b = mr[0] if mr else None
         return {"launches": launches, "avg_us": avg_s * 1e6, "share": share, "alg_bytes": b,
-                "alg_flops": f, "GBps": (b / avg_s / 1e9) if b else None}
+                "GBps": (b / avg_s / 1e9) if b else None}
 
     tot = max(sum(v[1] for v in kern_all.values()), 1e-12)
     rows = {n: row(n, c, ms, ms / tot) for n, (c, ms) in kern_all.items()}
     launches, total_ms = kern_dom[dom]
     r = row(dom, launches, total_ms, None)
     avg_s = r["avg_us"] / 1e6
-    # the dominant kernels stream fields: their floor is the HBM time of their bytes
-    ach = r["alg_bytes"] / avg_s / 1e9
+    b, fs, fp, _ = model[dom]
+    t_hbm, t_flop = kernel_floor(model[dom], prec)
     traffic = measured_traffic(wl, dom)
-    out = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-           "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
-           "alg_bytes_per_launch": r["alg_bytes"], "avg_launch_us": round(r["avg_us"], 2),
-           "timed_launches": launches}
+    out = {"kernel": dom}
+    if t_hbm >= t_flop:
+        ach = b / avg_s / 1e9
+        out.update({"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4)})
+    else:
+        ach = (fs + fp) / avg_s / 1e12
+        peak = (fs + fp) / t_flop / 1e12  # the kernel's own dtype mix
+        out.update({"bound": "mfma", "achieved": round(ach, 2), "peak": round(peak, 1),
+                    "unit": "TFLOP/s", "frac": round(ach / peak, 4)})
+    out.update({"traffic": traffic, "alg_bytes_per_launch": b,
+                "alg_flops_per_launch": fs + fp, "t_hbm_us": round(t_hbm * 1e6, 1),
+                "t_flop_us": round(t_flop * 1e6, 1), "avg_launch_us": round(r["avg_us"], 2),
+                "timed_launches": launches})
     return out, rows
 
 
@@ -304,7 +423,7 @@ def main():
     tucker_order = runner.tk.order if runner.tk is not None else None
     ms = wall / args.steps * 1e3
     value = wl.units / (wall / args.steps)
-    roof, rows = roofline(wl, runner, dom, kern_dom, kern_all)
+    roof, rows = roofline(wl, dtype, dom, kern_dom, kern_all)
     if switched:  # the committed counters were taken at the workload's own precision
         roof["traffic"] = None
     del runner
@@ -328,6 +447,7 @@ def main():
                                           f"order '{tucker_order}'"}
                       if wl.tucker_ranks else {})},
         "roofline": roof,
+        "step_roofline": step_roofline(wl, dtype, ms),
         "cpu_baseline": cpu,
         "kernels": {k: {"launches": v["launches"], "avg_us": round(v["avg_us"], 2),
                         "share": round(v["share"], 4),
