@@ -35,7 +35,8 @@ FNO_FLAG_INPUT_GELU = 8
 
 EXPORTS = [
     "fno_plan_validate", "fno_plan_create", "fno_plan_destroy", "fno_plan_query",
-    "fno_spectral_conv_fwd", "fno_spectral_conv_bwd", "fno_block_fwd", "fno_block_bwd",
+    "fno_spectral_conv_fwd", "fno_spectral_conv_bwd", "fno_block_fwd", "fno_block_fwd_static",
+    "fno_block_bwd",
     "fno_block_fwd_mse", "fno_block_bwd_preact", "fno_pointwise_fwd", "fno_mse_workspace_bytes", "fno_mse_grad", "fno_mse_grad_scaled",
     "fno_tucker_order", "fno_tucker_create", "fno_tucker_destroy", "fno_tucker_query",
     "fno_tucker_keep_intermediates", "fno_tucker_save_bytes",
@@ -77,6 +78,7 @@ def _load():
         "fno_spectral_conv_fwd": (c_int, [P, P, P, P, P, P, c_size_t, P]),
         "fno_spectral_conv_bwd": (c_int, [P, P, P, P, P, P, P, P, c_size_t, P]),
         "fno_block_fwd": (c_int, [P, P, P, P, P, P, P, P, c_size_t, P]),
+        "fno_block_fwd_static": (c_int, [P, P, P, P, P, P, P, P]),
         "fno_block_bwd": (c_int, [P, P, P, P, P, P, P, P, P, P, P, P, c_size_t, P]),
         "fno_block_fwd_mse": (c_int, [P, P, P, P, P, P, c_float, P, P, P, P, c_size_t, P]),
         "fno_block_bwd_preact": (c_int, [P, P, P, P, P, P, P, P, P, P, P, P, c_size_t, P]),
@@ -184,6 +186,11 @@ def fno_spectral_conv_bwd(plan, x, w, save, grad_y_spec, grad_x, grad_w, ws, ws_
 def fno_block_fwd(plan, x, w, w_bypass, bias, y, save, ws, ws_bytes, stream):
     _check(_lib.fno_block_fwd(plan, x, w, w_bypass, bias, y, save, ws, ws_bytes, stream),
            "fno_block_fwd")
+
+
+def fno_block_fwd_static(plan, x, w, w_bypass, bias, y, save, stream):
+    _check(_lib.fno_block_fwd_static(plan, x, w, w_bypass, bias, y, save, stream),
+           "fno_block_fwd_static")
 
 
 def fno_block_bwd(plan, x, w, w_bypass, bias, save, grad_y, grad_x, grad_w, grad_w_bypass,
@@ -348,6 +355,13 @@ class Plan:
         ws = self.workspace()
         fno_block_fwd(self.handle, x.data_ptr(), w.data_ptr(), wb.data_ptr(), _ptr(bias),
                       y.data_ptr(), _ptr(save), ws.data_ptr(), self.ws_bytes, self._stream())
+        return y
+
+    def block_fwd_static(self, x, w, wb, bias=None, save=None, out=None):
+        """block_fwd on libfno's static scratch (no workspace is allocated for it)."""
+        y = out if out is not None else self._field(self.c_out)
+        fno_block_fwd_static(self.handle, x.data_ptr(), w.data_ptr(), wb.data_ptr(), _ptr(bias),
+                             y.data_ptr(), _ptr(save), self._stream())
         return y
 
     def block_bwd(self, x, w, wb, bias, save, grad_y, want=("x", "w", "wb", "bias"), out=None):

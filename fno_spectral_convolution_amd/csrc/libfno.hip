@@ -1,6 +1,8 @@
 // libfno host runtime: descriptor validation, float64 table build, workspace layout and the
 // launch sequence of each entry point.  All device work is enqueued on the caller's stream;
-// nothing here allocates device memory except fno_plan_create (its tables, once).
+// nothing here allocates device memory except fno_plan_create (its tables, once) and the
+// static scratch array of fno_block_fwd_static (the runtime places it when it loads the
+// library's code on a device).
 #include "fno_internal.h"
 
 #include <math.h>
@@ -1143,6 +1145,39 @@ fno_status check_tucker_args(const fno_tucker* t, const float* core, const float
 
 }  // namespace
 
+// Device memory of fno_block_fwd_static, for callers that cannot allocate: one copy of this
+// array per GPU, present from the library's load on that GPU until the process ends.  Host code
+// never passes `scratch` itself to a kernel (on the host it names a stand-in, not the device
+// copy); it takes the device address from hipGetSymbolAddress, once per device.
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxScratchDevices];  // device address of `scratch` on each device
+
+// The device address of `scratch` on device `dev` (the current device), looked up on the first
+// call for that device.
+fno_status static_scratch(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(FNO_ERR_UNSUPPORTED, "device %d: at most %d devices have a static scratch", dev,
+                kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(FNO_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return FNO_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 fno_status fno_spectral_conv_fwd(const fno_plan* p, const float* x, const float* w,
@@ -1170,6 +1205,33 @@ fno_status fno_block_fwd(const fno_plan* p, const float* x, const float* w, cons
   if (p->desc.flags & FNO_FLAG_BIAS) REQ(bias, "bias");
   OPT(save, "save");
   fno_status st = check_ws(p, ws, ws_bytes);
+  if (st != FNO_OK) return st;
+  return block_fwd_impl(p, x, wb, bias, y, save, ws, static_cast<hipStream_t>(stream),
+                        DenseMix(p, w, nullptr));
+}
+
+fno_status fno_block_fwd_static(const fno_plan* p, const float* x, const float* w,
+                                const float* wb, const float* bias, float* y, void* save,
+                                void* stream) {
+  if (!p) return fail(FNO_ERR_INVALID_ARGUMENT, "plan is NULL");
+  REQ(x, "x");
+  REQ(w, "w");
+  REQ(wb, "w_bypass");
+  REQ(y, "y");
+  if (p->desc.flags & FNO_FLAG_BIAS) REQ(bias, "bias");
+  OPT(save, "save");
+  if (p->ws.total > kStaticScratchBytes)
+    return fail(FNO_ERR_INVALID_ARGUMENT,
+                "the plan's workspace (%zu bytes) exceeds the static scratch (%zu bytes); use "
+                "fno_block_fwd with a caller workspace",
+                p->ws.total, kStaticScratchBytes);
+  int dev = -1;
+  FNO_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev != p->device)
+    return fail(FNO_ERR_INVALID_ARGUMENT, "current device %d is not the plan's device %d", dev,
+                p->device);
+  void* ws = nullptr;
+  fno_status st = static_scratch(dev, &ws);
   if (st != FNO_OK) return st;
   return block_fwd_impl(p, x, wb, bias, y, save, ws, static_cast<hipStream_t>(stream),
                         DenseMix(p, w, nullptr));

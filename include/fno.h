@@ -144,6 +144,20 @@ fno_status fno_block_fwd(const fno_plan* plan, const float* x, const float* w,
                          const float* w_bypass, const float* bias, float* y, void* save,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* fno_block_fwd without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * workspace is a static device array of 64 MiB inside libfno, one per GPU, present from the
+ * library's load on that GPU until the process ends; this call allocates nothing and frees
+ * nothing.  Its limit: plans whose fno_plan_query workspace exceeds 64 MiB are rejected with
+ * FNO_ERR_INVALID_ARGUMENT (use fno_block_fwd).  The current device must be the plan's
+ * (else FNO_ERR_INVALID_ARGUMENT).  Every call on one GPU uses the same array, which keeps the
+ * last call's contents (nothing in it needs to start at zero: the forward writes every byte
+ * it reads): calls that overlap on one GPU (other streams, other threads) race, so the caller
+ * orders them (one stream, or events).  Other arguments, results and errors as fno_block_fwd. */
+fno_status fno_block_fwd_static(const fno_plan* plan, const float* x, const float* w,
+                                const float* w_bypass, const float* bias, float* y, void* save,
+                                void* stream);
+
 /* Full block backward for the incoming gradient grad_y.  `save` must come from
  * fno_block_fwd with the same inputs (required when FNO_FLAG_GELU is set).
  * Outputs (each may be NULL to skip): grad_x [B,C_in,N..], grad_w (complex64, W's layout),
