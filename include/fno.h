@@ -69,8 +69,10 @@ typedef enum fno_status {
  * F32:  float32 operands, float32 accumulation.
  * BF16: bfloat16 operands (pre-activated input, transform tables, spectra, weights rounded
  *       to nearest-even on load) with float32 accumulation -- the half-precision transform
- *       and contraction of [MIXED].  The bypass, bias, GELU and every HBM activation stay
- *       float32.
+ *       and contraction of [MIXED].  The bias, GELU and every HBM activation stay float32; the
+ *       1x1 bypass and its weight gradient are float32 products, computed on plans with a
+ *       multiple of 32 channels as three bfloat16 products of hi/lo split operands (each
+ *       product exact to about 3 * 2^-18 relative, float32 accumulation).
  * F16:  the same with IEEE half operands.  Half's 5-bit exponent is kept in range by scaling
  *       every transform of the plan by 1/sqrt(N_j) per axis in both directions (tables built
  *       so), and by multiplying the mixed spectra by the power of two nearest sqrt(Cin) Cout
