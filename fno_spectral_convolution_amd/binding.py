@@ -35,6 +35,7 @@ FNO_FLAG_INPUT_GELU = 8
 
 EXPORTS = [
     "fno_plan_validate", "fno_plan_create", "fno_plan_destroy", "fno_plan_query",
+    "fno_plan_half_range",
     "fno_spectral_conv_fwd", "fno_spectral_conv_bwd", "fno_block_fwd", "fno_block_fwd_static",
     "fno_block_bwd",
     "fno_block_fwd_mse", "fno_block_bwd_preact", "fno_pointwise_fwd", "fno_mse_workspace_bytes", "fno_mse_grad", "fno_mse_grad_scaled",
@@ -75,6 +76,7 @@ def _load():
         "fno_plan_create": (c_int, [POINTER(fno_plan_desc), POINTER(c_void_p)]),
         "fno_plan_destroy": (c_int, [P]),
         "fno_plan_query": (c_int, [P, POINTER(c_size_t), POINTER(c_size_t), POINTER(c_size_t)]),
+        "fno_plan_half_range": (c_int, [P, POINTER(c_int), c_int]),
         "fno_spectral_conv_fwd": (c_int, [P, P, P, P, P, P, c_size_t, P]),
         "fno_spectral_conv_bwd": (c_int, [P, P, P, P, P, P, P, P, c_size_t, P]),
         "fno_block_fwd": (c_int, [P, P, P, P, P, P, P, P, c_size_t, P]),
@@ -171,6 +173,13 @@ def fno_plan_query(plan: int):
     ws, sv, we = c_size_t(), c_size_t(), c_size_t()
     _check(_lib.fno_plan_query(plan, byref(ws), byref(sv), byref(we)), "fno_plan_query")
     return ws.value, sv.value, we.value
+
+
+def fno_plan_half_range(plan: int, clear: bool = False) -> bool:
+    """Whether a call on this IEEE-half plan wrote a non-finite output (synchronous read)."""
+    v = c_int()
+    _check(_lib.fno_plan_half_range(plan, byref(v), int(bool(clear))), "fno_plan_half_range")
+    return bool(v.value)
 
 
 def fno_spectral_conv_fwd(plan, x, w, y_spec, save, ws, ws_bytes, stream):
@@ -314,6 +323,11 @@ class Plan:
             self.close()
         except Exception:
             pass
+
+    def half_range_exceeded(self, clear=False):
+        """IEEE-half plans: whether a call since creation (or the last clear) wrote a
+        non-finite output; synchronise the calls' streams first."""
+        return fno_plan_half_range(self.handle, clear)
 
     # buffers
     def workspace(self):

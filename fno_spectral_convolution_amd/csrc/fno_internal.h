@@ -46,6 +46,9 @@ struct Geom {
   // half table or applied in float).  Powers of two: both steps are exact.  1 otherwise.
   float mix_gain[2];
   float inv_gain[2];
+  // IEEE-half plans: a device word the output-writing kernels set to 1 when they write a
+  // non-finite value (half's range exceeded upstream); null on other plans
+  int* half_flag;
 };
 
 // Device tables owned by a plan (all in one allocation).

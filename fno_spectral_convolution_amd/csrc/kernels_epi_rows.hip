@@ -49,6 +49,7 @@ struct RowsEpiArgs {
   const uint16_t* ainv_lo;
   const float* gt;          // [Nb][kpad]: g(k)/Ntot (cos, -sin)(2 pi k c / Nb)
   const uint16_t* gt_bf;
+  int* flag;                // IEEE-half plans: set to 1 when a non-finite output is written
 };
 
 // float4 e of a chunk -> (channel, float4 within the channel's 4 Nb); exact float division
@@ -123,6 +124,7 @@ k_epi_rows(RowsEpiArgs a) {
   // Nb .. 31 those of absent columns); s_x: the x chunk, dense [channel][RP] (block modes)
   float* s_y = s_er;
   float* s_x = s_y + (a.Cout + 1) * kErYC;
+  bool bad = false;  // IEEE-half plans: a non-finite output was written
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 15, q = lane >> 4;
@@ -365,9 +367,11 @@ k_epi_rows(RowsEpiArgs a) {
           v.w = gelu_as(zv[i].w);
         }
       }
+      if constexpr (H == 2) bad |= !finite4(v);
       *reinterpret_cast<float4*>(a.y + yo[i]) = v;
     }
   }
+  if constexpr (H == 2) raise_half_flag(a.flag, bad);
 }
 
 // The fused row-axis epilogue applies when the contiguous axis is short, the retained rows and
@@ -433,6 +437,7 @@ hipError_t launch_epilogue_rows(const fno_plan* p, int mode, const float2* T, co
   a.ainv_lo = p->t.oinv_bf_lo[g.d - 2];
   a.gt = p->t.gt_fwd;
   a.gt_bf = p->t.gt_fwd_bf;
+  a.flag = p->g.half_flag;
   const int md = mode == EPI_SPECTRAL ? 0 : (zsave ? 2 : 1);
   if (g.half == 2) {
     if (md == 0) return launch_rows_t<2, 0>(a, g.B, s);

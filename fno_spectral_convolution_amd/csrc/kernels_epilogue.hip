@@ -49,6 +49,7 @@ struct EpiArgs {
   float msc;           // its gradient scale (grad_scale 2 / n); the target is gy
   int block;           // bypass/bias/GELU present (else spectral only)
   int gelu;
+  int* flag;           // IEEE-half plans: set to 1 when a non-finite output is written
 };
 
 __device__ __forceinline__ float comp(const float4& v, int j) {
@@ -329,6 +330,7 @@ k_epi_fwd_line(EpiArgs a) {
   // fused loss: target rows of the current step; the copies past the tile add nothing
   float4 ptg[MS ? NPT : 1];
   double lsum = 0.0;
+  bool bad = false;  // IEEE-half plans: a non-finite output was written
   GtFrag<G, H> gtf;
   if (BLK) {
 #pragma unroll
@@ -482,9 +484,10 @@ k_epi_fwd_line(EpiArgs a) {
           } else {
             lsum += (tid + 256 * u < NF4) ? sq : 0.0;
           }
-          *reinterpret_cast<float4*>(a.y + off) =
-              make_float4(a.msc * d.x * gp.x, a.msc * d.y * gp.y, a.msc * d.z * gp.z,
-                          a.msc * d.w * gp.w);
+          const float4 gzv = make_float4(a.msc * d.x * gp.x, a.msc * d.y * gp.y,
+                                         a.msc * d.z * gp.z, a.msc * d.w * gp.w);
+          if constexpr (H == 2) bad |= !finite4(gzv);
+          *reinterpret_cast<float4*>(a.y + off) = gzv;
           continue;
         }
         if (ZS) *reinterpret_cast<float4*>(a.z + off) = v;
@@ -494,10 +497,12 @@ k_epi_fwd_line(EpiArgs a) {
           v.z = gelu_as(v.z);
           v.w = gelu_as(v.w);
         }
+        if constexpr (H == 2) bad |= !finite4(v);
         *reinterpret_cast<float4*>(a.y + off) = v;
       }
     }
   }
+  if constexpr (H == 2) raise_half_flag(a.flag, bad);
   if constexpr (MS) {
     // fixed order: xor butterflies within each wave, then the four waves in turn
 #pragma unroll
@@ -616,6 +621,7 @@ k_epi_bwd_line(EpiArgs a) {
     xl[u] = (e / FPC) * XSG + 4 * (e % FPC);
     ol[u] = (ec / FPC) * XSG + 4 * (ec % FPC);
   }
+  bool bad = false;  // IEEE-half plans: a non-finite output was written
   float4 pg_y[NPT], pz[NPT], px[NPT];
 #pragma unroll
   for (int u = 0; u < NPT; ++u) {
@@ -830,10 +836,12 @@ k_epi_bwd_line(EpiArgs a) {
           v.z *= gp.z;
           v.w *= gp.w;
         }
+        if constexpr (H == 2) bad |= !finite4(v);
         *reinterpret_cast<float4*>(a.y + goff[u] + PI * f) = v;
       }
     }
   }
+  if constexpr (H == 2) raise_half_flag(a.flag, bad);
   if (!BLK || !a.part) return;
   // Deterministic work-group reduction (fixed wave order) into LDS, then one partial row.
   float* s_red = s_gz;  // [C][CP] dWb
@@ -1025,6 +1033,7 @@ static EpiArgs fwd_args(const fno_plan* p, int* G, int64_t* wgs) {
   while ((PG * *G << gl) < g.Nb) ++gl;
   a.gpl_log2 = gl;
   a.gt = g.bf16 ? (const void*)p->t.gt_fwd_bf : (const void*)p->t.gt_fwd;
+  a.flag = g.half_flag;
   *wgs = (int64_t)g.B * a.lines / a.lpw;
   return a;
 }
@@ -1142,6 +1151,7 @@ hipError_t launch_epilogue_bwd_fast(const fno_plan* p, int mode, const void* Tg,
   a.gy = gy;
   a.zin = z;
   a.part = red_part;
+  a.flag = g.half_flag;
   a.block = mode == EPI_BLOCK;
   a.gelu = z != nullptr;
   const bool tanh_pre = (p->desc.flags & FNO_FLAG_TANH_PREACT) != 0;

@@ -23,6 +23,7 @@
 // and is bound by that read (or, for dW, by its write).
 #include "fno_internal.h"
 #include "mfma.h"
+#include "pointwise.h"
 
 namespace fno {
 
@@ -193,6 +194,7 @@ __global__ void __launch_bounds__(256) k_mix_mfma_dw(Geom g, const int32_t* __re
   constexpr int BC = BF ? 16 : 8;  // batch entries per chunk (K = 2 BC)
   constexpr int NX = 8 * BC / 16;   // x values per thread per chunk (16 modes x 8 ch x BC / 256)
   constexpr int NG = 16 * BC / 16;  // g values per thread per chunk (16 modes x 16 ch x BC / 256)
+  bool bad = false;  // IEEE-half plans: a non-finite weight gradient was written
   __shared__ __attribute__((aligned(16))) unsigned char s_a[kMT * kTB];
   __shared__ __attribute__((aligned(16))) unsigned char s_b[kMT * kTB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -269,11 +271,13 @@ __global__ void __launch_bounds__(256) k_mix_mfma_dw(Geom g, const int32_t* __re
         if (i0 + ii < g.Cin && o0 + oo < g.Cout) {
           const float2 v =
               *reinterpret_cast<const float2*>(s_out + tl * kOutTB + (ii * 16 + oo) * 8);
+          if constexpr (H == 2) bad |= !(__builtin_isfinite(v.x) & __builtin_isfinite(v.y));
           dw[wmode + (int64_t)(i0 + ii) * g.w_si + (int64_t)(o0 + oo) * g.w_so] = v;
         }
       }
     }
   }
+  if constexpr (H == 2) raise_half_flag(g.half_flag, bad);
 }
 
 // ------------------------------------------------------------------------------------------

@@ -11,6 +11,7 @@
 // (nearest-even) before the multiply; products and sums are float32.  IEEE-half plans scale each
 // transform by 1/sqrt(N_j) in both directions (Geom::sc), as their tables do.
 #include "fno_internal.h"
+#include "pointwise.h"
 
 #include <math.h>
 
@@ -326,7 +327,9 @@ k_epilogue_fwd(Geom g, int mode, bool gelu, bool ig, const float2* __restrict__ 
     }
     const int64_t off = ((int64_t)b * Cout + o) * P + p;
     if (zsave) zsave[off] = z;
-    y[off] = (block && gelu) ? gelu_f(z) : z;
+    const float yv = (block && gelu) ? gelu_f(z) : z;
+    raise_half_flag(g.half_flag, !__builtin_isfinite(yv));
+    y[off] = yv;
   }
 }
 
@@ -433,6 +436,7 @@ k_epilogue_bwd(Geom g, int mode, bool gelu, bool tanh_pre, bool ig,
           gs += acc;
         }
         if (ig) gs *= gelu_grad_f(x[off]);  // the input was GELU(x)
+        raise_half_flag(g.half_flag, !__builtin_isfinite(gs));
         grad_x[off] = gs;
       }
     }

@@ -335,6 +335,8 @@ fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out) {
   toff += align_up(sizeof(int32_t) * (size_t)g.K);
   const size_t woff_mode_off = toff;
   toff += align_up(sizeof(int32_t) * woff_mode_elems);
+  const size_t half_flag_off = toff;  // the half-range flag word, uploaded as 0
+  toff += align_up(sizeof(int32_t));
   std::vector<unsigned char> host(toff, 0);
   for (int j = 0; j < g.d; ++j) {
     float2* r = reinterpret_cast<float2*>(host.data() + root_off[j]);
@@ -510,6 +512,7 @@ fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out) {
   }
   p->t.mode_woff = reinterpret_cast<const int32_t*>(base + mode_woff_off);
   p->t.woff_mode = reinterpret_cast<const int32_t*>(base + woff_mode_off);
+  p->g.half_flag = g.half == 2 ? reinterpret_cast<int*>(base + half_flag_off) : nullptr;
   *out = p;
   return FNO_OK;
 }
@@ -520,6 +523,24 @@ fno_status fno_plan_destroy(fno_plan* p) {
   if (p->table_mem) e = hipFree(p->table_mem);
   delete p;
   if (e != hipSuccess) return hip_fail(e, "hipFree(plan tables)");
+  return FNO_OK;
+}
+
+fno_status fno_plan_half_range(const fno_plan* p, int* exceeded, int clear) {
+  if (!p) return fail(FNO_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (!exceeded) return fail(FNO_ERR_INVALID_ARGUMENT, "exceeded is NULL");
+  *exceeded = 0;
+  int* flag = p->g.half_flag;
+  if (!flag) return FNO_OK;  // only IEEE-half plans keep the flag
+  int dev = -1;
+  FNO_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev != p->device)
+    return fail(FNO_ERR_INVALID_ARGUMENT, "current device %d is not the plan's device %d", dev,
+                p->device);
+  int v = 0;
+  FNO_HIP(hipMemcpy(&v, flag, sizeof(int), hipMemcpyDeviceToHost), "hipMemcpy(half flag)");
+  *exceeded = v != 0;
+  if (clear) FNO_HIP(hipMemset(flag, 0, sizeof(int)), "hipMemset(half flag)");
   return FNO_OK;
 }
 

@@ -73,4 +73,16 @@ __device__ __forceinline__ float tanh_gelu(float z) {
   return fmaf(-2.0f, __builtin_amdgcn_rcpf(e + 1.0f), 1.0f);
 }
 
+// all four components finite (not inf, not NaN)
+__device__ __forceinline__ bool finite4(const float4& v) {
+  return __builtin_isfinite(v.x) & __builtin_isfinite(v.y) & __builtin_isfinite(v.z) &
+         __builtin_isfinite(v.w);
+}
+
+// IEEE-half plans: a kernel that wrote a non-finite output sets the plan's flag word (every
+// writer stores the same 1, so the result does not depend on their order)
+__device__ __forceinline__ void raise_half_flag(int* flag, bool bad) {
+  if (bad && flag) *flag = 1;
+}
+
 }  // namespace fno

@@ -34,7 +34,7 @@
  *
  * Ownership: the caller allocates every tensor, the workspace and the save buffer (sizes from
  * fno_plan_query) on the plan's device and keeps them alive until the stream has run the
- * call.  A plan owns only its constant tables.  Calls enqueue work on `stream` (a
+ * call.  A plan owns only its constant tables (and, on IEEE-half plans, one flag word).  Calls enqueue work on `stream` (a
  * hipStream_t; NULL = the null stream) and return without synchronising; they never
  * allocate device memory.  A plan is immutable after creation: concurrent calls on
  * different streams are safe when each has its own workspace.
@@ -78,9 +78,10 @@ typedef enum fno_status {
  *       so), and by multiplying the mixed spectra by the power of two nearest sqrt(Cin) Cout
  *       (forward; sqrt(Cout) Cin for the input gradient), which the last inverse stage divides
  *       out.  The gain suits spectral weights of size about 1/(Cin Cout), the usual FNO
- *       initialisation; weights orders of magnitude larger can overflow half (inf in the
- *       output).  Results are unchanged up to rounding.  Gradients far below half's range (a
- *       mean over 10^8 elements) need a loss scale, see fno_mse_grad_scaled.  */
+ *       initialisation; weights orders of magnitude larger can overflow half, and the
+ *       outputs then hold inf or NaN: the plan records that (fno_plan_half_range).  Results
+ *       are unchanged up to rounding.  Gradients far below half's range (a mean over 10^8
+ *       elements) need a loss scale, see fno_mse_grad_scaled.  */
 typedef enum fno_dtype { FNO_DTYPE_F32 = 0, FNO_DTYPE_BF16 = 1, FNO_DTYPE_F16 = 2 } fno_dtype;
 
 enum {
@@ -122,6 +123,15 @@ fno_status fno_plan_destroy(fno_plan* plan);
  * of complex elements of w.  Any output pointer may be NULL. */
 fno_status fno_plan_query(const fno_plan* plan, size_t* workspace_bytes, size_t* save_bytes,
                           size_t* weight_elems);
+
+/* IEEE-half (F16) plans: whether a call made with this plan since its creation (or the last
+ * clear) wrote a non-finite value into y, y_spec, z, grad_z, grad_x or the dense grad_w, i.e.
+ * an operand left half's range on the way (*exceeded = 1, else 0).  The kernels that write
+ * those outputs set a device word of the plan; this call reads it with a synchronous copy, so
+ * the caller first synchronises the streams of the calls it asks about.  clear != 0 resets
+ * the word after reading it.  Other plans: *exceeded = 0, no device access.  Calls on several
+ * streams that share the plan share the word. */
+fno_status fno_plan_half_range(const fno_plan* plan, int* exceeded, int clear);
 
 /* Spectral convolution only: y_spec = inverse(mix(forward(x')))  (no bypass, bias or GELU).
  * `save` (nullable, save_bytes) receives the retained spectrum xhat for a later backward. */

@@ -184,6 +184,83 @@ def test_half_plan_bypass_split(L, case, mixed, ig):
     check("grad_bias", _host(g["bias"]), ref["grad_bias"], TOL_SPLIT)
     plan.close()
 
+
+# The spectral-dominant variant: spectral weights scaled by C^2 (about U(0,1) per entry instead
+# of U(0,1)/(Cin Cout)), so the spectral path dominates the block output.  fp32 and bf16 plans
+# keep their tolerances.  An IEEE-half plan may leave half's range: then its outputs hold inf /
+# NaN and the plan must say so (fno_plan_half_range); otherwise it meets its tolerance.
+@pytest.mark.parametrize("prec", [("f32", False), ("bf16", True), ("f16", "f16")],
+                         ids=lambda p: p[0])
+@pytest.mark.parametrize("case", [c for c in CASES if c[0] in (
+    "2d_mc_c64", "2d_wide", "2d_mc_c32", "3d_mc_c20", "4d_short_t20", "2d_c1shape")],
+    ids=lambda c: c[0])
+def test_spectral_dominant_weights(L, case, prec):
+    name, batch, cin, cout, grid, modes = case
+    pname, mixed = prec
+    announce("spectral-dominant", name, pname)
+    seed = 1300 + zlib.crc32(name.encode()) % 1000
+    x, w, wb, b = inputs.small_case(seed, batch, cin, cout, grid, modes)
+    w = (w * np.float32(cin * cout)).astype(w.dtype)
+    gy = inputs.normal_like(seed, (batch, cout) + grid)
+    plan = L.Plan(batch, cin, cout, grid, modes, mixed=mixed)
+    assert not plan.half_range_exceeded()
+    tx, tw, twb, tb, tg = (_dev(a) for a in (x, w, wb, b, gy))
+    save = plan.new_save()
+    y = plan.block_fwd(tx, tw, twb, tb, save=save)
+    g = plan.block_bwd(tx, tw, twb, tb, save, tg)
+    _torch().cuda.synchronize()
+    outs = {"y": _host(y), "grad_x": _host(g["x"]), "grad_w": _host(g["w"]),
+            "grad_wb": _host(g["wb"]), "grad_bias": _host(g["bias"])}
+    nonfinite = [k for k in ("y", "grad_x", "grad_w") if not np.all(np.isfinite(outs[k]))]
+    flagged = plan.half_range_exceeded(clear=True)
+    print(f"    half range exceeded: {flagged}; non-finite outputs: {nonfinite}", flush=True)
+    assert flagged == bool(nonfinite), (flagged, nonfinite)
+    if mixed != "f16":
+        assert not flagged
+    if not flagged:
+        ref = O.block_bwd(x, w, wb, b, modes, gy, tanh=bool(mixed))
+        tol = tol_for(mixed)
+        check("y", outs["y"], ref["fwd"]["y"], tol)
+        check("grad_x", outs["grad_x"], ref["grad_x"], tol)
+        check("grad_w", outs["grad_w"], ref["grad_w"], tol)
+        check("grad_wb", outs["grad_wb"], ref["grad_wb"], tol)
+        check("grad_bias", outs["grad_bias"], ref["grad_bias"], tol)
+    # the flag was cleared: a call at the usual weight scale leaves it clear
+    x2, w2, wb2, b2 = inputs.small_case(seed + 1, batch, cin, cout, grid, modes)
+    plan.block_fwd(_dev(x2), _dev(w2), _dev(wb2), _dev(b2))
+    _torch().cuda.synchronize()
+    assert not plan.half_range_exceeded()
+    plan.close()
+
+
+@pytest.mark.parametrize("case", [c for c in CASES if c[0] in (
+    "2d_mc_c64", "2d_ragged", "4d_short_t20", "3d_mc_c20")], ids=lambda c: c[0])
+def test_f16_overflow_is_reported(L, case):
+    """Spectral weights far beyond half's range on an IEEE-half plan: the outputs are
+    non-finite and the plan reports it; a bfloat16 plan (float32's exponent range) keeps the
+    same inputs finite."""
+    name, batch, cin, cout, grid, modes = case
+    announce("f16 overflow", name)
+    seed = 1700 + zlib.crc32(name.encode()) % 1000
+    x, w, wb, b = inputs.small_case(seed, batch, cin, cout, grid, modes)
+    w = (w * np.float32(cin * cout * 65536.0)).astype(w.dtype)
+    gy = inputs.normal_like(seed, (batch, cout) + grid)
+    for mixed in ("f16", True):
+        plan = L.Plan(batch, cin, cout, grid, modes, mixed=mixed)
+        tx, tw, twb, tb, tg = (_dev(a) for a in (x, w, wb, b, gy))
+        save = plan.new_save()
+        y = plan.block_fwd(tx, tw, twb, tb, save=save)
+        g = plan.block_bwd(tx, tw, twb, tb, save, tg)
+        _torch().cuda.synchronize()
+        finite = all(bool(np.all(np.isfinite(_host(t)))) for t in (y, g["x"], g["w"]))
+        flagged = plan.half_range_exceeded()
+        print(f"    {mixed}: finite outputs {finite}, half range exceeded {flagged}", flush=True)
+        if mixed == "f16":
+            assert flagged and not finite
+        else:
+            assert finite and not flagged
+        plan.close()
+
 def test_gelu_off_and_bias_off(L):
     """Flags: without GELU the block returns z; without BIAS the bias pointer is ignored."""
     announce("flags")
