@@ -15,7 +15,8 @@ from ctypes import (POINTER, byref, c_char_p, c_float, c_int, c_int32, c_int64, 
                     c_uint32, c_void_p)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfno.so")
+# FNO_LIBRARY names another build of libfno (e.g. the host-sanitized one for CPU checks)
+LIB_PATH = os.environ.get("FNO_LIBRARY") or os.path.join(_HERE, "libfno.so")
 
 FNO_OK = 0
 FNO_ERR_INVALID_ARGUMENT = 1
