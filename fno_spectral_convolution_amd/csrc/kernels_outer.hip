@@ -61,6 +61,48 @@ __global__ void __launch_bounds__(256) k_outer_mfma(OuterArgs a) {
   // the loads (which would make each wait for the one before it)
   constexpr int SU = 8;
   const int nel = a.Lin_pad * CT;
+  if (NT == 4 && (a.post2 & 3) == 0) {
+    // rows of whole float4: thread f = tid + 256 u loads columns 4 (f % 16) .. + 3 of input row
+    // f / 16 (zero past the slab's rows or columns); staged row of column 4 c4 + j is
+    // 16 j + c4, and the swapped copy of column c goes to the row of column c ^ 1
+    constexpr int FU = 4;
+    const int nf = a.Lin_pad * (CT / 4);
+    for (int f0 = 0; f0 < nf; f0 += 256 * FU) {
+      float4 v[FU];
+#pragma unroll
+      for (int u = 0; u < FU; ++u) {
+        const int f = f0 + tid + 256 * u;
+        const int li = f >> 4, c4 = f & 15;
+        const int64_t col = c0 + 4 * c4;
+        const bool ok = f < nf && li < a.Lin && col < a.post2;
+        const int64_t off = (int64_t)min(li, a.Lin - 1) * a.post2 + min(col, a.post2 - 4);
+        const float4 x = *reinterpret_cast<const float4*>(src + off);
+        v[u] = ok ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the LDS writes
+#pragma unroll
+      for (int u = 0; u < FU; ++u) {
+        const int f = f0 + tid + 256 * u;
+        if (f >= nf) continue;
+        const int li = f >> 4, c4 = f & 15;
+        const float w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float vs = (j & 1) ? -w[j] : w[j];  // Xs[li][(4 c4 + j) ^ 1]
+          const int rj = 16 * j + c4, rs = 16 * (j ^ 1) + c4;
+          if (BF) {
+            uint16_t* bt = reinterpret_cast<uint16_t*>(s_raw);
+            bt[rj * KS + li] = HalfOf<H>::bits(w[j]);
+            bt[rs * KS + a.Lin_pad + li] = HalfOf<H>::bits(vs);
+          } else {
+            float* bt = reinterpret_cast<float*>(s_raw);
+            bt[rj * KS + li] = w[j];
+            bt[rs * KS + a.Lin_pad + li] = vs;
+          }
+        }
+      }
+    }
+  } else
   for (int e0 = 0; e0 < nel; e0 += 256 * SU) {
     float v[SU];
 #pragma unroll
