@@ -164,6 +164,16 @@ struct GtFrag<TMW, 0> {
   float4 v[TMW][4];  // K-groups of 16
 };
 
+// Point of a 64-point step held by row i of M-tile t (one tile per wave, one 64-point group
+// per step): 16 (i % 4) + 4 t + i / 4.  Result row 4 q + r of a tile is then point
+// 16 r + 4 t + q, so the 64 lanes writing (or reading) one register of a tile in a
+// [channel][point] LDS tile of row stride 68 floats (16 channel rows m, 4 q) hit 64 distinct
+// banks, and row m of the A operand (point 16 (m % 4) + 4 t + m / 4) spreads a lane quarter's
+// reads of 8 channel rows over two bank halves.
+__device__ __forceinline__ int step_point1(int i, int t) {
+  return 16 * (i & 3) + 4 * t + (i >> 2);
+}
+
 template <int TMW, int H, bool IL = false, int MT = 4>
 __device__ __forceinline__ void load_gt(const EpiArgs& a, int pb0, int tbase, int m, int q,
                                         GtFrag<TMW, H>& f) {
@@ -173,7 +183,8 @@ __device__ __forceinline__ void load_gt(const EpiArgs& a, int pb0, int tbase, in
   for (int j = 0; j < TMW; ++j) {
     // row m of M-tile t: point MT m + t (interleaved over the MT tiles of the step) or
     // 16 t + m of the group
-    const int pt = IL ? MT * m + tbase + j : 16 * (tbase + j) + m;
+    const int pt = IL ? (TMW == 1 ? step_point1(m, tbase) : MT * m + tbase + j)
+                      : 16 * (tbase + j) + m;
     const int64_t row = (int64_t)(pb0 + pt) * a.kpad;
     if constexpr (BF) {
       const uint16_t* gt = static_cast<const uint16_t*>(a.gt) + row;
@@ -236,9 +247,11 @@ __device__ __forceinline__ void load_rows(float4 (&v)[NPT], const float* base, i
 // across it: the x rows of step f + 1 are loaded while step f is computed, then the table
 // fragments of step f + 1 (the last step re-loads itself instead of branching).  Wave w owns
 // the M-tiles (16 points each) w G .. w G + G - 1 of the step for every channel tile, so each
-// table fragment is loaded once per work-group and each x operand feeds NT products.  Row m of
-// M-tile t is point MT m + t of the step (MT = 4 G tiles), so a lane's A operands of its G
-// tiles are adjacent in the [channel][point] LDS tile.  The z tile goes through LDS and the
+// table fragment is loaded once per work-group and each x operand feeds NT products.  With
+// G = 2, row m of M-tile t is point MT m + t of the step (MT = 4 G tiles), so a lane's A
+// operands of its two tiles are adjacent in the [channel][point] LDS tile; with G = 1 it is
+// point 16 (m % 4) + 4 t + m / 4 (step_point1), which keeps the LDS accesses of the result
+// layout free of bank conflicts.  The z tile goes through LDS and the
 // stores are row-contiguous: 16 G threads write one channel's 64 G points.
 // MODE: 0 spectral part only, 1 block (bypass, bias, optional GELU), 2 block + z save; plus 8
 // when x is a pre-activation (the bypass takes GELU(x), applied as the x tile is staged); plus
@@ -272,6 +285,9 @@ k_epi_fwd_line(EpiArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, q = lane >> 4;
   const int tbase = wave * G;
+  // step point of row i of this wave's first tile (G = 2: tiles tbase, tbase + 1 interleaved,
+  // so the two tiles' points are adjacent)
+  auto lp = [&](int i) { return G == 1 ? step_point1(i, tbase) : MT * i + tbase; };
   const int64_t wg_per_b = a.lines / a.lpw;
   const int b = (int)(blockIdx.x / wg_per_b);
   const int64_t l0 = (int64_t)(blockIdx.x - (int64_t)b * wg_per_b) * a.lpw;
@@ -424,7 +440,7 @@ k_epi_fwd_line(EpiArgs a) {
             float xv[8][G];
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-              load_lds_run<G>(xv[e], s_x + (32 * s + 8 * q + e) * XSG + MT * m + tbase);
+              load_lds_run<G>(xv[e], s_x + (32 * s + 8 * q + e) * XSG + lp(m));
 #pragma unroll
             for (int j = 0; j < G; ++j) {
               float v[8];
@@ -441,7 +457,7 @@ k_epi_fwd_line(EpiArgs a) {
 #pragma unroll
           for (int kb = 0; kb < C / 4; ++kb) {
             float av[G];
-            load_lds_run<G>(av, s_x + (4 * kb + q) * XSG + MT * m + tbase);
+            load_lds_run<G>(av, s_x + (4 * kb + q) * XSG + lp(m));
 #pragma unroll
             for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
@@ -450,7 +466,7 @@ k_epi_fwd_line(EpiArgs a) {
         }
       }
       // lane (n = m, q), tile tbase + j, register r: channel 16 ct + m, point
-      // MT (4 q + r) + tbase + j
+      // lp(4 q + r) + j
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct) {
         const int o = 16 * ct + m;
@@ -460,7 +476,7 @@ k_epi_fwd_line(EpiArgs a) {
           float v[G];
 #pragma unroll
           for (int j = 0; j < G; ++j) v[j] = acc[j][ct][r] + bo;
-          store_lds_run<G>(s_o + o * XSG + MT * (4 * q + r) + tbase, v);
+          store_lds_run<G>(s_o + o * XSG + lp(4 * q + r), v);
         }
       }
       __syncthreads();  // z tile complete; x tile free
@@ -555,6 +571,9 @@ k_epi_bwd_line(EpiArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, q = lane >> 4;
   const int tbase = wave * G;
+  // step point of row i of this wave's first tile (G = 2: tiles tbase, tbase + 1 interleaved,
+  // so the two tiles' points are adjacent)
+  auto lp = [&](int i) { return G == 1 ? step_point1(i, tbase) : MT * i + tbase; };
   const int64_t wg_per_b = a.lines / a.lpw;
   const int b = (int)(blockIdx.x / wg_per_b);
   const int64_t l0 = (int64_t)(blockIdx.x - (int64_t)b * wg_per_b) * a.lpw;
@@ -722,13 +741,13 @@ k_epi_bwd_line(EpiArgs a) {
       load_gt<G, H, true, MT>(a, (fn & (gpl - 1)) * PI, tbase, m, q, gtf);
       if (TANH) {
         // lane (n = m, q), tile tbase + j, register r: channel 16 ct + m, point
-        // MT (4 q + r) + tbase + j
+        // lp(4 q + r) + j
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             float xv[G];
-            load_lds_run<G>(xv, s_x + (16 * ct + m) * XSG + MT * (4 * q + r) + tbase);
+            load_lds_run<G>(xv, s_x + (16 * ct + m) * XSG + lp(4 * q + r));
 #pragma unroll
             for (int j = 0; j < G; ++j) {
               const float t = tanh_fast(xv[j]);
@@ -744,7 +763,7 @@ k_epi_bwd_line(EpiArgs a) {
             float gv[8][G];
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-              load_lds_run<G>(gv[e], s_gz + (32 * s + 8 * q + e) * XSG + MT * m + tbase);
+              load_lds_run<G>(gv[e], s_gz + (32 * s + 8 * q + e) * XSG + lp(m));
 #pragma unroll
             for (int j = 0; j < G; ++j) {
               float v[8];
@@ -761,7 +780,7 @@ k_epi_bwd_line(EpiArgs a) {
 #pragma unroll
           for (int kb = 0; kb < C / 4; ++kb) {
             float av[G];
-            load_lds_run<G>(av, s_gz + (4 * kb + q) * XSG + MT * m + tbase);
+            load_lds_run<G>(av, s_gz + (4 * kb + q) * XSG + lp(m));
 #pragma unroll
             for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
@@ -776,7 +795,7 @@ k_epi_bwd_line(EpiArgs a) {
           float v[G];
 #pragma unroll
           for (int j = 0; j < G; ++j) v[j] = acc[j][ct][r];
-          store_lds_run<G>(s_o + (16 * ct + m) * XSG + MT * (4 * q + r) + tbase, v);
+          store_lds_run<G>(s_o + (16 * ct + m) * XSG + lp(4 * q + r), v);
         }
       if (BLK && S3) {
         // dWb[o][i] += sum_points g_z[o][p] x[i][p] over 32-point chunks h: A lane (m, q) holds
