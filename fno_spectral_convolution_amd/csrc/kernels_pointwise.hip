@@ -7,7 +7,8 @@
 // runs as 16x16x4 f32 MFMAs with bias and GELU applied to its fragments, the hidden tile goes
 // to LDS and feeds the second product (M = cout, K = hidden); the output tile leaves through
 // LDS as row-contiguous float4 stores.  Waves take M-tiles round-robin; weight fragments are
-// read through L2.  Point tails are zero-filled on load and masked on store.
+// read through L2.  Point tails are zero-filled on load and masked on store.  A projection to
+// at most kPwSmallOut channels does its second product on the VALU instead (see below).
 #include "fno_internal.h"
 #include "mfma.h"
 #include "pointwise.h"
@@ -16,6 +17,7 @@ namespace fno {
 
 constexpr int kPwP = 64;        // points per work-group
 constexpr int kPwS = kPwP + 4;  // LDS row stride (floats)
+constexpr int kPwSmallOut = 4;  // projections to at most this many channels skip the hidden tile
 
 // D[M][64] += W[M rows][K] . S[K][64] over N-tiles nt0 .. nt0 + NN - 1 of M-tile mt; W
 // row-major with row stride ldw.  Fragment of M-tile mt, N-tile nt: lane (m, q), register r
@@ -106,6 +108,75 @@ k_pointwise_mfma(int64_t npts, int cin, int hidden, int cout, const float* __res
     }
   }
   __syncthreads();
+  if (hidden > 0 && cout <= kPwSmallOut) {
+    // narrow output (the projection to a few channels): the second product runs on the
+    // VALU from the GELU'd fragments of the first, without the hidden tile.  Lane (m, q) adds
+    // W2[o][h] GELU(.)[h][p] over its rows h = 16 mt + 4 q + r for points p = 16 nt + m; the
+    // four lane quarters are then summed by two xor butterflies and the four waves in order
+    // (a fixed order: deterministic).
+    float part[kPwSmallOut][4];
+#pragma unroll
+    for (int o = 0; o < kPwSmallOut; ++o)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) part[o][nt] = 0.f;
+    for (int mt = wave; mt < mid_p / 16; mt += 4) {
+      f32x4 acc[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) acc[nt] = zero4();
+      pw_tile<4>(w1, cin, mid, cin, s_x, mt, 0, m, q, acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 16 * mt + 4 * q + r;
+        const float bh = masked_bias(b1, h, mid);
+        float w2v[kPwSmallOut];
+#pragma unroll
+        for (int o = 0; o < kPwSmallOut; ++o) {
+          const float wv = w2[min(o, cout - 1) * hidden + min(h, hidden - 1)];
+          w2v[o] = __uint_as_float(__float_as_uint(wv) &
+                                   ((o < cout && h < hidden) ? 0xffffffffu : 0u));
+        }
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const float gv = gelu_as(acc[nt][r] + bh);
+#pragma unroll
+          for (int o = 0; o < kPwSmallOut; ++o) part[o][nt] = fmaf(w2v[o], gv, part[o][nt]);
+        }
+      }
+    }
+    float* s_red = s_h;  // [4 waves][kPwSmallOut][kPwP]
+#pragma unroll
+    for (int o = 0; o < kPwSmallOut; ++o)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        float v = part[o][nt];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        if (q == 0) s_red[(wave * kPwSmallOut + o) * kPwP + 16 * nt + m] = v;
+      }
+    __syncthreads();
+    for (int e = tid; e < cout * (kPwP / 4); e += 256) {
+      const int o = e / (kPwP / 4), c4 = e % (kPwP / 4);
+      const float bo = masked_bias(b2, o, cout);
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int pp = 4 * c4 + j;
+        v[j] = bo + (((s_red[(0 * kPwSmallOut + o) * kPwP + pp] +
+                       s_red[(1 * kPwSmallOut + o) * kPwP + pp]) +
+                      s_red[(2 * kPwSmallOut + o) * kPwP + pp]) +
+                     s_red[(3 * kPwSmallOut + o) * kPwP + pp]);
+      }
+      float* dst = y + ((int64_t)b * cout + o) * npts + p0 + 4 * c4;
+      if (4 * c4 + 4 <= np && (npts % 4) == 0) {
+        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (4 * c4 + j < np) dst[j] = v[j];
+      }
+    }
+    return;
+  }
   for (int mt = wave; mt < mid_p / 16; mt += 4) {
     f32x4 acc[4];
 #pragma unroll
@@ -163,7 +234,10 @@ hipError_t launch_pointwise(int64_t batch, int64_t npts, int cin, int hidden, in
   const int mid = hidden > 0 ? hidden : cout;
   const int mid_p = (mid + 15) / 16 * 16;
   const int cout_p = (cout + 15) / 16 * 16;
-  const size_t lds = sizeof(float) * kPwS * (cin_p + mid_p + (hidden > 0 ? cout_p : 0));
+  // a narrow projection keeps only the x tile and the per-wave partial sums (in s_h's place)
+  const size_t lds = (hidden > 0 && cout <= kPwSmallOut)
+                         ? sizeof(float) * ((size_t)kPwS * cin_p + 4 * kPwSmallOut * kPwP)
+                         : sizeof(float) * kPwS * (cin_p + mid_p + (hidden > 0 ? cout_p : 0));
   const int64_t tiles = (npts + kPwP - 1) / kPwP;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
   if (lds > 65536) {  // wide hidden layers need more than the default dynamic LDS limit

@@ -309,6 +309,23 @@ def test_pointwise_and_mse(L):
     assert float(_host(loss2)[0]) == float(_host(loss)[0])
 
 
+
+@pytest.mark.parametrize("cout,hidden", [(1, 128), (3, 20), (4, 64), (5, 40)])
+def test_projection_narrow_outputs(L, cout, hidden):
+    """Projection heads around the narrow-output path (<= 4 outputs take the VALU second
+    product), with a point count that leaves a ragged last tile."""
+    announce("projection", cout, hidden)
+    g = np.random.default_rng(40 + cout)
+    cin, npts = 32, 3 * 64 + 9
+    x = g.standard_normal((2, cin, npts)).astype(np.float32)
+    w1 = (g.standard_normal((hidden, cin)) / np.sqrt(cin)).astype(np.float32)
+    b1 = g.standard_normal(hidden).astype(np.float32)
+    w2 = (g.standard_normal((cout, hidden)) / np.sqrt(hidden)).astype(np.float32)
+    b2 = g.standard_normal(cout).astype(np.float32)
+    proj = L.pointwise(_dev(x), _dev(w1), _dev(b1), _dev(w2), _dev(b2))
+    _torch().cuda.synchronize()
+    check("projection", _host(proj), O.projection_fwd(x, w1, b1, w2, b2), TOL_F32)
+
 def test_pointwise_widest(L):
     """The widest pointwise layers the boundary accepts (64 -> 256 -> 128), ragged point count."""
     announce("pointwise widest")
