@@ -42,6 +42,9 @@ def parse():
                     help="run the workload's plan at this spectral precision, tanh kept as the "
                          "workload has it (e.g. f32: a mixed run after a precision-schedule "
                          "switch)")
+    ap.add_argument("--last-axis", choices=["auto", "fft", "dense"], default="auto",
+                    help="float32 plans: forward transform of the contiguous axis by FFT or by "
+                         "dense matrix-core products (auto: the plan's choice for its shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-batch", type=int, default=3)
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -238,7 +241,7 @@ def dominant_kernel(wl, kern):
     return max(model, key=lambda n: model[n][0])
 
 
-def bench_gpu(wl, steps, warmup, precision=None):
+def bench_gpu(wl, steps, warmup, precision=None, last_axis=None):
     """Warm-up (every launch timed: names the dominant kernel), the timed region (events only
     around the dominant kernel's launches, so the other launches run as in production), then
     `steps` more untimed steps with every launch timed for the per-kernel breakdown."""
@@ -249,7 +252,7 @@ def bench_gpu(wl, steps, warmup, precision=None):
 
     torch.cuda.set_device(0)
     t0 = time.perf_counter()
-    runner = StackRunner(wl, device="cuda:0")
+    runner = StackRunner(wl, device="cuda:0", last_axis=last_axis)
     if precision is not None:
         runner.set_precision(precision)
     torch.cuda.synchronize()
@@ -416,8 +419,9 @@ def main():
         sys.exit(2)
     from fno_spectral_convolution_amd import configs
     wl = configs.get(args.workload)
+    last_axis = None if args.last_axis == "auto" else args.last_axis
     runner, wall, dom, kern_dom, kern_all = bench_gpu(wl, args.steps, args.warmup,
-                                                      args.spectral_precision)
+                                                      args.spectral_precision, last_axis)
     dtype = runner.precision
     switched = dtype != configs.precision(wl)
     tucker_order = runner.tk.order if runner.tk is not None else None

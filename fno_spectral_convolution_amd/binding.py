@@ -33,10 +33,12 @@ FNO_FLAG_TANH_PREACT = 1
 FNO_FLAG_GELU = 2
 FNO_FLAG_BIAS = 4
 FNO_FLAG_INPUT_GELU = 8
+FNO_FLAG_LAST_AXIS_FFT = 16
+FNO_FLAG_LAST_AXIS_DENSE = 32
 
 EXPORTS = [
     "fno_plan_validate", "fno_plan_create", "fno_plan_destroy", "fno_plan_query",
-    "fno_plan_half_range",
+    "fno_plan_half_range", "fno_plan_last_axis_fft",
     "fno_spectral_conv_fwd", "fno_spectral_conv_bwd", "fno_block_fwd", "fno_block_fwd_static",
     "fno_block_bwd",
     "fno_block_fwd_mse", "fno_block_bwd_preact", "fno_pointwise_fwd", "fno_mse_workspace_bytes", "fno_mse_grad", "fno_mse_grad_scaled",
@@ -78,6 +80,7 @@ def _load():
         "fno_plan_destroy": (c_int, [P]),
         "fno_plan_query": (c_int, [P, POINTER(c_size_t), POINTER(c_size_t), POINTER(c_size_t)]),
         "fno_plan_half_range": (c_int, [P, POINTER(c_int), c_int]),
+        "fno_plan_last_axis_fft": (c_int, [P, POINTER(c_int)]),
         "fno_spectral_conv_fwd": (c_int, [P, P, P, P, P, P, c_size_t, P]),
         "fno_spectral_conv_bwd": (c_int, [P, P, P, P, P, P, P, P, c_size_t, P]),
         "fno_block_fwd": (c_int, [P, P, P, P, P, P, P, P, c_size_t, P]),
@@ -180,6 +183,13 @@ def fno_plan_half_range(plan: int, clear: bool = False) -> bool:
     """Whether a call on this IEEE-half plan wrote a non-finite output (synchronous read)."""
     v = c_int()
     _check(_lib.fno_plan_half_range(plan, byref(v), int(bool(clear))), "fno_plan_half_range")
+    return bool(v.value)
+
+
+def fno_plan_last_axis_fft(plan: int) -> bool:
+    """Whether the plan takes its contiguous-axis forward transform by FFT (host only)."""
+    v = c_int()
+    _check(_lib.fno_plan_last_axis_fft(plan, byref(v)), "fno_plan_last_axis_fft")
     return bool(v.value)
 
 
@@ -294,16 +304,22 @@ class Plan:
     [Cout, Cin], bias float32 [Cout]."""
 
     def __init__(self, batch, c_in, c_out, grid, modes, mixed=False, tanh=None, gelu=True,
-                 bias=True, device=None, input_gelu=False):
+                 bias=True, device=None, input_gelu=False, last_axis=None):
         """mixed: False (fp32 spectral path), True or "bf16" (bfloat16 operands), "f16" (IEEE
         half operands); a mixed plan takes the tanh pre-activation unless tanh says otherwise.
-        input_gelu: x is a pre-activation and the block's input is GELU(x)."""
+        input_gelu: x is a pre-activation and the block's input is GELU(x).
+        last_axis: None (the plan picks), "fft" or "dense": how a float32 plan takes the
+        forward transform of the contiguous axis."""
         import torch
         self.torch = torch
         self.device = torch.device(device) if device is not None else torch.device("cuda")
         tanh = bool(mixed) if tanh is None else tanh
         flags = (FNO_FLAG_TANH_PREACT if tanh else 0) | (FNO_FLAG_GELU if gelu else 0) | \
             (FNO_FLAG_BIAS if bias else 0) | (FNO_FLAG_INPUT_GELU if input_gelu else 0)
+        if last_axis not in (None, "fft", "dense"):
+            raise ValueError(f"last_axis must be None, 'fft' or 'dense', not {last_axis!r}")
+        flags |= {None: 0, "fft": FNO_FLAG_LAST_AXIS_FFT,
+                  "dense": FNO_FLAG_LAST_AXIS_DENSE}[last_axis]
         self.desc = make_desc(batch, c_in, c_out, tuple(grid), tuple(modes),
                               spectral_dtype(mixed), flags)
         self.batch, self.c_in, self.c_out = batch, c_in, c_out
@@ -329,6 +345,11 @@ class Plan:
         """IEEE-half plans: whether a call since creation (or the last clear) wrote a
         non-finite output; synchronise the calls' streams first."""
         return fno_plan_half_range(self.handle, clear)
+
+    @property
+    def last_axis_fft(self):
+        """True when the plan takes its contiguous-axis forward transform by FFT."""
+        return fno_plan_last_axis_fft(self.handle)
 
     # buffers
     def workspace(self):

@@ -107,6 +107,7 @@ struct fno_plan {
   int kpad;             // 2*mb rounded up to 32 (columns of the last-axis tables)
   int jpad;             // 2*mb rounded up to 16 (columns of the forward plane table t1)
   int plane_rows;       // rows of axis a per plane-transform chunk
+  bool plane_fft;       // forward row transform by FFT (float32 plans), else dense products
   int64_t complex_max;  // largest intermediate spectrum (complex elements)
   fno::Workspace ws;
   size_t save_bytes;
@@ -224,6 +225,11 @@ hipError_t launch_epilogue_bwd_fast(const fno_plan* p, int mode, const void* Tg,
                                     const float* z, float* grad_x, float* red_part,
                                     hipStream_t s, bool t_half = false);
 bool plane_fast_ok(const fno_plan* p);
+// float32 plans: the plane transform with an FFT along the contiguous axis
+bool plane_fft_ok(const fno_plan* p);
+bool plane_fft_default(const fno_plan* p);  // the shapes where it is the faster choice
+hipError_t launch_plane_fft(const fno_plan* p, int plane_in, int chans, const float* in0,
+                            const float* in1, float2* out, hipStream_t s);
 hipError_t launch_plane_fwd_fast(const fno_plan* p, int plane_in, int chans, const float* in0,
                                  const float* in1, float2* out, hipStream_t s);
 bool outer_fast_ok(const fno_plan* p, int axis, bool inv);

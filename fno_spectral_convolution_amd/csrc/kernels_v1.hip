@@ -136,6 +136,7 @@ hipError_t launch_plane_fwd(const fno_plan* p, int plane_in, int chans, const fl
   const bool al16 = ((uintptr_t)in0 % 16 == 0) && ((uintptr_t)in1 % 16 == 0);
   if (p->nch == 1 && al16 && plane_small_ok(p))
     return launch_plane_small(p, plane_in, chans, in0, in1, out, s);
+  if (p->plane_fft) return launch_plane_fft(p, plane_in, chans, in0, in1, out, s);
   if (plane_fast_ok(p)) return launch_plane_fwd_fast(p, plane_in, chans, in0, in1, out, s);
   const Geom& g = p->g;
   const int64_t planes = (int64_t)g.B * chans * g.O;

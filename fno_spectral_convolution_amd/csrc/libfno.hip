@@ -114,8 +114,11 @@ fno_status fno_plan_validate(const fno_plan_desc* d) {
     return fail(FNO_ERR_INVALID_ARGUMENT, "ndim %d not in {2,3,4}", d->ndim);
   if (d->reserved != 0) return fail(FNO_ERR_INVALID_ARGUMENT, "reserved field must be 0");
   if (d->flags & ~(uint32_t)(FNO_FLAG_TANH_PREACT | FNO_FLAG_GELU | FNO_FLAG_BIAS |
-                             FNO_FLAG_INPUT_GELU))
+                             FNO_FLAG_INPUT_GELU | FNO_FLAG_LAST_AXIS_FFT |
+                             FNO_FLAG_LAST_AXIS_DENSE))
     return fail(FNO_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", d->flags);
+  if ((d->flags & FNO_FLAG_LAST_AXIS_FFT) && (d->flags & FNO_FLAG_LAST_AXIS_DENSE))
+    return fail(FNO_ERR_INVALID_ARGUMENT, "LAST_AXIS_FFT and LAST_AXIS_DENSE exclude each other");
   if (d->spectral_dtype != FNO_DTYPE_F32 && d->spectral_dtype != FNO_DTYPE_BF16 &&
       d->spectral_dtype != FNO_DTYPE_F16)
     return fail(FNO_ERR_INVALID_ARGUMENT, "unknown spectral dtype %d", d->spectral_dtype);
@@ -228,6 +231,18 @@ fno_status fno_plan_create(const fno_plan_desc* desc, fno_plan** out) {
     if (fno::plane_small_ok(p)) rows = g.Na;  // the short-row kernel never chunks
     p->plane_rows = rows;
     p->nch = (g.Na + rows - 1) / rows;
+  }
+  // forward transform of the contiguous axis on float32 plans: FFT or dense product
+  {
+    const bool fft_ok = fno::plane_fft_ok(p);
+    if ((desc->flags & FNO_FLAG_LAST_AXIS_FFT) && !g.bf16 && !fft_ok) {
+      delete p;
+      return fail(FNO_ERR_UNSUPPORTED,
+                  "LAST_AXIS_FFT needs a float32 plan with N_last in {128,256,512}, "
+                  "m_last <= 32, m_{d-2} a multiple of 4 (<= 32) and N_{d-2} a multiple of 8");
+    }
+    p->plane_fft = fft_ok && !(desc->flags & FNO_FLAG_LAST_AXIS_DENSE) &&
+                   ((desc->flags & FNO_FLAG_LAST_AXIS_FFT) || fno::plane_fft_default(p));
   }
   {
     const int64_t tiles = (g.P + 63) / 64;
@@ -541,6 +556,13 @@ fno_status fno_plan_half_range(const fno_plan* p, int* exceeded, int clear) {
   FNO_HIP(hipMemcpy(&v, flag, sizeof(int), hipMemcpyDeviceToHost), "hipMemcpy(half flag)");
   *exceeded = v != 0;
   if (clear) FNO_HIP(hipMemset(flag, 0, sizeof(int)), "hipMemset(half flag)");
+  return FNO_OK;
+}
+
+fno_status fno_plan_last_axis_fft(const fno_plan* p, int* fft) {
+  if (!p) return fail(FNO_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (!fft) return fail(FNO_ERR_INVALID_ARGUMENT, "fft is NULL");
+  *fft = p->plane_fft ? 1 : 0;
   return FNO_OK;
 }
 

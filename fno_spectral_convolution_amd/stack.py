@@ -59,7 +59,7 @@ class StackRunner:
     is never written; step() then returns None.  With fuse_loss=False the step writes y and
     runs the stand-alone loss kernel between the two passes."""
 
-    def __init__(self, wl, device="cuda", host_inputs=None, fuse_loss=True):
+    def __init__(self, wl, device="cuda", host_inputs=None, fuse_loss=True, last_axis=None):
         import torch
         self.torch = torch
         self.wl = wl
@@ -69,6 +69,7 @@ class StackRunner:
         # one plan per spectral precision the run has used and block role (a plan holds only
         # its tables and workspace); the workload's tanh pre-activation is kept by all of them
         self._tanh = bool(wl.mixed)
+        self._last_axis = last_axis  # float32 plans: None (plan picks), "fft" or "dense"
         self._plans = {}
         self._tuckers = {}
         self.tucker = bool(wl.tucker_ranks)
@@ -136,7 +137,8 @@ class StackRunner:
             wl = self.wl
             plan = L.Plan(wl.batch, wl.width, wl.width, wl.grid, wl.modes,
                           mixed=_PLAN_MIXED[prec], tanh=self._tanh, gelu=role[1],
-                          input_gelu=role[0], device=self.device)
+                          input_gelu=role[0], device=self.device,
+                          last_axis=self._last_axis if prec == "f32" else None)
             if wl.tucker_ranks:
                 tk = L.Tucker(plan, wl.tucker_ranks)
                 tk.workspace()

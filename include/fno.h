@@ -88,9 +88,18 @@ enum {
   FNO_FLAG_TANH_PREACT = 1u, /* x' = tanh(x) feeds the spectral path only [MIXED] */
   FNO_FLAG_GELU = 2u,        /* block output y = GELU(z); without it y = z            */
   FNO_FLAG_BIAS = 4u,        /* bias pointer is read; without it bias is taken as 0    */
-  FNO_FLAG_INPUT_GELU = 8u   /* x is a pre-activation: the block's input is GELU(x), and
+  FNO_FLAG_INPUT_GELU = 8u,  /* x is a pre-activation: the block's input is GELU(x), and
                                 grad_x carries GELU'(x).  Lets a stack keep only each block's z
                                 (the previous block runs without FNO_FLAG_GELU)           */
+  /* How float32 plans take the forward transform of the contiguous axis (the forward and the
+     input-gradient spectra).  Without either flag the plan picks the faster one for its
+     shape.  FFT: a two-pass Stockham FFT in registers and LDS (N_{d-1} in {128, 256, 512},
+     m_{d-1} <= 32, m_{d-2} a multiple of 4 up to 32, N_{d-2} a multiple of 8; otherwise
+     fno_plan_create returns FNO_ERR_UNSUPPORTED).  DENSE: the truncated DFT as a matrix-core
+     product.  The results agree to float32 rounding.  Half plans always use the dense
+     products (at the half rate) and ignore both flags.                                    */
+  FNO_FLAG_LAST_AXIS_FFT = 16u,
+  FNO_FLAG_LAST_AXIS_DENSE = 32u
 };
 
 typedef struct fno_plan_desc {
@@ -123,6 +132,11 @@ fno_status fno_plan_destroy(fno_plan* plan);
  * of complex elements of w.  Any output pointer may be NULL. */
 fno_status fno_plan_query(const fno_plan* plan, size_t* workspace_bytes, size_t* save_bytes,
                           size_t* weight_elems);
+
+/* Whether the plan takes the forward transform of its contiguous axis by FFT (*fft = 1) or by
+ * dense matrix-core products (*fft = 0), as chosen at creation (FNO_FLAG_LAST_AXIS_FFT,
+ * FNO_FLAG_LAST_AXIS_DENSE or the plan's own choice).  Host only. */
+fno_status fno_plan_last_axis_fft(const fno_plan* plan, int* fft);
 
 /* IEEE-half (F16) plans: whether a call made with this plan since its creation (or the last
  * clear) wrote a non-finite value into y, y_spec, z, grad_z, grad_x or the dense grad_w, i.e.

@@ -45,6 +45,7 @@ def _desc(**kw):
     dict(grid=(512, 512), modes=(32, 32), c_in=64, c_out=64, dtype=1, flags=7),
     dict(grid=(512, 512), modes=(32, 32), c_in=64, c_out=64, dtype=2, flags=7),
     dict(grid=(512, 512), modes=(32, 32), c_in=64, c_out=64, dtype=1, flags=15),
+    dict(grid=(256, 256), modes=(16, 16), flags=16 | 7), dict(flags=32),
     dict(grid=(8, 8), modes=(4, 5)), dict(grid=(15, 9), modes=(7, 5)),
 ])
 def test_validate_accepts(kw):
@@ -58,7 +59,8 @@ def test_validate_accepts(kw):
     (dict(modes=(0, 12)), L.FNO_ERR_INVALID_ARGUMENT),
     (dict(batch=0), L.FNO_ERR_INVALID_ARGUMENT),
     (dict(c_in=0), L.FNO_ERR_INVALID_ARGUMENT),
-    (dict(flags=16), L.FNO_ERR_INVALID_ARGUMENT),
+    (dict(flags=64), L.FNO_ERR_INVALID_ARGUMENT),
+    (dict(flags=16 | 32), L.FNO_ERR_INVALID_ARGUMENT),
     (dict(dtype=7), L.FNO_ERR_INVALID_ARGUMENT),
     (dict(c_in=65), L.FNO_ERR_UNSUPPORTED),
     (dict(grid=(64, 8192), modes=(12, 12)), L.FNO_ERR_UNSUPPORTED),
@@ -121,6 +123,11 @@ def test_status_strings():
     dict(grid=(512, 512), modes=(32, 32), c_in=64, c_out=64, batch=8, dtype=2, flags=7),
     dict(grid=(128, 128, 128, 20), modes=(12, 12, 12, 8), batch=1, dtype=2, flags=7),
     dict(grid=(16, 32), modes=(1, 1), c_in=1, c_out=1),
+    dict(grid=(256, 256), modes=(16, 16), c_in=32, c_out=32, batch=16, flags=16 | 7),
+    dict(grid=(128, 128, 128), modes=(16, 16, 16), c_in=20, c_out=20, batch=2, flags=16),
+    dict(grid=(512, 512), modes=(32, 32), c_in=64, c_out=64, batch=8, flags=16 | 7),
+    dict(grid=(512, 512), modes=(32, 32), c_in=64, c_out=64, batch=8, flags=32 | 7),
+    dict(grid=(512, 512), modes=(32, 32), c_in=64, c_out=64, batch=8, dtype=1, flags=16 | 7),
 ])
 def test_plan_create_host_logic(kw):
     """fno_plan_create runs its whole host-side part (geometry, chunking, workspace sizing,
@@ -132,3 +139,22 @@ def test_plan_create_host_logic(kw):
     with pytest.raises(L.FnoError) as ei:
         L.fno_plan_create(_desc(**kw))
     assert ei.value.status == L.FNO_ERR_HIP
+
+
+@pytest.mark.parametrize("kw", [
+    dict(grid=(64, 64), modes=(12, 12), flags=16),           # rows of 64 points
+    dict(grid=(256, 1024), modes=(16, 16), flags=16),        # rows of 1024 points
+    dict(grid=(256, 256), modes=(16, 33), flags=16),         # more than 32 kept bins
+    dict(grid=(256, 256), modes=(14, 16), flags=16),         # m_a not a multiple of 4
+])
+def test_last_axis_fft_rejected_where_unsupported(kw):
+    """A float32 plan that asks for the contiguous-axis FFT outside the shapes it covers is
+    refused at creation, before any HIP call."""
+    with pytest.raises(L.FnoError) as ei:
+        L.fno_plan_create(_desc(**kw))
+    assert ei.value.status == L.FNO_ERR_UNSUPPORTED
+    assert "LAST_AXIS_FFT" in L.last_error_message()
+
+
+def test_last_axis_query_null_arguments():
+    assert L._lib.fno_plan_last_axis_fft(None, None) == L.FNO_ERR_INVALID_ARGUMENT
