@@ -27,6 +27,8 @@
 #include "plane_common.h"
 #include "pointwise.h"
 
+#include <type_traits>
+
 namespace fno {
 namespace {
 
@@ -179,95 +181,114 @@ __global__ void __launch_bounds__(256) k_plane_fft(PlaneArgs a, const float2* __
   const float2* base1 = (PIN == PLANE_GELU_GRAD)
                             ? reinterpret_cast<const float2*>(a.in1 + plane * (int64_t)a.Na * NB)
                             : nullptr;
-  float2 pre0[16], pre1[16];
-  bool pre_ok = false;
-  // rows past the chunk load a valid row (the chunk's first) and are zeroed on use: a branch
-  // around the loads would make the compiler wait for every load in flight
-  auto load_pass = [&](int rp) {
-    const int row = rp + wave * RPW + rw;
-    pre_ok = row < r_end;
-    const int64_t off = (int64_t)(pre_ok ? row : r_begin) * M + gi;
+  const float* f2 = static_cast<const float*>(a.f2);
+  const int nblk = (r_end - r_begin + 63) / 64;  // 64-row blocks of the chunk
+  // row of this lane in global pass pi (PASSES passes per 64-row block)
+  auto pass_row = [&](int pi) {
+    return r_begin + 64 * (pi / PASSES) + (pi % PASSES) * RPP + wave * RPW + rw;
+  };
+  // rows past the chunk load its last row again (an L2 hit) and their spectra are written as
+  // zeros: a branch around the loads would make the compiler wait for every load in flight
+  auto load_to = [&](float2 (&d0)[16], float2 (&d1)[16], int pi) {
+    const int64_t off = (int64_t)min(pass_row(pi), r_end - 1) * M + gi;
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
-      pre0[s] = base0[off + L * s];
-      if (PIN == PLANE_GELU_GRAD) pre1[s] = base1[off + L * s];
+      d0[s] = base0[off + L * s];
+      if (PIN == PLANE_GELU_GRAD) d1[s] = base1[off + L * s];
     }
   };
-
-  const float* f2 = static_cast<const float*>(a.f2);
-  load_pass(r_begin);
-  for (int r0 = r_begin; r0 < r_end; r0 += 64) {
+  // F2 fragments of a 64-row block (kg, u): rows 16 it + m, columns r0 + 16 kg + 4 q + jj;
+  // columns past the chunk are clamped into the table and masked to zero
+  float4 fa[4][2];
+  auto load_f2 = [&](int r0) {
 #pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) {
-      float2 v[16];
-      const bool ok = pre_ok;
+    for (int kg = 0; kg < 4; ++kg)
 #pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        const float2 w = (PIN == PLANE_GELU_GRAD) ? pre1[s] : make_float2(0.f, 0.f);
-        const float re = prologue<PIN>(pre0[s].x, w.x), im = prologue<PIN>(pre0[s].y, w.y);
-        v[s] = ok ? make_float2(re, im) : make_float2(0.f, 0.f);
+      for (int u = 0; u < 2; ++u) {
+        const int it = min(wave + 4 * u, IT - 1);
+        const int row0 = r0 + 16 * kg + 4 * q;
+        const int64_t fo = (int64_t)(16 * it + m) * a.Na + min(row0, a.Na - 4);
+        const float4 v = *reinterpret_cast<const float4*>(f2 + fo);
+        auto keep = [&](float x, int j) {
+          return __uint_as_float(__float_as_uint(x) & (row0 + j < r_end ? 0xffffffffu : 0u));
+        };
+        fa[kg][u] = make_float4(keep(v.x, 0), keep(v.y, 1), keep(v.z, 2), keep(v.w, 3));
       }
-      load_pass(r0 + (ps + 1) * RPP);  // the next pass (the next block's first after the last)
+  };
+  // one pass over RPP rows from the register set (d0, d1): the prologue, the next loads of
+  // the set (dist passes ahead; with the block's F2 fragments first when F2LOAD), the FFT
+  // and the half spectrum into s_rt
+  auto pass = [&](float2 (&d0)[16], float2 (&d1)[16], int pi, int dist, auto f2_tag) {
+    float2 v[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const float2 w = (PIN == PLANE_GELU_GRAD) ? d1[s] : make_float2(0.f, 0.f);
+      v[s] = make_float2(prologue<PIN>(d0[s].x, w.x), prologue<PIN>(d0[s].y, w.y));
+    }
+    const bool ok = pass_row(pi) < r_end;
+    if constexpr (decltype(f2_tag)::value) load_f2(r_begin + 64 * (pi / PASSES));
+    load_to(d0, d1, pi + dist);
 
-      // pass 1: radix 16 in registers, output at 16 gi + t (padded index 18 gi + t)
-      float2 y[16];
-      dft<16>(v, y);
+    // pass 1: radix 16 in registers, output at 16 gi + t (padded index 18 gi + t)
+    float2 y[16];
+    dft<16>(v, y);
 #pragma unroll
-      for (int t = 0; t < 16; t += 2)
-        *reinterpret_cast<float4*>(row_buf + 18 * gi + t) =
-            make_float4(y[t].x, y[t].y, y[t + 1].x, y[t + 1].y);
-      // a row's lanes are one wave's: LDS operations of a wave complete in order, so a
-      // scheduling barrier is all that the exchange needs
-      __builtin_amdgcn_wave_barrier();
+    for (int t = 0; t < 16; t += 2)
+      *reinterpret_cast<float4*>(row_buf + 18 * gi + t) =
+          make_float4(y[t].x, y[t].y, y[t + 1].x, y[t + 1].y);
+    // a row's lanes are one wave's: LDS operations of a wave complete in order, so a
+    // scheduling barrier is all that the exchange needs
+    __builtin_amdgcn_wave_barrier();
 
-      // pass 2: radix L; keep Z[i2 + 16 t] for t in {0, 1, L-2, L-1} (TN = 4) or {0, L-1}
-      float2 zs[U2][TN];
+    // pass 2: radix L; keep Z[i2 + 16 t] for t in {0, 1, L-2, L-1} (TN = 4) or {0, L-1}
+    float2 zs[U2][TN];
 #pragma unroll
-      for (int u = 0; u < U2; ++u) {
-        const int i2 = gi + L * u;
-        float2 w[L], Z[L];
+    for (int u = 0; u < U2; ++u) {
+      const int i2 = gi + L * u;
+      float2 w[L], Z[L];
 #pragma unroll
-        for (int t = 0; t < L; ++t) {
-          const float2 e = row_buf[i2 + 18 * t];
-          w[t] = t == 0 ? e : c_mul(e, tw[u][t]);
-        }
-        dft<L>(w, Z);
-#pragma unroll
-        for (int sl = 0; sl < TN; ++sl) zs[u][sl] = Z[sl < TN / 2 ? sl : L - TN + sl];
+      for (int t = 0; t < L; ++t) {
+        const float2 e = row_buf[i2 + 18 * t];
+        w[t] = t == 0 ? e : c_mul(e, tw[u][t]);
       }
-      __builtin_amdgcn_wave_barrier();
-      // kept outputs, slot sl at 16 sl + i2: Z[k] for k < 16 TN / 2 sits at index k
+      dft<L>(w, Z);
 #pragma unroll
-      for (int u = 0; u < U2; ++u)
+      for (int sl = 0; sl < TN; ++sl) zs[u][sl] = Z[sl < TN / 2 ? sl : L - TN + sl];
+    }
+    __builtin_amdgcn_wave_barrier();
+    // kept outputs, slot sl at 16 sl + i2: Z[k] for k < 16 TN / 2 sits at index k
 #pragma unroll
-        for (int sl = 0; sl < TN; ++sl) row_buf[16 * sl + gi + L * u] = zs[u][sl];
-      __builtin_amdgcn_wave_barrier();
+    for (int u = 0; u < U2; ++u)
+#pragma unroll
+      for (int sl = 0; sl < TN; ++sl) row_buf[16 * sl + gi + L * u] = zs[u][sl];
+    __builtin_amdgcn_wave_barrier();
 
-      // half spectrum of the real row, written transposed for the next-axis product
-      const int rin = ps * RPP + wave * RPW + rw;
+    // half spectrum of the real row, written transposed for the next-axis product
+    const int rin = (pi % PASSES) * RPP + wave * RPW + rw;
 #pragma unroll
-      for (int vv = 0; vv < KPL; ++vv) {
-        const int k = gi + L * vv;
-        if (k < JP2) {
-          float re = 0.f, im = 0.f;
-          if (k < a.mb) {
-            const float2 zk = row_buf[k];
-            // Z[M - k]: slot TN-1 holds Z[M-16 .. M-1], slot TN-2 (TN = 4) Z[M-32 .. M-17]
-            const int km = k == 0 ? 0 : (k <= 16 ? 16 * (TN - 1) + 16 - k : 16 * (TN - 2) + 32 - k);
-            const float2 zm = row_buf[km];
-            const float sr = zk.x + zm.x, si = zk.y - zm.y;  // Z[k] + conj Z[M-k]
-            const float dr = zk.x - zm.x, di = zk.y + zm.y;  // Z[k] - conj Z[M-k]
-            const float c = hw[vv].x, sn = hw[vv].y;
-            re = 0.5f * (sr + c * di - sn * dr);
-            im = 0.5f * (si - c * dr - sn * di);
-          }
-          s_rt[(2 * k) * RS + rin] = re;
-          s_rt[(2 * k + 1) * RS + rin] = im;
+    for (int vv = 0; vv < KPL; ++vv) {
+      const int k = gi + L * vv;
+      if (k < JP2) {
+        float re = 0.f, im = 0.f;
+        if (k < a.mb) {
+          const float2 zk = row_buf[k];
+          // Z[M - k]: slot TN-1 holds Z[M-16 .. M-1], slot TN-2 (TN = 4) Z[M-32 .. M-17]
+          const int km = k == 0 ? 0 : (k <= 16 ? 16 * (TN - 1) + 16 - k : 16 * (TN - 2) + 32 - k);
+          const float2 zm = row_buf[km];
+          const float sr = zk.x + zm.x, si = zk.y - zm.y;  // Z[k] + conj Z[M-k]
+          const float dr = zk.x - zm.x, di = zk.y + zm.y;  // Z[k] - conj Z[M-k]
+          const float c = hw[vv].x, sn = hw[vv].y;
+          re = ok ? 0.5f * (sr + c * di - sn * dr) : 0.f;
+          im = ok ? 0.5f * (si - c * dr - sn * di) : 0.f;
         }
+        s_rt[(2 * k) * RS + rin] = re;
+        s_rt[(2 * k + 1) * RS + rin] = im;
       }
     }
+  };
+  // next-axis product of a 64-row block: K-groups of 16 rows; MFMA jj uses row 16 kg + 4 q + jj
+  auto second = [&]() {
     __syncthreads();
-    // next-axis product: K-groups of 16 rows; MFMA jj uses row 16 kg + 4 q + jj
 #pragma unroll
     for (int kg = 0; kg < 4; ++kg) {
       float4 bv[NTJ];
@@ -276,27 +297,48 @@ __global__ void __launch_bounds__(256) k_plane_fft(PlaneArgs a, const float2* __
         bv[v] = *reinterpret_cast<const float4*>(s_rt + (16 * v + m) * RS + 16 * kg + 4 * q);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int it = wave + 4 * u;
-        if (it >= IT) break;
-        const int row0 = r0 + 16 * kg + 4 * q;
-        const int64_t fo = (int64_t)(16 * it + m) * a.Na + row0;
-        float4 av;
-        if (row0 + 4 <= r_end) {
-          av = *reinterpret_cast<const float4*>(f2 + fo);
-        } else {
-          av.x = (row0 + 0 < r_end) ? f2[fo + 0] : 0.f;
-          av.y = (row0 + 1 < r_end) ? f2[fo + 1] : 0.f;
-          av.z = (row0 + 2 < r_end) ? f2[fo + 2] : 0.f;
-          av.w = (row0 + 3 < r_end) ? f2[fo + 3] : 0.f;
-        }
+        if (wave + 4 * u >= IT) break;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
           for (int v = 0; v < NTJ; ++v)
-            x2[u][v] = mfma_f32(cmp4(av, jj), cmp4(bv[v], jj), x2[u][v]);
+            x2[u][v] = mfma_f32(cmp4(fa[kg][u], jj), cmp4(bv[v], jj), x2[u][v]);
       }
     }
     __syncthreads();
+  };
+
+  constexpr std::integral_constant<bool, true> kF2{};
+  constexpr std::integral_constant<bool, false> kNoF2{};
+  float2 pa0[16], pa1[16];
+  // (the gradient prologue reads two fields: two register sets of both would not fit)
+  if constexpr (PASSES >= 2 && PIN != PLANE_GELU_GRAD) {
+    // two register sets alternate over the passes, each reloaded two passes ahead, so one
+    // pass of rows is always in flight while another is transformed; a block's F2 fragments
+    // are loaded in its last pass ahead of that pass's row loads, so waiting for them does
+    // not wait for the rows
+    float2 pb0[16], pb1[16];
+    load_to(pa0, pa1, 0);
+    load_to(pb0, pb1, 1);
+    for (int blk = 0; blk < nblk; ++blk) {
+      const int p0 = blk * PASSES;
+#pragma unroll
+      for (int ps = 0; ps + 2 < PASSES; ps += 2) {
+        pass(pa0, pa1, p0 + ps, 2, kNoF2);
+        pass(pb0, pb1, p0 + ps + 1, 2, kNoF2);
+      }
+      pass(pa0, pa1, p0 + PASSES - 2, 2, kNoF2);
+      pass(pb0, pb1, p0 + PASSES - 1, 2, kF2);
+      second();
+    }
+  } else {
+    load_to(pa0, pa1, 0);
+    for (int blk = 0; blk < nblk; ++blk) {
+#pragma unroll
+      for (int ps = 0; ps + 1 < PASSES; ++ps) pass(pa0, pa1, blk * PASSES + ps, 1, kNoF2);
+      pass(pa0, pa1, blk * PASSES + PASSES - 1, 1, kF2);
+      second();
+    }
   }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
