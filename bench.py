@@ -202,6 +202,8 @@ def kernel_model(wl, prec):
         "mix_fwd": (max(wbytes, wdense) + 2 * spec, mixf, 0, False),
         "mix_bwd_dx": (max(wbytes, wdense) + 2 * spec, mixf, 0, False),
         "mix_bwd_dw": (max(wbytes, wdense) + 2 * spec, mixf, 0, False),
+        # both gradients in one launch: W in, dW out, the spectra (g, x in, g_x out)
+        "mix_bwd": (2 * max(wbytes, wdense) + 3 * spec, 2 * mixf, 0, False),
         # x in, y out (+ z saved for the backward)
         "epilogue_fwd": (8 * U + T, fft_last, bypass, split),
         "epilogue_fwd_zsave": (12 * U + T, fft_last, bypass, split),

@@ -142,6 +142,9 @@ hipError_t launch_mix_bwd_dx(const fno_plan* p, const float2* ghat, const float2
                              float2* ghx, hipStream_t s);
 hipError_t launch_mix_bwd_dw(const fno_plan* p, const float2* xhat, const float2* ghat,
                              float2* dw, hipStream_t s);
+// both mix gradients (ghx and dw) in one launch
+hipError_t launch_mix_bwd_both(const fno_plan* p, const float2* xhat, const float2* ghat,
+                               const float2* w, float2* ghx, float2* dw, hipStream_t s);
 // The same on an explicit geometry and per-mode weight offsets (woff[t] = offset of mode t
 // inside one [Cin][Cout] weight slab; input-channel stride Cout * Mprod, output stride Mprod).
 hipError_t launch_mix_fwd_g(const Geom& g, const int32_t* woff, const float2* xhat,

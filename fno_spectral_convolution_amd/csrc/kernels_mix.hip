@@ -86,24 +86,22 @@ __device__ __forceinline__ void put_out(unsigned char* out, int t, int m, int q,
 // Forward (DX = false) and input gradient (DX = true).  Grid: (mode groups, 16-column tiles of
 // the output channels, 8-entry batch tiles).  Contracted channels: Cin (forward) or Cout.
 template <int H, bool DX>
-__global__ void __launch_bounds__(256) k_mix_mfma(Geom g, const int32_t* __restrict__ mode_woff,
-                                                  const float2* __restrict__ spec,
-                                                  const float2* __restrict__ w,
-                                                  float2* __restrict__ out) {
+__device__ __forceinline__ void mix_body(const Geom& g, const int32_t* __restrict__ mode_woff,
+                                         const float2* __restrict__ spec,
+                                         const float2* __restrict__ w, float2* __restrict__ out,
+                                         uint3 bid, unsigned char* s_a, unsigned char* s_b) {
   constexpr bool BF = H != 0;       // half operands (bfloat16 or IEEE half)
   constexpr int IC = BF ? 16 : 8;  // contracted channels per chunk (K = 2 IC)
   constexpr int NW = 16 * IC / 16;  // weight complex values per thread per chunk (16 modes x IC x 16 cols / 256)
   constexpr int NS = 8 * IC / 16;   // spectrum values per thread per chunk (16 modes x 8 x IC / 256)
-  __shared__ __attribute__((aligned(16))) unsigned char s_a[kMT * kTB];
-  __shared__ __attribute__((aligned(16))) unsigned char s_b[kMT * kTB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, q = lane >> 4;
   const int64_t K = g.K;
   const int ncon = DX ? g.Cout : g.Cin;  // contracted
   const int nout = DX ? g.Cin : g.Cout;  // columns
-  const int64_t t0 = (int64_t)blockIdx.x * kMT;
-  const int n0 = blockIdx.y * 16;
-  const int b0 = blockIdx.z * 8;
+  const int64_t t0 = (int64_t)bid.x * kMT;
+  const int n0 = bid.y * 16;
+  const int b0 = bid.z * 8;
   // every load of this thread is for mode t0 + (tid & 15); offsets fit in 32 bits (fields and
   // weights are limited to 2^31 elements)
   const int tl = tid & 15;
@@ -180,29 +178,39 @@ __global__ void __launch_bounds__(256) k_mix_mfma(Geom g, const int32_t* __restr
   }
 }
 
+template <int H, bool DX>
+__global__ void __launch_bounds__(256) k_mix_mfma(Geom g, const int32_t* __restrict__ mode_woff,
+                                                  const float2* __restrict__ spec,
+                                                  const float2* __restrict__ w,
+                                                  float2* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) unsigned char s_a[kMT * kTB];
+  __shared__ __attribute__((aligned(16))) unsigned char s_b[kMT * kTB];
+  mix_body<H, DX>(g, mode_woff, spec, w, out, make_uint3(blockIdx.x, blockIdx.y, blockIdx.z),
+                  s_a, s_b);
+}
+
 // ------------------------------------------------------------------------------------------
 // Weight gradient.  Grid: (mode groups, gridDim.y parts of the 8-channel tiles of Cin, 16-column
 // tiles of Cout): a work-group walks the Cin tiles y, y + gridDim.y, ..., and the first batch
 // chunk of the next tile is loaded while the current one is computed and stored.
 // Rows 0..7: Re, rows 8..15: Im of the 8 input channels; K = (batch entry, re / im).
 template <int H>
-__global__ void __launch_bounds__(256) k_mix_mfma_dw(Geom g, const int32_t* __restrict__ mode_woff,
-                                                     const float2* __restrict__ xhat,
-                                                     const float2* __restrict__ ghat,
-                                                     float2* __restrict__ dw) {
+__device__ __forceinline__ void mix_dw_body(const Geom& g, const int32_t* __restrict__ mode_woff,
+                                            const float2* __restrict__ xhat,
+                                            const float2* __restrict__ ghat,
+                                            float2* __restrict__ dw, uint3 bid, int nparts,
+                                            unsigned char* s_a, unsigned char* s_b) {
   constexpr bool BF = H != 0;
   constexpr int BC = BF ? 16 : 8;  // batch entries per chunk (K = 2 BC)
   constexpr int NX = 8 * BC / 16;   // x values per thread per chunk (16 modes x 8 ch x BC / 256)
   constexpr int NG = 16 * BC / 16;  // g values per thread per chunk (16 modes x 16 ch x BC / 256)
   bool bad = false;  // IEEE-half plans: a non-finite weight gradient was written
-  __shared__ __attribute__((aligned(16))) unsigned char s_a[kMT * kTB];
-  __shared__ __attribute__((aligned(16))) unsigned char s_b[kMT * kTB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, q = lane >> 4;
   const int64_t K = g.K;
-  const int64_t t0 = (int64_t)blockIdx.x * kMT;
-  const int istride = gridDim.y * 8;
-  const int o0 = blockIdx.z * 16;
+  const int64_t t0 = (int64_t)bid.x * kMT;
+  const int istride = nparts * 8;
+  const int o0 = bid.z * 16;
   const int tl = tid & 15;
   const int tm = (int)min(t0 + tl, K - 1);
   const int Ki = (int)K;
@@ -225,8 +233,8 @@ __global__ void __launch_bounds__(256) k_mix_mfma_dw(Geom g, const int32_t* __re
       pg[u] = ghat[(b * g.Cout + ocol) * Ki + tm];
     }
   };
-  load_chunk(blockIdx.y * 8, 0);
-  for (int i0 = blockIdx.y * 8; i0 < g.Cin; i0 += istride) {
+  load_chunk(bid.y * 8, 0);
+  for (int i0 = bid.y * 8; i0 < g.Cin; i0 += istride) {
     f32x4 acc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] = zero4();
@@ -280,6 +288,42 @@ __global__ void __launch_bounds__(256) k_mix_mfma_dw(Geom g, const int32_t* __re
   if constexpr (H == 2) raise_half_flag(g.half_flag, bad);
 }
 
+template <int H>
+__global__ void __launch_bounds__(256) k_mix_mfma_dw(Geom g, const int32_t* __restrict__ mode_woff,
+                                                     const float2* __restrict__ xhat,
+                                                     const float2* __restrict__ ghat,
+                                                     float2* __restrict__ dw) {
+  __shared__ __attribute__((aligned(16))) unsigned char s_a[kMT * kTB];
+  __shared__ __attribute__((aligned(16))) unsigned char s_b[kMT * kTB];
+  mix_dw_body<H>(g, mode_woff, xhat, ghat, dw, make_uint3(blockIdx.x, blockIdx.y, blockIdx.z),
+                 gridDim.y, s_a, s_b);
+}
+
+// Both gradients of the mix in one launch: the first ndx work-groups take the input gradient
+// (grid gdx), the rest the weight gradient (grid gdw).  The two read the same incoming spectrum
+// and are otherwise independent; in one grid each fills the other's ramp and tail.
+template <int H>
+__global__ void __launch_bounds__(256) k_mix_mfma_bwd(Geom g, const int32_t* __restrict__ mode_woff,
+                                                      const float2* __restrict__ xhat,
+                                                      const float2* __restrict__ ghat,
+                                                      const float2* __restrict__ w,
+                                                      float2* __restrict__ ghx,
+                                                      float2* __restrict__ dw, uint3 gdx,
+                                                      uint3 gdw) {
+  __shared__ __attribute__((aligned(16))) unsigned char s_a[kMT * kTB];
+  __shared__ __attribute__((aligned(16))) unsigned char s_b[kMT * kTB];
+  const uint32_t ndx = gdx.x * gdx.y * gdx.z;
+  uint32_t i = blockIdx.x;
+  if (i < ndx) {
+    const uint3 bid = make_uint3(i % gdx.x, (i / gdx.x) % gdx.y, i / (gdx.x * gdx.y));
+    mix_body<H, true>(g, mode_woff, ghat, w, ghx, bid, s_a, s_b);
+  } else {
+    i -= ndx;
+    const uint3 bid = make_uint3(i % gdw.x, (i / gdw.x) % gdw.y, i / (gdw.x * gdw.y));
+    mix_dw_body<H>(g, mode_woff, xhat, ghat, dw, bid, (int)gdw.y, s_a, s_b);
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 static dim3 mix_grid(const Geom& g, int cols) {
   return dim3((unsigned)((g.K + kMT - 1) / kMT), (unsigned)((cols + 15) / 16),
@@ -314,14 +358,19 @@ hipError_t launch_mix_bwd_dx_g(const Geom& g, const int32_t* woff, const float2*
   return hipGetLastError();
 }
 
-hipError_t launch_mix_bwd_dw_g(const Geom& g, const int32_t* woff, const float2* xhat,
-                               const float2* ghat, float2* dw, hipStream_t s) {
-  // Cin tiles per work-group: about 1024 work-groups in all, at most every tile in one
+// weight-gradient grid: (mode groups, parts of the Cin tiles, Cout tiles); Cin tiles per
+// work-group: about 1024 work-groups in all, at most every tile in one
+static dim3 mix_dw_grid(const Geom& g) {
   const int64_t mg = (g.K + kMT - 1) / kMT, ot = (g.Cout + 15) / 16, itiles = (g.Cin + 7) / 8;
   int64_t parts = (1024 + mg * ot - 1) / (mg * ot);
   if (parts > itiles) parts = itiles;
   if (parts < 1) parts = 1;
-  const dim3 grid((unsigned)mg, (unsigned)parts, (unsigned)ot);
+  return dim3((unsigned)mg, (unsigned)parts, (unsigned)ot);
+}
+
+hipError_t launch_mix_bwd_dw_g(const Geom& g, const int32_t* woff, const float2* xhat,
+                               const float2* ghat, float2* dw, hipStream_t s) {
+  const dim3 grid = mix_dw_grid(g);
   if (g.half == 2)
     hipLaunchKernelGGL((k_mix_mfma_dw<2>), grid, dim3(256), 0, s, g, woff, xhat, ghat, dw);
   else if (g.half == 1)
@@ -346,6 +395,26 @@ hipError_t launch_mix_bwd_dx(const fno_plan* p, const float2* ghat, const float2
 hipError_t launch_mix_bwd_dw(const fno_plan* p, const float2* xhat, const float2* ghat,
                              float2* dw, hipStream_t s) {
   return launch_mix_bwd_dw_g(p->g, p->t.mode_woff, xhat, ghat, dw, s);
+}
+
+hipError_t launch_mix_bwd_both(const fno_plan* p, const float2* xhat, const float2* ghat,
+                               const float2* w, float2* ghx, float2* dw, hipStream_t s) {
+  const Geom& g = p->g;
+  const dim3 gx = mix_grid(g, g.Cin), gw = mix_dw_grid(g);
+  const uint64_t n = (uint64_t)gx.x * gx.y * gx.z + (uint64_t)gw.x * gw.y * gw.z;
+  if (n > 0x7fffffffu) return hipErrorInvalidValue;
+  const uint3 ux = make_uint3(gx.x, gx.y, gx.z), uw = make_uint3(gw.x, gw.y, gw.z);
+  const int32_t* woff = p->t.mode_woff;
+  if (g.half == 2)
+    hipLaunchKernelGGL((k_mix_mfma_bwd<2>), dim3((unsigned)n), dim3(256), 0, s, g, woff, xhat,
+                       ghat, w, ghx, dw, ux, uw);
+  else if (g.half == 1)
+    hipLaunchKernelGGL((k_mix_mfma_bwd<1>), dim3((unsigned)n), dim3(256), 0, s, g, woff, xhat,
+                       ghat, w, ghx, dw, ux, uw);
+  else
+    hipLaunchKernelGGL((k_mix_mfma_bwd<0>), dim3((unsigned)n), dim3(256), 0, s, g, woff, xhat,
+                       ghat, w, ghx, dw, ux, uw);
+  return hipGetLastError();
 }
 
 }  // namespace fno

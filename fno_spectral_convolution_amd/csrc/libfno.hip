@@ -787,6 +787,12 @@ struct DenseMix final : WeightMix {
   }
   fno_status bwd(const float2* xhat, const float2* ghat, float2* ghx, void*,
                  hipStream_t s) const override {
+    // one launch for both unless ghx overwrites the xhat that the weight gradient reads (a
+    // recomputed spectrum shares its workspace region): then the weight gradient goes first
+    if (grad_w && ghx && static_cast<const void*>(ghx) != static_cast<const void*>(xhat)) {
+      LAUNCH("mix_bwd", s, fno::launch_mix_bwd_both(p, xhat, ghat, w, ghx, grad_w, s));
+      return FNO_OK;
+    }
     if (grad_w) LAUNCH("mix_bwd_dw", s, fno::launch_mix_bwd_dw(p, xhat, ghat, grad_w, s));
     if (ghx) LAUNCH("mix_bwd_dx", s, fno::launch_mix_bwd_dx(p, ghat, w, ghx, s));
     return FNO_OK;
