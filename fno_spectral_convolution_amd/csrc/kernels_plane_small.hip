@@ -22,6 +22,7 @@
 #include "fno_internal.h"
 #include "mfma.h"
 #include "pointwise.h"
+#include "split6.h"
 
 namespace fno {
 
@@ -47,9 +48,11 @@ __device__ __forceinline__ float small_prologue(float v, float w) {
   return v;
 }
 
-// MT = Na / 16 row tiles, NTJ = jpad / 16 column tiles
-template <int PIN, int H, int MT, int NTJ>
+// MT = Na / 16 row tiles, NTJ = jpad / 16 column tiles.  E6 (float32 plans): both products
+// as six bfloat16 products of three-way split operands (split6.h), float32 to its rounding.
+template <int PIN, int H, int MT, int NTJ, bool E6 = false>
 __global__ void __launch_bounds__(256) k_plane_small(SmallPlaneArgs a) {
+  static_assert(!E6 || H == 0, "the split products stand in for float32 ones");
   constexpr bool BF = H != 0;  // half operands (bfloat16 or IEEE half)
   using HT = HalfOf<H>;
   using V8 = typename HT::v8;
@@ -59,20 +62,29 @@ __global__ void __launch_bounds__(256) k_plane_small(SmallPlaneArgs a) {
   extern __shared__ __attribute__((aligned(16))) float s_sp[];
   const int Na = 16 * MT;
   const int F2S = Na + 4;                    // F2 row stride (floats; f32 path)
-  const int F2H = Na + 8;                    // F2 row stride (bf16 elements; bf16 path)
+  const int F2H = Na + 8;                    // F2 row stride (16-bit elements; half and E6)
   const int ROWS2 = 4 * a.ma;                // F2 rows
   const int MT2 = ROWS2 / 16;                // F2 row tiles (ma % 4 == 0)
-  // F2 in LDS: f32 [4 ma][F2S], or the bf16 pair hi [4 ma][F2H], lo [4 ma][F2H]
+  // F2 in LDS: f32 [4 ma][F2S]; the half pair hi [4 ma][F2H], lo [4 ma][F2H]; or (E6) the
+  // bfloat16 split terms hi, mid, lo, each [4 ma][F2H]
   float* s_f2 = s_sp;
   uint16_t* s_f2h = reinterpret_cast<uint16_t*>(s_sp);
   uint16_t* s_f2l = s_f2h + ROWS2 * F2H;
-  const int f2_floats = BF ? ROWS2 * F2H : ROWS2 * F2S;  // the same bytes either way
+  uint16_t* s_f2m = s_f2l + ROWS2 * F2H;     // E6: the middle term (after hi and lo)
+  const int f2_floats = E6 ? (3 * ROWS2 * F2H + 3) / 4 * 2
+                           : (BF ? ROWS2 * F2H : ROWS2 * F2S);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, q = lane >> 4;
   float* s_w = s_sp + f2_floats + wave * (ROWS2 * JP);  // this wave's X2 tile [4 ma][JP]
   for (int e = tid; e < ROWS2 * Na; e += 256) {
     const int i = e / Na, r = e - i * Na;
-    if (BF) {
+    if constexpr (E6) {
+      __bf16 h, mi, lo;
+      split3(a.f2[e], h, mi, lo);
+      s_f2h[i * F2H + r] = __builtin_bit_cast(uint16_t, h);
+      s_f2m[i * F2H + r] = __builtin_bit_cast(uint16_t, mi);
+      s_f2l[i * F2H + r] = __builtin_bit_cast(uint16_t, lo);
+    } else if (BF) {
       s_f2h[i * F2H + r] = a.f2bf[e];
       s_f2l[i * F2H + r] = a.f2lo[e];
     } else {
@@ -82,8 +94,9 @@ __global__ void __launch_bounds__(256) k_plane_small(SmallPlaneArgs a) {
   // T1 fragments: B[k = 8 q + slot][n = 16 nt + m]; zero past Nb
   float t1r[NTJ][8];
   V8 t1b[NTJ];
+  bf16x8 t1h[E6 ? NTJ : 1], t1m[E6 ? NTJ : 1], t1l[E6 ? NTJ : 1];
 #pragma unroll
-  for (int nt = 0; nt < NTJ; ++nt)
+  for (int nt = 0; nt < NTJ; ++nt) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int c = 8 * q + s;
@@ -93,6 +106,8 @@ __global__ void __launch_bounds__(256) k_plane_small(SmallPlaneArgs a) {
       t1r[nt][s] = c < a.Nb ? v : 0.f;
       t1b[nt][s] = (E)t1r[nt][s];  // exact: t1r holds a half value (or zero)
     }
+    if constexpr (E6) split3_bf16x8(t1r[nt], t1h[nt], t1m[nt], t1l[nt]);
+  }
   __syncthreads();
   const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
   const int64_t nw = (int64_t)gridDim.x * 4;
@@ -135,10 +150,14 @@ __global__ void __launch_bounds__(256) k_plane_small(SmallPlaneArgs a) {
         if (BF) v = round_half<H>(v);
         xv[s] = __uint_as_float(__float_as_uint(v) & (live ? 0xffffffffu : 0u));
       }
+      bf16x8 xh, xm, xl;
+      if constexpr (E6) split3_bf16x8(xv, xh, xm, xl);
 #pragma unroll
       for (int nt = 0; nt < NTJ; ++nt) {
         f32x4 acc = zero4();
-        if constexpr (BF) {
+        if constexpr (E6) {
+          acc = mfma_split6(xh, xm, xl, t1h[nt], t1m[nt], t1l[nt], acc);
+        } else if constexpr (BF) {
           V8 av;
 #pragma unroll
           for (int s = 0; s < 8; ++s) av[s] = (E)xv[s];  // exact: already rounded
@@ -159,7 +178,34 @@ __global__ void __launch_bounds__(256) k_plane_small(SmallPlaneArgs a) {
       f32x4 x2[NTJ];
 #pragma unroll
       for (int nt = 0; nt < NTJ; ++nt) x2[nt] = zero4();
-      if constexpr (!BF) {
+      if constexpr (E6) {
+        // second product as the half path orders it (K-step p, slot (q, e) <-> row
+        // 16 (2 p + e / 4) + 4 q + e % 4), on the split terms of F2 and of R
+        const uint16_t* fh = s_f2h + (16 * mt2 + m) * F2H + 4 * q;
+        const uint16_t* fm = s_f2m + (16 * mt2 + m) * F2H + 4 * q;
+        const uint16_t* fl = s_f2l + (16 * mt2 + m) * F2H + 4 * q;
+        auto frag = [&](const uint16_t* f, int pp) {
+          const uint2 v0 = *reinterpret_cast<const uint2*>(f + 32 * pp);
+          uint2 v1 = make_uint2(0u, 0u);
+          if (2 * pp + 1 < MT) v1 = *reinterpret_cast<const uint2*>(f + 32 * pp + 16);
+          return __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+        };
+#pragma unroll
+        for (int pp = 0; pp < (MT + 1) / 2; ++pp) {
+          const int t0 = 2 * pp, t1 = min(2 * pp + 1, MT - 1);
+          const bf16x8 ah = frag(fh, pp), am = frag(fm, pp), al = frag(fl, pp);
+#pragma unroll
+          for (int nt = 0; nt < NTJ; ++nt) {
+            const bool two = 2 * pp + 1 < MT;  // compile-time after unrolling
+            const float bvals[8] = {d[t0][nt][0], d[t0][nt][1], d[t0][nt][2], d[t0][nt][3],
+                                    two ? d[t1][nt][0] : 0.f, two ? d[t1][nt][1] : 0.f,
+                                    two ? d[t1][nt][2] : 0.f, two ? d[t1][nt][3] : 0.f};
+            bf16x8 bh, bm, bl;
+            split3_bf16x8(bvals, bh, bm, bl);
+            x2[nt] = mfma_split6(ah, am, al, bh, bm, bl, x2[nt]);
+          }
+        }
+      } else if constexpr (!BF) {
         // second product: K-step 4 t + r, k-slot q <-> row 16 t + 4 q + r
         const float* fr = s_f2 + (16 * mt2 + m) * F2S + 4 * q;
 #pragma unroll
@@ -237,19 +283,30 @@ bool plane_small_ok(const fno_plan* p) {
 template <int PIN, int H, int MT>
 static void launch_small_t(const fno_plan* p, const SmallPlaneArgs& a, hipStream_t s) {
   const int jp = p->jpad;
-  const size_t lds = sizeof(float) * (4 * a.ma * (a.Na + (H != 0 ? 8 : 4)) + 4 * (4 * a.ma) * jp);
+  const int rows2 = 4 * a.ma;
   const int64_t want = (a.planes + 3) / 4;
   const unsigned grid = (unsigned)(want < 2048 ? want : 2048);
-  if (lds > 65536) {  // wide row spectra need more than the default dynamic LDS limit
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_plane_small<PIN, H, MT, 1>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_plane_small<PIN, H, MT, 2>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const size_t xw = 4 * (size_t)rows2 * jp;  // the waves' X2 tiles (floats)
+  // wide row spectra need more than the default dynamic LDS limit
+  auto lds_limit = [](const void* k, size_t bytes) {
+    if (bytes > 65536)
+      (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  };
+  if (jp == 16) {
+    // float32 plans with one column tile: the split bfloat16 products (with two tiles, or
+    // the gradient prologue's second field, the split operands would cost the kernel half
+    // its occupancy)
+    constexpr bool E6 = H == 0 && PIN != PLANE_GELU_GRAD;
+    const size_t f2 = E6 ? (size_t)(3 * rows2 * (a.Na + 8) + 3) / 4 * 2
+                         : (size_t)rows2 * (a.Na + (H != 0 ? 8 : 4));
+    const size_t lds = sizeof(float) * (f2 + xw);
+    lds_limit(reinterpret_cast<const void*>(k_plane_small<PIN, H, MT, 1, E6>), lds);
+    hipLaunchKernelGGL((k_plane_small<PIN, H, MT, 1, E6>), dim3(grid), dim3(256), lds, s, a);
+  } else {
+    const size_t lds = sizeof(float) * ((size_t)rows2 * (a.Na + (H != 0 ? 8 : 4)) + xw);
+    lds_limit(reinterpret_cast<const void*>(k_plane_small<PIN, H, MT, 2, false>), lds);
+    hipLaunchKernelGGL((k_plane_small<PIN, H, MT, 2, false>), dim3(grid), dim3(256), lds, s, a);
   }
-  if (jp == 16)
-    hipLaunchKernelGGL((k_plane_small<PIN, H, MT, 1>), dim3(grid), dim3(256), lds, s, a);
-  else
-    hipLaunchKernelGGL((k_plane_small<PIN, H, MT, 2>), dim3(grid), dim3(256), lds, s, a);
 }
 
 template <int PIN, int H>
