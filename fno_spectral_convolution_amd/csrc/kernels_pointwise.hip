@@ -58,6 +58,9 @@ __device__ __forceinline__ void pw_tile(const float* __restrict__ w, int ldw, in
   }
 }
 
+// NOUT = 1 .. kPwSmallOut: a projection to exactly NOUT channels (the narrow path below);
+// NOUT = 0: every other shape
+template <int NOUT>
 __global__ void __launch_bounds__(256)
 k_pointwise_mfma(int64_t npts, int cin, int hidden, int cout, const float* __restrict__ x,
                  const float* __restrict__ w1, const float* __restrict__ b1,
@@ -108,15 +111,15 @@ k_pointwise_mfma(int64_t npts, int cin, int hidden, int cout, const float* __res
     }
   }
   __syncthreads();
-  if (hidden > 0 && cout <= kPwSmallOut) {
+  if constexpr (NOUT > 0) {
     // narrow output (the projection to a few channels): the second product runs on the
     // VALU from the GELU'd fragments of the first, without the hidden tile.  Lane (m, q) adds
     // W2[o][h] GELU(.)[h][p] over its rows h = 16 mt + 4 q + r for points p = 16 nt + m; the
     // four lane quarters are then summed by two xor butterflies and the four waves in order
     // (a fixed order: deterministic).
-    float part[kPwSmallOut][4];
+    float part[NOUT][4];
 #pragma unroll
-    for (int o = 0; o < kPwSmallOut; ++o)
+    for (int o = 0; o < NOUT; ++o)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) part[o][nt] = 0.f;
     for (int mt = wave; mt < mid_p / 16; mt += 4) {
@@ -128,43 +131,42 @@ k_pointwise_mfma(int64_t npts, int cin, int hidden, int cout, const float* __res
       for (int r = 0; r < 4; ++r) {
         const int h = 16 * mt + 4 * q + r;
         const float bh = masked_bias(b1, h, mid);
-        float w2v[kPwSmallOut];
+        float w2v[NOUT];
 #pragma unroll
-        for (int o = 0; o < kPwSmallOut; ++o) {
-          const float wv = w2[min(o, cout - 1) * hidden + min(h, hidden - 1)];
-          w2v[o] = __uint_as_float(__float_as_uint(wv) &
-                                   ((o < cout && h < hidden) ? 0xffffffffu : 0u));
+        for (int o = 0; o < NOUT; ++o) {
+          const float wv = w2[o * hidden + min(h, hidden - 1)];
+          w2v[o] = __uint_as_float(__float_as_uint(wv) & (h < hidden ? 0xffffffffu : 0u));
         }
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
           const float gv = gelu_as(acc[nt][r] + bh);
 #pragma unroll
-          for (int o = 0; o < kPwSmallOut; ++o) part[o][nt] = fmaf(w2v[o], gv, part[o][nt]);
+          for (int o = 0; o < NOUT; ++o) part[o][nt] = fmaf(w2v[o], gv, part[o][nt]);
         }
       }
     }
-    float* s_red = s_h;  // [4 waves][kPwSmallOut][kPwP]
+    float* s_red = s_h;  // [4 waves][NOUT][kPwP]
 #pragma unroll
-    for (int o = 0; o < kPwSmallOut; ++o)
+    for (int o = 0; o < NOUT; ++o)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         float v = part[o][nt];
         v += __shfl_xor(v, 16);
         v += __shfl_xor(v, 32);
-        if (q == 0) s_red[(wave * kPwSmallOut + o) * kPwP + 16 * nt + m] = v;
+        if (q == 0) s_red[(wave * NOUT + o) * kPwP + 16 * nt + m] = v;
       }
     __syncthreads();
-    for (int e = tid; e < cout * (kPwP / 4); e += 256) {
+    for (int e = tid; e < NOUT * (kPwP / 4); e += 256) {
       const int o = e / (kPwP / 4), c4 = e % (kPwP / 4);
       const float bo = masked_bias(b2, o, cout);
       float v[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int pp = 4 * c4 + j;
-        v[j] = bo + (((s_red[(0 * kPwSmallOut + o) * kPwP + pp] +
-                       s_red[(1 * kPwSmallOut + o) * kPwP + pp]) +
-                      s_red[(2 * kPwSmallOut + o) * kPwP + pp]) +
-                     s_red[(3 * kPwSmallOut + o) * kPwP + pp]);
+        v[j] = bo + (((s_red[(0 * NOUT + o) * kPwP + pp] +
+                       s_red[(1 * NOUT + o) * kPwP + pp]) +
+                      s_red[(2 * NOUT + o) * kPwP + pp]) +
+                     s_red[(3 * NOUT + o) * kPwP + pp]);
       }
       float* dst = y + ((int64_t)b * cout + o) * npts + p0 + 4 * c4;
       if (4 * c4 + 4 <= np && (npts % 4) == 0) {
@@ -241,12 +243,24 @@ hipError_t launch_pointwise(int64_t batch, int64_t npts, int cin, int hidden, in
   const int64_t tiles = (npts + kPwP - 1) / kPwP;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
   if (lds > 65536) {  // wide hidden layers need more than the default dynamic LDS limit
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_pointwise_mfma),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_pointwise_mfma<0>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_pointwise_mfma, dim3((unsigned)tiles, (unsigned)batch), dim3(256), lds,
-                     s, npts, cin, hidden, cout, x, w1, b1, w2, b2, y);
+  const dim3 grid((unsigned)tiles, (unsigned)batch);
+  const int nout = (hidden > 0 && cout <= kPwSmallOut) ? cout : 0;
+  switch (nout) {
+    case 1: hipLaunchKernelGGL((k_pointwise_mfma<1>), grid, dim3(256), lds, s, npts, cin, hidden,
+                               cout, x, w1, b1, w2, b2, y); break;
+    case 2: hipLaunchKernelGGL((k_pointwise_mfma<2>), grid, dim3(256), lds, s, npts, cin, hidden,
+                               cout, x, w1, b1, w2, b2, y); break;
+    case 3: hipLaunchKernelGGL((k_pointwise_mfma<3>), grid, dim3(256), lds, s, npts, cin, hidden,
+                               cout, x, w1, b1, w2, b2, y); break;
+    case 4: hipLaunchKernelGGL((k_pointwise_mfma<4>), grid, dim3(256), lds, s, npts, cin, hidden,
+                               cout, x, w1, b1, w2, b2, y); break;
+    default: hipLaunchKernelGGL((k_pointwise_mfma<0>), grid, dim3(256), lds, s, npts, cin,
+                                hidden, cout, x, w1, b1, w2, b2, y); break;
+  }
   return hipGetLastError();
 }
 
