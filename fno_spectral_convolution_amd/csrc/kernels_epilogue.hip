@@ -350,7 +350,7 @@ k_epi_fwd_line(EpiArgs a) {
   GtFrag<G, H> gtf;
   if (BLK) {
 #pragma unroll
-    for (int u = 0; u < NPT; ++u) pre[u] = *reinterpret_cast<const float4*>(a.x + goff[u]);
+    for (int u = 0; u < NPT; ++u) pre[u] = load_stream4(a.x + goff[u]);
   }
   load_gt<G, H, true, MT>(a, 0, tbase, m, q, gtf);
   // narrow fields have few steps per line: the next line's spectrum rows stream in while
@@ -388,11 +388,11 @@ k_epi_fwd_line(EpiArgs a) {
         if constexpr (MS) {
 #pragma unroll
           for (int u = 0; u < NPT; ++u)
-            ptg[u] = *reinterpret_cast<const float4*>(a.gy + goff[u] + PI * f);
+            ptg[u] = load_stream4(a.gy + goff[u] + PI * f);
         }
 #pragma unroll
         for (int u = 0; u < NPT; ++u)
-          pre[u] = *reinterpret_cast<const float4*>(a.x + goff[u] + PI * fn);
+          pre[u] = load_stream4(a.x + goff[u] + PI * fn);
       }
       __syncthreads();  // x tile and spectrum rows visible; previous z tile consumed
       f32x4 acc[G][NT];
@@ -651,9 +651,9 @@ k_epi_bwd_line(EpiArgs a) {
   GtFrag<G, H> gtf;
 #pragma unroll
   for (int u = 0; u < NPT; ++u) {
-    if (BLK) pg_y[u] = *reinterpret_cast<const float4*>(a.gy + goff[u]);
-    if (GL) pz[u] = *reinterpret_cast<const float4*>(a.zin + goff[u]);
-    if (NX) px[u] = *reinterpret_cast<const float4*>(a.x + goff[u]);
+    if (BLK) pg_y[u] = load_stream4(a.gy + goff[u]);
+    if (GL) pz[u] = load_stream4(a.zin + goff[u]);
+    if (NX) px[u] = load_stream4(a.x + goff[u]);
   }
   load_gt<G, H, true, MT>(a, 0, tbase, m, q, gtf);
   constexpr bool LPF = C < 64;
@@ -698,9 +698,9 @@ k_epi_bwd_line(EpiArgs a) {
       }
 #pragma unroll
       for (int u = 0; u < NPT; ++u) {
-        if (BLK) pg_y[u] = *reinterpret_cast<const float4*>(a.gy + goff[u] + PI * fn);
-        if (GL) pz[u] = *reinterpret_cast<const float4*>(a.zin + goff[u] + PI * fn);
-        if (NX) px[u] = *reinterpret_cast<const float4*>(a.x + goff[u] + PI * fn);
+        if (BLK) pg_y[u] = load_stream4(a.gy + goff[u] + PI * fn);
+        if (GL) pz[u] = load_stream4(a.zin + goff[u] + PI * fn);
+        if (NX) px[u] = load_stream4(a.x + goff[u] + PI * fn);
       }
       __syncthreads();  // g_z / x tiles and spectrum rows visible; previous grad tile consumed
       f32x4 acc[G][NT];

@@ -83,9 +83,9 @@ __global__ void __launch_bounds__(256) k_plane_bf16(PlaneArgs a) {
       pre0[u] = make_float4(0.f, 0.f, 0.f, 0.f);
       pre1[u] = pre0[u];
       if (row < r_end) {
-        pre0[u] = *reinterpret_cast<const float4*>(base0 + (int64_t)row * NB + 4 * c4);
+        pre0[u] = load_stream4(base0 + (int64_t)row * NB + 4 * c4);
         if (PIN == PLANE_GELU_GRAD)
-          pre1[u] = *reinterpret_cast<const float4*>(base1 + (int64_t)row * NB + 4 * c4);
+          pre1[u] = load_stream4(base1 + (int64_t)row * NB + 4 * c4);
       }
     }
   };
@@ -229,9 +229,9 @@ __global__ void __launch_bounds__(256) k_plane_f32(PlaneArgs a) {
       pre0[u] = make_float4(0.f, 0.f, 0.f, 0.f);
       pre1[u] = pre0[u];
       if (row < r_end) {
-        pre0[u] = *reinterpret_cast<const float4*>(base0 + (int64_t)row * NB + 4 * c4);
+        pre0[u] = load_stream4(base0 + (int64_t)row * NB + 4 * c4);
         if (PIN == PLANE_GELU_GRAD)
-          pre1[u] = *reinterpret_cast<const float4*>(base1 + (int64_t)row * NB + 4 * c4);
+          pre1[u] = load_stream4(base1 + (int64_t)row * NB + 4 * c4);
       }
     }
   };
@@ -376,8 +376,8 @@ __global__ void __launch_bounds__(512) k_plane_bf16_lds(PlaneArgs a) {
       const int e = tid + 512 * u;
       const int row = min(r_begin + SUB * n + e / LPR, r_end - 1);
       const int64_t off = (int64_t)row * NB + 4 * (e % LPR);
-      d0[u] = *reinterpret_cast<const float4*>(base0 + off);
-      if (PIN == PLANE_GELU_GRAD) d1[u] = *reinterpret_cast<const float4*>(base1 + off);
+      d0[u] = load_stream4(base0 + off);
+      if (PIN == PLANE_GELU_GRAD) d1[u] = load_stream4(base1 + off);
     }
   };
   // stage sub-round n's rows (tanh / GELU' prologue, bf16); rows past the chunk are zero.

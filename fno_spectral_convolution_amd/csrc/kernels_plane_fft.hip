@@ -193,8 +193,8 @@ __global__ void __launch_bounds__(256) k_plane_fft(PlaneArgs a, const float2* __
     const int64_t off = (int64_t)min(pass_row(pi), r_end - 1) * M + gi;
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
-      d0[s] = base0[off + L * s];
-      if (PIN == PLANE_GELU_GRAD) d1[s] = base1[off + L * s];
+      d0[s] = load_stream2(base0 + off + L * s);
+      if (PIN == PLANE_GELU_GRAD) d1[s] = load_stream2(base1 + off + L * s);
     }
   };
   // F2 fragments of a 64-row block (kg, u): rows 16 it + m, columns r0 + 16 kg + 4 q + jj;

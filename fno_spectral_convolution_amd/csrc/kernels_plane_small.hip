@@ -122,11 +122,11 @@ __global__ void __launch_bounds__(256) k_plane_small(SmallPlaneArgs a) {
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       const int ro = (16 * t + m) * a.Nb;
-      p0[t][0] = *reinterpret_cast<const float4*>(b0 + ro + c0);
-      p0[t][1] = *reinterpret_cast<const float4*>(b0 + ro + c1);
+      p0[t][0] = load_stream4(b0 + ro + c0);
+      p0[t][1] = load_stream4(b0 + ro + c1);
       if constexpr (TWO) {
-        p1[t][0] = *reinterpret_cast<const float4*>(b1 + ro + c0);
-        p1[t][1] = *reinterpret_cast<const float4*>(b1 + ro + c1);
+        p1[t][0] = load_stream4(b1 + ro + c0);
+        p1[t][1] = load_stream4(b1 + ro + c1);
       }
     }
   };

@@ -89,7 +89,7 @@ k_pointwise_mfma(int64_t npts, int cin, int hidden, int cout, const float* __res
       for (int j = 0; j < 4; ++j) {
         const int e = e0 + 256 * j;
         const int c = min(e / (kPwP / 4), cin - 1), f = e % (kPwP / 4);
-        v[j] = *reinterpret_cast<const float4*>(xb + (int64_t)c * npts + 4 * f);
+        v[j] = load_stream4(xb + (int64_t)c * npts + 4 * f);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {

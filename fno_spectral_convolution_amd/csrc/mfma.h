@@ -136,4 +136,17 @@ __device__ __forceinline__ f32x4 zero4() {
   return z;
 }
 
+// Streaming loads of a field: a kernel reads each of its elements once, so the loads carry the
+// nontemporal hint and the lines are not kept for reuse, which leaves L2 and the memory-side
+// cache to the data that is reused (tables, spectra, the lines other kernels write next).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float4 load_stream4(const float* p) {
+  const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ float2 load_stream2(const float2* p) {
+  const f32x2 v = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(p));
+  return make_float2(v[0], v[1]);
+}
+
 }  // namespace fno
