@@ -470,3 +470,24 @@ def test_block_fused_loss(L, case, prec):
 @pytest.mark.parametrize("case", IG_CASES, ids=[c[0] for c in IG_CASES])
 def test_block_fused_loss_activations(L, case, prec, ig, act):
     _fused_loss_case(L, case, prec, ig, act, 3900)
+
+
+@pytest.mark.parametrize("scale_exp", [-40, 40], ids=["2^-40", "2^40"])
+@pytest.mark.parametrize("case", [c for c in CASES if c[0] in (
+    "4d_short_t20", "3d_short_na128", "2d_mc_c64", "2d_chunked_nb512")],
+    ids=lambda c: c[0])
+def test_f32_far_from_unit_scale(L, case, scale_exp):
+    """Float32 plans on fields far from unit size: the short-row transform's products run as
+    split bfloat16 products and the long rows take the FFT; both must keep float32's relative
+    accuracy at any exponent (the spectral path is linear in x, so the oracle is scaled)."""
+    name, batch, cin, cout, grid, modes = case
+    announce("f32 scale", name, scale_exp)
+    seed = 7100 + zlib.crc32(name.encode()) % 1000
+    x, w, _, _ = inputs.small_case(seed, batch, cin, cout, grid, modes)
+    xs = (x * np.float32(2.0 ** scale_exp)).astype(np.float32)
+    plan = L.Plan(batch, cin, cout, grid, modes, gelu=False, bias=False)
+    ys = plan.spectral_conv_fwd(_dev(xs), _dev(w))
+    _torch().cuda.synchronize()
+    ref = O.spectral_conv_fwd(xs.astype(np.float64), w, modes)["y_spec"]
+    check("y_spec", _host(ys), ref, TOL_F32)
+    plan.close()
