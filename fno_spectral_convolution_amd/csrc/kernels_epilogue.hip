@@ -1046,8 +1046,9 @@ static EpiArgs fwd_args(const fno_plan* p, int* G, int64_t* wgs) {
   a.kpad = p->kpad;
   a.lines = g.P / g.Nb;
   a.lpw = fwd_lines_per_wg(a.lines, g.B);
-  // narrow fields take two 64-point groups per step when a line holds them
-  *G = (g.Cout <= 32 && g.Nb >= 2 * PG) ? 2 : 1;
+  // fields of up to 20 channels take two 64-point groups per step when a line holds them (at
+  // 32 channels one group per step keeps more waves resident and is faster)
+  *G = (g.Cout <= 20 && g.Nb >= 2 * PG) ? 2 : 1;
   int gl = 0;
   while ((PG * *G << gl) < g.Nb) ++gl;
   a.gpl_log2 = gl;
