@@ -1024,14 +1024,21 @@ bool epilogue_fast_ok(const fno_plan* p, int mode, bool fwd) {
   return true;
 }
 
-// Lines per forward work-group: the largest power of two dividing the lines of a batch entry
-// that still leaves at least kFwdMinWgs work-groups.
-constexpr int64_t kFwdMinWgs = 2048;
+// Lines per work-group: the largest power of two dividing the lines of a batch entry that still
+// leaves at least min_wgs work-groups.  Measured: fields of up to 20 channels (little work per
+// line) keep 2048 work-groups in both directions; wider ones do best with 1024 (forward at 32
+// and 64 channels: 78 -> 75 and 230 -> 217 us per launch against 2048; backward at 64: 333
+// against 350 us with 2048, whose partials also double the gradient finish).
+static int64_t epi_min_wgs(int channels) { return channels <= 20 ? 2048 : 1024; }
 
-static int fwd_lines_per_wg(int64_t lines, int64_t batch) {
+static int lines_per_wg(int64_t lines, int64_t batch, int64_t min_wgs) {
   int lpw = 1;
-  while (lines % (2 * lpw) == 0 && batch * lines / (2 * lpw) >= kFwdMinWgs) lpw *= 2;
+  while (lines % (2 * lpw) == 0 && batch * lines / (2 * lpw) >= min_wgs) lpw *= 2;
   return lpw;
+}
+
+static int fwd_lines_per_wg(int64_t lines, int64_t batch, int channels) {
+  return lines_per_wg(lines, batch, epi_min_wgs(channels));
 }
 
 // Arguments of the forward line kernel; kmode bits as the kernel's MODE (without its width).
@@ -1045,7 +1052,7 @@ static EpiArgs fwd_args(const fno_plan* p, int* G, int64_t* wgs) {
   a.mb = g.mb;
   a.kpad = p->kpad;
   a.lines = g.P / g.Nb;
-  a.lpw = fwd_lines_per_wg(a.lines, g.B);
+  a.lpw = fwd_lines_per_wg(a.lines, g.B, g.Cout);
   // fields of up to 20 channels take two 64-point groups per step when a line holds them (at
   // 32 channels one group per step keeps more waves resident and is faster)
   *G = (g.Cout <= 20 && g.Nb >= 2 * PG) ? 2 : 1;
@@ -1128,20 +1135,16 @@ hipError_t launch_epilogue_fwd_mse(const fno_plan* p, const void* T, const float
   return launch_fwd_any(p, a, G, kmode, wgs, s, t_half);
 }
 
-// Lines per backward work-group: each work-group writes one row of bypass-gradient partials,
-// so it owns enough lines to keep the partials small (at least kBwdMinWgs work-groups still).
-constexpr int64_t kBwdMinWgs = 1024;
-
-static int bwd_lines_per_wg(int64_t lines, int64_t batch) {
-  int lpw = 1;
-  while (lines % (2 * lpw) == 0 && batch * lines / (2 * lpw) >= kBwdMinWgs) lpw *= 2;
-  return lpw;
+// Lines per backward work-group (each writes one row of bypass-gradient partials, so fewer
+// work-groups also mean a shorter finish): as the forward's.
+static int bwd_lines_per_wg(int64_t lines, int64_t batch, int channels) {
+  return lines_per_wg(lines, batch, epi_min_wgs(channels));
 }
 
 int epilogue_bwd_fast_groups(const fno_plan* p) {
   if (!epilogue_fast_ok(p, EPI_BLOCK, false)) return 0;
   const int64_t lines = p->g.P / p->g.Nb;
-  return (int)((int64_t)p->g.B * lines / bwd_lines_per_wg(lines, p->g.B));
+  return (int)((int64_t)p->g.B * lines / bwd_lines_per_wg(lines, p->g.B, p->g.Cin));
 }
 
 hipError_t launch_epilogue_bwd_fast(const fno_plan* p, int mode, const void* Tg,
@@ -1157,7 +1160,7 @@ hipError_t launch_epilogue_bwd_fast(const fno_plan* p, int mode, const void* Tg,
   a.mb = g.mb;
   a.kpad = p->kpad;
   a.lines = g.P / g.Nb;
-  a.lpw = bwd_lines_per_wg(a.lines, g.B);
+  a.lpw = bwd_lines_per_wg(a.lines, g.B, g.Cin);
   // one 64-point group per step: with three input tiles in flight, larger steps cost more in
   // occupancy than they save in barriers (measured on the 128^3 width-20 backward)
   int gl = 0;
