@@ -689,11 +689,11 @@ static hipError_t launch_outer_generic(const fno_plan* p, OuterArgs a, int64_t p
   const size_t lds = (size_t)ct * col_bytes;
   const int64_t ctiles = (a.post2 + ct - 1) / ct;
   // few slabs: split each slab's output row tiles over up to msplit work-groups (at least
-  // four tiles, one per wave, each) until about 2048 work-groups are in flight
+  // four tiles, one per wave, each) until about 1024 work-groups are in flight
   const int mtiles = a.Lout_pad / 16;
   a.pre = pre;
   a.msplit = 1;
-  while (2 * a.msplit * 4 <= mtiles && pre * ctiles * a.msplit < 2048) a.msplit *= 2;
+  while (2 * a.msplit * 4 <= mtiles && pre * ctiles * a.msplit < 1024) a.msplit *= 2;
   a.mt_per = (mtiles + a.msplit - 1) / a.msplit;
   const int64_t gx = a.msplit == 1 ? pre : (pre + 7) / 8 * 8 * a.msplit;
   if (gx > 0x7fffffff || ctiles > 65535) return hipErrorInvalidValue;

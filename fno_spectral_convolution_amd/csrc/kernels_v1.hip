@@ -492,32 +492,33 @@ hipError_t launch_epilogue_bwd(const fno_plan* p, int mode, const float2* Tg, co
   return hipGetLastError();
 }
 
-// Sum of the per-work-group bypass-gradient partials.  A group of 256 threads owns 8
-// consecutive entries; thread slice k (0..31) sums partials k, k+32, ... with 8 loads in
-// flight, and the 32 slice sums are added in the fixed order 0, 1, .., 31 (deterministic).
-constexpr int kFinE = 8, kFinS = 32;
-
+// Sum of the per-work-group bypass-gradient partials.  A group of 256 threads owns E
+// consecutive entries; thread slice k (0..256/E-1) sums partials k, k+256/E, ... with 8 loads
+// in flight, and the slice sums are added in the fixed order 0, 1, .. (deterministic).  E = 16
+// reads 64-byte row segments where the grid still has at least 128 work-groups, else E = 8.
+template <int E>
 __global__ void __launch_bounds__(256)
 k_bypass_finish(const float* __restrict__ part, int nparts, int cout, int cin,
                 float* __restrict__ dwb, float* __restrict__ dbias) {
-  __shared__ float s_sum[kFinS][kFinE];
+  constexpr int S = 256 / E;
+  __shared__ float s_sum[S][E];
   const int npair = cout * cin + cout;
-  const int el = threadIdx.x % kFinE, slice = threadIdx.x / kFinE;
-  const int e = blockIdx.x * kFinE + el;
+  const int el = threadIdx.x % E, slice = threadIdx.x / E;
+  const int e = blockIdx.x * E + el;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (e < npair) {
     int q = slice;
-    for (; q + 7 * kFinS < nparts; q += 8 * kFinS) {
+    for (; q + 7 * S < nparts; q += 8 * S) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] += part[(int64_t)(q + j * kFinS) * npair + e];
+      for (int j = 0; j < 8; ++j) acc[j] += part[(int64_t)(q + j * S) * npair + e];
     }
-    for (; q < nparts; q += kFinS) acc[0] += part[(int64_t)q * npair + e];
+    for (; q < nparts; q += S) acc[0] += part[(int64_t)q * npair + e];
   }
   s_sum[slice][el] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
   __syncthreads();
   if (slice == 0 && e < npair) {
     float v = 0.f;
-    for (int k = 0; k < kFinS; ++k) v += s_sum[k][el];
+    for (int k = 0; k < S; ++k) v += s_sum[k][el];
     if (e < cout * cin) {
       if (dwb) dwb[e] = v;
     } else if (dbias) {
@@ -531,8 +532,12 @@ hipError_t launch_bypass_grad_finish(const fno_plan* p, const float* red_part, f
   const Geom& g = p->g;
   const int npair = g.Cout * g.Cin + g.Cout;
   const int nparts = epilogue_bwd_fast(p, EPI_BLOCK, grad_x) ? epilogue_bwd_fast_groups(p) : p->nred;
-  hipLaunchKernelGGL(k_bypass_finish, dim3((npair + kFinE - 1) / kFinE), dim3(256), 0, s, red_part,
-                     nparts, g.Cout, g.Cin, dwb, dbias);
+  if (npair >= 128 * 16)
+    hipLaunchKernelGGL(k_bypass_finish<16>, dim3((npair + 15) / 16), dim3(256), 0, s, red_part,
+                       nparts, g.Cout, g.Cin, dwb, dbias);
+  else
+    hipLaunchKernelGGL(k_bypass_finish<8>, dim3((npair + 7) / 8), dim3(256), 0, s, red_part,
+                       nparts, g.Cout, g.Cin, dwb, dbias);
   return hipGetLastError();
 }
 
