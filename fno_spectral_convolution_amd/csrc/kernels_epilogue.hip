@@ -258,7 +258,7 @@ __device__ __forceinline__ void load_rows(float4 (&v)[NPT], const float* base, i
 // 16 (with 1) for the fused MSE loss: the target rows of a step are loaded at its start and
 // the store phase writes msc (y - t) GELU'(z) in place of y, and adds (y - t)^2 to a per-thread
 // sum, reduced over the work-group in a fixed order into one partial at the end.
-template <int C, int H, int MODE, int G, bool TH>
+template <int C, int H, int MODE, int G, bool TH, int GPL>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C == 64 ? 3 : 4)))
 k_epi_fwd_line(EpiArgs a) {
   constexpr bool BF = H != 0;  // half operands (bfloat16 or IEEE half)
@@ -347,12 +347,16 @@ k_epi_fwd_line(EpiArgs a) {
   float4 ptg[MS ? NPT : 1];
   double lsum = 0.0;
   bool bad = false;  // IEEE-half plans: a non-finite output was written
-  GtFrag<G, H> gtf;
+  // table fragments: GPL == 0 reloads fragment 0 for every step; GPL = 1 or 2 (the steps of a
+  // line) keeps the fragment of each step of a line in registers for the whole work-group
+  GtFrag<G, H> gts[GPL > 0 ? GPL : 1];
   if (BLK) {
 #pragma unroll
     for (int u = 0; u < NPT; ++u) pre[u] = load_stream4(a.x + goff[u]);
   }
-  load_gt<G, H, true, MT>(a, 0, tbase, m, q, gtf);
+#pragma unroll
+  for (int gg = 0; gg < (GPL > 0 ? GPL : 1); ++gg)
+    load_gt<G, H, true, MT>(a, gg * PI, tbase, m, q, gts[gg]);
   // narrow fields have few steps per line: the next line's spectrum rows stream in while
   // this one is computed (the last line re-loads itself); wide ones stage each line directly
   constexpr bool LPF = C < 64;
@@ -368,7 +372,9 @@ k_epi_fwd_line(EpiArgs a) {
     } else {
       stage_line<C, H, TH>(a, Tb + (int64_t)lf * a.mb, s_tl, tid);
     }
-    for (int g = 0; g < gpl; ++g) {
+#pragma unroll(GPL > 0 ? GPL : 1)
+    for (int g = 0; g < (GPL > 0 ? GPL : gpl); ++g) {
+      const GtFrag<G, H>& gtf = gts[GPL > 0 ? g : 0];
       const int f = (lf << a.gpl_log2) + g;
       const int fn = min(f + 1, nf - 1);
       if (BLK) {
@@ -431,7 +437,7 @@ k_epi_fwd_line(EpiArgs a) {
           }
         }
       }
-      load_gt<G, H, true, MT>(a, (fn & (gpl - 1)) * PI, tbase, m, q, gtf);
+      if constexpr (GPL == 0) load_gt<G, H, true, MT>(a, (fn & (gpl - 1)) * PI, tbase, m, q, gts[0]);
       if (BLK) {
         if constexpr (S3) {
           // A: lane (m, q) holds x[32 s + 8 q + e][point MT m + tbase + j], split
@@ -543,7 +549,7 @@ k_epi_fwd_line(EpiArgs a) {
 // MODE: 1 spectral part only (grad_x = s(x) * spectral), 3 block, 7 block with GELU' (z read);
 // plus 8 when x is a pre-activation: the x tile holds the block's input GELU(x) (for dWb and
 // the tanh factor), a second tile GELU'(x), which multiplies the grad tile as it is stored.
-template <int C, int H, bool TANH, int MODE, int G, bool TH>
+template <int C, int H, bool TANH, int MODE, int G, bool TH, int GPL>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C == 64 ? 2 : 3)))
 k_epi_bwd_line(EpiArgs a) {
   constexpr bool BF = H != 0;  // half operands (bfloat16 or IEEE half)
@@ -648,14 +654,18 @@ k_epi_bwd_line(EpiArgs a) {
     pz[u] = pg_y[u];
     px[u] = pg_y[u];
   }
-  GtFrag<G, H> gtf;
+  // table fragments: GPL == 0 reloads fragment 0 for every step; GPL = 1 or 2 (the steps of a
+  // line) keeps the fragment of each step of a line in registers for the whole work-group
+  GtFrag<G, H> gts[GPL > 0 ? GPL : 1];
 #pragma unroll
   for (int u = 0; u < NPT; ++u) {
     if (BLK) pg_y[u] = load_stream4(a.gy + goff[u]);
     if (GL) pz[u] = load_stream4(a.zin + goff[u]);
     if (NX) px[u] = load_stream4(a.x + goff[u]);
   }
-  load_gt<G, H, true, MT>(a, 0, tbase, m, q, gtf);
+#pragma unroll
+  for (int gg = 0; gg < (GPL > 0 ? GPL : 1); ++gg)
+    load_gt<G, H, true, MT>(a, gg * PI, tbase, m, q, gts[gg]);
   constexpr bool LPF = C < 64;
   const int64_t Tb = ((int64_t)b * C * a.lines + l0) * a.mb;  // complex index of this range
   LineT<LPF ? C : 16, TH> tln;
@@ -669,7 +679,9 @@ k_epi_bwd_line(EpiArgs a) {
     } else {
       stage_line<C, H, TH>(a, Tb + (int64_t)lf * a.mb, s_tl, tid);
     }
-    for (int g = 0; g < gpl; ++g) {
+#pragma unroll(GPL > 0 ? GPL : 1)
+    for (int g = 0; g < (GPL > 0 ? GPL : gpl); ++g) {
+      const GtFrag<G, H>& gtf = gts[GPL > 0 ? g : 0];
       const int f = (lf << a.gpl_log2) + g;
       const int fn = min(f + 1, nf - 1);
 #pragma unroll
@@ -738,7 +750,7 @@ k_epi_bwd_line(EpiArgs a) {
           }
         }
       }
-      load_gt<G, H, true, MT>(a, (fn & (gpl - 1)) * PI, tbase, m, q, gtf);
+      if constexpr (GPL == 0) load_gt<G, H, true, MT>(a, (fn & (gpl - 1)) * PI, tbase, m, q, gts[0]);
       if (TANH) {
         // lane (n = m, q), tile tbase + j, register r: channel 16 ct + m, point
         // lp(4 q + r) + j
@@ -919,7 +931,7 @@ static hipError_t launch_fwd_c(const EpiArgs& a, int half, int mode, int wgs, hi
   if constexpr (C == 64 && G == 1) {
     if (th && half != 0) {
 #define FNO_EPI_FWD(HV, MV) \
-  hipLaunchKernelGGL((k_epi_fwd_line<C, HV, MV, G, true>), dim3(wgs), dim3(256), 0, s, a)
+  hipLaunchKernelGGL((k_epi_fwd_line<C, HV, MV, G, true, 0>), dim3(wgs), dim3(256), 0, s, a)
 #define FNO_EPI_FWD_M(HV)                   \
   do {                                      \
     if (mode == 0) FNO_EPI_FWD(HV, 0);        \
@@ -938,21 +950,25 @@ static hipError_t launch_fwd_c(const EpiArgs& a, int half, int mode, int wgs, hi
     }
   }
   if (th) return hipErrorInvalidValue;
-#define FNO_EPI_FWD(HV, MV) \
-  hipLaunchKernelGGL((k_epi_fwd_line<C, HV, MV, G, false>), dim3(wgs), dim3(256), 0, s, a)
-#define FNO_EPI_FWD_M(HV)                   \
-  do {                                      \
-    if (mode == 0) FNO_EPI_FWD(HV, 0);        \
-    else if (mode == 1) FNO_EPI_FWD(HV, 1);   \
-    else if (mode == 2) FNO_EPI_FWD(HV, 2);   \
-    else if (mode == 9) FNO_EPI_FWD(HV, 9);   \
-    else if (mode == 10) FNO_EPI_FWD(HV, 10); \
-    else if (mode == 17) FNO_EPI_FWD(HV, 17); \
-    else FNO_EPI_FWD(HV, 25);                 \
+#define FNO_EPI_FWD(HV, MV, GP) \
+  hipLaunchKernelGGL((k_epi_fwd_line<C, HV, MV, G, false, GP>), dim3(wgs), dim3(256), 0, s, a)
+#define FNO_EPI_FWD_M(HV, GP)                   \
+  do {                                          \
+    if (mode == 0) FNO_EPI_FWD(HV, 0, GP);        \
+    else if (mode == 1) FNO_EPI_FWD(HV, 1, GP);   \
+    else if (mode == 2) FNO_EPI_FWD(HV, 2, GP);   \
+    else if (mode == 9) FNO_EPI_FWD(HV, 9, GP);   \
+    else if (mode == 10) FNO_EPI_FWD(HV, 10, GP); \
+    else if (mode == 17) FNO_EPI_FWD(HV, 17, GP); \
+    else FNO_EPI_FWD(HV, 25, GP);                 \
   } while (0)
-  if (half == 2) FNO_EPI_FWD_M(2);
-  else if (half == 1) FNO_EPI_FWD_M(1);
-  else FNO_EPI_FWD_M(0);
+  // float32 plans keep the table fragments of lines of one or two steps in registers
+  const int gpl = 1 << a.gpl_log2;
+  if (half == 2) FNO_EPI_FWD_M(2, 0);
+  else if (half == 1) FNO_EPI_FWD_M(1, 0);
+  else if (gpl == 1) FNO_EPI_FWD_M(0, 1);
+  else if (gpl == 2) FNO_EPI_FWD_M(0, 2);
+  else FNO_EPI_FWD_M(0, 0);
 #undef FNO_EPI_FWD_M
 #undef FNO_EPI_FWD
   return hipGetLastError();
@@ -964,7 +980,7 @@ static hipError_t launch_bwd_c(const EpiArgs& a, int half, bool tanh_pre, int mo
   if constexpr (C == 64 && G == 1) {
     if (th && half != 0) {
 #define FNO_EPI_BWD(BFV, TV, MV) \
-  hipLaunchKernelGGL((k_epi_bwd_line<C, BFV, TV, MV, G, true>), dim3(wgs), dim3(256), 0, s, a)
+  hipLaunchKernelGGL((k_epi_bwd_line<C, BFV, TV, MV, G, true, 0>), dim3(wgs), dim3(256), 0, s, a)
 #define FNO_EPI_BWD_M(BFV, TV)                   \
   do {                                           \
     if (mode == 1) FNO_EPI_BWD(BFV, TV, 1);        \
@@ -987,26 +1003,34 @@ static hipError_t launch_bwd_c(const EpiArgs& a, int half, bool tanh_pre, int mo
     }
   }
   if (th) return hipErrorInvalidValue;
-#define FNO_EPI_BWD(BFV, TV, MV) \
-  hipLaunchKernelGGL((k_epi_bwd_line<C, BFV, TV, MV, G, false>), dim3(wgs), dim3(256), 0, s, a)
-#define FNO_EPI_BWD_M(BFV, TV)                  \
-  do {                                          \
-    if (mode == 1) FNO_EPI_BWD(BFV, TV, 1);       \
-    else if (mode == 3) FNO_EPI_BWD(BFV, TV, 3);  \
-    else if (mode == 7) FNO_EPI_BWD(BFV, TV, 7);  \
-    else if (mode == 9) FNO_EPI_BWD(BFV, TV, 9);  \
-    else if (mode == 11) FNO_EPI_BWD(BFV, TV, 11); \
-    else FNO_EPI_BWD(BFV, TV, 15);                \
+#define FNO_EPI_BWD(BFV, TV, MV, GP) \
+  hipLaunchKernelGGL((k_epi_bwd_line<C, BFV, TV, MV, G, false, GP>), dim3(wgs), dim3(256), 0, s, a)
+#define FNO_EPI_BWD_M(BFV, TV, GP)                  \
+  do {                                              \
+    if (mode == 1) FNO_EPI_BWD(BFV, TV, 1, GP);       \
+    else if (mode == 3) FNO_EPI_BWD(BFV, TV, 3, GP);  \
+    else if (mode == 7) FNO_EPI_BWD(BFV, TV, 7, GP);  \
+    else if (mode == 9) FNO_EPI_BWD(BFV, TV, 9, GP);  \
+    else if (mode == 11) FNO_EPI_BWD(BFV, TV, 11, GP); \
+    else FNO_EPI_BWD(BFV, TV, 15, GP);                \
   } while (0)
+  // float32 plans keep the table fragments of lines of one or two steps in registers
+  const int gpl = 1 << a.gpl_log2;
   if (half == 2) {
-    if (tanh_pre) FNO_EPI_BWD_M(2, true);
-    else FNO_EPI_BWD_M(2, false);
+    if (tanh_pre) FNO_EPI_BWD_M(2, true, 0);
+    else FNO_EPI_BWD_M(2, false, 0);
   } else if (half == 1) {
-    if (tanh_pre) FNO_EPI_BWD_M(1, true);
-    else FNO_EPI_BWD_M(1, false);
+    if (tanh_pre) FNO_EPI_BWD_M(1, true, 0);
+    else FNO_EPI_BWD_M(1, false, 0);
+  } else if (gpl == 1) {
+    if (tanh_pre) FNO_EPI_BWD_M(0, true, 1);
+    else FNO_EPI_BWD_M(0, false, 1);
+  } else if (gpl == 2) {
+    if (tanh_pre) FNO_EPI_BWD_M(0, true, 2);
+    else FNO_EPI_BWD_M(0, false, 2);
   } else {
-    if (tanh_pre) FNO_EPI_BWD_M(0, true);
-    else FNO_EPI_BWD_M(0, false);
+    if (tanh_pre) FNO_EPI_BWD_M(0, true, 0);
+    else FNO_EPI_BWD_M(0, false, 0);
   }
 #undef FNO_EPI_BWD_M
 #undef FNO_EPI_BWD
