@@ -552,6 +552,119 @@ __global__ void __launch_bounds__(256) k_outer_inv_stream(OuterArgs a) {
   }
 }
 
+// Inverse transform of an outer axis for many narrow slabs (float32; at most 32 kept rows in,
+// at most 128 rows out, one column tile of 16 NT columns): a work-group walks spw consecutive
+// slabs.  Wave w owns output row tiles w and w + 4 for every slab and keeps their table
+// fragments (K-groups of 16) in registers, so the table is read from L2 once per work-group
+// rather than once per slab; the next slab's input is loaded into registers while the current
+// one is staged in LDS (transposed, with the swapped copy, as in k_outer_mfma) and multiplied.
+template <int NT>
+__global__ void __launch_bounds__(256) k_outer_inv_slabs(OuterArgs a, int spw) {
+  constexpr int CT = 16 * NT;
+  constexpr int KMAX = 64;             // 2 Lin_pad <= 64
+  constexpr int KSM = KMAX + 4;        // LDS row stride
+  constexpr int EU = 32 * CT / 256;    // input elements per thread (Lin_pad <= 32 rows)
+  __shared__ __attribute__((aligned(16))) float s_bt[CT * KSM];
+  const int K = 2 * a.Lin_pad;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, q = lane >> 4;
+  const int mtiles = a.Lout_pad / 16;
+  const int64_t c0 = (int64_t)blockIdx.y * CT;
+  const int64_t p0 = (int64_t)blockIdx.x * spw;
+  const int64_t p_end = min(p0 + spw, a.pre);
+  if (p0 >= a.pre) return;  // the whole work-group
+  const float* A = static_cast<const float*>(a.A);
+  // table fragments of row tiles wave + 4 t: lane (m, q), K-group g holds A[16 mt + m][16 g +
+  // 4 q .. + 3]; tiles past the table and groups past K load clamped copies, never used
+  float4 af[2][KMAX / 16];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int mt = min(wave + 4 * t, mtiles - 1);
+#pragma unroll
+    for (int g = 0; g < KMAX / 16; ++g)
+      af[t][g] = *reinterpret_cast<const float4*>(A + (int64_t)(16 * mt + m) * K +
+                                                  min(16 * g, K - 16) + 4 * q);
+  }
+  // input element e = tid + 256 u: row e / CT, column c0 + e % CT (zero past the slab)
+  float xv[EU];
+  auto load_slab = [&](int64_t pre) {
+    const float* src = a.in + pre * a.Lin * a.post2;
+#pragma unroll
+    for (int u = 0; u < EU; ++u) {
+      const int e = tid + 256 * u;
+      const int li = e / CT, c = e - li * CT;
+      const int64_t col = c0 + c;
+      const bool ok = li < a.Lin && col < a.post2;
+      const float x = src[(int64_t)min(li, a.Lin - 1) * a.post2 + min(col, a.post2 - 1)];
+      xv[u] = ok ? x : 0.f;
+    }
+  };
+  // Bt[c][k]: k < Lin_pad -> X[k][c0 + c]; k >= Lin_pad -> Xs[k - Lin_pad][c0 + c]; staged row
+  // of column c: 16 (c % NT) + c / NT
+  auto stage = [&]() {
+#pragma unroll
+    for (int u = 0; u < EU; ++u) {
+      const int e = tid + 256 * u;
+      const int li = e / CT, c = e - li * CT;
+      if (li >= a.Lin_pad) continue;
+      const int cp = c ^ 1;
+      s_bt[(16 * (c % NT) + c / NT) * KSM + li] = xv[u];
+      s_bt[(16 * (cp % NT) + cp / NT) * KSM + a.Lin_pad + li] = (c & 1) ? -xv[u] : xv[u];
+    }
+  };
+  load_slab(p0);
+  for (int64_t pre = p0; pre < p_end; ++pre) {
+    __syncthreads();  // the previous slab's products are done with s_bt
+    stage();
+    load_slab(min(pre + 1, p_end - 1));  // in flight during the products (the last reloads)
+    __syncthreads();
+    float* dst = a.out + pre * a.Lout * a.post2;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int mt = wave + 4 * t;
+      if (mt >= mtiles) break;
+      f32x4 acc[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nt] = zero4();
+#pragma unroll
+      for (int g = 0; g < KMAX / 16; ++g) {
+        if (16 * g >= K) break;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const float4 bv =
+              *reinterpret_cast<const float4*>(s_bt + (16 * nt + m) * KSM + 16 * g + 4 * q);
+          acc[nt] = mfma_f32(af[t][g].x, bv.x, acc[nt]);
+          acc[nt] = mfma_f32(af[t][g].y, bv.y, acc[nt]);
+          acc[nt] = mfma_f32(af[t][g].z, bv.z, acc[nt]);
+          acc[nt] = mfma_f32(af[t][g].w, bv.w, acc[nt]);
+        }
+      }
+      // lane (n = m, q): rows 16 mt + 4 q + r, columns c0 + NT m + nt
+      const int64_t col = c0 + NT * m;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pr = 16 * mt + 4 * q + r;
+        if (pr >= a.Lout) continue;
+        float* d = dst + (int64_t)pr * a.post2 + col;
+        if (col + NT <= a.post2 && (a.post2 % NT) == 0) {
+          if constexpr (NT == 4) {
+            *reinterpret_cast<float4*>(d) =
+                make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
+          } else if constexpr (NT == 2) {
+            *reinterpret_cast<float2*>(d) = make_float2(acc[0][r], acc[1][r]);
+          } else {
+            d[0] = acc[0][r];
+          }
+        } else {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            if (col + nt < a.post2) d[nt] = acc[nt][r];
+        }
+      }
+    }
+  }
+}
+
 template <int H>
 static hipError_t launch_inv_stream(int ntw, dim3 grid, size_t lds, const OuterArgs& a,
                                     hipStream_t s) {
@@ -617,6 +730,8 @@ static int pad16(int v) { return (v + 15) / 16 * 16; }
 
 static hipError_t launch_outer_generic(const fno_plan* p, OuterArgs a, int64_t pre,
                                        hipStream_t s);
+// work-groups the multi-slab inverse aims for (each walks ceil(slabs / this) slabs)
+constexpr int64_t kSlabWgs = 1024;
 
 // pre/post of the transform of axis j (see the generic kernel) and the launch
 hipError_t launch_outer_mfma(const fno_plan* p, int axis, int chans, bool inv, const float2* in,
@@ -658,6 +773,20 @@ hipError_t launch_outer_mfma(const fno_plan* p, int axis, int chans, bool inv, c
     return g.half == 2 ? launch_inv_stream<2>(ntw, grid, lds, a, s)
            : g.half == 1 ? launch_inv_stream<1>(ntw, grid, lds, a, s)
                          : launch_inv_stream<0>(ntw, grid, lds, a, s);
+  }
+  if (inv && !bf && a.Lin_pad <= 32 && a.Lout_pad <= 128 && a.post2 <= 64 && pre >= 4096) {
+    // many narrow float32 slabs: work-groups walk several slabs with the table in registers
+    const int nt = a.post2 > 32 ? 4 : (a.post2 > 16 ? 2 : 1);
+    const int64_t ctiles = (a.post2 + 16 * nt - 1) / (16 * nt);
+    const int spw = (int)((pre * ctiles + kSlabWgs - 1) / kSlabWgs);
+    const int64_t wgx = (pre + spw - 1) / spw;
+    a.pre = pre;
+    if (wgx > 0x7fffffff || ctiles > 65535) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)wgx, (unsigned)ctiles);
+    if (nt == 4) hipLaunchKernelGGL((k_outer_inv_slabs<4>), grid, dim3(256), 0, s, a, spw);
+    else if (nt == 2) hipLaunchKernelGGL((k_outer_inv_slabs<2>), grid, dim3(256), 0, s, a, spw);
+    else hipLaunchKernelGGL((k_outer_inv_slabs<1>), grid, dim3(256), 0, s, a, spw);
+    return hipGetLastError();
   }
   if (!inv && a.Lout_pad <= 64 && a.post2 % 4 == 0 && pre <= 65535) {
     // few kept rows, long K: stream the slab in column blocks of 64 NTW (as wide as the row

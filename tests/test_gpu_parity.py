@@ -131,6 +131,38 @@ def test_spectral_conv_fwd_bwd(L, case, prec):
     plan.close()
 
 
+# Many narrow float32 slabs on the row axis of a 3D field (batch x channels x first-axis
+# length >= 4096, at most 32 kept rows in, at most 128 rows out, at most 64 floats per row):
+# the inverse of that axis runs on work-groups that walk several slabs each with the table in
+# registers.  One case per column-tile width, one with idle row-tile waves (32 output rows).
+SLAB_CASES = [
+    # name, batch, cin, cout, grid, modes
+    ("3d_slabs_nt1", 1, 16, 16, (256, 32, 64), (2, 8, 8)),
+    ("3d_slabs_nt2", 2, 16, 16, (128, 128, 32), (4, 16, 16)),
+]
+
+
+@pytest.mark.parametrize("case", SLAB_CASES, ids=[c[0] for c in SLAB_CASES])
+def test_many_slab_outer_inverse(L, case):
+    name, batch, cin, cout, grid, modes = case
+    announce("slabs", name)
+    seed = zlib.crc32(name.encode()) % 1000
+    x, w, _, _ = inputs.small_case(seed, batch, cin, cout, grid, modes)
+    gy = inputs.normal_like(seed, (batch, cout) + grid)
+    plan = L.Plan(batch, cin, cout, grid, modes, mixed=False, tanh=False, gelu=False,
+                  bias=False)
+    tx, tw, tg = (_dev(a) for a in (x, w, gy))
+    ys = plan.spectral_conv_fwd(tx, tw)
+    gx, gw = plan.spectral_conv_bwd(tx, tw, tg)
+    _torch().cuda.synchronize()
+    fwd = O.spectral_conv_fwd(x, w, modes)
+    bwd = O.spectral_conv_bwd(x, w, modes, gy)
+    check("y_spec", _host(ys), fwd["y_spec"], TOL_F32)
+    check("grad_x", _host(gx), bwd["grad_x"], TOL_F32)
+    check("grad_w", _host(gw), bwd["grad_w"], TOL_F32)
+    plan.close()
+
+
 @pytest.mark.parametrize("mixed", [False, True, "f16"], ids=["f32", "mixed", "f16"])
 def test_bitwise_deterministic(L, mixed):
     announce("determinism", mixed)
