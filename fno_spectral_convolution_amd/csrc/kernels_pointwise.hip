@@ -8,7 +8,8 @@
 // to LDS and feeds the second product (M = cout, K = hidden); the output tile leaves through
 // LDS as row-contiguous float4 stores.  Waves take M-tiles round-robin; weight fragments are
 // read through L2.  Point tails are zero-filled on load and masked on store.  A projection to
-// at most kPwSmallOut channels does its second product on the VALU instead (see below).
+// at most kPwSmallOut channels does its second product on the VALU instead (see below), and a
+// lift from at most four channels runs on the VALU altogether (k_lift_valu).
 #include "fno_internal.h"
 #include "mfma.h"
 #include "pointwise.h"
@@ -229,9 +230,56 @@ k_pointwise_mfma(int64_t npts, int cin, int hidden, int cout, const float* __res
   }
 }
 
+// A lift from at most four input channels does 2 cin flops per output value, too little for the
+// matrix cores: a thread takes 4 consecutive points of one batch entry and writes them for
+// every output channel (each output row leaves as float4 stores, contiguous over the threads),
+// so the kernel is bound by its output stream.
+template <int CIN>
+__global__ void __launch_bounds__(256)
+k_lift_valu(int64_t npts, int cout, const float* __restrict__ x, const float* __restrict__ w1,
+            const float* __restrict__ b1, float* __restrict__ y) {
+  const int b = blockIdx.y;
+  const int64_t p = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (p >= npts) return;  // npts % 4 == 0: a thread's four points are all present or all absent
+  float4 xv[CIN];
+#pragma unroll
+  for (int c = 0; c < CIN; ++c) xv[c] = load_stream4(x + ((int64_t)b * CIN + c) * npts + p);
+  float* yb = y + (int64_t)b * cout * npts + p;
+  for (int o = 0; o < cout; ++o) {
+    const float bo = b1 ? b1[o] : 0.f;
+    float4 v = make_float4(bo, bo, bo, bo);
+#pragma unroll
+    for (int c = 0; c < CIN; ++c) {
+      const float wc = w1[o * CIN + c];
+      v.x = fmaf(wc, xv[c].x, v.x);
+      v.y = fmaf(wc, xv[c].y, v.y);
+      v.z = fmaf(wc, xv[c].z, v.z);
+      v.w = fmaf(wc, xv[c].w, v.w);
+    }
+    *reinterpret_cast<float4*>(yb + (int64_t)o * npts) = v;
+  }
+}
+
 hipError_t launch_pointwise(int64_t batch, int64_t npts, int cin, int hidden, int cout,
                             const float* x, const float* w1, const float* b1, const float* w2,
                             const float* b2, float* y, hipStream_t s) {
+  auto al16 = [](const void* v) { return ((uintptr_t)v & 15u) == 0; };
+  if (hidden == 0 && cin <= 4 && npts % 4 == 0 && al16(x) && al16(y)) {
+    const int64_t groups = (npts / 4 + 255) / 256;
+    if (groups > 0x7fffffff || batch > 65535) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)groups, (unsigned)batch);
+    switch (cin) {
+      case 1: hipLaunchKernelGGL(k_lift_valu<1>, grid, dim3(256), 0, s, npts, cout, x, w1, b1, y);
+              break;
+      case 2: hipLaunchKernelGGL(k_lift_valu<2>, grid, dim3(256), 0, s, npts, cout, x, w1, b1, y);
+              break;
+      case 3: hipLaunchKernelGGL(k_lift_valu<3>, grid, dim3(256), 0, s, npts, cout, x, w1, b1, y);
+              break;
+      default: hipLaunchKernelGGL(k_lift_valu<4>, grid, dim3(256), 0, s, npts, cout, x, w1, b1, y);
+               break;
+    }
+    return hipGetLastError();
+  }
   const int cin_p = (cin + 15) / 16 * 16;
   const int mid = hidden > 0 ? hidden : cout;
   const int mid_p = (mid + 15) / 16 * 16;

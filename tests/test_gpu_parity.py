@@ -342,6 +342,23 @@ def test_pointwise_and_mse(L):
 
 
 
+@pytest.mark.parametrize("cin,npts,bias", [(1, 2304, True), (2, 2304, False), (3, 4100, True),
+                                          (4, 2304, True), (3, 2302, True)])
+def test_lift_few_input_channels(L, cin, npts, bias):
+    """Lifts from at most four channels (point counts that are multiples of 4 take the VALU
+    lift, the last case the matrix-core path), with and without a bias."""
+    announce("lift", cin, npts, bias)
+    g = np.random.default_rng(60 + cin)
+    cout = 20
+    x = g.standard_normal((3, cin, npts)).astype(np.float32)
+    w1 = g.standard_normal((cout, cin)).astype(np.float32)
+    b1 = g.standard_normal(cout).astype(np.float32) if bias else None
+    lift = L.pointwise(_dev(x), _dev(w1), _dev(b1) if bias else None)
+    _torch().cuda.synchronize()
+    ref = O.pointwise_linear(x, w1, b1)
+    check("lift", _host(lift), ref, TOL_F32)
+
+
 @pytest.mark.parametrize("cout,hidden", [(1, 128), (3, 20), (4, 64), (5, 40)])
 def test_projection_narrow_outputs(L, cout, hidden):
     """Projection heads around the narrow-output path (<= 4 outputs take the VALU second
