@@ -108,8 +108,11 @@ __device__ __forceinline__ void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// MODE 0: y = y_spec;  1: y = act(y_spec + Wb x + bias);  2: the same and z saved
-template <int H, int MODE>
+// MODE 0: y = y_spec;  1: y = act(y_spec + Wb x + bias);  2: the same and z saved.
+// G: act is GELU (else the identity).  A compile-time choice: a run-time branch in the store
+// pass splits its stores over two paths, and the compiler then waits for some of them to be
+// acknowledged before the next chunk's products.
+template <int H, int MODE, bool G>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 k_epi_rows(RowsEpiArgs a) {
   constexpr bool BF = H != 0;  // half operands (bfloat16 or IEEE half)
@@ -150,18 +153,62 @@ k_epi_rows(RowsEpiArgs a) {
     for (int e = 4 * 256 * kErXPT + tid; e < 4 * kErKB * RP; e += 256) s_x[e] = 0.f;
     load_x(0);
   }
+  // first-product B fragments: A[row][s'] for this lane's row of chunk c
+  float bfr[BF ? 1 : kErMA];
+  V8 bhi[2], blo[2];
+  auto load_rowtab = [&](int c) {
+    const int row = kErRows * c + m;
+    if constexpr (!BF) {
+#pragma unroll
+      for (int i = 0; i < kErMA / 4; ++i) {
+        const int col = min((q >> 1) * a.SO + (q & 1) * a.ma + 4 * i, a.KA - 4);
+        const float4 v = *reinterpret_cast<const float4*>(a.ainv + row * a.KA + col);
+        bfr[4 * i + 0] = v.x;
+        bfr[4 * i + 1] = v.y;
+        bfr[4 * i + 2] = v.z;
+        bfr[4 * i + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int col = min(32 * jj + 8 * q, a.KA - 8);
+        bhi[jj] = *reinterpret_cast<const V8*>(a.ainv_bf + row * a.KA + col);
+        blo[jj] = *reinterpret_cast<const V8*>(a.ainv_lo + row * a.KA + col);
+      }
+    }
+  };
+  // the first chunk's row table is loaded before the set-up loads below, whose waits then cover
+  // it: as the kernel's last loads before the loop, the compiler would wait for every store of
+  // the previous chunk before each chunk's products
+  load_rowtab(0);
 
-  // first-product A fragments from T: lane (m, q) is k' = m (k = m / 2, re/im = m % 2)
+  // T of this (b, o): one contiguous block of 2 ma mb values per output channel.  The blocks
+  // are staged in LDS (in the s_y region, unused until the first chunk's bypass) with
+  // coalesced float4 loads, and the fragments below read them there: as per-lane gathers from
+  // global memory they kept some eighty loads and their registers in flight at once.
   const int k = m >> 1, ri = m & 1;
   const int twoma = 2 * a.ma;
+  const int tblk = twoma * a.mb;  // float2 per channel; even (ma % 4 == 0)
+  float2* s_t = reinterpret_cast<float2*>(s_y);
+  {
+    const int tf4 = tblk >> 1;
+    const float2* tsrc = a.T + ((int64_t)b * a.Cout * a.O + o) * (int64_t)tblk;
+    const int64_t cstride = (int64_t)a.O * tblk;
+    for (int e = tid; e < a.Cout * tf4; e += 256) {
+      const int ch = e / tf4, r = e - ch * tf4;
+      *reinterpret_cast<float4*>(s_t + ch * tblk + 2 * r) =
+          *reinterpret_cast<const float4*>(tsrc + ch * cstride + 2 * r);
+    }
+  }
+  __syncthreads();
+  // first-product A fragments from T: lane (m, q) is k' = m (k = m / 2, re/im = m % 2)
   float afr[BF ? 1 : kErCPW][BF ? 1 : kErMA];
   V8 afb[BF ? kErCPW : 1][2];
 #pragma unroll
   for (int j = 0; j < kErCPW; ++j) {
     const int cor = wave + 4 * j;
     const bool co_ok = cor < a.Cout;
-    const float2* tb =
-        a.T + (((int64_t)b * a.Cout + min(cor, a.Cout - 1)) * a.O + o) * (int64_t)(twoma * a.mb);
+    const float2* tb = s_t + min(cor, a.Cout - 1) * tblk;
     const int kc = min(k, a.mb - 1);
     if constexpr (!BF) {
       // K-step ks, slot q <-> s' = (q / 2) block, s = (q % 2) ma + ks.  The component is
@@ -191,6 +238,9 @@ k_epi_rows(RowsEpiArgs a) {
               (E)keep_if(t.x * fx + t.y * fy, co_ok && s < twoma && tcol < a.KA && k < a.mb);
         }
     }
+    // one channel's LDS reads at a time: scheduled together, all of them and their registers
+    // would be live at once
+    __builtin_amdgcn_sched_barrier(0);
   }
   // second-product B fragments (G[k' = 4 q + r][c]), c = 16 ct + m
   float gfr[BF ? 1 : 2][4];
@@ -233,31 +283,6 @@ k_epi_rows(RowsEpiArgs a) {
       }
     }
   }
-  // first-product B fragments: A[row][s'] for this lane's row of chunk c
-  float bfr[BF ? 1 : kErMA];
-  V8 bhi[2], blo[2];
-  auto load_rowtab = [&](int c) {
-    const int row = kErRows * c + m;
-    if constexpr (!BF) {
-#pragma unroll
-      for (int i = 0; i < kErMA / 4; ++i) {
-        const int col = min((q >> 1) * a.SO + (q & 1) * a.ma + 4 * i, a.KA - 4);
-        const float4 v = *reinterpret_cast<const float4*>(a.ainv + row * a.KA + col);
-        bfr[4 * i + 0] = v.x;
-        bfr[4 * i + 1] = v.y;
-        bfr[4 * i + 2] = v.z;
-        bfr[4 * i + 3] = v.w;
-      }
-    } else {
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int col = min(32 * jj + 8 * q, a.KA - 8);
-        bhi[jj] = *reinterpret_cast<const V8*>(a.ainv_bf + row * a.KA + col);
-        blo[jj] = *reinterpret_cast<const V8*>(a.ainv_lo + row * a.KA + col);
-      }
-    }
-  };
-  load_rowtab(0);
   const int64_t ybase = (int64_t)b * a.Cout * chs + (int64_t)o * plane;
 
   // global stores per thread in a chunk's store pass; vector-memory operations retire in issue
@@ -265,9 +290,9 @@ k_epi_rows(RowsEpiArgs a) {
   // stores in flight while guaranteeing this chunk's x copy and row table
   constexpr int kStores = (MODE == 2 ? 2 : 1) * kErXPT;
   static_assert(kStores < 16, "vmcnt field");
-  // fp32: set-up loads done before the loop, so that the loop's own waits are those of its
-  // steady state (the compiler merges the first iteration's state with the later ones); the
-  // bf16 variants spill registers with it and keep the merged waits
+  // set-up loads done before the loop, so that the loop's own waits are those of its steady
+  // state (the compiler merges the first iteration's state with the later ones).  The half
+  // variants run out of registers with this wait; the load order above gives them the same.
   if constexpr (!BF) __builtin_amdgcn_s_waitcnt(kWaitVm0);
   for (int c = 0; c < nchunk; ++c) {
     // x chunk c in s_x, the row table of chunk c in registers; s_y free (previous stores read)
@@ -359,8 +384,8 @@ k_epi_rows(RowsEpiArgs a) {
     for (int i = 0; i < kErXPT; ++i) {
       if constexpr (MODE == 2) *reinterpret_cast<float4*>(a.zsave + yo[i]) = zv[i];
       float4 v = zv[i];
-      if constexpr (BLK) {
-        if (a.gelu) {
+      if constexpr (BLK && G) {
+        {
           v.x = gelu_as(zv[i].x);
           v.y = gelu_as(zv[i].y);
           v.z = gelu_as(zv[i].z);
@@ -395,19 +420,27 @@ bool epilogue_rows_ok(const fno_plan* p, int mode, const float* x, const float* 
   return al16(x) && al16(y) && al16(zsave);
 }
 
-template <int H, int MODE>
+template <int H, int MODE, bool G>
 static hipError_t launch_rows_t(const RowsEpiArgs& a, int B, hipStream_t s) {
   const int RP = kErRows * a.Nb;
   const int xfl = 4 * kErKB * RP > 4 * 256 * kErXPT ? 4 * kErKB * RP : 4 * 256 * kErXPT;
   const size_t lds = sizeof(float) * ((size_t)(a.Cout + 1) * kErYC + (MODE >= 1 ? xfl : 0));
   if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_epi_rows<H, MODE>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_epi_rows<H, MODE, G>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((k_epi_rows<H, MODE>), dim3((unsigned)a.O, (unsigned)B), dim3(256), lds, s,
+  hipLaunchKernelGGL((k_epi_rows<H, MODE, G>), dim3((unsigned)a.O, (unsigned)B), dim3(256), lds, s,
                      a);
   return hipGetLastError();
+}
+
+template <int H>
+static hipError_t launch_rows_h(const RowsEpiArgs& a, int md, int B, hipStream_t s) {
+  if (md == 0) return launch_rows_t<H, 0, false>(a, B, s);
+  if (md == 1)
+    return a.gelu ? launch_rows_t<H, 1, true>(a, B, s) : launch_rows_t<H, 1, false>(a, B, s);
+  return a.gelu ? launch_rows_t<H, 2, true>(a, B, s) : launch_rows_t<H, 2, false>(a, B, s);
 }
 
 hipError_t launch_epilogue_rows(const fno_plan* p, int mode, const float2* T, const float* x,
@@ -439,19 +472,9 @@ hipError_t launch_epilogue_rows(const fno_plan* p, int mode, const float2* T, co
   a.gt_bf = p->t.gt_fwd_bf;
   a.flag = p->g.half_flag;
   const int md = mode == EPI_SPECTRAL ? 0 : (zsave ? 2 : 1);
-  if (g.half == 2) {
-    if (md == 0) return launch_rows_t<2, 0>(a, g.B, s);
-    if (md == 1) return launch_rows_t<2, 1>(a, g.B, s);
-    return launch_rows_t<2, 2>(a, g.B, s);
-  }
-  if (g.half == 1) {
-    if (md == 0) return launch_rows_t<1, 0>(a, g.B, s);
-    if (md == 1) return launch_rows_t<1, 1>(a, g.B, s);
-    return launch_rows_t<1, 2>(a, g.B, s);
-  }
-  if (md == 0) return launch_rows_t<0, 0>(a, g.B, s);
-  if (md == 1) return launch_rows_t<0, 1>(a, g.B, s);
-  return launch_rows_t<0, 2>(a, g.B, s);
+  if (g.half == 2) return launch_rows_h<2>(a, md, g.B, s);
+  if (g.half == 1) return launch_rows_h<1>(a, md, g.B, s);
+  return launch_rows_h<0>(a, md, g.B, s);
 }
 
 }  // namespace fno

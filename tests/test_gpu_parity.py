@@ -293,24 +293,28 @@ def test_f16_overflow_is_reported(L, case):
             assert finite and not flagged
         plan.close()
 
-def test_gelu_off_and_bias_off(L):
-    """Flags: without GELU the block returns z; without BIAS the bias pointer is ignored."""
-    announce("flags")
+@pytest.mark.parametrize("prec", PRECISIONS[:3], ids=[p[0] for p in PRECISIONS[:3]])
+def test_gelu_off_and_bias_off(L, prec):
+    """Flags: without GELU the block returns z; without BIAS the bias pointer is ignored.  The
+    grid's 24-point contiguous axis takes the fused row-axis epilogue."""
+    pname, mixed, tanh = prec
+    announce("flags", pname)
+    tol = tol_for(mixed)
     grid, modes = (16, 24), (4, 6)
     x, w, wb, b = inputs.small_case(21, 2, 3, 4, grid, modes)
     gy = inputs.normal_like(21, (2, 4) + grid)
-    plan = L.Plan(2, 3, 4, grid, modes, gelu=False, bias=False)
+    plan = L.Plan(2, 3, 4, grid, modes, mixed=mixed, tanh=tanh, gelu=False, bias=False)
     tx, tw, twb, tg = (_dev(a) for a in (x, w, wb, gy))
     save = plan.new_save()
     y = plan.block_fwd(tx, tw, twb, None, save=save)
     g = plan.block_bwd(tx, tw, twb, None, save, tg)
     _torch().cuda.synchronize()
-    ref = O.block_bwd(x, w, wb, None, modes, gy, act=False)
-    check("z", _host(y), ref["fwd"]["y"], TOL_F32)
-    check("grad_x", _host(g["x"]), ref["grad_x"], TOL_F32)
-    check("grad_w", _host(g["w"]), ref["grad_w"], TOL_F32)
-    check("grad_wb", _host(g["wb"]), ref["grad_wb"], TOL_F32)
-    check("grad_bias", _host(g["bias"]), ref["grad_bias"], TOL_F32)
+    ref = O.block_bwd(x, w, wb, None, modes, gy, tanh=tanh, act=False)
+    check("z", _host(y), ref["fwd"]["y"], tol)
+    check("grad_x", _host(g["x"]), ref["grad_x"], tol)
+    check("grad_w", _host(g["w"]), ref["grad_w"], tol)
+    check("grad_wb", _host(g["wb"]), ref["grad_wb"], tol)
+    check("grad_bias", _host(g["bias"]), ref["grad_bias"], tol)
     plan.close()
 
 
