@@ -39,6 +39,8 @@ CASES = [
     # and adds their partial spectra
     ("2d_chunked_nb64", 1, 4, 4, (256, 64), (8, 8)),
     ("2d_chunked_nb512", 1, 2, 2, (256, 512), (16, 32)),
+    # half plans: 64 kept bins on rows of 128 take the eight-wave plane kernel
+    ("2d_mc_nb128_jp64", 2, 6, 6, (48, 128), (4, 32)),
     # shapes taken by the short-row plane kernel (contiguous axis <= 32, a multiple of 4)
     ("4d_short_t20", 1, 3, 4, (4, 6, 16, 20), (2, 2, 4, 8)),
     ("3d_short_t20_jp32", 2, 5, 3, (6, 32, 20), (3, 8, 10)),
@@ -418,7 +420,7 @@ def test_bad_workspace_is_an_error(L):
 # contiguous axis (line kernels decline, generic epilogue), 3D and 4D
 IG_CASES = [c for c in CASES if c[0] in (
     "2d_ragged", "2d_c1shape", "2d_mc_c16", "2d_mc_c32", "2d_mc_c64", "3d_mc_c20",
-    "4d_short_t20", "2d_rows_c20", "2d_odd_maxmodes", "4d_t20")]
+    "4d_short_t20", "2d_rows_c20", "2d_odd_maxmodes", "4d_t20", "2d_mc_nb128_jp64")]
 
 
 @pytest.mark.parametrize("act", [True, False], ids=["gelu_out", "z_out"])
