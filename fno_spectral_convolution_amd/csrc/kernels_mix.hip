@@ -325,6 +325,92 @@ __global__ void __launch_bounds__(256) k_mix_mfma_bwd(Geom g, const int32_t* __r
 }
 
 // ------------------------------------------------------------------------------------------
+// ------------------------------------------------------------------------------------------
+// Forward mix for one or two batch entries, on the vector units.  The matrix-core tiles above
+// hold eight batch entries per fragment, so with one or two most of each product is padding
+// and the kernel streams W well below the memory rate.  Here lane l of a work-group owns mode
+// 64 blockIdx.x + l and wave v owns output channels OPT v .. OPT v + OPT - 1: every W load of a
+// wave is a run of 64 consecutive modes, and the waves of a work-group read the same input
+// spectrum (through L1 / L2).  Half plans round both operands to their format, whose products
+// are exact in float32, as the matrix cores take them.
+template <int H, int NB, int OPT>
+__global__ void __launch_bounds__(1024) k_mix_valu_fwd(Geom g, const int32_t* __restrict__ mode_woff,
+                                                       const float2* __restrict__ spec,
+                                                       const float2* __restrict__ w,
+                                                       float2* __restrict__ out) {
+  const int64_t K = g.K;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 64 + lane;
+  const int64_t tm = t < K ? t : K - 1;
+  const int o0 = wave * OPT;
+  const int wb = mode_woff[tm];
+  int wo[OPT];
+#pragma unroll
+  for (int j = 0; j < OPT; ++j) wo[j] = wb + min(o0 + j, g.Cout - 1) * g.w_so;
+  float ar[NB][OPT], ai[NB][OPT];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int j = 0; j < OPT; ++j) ar[b][j] = ai[b][j] = 0.f;
+#pragma unroll 4
+  for (int i = 0; i < g.Cin; ++i) {
+    float2 xv[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      xv[b] = spec[((int64_t)b * g.Cin + i) * K + tm];
+      if constexpr (H != 0) xv[b] = make_float2(round_half<H>(xv[b].x), round_half<H>(xv[b].y));
+    }
+#pragma unroll
+    for (int j = 0; j < OPT; ++j) {
+      float2 wv = w[wo[j] + i * g.w_si];
+      if constexpr (H != 0) wv = make_float2(round_half<H>(wv.x), round_half<H>(wv.y));
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        ar[b][j] = fmaf(xv[b].x, wv.x, ar[b][j]);
+        ar[b][j] = fmaf(-xv[b].y, wv.y, ar[b][j]);
+        ai[b][j] = fmaf(xv[b].x, wv.y, ai[b][j]);
+        ai[b][j] = fmaf(xv[b].y, wv.x, ai[b][j]);
+      }
+    }
+  }
+  if (t >= K) return;
+  const float gain = H == 2 ? g.mix_gain[0] : 1.0f;  // IEEE half: the mix gain (a power of two)
+#pragma unroll
+  for (int j = 0; j < OPT; ++j) {
+    if (o0 + j >= g.Cout) break;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      out[((int64_t)b * g.Cout + o0 + j) * K + t] = make_float2(ar[b][j] * gain, ai[b][j] * gain);
+  }
+}
+
+// the vector-unit forward mix applies to one or two batch entries and at most 16 x 8 outputs
+static bool mix_valu_ok(const Geom& g) { return g.B >= 1 && g.B <= 2 && g.Cout <= 128; }
+
+template <int H, int NB>
+static void launch_mix_valu_nb(const Geom& g, const int32_t* woff, const float2* xhat,
+                               const float2* w, float2* yhat, hipStream_t s) {
+  const unsigned blocks = (unsigned)((g.K + 63) / 64);
+  if (g.Cout <= 64) {
+    const int waves = (g.Cout + 3) / 4;
+    hipLaunchKernelGGL((k_mix_valu_fwd<H, NB, 4>), dim3(blocks), dim3(64 * waves), 0, s, g, woff,
+                       xhat, w, yhat);
+  } else {
+    const int waves = (g.Cout + 7) / 8;
+    hipLaunchKernelGGL((k_mix_valu_fwd<H, NB, 8>), dim3(blocks), dim3(64 * waves), 0, s, g, woff,
+                       xhat, w, yhat);
+  }
+}
+
+template <int H>
+static void launch_mix_valu(const Geom& g, const int32_t* woff, const float2* xhat,
+                            const float2* w, float2* yhat, hipStream_t s) {
+  if (g.B == 1)
+    launch_mix_valu_nb<H, 1>(g, woff, xhat, w, yhat, s);
+  else
+    launch_mix_valu_nb<H, 2>(g, woff, xhat, w, yhat, s);
+}
+
 static dim3 mix_grid(const Geom& g, int cols) {
   return dim3((unsigned)((g.K + kMT - 1) / kMT), (unsigned)((cols + 15) / 16),
               (unsigned)((g.B + 7) / 8));
@@ -332,6 +418,15 @@ static dim3 mix_grid(const Geom& g, int cols) {
 
 hipError_t launch_mix_fwd_g(const Geom& g, const int32_t* woff, const float2* xhat,
                             const float2* w, float2* yhat, hipStream_t s) {
+  if (mix_valu_ok(g)) {
+    if (g.half == 2)
+      launch_mix_valu<2>(g, woff, xhat, w, yhat, s);
+    else if (g.half == 1)
+      launch_mix_valu<1>(g, woff, xhat, w, yhat, s);
+    else
+      launch_mix_valu<0>(g, woff, xhat, w, yhat, s);
+    return hipGetLastError();
+  }
   if (g.half == 2)
     hipLaunchKernelGGL((k_mix_mfma<2, false>), mix_grid(g, g.Cout), dim3(256), 0, s, g, woff,
                        xhat, w, yhat);
