@@ -384,20 +384,156 @@ __global__ void __launch_bounds__(1024) k_mix_valu_fwd(Geom g, const int32_t* __
   }
 }
 
-// the vector-unit forward mix applies to one or two batch entries and at most 16 x 8 outputs
-static bool mix_valu_ok(const Geom& g) { return g.B >= 1 && g.B <= 2 && g.Cout <= 128; }
+// Both gradients of the mix for one or two batch entries, on the vector units: lane l owns mode
+// 64 blockIdx.x + l and wave v input channels OPT v .. OPT v + OPT - 1.  For each output
+// channel o the wave loads g[b, o] (shared by the work-group's waves) and, per input channel,
+//   ghx[b, i] += g[b, o] sc conj(W[i, o])          (when ghx is wanted)
+//   dW[i, o]   = sum_b conj(xhat[b, i]) g[b, o] sc  (when dw is wanted; xhat held in registers)
+// so that W loads and dW stores are runs of 64 consecutive modes.  Operands are rounded as the
+// matrix-core kernels round them (g after its scale).
+template <int H, int NB, int OPT>
+__global__ void __launch_bounds__(1024) k_mix_valu_bwd(Geom g, const int32_t* __restrict__ mode_woff,
+                                                       const float2* __restrict__ xhat,
+                                                       const float2* __restrict__ ghat,
+                                                       const float2* __restrict__ w,
+                                                       float2* __restrict__ ghx,
+                                                       float2* __restrict__ dw) {
+  const int64_t K = g.K;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 64 + lane;
+  const int64_t tm = t < K ? t : K - 1;
+  const bool live = t < K;
+  const int i0 = wave * OPT;
+  const int wb = mode_woff[tm];
+  const float sc = mix_scale(g, tm);
+  auto rnd = [](float2 v) {
+    if constexpr (H != 0) v = make_float2(round_half<H>(v.x), round_half<H>(v.y));
+    return v;
+  };
+  int wi[OPT];
+  float2 xv[NB][OPT];
+#pragma unroll
+  for (int j = 0; j < OPT; ++j) {
+    const int i = min(i0 + j, g.Cin - 1);
+    wi[j] = wb + i * g.w_si;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      xv[b][j] = dw ? rnd(xhat[((int64_t)b * g.Cin + i) * K + tm]) : make_float2(0.f, 0.f);
+  }
+  float ar[NB][OPT], ai[NB][OPT];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int j = 0; j < OPT; ++j) ar[b][j] = ai[b][j] = 0.f;
+  bool bad = false;  // IEEE-half plans: a non-finite weight gradient was written
+#pragma unroll 2
+  for (int o = 0; o < g.Cout; ++o) {
+    float2 gv[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float2 v = ghat[((int64_t)b * g.Cout + o) * K + tm];
+      gv[b] = rnd(make_float2(v.x * sc, v.y * sc));
+    }
+    if (ghx) {
+#pragma unroll
+      for (int j = 0; j < OPT; ++j) {
+        const float2 wv = rnd(w[wi[j] + o * g.w_so]);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {  // g conj(w)
+          ar[b][j] = fmaf(gv[b].x, wv.x, ar[b][j]);
+          ar[b][j] = fmaf(gv[b].y, wv.y, ar[b][j]);
+          ai[b][j] = fmaf(gv[b].y, wv.x, ai[b][j]);
+          ai[b][j] = fmaf(-gv[b].x, wv.y, ai[b][j]);
+        }
+      }
+    }
+    if (dw) {
+#pragma unroll
+      for (int j = 0; j < OPT; ++j) {
+        float re = 0.f, im = 0.f;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {  // conj(x) g
+          re = fmaf(xv[b][j].x, gv[b].x, re);
+          re = fmaf(xv[b][j].y, gv[b].y, re);
+          im = fmaf(xv[b][j].x, gv[b].y, im);
+          im = fmaf(-xv[b][j].y, gv[b].x, im);
+        }
+        if (live && i0 + j < g.Cin) {
+          if constexpr (H == 2) bad |= !(__builtin_isfinite(re) & __builtin_isfinite(im));
+          dw[wi[j] + o * g.w_so] = make_float2(re, im);
+        }
+      }
+    }
+  }
+  if (ghx && live) {
+    const float gain = H == 2 ? g.mix_gain[1] : 1.0f;
+#pragma unroll
+    for (int j = 0; j < OPT; ++j) {
+      if (i0 + j >= g.Cin) break;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        ghx[((int64_t)b * g.Cin + i0 + j) * K + t] = make_float2(ar[b][j] * gain, ai[b][j] * gain);
+    }
+  }
+  if constexpr (H == 2) raise_half_flag(g.half_flag, bad);
+}
+
+// the vector-unit mixes apply to one or two batch entries and at most 16 x 4 channels on the
+// side a work-group's waves split (plans hold at most 64)
+static bool mix_valu_ok(const Geom& g) { return g.B >= 1 && g.B <= 2 && g.Cout <= 64; }
+static bool mix_valu_bwd_ok(const Geom& g) { return g.B >= 1 && g.B <= 2 && g.Cin <= 64; }
+
+// channels per wave of the vector-unit mixes: two where four would leave fewer than 4096 waves
+// in the grid (the work-group keeps at most 16 waves), else four
+static int mix_valu_opt(int64_t blocks, int chans) {
+  return chans <= 32 && blocks * ((chans + 3) / 4) < 4096 ? 2 : 4;
+}
+
+template <int H, int NB>
+static void launch_mix_valu_bwd_nb(const Geom& g, const int32_t* woff, const float2* xhat,
+                                   const float2* ghat, const float2* w, float2* ghx, float2* dw,
+                                   hipStream_t s) {
+  const unsigned blocks = (unsigned)((g.K + 63) / 64);
+  const int opt = mix_valu_opt(blocks, g.Cin);
+  if (opt == 2) {
+    const int waves = (g.Cin + 1) / 2;
+    hipLaunchKernelGGL((k_mix_valu_bwd<H, NB, 2>), dim3(blocks), dim3(64 * waves), 0, s, g, woff,
+                       xhat, ghat, w, ghx, dw);
+  } else {
+    const int waves = (g.Cin + 3) / 4;
+    hipLaunchKernelGGL((k_mix_valu_bwd<H, NB, 4>), dim3(blocks), dim3(64 * waves), 0, s, g, woff,
+                       xhat, ghat, w, ghx, dw);
+  }
+}
+
+static hipError_t launch_mix_valu_bwd(const Geom& g, const int32_t* woff, const float2* xhat,
+                                      const float2* ghat, const float2* w, float2* ghx,
+                                      float2* dw, hipStream_t s) {
+  if (g.half == 2) {
+    if (g.B == 1) launch_mix_valu_bwd_nb<2, 1>(g, woff, xhat, ghat, w, ghx, dw, s);
+    else launch_mix_valu_bwd_nb<2, 2>(g, woff, xhat, ghat, w, ghx, dw, s);
+  } else if (g.half == 1) {
+    if (g.B == 1) launch_mix_valu_bwd_nb<1, 1>(g, woff, xhat, ghat, w, ghx, dw, s);
+    else launch_mix_valu_bwd_nb<1, 2>(g, woff, xhat, ghat, w, ghx, dw, s);
+  } else {
+    if (g.B == 1) launch_mix_valu_bwd_nb<0, 1>(g, woff, xhat, ghat, w, ghx, dw, s);
+    else launch_mix_valu_bwd_nb<0, 2>(g, woff, xhat, ghat, w, ghx, dw, s);
+  }
+  return hipGetLastError();
+}
 
 template <int H, int NB>
 static void launch_mix_valu_nb(const Geom& g, const int32_t* woff, const float2* xhat,
                                const float2* w, float2* yhat, hipStream_t s) {
   const unsigned blocks = (unsigned)((g.K + 63) / 64);
-  if (g.Cout <= 64) {
-    const int waves = (g.Cout + 3) / 4;
-    hipLaunchKernelGGL((k_mix_valu_fwd<H, NB, 4>), dim3(blocks), dim3(64 * waves), 0, s, g, woff,
+  const int opt = mix_valu_opt(blocks, g.Cout);
+  if (opt == 2) {
+    const int waves = (g.Cout + 1) / 2;
+    hipLaunchKernelGGL((k_mix_valu_fwd<H, NB, 2>), dim3(blocks), dim3(64 * waves), 0, s, g, woff,
                        xhat, w, yhat);
   } else {
-    const int waves = (g.Cout + 7) / 8;
-    hipLaunchKernelGGL((k_mix_valu_fwd<H, NB, 8>), dim3(blocks), dim3(64 * waves), 0, s, g, woff,
+    const int waves = (g.Cout + 3) / 4;
+    hipLaunchKernelGGL((k_mix_valu_fwd<H, NB, 4>), dim3(blocks), dim3(64 * waves), 0, s, g, woff,
                        xhat, w, yhat);
   }
 }
@@ -441,6 +577,7 @@ hipError_t launch_mix_fwd_g(const Geom& g, const int32_t* woff, const float2* xh
 
 hipError_t launch_mix_bwd_dx_g(const Geom& g, const int32_t* woff, const float2* ghat,
                                const float2* w, float2* ghx, hipStream_t s) {
+  if (mix_valu_bwd_ok(g)) return launch_mix_valu_bwd(g, woff, nullptr, ghat, w, ghx, nullptr, s);
   if (g.half == 2)
     hipLaunchKernelGGL((k_mix_mfma<2, true>), mix_grid(g, g.Cin), dim3(256), 0, s, g, woff,
                        ghat, w, ghx);
@@ -465,6 +602,7 @@ static dim3 mix_dw_grid(const Geom& g) {
 
 hipError_t launch_mix_bwd_dw_g(const Geom& g, const int32_t* woff, const float2* xhat,
                                const float2* ghat, float2* dw, hipStream_t s) {
+  if (mix_valu_bwd_ok(g)) return launch_mix_valu_bwd(g, woff, xhat, ghat, nullptr, nullptr, dw, s);
   const dim3 grid = mix_dw_grid(g);
   if (g.half == 2)
     hipLaunchKernelGGL((k_mix_mfma_dw<2>), grid, dim3(256), 0, s, g, woff, xhat, ghat, dw);
@@ -495,6 +633,8 @@ hipError_t launch_mix_bwd_dw(const fno_plan* p, const float2* xhat, const float2
 hipError_t launch_mix_bwd_both(const fno_plan* p, const float2* xhat, const float2* ghat,
                                const float2* w, float2* ghx, float2* dw, hipStream_t s) {
   const Geom& g = p->g;
+  if (mix_valu_bwd_ok(g))
+    return launch_mix_valu_bwd(g, p->t.mode_woff, xhat, ghat, w, ghx, dw, s);
   const dim3 gx = mix_grid(g, g.Cin), gw = mix_dw_grid(g);
   const uint64_t n = (uint64_t)gx.x * gx.y * gx.z + (uint64_t)gw.x * gw.y * gw.z;
   if (n > 0x7fffffffu) return hipErrorInvalidValue;
