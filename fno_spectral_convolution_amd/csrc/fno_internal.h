@@ -202,9 +202,10 @@ bool epilogue_fast_ok(const fno_plan* p, int mode, bool fwd);
 // spectrum after the inverse of the outer axes 0..d-3 only, [B][Cout][O][2ma][mb].
 bool epilogue_rows_ok(const fno_plan* p, int mode, const float* x, const float* y,
                       const float* zsave);
-hipError_t launch_epilogue_rows(const fno_plan* p, int mode, const float2* T, const float* x,
+// t_half: T in the plan's half format (half plans; the rounding the epilogue applies to T)
+hipError_t launch_epilogue_rows(const fno_plan* p, int mode, const void* T, const float* x,
                                 const float* wb, const float* bias, float* y, float* zsave,
-                                hipStream_t s);
+                                hipStream_t s, bool t_half = false);
 // the backward epilogue takes the matrix-core kernel (which writes epilogue_bwd_fast_groups
 // partial rows) only when grad_x is produced; otherwise the generic kernel (nred rows)
 inline bool epilogue_bwd_fast(const fno_plan* p, int mode, const float* grad_x) {
@@ -242,6 +243,10 @@ hipError_t launch_outer_mfma(const fno_plan* p, int axis, int chans, bool inv, c
 // the rounding the matrix-core line epilogues apply to T when they stage it.
 hipError_t launch_outer_mfma_half(const fno_plan* p, int axis, int chans, const float2* in,
                                   uint16_t* out, hipStream_t s);
+// whether the forward's inverse of outer axis `axis` (Cout channels) streams column blocks of
+// many wide slabs, so that launch_outer_mfma_half writes it in the half format with
+// k_outer_inv_stream (half plans)
+bool outer_inv_half_ok(const fno_plan* p, int axis);
 hipError_t launch_bypass_grad_finish(const fno_plan* p, const float* red_part, float* dwb,
                                      float* dbias, const float* grad_x, hipStream_t s);
 hipError_t launch_pointwise(int64_t batch, int64_t npts, int cin, int hidden, int cout,

@@ -39,6 +39,7 @@ struct RowsEpiArgs {
   int O;
   int gelu;
   const float2* T;          // [B][Cout][O][2 ma][mb]
+  const uint16_t* Th;       // the same in the plan's half format (re, im pairs), or null
   const float* x;           // [B][Cin][O][Na][Nb]
   const float* wb;          // [Cout][Cin]
   const float* bias;        // [Cout] or null
@@ -192,12 +193,24 @@ k_epi_rows(RowsEpiArgs a) {
   float2* s_t = reinterpret_cast<float2*>(s_y);
   {
     const int tf4 = tblk >> 1;
-    const float2* tsrc = a.T + ((int64_t)b * a.Cout * a.O + o) * (int64_t)tblk;
+    const int64_t tb0 = ((int64_t)b * a.Cout * a.O + o) * (int64_t)tblk;  // complex index
     const int64_t cstride = (int64_t)a.O * tblk;
     for (int e = tid; e < a.Cout * tf4; e += 256) {
       const int ch = e / tf4, r = e - ch * tf4;
-      *reinterpret_cast<float4*>(s_t + ch * tblk + 2 * r) =
-          *reinterpret_cast<const float4*>(tsrc + ch * cstride + 2 * r);
+      const int64_t ci = tb0 + ch * cstride + 2 * r;  // two complex values
+      float4 v;
+      if constexpr (BF) {
+        if (a.Th) {  // exact: the half values as floats
+          const uint2 u = *reinterpret_cast<const uint2*>(a.Th + 2 * ci);
+          v = make_float4(HT::value((uint16_t)(u.x & 0xffffu)), HT::value((uint16_t)(u.x >> 16)),
+                          HT::value((uint16_t)(u.y & 0xffffu)), HT::value((uint16_t)(u.y >> 16)));
+        } else {
+          v = *reinterpret_cast<const float4*>(a.T + ci);
+        }
+      } else {
+        v = *reinterpret_cast<const float4*>(a.T + ci);
+      }
+      *reinterpret_cast<float4*>(s_t + ch * tblk + 2 * r) = v;
     }
   }
   __syncthreads();
@@ -443,9 +456,9 @@ static hipError_t launch_rows_h(const RowsEpiArgs& a, int md, int B, hipStream_t
   return a.gelu ? launch_rows_t<H, 2, true>(a, B, s) : launch_rows_t<H, 2, false>(a, B, s);
 }
 
-hipError_t launch_epilogue_rows(const fno_plan* p, int mode, const float2* T, const float* x,
+hipError_t launch_epilogue_rows(const fno_plan* p, int mode, const void* T, const float* x,
                                 const float* wb, const float* bias, float* y, float* zsave,
-                                hipStream_t s) {
+                                hipStream_t s, bool t_half) {
   const Geom& g = p->g;
   RowsEpiArgs a{};
   a.Na = g.Na;
@@ -459,7 +472,9 @@ hipError_t launch_epilogue_rows(const fno_plan* p, int mode, const float2* T, co
   a.kpad = p->kpad;
   a.O = (int)g.O;
   a.gelu = (mode == EPI_BLOCK && (p->desc.flags & FNO_FLAG_GELU)) ? 1 : 0;
-  a.T = T;
+  if (t_half && !g.bf16) return hipErrorInvalidValue;
+  a.T = t_half ? nullptr : static_cast<const float2*>(T);
+  a.Th = t_half ? static_cast<const uint16_t*>(T) : nullptr;
   a.x = x;
   a.wb = wb;
   a.bias = (p->desc.flags & FNO_FLAG_BIAS) ? bias : nullptr;

@@ -539,6 +539,29 @@ __global__ void __launch_bounds__(256) k_outer_inv_stream(OuterArgs a) {
       }
     }
     // lane (n = m, q), register r: output row 16 mt + 4 q + r, column c0 + 16 (w NTW + j) + m
+    if constexpr (BF) {
+      if (a.outh) {
+        // the plan's half format (nearest even), as its consumer would round it: an even lane
+        // (real part) stores its value with its odd neighbour's (imaginary part, swapped in by
+        // a DPP quad permutation) as one 32-bit pair
+        uint16_t* dh = a.outh + pre * a.Lout * a.post2;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int o = 16 * mt + 4 * q + r;
+#pragma unroll
+          for (int j = 0; j < NTW; ++j) {
+            const float v = acc[j][r];
+            const float pv = __int_as_float(
+                __builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+            const int col = c0 + 16 * (wave * NTW + j) + m;
+            if (o < a.Lout && !odd && col < a.post2)
+              *reinterpret_cast<uint32_t*>(dh + (int64_t)o * a.post2 + col) =
+                  HT::pack2(v, pv);
+          }
+        }
+        continue;
+      }
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int o = 16 * mt + 4 * q + r;
@@ -728,6 +751,16 @@ static hipError_t launch_outer_stream(int mt, int ntw, dim3 grid, const OuterArg
 
 static int pad16(int v) { return (v + 15) / 16 * 16; }
 
+// the inverse from few kept rows streams column blocks of many wide slabs (k_outer_inv_stream)
+static bool inv_stream_ok(const OuterArgs& a, int64_t pre) {
+  return a.Lin_pad <= 64 && a.post2 % 4 == 0 && a.post2 >= 256 && pre >= 1024 && pre <= 65535;
+}
+
+// launch of k_outer_inv_stream for the shape in a (column blocks as wide as the row needs, up
+// to 6 N-tiles per wave, narrower while that leaves fewer than ~1024 work-groups)
+static hipError_t launch_inv_stream_any(const OuterArgs& a, int64_t pre, int half,
+                                        hipStream_t s);
+
 static hipError_t launch_outer_generic(const fno_plan* p, OuterArgs a, int64_t pre,
                                        hipStream_t s);
 // work-groups the multi-slab inverse aims for (each walks ceil(slabs / this) slabs)
@@ -758,21 +791,11 @@ hipError_t launch_outer_mfma(const fno_plan* p, int axis, int chans, bool inv, c
     a.A = bf ? (const void*)p->t.ofwd_bf[axis] : (const void*)p->t.ofwd[axis];
     a.Alo = p->t.ofwd_bf_lo[axis];
   }
-  if (inv && a.Lin_pad <= 64 && a.post2 % 4 == 0 && a.post2 >= 256 && pre >= 1024 &&
-      pre <= 65535) {
+  if (inv && inv_stream_ok(a, pre)) {
     // few kept rows in, N rows out, many wide slabs: stage the kept rows of a column block once
-    // and walk the output row tiles (blocks as wide as the row needs, up to 6 N-tiles per wave).
-    // Narrow or few slabs keep the generic kernel, whose waves split the output rows instead.
-    int ntw = (int)((a.post2 + 63) / 64);
-    if (ntw > 6) ntw = 6;
-    while (ntw > 1 && pre * ((a.post2 + 64 * ntw - 1) / (64 * ntw)) < 1024) --ntw;
-    while (ntw > 1 && sizeof(float) * (size_t)a.Lin_pad * (64 * ntw + 4) > 65536) --ntw;
-    const int cb = 64 * ntw;
-    const size_t lds = sizeof(float) * (size_t)a.Lin_pad * (cb + 4);
-    dim3 grid((unsigned)((a.post2 + cb - 1) / cb), (unsigned)pre);
-    return g.half == 2 ? launch_inv_stream<2>(ntw, grid, lds, a, s)
-           : g.half == 1 ? launch_inv_stream<1>(ntw, grid, lds, a, s)
-                         : launch_inv_stream<0>(ntw, grid, lds, a, s);
+    // and walk the output row tiles.  Narrow or few slabs keep the generic kernel, whose waves
+    // split the output rows instead.
+    return launch_inv_stream_any(a, pre, g.half, s);
   }
   if (inv && !bf && a.Lin_pad <= 32 && a.Lout_pad <= 128 && a.post2 <= 64 && pre >= 4096) {
     // many narrow float32 slabs: work-groups walk several slabs with the table in registers
@@ -801,6 +824,20 @@ hipError_t launch_outer_mfma(const fno_plan* p, int axis, int chans, bool inv, c
     return launch_outer_stream(mt, ntw, grid, a, g.half, s);
   }
   return launch_outer_generic(p, a, pre, s);
+}
+
+static hipError_t launch_inv_stream_any(const OuterArgs& a, int64_t pre, int half,
+                                        hipStream_t s) {
+  int ntw = (int)((a.post2 + 63) / 64);
+  if (ntw > 6) ntw = 6;
+  while (ntw > 1 && pre * ((a.post2 + 64 * ntw - 1) / (64 * ntw)) < 1024) --ntw;
+  while (ntw > 1 && sizeof(float) * (size_t)a.Lin_pad * (64 * ntw + 4) > 65536) --ntw;
+  const int cb = 64 * ntw;
+  const size_t lds = sizeof(float) * (size_t)a.Lin_pad * (cb + 4);
+  dim3 grid((unsigned)((a.post2 + cb - 1) / cb), (unsigned)pre);
+  return half == 2 ? launch_inv_stream<2>(ntw, grid, lds, a, s)
+         : half == 1 ? launch_inv_stream<1>(ntw, grid, lds, a, s)
+                     : launch_inv_stream<0>(ntw, grid, lds, a, s);
 }
 
 // k_outer_mfma for the arguments of launch_outer_mfma: column tiles of 64, 32 or 16, and the
@@ -863,8 +900,23 @@ hipError_t launch_outer_mfma_half(const fno_plan* p, int axis, int chans, const 
   a.outh = out;
   a.A = (const void*)p->t.oinv_bf[axis];
   a.Alo = p->t.oinv_bf_lo[axis];
+  if (inv_stream_ok(a, pre)) return launch_inv_stream_any(a, pre, g.half, s);
   if (a.post2 < 64) return hipErrorInvalidValue;
   return launch_outer_generic(p, a, pre, s);
+}
+
+bool outer_inv_half_ok(const fno_plan* p, int axis) {
+  const Geom& g = p->g;
+  if (!g.bf16 || !outer_fast_ok(p, axis, true)) return false;
+  int64_t pre = (int64_t)g.B * g.Cout;
+  for (int i = 0; i < axis; ++i) pre *= g.N[i];
+  int64_t post = g.mb;
+  for (int i = axis + 1; i <= g.d - 2; ++i) post *= 2 * g.M[i];
+  OuterArgs a{};
+  a.Lin = 2 * g.M[axis];
+  a.Lin_pad = pad16(a.Lin);
+  a.post2 = 2 * post;
+  return inv_stream_ok(a, pre);
 }
 
 bool outer_fast_ok(const fno_plan* p, int axis, bool inv) {

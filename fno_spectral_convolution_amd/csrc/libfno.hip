@@ -808,11 +808,14 @@ fno_status block_epilogue_fwd(const fno_plan* p, int mode, const float2* yhat, c
   const float2* T = nullptr;
   fno_status st;
   if (fno::epilogue_rows_ok(p, mode, x, y, zsave)) {
-    st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T, p->g.d - 2);
+    // half plans: the last outer inverse writes T in the half format the epilogue rounds it to
+    const int d = p->g.d;
+    const bool th = d >= 3 && fno::outer_inv_half_ok(p, d - 3);
+    st = inverse_outer(p, p->g.Cout, yhat, ws, s, &T, d - 2, th);
     if (st != FNO_OK) return st;
     // timer names tell launches that also save z apart (their bytes differ)
     LAUNCH(zsave ? "epilogue_rows_fwd_zsave" : "epilogue_rows_fwd", s,
-           fno::launch_epilogue_rows(p, mode, T, x, wb, bias, y, zsave, s));
+           fno::launch_epilogue_rows(p, mode, T, x, wb, bias, y, zsave, s, th));
     return FNO_OK;
   }
   const bool fast = fno::epilogue_fast_ok(p, mode, true);

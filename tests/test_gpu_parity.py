@@ -50,6 +50,9 @@ CASES = [
     ("2d_rows_c20", 2, 20, 20, (32, 20), (8, 8)),
     ("3d_rows_c9_17", 2, 9, 17, (4, 48, 24), (2, 8, 7)),
     ("2d_rows_nb32", 1, 12, 5, (64, 32), (12, 8)),
+    # 1024 wide slabs for the second outer inverse: the streaming inverse, whose half plans
+    # write the row epilogue's spectrum in the half format
+    ("4d_rows_stream_inv", 1, 16, 16, (64, 8, 16, 20), (2, 2, 8, 8)),
 ]
 
 
