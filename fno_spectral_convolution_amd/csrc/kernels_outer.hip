@@ -15,6 +15,13 @@
 
 namespace fno {
 
+// v where keep, else zeros, by masking the bits
+__device__ __forceinline__ float4 mask4(const float4& v, bool keep) {
+  const uint32_t k = keep ? 0xffffffffu : 0u;
+  return make_float4(__uint_as_float(__float_as_uint(v.x) & k), __uint_as_float(__float_as_uint(v.y) & k),
+                     __uint_as_float(__float_as_uint(v.z) & k), __uint_as_float(__float_as_uint(v.w) & k));
+}
+
 struct OuterArgs {
   int Lin, Lout, Lin_pad, Lout_pad;
   int64_t post2;         // floats per row (2 * post)
@@ -248,13 +255,17 @@ __global__ void __launch_bounds__(256) k_outer_fwd_stream(OuterArgs a) {
     xcol_ok[i] = col < a.post2;
     xcol[i] = min(col, a.post2 - 4);
   }
-  auto load_chunk = [&](int k0, float4 (&v)[NTW]) {
+  // the raw rows (clamped, valid addresses) and a bit per element telling whether it lies in
+  // the slab; the mask is applied when the chunk is staged, so that no instruction uses a load
+  // before then (a select or mask right after each load made the compiler wait for it before
+  // issuing the next)
+  auto load_chunk = [&](int k0, float4 (&v)[NTW], uint32_t& okm) {
+    okm = 0u;
 #pragma unroll
     for (int i = 0; i < NTW; ++i) {
       const int row = k0 + xrow[i];
-      const float4 t = *reinterpret_cast<const float4*>(src + (int64_t)min(row, a.Lin - 1) * a.post2 + xcol[i]);
-      const bool ok = row < a.Lin && xcol_ok[i];
-      v[i] = ok ? t : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[i] = *reinterpret_cast<const float4*>(src + (int64_t)min(row, a.Lin - 1) * a.post2 + xcol[i]);
+      okm |= (row < a.Lin && xcol_ok[i]) ? (1u << i) : 0u;
     }
   };
   auto load_tab = [&](int k0, float4 (&r)[MT], float4 (&im)[MT]) {
@@ -271,14 +282,16 @@ __global__ void __launch_bounds__(256) k_outer_fwd_stream(OuterArgs a) {
 #pragma unroll
     for (int j = 0; j < NTW; ++j) acc[mt][j] = zero4();
   float4 xv[NTW], tr[MT], ti[MT];
-  load_chunk(0, xv);
+  uint32_t xok;
+  load_chunk(0, xv, xok);
   load_tab(0, tr, ti);
   const float sgn = (m & 1) ? 1.f : -1.f;  // Xs[k][c] = sgn * X[k][c ^ 1]
   const int nchunk = a.Lin_pad / 16;
   for (int ch = 0; ch < nchunk; ++ch) {
 #pragma unroll
     for (int i = 0; i < NTW; ++i)
-      *reinterpret_cast<float4*>(s_x + xrow[i] * CBS + 4 * ((tid + 256 * i) % F4R)) = xv[i];
+      *reinterpret_cast<float4*>(s_x + xrow[i] * CBS + 4 * ((tid + 256 * i) % F4R)) =
+          mask4(xv[i], (xok >> i) & 1u);
     float4 cr[MT], ci[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -287,7 +300,7 @@ __global__ void __launch_bounds__(256) k_outer_fwd_stream(OuterArgs a) {
     }
     // the next chunk (the last one loads itself again: no branch around the loads)
     const int kn = 16 * min(ch + 1, nchunk - 1);
-    load_chunk(kn, xv);
+    load_chunk(kn, xv, xok);
     load_tab(kn, tr, ti);
     __syncthreads();
 #pragma unroll
@@ -355,13 +368,14 @@ __global__ void __launch_bounds__(256) k_outer_fwd_stream_bf(OuterArgs a) {
     xcol_ok[i] = col < a.post2;
     xcol[i] = min(col, a.post2 - 4);
   }
-  auto load_chunk = [&](int k0, float4 (&v)[NL]) {
+  // raw rows and an in-slab bit per element, masked when staged (as in k_outer_fwd_stream)
+  auto load_chunk = [&](int k0, float4 (&v)[NL], uint32_t& okm) {
+    okm = 0u;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int row = k0 + xrow[i];
-      const float4 t = *reinterpret_cast<const float4*>(src + (int64_t)min(row, a.Lin - 1) * a.post2 + xcol[i]);
-      const bool ok = row < a.Lin && xcol_ok[i];
-      v[i] = ok ? t : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[i] = *reinterpret_cast<const float4*>(src + (int64_t)min(row, a.Lin - 1) * a.post2 + xcol[i]);
+      okm |= (row < a.Lin && xcol_ok[i]) ? (1u << i) : 0u;
     }
   };
   // table fragments of a K-step: [row tile][Mr hi, Mr lo, Mi hi, Mi lo], columns k0 + 8 q ..
@@ -381,15 +395,17 @@ __global__ void __launch_bounds__(256) k_outer_fwd_stream_bf(OuterArgs a) {
 #pragma unroll
     for (int j = 0; j < NTW; ++j) acc[mt][j] = zero4();
   float4 xv[NL];
+  uint32_t xok;
   V8 tb[MT][4];
-  load_chunk(0, xv);
+  load_chunk(0, xv, xok);
   load_tab(0, tb);
   const bool odd = (m & 1) != 0;
   const int nchunk = (a.Lin_pad + 31) / 32;
   for (int ch = 0; ch < nchunk; ++ch) {
 #pragma unroll
     for (int i = 0; i < NL; ++i)
-      *reinterpret_cast<float4*>(s_x + xrow[i] * CBS + 4 * ((tid + 256 * i) % F4R)) = xv[i];
+      *reinterpret_cast<float4*>(s_x + xrow[i] * CBS + 4 * ((tid + 256 * i) % F4R)) =
+          mask4(xv[i], (xok >> i) & 1u);
     V8 ct[MT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -398,7 +414,7 @@ __global__ void __launch_bounds__(256) k_outer_fwd_stream_bf(OuterArgs a) {
     // rows past Lin in a chunk are loaded as zeros, so the (clamped) table operands of K-slots
     // past Lin_pad multiply zeros
     const int kn = 32 * min(ch + 1, nchunk - 1);
-    load_chunk(kn, xv);
+    load_chunk(kn, xv, xok);
     load_tab(kn, tb);
     __syncthreads();
 #pragma unroll
