@@ -8,8 +8,9 @@
 // to LDS and feeds the second product (M = cout, K = hidden); the output tile leaves through
 // LDS as row-contiguous float4 stores.  Waves take M-tiles round-robin; weight fragments are
 // read through L2.  Point tails are zero-filled on load and masked on store.  A projection to
-// at most kPwSmallOut channels does its second product on the VALU instead (see below), and a
-// lift from at most four channels runs on the VALU altogether (k_lift_valu).
+// at most kPwSmallOut channels does its second product on the VALU instead (see below); on whole
+// tiles with cin <= 32 and hidden <= 128 it runs as a grid-stride walk (k_proj_narrow).  A lift
+// from at most four channels runs on the VALU altogether (k_lift_valu).
 #include "fno_internal.h"
 #include "mfma.h"
 #include "pointwise.h"
@@ -230,6 +231,136 @@ k_pointwise_mfma(int64_t npts, int cin, int hidden, int cout, const float* __res
   }
 }
 
+// The narrow projection (NOUT <= kPwSmallOut outputs) for cin <= 32, hidden <= 64 MPW and a point
+// count that is a multiple of kPwP, as a grid-stride walk over the 64-point tiles of all batch
+// entries.  What k_pointwise_mfma<NOUT> loads per tile stays in registers for the whole walk:
+// wave w's W1 fragments (M-tiles w + 4 j, j < MPW, eight K-steps of 4: K is padded to 32 with
+// zero weights and zero x rows), b1 (the accumulators start from it) and W2 / 2 (GELU's factor
+// 1/2 is exact there).  The next tile's x rows are loaded into registers while the current one
+// is multiplied.  Same per-point arithmetic and summation order over the hidden rows and waves
+// as the tile kernel, except that the bias enters the products first.
+template <int NOUT, int MPW>
+__global__ void __launch_bounds__(256)
+    __attribute__((amdgpu_waves_per_eu(NOUT * MPW < 6 ? 4 : 3)))
+k_proj_narrow(int64_t ntiles, int64_t tiles_per_entry, int64_t npts, int cin, int hidden,
+              const float* __restrict__ x, const float* __restrict__ w1,
+              const float* __restrict__ b1, const float* __restrict__ w2,
+              const float* __restrict__ b2, float* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) float s_x[32 * kPwS];          // [32 rows][64 points]
+  __shared__ __attribute__((aligned(16))) float s_red[4 * NOUT * kPwP];  // [wave][o][point]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, q = lane >> 4;
+  float wa[MPW][8], w2h[MPW][4][NOUT];
+  f32x4 bias0[MPW];
+#pragma unroll
+  for (int j = 0; j < MPW; ++j) {
+    const int row = 16 * (wave + 4 * j) + m;
+    const float* wr = w1 + (int64_t)min(row, hidden - 1) * cin;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const int k = 4 * ks + q;
+      const float wv = wr[min(k, cin - 1)];
+      wa[j][ks] = __uint_as_float(__float_as_uint(wv) & (row < hidden && k < cin ? ~0u : 0u));
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 16 * (wave + 4 * j) + 4 * q + r;
+      bias0[j][r] = masked_bias(b1, h, hidden);
+#pragma unroll
+      for (int o = 0; o < NOUT; ++o) {
+        const float wv = w2[o * hidden + min(h, hidden - 1)];
+        w2h[j][r][o] = 0.5f * __uint_as_float(__float_as_uint(wv) & (h < hidden ? ~0u : 0u));
+      }
+    }
+  }
+  // the output bias of the channel this thread stores (threads below NOUT * 16), loaded once:
+  // a load in the store phase would wait for the next tile's loads as well
+  const float bo = masked_bias(b2, tid / (kPwP / 4), NOUT);
+  // x rows: thread item e = tid + 256 u is row e / 16 (clamped into the input; rows >= cin are
+  // zeroed when staged), points 4 (e % 16) .. + 3
+  float4 xv[2];
+  auto load_tile = [&](int64_t i) {
+    const int64_t b = i / tiles_per_entry, t = i - b * tiles_per_entry;
+    const float* xb = x + b * cin * npts + t * kPwP;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = tid + 256 * u;
+      xv[u] = load_stream4(xb + (int64_t)min(e / 16, cin - 1) * npts + 4 * (e % 16));
+    }
+  };
+  const int64_t G = gridDim.x;
+  int64_t i = blockIdx.x;
+  load_tile(i);
+  for (; i < ntiles; i += G) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = tid + 256 * u;
+      const uint32_t keep = e / 16 < cin ? ~0u : 0u;
+      float4 v = xv[u];
+      v.x = __uint_as_float(__float_as_uint(v.x) & keep);
+      v.y = __uint_as_float(__float_as_uint(v.y) & keep);
+      v.z = __uint_as_float(__float_as_uint(v.z) & keep);
+      v.w = __uint_as_float(__float_as_uint(v.w) & keep);
+      *reinterpret_cast<float4*>(s_x + (e / 16) * kPwS + 4 * (e % 16)) = v;
+    }
+    __syncthreads();
+    // the next tile of this work-group (the last walk reloads its own tile, unused): its loads
+    // are in flight while this tile is multiplied
+    load_tile(min(i + G, ntiles - 1));
+    float part[NOUT][4];
+#pragma unroll
+    for (int o = 0; o < NOUT; ++o)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) part[o][nt] = 0.f;
+#pragma unroll
+    for (int j = 0; j < MPW; ++j) {
+      f32x4 acc[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) acc[nt] = bias0[j];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          acc[nt] = mfma_f32(wa[j][ks], s_x[(4 * ks + q) * kPwS + 16 * nt + m], acc[nt]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const float v = acc[nt][r];
+          const float g2 = fmaf(fabsf(v), normal_erf(v).erf_abs, v);  // 2 GELU(v)
+#pragma unroll
+          for (int o = 0; o < NOUT; ++o) part[o][nt] = fmaf(w2h[j][r][o], g2, part[o][nt]);
+        }
+    }
+#pragma unroll
+    for (int o = 0; o < NOUT; ++o)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        float v = part[o][nt];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        if (q == 0) s_red[(wave * NOUT + o) * kPwP + 16 * nt + m] = v;
+      }
+    __syncthreads();
+    // one float4 of 4 points per thread of the first NOUT * 16; s_x and s_red are next written
+    // after the following tile's first barrier, which these reads precede
+    if (tid < NOUT * (kPwP / 4)) {
+      const int o = tid / (kPwP / 4), c4 = tid % (kPwP / 4);
+      float v[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int pp = 4 * c4 + jj;
+        v[jj] = bo + (((s_red[(0 * NOUT + o) * kPwP + pp] + s_red[(1 * NOUT + o) * kPwP + pp]) +
+                       s_red[(2 * NOUT + o) * kPwP + pp]) +
+                      s_red[(3 * NOUT + o) * kPwP + pp]);
+      }
+      const int64_t b = i / tiles_per_entry, t = i - b * tiles_per_entry;
+      *reinterpret_cast<float4*>(y + (b * NOUT + o) * npts + t * kPwP + 4 * c4) =
+          make_float4(v[0], v[1], v[2], v[3]);
+    }
+  }
+}
+
 // A lift from at most four input channels does 2 cin flops per output value, too little for the
 // matrix cores: a thread takes 4 consecutive points of one batch entry and writes them for
 // every output channel (each output row leaves as float4 stores, contiguous over the threads),
@@ -278,6 +409,28 @@ hipError_t launch_pointwise(int64_t batch, int64_t npts, int cin, int hidden, in
       default: hipLaunchKernelGGL(k_lift_valu<4>, grid, dim3(256), 0, s, npts, cout, x, w1, b1, y);
                break;
     }
+    return hipGetLastError();
+  }
+  if (hidden > 0 && cout <= kPwSmallOut && cin <= 32 && hidden <= 128 && npts % kPwP == 0 &&
+      al16(x) && al16(y)) {
+    const int64_t tpe = npts / kPwP, ntiles = batch * tpe;
+    // eight work-groups per compute unit; each walks about ntiles / 2048 tiles
+    const unsigned grid = (unsigned)min(ntiles, (int64_t)2048);
+    const bool two = hidden > 64;
+#define FNO_PROJ_NARROW(NO)                                                                     \
+  if (two)                                                                                    \
+    hipLaunchKernelGGL((k_proj_narrow<NO, 2>), dim3(grid), dim3(256), 0, s, ntiles, tpe, npts, \
+                       cin, hidden, x, w1, b1, w2, b2, y);                                    \
+  else                                                                                        \
+    hipLaunchKernelGGL((k_proj_narrow<NO, 1>), dim3(grid), dim3(256), 0, s, ntiles, tpe, npts, \
+                       cin, hidden, x, w1, b1, w2, b2, y);
+    switch (cout) {
+      case 1: FNO_PROJ_NARROW(1) break;
+      case 2: FNO_PROJ_NARROW(2) break;
+      case 3: FNO_PROJ_NARROW(3) break;
+      default: FNO_PROJ_NARROW(4) break;
+    }
+#undef FNO_PROJ_NARROW
     return hipGetLastError();
   }
   const int cin_p = (cin + 15) / 16 * 16;

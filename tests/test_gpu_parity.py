@@ -384,6 +384,30 @@ def test_projection_narrow_outputs(L, cout, hidden):
     _torch().cuda.synchronize()
     check("projection", _host(proj), O.projection_fwd(x, w1, b1, w2, b2), TOL_F32)
 
+@pytest.mark.parametrize("cout,hidden,cin,batch,npts", [
+    (1, 128, 32, 3, 64 * 1000),   # 3000 tiles: work-groups walk more than one
+    (2, 64, 32, 2, 64 * 5),       # four M-tiles: one per wave
+    (3, 100, 20, 2, 64 * 1100),   # hidden rows and input channels padded inside the tiles
+    (4, 128, 7, 1, 64 * 2500),
+    (4, 40, 32, 5, 64),           # one tile per batch entry
+])
+def test_projection_narrow_whole_tiles(L, cout, hidden, cin, batch, npts):
+    """Narrow projection heads on whole 64-point tiles (cin <= 32, hidden <= 128): the
+    grid-stride path that keeps the weights in registers and loads the next tile ahead."""
+    announce("projection whole tiles", cout, hidden, cin, batch, npts)
+    g = np.random.default_rng(400 + 10 * cout + cin)
+    x = g.standard_normal((batch, cin, npts)).astype(np.float32)
+    w1 = (g.standard_normal((hidden, cin)) / np.sqrt(cin)).astype(np.float32)
+    b1 = g.standard_normal(hidden).astype(np.float32)
+    w2 = (g.standard_normal((cout, hidden)) / np.sqrt(hidden)).astype(np.float32)
+    b2 = g.standard_normal(cout).astype(np.float32)
+    proj = L.pointwise(_dev(x), _dev(w1), _dev(b1), _dev(w2), _dev(b2))
+    nob = L.pointwise(_dev(x), _dev(w1), None, _dev(w2), None)
+    _torch().cuda.synchronize()
+    check("projection", _host(proj), O.projection_fwd(x, w1, b1, w2, b2), TOL_F32)
+    check("projection, no biases", _host(nob), O.projection_fwd(x, w1, None, w2, None), TOL_F32)
+
+
 def test_pointwise_widest(L):
     """The widest pointwise layers the boundary accepts (64 -> 256 -> 128), ragged point count."""
     announce("pointwise widest")
