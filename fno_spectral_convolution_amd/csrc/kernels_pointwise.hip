@@ -231,14 +231,40 @@ k_pointwise_mfma(int64_t npts, int cin, int hidden, int cout, const float* __res
   }
 }
 
+// v = h + m + l exactly for eight floats: h = bf16(v), m = bf16(v - h), l = bf16(v - h - m),
+// each rounded to nearest even (two values per conversion); every remainder is exact in
+// float32 and carries the next 8 of v's 24 significant bits, so l is exact too.
+__device__ __forceinline__ void split3_x8(const float (&v)[8], bf16x8& h, bf16x8& m,
+                                          bf16x8& l) {
+  uint32_t hh[4], mm[4], ll[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    hh[k] = pack_bf16x2(v[2 * k], v[2 * k + 1]);
+    const float r0 = v[2 * k] - __uint_as_float(hh[k] << 16);
+    const float r1 = v[2 * k + 1] - __uint_as_float(hh[k] & 0xffff0000u);
+    mm[k] = pack_bf16x2(r0, r1);
+    ll[k] = pack_bf16x2(r0 - __uint_as_float(mm[k] << 16),
+                        r1 - __uint_as_float(mm[k] & 0xffff0000u));
+  }
+  h = __builtin_bit_cast(bf16x8, make_uint4(hh[0], hh[1], hh[2], hh[3]));
+  m = __builtin_bit_cast(bf16x8, make_uint4(mm[0], mm[1], mm[2], mm[3]));
+  l = __builtin_bit_cast(bf16x8, make_uint4(ll[0], ll[1], ll[2], ll[3]));
+}
+
 // The narrow projection (NOUT <= kPwSmallOut outputs) for cin <= 32, hidden <= 64 MPW and a point
 // count that is a multiple of kPwP, as a grid-stride walk over the 64-point tiles of all batch
 // entries.  What k_pointwise_mfma<NOUT> loads per tile stays in registers for the whole walk:
-// wave w's W1 fragments (M-tiles w + 4 j, j < MPW, eight K-steps of 4: K is padded to 32 with
-// zero weights and zero x rows), b1 (the accumulators start from it) and W2 / 2 (GELU's factor
-// 1/2 is exact there).  The next tile's x rows are loaded into registers while the current one
-// is multiplied.  Same per-point arithmetic and summation order over the hidden rows and waves
-// as the tile kernel, except that the bias enters the products first.
+// wave w's W1 fragments (M-tiles w + 4 j, j < MPW; K padded to 32 with zero weights and zero
+// x rows), b1 (the accumulators start from it) and W2 / 2 (GELU's factor 1/2 is exact there).
+// The next tile's x rows are loaded into registers while the current one is multiplied.
+// The first product runs in float32 precision on the bfloat16 matrix cores: both operands are
+// split exactly into three bfloat16 terms and the six term products of order <= 2 are
+// accumulated in float32 (the dropped three are below 2^-23 |a b|), one 16x16x32 MFMA per term
+// product over the whole K, 96 cycles per 16x16 tile against 256 for eight float32 16x16x4
+// MFMAs.  The x tile is staged as the three term planes [point][32 channels] (64-byte point
+// rows of four 16-byte channel chunks, chunk c of point p at c ^ ((p >> 1) & 3), so that eight
+// consecutive lanes of a 16-byte access cover every bank).  Same summation order over the
+// hidden rows and waves as the tile kernel, except that the bias enters the products first.
 template <int NOUT, int MPW>
 __global__ void __launch_bounds__(256)
     __attribute__((amdgpu_waves_per_eu(NOUT * MPW < 6 ? 4 : 3)))
@@ -246,62 +272,66 @@ k_proj_narrow(int64_t ntiles, int64_t tiles_per_entry, int64_t npts, int cin, in
               const float* __restrict__ x, const float* __restrict__ w1,
               const float* __restrict__ b1, const float* __restrict__ w2,
               const float* __restrict__ b2, float* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) float s_x[32 * kPwS];          // [32 rows][64 points]
+  __shared__ uint4 s_xs[3 * kPwP * 4];                                   // [term][point][chunk]
   __shared__ __attribute__((aligned(16))) float s_red[4 * NOUT * kPwP];  // [wave][o][point]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, q = lane >> 4;
-  float wa[MPW][8], w2h[MPW][4][NOUT];
+  bf16x8 wh[MPW], wm[MPW], wl[MPW];
+  float w2h[MPW][4][NOUT];
   f32x4 bias0[MPW];
 #pragma unroll
   for (int j = 0; j < MPW; ++j) {
+    // A operand: lane (m, q) holds W1[16 mt + m][8 q + e], e = 0..7
     const int row = 16 * (wave + 4 * j) + m;
     const float* wr = w1 + (int64_t)min(row, hidden - 1) * cin;
+    float wv[8];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const int k = 4 * ks + q;
-      const float wv = wr[min(k, cin - 1)];
-      wa[j][ks] = __uint_as_float(__float_as_uint(wv) & (row < hidden && k < cin ? ~0u : 0u));
+    for (int e = 0; e < 8; ++e) {
+      const int k = 8 * q + e;
+      const float v = wr[min(k, cin - 1)];
+      wv[e] = __uint_as_float(__float_as_uint(v) & (row < hidden && k < cin ? ~0u : 0u));
     }
+    split3_x8(wv, wh[j], wm[j], wl[j]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int h = 16 * (wave + 4 * j) + 4 * q + r;
       bias0[j][r] = masked_bias(b1, h, hidden);
 #pragma unroll
       for (int o = 0; o < NOUT; ++o) {
-        const float wv = w2[o * hidden + min(h, hidden - 1)];
-        w2h[j][r][o] = 0.5f * __uint_as_float(__float_as_uint(wv) & (h < hidden ? ~0u : 0u));
+        const float wv2 = w2[o * hidden + min(h, hidden - 1)];
+        w2h[j][r][o] = 0.5f * __uint_as_float(__float_as_uint(wv2) & (h < hidden ? ~0u : 0u));
       }
     }
   }
   // the output bias of the channel this thread stores (threads below NOUT * 16), loaded once:
   // a load in the store phase would wait for the next tile's loads as well
   const float bo = masked_bias(b2, tid / (kPwP / 4), NOUT);
-  // x rows: thread item e = tid + 256 u is row e / 16 (clamped into the input; rows >= cin are
-  // zeroed when staged), points 4 (e % 16) .. + 3
-  float4 xv[2];
+  // x: thread (point p = tid % 64, channel chunk cg = tid / 64) loads channels 8 cg .. 8 cg + 7
+  // of its point (clamped into the input; channels >= cin are zeroed when staged)
+  const int p = tid & (kPwP - 1), cg = tid / kPwP;
+  float xv[8];
   auto load_tile = [&](int64_t i) {
     const int64_t b = i / tiles_per_entry, t = i - b * tiles_per_entry;
-    const float* xb = x + b * cin * npts + t * kPwP;
+    const float* xb = x + b * cin * npts + t * kPwP + p;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int e = tid + 256 * u;
-      xv[u] = load_stream4(xb + (int64_t)min(e / 16, cin - 1) * npts + 4 * (e % 16));
-    }
+    for (int e = 0; e < 8; ++e)
+      xv[e] = __builtin_nontemporal_load(xb + (int64_t)min(8 * cg + e, cin - 1) * npts);
   };
   const int64_t G = gridDim.x;
   int64_t i = blockIdx.x;
   load_tile(i);
   for (; i < ntiles; i += G) {
+    {
+      float v[8];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int e = tid + 256 * u;
-      const uint32_t keep = e / 16 < cin ? ~0u : 0u;
-      float4 v = xv[u];
-      v.x = __uint_as_float(__float_as_uint(v.x) & keep);
-      v.y = __uint_as_float(__float_as_uint(v.y) & keep);
-      v.z = __uint_as_float(__float_as_uint(v.z) & keep);
-      v.w = __uint_as_float(__float_as_uint(v.w) & keep);
-      *reinterpret_cast<float4*>(s_x + (e / 16) * kPwS + 4 * (e % 16)) = v;
+      for (int e = 0; e < 8; ++e)
+        v[e] = __uint_as_float(__float_as_uint(xv[e]) & (8 * cg + e < cin ? ~0u : 0u));
+      bf16x8 h, mm, l;
+      split3_x8(v, h, mm, l);
+      const int slot = 4 * p + (cg ^ ((p >> 1) & 3));
+      s_xs[slot] = __builtin_bit_cast(uint4, h);
+      s_xs[4 * kPwP + slot] = __builtin_bit_cast(uint4, mm);
+      s_xs[8 * kPwP + slot] = __builtin_bit_cast(uint4, l);
     }
     __syncthreads();
     // the next tile of this work-group (the last walk reloads its own tile, unused): its loads
@@ -313,24 +343,30 @@ k_proj_narrow(int64_t ntiles, int64_t tiles_per_entry, int64_t npts, int cin, in
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) part[o][nt] = 0.f;
 #pragma unroll
-    for (int j = 0; j < MPW; ++j) {
-      f32x4 acc[4];
+    for (int nt = 0; nt < 4; ++nt) {
+      // B operand: lane (m, q) holds x[8 q + e][point 16 nt + m]
+      const int pp = 16 * nt + m;
+      const int slot = 4 * pp + (q ^ ((pp >> 1) & 3));
+      const bf16x8 bh = __builtin_bit_cast(bf16x8, s_xs[slot]);
+      const bf16x8 bm = __builtin_bit_cast(bf16x8, s_xs[4 * kPwP + slot]);
+      const bf16x8 bl = __builtin_bit_cast(bf16x8, s_xs[8 * kPwP + slot]);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[nt] = bias0[j];
+      for (int j = 0; j < MPW; ++j) {
+        f32x4 acc = bias0[j];  // the six term products, smallest first
+        acc = mfma_bf16(wm[j], bm, acc);
+        acc = mfma_bf16(wh[j], bl, acc);
+        acc = mfma_bf16(wl[j], bh, acc);
+        acc = mfma_bf16(wh[j], bm, acc);
+        acc = mfma_bf16(wm[j], bh, acc);
+        acc = mfma_bf16(wh[j], bh, acc);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          acc[nt] = mfma_f32(wa[j][ks], s_x[(4 * ks + q) * kPwS + 16 * nt + m], acc[nt]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const float v = acc[nt][r];
+        for (int r = 0; r < 4; ++r) {
+          const float v = acc[r];
           const float g2 = fmaf(fabsf(v), normal_erf(v).erf_abs, v);  // 2 GELU(v)
 #pragma unroll
           for (int o = 0; o < NOUT; ++o) part[o][nt] = fmaf(w2h[j][r][o], g2, part[o][nt]);
         }
+      }
     }
 #pragma unroll
     for (int o = 0; o < NOUT; ++o)
